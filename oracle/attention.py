@@ -1,0 +1,187 @@
+"""Plain float64 attention: the definition written out, one head at a time.
+
+Test infrastructure only (see the package docstring).  Nothing here is blocked,
+fused or reordered: S and P are built in full, as the unfused chain of
+operators the pages contrast FlashAttention with (page 1, "引言/动机": matmul,
+scale, mask, softmax, matmul).
+
+Conventions (the readings of the pages that this oracle fixes):
+
+* S = scale * Q K^T.  Page 1 writes S = Q K^T; the scale is the
+  ``sm_scale`` argument of the kernel call printed on page 2 ("Sequence
+  Parallel"), and callers pass 1/sqrt(d).
+* Causal mask: key j is visible to query row i iff j <= i + (Nk - Nq)
+  (bottom-right alignment; for Nq == Nk this is the usual lower triangle that
+  page 2 describes when it skips the upper-right blocks).  Masked scores are
+  -inf, so they get probability exactly 0.
+* L is the natural-log logsumexp of the scaled, masked score row.
+* All arithmetic is float64 on inputs converted exactly from bf16 or fp32.
+"""
+
+from __future__ import annotations
+
+import numpy as np
+
+
+def _as_f64(x) -> np.ndarray:
+    a = np.asarray(x)
+    if a.dtype != np.float64:
+        a = a.astype(np.float64)
+    return a
+
+
+def causal_visible(nq: int, nk: int) -> np.ndarray:
+    """Boolean [nq, nk] matrix: True where key j is visible to query row i.
+
+    Bottom-right alignment: j <= i + (nk - nq).  Page 2 ("FlashAttention V2 相比
+    V1 有哪些改进") describes the causal case as skipping the blocks above the
+    diagonal; for nq == nk the visible set is j <= i.
+    """
+    i = np.arange(nq)[:, None]
+    j = np.arange(nk)[None, :]
+    return j <= i + (nk - nq)
+
+
+def scores(Q, K, scale: float, causal: bool) -> np.ndarray:
+    """S = scale * Q K^T with -inf at masked positions.  Q [nq, dk], K [nk, dk].
+
+    Page 1, "Flash Attention" section, first line of the formula (S = Q K^T),
+    with the softmax scale applied to the product.
+    """
+    Q = _as_f64(Q)
+    K = _as_f64(K)
+    S = scale * (Q @ K.T)
+    if causal:
+        S = np.where(causal_visible(Q.shape[0], K.shape[0]), S, -np.inf)
+    return S
+
+
+def softmax_with_lse(S) -> tuple[np.ndarray, np.ndarray]:
+    """Row softmax P and natural-log logsumexp L of a score matrix S [nq, nk].
+
+    Safe softmax (page 2, "理解FlashAttention核心逻辑": softmax -> safe
+    softmax): subtract the row maximum m before exponentiating, so
+    P_ij = exp(S_ij - m_i) / l_i with l_i = sum_j exp(S_ij - m_i), and
+    L_i = m_i + ln l_i.  Every row must hold at least one finite score.
+    """
+    S = _as_f64(S)
+    m = S.max(axis=1, keepdims=True)
+    if not np.all(np.isfinite(m)):
+        raise ValueError("every score row needs at least one unmasked entry")
+    e = np.exp(S - m)
+    l = e.sum(axis=1, keepdims=True)
+    P = e / l
+    L = (m + np.log(l))[:, 0]
+    return P, L
+
+
+def attention_forward(Q, K, V, scale: float, causal: bool):
+    """Forward pass for one head: returns (O [nq, dv], L [nq]).
+
+    Page 1, "Flash Attention" section: S = Q K^T, P = softmax(S), O = P V;
+    L as defined in ``softmax_with_lse``.
+    """
+    S = scores(Q, K, scale, causal)
+    P, L = softmax_with_lse(S)
+    O = P @ _as_f64(V)
+    return O, L
+
+
+def attention_forward_rows(Q, K, V, rows, scale: float, causal: bool):
+    """Forward pass for selected query rows of one head (same definition).
+
+    Row i of O and L depends only on Q_i and all of K, V, so a sample of rows
+    can be checked at sizes where the full S would be too large to hold.
+    """
+    Q = _as_f64(Q)
+    K = _as_f64(K)
+    V = _as_f64(V)
+    nq, nk = Q.shape[0], K.shape[0]
+    rows = np.asarray(rows, dtype=np.int64)
+    S = scale * (Q[rows] @ K.T)
+    if causal:
+        vis = np.arange(nk)[None, :] <= (rows[:, None] + (nk - nq))
+        S = np.where(vis, S, -np.inf)
+    P, L = softmax_with_lse(S)
+    return P @ V, L
+
+
+def attention_backward(Q, K, V, dO, scale: float, causal: bool, return_aux: bool = False):
+    """Gradients of f = sum(dO * O) for one head: returns (dQ, dK, dV).
+
+    P is recomputed from the inputs (page 3, section 3: recomputation in the
+    backward pass instead of storing the N x N intermediates).  The steps are
+    the chain rule through O = P V and the row softmax; the pages name the
+    per-row auxiliary D (page 2, the ``D`` argument of the backward kernel
+    call) but do not print its formula, which the softmax Jacobian fixes:
+
+        dV = P^T dO
+        dP = dO V^T
+        D_i = sum_j P_ij dP_ij
+        dS = P * (dP - D)            (elementwise, D broadcast along rows)
+        dQ = scale * dS K
+        dK = scale * dS^T Q
+
+    D is formed from P and dP, not from the shortcut dO_i . O_i that a kernel
+    uses; the two agree because O_i = sum_j P_ij V_j.
+    With ``return_aux`` also returns a dict holding P, L, dP, D and dS.
+    """
+    Q = _as_f64(Q)
+    K = _as_f64(K)
+    V = _as_f64(V)
+    dO = _as_f64(dO)
+    S = scores(Q, K, scale, causal)
+    P, L = softmax_with_lse(S)
+    dV = P.T @ dO
+    dP = dO @ V.T
+    D = (P * dP).sum(axis=1, keepdims=True)
+    dS = P * (dP - D)
+    dQ = scale * (dS @ K)
+    dK = scale * (dS.T @ Q)
+    if return_aux:
+        return dQ, dK, dV, {"P": P, "L": L, "dP": dP, "D": D[:, 0], "dS": dS}
+    return dQ, dK, dV
+
+
+def _heads(x):
+    x = _as_f64(x)
+    lead = x.shape[:-2]
+    return x.reshape((-1,) + x.shape[-2:]), lead
+
+
+def attention_forward_batched(Q, K, V, scale: float, causal: bool, heads=None):
+    """``attention_forward`` over leading [B, H] dims, one head at a time.
+
+    Q [B, H, nq, d], K and V [B, H, nk, d].  ``heads`` (flat b*H + h indices)
+    restricts the work to a sample of heads; the result then has shape
+    [len(heads), nq, d] and [len(heads), nq].
+    """
+    q, lead = _heads(Q)
+    k, _ = _heads(K)
+    v, _ = _heads(V)
+    idx = range(q.shape[0]) if heads is None else list(heads)
+    O = np.empty((len(idx), q.shape[1], v.shape[2]))
+    L = np.empty((len(idx), q.shape[1]))
+    for n, h in enumerate(idx):
+        O[n], L[n] = attention_forward(q[h], k[h], v[h], scale, causal)
+    if heads is None:
+        return O.reshape(lead + O.shape[1:]), L.reshape(lead + L.shape[1:])
+    return O, L
+
+
+def attention_backward_batched(Q, K, V, dO, scale: float, causal: bool, heads=None):
+    """``attention_backward`` over leading [B, H] dims, one head at a time."""
+    q, lead = _heads(Q)
+    k, _ = _heads(K)
+    v, _ = _heads(V)
+    do, _ = _heads(dO)
+    idx = range(q.shape[0]) if heads is None else list(heads)
+    dQ = np.empty((len(idx),) + q.shape[1:])
+    dK = np.empty((len(idx),) + k.shape[1:])
+    dV = np.empty((len(idx),) + v.shape[1:])
+    for n, h in enumerate(idx):
+        dQ[n], dK[n], dV[n] = attention_backward(q[h], k[h], v[h], do[h], scale, causal)
+    if heads is None:
+        return (dQ.reshape(lead + dQ.shape[1:]), dK.reshape(lead + dK.shape[1:]),
+                dV.reshape(lead + dV.shape[1:]))
+    return dQ, dK, dV
