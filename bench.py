@@ -1,0 +1,250 @@
+#!/usr/bin/env python3
+"""Throughput of the fused attention path on one MI355X.
+
+One step = the whole hot path on one batch: forward (fa_fwd) then backward
+(fa_bwd: preprocess, main kernel, dQ conversion) on the long-sequence
+workload B=1, H=32, N=8192, d=128, causal, bf16 (Q and K scaled by 3).
+Inputs are synthetic (seeded normal draws on the GPU) and resident in HBM
+before timing starts.  Prints ONE JSON line on stdout; progress goes to stderr.
+
+FLOP convention: forward 2 GEMMs = 4*d per unmasked (query, key) pair,
+backward 5 GEMMs = 10*d per pair; pairs = N(N+1)/2 per head when causal.
+"""
+
+import argparse
+import hashlib
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "attention fwd/bwd TFLOP/s (bf16) at B·H·N·d, and % of MI355X MFMA peak"
+PEAK_BF16_TFLOPS = 2516.6  # dense bf16 MFMA: 256 CUs x 4096 flop/clk x 2.4 GHz
+PEAK_HBM_GBS = 8000.0
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "hbm_traffic.json")
+
+
+def log(msg):
+    print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+
+def unmasked_pairs(Nq, Nk, causal):
+    if not causal:
+        return Nq * Nk
+    off = Nk - Nq  # key j visible to row i iff j <= i + off
+    # rows i with i + off + 1 >= Nk see all keys; the others see i + off + 1
+    full_from = max(0, Nk - off - 1)
+    part = sum(min(Nk, i + off + 1) for i in range(min(Nq, full_from)))
+    return part + max(0, Nq - full_from) * Nk
+
+
+def source_sha(path):
+    with open(path, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()
+
+
+def measured_traffic(kernel_name, source):
+    """HBM bytes per launch from the committed rocprofv3 counter summary, or
+    None when there is none or the kernel source changed since it was taken."""
+    if not os.path.exists(TRAFFIC_FILE):
+        return None
+    with open(TRAFFIC_FILE) as f:
+        rec = json.load(f)
+    k = rec.get("kernels", {}).get(kernel_name)
+    if not k or k.get("source_sha256") != source_sha(source):
+        return None
+    return k.get("bytes_per_launch")
+
+
+def cpu_baseline(w, x, heads):
+    """The float64 oracle, untuned, on the first `heads` heads at full size."""
+    import numpy as np
+
+    import oracle
+
+    try:
+        from threadpoolctl import threadpool_info
+        cores = max((i.get("num_threads", 1) for i in threadpool_info()), default=1)
+    except Exception:  # pragma: no cover - threadpoolctl is optional
+        cores = os.cpu_count() or 1
+    BH = w.B * w.H
+    flat = {k: v.reshape(BH, v.shape[2], w.d) for k, v in x.items()}
+    t0 = time.perf_counter()
+    for h in range(heads):
+        Q, K, V, dO = (flat[k][h].float().cpu().double().numpy() for k in ("Q", "K", "V", "dO"))
+        t_in = time.perf_counter()
+        oracle.attention_forward(Q, K, V, w.scale, w.causal)
+        oracle.attention_backward(Q, K, V, dO, w.scale, w.causal)
+        log(f"oracle head {h}: {time.perf_counter() - t_in:.1f} s")
+        del Q, K, V, dO
+    dt = time.perf_counter() - t0
+    flops = 14 * w.d * unmasked_pairs(w.Nq, w.Nk, w.causal) * heads
+    return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": int(cores), "kind": "oracle",
+            "sample": f"forward+backward of {heads} of {BH} heads of {w.name} at full size "
+                      f"(float64 numpy, {dt:.1f} s)", "seconds": dt}
+
+
+def bench_decode(fa, torch, steps):
+    from exact_attention_118_amd import synth
+
+    w = synth.WORKLOADS["decode_b16h32k16384d128"]
+    x = synth.make_inputs(w, seed=0, device="cuda")
+    O = torch.empty_like(x["Q"])
+    L = torch.empty(w.B, w.H, 1, dtype=torch.float32, device="cuda")
+    splits = fa.fwd_num_splits(w.B, w.H, 1, w.Nk, w.d, fa.FA_BF16, 0)
+    ws = torch.empty(fa.fwd_workspace_size(w.B, w.H, 1, w.Nk, w.d, fa.FA_BF16, 0),
+                     dtype=torch.uint8, device="cuda")
+    for _ in range(2):
+        fa.fa_fwd(x["Q"], x["K"], x["V"], O, L, w.scale, False, workspace=ws)
+    torch.cuda.synchronize()
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(steps + 1)]
+    ev[0].record()
+    for i in range(steps):
+        fa.fa_fwd(x["Q"], x["K"], x["V"], O, L, w.scale, False, workspace=ws)
+        ev[i + 1].record()
+    torch.cuda.synchronize()
+    ms = ev[0].elapsed_time(ev[-1]) / steps
+    kv_bytes = 2 * w.B * w.H * w.Nk * w.d * 2
+    all_bytes = kv_bytes + 2 * w.B * w.H * w.d * 2 + w.B * w.H * 4
+    del x
+    return {"workload": w.name, "ms": ms, "splits": splits,
+            "GB/s": all_bytes / (ms * 1e-3) / 1e9,
+            "hbm_frac": all_bytes / (ms * 1e-3) / 1e9 / PEAK_HBM_GBS,
+            "algorithmic_bytes": all_bytes}
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--workload", default="b1h32n8192d128_causal")
+    ap.add_argument("--cpu-heads", type=int, default=2,
+                    help="heads of the workload the float64 oracle is timed on (0 = skip)")
+    ap.add_argument("--no-decode", action="store_true", help="skip the decode-shaped forward")
+    args = ap.parse_args()
+
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
+              "(attention heads shard across GPUs with no communication, so the per-GPU "
+              "figure is the one-GPU figure)", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    import exact_attention_118_amd as fa
+    from exact_attention_118_amd import synth
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(1)
+    fa.load_library()
+    w = synth.WORKLOADS[args.workload]
+    log(f"workload {w}")
+    x = synth.make_inputs(w, seed=0, device="cuda")
+    Q, K, V, dO = x["Q"], x["K"], x["V"], x["dO"]
+    O = torch.empty_like(Q)
+    L = torch.empty(w.B, w.H, w.Nq, dtype=torch.float32, device="cuda")
+    dQ, dK, dV = torch.empty_like(Q), torch.empty_like(K), torch.empty_like(V)
+    ws = torch.empty(fa.bwd_workspace_size(w.B, w.H, w.Nq, w.Nk, w.d, fa.FA_BF16),
+                     dtype=torch.uint8, device="cuda")
+
+    def step(ev=None):
+        if ev is not None:
+            ev[0].record()
+        fa.fa_fwd(Q, K, V, O, L, w.scale, w.causal)
+        if ev is not None:
+            ev[1].record()
+        fa.fa_bwd(Q, K, V, O, L, dO, dQ, dK, dV, w.scale, w.causal, workspace=ws,
+                  stages=fa.FA_BWD_PREPROCESS)
+        if ev is not None:
+            ev[2].record()
+        fa.fa_bwd(Q, K, V, O, L, dO, dQ, dK, dV, w.scale, w.causal, workspace=ws,
+                  stages=fa.FA_BWD_MAIN)
+        if ev is not None:
+            ev[3].record()
+        fa.fa_bwd(Q, K, V, O, L, dO, dQ, dK, dV, w.scale, w.causal, workspace=ws,
+                  stages=fa.FA_BWD_FINALIZE)
+        if ev is not None:
+            ev[4].record()
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    log(f"warmup {args.warmup} done")
+
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(5)] for _ in range(args.steps)]
+    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    start.record()
+    for k in range(args.steps):
+        step(evs[k])
+    end.record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms_per_step = start.elapsed_time(end) / args.steps
+    log(f"timed {args.steps} steps: {ms_per_step:.3f} ms/step (wall {wall * 1e3 / args.steps:.3f})")
+
+    def mean_ms(a, b):
+        return sum(e[a].elapsed_time(e[b]) for e in evs) / len(evs)
+
+    fwd_ms, pre_ms, main_ms, fin_ms = mean_ms(0, 1), mean_ms(1, 2), mean_ms(2, 3), mean_ms(3, 4)
+    bwd_ms = pre_ms + main_ms + fin_ms
+    pairs = unmasked_pairs(w.Nq, w.Nk, w.causal) * w.B * w.H
+    fwd_flops, bwd_flops = 4 * w.d * pairs, 10 * w.d * pairs
+    value = (fwd_flops + bwd_flops) / (ms_per_step * 1e-3) / 1e12
+
+    kernels = {
+        "fwd_bf16_kernel": {"ms": fwd_ms, "flops": fwd_flops,
+                            "source": os.path.join(ROOT, "exact_attention_118_amd", "csrc", "fa_fwd.hip")},
+        "bwd_dkdv_bf16_kernel": {"ms": main_ms, "flops": bwd_flops,
+                                 "source": os.path.join(ROOT, "exact_attention_118_amd", "csrc", "fa_bwd.hip")},
+    }
+    dom_name = max(kernels, key=lambda k: kernels[k]["ms"])
+    dom = kernels[dom_name]
+    achieved = dom["flops"] / (dom["ms"] * 1e-3) / 1e12
+    roofline = {"bound": "mfma", "achieved": achieved, "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                "frac": achieved / PEAK_BF16_TFLOPS, "traffic": measured_traffic(dom_name, dom["source"]),
+                "kernel": dom_name, "kernel_ms": dom["ms"]}
+
+    out = {
+        "metric": METRIC,
+        "value": value,
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_per_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": w.name, "B": w.B, "H": w.H, "N": w.Nq, "d": w.d,
+                   "causal": w.causal, "qk_mult": w.qk_mult, "pass": "fwd+bwd"},
+        "roofline": roofline,
+        "fwd": {"ms": fwd_ms, "TFLOP/s": fwd_flops / (fwd_ms * 1e-3) / 1e12,
+                "mfma_frac": fwd_flops / (fwd_ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS},
+        "bwd": {"ms": bwd_ms, "TFLOP/s": bwd_flops / (bwd_ms * 1e-3) / 1e12,
+                "mfma_frac": bwd_flops / (bwd_ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS,
+                "preprocess_ms": pre_ms, "main_ms": main_ms, "finalize_ms": fin_ms},
+    }
+    del dQ, dK, dV, ws
+    if not args.no_decode:
+        log("decode-shaped forward")
+        out["decode"] = bench_decode(fa, torch, steps=10)
+    if args.cpu_heads > 0:
+        log(f"float64 oracle on {args.cpu_heads} heads")
+        out["cpu_baseline"] = cpu_baseline(w, x, args.cpu_heads)
+    else:
+        out["cpu_baseline"] = None
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,1 +1,215 @@
-"""MI355X (gfx950) fused attention: Python binding of the libfa C ABI."""
+"""MI355X (gfx950) fused scaled-dot-product attention: Python binding of libfa.
+
+The binding only marshals arguments: every step of the computation runs in the
+HIP kernels of ``libfa.so`` (built in-tree from ``csrc/`` by ``build.py``).
+torch is used for device memory and the current stream.  There is no fallback:
+if the library is missing or a call fails, an exception is raised.
+"""
+
+from __future__ import annotations
+
+import ctypes
+import math
+import os
+
+__all__ = [
+    "FAError", "load_library", "lib_path", "fa_fwd", "fa_bwd", "forward", "backward",
+    "fwd_workspace_size", "bwd_workspace_size", "fwd_num_splits", "status_string", "version",
+    "FA_OK", "FA_ERR_NULL", "FA_ERR_SHAPE", "FA_ERR_UNSUPPORTED", "FA_ERR_ALIGN",
+    "FA_ERR_WORKSPACE", "FA_ERR_HIP", "FA_BF16", "FA_FP32", "EXPORTED_SYMBOLS",
+    "FA_BWD_PREPROCESS", "FA_BWD_MAIN", "FA_BWD_FINALIZE", "FA_BWD_ALL",
+]
+
+FA_OK, FA_ERR_NULL, FA_ERR_SHAPE, FA_ERR_UNSUPPORTED, FA_ERR_ALIGN, FA_ERR_WORKSPACE, FA_ERR_HIP = range(7)
+FA_BF16, FA_FP32 = 0, 1
+
+FA_BWD_PREPROCESS, FA_BWD_MAIN, FA_BWD_FINALIZE, FA_BWD_ALL = 1, 2, 4, 7
+
+EXPORTED_SYMBOLS = ("fa_fwd", "fa_bwd", "fa_bwd_stages", "fa_fwd_workspace_size",
+                    "fa_bwd_workspace_size", "fa_fwd_num_splits", "fa_status_string", "fa_version")
+
+_LIB = None
+
+
+class FAError(RuntimeError):
+    def __init__(self, status: int, where: str):
+        self.status = status
+        super().__init__(f"{where}: {status_string(status)}")
+
+
+def lib_path() -> str:
+    return os.path.join(os.path.dirname(os.path.abspath(__file__)), "libfa.so")
+
+
+def load_library():
+    """Load libfa.so (built by ``build.py``) and declare its C signatures."""
+    global _LIB
+    if _LIB is not None:
+        return _LIB
+    path = lib_path()
+    if not os.path.exists(path):
+        raise RuntimeError(f"{path} is missing: build it with exact_attention_118_amd.build.build()")
+    lib = ctypes.CDLL(path)
+    vp, sz, i, f = ctypes.c_void_p, ctypes.c_size_t, ctypes.c_int, ctypes.c_float
+    lib.fa_fwd.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, i, f, i, i, i, vp, sz, vp]
+    lib.fa_fwd.restype = i
+    lib.fa_bwd.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, i, i, i, i, i, f, i, i, vp, sz, vp]
+    lib.fa_bwd.restype = i
+    lib.fa_bwd_stages.argtypes = lib.fa_bwd.argtypes + [i]
+    lib.fa_bwd_stages.restype = i
+    lib.fa_fwd_workspace_size.argtypes = [i, i, i, i, i, i, i]
+    lib.fa_fwd_workspace_size.restype = sz
+    lib.fa_bwd_workspace_size.argtypes = [i, i, i, i, i, i]
+    lib.fa_bwd_workspace_size.restype = sz
+    lib.fa_fwd_num_splits.argtypes = [i, i, i, i, i, i, i]
+    lib.fa_fwd_num_splits.restype = i
+    lib.fa_status_string.argtypes = [i]
+    lib.fa_status_string.restype = ctypes.c_char_p
+    lib.fa_version.argtypes = []
+    lib.fa_version.restype = i
+    _LIB = lib
+    return lib
+
+
+def status_string(status: int) -> str:
+    return load_library().fa_status_string(int(status)).decode()
+
+
+def version() -> int:
+    return load_library().fa_version()
+
+
+# --------------------------------------------------------------------------- torch helpers
+
+def _torch():
+    import torch
+    return torch
+
+
+def _dtype_code(t) -> int:
+    torch = _torch()
+    if t.dtype == torch.bfloat16:
+        return FA_BF16
+    if t.dtype == torch.float32:
+        return FA_FP32
+    raise TypeError(f"unsupported dtype {t.dtype}; libfa takes bfloat16 or float32")
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream_handle(device, stream):
+    torch = _torch()
+    s = stream if stream is not None else torch.cuda.current_stream(device)
+    return ctypes.c_void_p(s.cuda_stream)
+
+
+def _check_tensor(name, t, shape, dtype, device):
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a GPU tensor")
+    if t.device != device:
+        raise ValueError(f"{name} is on {t.device}, expected {device}")
+    if tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} has shape {tuple(t.shape)}, expected {tuple(shape)}")
+    if t.dtype != dtype:
+        raise ValueError(f"{name} has dtype {t.dtype}, expected {dtype}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+
+
+def fwd_workspace_size(B, H, Nq, Nk, d, dtype_code, num_splits=0) -> int:
+    return load_library().fa_fwd_workspace_size(B, H, Nq, Nk, d, dtype_code, num_splits)
+
+
+def bwd_workspace_size(B, H, Nq, Nk, d, dtype_code) -> int:
+    return load_library().fa_bwd_workspace_size(B, H, Nq, Nk, d, dtype_code)
+
+
+def fwd_num_splits(B, H, Nq, Nk, d, dtype_code, num_splits=0) -> int:
+    return load_library().fa_fwd_num_splits(B, H, Nq, Nk, d, dtype_code, num_splits)
+
+
+def _alloc_workspace(nbytes, device):
+    torch = _torch()
+    if nbytes == 0:
+        return None
+    return torch.empty(nbytes, dtype=torch.uint8, device=device)
+
+
+def fa_fwd(Q, K, V, O, L, scale, causal, num_splits=0, workspace=None, stream=None):
+    """Call ``fa_fwd`` on existing tensors (O and L are written in place)."""
+    lib = load_library()
+    B, H, Nq, d = Q.shape
+    Nk = K.shape[2]
+    dev = Q.device
+    _check_tensor("Q", Q, (B, H, Nq, d), Q.dtype, dev)
+    _check_tensor("K", K, (B, H, Nk, d), Q.dtype, dev)
+    _check_tensor("V", V, (B, H, Nk, d), Q.dtype, dev)
+    _check_tensor("O", O, (B, H, Nq, d), Q.dtype, dev)
+    _check_tensor("L", L, (B, H, Nq), _torch().float32, dev)
+    code = _dtype_code(Q)
+    need = lib.fa_fwd_workspace_size(B, H, Nq, Nk, d, code, num_splits)
+    if workspace is None:
+        workspace = _alloc_workspace(need, dev)
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    st = lib.fa_fwd(_ptr(Q), _ptr(K), _ptr(V), _ptr(O), _ptr(L), B, H, Nq, Nk, d, float(scale),
+                    int(bool(causal)), code, int(num_splits), _ptr(workspace), ws_bytes,
+                    _stream_handle(dev, stream))
+    if st != FA_OK:
+        raise FAError(st, "fa_fwd")
+    return O, L
+
+
+def fa_bwd(Q, K, V, O, L, dO, dQ, dK, dV, scale, causal, workspace=None, stream=None,
+           stages=FA_BWD_ALL):
+    """Call ``fa_bwd`` (or ``fa_bwd_stages`` for a partial stage mask) on
+    existing tensors (dQ, dK, dV are overwritten)."""
+    lib = load_library()
+    B, H, Nq, d = Q.shape
+    Nk = K.shape[2]
+    dev = Q.device
+    for name, t, shp in (("Q", Q, (B, H, Nq, d)), ("K", K, (B, H, Nk, d)), ("V", V, (B, H, Nk, d)),
+                         ("O", O, (B, H, Nq, d)), ("dO", dO, (B, H, Nq, d)),
+                         ("dQ", dQ, (B, H, Nq, d)), ("dK", dK, (B, H, Nk, d)),
+                         ("dV", dV, (B, H, Nk, d))):
+        _check_tensor(name, t, shp, Q.dtype, dev)
+    _check_tensor("L", L, (B, H, Nq), _torch().float32, dev)
+    code = _dtype_code(Q)
+    need = lib.fa_bwd_workspace_size(B, H, Nq, Nk, d, code)
+    if workspace is None:
+        workspace = _alloc_workspace(need, dev)
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    args = (_ptr(Q), _ptr(K), _ptr(V), _ptr(O), _ptr(L), _ptr(dO), _ptr(dQ), _ptr(dK), _ptr(dV),
+            B, H, Nq, Nk, d, float(scale), int(bool(causal)), code, _ptr(workspace), ws_bytes,
+            _stream_handle(dev, stream))
+    if stages == FA_BWD_ALL:
+        st = lib.fa_bwd(*args)
+    else:
+        st = lib.fa_bwd_stages(*args, int(stages))
+    if st != FA_OK:
+        raise FAError(st, "fa_bwd")
+    return dQ, dK, dV
+
+
+def forward(Q, K, V, scale=None, causal=False, num_splits=0, stream=None):
+    """Allocate O, L and run ``fa_fwd``.  Returns (O, L)."""
+    torch = _torch()
+    B, H, Nq, d = Q.shape
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    O = torch.empty_like(Q)
+    L = torch.empty((B, H, Nq), dtype=torch.float32, device=Q.device)
+    return fa_fwd(Q, K, V, O, L, scale, causal, num_splits=num_splits, stream=stream)
+
+
+def backward(Q, K, V, O, L, dO, scale=None, causal=False, stream=None):
+    """Allocate dQ, dK, dV and run ``fa_bwd``.  Returns (dQ, dK, dV)."""
+    torch = _torch()
+    d = Q.shape[-1]
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    dQ = torch.empty_like(Q)
+    dK = torch.empty_like(K)
+    dV = torch.empty_like(V)
+    return fa_bwd(Q, K, V, O, L, dO, dQ, dK, dV, scale, causal, stream=stream)

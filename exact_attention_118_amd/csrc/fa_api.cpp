@@ -1,0 +1,198 @@
+// libfa C ABI: argument checks, path selection and launches (declared in include/fa.h).
+#include "fa.h"
+
+#include <hip/hip_runtime.h>
+
+#include <climits>
+#include <cmath>
+#include <cstdint>
+
+#include "fa_launch.h"
+
+namespace {
+
+constexpr int kVersion = 1 * 10000 + 0 * 100 + 0;
+constexpr size_t kAlign = 16;
+constexpr size_t kWsAlign = 256;
+constexpr int kSplitTargetBlocks = 2048;  // aim for ~8 workgroups per CU on the split path
+constexpr int kSplitMinKeys = 256;        // do not split below this many keys per chunk
+
+size_t round_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
+
+bool aligned(const void* p) { return (reinterpret_cast<uintptr_t>(p) % kAlign) == 0; }
+
+bool dtype_ok(fa_dtype t) { return t == FA_BF16 || t == FA_FP32; }
+
+// Common shape checks.  Returns FA_OK when the sizes are usable; sets *empty
+// when there is nothing to compute for the forward pass.
+fa_status check_dims(int B, int H, int Nq, int Nk, int d, float scale, int causal, fa_dtype dtype) {
+  if (!dtype_ok(dtype)) return FA_ERR_UNSUPPORTED;
+  if (B < 0 || H < 0 || Nq < 0 || Nk < 0) return FA_ERR_SHAPE;
+  if (d != 64 && d != 128) return FA_ERR_UNSUPPORTED;
+  if (!std::isfinite(scale) || scale < 0.f) return FA_ERR_UNSUPPORTED;
+  const long long bh = (long long)B * H;
+  if (bh > INT_MAX) return FA_ERR_SHAPE;
+  // every workgroup count below is at most bh * ceil(N / 64) and must fit in int
+  const long long nmax = (Nq > Nk ? Nq : Nk);
+  if (bh * ((nmax + 63) / 64) > INT_MAX) return FA_ERR_SHAPE;
+  if (bh > 0 && Nq > 0 && Nk == 0) return FA_ERR_SHAPE;
+  if (causal && Nq > Nk && bh > 0 && Nq > 0) return FA_ERR_SHAPE;
+  return FA_OK;
+}
+
+int auto_splits(int BH, int Nk) {
+  int s = (kSplitTargetBlocks + BH - 1) / BH;
+  const int by_keys = (Nk + kSplitMinKeys - 1) / kSplitMinKeys;
+  if (s > by_keys) s = by_keys;
+  return s < 1 ? 1 : s;
+}
+
+// Effective split count: chunks of ceil(Nk/s) keys, none empty.
+int effective_splits(int Nk, int s) {
+  if (s < 1) s = 1;
+  if (s > Nk) s = Nk;
+  const int chunk = fa::split_chunk(Nk, s);
+  return (Nk + chunk - 1) / chunk;
+}
+
+// 0: tiled path, >0: split path with that many splits, <0: unsupported combination.
+int choose_splits(int B, int H, int Nq, int Nk, fa_dtype dtype, int num_splits) {
+  if (num_splits < 0) return -1;
+  if (Nq == 1 && dtype == FA_BF16) {
+    const int s = num_splits == 0 ? auto_splits(B * H, Nk) : num_splits;
+    return effective_splits(Nk, s);
+  }
+  if (num_splits > 1) return -1;
+  return 0;
+}
+
+struct SplitWs {
+  size_t o_bytes, l_off, total;
+};
+
+SplitWs split_ws(int BH, int d, int splits) {
+  SplitWs w;
+  w.o_bytes = (size_t)splits * BH * d * sizeof(float);
+  w.l_off = round_up(w.o_bytes, kWsAlign);
+  w.total = w.l_off + round_up((size_t)splits * BH * sizeof(float), kWsAlign);
+  return w;
+}
+
+struct BwdWs {
+  size_t d_bytes, acc_off, total;
+};
+
+BwdWs bwd_ws(int BH, int Nq, int d) {
+  BwdWs w;
+  w.d_bytes = (size_t)BH * Nq * sizeof(float);
+  w.acc_off = round_up(w.d_bytes, kWsAlign);
+  w.total = w.acc_off + round_up((size_t)BH * Nq * d * sizeof(float), kWsAlign);
+  return w;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* fa_status_string(fa_status s) {
+  switch (s) {
+    case FA_OK: return "FA_OK";
+    case FA_ERR_NULL: return "FA_ERR_NULL: a required pointer is NULL";
+    case FA_ERR_SHAPE: return "FA_ERR_SHAPE: invalid or inconsistent sizes";
+    case FA_ERR_UNSUPPORTED: return "FA_ERR_UNSUPPORTED: dtype, head dim, scale or option not supported";
+    case FA_ERR_ALIGN: return "FA_ERR_ALIGN: a pointer is not 16-byte aligned";
+    case FA_ERR_WORKSPACE: return "FA_ERR_WORKSPACE: workspace missing or too small";
+    case FA_ERR_HIP: return "FA_ERR_HIP: kernel launch failed";
+  }
+  return "unknown fa_status";
+}
+
+int fa_version(void) { return kVersion; }
+
+int fa_fwd_num_splits(int B, int H, int Nq, int Nk, int d, fa_dtype dtype, int num_splits) {
+  if (check_dims(B, H, Nq, Nk, d, 1.f, 0, dtype) != FA_OK) return 0;
+  if ((long long)B * H * Nq == 0) return 0;
+  const int s = choose_splits(B, H, Nq, Nk, dtype, num_splits);
+  return s > 0 ? s : (s == 0 ? 1 : 0);
+}
+
+size_t fa_fwd_workspace_size(int B, int H, int Nq, int Nk, int d, fa_dtype dtype, int num_splits) {
+  if (check_dims(B, H, Nq, Nk, d, 1.f, 0, dtype) != FA_OK) return 0;
+  if ((long long)B * H * Nq == 0) return 0;
+  const int s = choose_splits(B, H, Nq, Nk, dtype, num_splits);
+  if (s <= 0) return 0;
+  return split_ws(B * H, d, s).total;
+}
+
+size_t fa_bwd_workspace_size(int B, int H, int Nq, int Nk, int d, fa_dtype dtype) {
+  if (check_dims(B, H, Nq, Nk, d, 1.f, 0, dtype) != FA_OK) return 0;
+  return bwd_ws(B * H, Nq, d).total;
+}
+
+fa_status fa_fwd(const void* Q, const void* K, const void* V, void* O, float* L, int B, int H,
+                 int Nq, int Nk, int d, float scale, int causal, fa_dtype dtype, int num_splits,
+                 void* workspace, size_t workspace_bytes, void* stream) {
+  fa_status st = check_dims(B, H, Nq, Nk, d, scale, causal, dtype);
+  if (st != FA_OK) return st;
+  if (num_splits < 0) return FA_ERR_UNSUPPORTED;
+  if ((long long)B * H * Nq == 0) return FA_OK;
+  if (!Q || !K || !V || !O || !L) return FA_ERR_NULL;
+  if (!aligned(Q) || !aligned(K) || !aligned(V) || !aligned(O) || !aligned(L)) return FA_ERR_ALIGN;
+  const int splits = choose_splits(B, H, Nq, Nk, dtype, num_splits);
+  if (splits < 0) return FA_ERR_UNSUPPORTED;
+  fa::FwdArgs a{Q, K, V, O, L, B, H, Nq, Nk, d, scale, causal != 0};
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  hipError_t e;
+  if (splits > 0) {
+    const SplitWs w = split_ws(B * H, d, splits);
+    if (!workspace || workspace_bytes < w.total) return FA_ERR_WORKSPACE;
+    if (!aligned(workspace)) return FA_ERR_ALIGN;
+    float* part_o = static_cast<float*>(workspace);
+    float* part_l = reinterpret_cast<float*>(static_cast<char*>(workspace) + w.l_off);
+    a.causal = false;  // one query row sees every key under bottom-right alignment
+    e = fa::launch_fwd_split_bf16(a, splits, part_o, part_l, s);
+  } else if (dtype == FA_BF16) {
+    e = fa::launch_fwd_bf16(a, s);
+  } else {
+    e = fa::launch_fwd_f32(a, s);
+  }
+  return e == hipSuccess ? FA_OK : FA_ERR_HIP;
+}
+
+fa_status fa_bwd(const void* Q, const void* K, const void* V, const void* O, const float* L,
+                 const void* dO, void* dQ, void* dK, void* dV, int B, int H, int Nq, int Nk, int d,
+                 float scale, int causal, fa_dtype dtype, void* workspace, size_t workspace_bytes,
+                 void* stream) {
+  return fa_bwd_stages(Q, K, V, O, L, dO, dQ, dK, dV, B, H, Nq, Nk, d, scale, causal, dtype,
+                       workspace, workspace_bytes, stream, FA_BWD_ALL);
+}
+
+fa_status fa_bwd_stages(const void* Q, const void* K, const void* V, const void* O,
+                        const float* L, const void* dO, void* dQ, void* dK, void* dV, int B,
+                        int H, int Nq, int Nk, int d, float scale, int causal, fa_dtype dtype,
+                        void* workspace, size_t workspace_bytes, void* stream, int stages) {
+  if (stages <= 0 || stages > FA_BWD_ALL) return FA_ERR_UNSUPPORTED;
+  fa_status st = check_dims(B, H, Nq, Nk, d, scale, causal, dtype);
+  if (st != FA_OK) return st;
+  if ((long long)B * H == 0 || (Nq == 0 && Nk == 0)) return FA_OK;
+  if (!K || !V || !dK || !dV) return FA_ERR_NULL;
+  if (Nq > 0 && (!Q || !O || !L || !dO || !dQ)) return FA_ERR_NULL;
+  if (!aligned(K) || !aligned(V) || !aligned(dK) || !aligned(dV)) return FA_ERR_ALIGN;
+  if (Nq > 0 && (!aligned(Q) || !aligned(O) || !aligned(L) || !aligned(dO) || !aligned(dQ)))
+    return FA_ERR_ALIGN;
+  const BwdWs w = bwd_ws(B * H, Nq, d);
+  if (Nq > 0 && (!workspace || workspace_bytes < w.total)) return FA_ERR_WORKSPACE;
+  if (Nq > 0 && !aligned(workspace)) return FA_ERR_ALIGN;
+  fa::BwdArgs a{Q, K, V, O, L, dO, dQ, dK, dV, B, H, Nq, Nk, d, scale, causal != 0, nullptr,
+                nullptr};
+  if (Nq > 0) {
+    a.Dvec = static_cast<float*>(workspace);
+    a.dQacc = reinterpret_cast<float*>(static_cast<char*>(workspace) + w.acc_off);
+  }
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  const hipError_t e =
+      (dtype == FA_BF16) ? fa::launch_bwd_bf16(a, stages, s) : fa::launch_bwd_f32(a, stages, s);
+  return e == hipSuccess ? FA_OK : FA_ERR_HIP;
+}
+
+}  // extern "C"

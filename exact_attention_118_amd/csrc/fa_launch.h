@@ -1,0 +1,56 @@
+// Host-side launchers of the libfa kernels (internal to the library).
+// Each returns the hipError_t of its launch(es); shapes are validated by the
+// caller (fa_api.cpp) before any of these is called.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+
+namespace fa {
+
+struct FwdArgs {
+  const void* Q;
+  const void* K;
+  const void* V;
+  void* O;
+  float* L;
+  int B, H, Nq, Nk, d;
+  float scale;
+  bool causal;
+};
+
+struct BwdArgs {
+  const void* Q;
+  const void* K;
+  const void* V;
+  const void* O;
+  const float* L;
+  const void* dO;
+  void* dQ;
+  void* dK;
+  void* dV;
+  int B, H, Nq, Nk, d;
+  float scale;
+  bool causal;
+  float* Dvec;   // [B*H*Nq] fp32 scratch (workspace)
+  float* dQacc;  // [B*H*Nq*d] fp32 scratch (workspace)
+};
+
+// Tiled forward (Q-tile per workgroup, K/V streamed through LDS).
+hipError_t launch_fwd_bf16(const FwdArgs& a, hipStream_t s);
+hipError_t launch_fwd_f32(const FwdArgs& a, hipStream_t s);
+
+// Split-key forward for one query row per head, then the logsumexp combine.
+// part_o: [splits, B*H, d] fp32, part_l: [splits, B*H] fp32.
+hipError_t launch_fwd_split_bf16(const FwdArgs& a, int splits, float* part_o, float* part_l,
+                                 hipStream_t s);
+
+// Backward: D = rowsum(dO*O) and clearing dQacc; dK/dV (+ dQ atomics); dQ conversion.
+// `stages`: bit 1 preprocess, bit 2 main kernel(s), bit 4 dQ conversion.
+hipError_t launch_bwd_bf16(const BwdArgs& a, int stages, hipStream_t s);
+hipError_t launch_bwd_f32(const BwdArgs& a, int stages, hipStream_t s);
+
+// Key-chunk length used by the split path for `splits` chunks of Nk keys.
+int split_chunk(int Nk, int splits);
+
+}  // namespace fa

@@ -1,0 +1,135 @@
+/*
+ * libfa -- fused scaled-dot-product attention for AMD Instinct MI355X (gfx950).
+ *
+ * The operation (FlashAttention, as described on the pages this library is
+ * built from):
+ *
+ *   S = scale * Q K^T  (+ causal mask),   P = softmax(S) row-wise,   O = P V
+ *
+ * page 1 ("Flash Attention1", section "Flash Attention": the three-line
+ * formula and the blockwise running-max / running-sum softmax); page 2
+ * (FlashAttention V1 vs V2 notes, section "FlashAttention V2 相比V1有哪些改进":
+ * the forward pass keeps only the row logsumexp L for the backward pass, and
+ * causal masking skips the blocks above the diagonal).
+ *
+ * Conventions shared by every entry point
+ * ---------------------------------------
+ *  - Tensors are contiguous row-major [B, H, N, d] with d fastest.  Q, O, dO,
+ *    dQ are [B, H, Nq, d]; K, V, dK, dV are [B, H, Nk, d].  L is [B, H, Nq]
+ *    float32.  Element type of Q, K, V, O, dO, dQ, dK, dV is `dtype`.
+ *  - Causal masking keeps key j for query row i iff j <= i + (Nk - Nq)
+ *    (bottom-right alignment; the usual lower triangle when Nq == Nk).
+ *  - L is the natural-log logsumexp of the scaled, masked score row.
+ *  - All pointers are DEVICE pointers on the current HIP device, 16-byte
+ *    aligned.  The caller owns every buffer; the library never allocates,
+ *    frees or synchronises.  Work is enqueued on `stream` (a hipStream_t; NULL
+ *    means the default stream) and is asynchronous.
+ *  - Arguments are checked before anything is enqueued; on any error status
+ *    nothing is launched and no buffer is written.  FA_ERR_HIP reports a
+ *    failed launch (hipGetLastError).  Faults inside a kernel surface at the
+ *    caller's next synchronisation, as for any HIP kernel.
+ *  - An empty problem (B*H*Nq == 0) returns FA_OK and launches nothing.
+ *  - Supported: dtype FA_BF16 with d in {64, 128} for every entry point;
+ *    dtype FA_FP32 with d in {64, 128} for fa_fwd (non-split) and fa_bwd.
+ *  - Thread safety: no global mutable state; concurrent calls on different
+ *    streams with disjoint buffers are safe.
+ */
+#ifndef FA_H_
+#define FA_H_
+
+#include <stddef.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum fa_status {
+  FA_OK = 0,
+  FA_ERR_NULL = 1,        /* a required pointer is NULL */
+  FA_ERR_SHAPE = 2,       /* negative size, Nk == 0 with Nq > 0, causal with Nq > Nk, size overflow */
+  FA_ERR_UNSUPPORTED = 3, /* dtype / head dim / option combination not implemented */
+  FA_ERR_ALIGN = 4,       /* a pointer is not 16-byte aligned */
+  FA_ERR_WORKSPACE = 5,   /* workspace missing or smaller than the query function returns */
+  FA_ERR_HIP = 6          /* a kernel launch failed */
+} fa_status;
+
+typedef enum fa_dtype { FA_BF16 = 0, FA_FP32 = 1 } fa_dtype;
+
+/*
+ * Forward pass: O = softmax(scale * Q K^T + mask) V and L = logsumexp of each
+ * scaled, masked score row (page 1, section "Flash Attention"; page 2,
+ * "FlashAttention V2 相比V1有哪些改进").
+ *
+ *  Q [B,H,Nq,d], K and V [B,H,Nk,d] (read); O [B,H,Nq,d] and L [B,H,Nq] fp32
+ *  (written, every element).  scale is the score multiplier (usually
+ *  1/sqrt(d)); causal != 0 applies the mask above.
+ *
+ *  num_splits chooses the key-split ("Flash-Decoding", page 2, last paragraph
+ *  of "Sequence Parallel") path, available for Nq == 1 with FA_BF16:
+ *    0  = automatic (split path for Nq == 1 and bf16, tiled path otherwise),
+ *    1  = tiled path for Nq > 1; for Nq == 1 the split path with one split,
+ *    >1 = split path with that many key chunks (Nq must be 1).
+ *  The split path needs a workspace of fa_fwd_workspace_size() bytes (fp32
+ *  partial outputs and logsumexps); the tiled path needs none (pass NULL, 0).
+ */
+fa_status fa_fwd(const void* Q, const void* K, const void* V, void* O, float* L,
+                 int B, int H, int Nq, int Nk, int d, float scale, int causal,
+                 fa_dtype dtype, int num_splits, void* workspace, size_t workspace_bytes,
+                 void* stream);
+
+/*
+ * Backward pass: dQ, dK, dV of f = sum(dO * O) for the forward above,
+ * recomputing P from Q, K and L instead of storing it (page 3, section 3
+ * "Recomputation"; page 2: only L is kept for the backward pass, and the
+ * backward kernel also takes the per-row auxiliary D = rowsum(dO * O)).
+ *
+ *  Q, K, V, O (from fa_fwd), L (from fa_fwd), dO: read.  dQ [B,H,Nq,d],
+ *  dK, dV [B,H,Nk,d]: overwritten, every element (not accumulated into).
+ *  workspace: fa_bwd_workspace_size() bytes of device memory, holding D
+ *  [B,H,Nq] fp32 and an fp32 dQ accumulator [B,H,Nq,d]; the library clears
+ *  what it needs.  dQ is reduced across key blocks with fp32 atomic adds, so
+ *  its low-order bits may differ between runs; dK and dV are deterministic.
+ */
+fa_status fa_bwd(const void* Q, const void* K, const void* V, const void* O, const float* L,
+                 const void* dO, void* dQ, void* dK, void* dV,
+                 int B, int H, int Nq, int Nk, int d, float scale, int causal,
+                 fa_dtype dtype, void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * The backward pass as its three launches, for callers that schedule or time
+ * them separately.  Same arguments as fa_bwd plus `stages`, a bit mask:
+ *   FA_BWD_PREPROCESS (1): D = rowsum(dO * O) into the workspace and clear the
+ *                          workspace dQ accumulator;
+ *   FA_BWD_MAIN       (2): dK, dV written; dQ contributions added into the
+ *                          workspace accumulator (needs stage 1 first);
+ *   FA_BWD_FINALIZE   (4): dQ = scale * accumulator, converted to dtype.
+ * fa_bwd(...) is fa_bwd_stages(..., FA_BWD_ALL).  Stages must run in order on
+ * one workspace; a mask of 0 or above 7 returns FA_ERR_UNSUPPORTED.
+ */
+enum { FA_BWD_PREPROCESS = 1, FA_BWD_MAIN = 2, FA_BWD_FINALIZE = 4, FA_BWD_ALL = 7 };
+fa_status fa_bwd_stages(const void* Q, const void* K, const void* V, const void* O,
+                        const float* L, const void* dO, void* dQ, void* dK, void* dV,
+                        int B, int H, int Nq, int Nk, int d, float scale, int causal,
+                        fa_dtype dtype, void* workspace, size_t workspace_bytes, void* stream,
+                        int stages);
+
+/* Workspace bytes fa_fwd needs for these arguments (0 when none). */
+size_t fa_fwd_workspace_size(int B, int H, int Nq, int Nk, int d, fa_dtype dtype, int num_splits);
+
+/* Workspace bytes fa_bwd needs for these arguments. */
+size_t fa_bwd_workspace_size(int B, int H, int Nq, int Nk, int d, fa_dtype dtype);
+
+/* Number of key splits fa_fwd uses for these arguments (1 on the tiled path). */
+int fa_fwd_num_splits(int B, int H, int Nq, int Nk, int d, fa_dtype dtype, int num_splits);
+
+/* Static, human-readable name of a status code. */
+const char* fa_status_string(fa_status s);
+
+/* Library version as major*10000 + minor*100 + patch. */
+int fa_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* FA_H_ */

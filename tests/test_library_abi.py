@@ -1,0 +1,161 @@
+"""CPU checks of the C-ABI library: it loads, exports what include/fa.h declares,
+and rejects bad arguments with the documented status codes before launching
+anything (no call below reaches a kernel launch)."""
+
+import ctypes
+import os
+import re
+import subprocess
+
+import pytest
+
+import exact_attention_118_amd as fa
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "fa.h")
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(fa.lib_path()):
+        from exact_attention_118_amd import build
+        build.build()
+    return fa.load_library()
+
+
+def _declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(fa_[a-z0-9_]+)\s*\(", text)))
+
+
+def test_header_declares_the_binding_symbols():
+    assert _declared_functions() == sorted(fa.EXPORTED_SYMBOLS)
+
+
+def test_library_exports_every_declared_symbol(lib):
+    out = subprocess.run(["nm", "-D", "--defined-only", fa.lib_path()], capture_output=True,
+                         text=True, check=True).stdout
+    exported = {line.split()[-1] for line in out.splitlines() if " T " in line}
+    for name in _declared_functions():
+        assert name in exported, name
+        assert hasattr(lib, name)
+
+
+def test_status_strings_and_version(lib):
+    for code in range(7):
+        s = fa.status_string(code)
+        assert s.startswith(["FA_OK", "FA_ERR_NULL", "FA_ERR_SHAPE", "FA_ERR_UNSUPPORTED",
+                             "FA_ERR_ALIGN", "FA_ERR_WORKSPACE", "FA_ERR_HIP"][code])
+    assert "unknown" in fa.status_string(99)
+    assert fa.version() == 10000
+
+
+# Fake device addresses: only ever passed in combinations that validation rejects.
+A = 0x10000  # 16-byte aligned
+MIS = 0x10004
+
+
+def fwd(lib, Q=A, K=A, V=A, O=A, L=A, B=1, H=1, Nq=16, Nk=16, d=64, scale=0.125, causal=0,
+        dtype=fa.FA_BF16, splits=0, ws=None, ws_bytes=0):
+    return lib.fa_fwd(Q, K, V, O, L, B, H, Nq, Nk, d, scale, causal, dtype, splits, ws, ws_bytes, None)
+
+
+def bwd(lib, ptrs=None, B=1, H=1, Nq=16, Nk=16, d=64, scale=0.125, causal=0, dtype=fa.FA_BF16,
+        ws=None, ws_bytes=0):
+    p = [A] * 9 if ptrs is None else ptrs
+    return lib.fa_bwd(*p, B, H, Nq, Nk, d, scale, causal, dtype, ws, ws_bytes, None)
+
+
+def test_fwd_rejects_bad_arguments(lib):
+    assert fwd(lib, Q=None) == fa.FA_ERR_NULL
+    assert fwd(lib, L=None) == fa.FA_ERR_NULL
+    assert fwd(lib, V=MIS) == fa.FA_ERR_ALIGN
+    assert fwd(lib, L=MIS) == fa.FA_ERR_ALIGN
+    assert fwd(lib, Q=None, d=96) == fa.FA_ERR_UNSUPPORTED
+    assert fwd(lib, Q=None, d=0) == fa.FA_ERR_UNSUPPORTED
+    assert fwd(lib, Q=None, dtype=7) == fa.FA_ERR_UNSUPPORTED
+    assert fwd(lib, Q=None, Nq=-1) == fa.FA_ERR_SHAPE
+    assert fwd(lib, Q=None, B=-2) == fa.FA_ERR_SHAPE
+    assert fwd(lib, Q=None, Nk=0) == fa.FA_ERR_SHAPE
+    assert fwd(lib, Q=None, Nq=20, Nk=16, causal=1) == fa.FA_ERR_SHAPE
+    assert fwd(lib, Q=None, scale=-1.0) == fa.FA_ERR_UNSUPPORTED
+    assert fwd(lib, Q=None, scale=float("nan")) == fa.FA_ERR_UNSUPPORTED
+    assert fwd(lib, Q=None, scale=float("inf")) == fa.FA_ERR_UNSUPPORTED
+    assert fwd(lib, Q=None, B=1 << 20, H=1 << 12) == fa.FA_ERR_SHAPE
+    # key splits need a single query row (bf16); fp32 never splits
+    assert fwd(lib, splits=2) == fa.FA_ERR_UNSUPPORTED
+    assert fwd(lib, splits=-1) == fa.FA_ERR_UNSUPPORTED
+    assert fwd(lib, Nq=1, dtype=fa.FA_FP32, splits=3) == fa.FA_ERR_UNSUPPORTED
+    # the split path needs its workspace
+    assert fwd(lib, Nq=1, Nk=4096) == fa.FA_ERR_WORKSPACE
+    need = lib.fa_fwd_workspace_size(1, 1, 1, 4096, 64, fa.FA_BF16, 0)
+    assert need > 0
+    assert fwd(lib, Nq=1, Nk=4096, ws=A, ws_bytes=need - 1) == fa.FA_ERR_WORKSPACE
+    assert fwd(lib, Nq=1, Nk=4096, ws=MIS, ws_bytes=need) == fa.FA_ERR_ALIGN
+
+
+def test_empty_problems_return_ok_without_launching(lib):
+    assert fwd(lib, Q=None, K=None, V=None, O=None, L=None, B=0) == fa.FA_OK
+    assert fwd(lib, Q=None, K=None, V=None, O=None, L=None, Nq=0) == fa.FA_OK
+    assert bwd(lib, ptrs=[None] * 9, H=0) == fa.FA_OK
+    assert bwd(lib, ptrs=[None] * 9, Nq=0, Nk=0) == fa.FA_OK
+
+
+def test_bwd_rejects_bad_arguments(lib):
+    need = lib.fa_bwd_workspace_size(1, 1, 16, 16, 64, fa.FA_BF16)
+    for i in range(9):
+        p = [A] * 9
+        p[i] = None
+        assert bwd(lib, ptrs=p, ws=A, ws_bytes=need) == fa.FA_ERR_NULL, i
+        p[i] = MIS
+        assert bwd(lib, ptrs=p, ws=A, ws_bytes=need) == fa.FA_ERR_ALIGN, i
+    assert bwd(lib) == fa.FA_ERR_WORKSPACE
+    assert bwd(lib, ws=A, ws_bytes=need - 4) == fa.FA_ERR_WORKSPACE
+    assert bwd(lib, ws=MIS, ws_bytes=need) == fa.FA_ERR_ALIGN
+    assert bwd(lib, d=80) == fa.FA_ERR_UNSUPPORTED
+    assert bwd(lib, Nq=17, Nk=16, causal=1) == fa.FA_ERR_SHAPE
+    assert bwd(lib, Nq=4, Nk=0) == fa.FA_ERR_SHAPE
+    assert bwd(lib, scale=-0.5) == fa.FA_ERR_UNSUPPORTED
+    for bad in (0, 8, -1):
+        assert lib.fa_bwd_stages(*([A] * 9), 1, 1, 16, 16, 64, 0.125, 0, fa.FA_BF16, A, need, None,
+                                 bad) == fa.FA_ERR_UNSUPPORTED
+    assert lib.fa_bwd_stages(*([A] * 9), 1, 1, 16, 16, 64, 0.125, 0, fa.FA_BF16, None, 0, None,
+                             fa.FA_BWD_MAIN) == fa.FA_ERR_WORKSPACE
+
+
+def test_workspace_queries(lib):
+    B, H, N, d = 2, 3, 100, 128
+    # backward: D [B,H,N] fp32 then the fp32 dQ accumulator, each padded to 256 bytes
+    def up(x):
+        return (x + 255) // 256 * 256
+    assert lib.fa_bwd_workspace_size(B, H, N, N, d, fa.FA_BF16) == up(B * H * N * 4) + up(B * H * N * d * 4)
+    # tiled forward needs none; the split path holds per-split outputs and logsumexps
+    assert lib.fa_fwd_workspace_size(B, H, N, N, d, fa.FA_BF16, 0) == 0
+    assert lib.fa_fwd_num_splits(B, H, N, N, d, fa.FA_BF16, 0) == 1
+    s = lib.fa_fwd_num_splits(16, 32, 1, 16384, 128, fa.FA_BF16, 0)
+    assert s > 1
+    assert lib.fa_fwd_workspace_size(16, 32, 1, 16384, 128, fa.FA_BF16, 0) == \
+        up(s * 512 * 128 * 4) + up(s * 512 * 4)
+    # forced split counts never leave an empty chunk
+    assert lib.fa_fwd_num_splits(1, 1, 1, 4, 64, fa.FA_BF16, 3) == 2
+    assert lib.fa_fwd_num_splits(1, 1, 1, 1000, 64, fa.FA_BF16, 3) == 3
+    assert lib.fa_fwd_num_splits(1, 1, 1, 10, 64, fa.FA_BF16, 50) == 10
+    assert lib.fa_fwd_num_splits(1, 1, 1, 10, 64, fa.FA_FP32, 0) == 1
+
+
+def test_binding_fails_loudly_without_the_library(monkeypatch, tmp_path):
+    monkeypatch.setattr(fa, "_LIB", None)
+    monkeypatch.setattr(fa, "lib_path", lambda: str(tmp_path / "missing.so"))
+    with pytest.raises(RuntimeError, match="missing"):
+        fa.load_library()
+
+
+def test_product_code_does_not_touch_the_oracle():
+    pkg = os.path.join(ROOT, "exact_attention_118_amd")
+    for dirpath, _, files in os.walk(pkg):
+        for f in files:
+            if f.endswith((".py", ".hip", ".cpp", ".h")):
+                text = open(os.path.join(dirpath, f), encoding="utf-8").read()
+                assert not re.search(r"^\s*(import|from)\s+oracle\b", text, re.M), f
+                assert "import_module(\"oracle" not in text, f
