@@ -123,9 +123,12 @@ def main():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--workload", default="b1h32n8192d128_causal")
-    ap.add_argument("--cpu-heads", type=int, default=2,
+    ap.add_argument("--cpu-heads", type=int, default=16,
                     help="heads of the workload the float64 oracle is timed on (0 = skip)")
     ap.add_argument("--no-decode", action="store_true", help="skip the decode-shaped forward")
+    ap.add_argument("--copy-calibration-mib", type=int, default=0,
+                    help="after the timed steps, run one plain device-to-device copy of this many "
+                         "MiB (reference point for HBM byte counters under rocprofv3 --pmc)")
     args = ap.parse_args()
 
     if args.gpus != 1:
@@ -235,6 +238,15 @@ def main():
                 "preprocess_ms": pre_ms, "main_ms": main_ms, "finalize_ms": fin_ms},
     }
     del dQ, dK, dV, ws
+    if args.copy_calibration_mib > 0:
+        n = args.copy_calibration_mib << 20
+        src = torch.ones(n // 4, dtype=torch.float32, device="cuda")
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        torch.mul(src, 1.0, out=dst)  # one elementwise kernel: reads n bytes, writes n bytes
+        torch.cuda.synchronize()
+        log(f"copy calibration: {n} bytes read, {n} bytes written")
+        del src, dst
     if not args.no_decode:
         log("decode-shaped forward")
         out["decode"] = bench_decode(fa, torch, steps=10)

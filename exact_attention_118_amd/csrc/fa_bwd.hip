@@ -1,27 +1,27 @@
 // Backward pass kernels: dQ, dK, dV of f = sum(dO * O).
 //
 // Method: FlashAttention's backward pass recomputes the probabilities from
-// Q, K and the forward logsumexp L instead of storing them (page 3, section 3
-// "Recomputation"; page 2: the backward pass needs only L, and takes the
+// Q, K and the forward logsumexp L instead of storing them (the Huawei Cloud post "FlashAttention", section 3
+// "Recomputation"; the 51CTO FlashAttention V1/V2 notes: the backward pass needs only L, and takes the
 // per-row auxiliary D, which the softmax Jacobian fixes as D = rowsum(dO * O)).
-// Five GEMMs per (key block, query block) pair (page 2, "FlashAttention V2
+// Five GEMMs per (key block, query block) pair (the 51CTO FlashAttention V1/V2 notes, "FlashAttention V2
 // 相比V1有哪些改进": fwd 2 GEMMs, bwd 5):
 //     S = Q K^T            P  = exp(S * scale - L)
 //     dP = dO V^T          dS = P * (dP - D)
 //     dV += P^T dO         dK += scale * dS^T Q         dQ += scale * dS K
-// The grid is parallel over key blocks ("N 方向并行，竖着切", page 2 "Thread
-// Block Level 并行"); each workgroup keeps its dK and dV block on chip and
+// The grid is parallel over key blocks (the 51CTO FlashAttention V1/V2 notes, "Thread
+// Block Level 并行": the backward pass splits the key sequence across blocks); each workgroup keeps its dK and dV block on chip and
 // loops over query blocks.  dQ receives contributions from every key block
 // and is reduced with fp32 global atomic adds into a workspace accumulator
-// (page 2, "Sequence Parallel": bf16 atomics would be a performance disaster,
+// (the 51CTO FlashAttention V1/V2 notes, "Sequence Parallel": bf16 atomics would be a performance disaster,
 // so the accumulator is fp32 and is converted once at the end); consecutive
 // workgroups start their query loop at different blocks so that their atomic
-// adds target different rows at any moment (page 2: place tiles whose
+// adds target different rows at any moment (the 51CTO FlashAttention V1/V2 notes: place tiles whose
 // atomics would collide in different waves).
 //
 // gfx950 mapping (bf16 kernel):
 //  * 256 threads = 4 waves, BC = 128 keys per workgroup, 32 keys per wave:
-//    dK and dV stay wave-private (page 2, "Warp Level 并行", the partition in
+//    dK and dV stay wave-private (the 51CTO FlashAttention V1/V2 notes, "Warp Level 并行", the partition in
 //    which dV, dS and dK need no cross-warp sync and only dQ does).
 //  * Accumulators are laid out with the key index along lanes (S = Q K^T with
 //    the 32x32x16 bf16 MFMA), so P and dS feed dV^T = dO^T P and dK^T = Q^T dS

@@ -1,19 +1,19 @@
 // Forward pass kernels: O = softmax(scale * Q K^T + mask) V, L = row logsumexp.
 //
-// Method: FlashAttention's tiled online softmax (page 1, "Flash Attention1",
+// Method: FlashAttention's tiled online softmax (the CSDN post "Flash Attention1",
 // section "Flash Attention" and its 1 x N walk-through: a running row max and
 // running row sum let each block of keys be folded into the output without
 // ever storing the N x N score matrix), in the loop order of FlashAttention-2
-// (page 2, "Sequence Length 并行" and "Thread Block Level 并行": the Q tile is
+// (the 51CTO FlashAttention V1/V2 notes, "Sequence Length 并行" and "Thread Block Level 并行": the Q tile is
 // the outer, parallel dimension -- one workgroup per Q tile -- and K/V tiles
 // are the inner loop; O stays on chip and is written once).  Normalisation by
 // the row sum is deferred to the epilogue and only L is kept for the backward
-// pass (page 2, "FlashAttention V2 相比V1有哪些改进").  The exponent uses
-// exp2 with scale*log2(e) folded on the host (page 2, "指令级别的优化").
+// pass (the 51CTO FlashAttention V1/V2 notes, "FlashAttention V2 相比V1有哪些改进").  The exponent uses
+// exp2 with scale*log2(e) folded on the host (the 51CTO FlashAttention V1/V2 notes, "指令级别的优化").
 //
 // gfx950 mapping (bf16 kernel):
 //  * 256 threads = 4 waves; the workgroup owns BR = 128 query rows and each
-//    wave owns 32 of them ("sliced-Q", page 2 "Warp Level 并行": all waves
+//    wave owns 32 of them ("sliced-Q", the 51CTO FlashAttention V1/V2 notes "Warp Level 并行": all waves
 //    read the same K/V tile, so no cross-wave reduction is needed).
 //  * Scores are computed transposed, S^T = K Q^T, with the 32x32x16 bf16
 //    MFMA: each lane then holds 16 scores of ONE query row (its lane % 32), so
@@ -24,11 +24,11 @@
 //  * K/V tiles of BC = 64 keys are staged in LDS; the next tile's global
 //    loads are issued before the current tile's math (register prefetch).
 //  * Causal: tiles beyond the diagonal are never loaded, the mask is applied
-//    only on tiles that straddle it (page 2, "FlashAttention V2 相比V1有哪些改进"),
+//    only on tiles that straddle it (the 51CTO FlashAttention V1/V2 notes, "FlashAttention V2 相比V1有哪些改进"),
 //    and a wave whose rows see none of a tile skips its math.
 //  * Grid: one workgroup per (Q tile, batch*head), remapped so each XCD gets a
 //    contiguous range of Q tiles of the same heads (K/V stay in that XCD's L2;
-//    page 2, "Thread Block Level 并行", grid order with the Q tile fastest),
+//    the 51CTO FlashAttention V1/V2 notes, "Thread Block Level 并行", grid order with the Q tile fastest),
 //    causal tiles longest first.
 #include "fa_common.h"
 #include "fa_launch.h"
@@ -155,7 +155,7 @@ __global__ __launch_bounds__(kFwdThreads, 2) void fwd_bf16_kernel(
             if (!vis) sacc[mt][i] = -INFINITY;
           }
       }
-      // Online softmax (page 1 walk-through; deferred normalisation).
+      // Online softmax (the CSDN post "Flash Attention1" walk-through; deferred normalisation).
       float mx = -INFINITY;
 #pragma unroll
       for (int mt = 0; mt < 2; ++mt)

@@ -3,10 +3,10 @@
 //
 // Method: with one query row, the query dimension offers no parallelism, so
 // the keys are split across workgroups and a reduction rescales and sums the
-// partial outputs (page 2, "Sequence Length 并行": Flash-Decoding parallelises
+// partial outputs (the 51CTO FlashAttention V1/V2 notes, "Sequence Length 并行": Flash-Decoding parallelises
 // over the K/V sequence when the query length is 1; and the last paragraph of
 // "Sequence Parallel": partial softmax results are combined by a reduction
-// kernel that rescales them).  Each split runs the online softmax of page 1's
+// kernel that rescales them).  Each split runs the online softmax of the CSDN "Flash Attention1" post's
 // walk-through over its keys and emits its normalised output O_s and
 // logsumexp L_s; the combine forms L = log sum_s exp(L_s) and
 // O = sum_s exp(L_s - L) O_s.

@@ -6,8 +6,8 @@
  *
  *   S = scale * Q K^T  (+ causal mask),   P = softmax(S) row-wise,   O = P V
  *
- * page 1 ("Flash Attention1", section "Flash Attention": the three-line
- * formula and the blockwise running-max / running-sum softmax); page 2
+ * the CSDN post "Flash Attention1" (section "Flash Attention": the three-line
+ * formula and the blockwise running-max / running-sum softmax); the 51CTO FlashAttention V1/V2 notes
  * (FlashAttention V1 vs V2 notes, section "FlashAttention V2 相比V1有哪些改进":
  * the forward pass keeps only the row logsumexp L for the backward pass, and
  * causal masking skips the blocks above the diagonal).
@@ -57,14 +57,14 @@ typedef enum fa_dtype { FA_BF16 = 0, FA_FP32 = 1 } fa_dtype;
 
 /*
  * Forward pass: O = softmax(scale * Q K^T + mask) V and L = logsumexp of each
- * scaled, masked score row (page 1, section "Flash Attention"; page 2,
+ * scaled, masked score row (the CSDN post "Flash Attention1", section "Flash Attention"; the 51CTO FlashAttention V1/V2 notes,
  * "FlashAttention V2 相比V1有哪些改进").
  *
  *  Q [B,H,Nq,d], K and V [B,H,Nk,d] (read); O [B,H,Nq,d] and L [B,H,Nq] fp32
  *  (written, every element).  scale is the score multiplier (usually
  *  1/sqrt(d)); causal != 0 applies the mask above.
  *
- *  num_splits chooses the key-split ("Flash-Decoding", page 2, last paragraph
+ *  num_splits chooses the key-split ("Flash-Decoding", the 51CTO FlashAttention V1/V2 notes, last paragraph
  *  of "Sequence Parallel") path, available for Nq == 1 with FA_BF16:
  *    0  = automatic (split path for Nq == 1 and bf16, tiled path otherwise),
  *    1  = tiled path for Nq > 1; for Nq == 1 the split path with one split,
@@ -79,8 +79,8 @@ fa_status fa_fwd(const void* Q, const void* K, const void* V, void* O, float* L,
 
 /*
  * Backward pass: dQ, dK, dV of f = sum(dO * O) for the forward above,
- * recomputing P from Q, K and L instead of storing it (page 3, section 3
- * "Recomputation"; page 2: only L is kept for the backward pass, and the
+ * recomputing P from Q, K and L instead of storing it (the Huawei Cloud post "FlashAttention", section 3
+ * "Recomputation"; the 51CTO FlashAttention V1/V2 notes: only L is kept for the backward pass, and the
  * backward kernel also takes the per-row auxiliary D = rowsum(dO * O)).
  *
  *  Q, K, V, O (from fa_fwd), L (from fa_fwd), dO: read.  dQ [B,H,Nq,d],

@@ -8,10 +8,10 @@ It computes, in float64 and with the full score matrix S and probability matrix
 P materialised, exactly what the fused kernels compute tile by tile:
 
 * forward  -- O = softmax(scale * Q K^T + mask) V and the per-row natural-log
-  logsumexp L (page 1, "Flash Attention" section, the three-line formula;
-  page 2, "FlashAttention V2 相比 V1 有哪些改进": the backward pass keeps only L);
+  logsumexp L (the CSDN post "Flash Attention1", "Flash Attention" section, the three-line formula;
+  the 51CTO FlashAttention V1/V2 notes, "FlashAttention V2 相比 V1 有哪些改进": the backward pass keeps only L);
 * backward -- dQ, dK, dV of f = sum(dO * O), recomputing P from the inputs
-  (page 3, section 3 "Recomputation"; page 2 names the auxiliary row vector D).
+  (the Huawei Cloud post "FlashAttention", section 3 "Recomputation"; the 51CTO FlashAttention V1/V2 notes names the auxiliary row vector D).
 
 Every function is pinned by CPU tests against facts that do not come from this
 code: hand-derived closed forms (tests/golden), the page-1 online-softmax

@@ -2,17 +2,17 @@
 
 Test infrastructure only (see the package docstring).  Nothing here is blocked,
 fused or reordered: S and P are built in full, as the unfused chain of
-operators the pages contrast FlashAttention with (page 1, "引言/动机": matmul,
+operators the pages contrast FlashAttention with (the CSDN post "Flash Attention1", "引言/动机": matmul,
 scale, mask, softmax, matmul).
 
 Conventions (the readings of the pages that this oracle fixes):
 
-* S = scale * Q K^T.  Page 1 writes S = Q K^T; the scale is the
-  ``sm_scale`` argument of the kernel call printed on page 2 ("Sequence
+* S = scale * Q K^T.  The CSDN post "Flash Attention1" writes S = Q K^T; the scale is the
+  ``sm_scale`` argument of the kernel call printed on the 51CTO FlashAttention V1/V2 notes ("Sequence
   Parallel"), and callers pass 1/sqrt(d).
 * Causal mask: key j is visible to query row i iff j <= i + (Nk - Nq)
   (bottom-right alignment; for Nq == Nk this is the usual lower triangle that
-  page 2 describes when it skips the upper-right blocks).  Masked scores are
+  the 51CTO FlashAttention V1/V2 notes describes when it skips the upper-right blocks).  Masked scores are
   -inf, so they get probability exactly 0.
 * L is the natural-log logsumexp of the scaled, masked score row.
 * All arithmetic is float64 on inputs converted exactly from bf16 or fp32.
@@ -33,7 +33,7 @@ def _as_f64(x) -> np.ndarray:
 def causal_visible(nq: int, nk: int) -> np.ndarray:
     """Boolean [nq, nk] matrix: True where key j is visible to query row i.
 
-    Bottom-right alignment: j <= i + (nk - nq).  Page 2 ("FlashAttention V2 相比
+    Bottom-right alignment: j <= i + (nk - nq).  The 51CTO FlashAttention V1/V2 notes ("FlashAttention V2 相比
     V1 有哪些改进") describes the causal case as skipping the blocks above the
     diagonal; for nq == nk the visible set is j <= i.
     """
@@ -45,7 +45,7 @@ def causal_visible(nq: int, nk: int) -> np.ndarray:
 def scores(Q, K, scale: float, causal: bool) -> np.ndarray:
     """S = scale * Q K^T with -inf at masked positions.  Q [nq, dk], K [nk, dk].
 
-    Page 1, "Flash Attention" section, first line of the formula (S = Q K^T),
+    The CSDN post "Flash Attention1", "Flash Attention" section, first line of the formula (S = Q K^T),
     with the softmax scale applied to the product.
     """
     Q = _as_f64(Q)
@@ -59,7 +59,7 @@ def scores(Q, K, scale: float, causal: bool) -> np.ndarray:
 def softmax_with_lse(S) -> tuple[np.ndarray, np.ndarray]:
     """Row softmax P and natural-log logsumexp L of a score matrix S [nq, nk].
 
-    Safe softmax (page 2, "理解FlashAttention核心逻辑": softmax -> safe
+    Safe softmax (the 51CTO FlashAttention V1/V2 notes, "理解FlashAttention核心逻辑": softmax -> safe
     softmax): subtract the row maximum m before exponentiating, so
     P_ij = exp(S_ij - m_i) / l_i with l_i = sum_j exp(S_ij - m_i), and
     L_i = m_i + ln l_i.  Every row must hold at least one finite score.
@@ -78,7 +78,7 @@ def softmax_with_lse(S) -> tuple[np.ndarray, np.ndarray]:
 def attention_forward(Q, K, V, scale: float, causal: bool):
     """Forward pass for one head: returns (O [nq, dv], L [nq]).
 
-    Page 1, "Flash Attention" section: S = Q K^T, P = softmax(S), O = P V;
+    The CSDN post "Flash Attention1", "Flash Attention" section: S = Q K^T, P = softmax(S), O = P V;
     L as defined in ``softmax_with_lse``.
     """
     S = scores(Q, K, scale, causal)
@@ -109,10 +109,10 @@ def attention_forward_rows(Q, K, V, rows, scale: float, causal: bool):
 def attention_backward(Q, K, V, dO, scale: float, causal: bool, return_aux: bool = False):
     """Gradients of f = sum(dO * O) for one head: returns (dQ, dK, dV).
 
-    P is recomputed from the inputs (page 3, section 3: recomputation in the
+    P is recomputed from the inputs (the Huawei Cloud post "FlashAttention", section 3: recomputation in the
     backward pass instead of storing the N x N intermediates).  The steps are
     the chain rule through O = P V and the row softmax; the pages name the
-    per-row auxiliary D (page 2, the ``D`` argument of the backward kernel
+    per-row auxiliary D (the 51CTO FlashAttention V1/V2 notes, the ``D`` argument of the backward kernel
     call) but do not print its formula, which the softmax Jacobian fixes:
 
         dV = P^T dO

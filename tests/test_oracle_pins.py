@@ -7,11 +7,11 @@ some pin fails for every one of them.
 
 Sources of truth used here:
 * tests/golden/hand_derived_attention.json -- exact closed forms derived by
-  hand from page 1's formula (the pages print no numeric example);
-* page 1's online-softmax walk-through ("例子说明"), re-implemented
+  hand from the CSDN "Flash Attention1" post's formula (the pages print no numeric example);
+* the CSDN "Flash Attention1" post's online-softmax walk-through ("例子说明"), re-implemented
   independently as a running max / running sum recurrence;
 * softmax identities: rows of P sum to 1, invariance under a per-row shift
-  of the scores (page 2, "理解FlashAttention核心逻辑": softmax -> safe softmax);
+  of the scores (the 51CTO FlashAttention V1/V2 notes, "理解FlashAttention核心逻辑": softmax -> safe softmax);
 * central finite differences of f = sum(dO * O);
 * torch's float64 scaled_dot_product_attention and autograd on the CPU.
 """
@@ -79,7 +79,7 @@ def check_golden(fwd, bwd):
 
 
 def walkthrough_row(s, V):
-    """Page 1's 1 x N walk-through, written afresh: one key at a time, keep the
+    """The CSDN "Flash Attention1" post's 1 x N walk-through, written afresh: one key at a time, keep the
     running max and running sum, renormalise the accumulated output by
     old_sum / new_sum at every step (the page's accumulator is normalised at
     each step, not at the end)."""
@@ -203,7 +203,7 @@ def _lse_combine(parts):
 
 def check_split_combine(fwd, bwd):
     """Attention over key chunks, merged by their logsumexps, equals attention
-    over all keys (the Flash-Decoding reduction of page 2, "Sequence
+    over all keys (the Flash-Decoding reduction of the 51CTO FlashAttention V1/V2 notes, "Sequence
     Parallel", final paragraph)."""
     ok = True
     r = _rng(41)
@@ -281,7 +281,7 @@ def test_oracle_pin(check):
 
 
 def test_walkthrough_matches_two_pass_softmax():
-    """Page 1 walk-through (online, normalised per step) equals the two-pass
+    """The CSDN post "Flash Attention1" walk-through (online, normalised per step) equals the two-pass
     softmax followed by the product with V, at N = 4, d = 2 as on the page."""
     r = _rng(5)
     s, V = r.random(4), r.random((4, 2))
