@@ -167,11 +167,11 @@ def main():
         if ev is not None:
             ev[2].record()
         fa.fa_bwd(Q, K, V, O, L, dO, dQ, dK, dV, w.scale, w.causal, workspace=ws,
-                  stages=fa.FA_BWD_MAIN)
+                  stages=fa.FA_BWD_DKDV)
         if ev is not None:
             ev[3].record()
         fa.fa_bwd(Q, K, V, O, L, dO, dQ, dK, dV, w.scale, w.causal, workspace=ws,
-                  stages=fa.FA_BWD_FINALIZE)
+                  stages=fa.FA_BWD_DQ)
         if ev is not None:
             ev[4].record()
 
@@ -196,17 +196,22 @@ def main():
     def mean_ms(a, b):
         return sum(e[a].elapsed_time(e[b]) for e in evs) / len(evs)
 
-    fwd_ms, pre_ms, main_ms, fin_ms = mean_ms(0, 1), mean_ms(1, 2), mean_ms(2, 3), mean_ms(3, 4)
-    bwd_ms = pre_ms + main_ms + fin_ms
+    fwd_ms, pre_ms, dkdv_ms, dq_ms = mean_ms(0, 1), mean_ms(1, 2), mean_ms(2, 3), mean_ms(3, 4)
+    bwd_ms = pre_ms + dkdv_ms + dq_ms
     pairs = unmasked_pairs(w.Nq, w.Nk, w.causal) * w.B * w.H
     fwd_flops, bwd_flops = 4 * w.d * pairs, 10 * w.d * pairs
     value = (fwd_flops + bwd_flops) / (ms_per_step * 1e-3) / 1e12
 
+    # Algorithmic flops per kernel: the forward's 2 GEMMs; the dK/dV kernel's
+    # S, dP, dV and dK GEMMs (8*d per pair); the dQ kernel's dQ GEMM (2*d per
+    # pair) -- its recomputation of S and dP is overhead, not algorithmic work.
+    csrc = os.path.join(ROOT, "exact_attention_118_amd", "csrc")
     kernels = {
-        "fwd_bf16_kernel": {"ms": fwd_ms, "flops": fwd_flops,
-                            "source": os.path.join(ROOT, "exact_attention_118_amd", "csrc", "fa_fwd.hip")},
-        "bwd_dkdv_bf16_kernel": {"ms": main_ms, "flops": bwd_flops,
-                                 "source": os.path.join(ROOT, "exact_attention_118_amd", "csrc", "fa_bwd.hip")},
+        "fwd_bf16_kernel": {"ms": fwd_ms, "flops": fwd_flops, "source": os.path.join(csrc, "fa_fwd.hip")},
+        "bwd_dkdv_bf16_kernel": {"ms": dkdv_ms, "flops": 8 * w.d * pairs,
+                                 "source": os.path.join(csrc, "fa_bwd.hip")},
+        "bwd_dq_bf16_kernel": {"ms": dq_ms, "flops": 2 * w.d * pairs,
+                               "source": os.path.join(csrc, "fa_bwd.hip")},
     }
     dom_name = max(kernels, key=lambda k: kernels[k]["ms"])
     dom = kernels[dom_name]
@@ -235,7 +240,8 @@ def main():
                 "mfma_frac": fwd_flops / (fwd_ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS},
         "bwd": {"ms": bwd_ms, "TFLOP/s": bwd_flops / (bwd_ms * 1e-3) / 1e12,
                 "mfma_frac": bwd_flops / (bwd_ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS,
-                "preprocess_ms": pre_ms, "main_ms": main_ms, "finalize_ms": fin_ms},
+                "preprocess_ms": pre_ms, "dkdv_ms": dkdv_ms, "dq_ms": dq_ms,
+                "executed_mfma_frac": 14 * w.d * pairs / (bwd_ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS},
     }
     del dQ, dK, dV, ws
     if args.copy_calibration_mib > 0:

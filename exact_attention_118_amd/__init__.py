@@ -17,13 +17,13 @@ __all__ = [
     "fwd_workspace_size", "bwd_workspace_size", "fwd_num_splits", "status_string", "version",
     "FA_OK", "FA_ERR_NULL", "FA_ERR_SHAPE", "FA_ERR_UNSUPPORTED", "FA_ERR_ALIGN",
     "FA_ERR_WORKSPACE", "FA_ERR_HIP", "FA_BF16", "FA_FP32", "EXPORTED_SYMBOLS",
-    "FA_BWD_PREPROCESS", "FA_BWD_MAIN", "FA_BWD_FINALIZE", "FA_BWD_ALL",
+    "FA_BWD_PREPROCESS", "FA_BWD_DKDV", "FA_BWD_DQ", "FA_BWD_ALL",
 ]
 
 FA_OK, FA_ERR_NULL, FA_ERR_SHAPE, FA_ERR_UNSUPPORTED, FA_ERR_ALIGN, FA_ERR_WORKSPACE, FA_ERR_HIP = range(7)
 FA_BF16, FA_FP32 = 0, 1
 
-FA_BWD_PREPROCESS, FA_BWD_MAIN, FA_BWD_FINALIZE, FA_BWD_ALL = 1, 2, 4, 7
+FA_BWD_PREPROCESS, FA_BWD_DKDV, FA_BWD_DQ, FA_BWD_ALL = 1, 2, 4, 7
 
 EXPORTED_SYMBOLS = ("fa_fwd", "fa_bwd", "fa_bwd_stages", "fa_fwd_workspace_size",
                     "fa_bwd_workspace_size", "fa_fwd_num_splits", "fa_status_string", "fa_version")

@@ -78,17 +78,8 @@ SplitWs split_ws(int BH, int d, int splits) {
   return w;
 }
 
-struct BwdWs {
-  size_t d_bytes, acc_off, total;
-};
-
-BwdWs bwd_ws(int BH, int Nq, int d) {
-  BwdWs w;
-  w.d_bytes = (size_t)BH * Nq * sizeof(float);
-  w.acc_off = round_up(w.d_bytes, kWsAlign);
-  w.total = w.acc_off + round_up((size_t)BH * Nq * d * sizeof(float), kWsAlign);
-  return w;
-}
+// Backward workspace: D [B*H*Nq] fp32.
+size_t bwd_ws_bytes(int BH, int Nq) { return round_up((size_t)BH * Nq * sizeof(float), kWsAlign); }
 
 }  // namespace
 
@@ -126,7 +117,7 @@ size_t fa_fwd_workspace_size(int B, int H, int Nq, int Nk, int d, fa_dtype dtype
 
 size_t fa_bwd_workspace_size(int B, int H, int Nq, int Nk, int d, fa_dtype dtype) {
   if (check_dims(B, H, Nq, Nk, d, 1.f, 0, dtype) != FA_OK) return 0;
-  return bwd_ws(B * H, Nq, d).total;
+  return bwd_ws_bytes(B * H, Nq);
 }
 
 fa_status fa_fwd(const void* Q, const void* K, const void* V, void* O, float* L, int B, int H,
@@ -180,15 +171,10 @@ fa_status fa_bwd_stages(const void* Q, const void* K, const void* V, const void*
   if (!aligned(K) || !aligned(V) || !aligned(dK) || !aligned(dV)) return FA_ERR_ALIGN;
   if (Nq > 0 && (!aligned(Q) || !aligned(O) || !aligned(L) || !aligned(dO) || !aligned(dQ)))
     return FA_ERR_ALIGN;
-  const BwdWs w = bwd_ws(B * H, Nq, d);
-  if (Nq > 0 && (!workspace || workspace_bytes < w.total)) return FA_ERR_WORKSPACE;
+  if (Nq > 0 && (!workspace || workspace_bytes < bwd_ws_bytes(B * H, Nq))) return FA_ERR_WORKSPACE;
   if (Nq > 0 && !aligned(workspace)) return FA_ERR_ALIGN;
-  fa::BwdArgs a{Q, K, V, O, L, dO, dQ, dK, dV, B, H, Nq, Nk, d, scale, causal != 0, nullptr,
-                nullptr};
-  if (Nq > 0) {
-    a.Dvec = static_cast<float*>(workspace);
-    a.dQacc = reinterpret_cast<float*>(static_cast<char*>(workspace) + w.acc_off);
-  }
+  fa::BwdArgs a{Q, K, V, O, L, dO, dQ, dK, dV, B, H, Nq, Nk, d, scale, causal != 0,
+                Nq > 0 ? static_cast<float*>(workspace) : nullptr};
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
   const hipError_t e =
       (dtype == FA_BF16) ? fa::launch_bwd_bf16(a, stages, s) : fa::launch_bwd_f32(a, stages, s);

@@ -1,37 +1,51 @@
 // Backward pass kernels: dQ, dK, dV of f = sum(dO * O).
 //
-// Method: FlashAttention's backward pass recomputes the probabilities from
-// Q, K and the forward logsumexp L instead of storing them (the Huawei Cloud post "FlashAttention", section 3
-// "Recomputation"; the 51CTO FlashAttention V1/V2 notes: the backward pass needs only L, and takes the
-// per-row auxiliary D, which the softmax Jacobian fixes as D = rowsum(dO * O)).
-// Five GEMMs per (key block, query block) pair (the 51CTO FlashAttention V1/V2 notes, "FlashAttention V2
-// 相比V1有哪些改进": fwd 2 GEMMs, bwd 5):
+// Method: the backward pass recomputes the probabilities from Q, K and the
+// forward logsumexp L instead of storing them (the Huawei Cloud post
+// "FlashAttention", section 3, Recomputation; the 51CTO FlashAttention V1/V2
+// notes, "FlashAttention V2相比V1有哪些改进": the backward pass needs only L).
+// It also takes the per-row auxiliary D, which the notes name and the softmax
+// Jacobian fixes as D = rowsum(dO * O).  Per (query, key) pair:
 //     S = Q K^T            P  = exp(S * scale - L)
 //     dP = dO V^T          dS = P * (dP - D)
 //     dV += P^T dO         dK += scale * dS^T Q         dQ += scale * dS K
-// The grid is parallel over key blocks (the 51CTO FlashAttention V1/V2 notes, "Thread
-// Block Level 并行": the backward pass splits the key sequence across blocks); each workgroup keeps its dK and dV block on chip and
-// loops over query blocks.  dQ receives contributions from every key block
-// and is reduced with fp32 global atomic adds into a workspace accumulator
-// (the 51CTO FlashAttention V1/V2 notes, "Sequence Parallel": bf16 atomics would be a performance disaster,
-// so the accumulator is fp32 and is converted once at the end); consecutive
-// workgroups start their query loop at different blocks so that their atomic
-// adds target different rows at any moment (the 51CTO FlashAttention V1/V2 notes: place tiles whose
-// atomics would collide in different waves).
 //
-// gfx950 mapping (bf16 kernel):
-//  * 256 threads = 4 waves, BC = 128 keys per workgroup, 32 keys per wave:
-//    dK and dV stay wave-private (the 51CTO FlashAttention V1/V2 notes, "Warp Level 并行", the partition in
-//    which dV, dS and dK need no cross-warp sync and only dQ does).
-//  * Accumulators are laid out with the key index along lanes (S = Q K^T with
-//    the 32x32x16 bf16 MFMA), so P and dS feed dV^T = dO^T P and dK^T = Q^T dS
-//    straight from registers; dO^T and Q^T come from the row-major LDS tiles
-//    via the transpose read ds_read_b64_tr_b16.
-//  * dS^T is written once to LDS; dQ = dS K is then split over the waves by
-//    output tile, so the cross-wave reduction happens inside the MFMA k-loop
-//    and each dQ element gets one atomic add per (query block, key block).
-//  * Q, dO, L and D of the next query block are prefetched into registers
-//    while the current block is processed.
+// dK and dV are computed with the grid over key blocks (the notes, "Thread
+// Block Level 并行": the backward pass splits the key sequence across thread
+// blocks), each workgroup keeping its dK and dV block on chip while it loops
+// over query blocks.  dQ needs a sum over every key block.  The notes
+// ("Sequence Parallel") weigh global atomic adds, which are slow, against
+// per-key-block dQ buffers reduced afterwards, whose size grows with N^2 / BC.
+// On MI355X fp32 atomic adds run at about a fifth of the store bandwidth, so
+// this library takes a third route: a second kernel, gridded over query
+// blocks like the forward pass, recomputes S and dP for its rows and
+// accumulates dQ in registers.  That costs two extra GEMMs per pair (seven in
+// all instead of five) but needs no atomics, no fp32 accumulator and no
+// workspace beyond D, and every output is deterministic.
+//
+// gfx950 mapping:
+//  * bwd_dkdv_bf16_kernel: 512 threads = 8 waves, two per SIMD, so one wave's
+//    MFMAs overlap the other's LDS reads, exponentials and barrier waits.  A
+//    workgroup owns BC = 256 keys and each wave 32 of them, so dK and dV stay
+//    wave-private (the notes, "Warp Level 并行": with keys split across warps,
+//    dV, dS and dK need no cross-warp reduction).  Scores are laid out with the
+//    key along lanes (S = Q K^T on the 32x32x16 bf16 MFMA): rounded to bf16,
+//    the fp32 accumulators of P and dS are directly the B operands of
+//    dV^T = dO^T P and dK^T = Q^T dS; dO^T and Q^T come from the row-major LDS
+//    tiles through the transpose read ds_read_b64_tr_b16.  K stays in LDS, the
+//    wave's 32 rows of V in registers; Q, dO, L, D of the next 32-row query
+//    block are loaded into registers while the current one is processed and
+//    are double-buffered in LDS, so one barrier per query block suffices.
+//  * bwd_dq_bf16_kernel: the forward pass's layout.  4 waves own 32 query rows
+//    each (the notes' "sliced-Q": no cross-wave reduction); scores are computed
+//    transposed, S^T = K Q^T and dP^T = V dO^T, so each lane holds one query
+//    row and its L and D are scalars; dS^T feeds dQ^T = K^T dS^T from
+//    registers, with K^T read from the K tile by the transpose read.  K and V
+//    tiles of 64 keys are staged in LDS with a register prefetch of the next.
+//  * Grids: the key-block grid pins heads to XCDs when B*H is a multiple of 8
+//    (a head's workgroups then share one L2 for their re-reads of Q and dO)
+//    and dispatches key blocks in order of decreasing work; the query-block
+//    grid uses the forward pass's mapping.
 #include "fa_common.h"
 #include "fa_launch.h"
 
@@ -39,16 +53,11 @@ namespace fa {
 
 namespace {
 
-constexpr int kBwdBC = 128;  // keys per workgroup
-constexpr int kBwdBR = 64;   // query rows per inner iteration
-constexpr int kBwdThreads = 256;
-
-// D_i = sum_k dO_ik O_ik in fp32, and clear the fp32 dQ accumulator rows.
+// D_i = sum_k dO_ik O_ik in fp32.
 template <int D, typename T>
 __global__ __launch_bounds__(256) void bwd_pre_kernel(const T* __restrict__ O,
                                                       const T* __restrict__ dO,
-                                                      float* __restrict__ Dvec,
-                                                      float* __restrict__ dQacc, long rows) {
+                                                      float* __restrict__ Dvec, long rows) {
   constexpr int TPR = D / 8;  // threads per row, 8 elements each
   constexpr int RPB = 256 / TPR;
   const long row = (long)blockIdx.x * RPB + threadIdx.x / TPR;
@@ -58,68 +67,73 @@ __global__ __launch_bounds__(256) void bwd_pre_kernel(const T* __restrict__ O,
     const size_t base = (size_t)row * D + part * 8;
 #pragma unroll
     for (int e = 0; e < 8; ++e) acc = fmaf((float)O[base + e], (float)dO[base + e], acc);
-    float4* z = (float4*)(dQacc + base);
-    z[0] = make_float4(0.f, 0.f, 0.f, 0.f);
-    z[1] = make_float4(0.f, 0.f, 0.f, 0.f);
   }
 #pragma unroll
   for (int msk = TPR / 2; msk >= 1; msk >>= 1) acc += __shfl_xor(acc, msk, 64);
   if (row < rows && part == 0) Dvec[row] = acc;
 }
 
+// ---------------------------------------------------------------------------
+// dK and dV: one workgroup per (key block of 256, batch*head).
+constexpr int kKvBC = 256;  // keys per workgroup
+constexpr int kKvBR = 32;   // query rows per inner iteration
+constexpr int kKvWaves = 8;
+constexpr int kKvThreads = kKvWaves * 64;
+
 template <int D, bool CAUSAL>
-__global__ __launch_bounds__(kBwdThreads, 1) void bwd_dkdv_bf16_kernel(
+__global__ __launch_bounds__(kKvThreads, 1) void bwd_dkdv_bf16_kernel(
     const bf16* __restrict__ Q, const bf16* __restrict__ K, const bf16* __restrict__ V,
     const float* __restrict__ L, const bf16* __restrict__ dO, const float* __restrict__ Dvec,
-    float* __restrict__ dQacc, bf16* __restrict__ dK, bf16* __restrict__ dV, int Nq, int Nk,
-    int nkt, float c, float scale, int off) {
-  constexpr int BC = kBwdBC, BR = kBwdBR;
-  constexpr int TSTR = D + 16;    // LDS pitch of K, Q, dO tiles (elements)
-  constexpr int SSTR = BR + 16;   // LDS pitch of the dS^T tile (elements)
-  constexpr int CPR = D / 8;
-  constexpr int NLQ = BR * CPR / kBwdThreads;  // 16-byte loads per thread per Q-block tensor
-  constexpr int NKK = D / 16;
-  constexpr int NNT = D / 32;
-  constexpr int NQT_W = NNT / 2;  // dQ output tiles (over d) per wave
-  static_assert(NLQ * kBwdThreads == BR * CPR, "tile load must divide evenly");
+    bf16* __restrict__ dK, bf16* __restrict__ dV, int Nq, int Nk, int nkt, int BH, int hpx,
+    float c, float scale, int off) {
+  constexpr int BC = kKvBC, BR = kKvBR;
+  constexpr int KSTR = D + 8;     // LDS pitch of the K block (elements)
+  constexpr int QSTR = D + 16;    // LDS pitch of the Q and dO tiles
+  constexpr int CPR = D / 8;      // 16-byte chunks per row
+  constexpr int NKK = D / 16;     // MFMA k-steps over the head dim
+  constexpr int NNT = D / 32;     // 32-wide tiles over the head dim
+  constexpr int NQL = 2 * BR * CPR / kKvThreads;  // 16-byte loads per thread per query block
+  static_assert(NQL * kKvThreads == 2 * BR * CPR, "query block load must divide evenly");
 
-  __shared__ __attribute__((aligned(16))) bf16 sK[BC * TSTR];
-  __shared__ __attribute__((aligned(16))) bf16 sQ[BR * TSTR];
-  __shared__ __attribute__((aligned(16))) bf16 sdO[BR * TSTR];
-  __shared__ __attribute__((aligned(16))) bf16 sdS[BC * SSTR];
-  __shared__ __attribute__((aligned(16))) float sL2[BR];
-  __shared__ __attribute__((aligned(16))) float sD[BR];
+  __shared__ __attribute__((aligned(16))) bf16 sK[BC * KSTR];
+  __shared__ __attribute__((aligned(16))) bf16 sQ[2][BR * QSTR];
+  __shared__ __attribute__((aligned(16))) bf16 sdO[2][BR * QSTR];
+  __shared__ __attribute__((aligned(16))) float sL2[2][BR];
+  __shared__ __attribute__((aligned(16))) float sD[2][BR];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63, wave = tid >> 6;
   const int half = lane >> 5, l32 = lane & 31;
   const int g = lane >> 4, s16 = lane & 15;
 
-  const int logical = xcd_remap(blockIdx.x, gridDim.x);
-  const int bh = logical / nkt;
-  const int kt = logical - bh * nkt;
+  int bh, kt;
+  if (hpx > 0) {  // B*H = 8 * hpx: head bh runs on XCD bh % 8
+    const int x = blockIdx.x % kNumXcd, slot = blockIdx.x / kNumXcd;
+    bh = x + kNumXcd * (slot % hpx);
+    kt = slot / hpx;
+  } else {
+    kt = blockIdx.x / BH;
+    bh = blockIdx.x - kt * BH;
+  }
   const int k0 = kt * BC;
   const int kw0 = k0 + wave * 32;  // this wave's first key
+  const int mykey = kw0 + l32;     // the key of this lane's accumulator column
   const size_t qbase = (size_t)bh * Nq * D;
   const size_t kbase = (size_t)bh * Nk * D;
   const size_t lbase = (size_t)bh * Nq;
 
-  // Stage the K block in LDS (for the dQ GEMM) and keep this wave's K and V
-  // rows in registers (B operands of S = Q K^T and dP = dO V^T).
-  for (int idx = tid; idx < BC * CPR; idx += kBwdThreads) {
+  // K block -> LDS; this wave's V rows -> registers (B operand of dP = dO V^T).
+  for (int idx = tid; idx < BC * CPR; idx += kKvThreads) {
     const int r = idx / CPR, ch = idx - r * CPR;
     const int key = k0 + r;
-    *(bf16x8*)(sK + r * TSTR + ch * 8) =
+    *(bf16x8*)(sK + r * KSTR + ch * 8) =
         (key < Nk) ? *(const bf16x8*)(K + kbase + (size_t)key * D + ch * 8) : zero_bf16x8();
   }
-  const int mykey = kw0 + l32;
-  bf16x8 kf[NKK], vf[NKK];
+  bf16x8 vf[NKK];
 #pragma unroll
-  for (int kk = 0; kk < NKK; ++kk) {
-    const size_t o = kbase + (size_t)mykey * D + kk * 16 + half * 8;
-    kf[kk] = (mykey < Nk) ? *(const bf16x8*)(K + o) : zero_bf16x8();
-    vf[kk] = (mykey < Nk) ? *(const bf16x8*)(V + o) : zero_bf16x8();
-  }
+  for (int kk = 0; kk < NKK; ++kk)
+    vf[kk] = (mykey < Nk) ? *(const bf16x8*)(V + kbase + (size_t)mykey * D + kk * 16 + half * 8)
+                          : zero_bf16x8();
 
   f32x16 dkacc[NNT], dvacc[NNT];
 #pragma unroll
@@ -128,182 +142,119 @@ __global__ __launch_bounds__(kBwdThreads, 1) void bwd_dkdv_bf16_kernel(
     dvacc[nt] = (f32x16){};
   }
 
-  // Query blocks that can see any of this workgroup's keys.
+  // Query blocks that can see any key of this workgroup.
   const int nqb = (Nq + BR - 1) / BR;
   const int qb_first = CAUSAL ? max(0, k0 - off) / BR : 0;
   const int nloop = nqb - qb_first;
-  // Stagger the start so concurrent workgroups of one head add into different dQ rows.
-  const int rot = CAUSAL ? 0 : (nloop > 0 ? kt % nloop : 0);
 
-  bf16x8 qreg[NLQ], doreg[NLQ];
-  float lreg = 0.f;
+  bf16x8 stage[NQL];
+  float lstage = 0.f;
   auto gload = [&](int qb) {
     const int qi0 = qb * BR;
 #pragma unroll
-    for (int u = 0; u < NLQ; ++u) {
-      const int idx = tid + u * kBwdThreads;
-      const int r = idx / CPR, ch = idx - r * CPR;
+    for (int u = 0; u < NQL; ++u) {
+      const int idx = tid + u * kKvThreads;
+      const int tsel = idx / (BR * CPR);  // 0: Q, 1: dO (uniform per wave)
+      const int rem = idx - tsel * (BR * CPR);
+      const int r = rem / CPR, ch = rem - r * CPR;
       const int q = qi0 + r;
-      if (q < Nq) {
-        qreg[u] = *(const bf16x8*)(Q + qbase + (size_t)q * D + ch * 8);
-        doreg[u] = *(const bf16x8*)(dO + qbase + (size_t)q * D + ch * 8);
-      } else {
-        qreg[u] = zero_bf16x8();
-        doreg[u] = zero_bf16x8();
-      }
+      const bf16* src = tsel ? dO : Q;
+      stage[u] = (q < Nq) ? *(const bf16x8*)(src + qbase + (size_t)q * D + ch * 8) : zero_bf16x8();
     }
     if (tid < 2 * BR) {
       const int q = qi0 + (tid & (BR - 1));
-      if (tid < BR) lreg = (q < Nq) ? L[lbase + q] * kLog2e : INFINITY;
-      else lreg = (q < Nq) ? Dvec[lbase + q] : 0.f;
+      if (tid < BR) lstage = (q < Nq) ? L[lbase + q] * kLog2e : INFINITY;
+      else lstage = (q < Nq) ? Dvec[lbase + q] : 0.f;
     }
   };
-  auto sstore = [&]() {
+  auto sstore = [&](int buf) {
 #pragma unroll
-    for (int u = 0; u < NLQ; ++u) {
-      const int idx = tid + u * kBwdThreads;
-      const int r = idx / CPR, ch = idx - r * CPR;
-      *(bf16x8*)(sQ + r * TSTR + ch * 8) = qreg[u];
-      *(bf16x8*)(sdO + r * TSTR + ch * 8) = doreg[u];
+    for (int u = 0; u < NQL; ++u) {
+      const int idx = tid + u * kKvThreads;
+      const int tsel = idx / (BR * CPR);
+      const int rem = idx - tsel * (BR * CPR);
+      const int r = rem / CPR, ch = rem - r * CPR;
+      bf16* dst = tsel ? sdO[buf] : sQ[buf];
+      *(bf16x8*)(dst + r * QSTR + ch * 8) = stage[u];
     }
-    if (tid < BR) sL2[tid] = lreg;
-    else if (tid < 2 * BR) sD[tid - BR] = lreg;
+    if (tid < BR) sL2[buf][tid] = lstage;
+    else if (tid < 2 * BR) sD[buf][tid - BR] = lstage;
   };
 
   if (nloop > 0) {
-    gload(qb_first + rot);
-    sstore();
+    gload(qb_first);
+    sstore(0);
   }
   __syncthreads();
 
-  // Lane-constant parts of the transpose-read addresses.
-  const int tr_row = (g >> 1) * 4 + (s16 >> 2);     // row within a 16-row chunk (+8 for hi)
-  const int tr_col = (g & 1) * 16 + (s16 & 3) * 4;  // column within a 32-wide tile
-  // dQ tiles of this wave: query rows [mq*32, mq*32+32), d columns nt0*32 ...
-  const int mq = wave & 1;
-  const int nt0 = (wave >> 1) * NQT_W;
+  // Lane-constant parts of the transpose-read addresses (see lds_read_tr).
+  const int tr_row = (g >> 1) * 4 + (s16 >> 2);
+  const int tr_col = (g & 1) * 16 + (s16 & 3) * 4;
 
   for (int it = 0; it < nloop; ++it) {
-    const int qb = qb_first + (it + rot) % nloop;
-    const int qi0 = qb * BR;
-    if (it + 1 < nloop) gload(qb_first + (it + 1 + rot) % nloop);
+    const int buf = it & 1;
+    const int qi0 = (qb_first + it) * BR;
+    if (it + 1 < nloop) gload(qb_first + it + 1);
 
-    const bool wave_idle = CAUSAL && (qi0 + BR - 1 + off < kw0);
-    bf16x8 dsf[4];
+    const bf16* tQ = sQ[buf];
+    const bf16* tdO = sdO[buf];
+    // Causal: a wave whose keys all lie after every row of the block has no work.
+    const bool wave_idle = CAUSAL && (kw0 > qi0 + BR - 1 + off);
     if (!wave_idle) {
-      // S = Q K^T and dP = dO V^T for 64 query rows x this wave's 32 keys.
-      f32x16 sacc[2], dpacc[2];
+      // S = Q K^T and dP = dO V^T: 32 rows x this wave's 32 keys.
+      f32x16 sacc = (f32x16){}, dpacc = (f32x16){};
+      const bf16* qrow = tQ + l32 * QSTR + half * 8;
+      const bf16* dorow = tdO + l32 * QSTR + half * 8;
+      const bf16* krow = sK + (wave * 32 + l32) * KSTR + half * 8;
 #pragma unroll
-      for (int mt = 0; mt < 2; ++mt) {
-        sacc[mt] = (f32x16){};
-        dpacc[mt] = (f32x16){};
-        const bf16* qrow = sQ + (mt * 32 + l32) * TSTR + half * 8;
-        const bf16* dorow = sdO + (mt * 32 + l32) * TSTR + half * 8;
+      for (int kk = 0; kk < NKK; ++kk) {
+        sacc = mfma32(*(const bf16x8*)(qrow + kk * 16), *(const bf16x8*)(krow + kk * 16), sacc);
+        dpacc = mfma32(*(const bf16x8*)(dorow + kk * 16), vf[kk], dpacc);
+      }
+      const bool need_mask =
+          (qi0 + BR > Nq) || (kw0 + 32 > Nk) || (CAUSAL && (kw0 + 31 > qi0 + off));
+      // P = exp2(S*c - L*log2e) and dS = P * (dP - D); lane holds key mykey and
+      // rows (i/4)*8 + half*4 + i%4 of the block.
+      bf16x8 pf[2], dsf[2];
 #pragma unroll
-        for (int kk = 0; kk < NKK; ++kk) {
-          sacc[mt] = mfma32(*(const bf16x8*)(qrow + kk * 16), kf[kk], sacc[mt]);
-          dpacc[mt] = mfma32(*(const bf16x8*)(dorow + kk * 16), vf[kk], dpacc[mt]);
+      for (int i4 = 0; i4 < 4; ++i4) {
+        const int ql = i4 * 8 + half * 4;
+        const float4 l2 = *(const float4*)(sL2[buf] + ql);
+        const float4 dd = *(const float4*)(sD[buf] + ql);
+        const float l2v[4] = {l2.x, l2.y, l2.z, l2.w};
+        const float ddv[4] = {dd.x, dd.y, dd.z, dd.w};
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int i = i4 * 4 + e;
+          float p = fast_exp2(fmaf(sacc[i], c, -l2v[e]));
+          if (need_mask) {
+            const int q = qi0 + ql + e;
+            const bool vis = (q < Nq) && (mykey < Nk) && (!CAUSAL || mykey <= q + off);
+            if (!vis) p = 0.f;
+          }
+          const float ds = p * (dpacc[i] - ddv[e]);
+          pf[i4 >> 1][(i4 & 1) * 4 + e] = (bf16)p;
+          dsf[i4 >> 1][(i4 & 1) * 4 + e] = (bf16)ds;
         }
       }
-      const bool need_mask = (qi0 + BR > Nq) || (k0 + BC > Nk) ||
-                             (CAUSAL && (qi0 + off < kw0 + 31));
-      // P = exp2(S*c - L*log2e), dS = P * (dP - D).
-      bf16x8 pf[4];
-#pragma unroll
-      for (int mt = 0; mt < 2; ++mt)
-#pragma unroll
-        for (int i4 = 0; i4 < 4; ++i4) {
-          const int ql = mt * 32 + i4 * 8 + half * 4;
-          const float4 l2 = *(const float4*)(sL2 + ql);
-          const float4 dd = *(const float4*)(sD + ql);
-          const float l2v[4] = {l2.x, l2.y, l2.z, l2.w};
-          const float ddv[4] = {dd.x, dd.y, dd.z, dd.w};
-#pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            const int i = i4 * 4 + e;
-            float p = fast_exp2(fmaf(sacc[mt][i], c, -l2v[e]));
-            if (need_mask) {
-              const int q = qi0 + ql + e;
-              const bool vis = (q < Nq) && (mykey < Nk) && (!CAUSAL || mykey <= q + off);
-              if (!vis) p = 0.f;
-            }
-            const float ds = p * (dpacc[mt][i] - ddv[e]);
-            const int kc = mt * 2 + (i4 >> 1);
-            const int slot = (i4 & 1) * 4 + e;
-            pf[kc][slot] = (bf16)p;
-            dsf[kc][slot] = (bf16)ds;
-          }
-        }
       // dV^T += dO^T P and dK^T += Q^T dS (A operands by LDS transpose reads).
 #pragma unroll
       for (int nt = 0; nt < NNT; ++nt) {
 #pragma unroll
-        for (int kc = 0; kc < 4; ++kc) {
-          const int off_lo = (kc * 16 + tr_row) * TSTR + nt * 32 + tr_col;
-          const bf16x8 a_do = concat(lds_read_tr(to_lds(sdO + off_lo)),
-                                     lds_read_tr(to_lds(sdO + off_lo + 8 * TSTR)));
+        for (int kc = 0; kc < 2; ++kc) {
+          const int o = (kc * 16 + tr_row) * QSTR + nt * 32 + tr_col;
+          const bf16x8 a_do = concat(lds_read_tr(to_lds(tdO + o)), lds_read_tr(to_lds(tdO + o + 8 * QSTR)));
           dvacc[nt] = mfma32(a_do, pf[kc], dvacc[nt]);
-          const bf16x8 a_q = concat(lds_read_tr(to_lds(sQ + off_lo)),
-                                    lds_read_tr(to_lds(sQ + off_lo + 8 * TSTR)));
+          const bf16x8 a_q = concat(lds_read_tr(to_lds(tQ + o)), lds_read_tr(to_lds(tQ + o + 8 * QSTR)));
           dkacc[nt] = mfma32(a_q, dsf[kc], dkacc[nt]);
         }
       }
-    } else {
-#pragma unroll
-      for (int kc = 0; kc < 4; ++kc) dsf[kc] = zero_bf16x8();
     }
-    // dS^T -> LDS: row = key, 4 consecutive query columns per store.
-    {
-      bf16* srow = sdS + (wave * 32 + l32) * SSTR + half * 4;
-#pragma unroll
-      for (int kc = 0; kc < 4; ++kc)
-#pragma unroll
-        for (int hh = 0; hh < 2; ++hh) {
-          bf16x4 v;
-#pragma unroll
-          for (int e = 0; e < 4; ++e) v[e] = dsf[kc][hh * 4 + e];
-          *(bf16x4*)(srow + kc * 16 + hh * 8) = v;
-        }
-    }
+    if (it + 1 < nloop) sstore(buf ^ 1);
     __syncthreads();
-
-    // dQ (unscaled) = dS K over the 128 keys of this workgroup, then atomics.
-    {
-      f32x16 qacc[NQT_W];
-#pragma unroll
-      for (int n = 0; n < NQT_W; ++n) qacc[n] = (f32x16){};
-#pragma unroll
-      for (int kc = 0; kc < BC / 16; ++kc) {
-        const int srow_lo = kc * 16 + half * 8 + (s16 >> 2);
-        const bf16* ap = sdS + srow_lo * SSTR + mq * 32 + (g & 1) * 16 + (s16 & 3) * 4;
-        const bf16x8 a = concat(lds_read_tr(to_lds(ap)), lds_read_tr(to_lds(ap + 4 * SSTR)));
-#pragma unroll
-        for (int n = 0; n < NQT_W; ++n) {
-          const bf16* bp = sK + srow_lo * TSTR + (nt0 + n) * 32 + (g & 1) * 16 + (s16 & 3) * 4;
-          const bf16x8 b = concat(lds_read_tr(to_lds(bp)), lds_read_tr(to_lds(bp + 4 * TSTR)));
-          qacc[n] = mfma32(a, b, qacc[n]);
-        }
-      }
-#pragma unroll
-      for (int n = 0; n < NQT_W; ++n) {
-        const int dc = (nt0 + n) * 32 + l32;
-#pragma unroll
-        for (int i = 0; i < 16; ++i) {
-          const int q = qi0 + mq * 32 + (i >> 2) * 8 + half * 4 + (i & 3);
-          if (q < Nq)
-            __hip_atomic_fetch_add(dQacc + (qbase + (size_t)q * D + dc), qacc[n][i],
-                                   __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        }
-      }
-    }
-    __syncthreads();
-    if (it + 1 < nloop) {
-      sstore();
-      __syncthreads();
-    }
   }
 
-  // Epilogue: dK = scale * dK_acc, dV = dV_acc; lane holds key kw0 + l32.
+  // Epilogue: dK = scale * dK_acc, dV = dV_acc; lane holds key mykey.
   if (mykey < Nk) {
     bf16* dkrow = dK + kbase + (size_t)mykey * D;
     bf16* dvrow = dV + kbase + (size_t)mykey * D;
@@ -323,24 +274,161 @@ __global__ __launch_bounds__(kBwdThreads, 1) void bwd_dkdv_bf16_kernel(
   }
 }
 
-// dQ = dtype(scale * dQacc), 8 elements per thread.
-template <typename T>
-__global__ __launch_bounds__(256) void bwd_dq_convert_kernel(const float* __restrict__ dQacc,
-                                                             T* __restrict__ dQ, float scale,
-                                                             long n8) {
-  const long i = (long)blockIdx.x * 256 + threadIdx.x;
-  if (i >= n8) return;
-  const float4 a = ((const float4*)dQacc)[2 * i];
-  const float4 b = ((const float4*)dQacc)[2 * i + 1];
-  const float v[8] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
-  if constexpr (sizeof(T) == 2) {
-    bf16x8 o;
+// ---------------------------------------------------------------------------
+// dQ: one workgroup per (query tile of 128, batch*head), key tiles streamed.
+constexpr int kDqBR = 128;  // query rows per workgroup
+constexpr int kDqBC = 64;   // keys per K/V tile
+constexpr int kDqThreads = 256;
+
+template <int D, bool CAUSAL>
+__global__ __launch_bounds__(kDqThreads, 2) void bwd_dq_bf16_kernel(
+    const bf16* __restrict__ Q, const bf16* __restrict__ K, const bf16* __restrict__ V,
+    const float* __restrict__ L, const bf16* __restrict__ dO, const float* __restrict__ Dvec,
+    bf16* __restrict__ dQ, int Nq, int Nk, int nqt, float c, float scale, int off) {
+  constexpr int BR = kDqBR, BC = kDqBC;
+  constexpr int KSTR = D + 16;   // K tile: row reads (S^T) and transpose reads (dQ^T)
+  constexpr int VSTR = D + 8;    // V tile: row reads (dP^T)
+  constexpr int CPR = D / 8;
+  constexpr int NLD = BC * CPR / kDqThreads;
+  constexpr int NKK = D / 16;
+  constexpr int NNT = D / 32;
+  static_assert(NLD * kDqThreads == BC * CPR, "tile load must divide evenly");
+
+  __shared__ __attribute__((aligned(16))) bf16 sK[BC * KSTR];
+  __shared__ __attribute__((aligned(16))) bf16 sV[BC * VSTR];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63, wave = tid >> 6;
+  const int half = lane >> 5, l32 = lane & 31;
+  const int g = lane >> 4, s16 = lane & 15;
+
+  const int logical = xcd_remap(blockIdx.x, gridDim.x);
+  const int bh = logical / nqt;
+  const int t = logical - bh * nqt;
+  const int qt = CAUSAL ? (nqt - 1 - t) : t;
+  const int q0 = qt * BR;
+  const size_t qbase = (size_t)bh * Nq * D;
+  const size_t kbase = (size_t)bh * Nk * D;
+
+  // This lane's query row: Q^T and dO^T fragments (B operands), L and D.
+  const int qrow = q0 + wave * 32 + l32;
+  bf16x8 qf[NKK], dof[NKK];
 #pragma unroll
-    for (int e = 0; e < 8; ++e) o[e] = (bf16)(v[e] * scale);
-    ((bf16x8*)dQ)[i] = o;
-  } else {
+  for (int kk = 0; kk < NKK; ++kk) {
+    const size_t o = qbase + (size_t)qrow * D + kk * 16 + half * 8;
+    qf[kk] = (qrow < Nq) ? *(const bf16x8*)(Q + o) : zero_bf16x8();
+    dof[kk] = (qrow < Nq) ? *(const bf16x8*)(dO + o) : zero_bf16x8();
+  }
+  const float l2 = (qrow < Nq) ? L[(size_t)bh * Nq + qrow] * kLog2e : INFINITY;
+  const float drow = (qrow < Nq) ? Dvec[(size_t)bh * Nq + qrow] : 0.f;
+
+  int kend = Nk;
+  if (CAUSAL) kend = min(Nk, q0 + BR + off);
+  const int ntiles = (kend + BC - 1) / BC;
+  const int wrow_lo = q0 + wave * 32;
+
+  bf16x8 kreg[NLD], vreg[NLD];
+  auto gload = [&](int tile) {
 #pragma unroll
-    for (int e = 0; e < 8; ++e) dQ[8 * i + e] = v[e] * scale;
+    for (int u = 0; u < NLD; ++u) {
+      const int idx = tid + u * kDqThreads;
+      const int r = idx / CPR, ch = idx - r * CPR;
+      const int key = tile * BC + r;
+      if (key < Nk) {
+        kreg[u] = *(const bf16x8*)(K + kbase + (size_t)key * D + ch * 8);
+        vreg[u] = *(const bf16x8*)(V + kbase + (size_t)key * D + ch * 8);
+      } else {
+        kreg[u] = zero_bf16x8();
+        vreg[u] = zero_bf16x8();
+      }
+    }
+  };
+  auto sstore = [&]() {
+#pragma unroll
+    for (int u = 0; u < NLD; ++u) {
+      const int idx = tid + u * kDqThreads;
+      const int r = idx / CPR, ch = idx - r * CPR;
+      *(bf16x8*)(sK + r * KSTR + ch * 8) = kreg[u];
+      *(bf16x8*)(sV + r * VSTR + ch * 8) = vreg[u];
+    }
+  };
+
+  f32x16 dqacc[NNT];
+#pragma unroll
+  for (int nt = 0; nt < NNT; ++nt) dqacc[nt] = (f32x16){};
+
+  gload(0);
+  sstore();
+  __syncthreads();
+
+  const int tr_row = (g >> 1) * 4 + (s16 >> 2);
+  const int tr_col = (g & 1) * 16 + (s16 & 3) * 4;
+
+  for (int j = 0; j < ntiles; ++j) {
+    if (j + 1 < ntiles) gload(j + 1);
+    const int k0 = j * BC;
+    const bool wave_idle = CAUSAL && (k0 > wrow_lo + 31 + off);
+    if (!wave_idle) {
+      // S^T = K Q^T and dP^T = V dO^T: keys [k0, k0+64) x this wave's 32 rows.
+      f32x16 sacc[2], dpacc[2];
+#pragma unroll
+      for (int mt = 0; mt < 2; ++mt) {
+        sacc[mt] = (f32x16){};
+        dpacc[mt] = (f32x16){};
+        const bf16* krow = sK + (mt * 32 + l32) * KSTR + half * 8;
+        const bf16* vrow = sV + (mt * 32 + l32) * VSTR + half * 8;
+#pragma unroll
+        for (int kk = 0; kk < NKK; ++kk) {
+          sacc[mt] = mfma32(*(const bf16x8*)(krow + kk * 16), qf[kk], sacc[mt]);
+          dpacc[mt] = mfma32(*(const bf16x8*)(vrow + kk * 16), dof[kk], dpacc[mt]);
+        }
+      }
+      const bool need_mask = (k0 + BC > Nk) || (CAUSAL && (k0 + BC - 1 > wrow_lo + off));
+      // dS^T = P^T * (dP^T - D) with P^T = exp2(S^T*c - L*log2e); lane holds
+      // row qrow and keys k0 + mt*32 + (i/4)*8 + half*4 + i%4.
+      bf16x8 dsf[4];
+#pragma unroll
+      for (int mt = 0; mt < 2; ++mt)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+          float p = fast_exp2(fmaf(sacc[mt][i], c, -l2));
+          if (need_mask) {
+            const int key = k0 + mt * 32 + (i >> 2) * 8 + half * 4 + (i & 3);
+            const bool vis = (key < Nk) && (!CAUSAL || key <= qrow + off);
+            if (!vis) p = 0.f;
+          }
+          dsf[mt * 2 + (i >> 3)][i & 7] = (bf16)(p * (dpacc[mt][i] - drow));
+        }
+      // dQ^T += K^T dS^T (K^T by LDS transpose reads of the K tile).
+#pragma unroll
+      for (int nt = 0; nt < NNT; ++nt) {
+#pragma unroll
+        for (int kc = 0; kc < 4; ++kc) {
+          const bf16* kp = sK + (kc * 16 + tr_row) * KSTR + nt * 32 + tr_col;
+          const bf16x8 a = concat(lds_read_tr(to_lds(kp)), lds_read_tr(to_lds(kp + 8 * KSTR)));
+          dqacc[nt] = mfma32(a, dsf[kc], dqacc[nt]);
+        }
+      }
+    }
+    __syncthreads();
+    if (j + 1 < ntiles) {
+      sstore();
+      __syncthreads();
+    }
+  }
+
+  // Epilogue: dQ = scale * dQ_acc; lane holds row qrow.
+  if (qrow < Nq) {
+    bf16* out = dQ + qbase + (size_t)qrow * D;
+#pragma unroll
+    for (int nt = 0; nt < NNT; ++nt)
+#pragma unroll
+      for (int gg = 0; gg < 4; ++gg) {
+        bf16x4 v;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) v[e] = (bf16)(dqacc[nt][gg * 4 + e] * scale);
+        *(bf16x4*)(out + nt * 32 + gg * 8 + half * 4) = v;
+      }
   }
 }
 
@@ -455,7 +543,7 @@ hipError_t launch_pre(const BwdArgs& a, hipStream_t s) {
   const long nb = (rows + RPB - 1) / RPB;
   if (nb == 0) return hipSuccess;
   hipLaunchKernelGGL((bwd_pre_kernel<D, T>), dim3((unsigned)nb), dim3(256), 0, s,
-                     (const T*)a.O, (const T*)a.dO, a.Dvec, a.dQacc, rows);
+                     (const T*)a.O, (const T*)a.dO, a.Dvec, rows);
   return hipGetLastError();
 }
 
@@ -463,34 +551,45 @@ hipError_t launch_pre(const BwdArgs& a, hipStream_t s) {
 
 hipError_t launch_bwd_bf16(const BwdArgs& a, int stages, hipStream_t s) {
   const int BH = a.B * a.H;
+  const float c = a.scale * kLog2e;
+  const int off = a.Nk - a.Nq;
+  const bf16* Q = (const bf16*)a.Q;
+  const bf16* K = (const bf16*)a.K;
+  const bf16* V = (const bf16*)a.V;
+  const bf16* dO = (const bf16*)a.dO;
   if (stages & 1) {
     const hipError_t e = (a.d == 128) ? launch_pre<128, bf16>(a, s) : launch_pre<64, bf16>(a, s);
     if (e != hipSuccess) return e;
   }
-  if (stages & 2) {
-    const int nkt = (a.Nk + kBwdBC - 1) / kBwdBC;
+  if ((stages & 2) && a.Nk > 0) {
+    const int nkt = (a.Nk + kKvBC - 1) / kKvBC;
     const int nblocks = nkt * BH;
-    const float c = a.scale * kLog2e;
-    const int off = a.Nk - a.Nq;
-#define FA_BWD_LAUNCH(DD, CC)                                                                   \
-  hipLaunchKernelGGL((bwd_dkdv_bf16_kernel<DD, CC>), dim3(nblocks), dim3(kBwdThreads), 0, s,     \
-                     (const bf16*)a.Q, (const bf16*)a.K, (const bf16*)a.V, a.L,                  \
-                     (const bf16*)a.dO, a.Dvec, a.dQacc, (bf16*)a.dK, (bf16*)a.dV, a.Nq, a.Nk,   \
-                     nkt, c, a.scale, off)
+    const int hpx = (BH % kNumXcd == 0) ? BH / kNumXcd : 0;
+#define FA_DKDV_LAUNCH(DD, CC)                                                                  \
+  hipLaunchKernelGGL((bwd_dkdv_bf16_kernel<DD, CC>), dim3(nblocks), dim3(kKvThreads), 0, s, Q, K, \
+                     V, a.L, dO, a.Dvec, (bf16*)a.dK, (bf16*)a.dV, a.Nq, a.Nk, nkt, BH, hpx, c,  \
+                     a.scale, off)
     if (a.d == 128) {
-      if (a.causal) FA_BWD_LAUNCH(128, true); else FA_BWD_LAUNCH(128, false);
+      if (a.causal) FA_DKDV_LAUNCH(128, true); else FA_DKDV_LAUNCH(128, false);
     } else {
-      if (a.causal) FA_BWD_LAUNCH(64, true); else FA_BWD_LAUNCH(64, false);
+      if (a.causal) FA_DKDV_LAUNCH(64, true); else FA_DKDV_LAUNCH(64, false);
     }
-#undef FA_BWD_LAUNCH
+#undef FA_DKDV_LAUNCH
     const hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
-  if (stages & 4) {
-    const long n8 = (long)BH * a.Nq * a.d / 8;
-    if (n8 == 0) return hipSuccess;
-    hipLaunchKernelGGL((bwd_dq_convert_kernel<bf16>), dim3((unsigned)((n8 + 255) / 256)),
-                       dim3(256), 0, s, a.dQacc, (bf16*)a.dQ, a.scale, n8);
+  if ((stages & 4) && a.Nq > 0) {
+    const int nqt = (a.Nq + kDqBR - 1) / kDqBR;
+    const int nblocks = nqt * BH;
+#define FA_DQ_LAUNCH(DD, CC)                                                                    \
+  hipLaunchKernelGGL((bwd_dq_bf16_kernel<DD, CC>), dim3(nblocks), dim3(kDqThreads), 0, s, Q, K,  \
+                     V, a.L, dO, a.Dvec, (bf16*)a.dQ, a.Nq, a.Nk, nqt, c, a.scale, off)
+    if (a.d == 128) {
+      if (a.causal) FA_DQ_LAUNCH(128, true); else FA_DQ_LAUNCH(128, false);
+    } else {
+      if (a.causal) FA_DQ_LAUNCH(64, true); else FA_DQ_LAUNCH(64, false);
+    }
+#undef FA_DQ_LAUNCH
     return hipGetLastError();
   }
   return hipSuccess;
@@ -502,7 +601,6 @@ hipError_t launch_bwd_f32(const BwdArgs& a, int stages, hipStream_t s) {
     const hipError_t e = (a.d == 128) ? launch_pre<128, float>(a, s) : launch_pre<64, float>(a, s);
     if (e != hipSuccess) return e;
   }
-  if (!(stages & 2)) return hipSuccess;  // the fp32 path writes dQ directly in its main stage
   const int nkt = (a.Nk + kF32BT - 1) / kF32BT;
   const int nqt = (a.Nq + kF32BT - 1) / kF32BT;
   const int off = a.Nk - a.Nq;
@@ -510,22 +608,32 @@ hipError_t launch_bwd_f32(const BwdArgs& a, int stages, hipStream_t s) {
   const float* K = (const float*)a.K;
   const float* V = (const float*)a.V;
   const float* dO = (const float*)a.dO;
-#define FA_BWD32_LAUNCH(DD, CC)                                                                  \
-  do {                                                                                            \
-    hipLaunchKernelGGL((bwd_dkdv_f32_kernel<DD, CC>), dim3(nkt * BH), dim3(kF32BT), 0, s, Q, K,   \
-                       V, a.L, dO, a.Dvec, (float*)a.dK, (float*)a.dV, a.Nq, a.Nk, nkt, a.scale,  \
-                       off);                                                                      \
-    if (nqt > 0)                                                                                  \
-      hipLaunchKernelGGL((bwd_dq_f32_kernel<DD, CC>), dim3(nqt * BH), dim3(kF32BT), 0, s, Q, K,   \
-                         V, a.L, dO, a.Dvec, (float*)a.dQ, a.Nq, a.Nk, nqt, a.scale, off);        \
-  } while (0)
-  if (a.d == 128) {
-    if (a.causal) FA_BWD32_LAUNCH(128, true); else FA_BWD32_LAUNCH(128, false);
-  } else {
-    if (a.causal) FA_BWD32_LAUNCH(64, true); else FA_BWD32_LAUNCH(64, false);
+  if ((stages & 2) && nkt > 0) {
+#define FA_DKDV32_LAUNCH(DD, CC)                                                                \
+  hipLaunchKernelGGL((bwd_dkdv_f32_kernel<DD, CC>), dim3(nkt * BH), dim3(kF32BT), 0, s, Q, K, V, \
+                     a.L, dO, a.Dvec, (float*)a.dK, (float*)a.dV, a.Nq, a.Nk, nkt, a.scale, off)
+    if (a.d == 128) {
+      if (a.causal) FA_DKDV32_LAUNCH(128, true); else FA_DKDV32_LAUNCH(128, false);
+    } else {
+      if (a.causal) FA_DKDV32_LAUNCH(64, true); else FA_DKDV32_LAUNCH(64, false);
+    }
+#undef FA_DKDV32_LAUNCH
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
   }
-#undef FA_BWD32_LAUNCH
-  return hipGetLastError();
+  if ((stages & 4) && nqt > 0) {
+#define FA_DQ32_LAUNCH(DD, CC)                                                                \
+  hipLaunchKernelGGL((bwd_dq_f32_kernel<DD, CC>), dim3(nqt * BH), dim3(kF32BT), 0, s, Q, K, V, \
+                     a.L, dO, a.Dvec, (float*)a.dQ, a.Nq, a.Nk, nqt, a.scale, off)
+    if (a.d == 128) {
+      if (a.causal) FA_DQ32_LAUNCH(128, true); else FA_DQ32_LAUNCH(128, false);
+    } else {
+      if (a.causal) FA_DQ32_LAUNCH(64, true); else FA_DQ32_LAUNCH(64, false);
+    }
+#undef FA_DQ32_LAUNCH
+    return hipGetLastError();
+  }
+  return hipSuccess;
 }
 
 }  // namespace fa

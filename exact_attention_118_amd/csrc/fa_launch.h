@@ -32,8 +32,7 @@ struct BwdArgs {
   int B, H, Nq, Nk, d;
   float scale;
   bool causal;
-  float* Dvec;   // [B*H*Nq] fp32 scratch (workspace)
-  float* dQacc;  // [B*H*Nq*d] fp32 scratch (workspace)
+  float* Dvec;  // [B*H*Nq] fp32 scratch (workspace)
 };
 
 // Tiled forward (Q-tile per workgroup, K/V streamed through LDS).
@@ -45,8 +44,8 @@ hipError_t launch_fwd_f32(const FwdArgs& a, hipStream_t s);
 hipError_t launch_fwd_split_bf16(const FwdArgs& a, int splits, float* part_o, float* part_l,
                                  hipStream_t s);
 
-// Backward: D = rowsum(dO*O) and clearing dQacc; dK/dV (+ dQ atomics); dQ conversion.
-// `stages`: bit 1 preprocess, bit 2 main kernel(s), bit 4 dQ conversion.
+// Backward: D = rowsum(dO*O); dK and dV; dQ.
+// `stages`: bit 1 D, bit 2 dK/dV kernel, bit 4 dQ kernel (2 and 4 read D).
 hipError_t launch_bwd_bf16(const BwdArgs& a, int stages, hipStream_t s);
 hipError_t launch_bwd_f32(const BwdArgs& a, int stages, hipStream_t s);
 

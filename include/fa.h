@@ -79,16 +79,17 @@ fa_status fa_fwd(const void* Q, const void* K, const void* V, void* O, float* L,
 
 /*
  * Backward pass: dQ, dK, dV of f = sum(dO * O) for the forward above,
- * recomputing P from Q, K and L instead of storing it (the Huawei Cloud post "FlashAttention", section 3
- * "Recomputation"; the 51CTO FlashAttention V1/V2 notes: only L is kept for the backward pass, and the
- * backward kernel also takes the per-row auxiliary D = rowsum(dO * O)).
+ * recomputing P from Q, K and L instead of storing it (the Huawei Cloud post
+ * "FlashAttention", section 3, Recomputation; the 51CTO FlashAttention V1/V2
+ * notes, "FlashAttention V2相比V1有哪些改进": only L is kept for the backward
+ * pass, which also takes the per-row auxiliary D = rowsum(dO * O)).
  *
  *  Q, K, V, O (from fa_fwd), L (from fa_fwd), dO: read.  dQ [B,H,Nq,d],
  *  dK, dV [B,H,Nk,d]: overwritten, every element (not accumulated into).
- *  workspace: fa_bwd_workspace_size() bytes of device memory, holding D
- *  [B,H,Nq] fp32 and an fp32 dQ accumulator [B,H,Nq,d]; the library clears
- *  what it needs.  dQ is reduced across key blocks with fp32 atomic adds, so
- *  its low-order bits may differ between runs; dK and dV are deterministic.
+ *  workspace: fa_bwd_workspace_size() bytes of device memory (D, [B,H,Nq]
+ *  fp32), written by the first stage.  dK and dV are computed per key block and
+ *  dQ per query block by a second kernel that recomputes P and dP, so there
+ *  are no atomic operations and every output is deterministic.
  */
 fa_status fa_bwd(const void* Q, const void* K, const void* V, const void* O, const float* L,
                  const void* dO, void* dQ, void* dK, void* dV,
@@ -98,15 +99,14 @@ fa_status fa_bwd(const void* Q, const void* K, const void* V, const void* O, con
 /*
  * The backward pass as its three launches, for callers that schedule or time
  * them separately.  Same arguments as fa_bwd plus `stages`, a bit mask:
- *   FA_BWD_PREPROCESS (1): D = rowsum(dO * O) into the workspace and clear the
- *                          workspace dQ accumulator;
- *   FA_BWD_MAIN       (2): dK, dV written; dQ contributions added into the
- *                          workspace accumulator (needs stage 1 first);
- *   FA_BWD_FINALIZE   (4): dQ = scale * accumulator, converted to dtype.
- * fa_bwd(...) is fa_bwd_stages(..., FA_BWD_ALL).  Stages must run in order on
- * one workspace; a mask of 0 or above 7 returns FA_ERR_UNSUPPORTED.
+ *   FA_BWD_PREPROCESS (1): D = rowsum(dO * O) into the workspace;
+ *   FA_BWD_DKDV       (2): dK and dV written (reads D);
+ *   FA_BWD_DQ         (4): dQ written (reads D).
+ * fa_bwd(...) is fa_bwd_stages(..., FA_BWD_ALL).  Stages 2 and 4 need stage 1
+ * to have run on the same workspace; a mask of 0 or above 7 returns
+ * FA_ERR_UNSUPPORTED.
  */
-enum { FA_BWD_PREPROCESS = 1, FA_BWD_MAIN = 2, FA_BWD_FINALIZE = 4, FA_BWD_ALL = 7 };
+enum { FA_BWD_PREPROCESS = 1, FA_BWD_DKDV = 2, FA_BWD_DQ = 4, FA_BWD_ALL = 7 };
 fa_status fa_bwd_stages(const void* Q, const void* K, const void* V, const void* O,
                         const float* L, const void* dO, void* dQ, void* dK, void* dV,
                         int B, int H, int Nq, int Nk, int d, float scale, int causal,

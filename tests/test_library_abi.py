@@ -121,15 +121,15 @@ def test_bwd_rejects_bad_arguments(lib):
         assert lib.fa_bwd_stages(*([A] * 9), 1, 1, 16, 16, 64, 0.125, 0, fa.FA_BF16, A, need, None,
                                  bad) == fa.FA_ERR_UNSUPPORTED
     assert lib.fa_bwd_stages(*([A] * 9), 1, 1, 16, 16, 64, 0.125, 0, fa.FA_BF16, None, 0, None,
-                             fa.FA_BWD_MAIN) == fa.FA_ERR_WORKSPACE
+                             fa.FA_BWD_DKDV) == fa.FA_ERR_WORKSPACE
 
 
 def test_workspace_queries(lib):
     B, H, N, d = 2, 3, 100, 128
-    # backward: D [B,H,N] fp32 then the fp32 dQ accumulator, each padded to 256 bytes
+    # backward: D [B,H,N] fp32, padded to 256 bytes
     def up(x):
         return (x + 255) // 256 * 256
-    assert lib.fa_bwd_workspace_size(B, H, N, N, d, fa.FA_BF16) == up(B * H * N * 4) + up(B * H * N * d * 4)
+    assert lib.fa_bwd_workspace_size(B, H, N, N, d, fa.FA_BF16) == up(B * H * N * 4)
     # tiled forward needs none; the split path holds per-split outputs and logsumexps
     assert lib.fa_fwd_workspace_size(B, H, N, N, d, fa.FA_BF16, 0) == 0
     assert lib.fa_fwd_num_splits(B, H, N, N, d, fa.FA_BF16, 0) == 1
