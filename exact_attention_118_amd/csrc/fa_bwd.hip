@@ -281,21 +281,23 @@ constexpr int kDqBC = 64;   // keys per K/V tile
 constexpr int kDqThreads = 256;
 
 template <int D, bool CAUSAL>
-__global__ __launch_bounds__(kDqThreads, 2) void bwd_dq_bf16_kernel(
-    const bf16* __restrict__ Q, const bf16* __restrict__ K, const bf16* __restrict__ V,
-    const float* __restrict__ L, const bf16* __restrict__ dO, const float* __restrict__ Dvec,
-    bf16* __restrict__ dQ, int Nq, int Nk, int nqt, float c, float scale, int off) {
+__global__ __launch_bounds__(kDqThreads, 2) __attribute__((amdgpu_waves_per_eu(2, 2)))
+void bwd_dq_bf16_kernel(const bf16* __restrict__ Q, const bf16* __restrict__ K,
+                        const bf16* __restrict__ V, const float* __restrict__ L,
+                        const bf16* __restrict__ dO, const float* __restrict__ Dvec,
+                        bf16* __restrict__ dQ, int Nq, int Nk, int nqt, float c, float scale,
+                        int off) {
   constexpr int BR = kDqBR, BC = kDqBC;
-  constexpr int KSTR = D + 16;   // K tile: row reads (S^T) and transpose reads (dQ^T)
-  constexpr int VSTR = D + 8;    // V tile: row reads (dP^T)
-  constexpr int CPR = D / 8;
-  constexpr int NLD = BC * CPR / kDqThreads;
   constexpr int NKK = D / 16;
   constexpr int NNT = D / 32;
-  static_assert(NLD * kDqThreads == BC * CPR, "tile load must divide evenly");
+  constexpr int TILE = BC * D;
 
-  __shared__ __attribute__((aligned(16))) bf16 sK[BC * KSTR];
-  __shared__ __attribute__((aligned(16))) bf16 sV[BC * VSTR];
+  constexpr unsigned TB = TILE * 2;  // bytes per tile (a power of two)
+  // K tiles (buffers 0/1) and V tiles (buffers 2/3), swizzled (see swz) and
+  // double-buffered: tile j+1 loads while tile j is read.
+  __shared__ __attribute__((aligned(1024))) bf16 smem[4 * TILE];
+  bf16* const sK0 = smem;
+  bf16* const sV0 = smem + 2 * TILE;
 
   const int tid = threadIdx.x;
   const int lane = tid & 63, wave = tid >> 6;
@@ -308,7 +310,8 @@ __global__ __launch_bounds__(kDqThreads, 2) void bwd_dq_bf16_kernel(
   const int qt = CAUSAL ? (nqt - 1 - t) : t;
   const int q0 = qt * BR;
   const size_t qbase = (size_t)bh * Nq * D;
-  const size_t kbase = (size_t)bh * Nk * D;
+  const bf16* Kh = K + (size_t)bh * Nk * D;
+  const bf16* Vh = V + (size_t)bh * Nk * D;
 
   // This lane's query row: Q^T and dO^T fragments (B operands), L and D.
   const int qrow = q0 + wave * 32 + l32;
@@ -322,99 +325,107 @@ __global__ __launch_bounds__(kDqThreads, 2) void bwd_dq_bf16_kernel(
   const float l2 = (qrow < Nq) ? L[(size_t)bh * Nq + qrow] * kLog2e : INFINITY;
   const float drow = (qrow < Nq) ? Dvec[(size_t)bh * Nq + qrow] : 0.f;
 
-  int kend = Nk;
-  if (CAUSAL) kend = min(Nk, q0 + BR + off);
+  const int kend = CAUSAL ? min(Nk, q0 + BR + off) : Nk;
   const int ntiles = (kend + BC - 1) / BC;
   const int wrow_lo = q0 + wave * 32;
 
-  bf16x8 kreg[NLD], vreg[NLD];
-  auto gload = [&](int tile) {
-#pragma unroll
-    for (int u = 0; u < NLD; ++u) {
-      const int idx = tid + u * kDqThreads;
-      const int r = idx / CPR, ch = idx - r * CPR;
-      const int key = tile * BC + r;
-      if (key < Nk) {
-        kreg[u] = *(const bf16x8*)(K + kbase + (size_t)key * D + ch * 8);
-        vreg[u] = *(const bf16x8*)(V + kbase + (size_t)key * D + ch * 8);
-      } else {
-        kreg[u] = zero_bf16x8();
-        vreg[u] = zero_bf16x8();
-      }
-    }
+  const int tr_row = (g >> 1) * 4 + (s16 >> 2);
+  const int tr_col = (g & 1) * 16 + (s16 & 3) * 4;
+  // S^T and dP^T for one 32-key half mt: 2 x NKK steps alternating the K
+  // (even step, S^T) and V (odd step, dP^T) row fragments.
+  const SwzRow<D> rowsw(l32, half);
+  const SwzTr<D> trsw(tr_row, tr_col);
+  auto sfrag = [&](const SwzRow<D>& rs, int mt, int st) {
+    const bf16* base = (st & 1) ? sV0 : sK0;
+    return *at_byte<bf16x8>(base, rs.off(mt * 32, (st >> 1) * 2));
   };
-  auto sstore = [&]() {
-#pragma unroll
-    for (int u = 0; u < NLD; ++u) {
-      const int idx = tid + u * kDqThreads;
-      const int r = idx / CPR, ch = idx - r * CPR;
-      *(bf16x8*)(sK + r * KSTR + ch * 8) = kreg[u];
-      *(bf16x8*)(sV + r * VSTR + ch * 8) = vreg[u];
-    }
+  // dQ^T += K^T dS^T for one 32-key half mt: 2 x NNT steps (16-key chunk
+  // kc = st / NNT of the half, head-dim tile st % NNT); K^T by transpose reads.
+  auto kt_frag = [&](const SwzTr<D>& ts, int mt, int st) {
+    const int rb = mt * 32 + (st / NNT) * 16, cb = (st % NNT) * 32;
+    return concat(lds_read_tr(to_lds(at_byte<bf16>(sK0, ts.off(rb, 0, cb)))),
+                  lds_read_tr(to_lds(at_byte<bf16>(sK0, ts.off(rb, 1, cb)))));
   };
+  constexpr int SRING = 4, TRING = 3;
 
   f32x16 dqacc[NNT];
 #pragma unroll
   for (int nt = 0; nt < NNT; ++nt) dqacc[nt] = (f32x16){};
 
-  gload(0);
-  sstore();
+  dma_tile<D, BC, kDqThreads>(Kh, 0, Nk, sK0, tid);
+  dma_tile<D, BC, kDqThreads>(Vh, 0, Nk, sV0, tid);
+  vm_wait_all();
   __syncthreads();
 
-  const int tr_row = (g >> 1) * 4 + (s16 >> 2);
-  const int tr_col = (g & 1) * 16 + (s16 & 3) * 4;
-
   for (int j = 0; j < ntiles; ++j) {
-    if (j + 1 < ntiles) gload(j + 1);
-    const int k0 = j * BC;
-    const bool wave_idle = CAUSAL && (k0 > wrow_lo + 31 + off);
-    if (!wave_idle) {
-      // S^T = K Q^T and dP^T = V dO^T: keys [k0, k0+64) x this wave's 32 rows.
-      f32x16 sacc[2], dpacc[2];
-#pragma unroll
-      for (int mt = 0; mt < 2; ++mt) {
-        sacc[mt] = (f32x16){};
-        dpacc[mt] = (f32x16){};
-        const bf16* krow = sK + (mt * 32 + l32) * KSTR + half * 8;
-        const bf16* vrow = sV + (mt * 32 + l32) * VSTR + half * 8;
-#pragma unroll
-        for (int kk = 0; kk < NKK; ++kk) {
-          sacc[mt] = mfma32(*(const bf16x8*)(krow + kk * 16), qf[kk], sacc[mt]);
-          dpacc[mt] = mfma32(*(const bf16x8*)(vrow + kk * 16), dof[kk], dpacc[mt]);
-        }
-      }
-      const bool need_mask = (k0 + BC > Nk) || (CAUSAL && (k0 + BC - 1 > wrow_lo + off));
-      // dS^T = P^T * (dP^T - D) with P^T = exp2(S^T*c - L*log2e); lane holds
-      // row qrow and keys k0 + mt*32 + (i/4)*8 + half*4 + i%4.
-      bf16x8 dsf[4];
-#pragma unroll
-      for (int mt = 0; mt < 2; ++mt)
-#pragma unroll
-        for (int i = 0; i < 16; ++i) {
-          float p = fast_exp2(fmaf(sacc[mt][i], c, -l2));
-          if (need_mask) {
-            const int key = k0 + mt * 32 + (i >> 2) * 8 + half * 4 + (i & 3);
-            const bool vis = (key < Nk) && (!CAUSAL || key <= qrow + off);
-            if (!vis) p = 0.f;
-          }
-          dsf[mt * 2 + (i >> 3)][i & 7] = (bf16)(p * (dpacc[mt][i] - drow));
-        }
-      // dQ^T += K^T dS^T (K^T by LDS transpose reads of the K tile).
-#pragma unroll
-      for (int nt = 0; nt < NNT; ++nt) {
-#pragma unroll
-        for (int kc = 0; kc < 4; ++kc) {
-          const bf16* kp = sK + (kc * 16 + tr_row) * KSTR + nt * 32 + tr_col;
-          const bf16x8 a = concat(lds_read_tr(to_lds(kp)), lds_read_tr(to_lds(kp + 8 * KSTR)));
-          dqacc[nt] = mfma32(a, dsf[kc], dqacc[nt]);
-        }
-      }
-    }
-    __syncthreads();
     if (j + 1 < ntiles) {
-      sstore();
-      __syncthreads();
+      dma_tile<D, BC, kDqThreads>(Kh, (j + 1) * BC, Nk, sK0 + ((j + 1) & 1) * TILE, tid);
+      dma_tile<D, BC, kDqThreads>(Vh, (j + 1) * BC, Nk, sV0 + ((j + 1) & 1) * TILE, tid);
     }
+    const SwzRow<D> rs = rowsw.flipped((j & 1) * TB);
+    const SwzTr<D> ts = trsw.flipped((j & 1) * TB);
+    const int k0 = j * BC;
+    const bool need_mask = (k0 + BC > Nk) || (CAUSAL && (k0 + BC - 1 > wrow_lo + off));
+
+    // dS^T for the 16 keys of element e of half mt: lane holds row qrow and
+    // keys k0 + mt*32 + (i/4)*8 + half*4 + i%4.
+    f32x16 sacc[2], dpacc[2];
+    bf16x8 dsf[4];
+    auto ds_elem = [&](int mt, int i) {
+      float p = fast_exp2(fmaf(sacc[mt][i], c, -l2));
+      if (need_mask) {
+        const int key = k0 + mt * 32 + (i >> 2) * 8 + half * 4 + (i & 3);
+        const bool vis = (key < Nk) && (!CAUSAL || key <= qrow + off);
+        if (!vis) p = 0.f;
+      }
+      dsf[mt * 2 + (i >> 3)][i & 7] = (bf16)(p * (dpacc[mt][i] - drow));
+    };
+    // S^T, dP^T of half mt (16 MFMAs); with `overlap`, the dS elements of half
+    // mt - 1 are computed between them.
+    auto sdp_half = [&](int mt, bool overlap) {
+      sacc[mt] = (f32x16){};
+      dpacc[mt] = (f32x16){};
+      bf16x8 ring[SRING];
+#pragma unroll
+      for (int st = 0; st < SRING; ++st) ring[st] = sfrag(rs, mt, st);
+#pragma unroll
+      for (int st = 0; st < 2 * NKK; ++st) {
+        const bf16x8 a = ring[st % SRING];
+        if (st + SRING < 2 * NKK) ring[st % SRING] = sfrag(rs, mt, st + SRING);
+        if (st & 1) dpacc[mt] = mfma32(a, dof[st >> 1], dpacc[mt]);
+        else sacc[mt] = mfma32(a, qf[st >> 1], sacc[mt]);
+        if (overlap) {
+#pragma unroll
+          for (int h = 0; h < 16 / (2 * NKK); ++h) ds_elem(mt - 1, st * (16 / (2 * NKK)) + h);
+        }
+        __builtin_amdgcn_sched_barrier(0);
+      }
+    };
+    // dQ^T += K^T dS^T over half mt (2*NNT MFMAs); with `overlap`, the dS
+    // elements of half mt + 1 are computed between them.
+    auto dq_half = [&](int mt, bool overlap) {
+      bf16x8 ring[TRING];
+#pragma unroll
+      for (int st = 0; st < TRING; ++st) ring[st] = kt_frag(ts, mt, st);
+#pragma unroll
+      for (int st = 0; st < 2 * NNT; ++st) {
+        const bf16x8 a = ring[st % TRING];
+        if (st + TRING < 2 * NNT) ring[st % TRING] = kt_frag(ts, mt, st + TRING);
+        dqacc[st % NNT] = mfma32(a, dsf[mt * 2 + st / NNT], dqacc[st % NNT]);
+        if (overlap) {
+#pragma unroll
+          for (int h = 0; h < 16 / (2 * NNT); ++h) ds_elem(mt + 1, st * (16 / (2 * NNT)) + h);
+        }
+        __builtin_amdgcn_sched_barrier(0);
+      }
+    };
+    sdp_half(0, false);
+    sdp_half(1, true);   // dS of half 0 overlaps the MFMAs of half 1
+    dq_half(0, true);    // dS of half 1 overlaps dQ of half 0
+    dq_half(1, false);
+
+    vm_wait_all();  // this wave's part of tile j+1 has landed
+    __syncthreads();
   }
 
   // Epilogue: dQ = scale * dQ_acc; lane holds row qrow.

@@ -69,4 +69,99 @@ __device__ __forceinline__ float wave_shfl_xor(float v, int mask) {
   return __shfl_xor(v, mask, 64);
 }
 
+// Swizzled LDS tiles.  A [rows][D] bf16 tile is stored without padding, each
+// row's 16-byte chunks permuted: logical chunk c of row r sits at physical
+// chunk c ^ swz<D>(r).  The permutation makes both access patterns of the
+// kernels free of LDS bank conflicts: 16 lanes reading 16 consecutive rows at
+// one logical chunk (ds_read_b128), and 32 lanes reading 4 consecutive rows
+// times 4 consecutive chunks (ds_read_b64_tr_b16).
+template <int D>
+__device__ __forceinline__ int swz(int r) {
+  static_assert(D == 64 || D == 128, "head dim");
+  if constexpr (D == 128) return ((r & 3) << 2) | ((r >> 2) & 3);
+  return ((r >> 1) & 1) | (((r >> 2) & 1) << 1) | ((((r >> 1) ^ (r >> 3)) & 1) << 2);
+}
+
+// Byte offsets into swizzled tiles, in a form that costs one VALU XOR per LDS
+// read: the row part, the swizzled chunk and the byte within the chunk occupy
+// disjoint bit ranges, so the lane-dependent part is computed once and each
+// read XORs in a compile-time constant.
+
+// Row reads (ds_read_b128): the lane reads row rb + l32 (rb a multiple of 32)
+// at logical chunk c.
+// `chalf` (0 or 1) is a lane-dependent chunk added to every c (the lane half).
+template <int D>
+struct SwzRow {
+  unsigned x;
+  __device__ __forceinline__ SwzRow(int l32, int chalf)
+      : x((unsigned)(l32 * 2 * D) ^ ((unsigned)(swz<D>(l32) ^ chalf) << 4)) {}
+  __device__ __forceinline__ explicit SwzRow(unsigned x_) : x(x_) {}
+  // The same lane offsets in the tile buffer `flip` bytes away, flip being a
+  // power of two above every offset inside a tile.
+  __device__ __forceinline__ SwzRow flipped(unsigned flip) const { return SwzRow(x ^ flip); }
+  __device__ __forceinline__ unsigned off(int rb, int c) const {
+    return (unsigned)(rb * 2 * D) + (x ^ ((unsigned)c << 4));
+  }
+};
+
+// Transpose reads (ds_read_b64_tr_b16): the lane supplies row
+// rb + tr_row + 8*hi (rb a multiple of 16) and column cb + tr_col (cb a
+// multiple of 32), where tr_row < 8 and tr_col < 32 are its lane constants.
+template <int D>
+struct SwzTr {
+  unsigned y[2];
+  __device__ __forceinline__ SwzTr(int tr_row, int tr_col) {
+#pragma unroll
+    for (int hi = 0; hi < 2; ++hi) {
+      const int r = tr_row + 8 * hi;
+      y[hi] = (unsigned)(r * 2 * D) ^ ((unsigned)((tr_col >> 3) ^ swz<D>(r)) << 4) ^
+              (unsigned)((tr_col & 7) * 2);
+    }
+  }
+  __device__ __forceinline__ SwzTr() {}
+  __device__ __forceinline__ SwzTr flipped(unsigned flip) const {
+    SwzTr t;
+    t.y[0] = y[0] ^ flip;
+    t.y[1] = y[1] ^ flip;
+    return t;
+  }
+  __device__ __forceinline__ unsigned off(int rb, int hi, int cb) const {
+    return (unsigned)(rb * 2 * D) + (y[hi] ^ ((unsigned)(cb >> 3) << 4));
+  }
+};
+
+template <typename T>
+__device__ __forceinline__ const T* at_byte(const void* base, unsigned off) {
+  return (const T*)((const char*)base + off);
+}
+
+// Rows [row0, row0 + ROWS) of a row-major [*, D] bf16 matrix g into a swizzled
+// LDS tile, with direct-to-LDS loads (global_load_lds_dwordx4: lane i of a
+// wave instruction writes 16 bytes at the instruction's LDS base + 16 i).
+// Rows at or beyond nvalid (>= 1) are read from row nvalid - 1 instead, so the
+// tile holds finite data that the caller masks.  All THREADS threads call it;
+// the data is in LDS once this wave has waited for vmcnt and the workgroup has
+// passed a barrier.
+template <int D, int ROWS, int THREADS>
+__device__ __forceinline__ void dma_tile(const bf16* __restrict__ g, int row0, int nvalid,
+                                         bf16* lds, int tid) {
+  constexpr int CPR = D / 8;
+  constexpr int PER = ROWS * CPR / THREADS;
+  static_assert(PER * THREADS == ROWS * CPR && THREADS % 64 == 0, "tile split");
+  const int wave = tid >> 6, lane = tid & 63;
+#pragma unroll
+  for (int u = 0; u < PER; ++u) {
+    const int slot0 = (wave * PER + u) * 64;
+    const int slot = slot0 + lane;
+    const int r = slot / CPR, pch = slot % CPR;
+    const int grow = min(row0 + r, nvalid - 1);
+    const bf16* src = g + (size_t)grow * D + ((pch ^ swz<D>(r)) << 3);
+    __builtin_amdgcn_global_load_lds((const void*)src, (FA_LDS void*)(lds + slot0 * 8), 16, 0, 0);
+  }
+}
+
+// Wait for this wave's outstanding vector-memory operations (including the
+// direct-to-LDS loads above).
+__device__ __forceinline__ void vm_wait_all() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
+
 }  // namespace fa

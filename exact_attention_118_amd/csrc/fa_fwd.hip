@@ -40,26 +40,29 @@ namespace {
 constexpr int kFwdBR = 128;  // query rows per workgroup
 constexpr int kFwdBC = 64;   // keys per K/V tile
 constexpr int kFwdThreads = 256;
+constexpr float kRescaleSlack = 8.f;  // see the online softmax below
 
 template <int D, bool CAUSAL>
-__global__ __launch_bounds__(kFwdThreads, 2) void fwd_bf16_kernel(
-    const bf16* __restrict__ Q, const bf16* __restrict__ K, const bf16* __restrict__ V,
-    bf16* __restrict__ O, float* __restrict__ L, int Nq, int Nk, int nqt, float c, int off) {
+__global__ __launch_bounds__(kFwdThreads, 2) __attribute__((amdgpu_waves_per_eu(2, 2)))
+void fwd_bf16_kernel(const bf16* __restrict__ Q, const bf16* __restrict__ K,
+                     const bf16* __restrict__ V, bf16* __restrict__ O, float* __restrict__ L,
+                     int Nq, int Nk, int nqt, float c, int off) {
   constexpr int BR = kFwdBR, BC = kFwdBC;
-  constexpr int KSTR = D + 8;    // LDS row pitch (elements) of the K tile
-  constexpr int VSTR = D + 16;   // LDS row pitch (elements) of the V tile
-  constexpr int CPR = D / 8;     // 16-byte chunks per row
-  constexpr int NLD = BC * CPR / kFwdThreads;
-  constexpr int NKK = D / 16;    // MFMA k-steps over the head dim
-  constexpr int NNT = D / 32;    // 32-wide output tiles over the head dim
-  static_assert(NLD * kFwdThreads == BC * CPR, "tile load must divide evenly");
+  constexpr int NKK = D / 16;  // MFMA k-steps over the head dim
+  constexpr int NNT = D / 32;  // 32-wide output tiles over the head dim
+  constexpr int TILE = BC * D;  // elements per K or V tile
 
-  __shared__ __attribute__((aligned(16))) bf16 sK[BC * KSTR];
-  __shared__ __attribute__((aligned(16))) bf16 sV[BC * VSTR];
+  constexpr unsigned TB = TILE * 2;  // bytes per tile (a power of two)
+  // K tiles j+1 (read) and j+2 (loading) at buffers 0/1, V tiles j (read) and
+  // j+1 (loading) at buffers 2/3; all swizzled (see swz).
+  __shared__ __attribute__((aligned(1024))) bf16 smem[4 * TILE];
+  bf16* const sK0 = smem;
+  bf16* const sV0 = smem + 2 * TILE;
 
   const int tid = threadIdx.x;
   const int lane = tid & 63, wave = tid >> 6;
   const int half = lane >> 5, l32 = lane & 31;
+  const int g = lane >> 4, s16 = lane & 15;
 
   const int logical = xcd_remap(blockIdx.x, gridDim.x);
   const int bh = logical / nqt;
@@ -67,141 +70,169 @@ __global__ __launch_bounds__(kFwdThreads, 2) void fwd_bf16_kernel(
   const int qt = CAUSAL ? (nqt - 1 - t) : t;
   const int q0 = qt * BR;
   const size_t qbase = (size_t)bh * Nq * D;
-  const size_t kbase = (size_t)bh * Nk * D;
+  const bf16* Kh = K + (size_t)bh * Nk * D;
+  const bf16* Vh = V + (size_t)bh * Nk * D;
 
   // This lane's query row and its Q^T fragments (B operand of S^T = K Q^T).
   const int qrow = q0 + wave * 32 + l32;
   bf16x8 qf[NKK];
 #pragma unroll
-  for (int kk = 0; kk < NKK; ++kk) {
+  for (int kk = 0; kk < NKK; ++kk)
     qf[kk] = (qrow < Nq) ? *(const bf16x8*)(Q + qbase + (size_t)qrow * D + kk * 16 + half * 8)
                          : zero_bf16x8();
-  }
 
   // Keys this workgroup needs: all, or (causal) up to the last row's diagonal.
-  int kend = Nk;
-  if (CAUSAL) kend = min(Nk, q0 + BR + off);
+  const int kend = CAUSAL ? min(Nk, q0 + BR + off) : Nk;
   const int ntiles = (kend + BC - 1) / BC;
   const int wrow_lo = q0 + wave * 32;  // smallest query row of this wave
 
-  bf16x8 kreg[NLD], vreg[NLD];
-  auto gload = [&](int tile) {
-#pragma unroll
-    for (int u = 0; u < NLD; ++u) {
-      const int idx = tid + u * kFwdThreads;
-      const int r = idx / CPR, ch = idx - r * CPR;
-      const int key = tile * BC + r;
-      if (key < Nk) {
-        kreg[u] = *(const bf16x8*)(K + kbase + (size_t)key * D + ch * 8);
-        vreg[u] = *(const bf16x8*)(V + kbase + (size_t)key * D + ch * 8);
-      } else {
-        kreg[u] = zero_bf16x8();
-        vreg[u] = zero_bf16x8();
-      }
-    }
+  // Lane-constant parts of the LDS reads.
+  const int tr_row = (g >> 1) * 4 + (s16 >> 2);      // transpose read: row in a 16-row chunk
+  const int tr_col = (g & 1) * 16 + (s16 & 3) * 4;   // and column in a 32-wide tile
+  // S^T = K Q^T for one K tile: 2 x NKK MFMA steps (step st: key half st & 1,
+  // head-dim chunk st >> 1); the A fragment of step st is K row (st&1)*32 + l32,
+  // columns (st>>1)*16 + half*8 .. +8.
+  const SwzRow<D> krow(l32, half);
+  const SwzTr<D> vtr(tr_row, tr_col);
+  auto kfrag = [&](const SwzRow<D>& kr, int st) {
+    return *at_byte<bf16x8>(sK0, kr.off((st & 1) * 32, (st >> 1) * 2));
   };
-  auto sstore = [&]() {
-#pragma unroll
-    for (int u = 0; u < NLD; ++u) {
-      const int idx = tid + u * kFwdThreads;
-      const int r = idx / CPR, ch = idx - r * CPR;
-      *(bf16x8*)(sK + r * KSTR + ch * 8) = kreg[u];
-      *(bf16x8*)(sV + r * VSTR + ch * 8) = vreg[u];
-    }
+  // O^T += V^T P^T: 4 x NNT steps (step st: 16-key chunk st / NNT, head-dim tile
+  // st % NNT); the A fragment is V^T by two transpose reads.
+  auto vfrag = [&](const SwzTr<D>& vt, int st) {
+    const int rb = (st / NNT) * 16, cb = (st % NNT) * 32;
+    return concat(lds_read_tr(to_lds(at_byte<bf16>(sV0, vt.off(rb, 0, cb)))),
+                  lds_read_tr(to_lds(at_byte<bf16>(sV0, vt.off(rb, 1, cb)))));
   };
+  constexpr int KRING = 4, VRING = 3;
 
-  float m_run = -INFINITY;  // running max of scores * c (log2 domain)
+  float m_run = -INFINITY;  // reference of the exponentials (row max so far, log2 units)
   float l_run = 0.f;        // running sum of this lane half's probabilities
   f32x16 oacc[NNT];
 #pragma unroll
   for (int nt = 0; nt < NNT; ++nt) oacc[nt] = (f32x16){};
 
-  gload(0);
-  sstore();
+  // Prologue: K tiles 0 and 1, V tile 0; scores of tile 0.
+  dma_tile<D, BC, kFwdThreads>(Kh, 0, Nk, sK0, tid);
+  if (ntiles > 1) dma_tile<D, BC, kFwdThreads>(Kh, BC, Nk, sK0 + TILE, tid);
+  dma_tile<D, BC, kFwdThreads>(Vh, 0, Nk, sV0, tid);
+  vm_wait_all();
   __syncthreads();
-
-  // Per-lane constant parts of the LDS addresses.
-  const int g = lane >> 4, s16 = lane & 15;
-  // V^T operand via transpose read: this lane supplies row (s16/4) and
-  // column ((g%2)*16 + (s16%4)*4) of a 4-row block; rows offset by half*4.
-  const int vrow_lane = (g >> 1) * 4 + (s16 >> 2);
-  const int vcol_lane = (g & 1) * 16 + (s16 & 3) * 4;
+  f32x16 snext[2] = {(f32x16){}, (f32x16){}};
+  {
+    bf16x8 ring[KRING];
+#pragma unroll
+    for (int st = 0; st < KRING; ++st) ring[st] = kfrag(krow, st);
+#pragma unroll
+    for (int st = 0; st < 2 * NKK; ++st) {
+      const bf16x8 a = ring[st % KRING];
+      if (st + KRING < 2 * NKK) ring[st % KRING] = kfrag(krow, st + KRING);
+      snext[st & 1] = mfma32(a, qf[st >> 1], snext[st & 1]);
+    }
+  }
+  __syncthreads();  // every wave is done with K tile 0 before tile 2 replaces it
 
   for (int j = 0; j < ntiles; ++j) {
-    if (j + 1 < ntiles) gload(j + 1);
+    // Start loading K tile j+2 (over tile j's buffer, last read for tile j's
+    // scores) and V tile j+1.
+    if (j + 2 < ntiles) dma_tile<D, BC, kFwdThreads>(Kh, (j + 2) * BC, Nk, sK0 + (j & 1) * TILE, tid);
+    if (j + 1 < ntiles)
+      dma_tile<D, BC, kFwdThreads>(Vh, (j + 1) * BC, Nk, sV0 + ((j + 1) & 1) * TILE, tid);
+
     const int k0 = j * BC;
-    const bool wave_idle = CAUSAL && (k0 > wrow_lo + 31 + off);
-    if (!wave_idle) {
-      // S^T tile pair: keys [k0, k0+64) x this wave's 32 rows.
-      f32x16 sacc[2];
-#pragma unroll
-      for (int mt = 0; mt < 2; ++mt) {
-        sacc[mt] = (f32x16){};
-        const bf16* krow = sK + (mt * 32 + l32) * KSTR + half * 8;
-#pragma unroll
-        for (int kk = 0; kk < NKK; ++kk) {
-          const bf16x8 a = *(const bf16x8*)(krow + kk * 16);
-          sacc[mt] = mfma32(a, qf[kk], sacc[mt]);
-        }
-      }
-      const bool need_mask = (k0 + BC > Nk) || (CAUSAL && (k0 + BC - 1 > wrow_lo + off));
-      if (need_mask) {
-#pragma unroll
-        for (int mt = 0; mt < 2; ++mt)
-#pragma unroll
-          for (int i = 0; i < 16; ++i) {
-            const int key = k0 + mt * 32 + (i >> 2) * 8 + half * 4 + (i & 3);
-            const bool vis = (key < Nk) && (!CAUSAL || key <= qrow + off);
-            if (!vis) sacc[mt][i] = -INFINITY;
-          }
-      }
-      // Online softmax (the CSDN post "Flash Attention1" walk-through; deferred normalisation).
-      float mx = -INFINITY;
-#pragma unroll
-      for (int mt = 0; mt < 2; ++mt)
-#pragma unroll
-        for (int i = 0; i < 16; ++i) mx = fmaxf(mx, sacc[mt][i]);
-      mx = fmaxf(mx, wave_shfl_xor(mx, 32));
-      const float m_new = fmaxf(m_run, mx * c);
-      const float m_base = (m_new == -INFINITY) ? 0.f : m_new;
-      const float alpha = fast_exp2(m_run - m_base);
-      float rs = 0.f;
+    f32x16 scur[2] = {snext[0], snext[1]};
+    // Mask keys past the end and, causal, keys after the row's diagonal (only
+    // tiles that cross it); lane holds row qrow, keys k0 + mt*32 + (i/4)*8 +
+    // half*4 + i%4.
+    const bool need_mask = (k0 + BC > Nk) || (CAUSAL && (k0 + BC - 1 > wrow_lo + off));
+    if (need_mask) {
 #pragma unroll
       for (int mt = 0; mt < 2; ++mt)
 #pragma unroll
         for (int i = 0; i < 16; ++i) {
-          const float p = fast_exp2(fmaf(sacc[mt][i], c, -m_base));
-          sacc[mt][i] = p;
-          rs += p;
+          const int key = k0 + mt * 32 + (i >> 2) * 8 + half * 4 + (i & 3);
+          const bool vis = (key < Nk) && (!CAUSAL || key <= qrow + off);
+          if (!vis) scur[mt][i] = -INFINITY;
         }
-      l_run = fmaf(l_run, alpha, rs);
-      m_run = m_new;
+    }
+    // Online softmax (the CSDN post "Flash Attention1", 例子说明: running max
+    // and running sum), normalised once in the epilogue.  The reference m_run
+    // of the exponentials moves to the new row max only when some row of the
+    // wave has grown by more than kRescaleSlack (log2 units); until then
+    // probabilities are taken against the older, smaller reference and stay
+    // below 2^kRescaleSlack, where fp32 sums and bf16 operands keep their full
+    // relative precision.  The result is the same in exact arithmetic, and
+    // most tiles skip rescaling the accumulators.
+    float mx = -INFINITY;
+#pragma unroll
+    for (int mt = 0; mt < 2; ++mt)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) mx = fmaxf(mx, scur[mt][i]);
+    mx = fmaxf(mx, wave_shfl_xor(mx, 32));
+    const float m_tile = mx * c;
+    if (__builtin_amdgcn_ballot_w64(m_tile > m_run + kRescaleSlack) != 0) {
+      const float m_new = fmaxf(m_run, m_tile);
+      const float alpha = fast_exp2(m_run - (m_new == -INFINITY ? 0.f : m_new));
+      l_run *= alpha;
 #pragma unroll
       for (int nt = 0; nt < NNT; ++nt) oacc[nt] *= alpha;
+      m_run = m_new;
+    }
+    const float m_ref = (m_run == -INFINITY) ? 0.f : m_run;
 
-      // P^T fragments for the four 16-key chunks (B operand of O^T = V^T P^T).
-      bf16x8 pf[4];
+    // Scores of tile j+1 on the MFMA pipe, interleaved step by step with the
+    // exponentials of tile j on the vector ALU.  Step st converts the pair of
+    // probabilities pf[st/4][2*(st%4) .. +1] (keys of chunk st/4).  The last
+    // iteration also computes scores, of a stale buffer, and discards them:
+    // one extra tile of S per workgroup keeps this block free of branches, so
+    // the two kinds of work stay interleaved.
+    bf16x8 pf[4];
+    float rs0 = 0.f, rs1 = 0.f;
+    {
+      const SwzRow<D> kr = krow.flipped(((j + 1) & 1) * TB);
+      bf16x8 ring[KRING];
+      snext[0] = (f32x16){};
+      snext[1] = (f32x16){};
 #pragma unroll
-      for (int kc = 0; kc < 4; ++kc)
+      for (int st = 0; st < KRING; ++st) ring[st] = kfrag(kr, st);
 #pragma unroll
-        for (int e = 0; e < 8; ++e) pf[kc][e] = (bf16)sacc[kc >> 1][(kc & 1) * 8 + e];
-
+      for (int st = 0; st < 2 * NKK; ++st) {
+        const bf16x8 a = ring[st % KRING];
+        if (st + KRING < 2 * NKK) ring[st % KRING] = kfrag(kr, st + KRING);
+        snext[st & 1] = mfma32(a, qf[st >> 1], snext[st & 1]);
 #pragma unroll
-      for (int nt = 0; nt < NNT; ++nt) {
-#pragma unroll
-        for (int kc = 0; kc < 4; ++kc) {
-          const bf16* vp = sV + (kc * 16 + vrow_lane) * VSTR + nt * 32 + vcol_lane;
-          const bf16x4 lo = lds_read_tr(to_lds(vp));
-          const bf16x4 hi = lds_read_tr(to_lds(vp + 8 * VSTR));
-          oacc[nt] = mfma32(concat(lo, hi), pf[kc], oacc[nt]);
+        for (int h = 0; h < 32 / (2 * NKK); h += 2) {
+          const int el = st * (32 / (2 * NKK)) + h;  // probability index 0..31
+          const int kc = el >> 3, e = el & 7;
+          const int mt = kc >> 1, i = (kc & 1) * 8 + e;
+          const float p0 = fast_exp2(fmaf(scur[mt][i], c, -m_ref));
+          const float p1 = fast_exp2(fmaf(scur[mt][i + 1], c, -m_ref));
+          rs0 += p0;
+          rs1 += p1;
+          pf[kc][e] = (bf16)p0;
+          pf[kc][e + 1] = (bf16)p1;
         }
+        __builtin_amdgcn_sched_barrier(0);
       }
     }
-    __syncthreads();
-    if (j + 1 < ntiles) {
-      sstore();
-      __syncthreads();
+    l_run += rs0 + rs1;
+
+    // O^T += V^T P^T for tile j.
+    {
+      const SwzTr<D> vt = vtr.flipped((j & 1) * TB);
+      bf16x8 ring[VRING];
+#pragma unroll
+      for (int st = 0; st < VRING; ++st) ring[st] = vfrag(vt, st);
+#pragma unroll
+      for (int st = 0; st < 4 * NNT; ++st) {
+        const bf16x8 a = ring[st % VRING];
+        if (st + VRING < 4 * NNT) ring[st % VRING] = vfrag(vt, st + VRING);
+        oacc[st % NNT] = mfma32(a, pf[st / NNT], oacc[st % NNT]);
+        __builtin_amdgcn_sched_barrier(0);
+      }
     }
+    vm_wait_all();  // this wave's part of tiles K j+2 and V j+1 has landed
+    __syncthreads();
   }
 
   // Epilogue: O = O_acc / l, L = (m + log2 l) * ln 2.
