@@ -53,11 +53,14 @@ namespace fa {
 
 namespace {
 
-// D_i = sum_k dO_ik O_ik in fp32.
+// D_i = sum_k dO_ik O_ik in fp32, and L2_i = L_i * log2(e) (the exponent
+// base of the kernels below).
 template <int D, typename T>
 __global__ __launch_bounds__(256) void bwd_pre_kernel(const T* __restrict__ O,
                                                       const T* __restrict__ dO,
-                                                      float* __restrict__ Dvec, long rows) {
+                                                      const float* __restrict__ L,
+                                                      float* __restrict__ Dvec,
+                                                      float* __restrict__ L2, long rows) {
   constexpr int TPR = D / 8;  // threads per row, 8 elements each
   constexpr int RPB = 256 / TPR;
   const long row = (long)blockIdx.x * RPB + threadIdx.x / TPR;
@@ -70,7 +73,10 @@ __global__ __launch_bounds__(256) void bwd_pre_kernel(const T* __restrict__ O,
   }
 #pragma unroll
   for (int msk = TPR / 2; msk >= 1; msk >>= 1) acc += __shfl_xor(acc, msk, 64);
-  if (row < rows && part == 0) Dvec[row] = acc;
+  if (row < rows && part == 0) {
+    Dvec[row] = acc;
+    L2[row] = L[row] * kLog2e;
+  }
 }
 
 // ---------------------------------------------------------------------------
@@ -81,25 +87,31 @@ constexpr int kKvWaves = 8;
 constexpr int kKvThreads = kKvWaves * 64;
 
 template <int D, bool CAUSAL>
-__global__ __launch_bounds__(kKvThreads, 1) void bwd_dkdv_bf16_kernel(
-    const bf16* __restrict__ Q, const bf16* __restrict__ K, const bf16* __restrict__ V,
-    const float* __restrict__ L, const bf16* __restrict__ dO, const float* __restrict__ Dvec,
-    bf16* __restrict__ dK, bf16* __restrict__ dV, int Nq, int Nk, int nkt, int BH, int hpx,
-    float c, float scale, int off) {
+__global__ __launch_bounds__(kKvThreads, 1) __attribute__((amdgpu_waves_per_eu(2, 2)))
+void bwd_dkdv_bf16_kernel(const bf16* __restrict__ Q, const bf16* __restrict__ K,
+                          const bf16* __restrict__ V, const float* __restrict__ L2vec,
+                          const bf16* __restrict__ dO, const float* __restrict__ Dvec,
+                          bf16* __restrict__ dK, bf16* __restrict__ dV, int Nq, int Nk, int nkt,
+                          int BH, int hpx, float c, float scale, int off) {
   constexpr int BC = kKvBC, BR = kKvBR;
-  constexpr int KSTR = D + 8;     // LDS pitch of the K block (elements)
-  constexpr int QSTR = D + 16;    // LDS pitch of the Q and dO tiles
-  constexpr int CPR = D / 8;      // 16-byte chunks per row
-  constexpr int NKK = D / 16;     // MFMA k-steps over the head dim
-  constexpr int NNT = D / 32;     // 32-wide tiles over the head dim
-  constexpr int NQL = 2 * BR * CPR / kKvThreads;  // 16-byte loads per thread per query block
-  static_assert(NQL * kKvThreads == 2 * BR * CPR, "query block load must divide evenly");
+  constexpr int CPR = D / 8;     // 16-byte chunks per row
+  constexpr int NKK = D / 16;    // MFMA k-steps over the head dim
+  constexpr int NNT = D / 32;    // 32-wide tiles over the head dim
+  constexpr int KTILE = BC * D;  // elements of the K block
+  constexpr int QTILE = BR * D;  // elements of one Q or dO tile
+  constexpr unsigned QB = QTILE * 2;           // bytes of one Q or dO tile (a power of two)
+  constexpr int NIQ = BR * CPR / 64;           // direct-to-LDS instructions per Q (or dO) tile
+  constexpr int IPW = 2 * NIQ / kKvWaves;      // ... per wave for both tiles
+  static_assert(IPW * kKvWaves == 2 * NIQ && IPW >= 1, "query tile load split");
+  static_assert(2 * BR == 64, "one dword load per lane carries L2 and D of a block");
 
-  __shared__ __attribute__((aligned(16))) bf16 sK[BC * KSTR];
-  __shared__ __attribute__((aligned(16))) bf16 sQ[2][BR * QSTR];
-  __shared__ __attribute__((aligned(16))) bf16 sdO[2][BR * QSTR];
-  __shared__ __attribute__((aligned(16))) float sL2[2][BR];
-  __shared__ __attribute__((aligned(16))) float sD[2][BR];
+  // [K block | Q buffers 0,1 | dO buffers 0,1], all swizzled (see swz); L2 and
+  // D of the query block per buffer.
+  __shared__ __attribute__((aligned(1024))) bf16 smem[KTILE + 4 * QTILE];
+  __shared__ __attribute__((aligned(16))) float sLD[2][2 * BR];
+  bf16* const sK = smem;
+  bf16* const sQ0 = smem + KTILE;
+  bf16* const sdO0 = smem + KTILE + 2 * QTILE;
 
   const int tid = threadIdx.x;
   const int lane = tid & 63, wave = tid >> 6;
@@ -122,135 +134,143 @@ __global__ __launch_bounds__(kKvThreads, 1) void bwd_dkdv_bf16_kernel(
   const size_t kbase = (size_t)bh * Nk * D;
   const size_t lbase = (size_t)bh * Nq;
 
-  // K block -> LDS; this wave's V rows -> registers (B operand of dP = dO V^T).
-  for (int idx = tid; idx < BC * CPR; idx += kKvThreads) {
-    const int r = idx / CPR, ch = idx - r * CPR;
-    const int key = k0 + r;
-    *(bf16x8*)(sK + r * KSTR + ch * 8) =
-        (key < Nk) ? *(const bf16x8*)(K + kbase + (size_t)key * D + ch * 8) : zero_bf16x8();
-  }
+  // Query blocks that can see any key of this workgroup.
+  const int nqb = (Nq + BR - 1) / BR;
+  const int qb_first = CAUSAL ? max(0, k0 - off) / BR : 0;
+  const int nloop = nqb - qb_first;
+
+  // Q and dO rows of query block qb into buffer buf (direct-to-LDS,
+  // swizzled), and its L2 and D (one dword per lane of the last wave).
+  auto load_block = [&](int qb, int buf) {
+    const int qi0 = qb * BR;
+#pragma unroll
+    for (int u = 0; u < IPW; ++u) {
+      const int gi = wave * IPW + u;
+      const int tsel = gi / NIQ;  // 0: Q, 1: dO
+      const int slot0 = (gi - tsel * NIQ) * 64;
+      const int slot = slot0 + lane;
+      const int r = slot / CPR, pch = slot % CPR;
+      const int q = min(qi0 + r, Nq - 1);
+      const bf16* src = (tsel ? dO : Q) + qbase + (size_t)q * D + ((pch ^ swz<D>(r)) << 3);
+      bf16* dst = (tsel ? sdO0 : sQ0) + buf * QTILE + slot0 * 8;
+      __builtin_amdgcn_global_load_lds((const void*)src, (FA_LDS void*)dst, 16, 0, 0);
+    }
+    if (wave == kKvWaves - 1) {
+      const int q = min(qi0 + (lane & (BR - 1)), Nq - 1);
+      const float* src = (lane < BR ? L2vec : Dvec) + lbase + q;
+      __builtin_amdgcn_global_load_lds((const void*)src, (FA_LDS void*)&sLD[buf][0], 4, 0, 0);
+    }
+  };
+
+  // K block (rows clamped to Nk - 1) and the first query block.
+  dma_tile<D, BC, kKvThreads>(K + kbase, k0, Nk, sK, tid);
+  if (nloop > 0) load_block(qb_first, 0);
+  // This wave's V rows in registers (B operand of dP = dO V^T).
   bf16x8 vf[NKK];
 #pragma unroll
   for (int kk = 0; kk < NKK; ++kk)
     vf[kk] = (mykey < Nk) ? *(const bf16x8*)(V + kbase + (size_t)mykey * D + kk * 16 + half * 8)
                           : zero_bf16x8();
-
   f32x16 dkacc[NNT], dvacc[NNT];
 #pragma unroll
   for (int nt = 0; nt < NNT; ++nt) {
     dkacc[nt] = (f32x16){};
     dvacc[nt] = (f32x16){};
   }
-
-  // Query blocks that can see any key of this workgroup.
-  const int nqb = (Nq + BR - 1) / BR;
-  const int qb_first = CAUSAL ? max(0, k0 - off) / BR : 0;
-  const int nloop = nqb - qb_first;
-
-  bf16x8 stage[NQL];
-  float lstage = 0.f;
-  auto gload = [&](int qb) {
-    const int qi0 = qb * BR;
-#pragma unroll
-    for (int u = 0; u < NQL; ++u) {
-      const int idx = tid + u * kKvThreads;
-      const int tsel = idx / (BR * CPR);  // 0: Q, 1: dO (uniform per wave)
-      const int rem = idx - tsel * (BR * CPR);
-      const int r = rem / CPR, ch = rem - r * CPR;
-      const int q = qi0 + r;
-      const bf16* src = tsel ? dO : Q;
-      stage[u] = (q < Nq) ? *(const bf16x8*)(src + qbase + (size_t)q * D + ch * 8) : zero_bf16x8();
-    }
-    if (tid < 2 * BR) {
-      const int q = qi0 + (tid & (BR - 1));
-      if (tid < BR) lstage = (q < Nq) ? L[lbase + q] * kLog2e : INFINITY;
-      else lstage = (q < Nq) ? Dvec[lbase + q] : 0.f;
-    }
-  };
-  auto sstore = [&](int buf) {
-#pragma unroll
-    for (int u = 0; u < NQL; ++u) {
-      const int idx = tid + u * kKvThreads;
-      const int tsel = idx / (BR * CPR);
-      const int rem = idx - tsel * (BR * CPR);
-      const int r = rem / CPR, ch = rem - r * CPR;
-      bf16* dst = tsel ? sdO[buf] : sQ[buf];
-      *(bf16x8*)(dst + r * QSTR + ch * 8) = stage[u];
-    }
-    if (tid < BR) sL2[buf][tid] = lstage;
-    else if (tid < 2 * BR) sD[buf][tid - BR] = lstage;
-  };
-
-  if (nloop > 0) {
-    gload(qb_first);
-    sstore(0);
-  }
+  vm_wait_all();
   __syncthreads();
 
-  // Lane-constant parts of the transpose-read addresses (see lds_read_tr).
   const int tr_row = (g >> 1) * 4 + (s16 >> 2);
   const int tr_col = (g & 1) * 16 + (s16 & 3) * 4;
+  const SwzRow<D> qrow_sw(l32, half);  // Q / dO rows l32 of a block
+  const SwzRow<D> krow_sw(SwzRow<D>(l32, half).x + (unsigned)(wave * 64 * D));  // K rows kw0 - k0 + l32
+  const SwzTr<D> tr_sw(tr_row, tr_col);
 
   for (int it = 0; it < nloop; ++it) {
     const int buf = it & 1;
     const int qi0 = (qb_first + it) * BR;
-    if (it + 1 < nloop) gload(qb_first + it + 1);
+    if (it + 1 < nloop) load_block(qb_first + it + 1, buf ^ 1);
 
-    const bf16* tQ = sQ[buf];
-    const bf16* tdO = sdO[buf];
     // Causal: a wave whose keys all lie after every row of the block has no work.
     const bool wave_idle = CAUSAL && (kw0 > qi0 + BR - 1 + off);
     if (!wave_idle) {
-      // S = Q K^T and dP = dO V^T: 32 rows x this wave's 32 keys.
+      const SwzRow<D> qs = qrow_sw.flipped(buf * QB);
+      const SwzTr<D> ts = tr_sw.flipped(buf * QB);
+      const float* tLD = sLD[buf];
+      // S = Q K^T and dP = dO V^T: 32 rows x this wave's 32 keys.  Step kk
+      // needs the Q, K and dO fragments of head-dim chunk kk; those of step
+      // kk + 1 are read before step kk's MFMAs are issued.
       f32x16 sacc = (f32x16){}, dpacc = (f32x16){};
-      const bf16* qrow = tQ + l32 * QSTR + half * 8;
-      const bf16* dorow = tdO + l32 * QSTR + half * 8;
-      const bf16* krow = sK + (wave * 32 + l32) * KSTR + half * 8;
+      {
+        auto ldstep = [&](int kk, bf16x8* f) {
+          f[0] = *at_byte<bf16x8>(sQ0, qs.off(0, kk * 2));
+          f[1] = *at_byte<bf16x8>(sK, krow_sw.off(0, kk * 2));
+          f[2] = *at_byte<bf16x8>(sdO0, qs.off(0, kk * 2));
+        };
+        bf16x8 fa[3], fb[3];
+        ldstep(0, fa);
 #pragma unroll
-      for (int kk = 0; kk < NKK; ++kk) {
-        sacc = mfma32(*(const bf16x8*)(qrow + kk * 16), *(const bf16x8*)(krow + kk * 16), sacc);
-        dpacc = mfma32(*(const bf16x8*)(dorow + kk * 16), vf[kk], dpacc);
+        for (int kk = 0; kk < NKK; ++kk) {
+          bf16x8* cur = (kk & 1) ? fb : fa;
+          bf16x8* nxt = (kk & 1) ? fa : fb;
+          if (kk + 1 < NKK) ldstep(kk + 1, nxt);
+          sacc = mfma32(cur[0], cur[1], sacc);
+          dpacc = mfma32(cur[2], vf[kk], dpacc);
+          __builtin_amdgcn_sched_barrier(0);
+        }
       }
       const bool need_mask =
           (qi0 + BR > Nq) || (kw0 + 32 > Nk) || (CAUSAL && (kw0 + 31 > qi0 + off));
-      // P = exp2(S*c - L*log2e) and dS = P * (dP - D); lane holds key mykey and
-      // rows (i/4)*8 + half*4 + i%4 of the block.
+      // P = exp2(S*c - L2) and dS = P * (dP - D) for the 8 rows of chunk kc
+      // (elements i = kc*8 .. kc*8+7); lane holds key mykey and rows
+      // (i/4)*8 + half*4 + i%4 of the block.
       bf16x8 pf[2], dsf[2];
+      auto pds = [&](int kc, int i) {
+        const int i4 = i >> 2, e = i & 3;
+        const int ql = i4 * 8 + half * 4 + e;
+        float p = fast_exp2(fmaf(sacc[i], c, -tLD[ql]));
+        if (need_mask) {
+          const int q = qi0 + ql;
+          const bool vis = (q < Nq) && (mykey < Nk) && (!CAUSAL || mykey <= q + off);
+          if (!vis) p = 0.f;
+        }
+        const float ds = p * (dpacc[i] - tLD[BR + ql]);
+        pf[kc][(i4 & 1) * 4 + e] = (bf16)p;
+        dsf[kc][(i4 & 1) * 4 + e] = (bf16)ds;
+      };
+      // dV^T += dO^T P and dK^T += Q^T dS over the 16 rows of chunk kc
+      // (2 * NNT MFMAs, A operands by transpose reads); with `overlap`, the
+      // probabilities of chunk kc + 1 are computed between them.
+      auto dvdk = [&](int kc, bool overlap) {
+        auto afrag = [&](int st) {  // st: (head-dim tile st/2, dO^T if even else Q^T)
+          const bf16* base = (st & 1) ? sQ0 : sdO0;
+          const int cb = (st >> 1) * 32;
+          return concat(lds_read_tr(to_lds(at_byte<bf16>(base, ts.off(kc * 16, 0, cb)))),
+                        lds_read_tr(to_lds(at_byte<bf16>(base, ts.off(kc * 16, 1, cb)))));
+        };
+        constexpr int NS = 2 * NNT, RING = 2;
+        bf16x8 ring[RING];
 #pragma unroll
-      for (int i4 = 0; i4 < 4; ++i4) {
-        const int ql = i4 * 8 + half * 4;
-        const float4 l2 = *(const float4*)(sL2[buf] + ql);
-        const float4 dd = *(const float4*)(sD[buf] + ql);
-        const float l2v[4] = {l2.x, l2.y, l2.z, l2.w};
-        const float ddv[4] = {dd.x, dd.y, dd.z, dd.w};
+        for (int st = 0; st < RING; ++st) ring[st] = afrag(st);
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const int i = i4 * 4 + e;
-          float p = fast_exp2(fmaf(sacc[i], c, -l2v[e]));
-          if (need_mask) {
-            const int q = qi0 + ql + e;
-            const bool vis = (q < Nq) && (mykey < Nk) && (!CAUSAL || mykey <= q + off);
-            if (!vis) p = 0.f;
+        for (int st = 0; st < NS; ++st) {
+          const bf16x8 a = ring[st % RING];
+          if (st + RING < NS) ring[st % RING] = afrag(st + RING);
+          if (st & 1) dkacc[st >> 1] = mfma32(a, dsf[kc], dkacc[st >> 1]);
+          else dvacc[st >> 1] = mfma32(a, pf[kc], dvacc[st >> 1]);
+          if (overlap) {
+#pragma unroll
+            for (int h = 0; h < 8 / NS; ++h) pds(kc + 1, (kc + 1) * 8 + st * (8 / NS) + h);
           }
-          const float ds = p * (dpacc[i] - ddv[e]);
-          pf[i4 >> 1][(i4 & 1) * 4 + e] = (bf16)p;
-          dsf[i4 >> 1][(i4 & 1) * 4 + e] = (bf16)ds;
+          __builtin_amdgcn_sched_barrier(0);
         }
-      }
-      // dV^T += dO^T P and dK^T += Q^T dS (A operands by LDS transpose reads).
+      };
 #pragma unroll
-      for (int nt = 0; nt < NNT; ++nt) {
-#pragma unroll
-        for (int kc = 0; kc < 2; ++kc) {
-          const int o = (kc * 16 + tr_row) * QSTR + nt * 32 + tr_col;
-          const bf16x8 a_do = concat(lds_read_tr(to_lds(tdO + o)), lds_read_tr(to_lds(tdO + o + 8 * QSTR)));
-          dvacc[nt] = mfma32(a_do, pf[kc], dvacc[nt]);
-          const bf16x8 a_q = concat(lds_read_tr(to_lds(tQ + o)), lds_read_tr(to_lds(tQ + o + 8 * QSTR)));
-          dkacc[nt] = mfma32(a_q, dsf[kc], dkacc[nt]);
-        }
-      }
+      for (int i = 0; i < 8; ++i) pds(0, i);
+      dvdk(0, true);   // probabilities of rows 16..31 overlap the MFMAs of rows 0..15
+      dvdk(1, false);
     }
-    if (it + 1 < nloop) sstore(buf ^ 1);
+    vm_wait_all();  // this wave's part of the next query block has landed
     __syncthreads();
   }
 
@@ -554,7 +574,7 @@ hipError_t launch_pre(const BwdArgs& a, hipStream_t s) {
   const long nb = (rows + RPB - 1) / RPB;
   if (nb == 0) return hipSuccess;
   hipLaunchKernelGGL((bwd_pre_kernel<D, T>), dim3((unsigned)nb), dim3(256), 0, s,
-                     (const T*)a.O, (const T*)a.dO, a.Dvec, rows);
+                     (const T*)a.O, (const T*)a.dO, a.L, a.Dvec, a.L2, rows);
   return hipGetLastError();
 }
 
@@ -578,7 +598,7 @@ hipError_t launch_bwd_bf16(const BwdArgs& a, int stages, hipStream_t s) {
     const int hpx = (BH % kNumXcd == 0) ? BH / kNumXcd : 0;
 #define FA_DKDV_LAUNCH(DD, CC)                                                                  \
   hipLaunchKernelGGL((bwd_dkdv_bf16_kernel<DD, CC>), dim3(nblocks), dim3(kKvThreads), 0, s, Q, K, \
-                     V, a.L, dO, a.Dvec, (bf16*)a.dK, (bf16*)a.dV, a.Nq, a.Nk, nkt, BH, hpx, c,  \
+                     V, a.L2, dO, a.Dvec, (bf16*)a.dK, (bf16*)a.dV, a.Nq, a.Nk, nkt, BH, hpx, c, \
                      a.scale, off)
     if (a.d == 128) {
       if (a.causal) FA_DKDV_LAUNCH(128, true); else FA_DKDV_LAUNCH(128, false);

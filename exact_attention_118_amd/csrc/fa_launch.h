@@ -32,7 +32,8 @@ struct BwdArgs {
   int B, H, Nq, Nk, d;
   float scale;
   bool causal;
-  float* Dvec;  // [B*H*Nq] fp32 scratch (workspace)
+  float* Dvec;  // [B*H*Nq] fp32 scratch (workspace): D = rowsum(dO * O)
+  float* L2;    // [B*H*Nq] fp32 scratch (workspace): L * log2(e)
 };
 
 // Tiled forward (Q-tile per workgroup, K/V streamed through LDS).
@@ -44,8 +45,8 @@ hipError_t launch_fwd_f32(const FwdArgs& a, hipStream_t s);
 hipError_t launch_fwd_split_bf16(const FwdArgs& a, int splits, float* part_o, float* part_l,
                                  hipStream_t s);
 
-// Backward: D = rowsum(dO*O); dK and dV; dQ.
-// `stages`: bit 1 D, bit 2 dK/dV kernel, bit 4 dQ kernel (2 and 4 read D).
+// Backward: D = rowsum(dO*O) and L*log2(e); dK and dV; dQ.
+// `stages`: bit 1 D and L2, bit 2 dK/dV kernel, bit 4 dQ kernel (2 and 4 read them).
 hipError_t launch_bwd_bf16(const BwdArgs& a, int stages, hipStream_t s);
 hipError_t launch_bwd_f32(const BwdArgs& a, int stages, hipStream_t s);
 

@@ -86,8 +86,8 @@ fa_status fa_fwd(const void* Q, const void* K, const void* V, void* O, float* L,
  *
  *  Q, K, V, O (from fa_fwd), L (from fa_fwd), dO: read.  dQ [B,H,Nq,d],
  *  dK, dV [B,H,Nk,d]: overwritten, every element (not accumulated into).
- *  workspace: fa_bwd_workspace_size() bytes of device memory (D, [B,H,Nq]
- *  fp32), written by the first stage.  dK and dV are computed per key block and
+ *  workspace: fa_bwd_workspace_size() bytes of device memory (D and
+ *  L*log2(e), each [B,H,Nq] fp32), written by the first stage.  dK and dV are computed per key block and
  *  dQ per query block by a second kernel that recomputes P and dP, so there
  *  are no atomic operations and every output is deterministic.
  */
@@ -99,9 +99,9 @@ fa_status fa_bwd(const void* Q, const void* K, const void* V, const void* O, con
 /*
  * The backward pass as its three launches, for callers that schedule or time
  * them separately.  Same arguments as fa_bwd plus `stages`, a bit mask:
- *   FA_BWD_PREPROCESS (1): D = rowsum(dO * O) into the workspace;
- *   FA_BWD_DKDV       (2): dK and dV written (reads D);
- *   FA_BWD_DQ         (4): dQ written (reads D).
+ *   FA_BWD_PREPROCESS (1): D = rowsum(dO * O) and L*log2(e) into the workspace;
+ *   FA_BWD_DKDV       (2): dK and dV written (reads the workspace);
+ *   FA_BWD_DQ         (4): dQ written (reads the workspace).
  * fa_bwd(...) is fa_bwd_stages(..., FA_BWD_ALL).  Stages 2 and 4 need stage 1
  * to have run on the same workspace; a mask of 0 or above 7 returns
  * FA_ERR_UNSUPPORTED.

@@ -126,10 +126,10 @@ def test_bwd_rejects_bad_arguments(lib):
 
 def test_workspace_queries(lib):
     B, H, N, d = 2, 3, 100, 128
-    # backward: D [B,H,N] fp32, padded to 256 bytes
+    # backward: D and L*log2(e), each [B,H,N] fp32 padded to 256 bytes
     def up(x):
         return (x + 255) // 256 * 256
-    assert lib.fa_bwd_workspace_size(B, H, N, N, d, fa.FA_BF16) == up(B * H * N * 4)
+    assert lib.fa_bwd_workspace_size(B, H, N, N, d, fa.FA_BF16) == 2 * up(B * H * N * 4)
     # tiled forward needs none; the split path holds per-split outputs and logsumexps
     assert lib.fa_fwd_workspace_size(B, H, N, N, d, fa.FA_BF16, 0) == 0
     assert lib.fa_fwd_num_splits(B, H, N, N, d, fa.FA_BF16, 0) == 1
