@@ -29,7 +29,9 @@ fa_status check_dims(int B, int H, int Nq, int Nk, int d, float scale, int causa
   if (!dtype_ok(dtype)) return FA_ERR_UNSUPPORTED;
   if (B < 0 || H < 0 || Nq < 0 || Nk < 0) return FA_ERR_SHAPE;
   if (d != 64 && d != 128) return FA_ERR_UNSUPPORTED;
-  if (!std::isfinite(scale) || scale < 0.f) return FA_ERR_UNSUPPORTED;
+  // The kernels mask a score by setting it to -inf before it is multiplied by
+  // scale, which needs a positive, finite multiplier.
+  if (!std::isfinite(scale) || !(scale > 0.f)) return FA_ERR_UNSUPPORTED;
   const long long bh = (long long)B * H;
   if (bh > INT_MAX) return FA_ERR_SHAPE;
   // every workgroup count below is at most bh * ceil(N / 64) and must fit in int

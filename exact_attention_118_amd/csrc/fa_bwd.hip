@@ -41,11 +41,13 @@
 //    transposed, S^T = K Q^T and dP^T = V dO^T, so each lane holds one query
 //    row and its L and D are scalars; dS^T feeds dQ^T = K^T dS^T from
 //    registers, with K^T read from the K tile by the transpose read.  K and V
-//    tiles of 64 keys are staged in LDS with a register prefetch of the next.
+//    tiles of 64 keys are loaded straight into LDS (swizzled, double-buffered).
 //  * Grids: the key-block grid pins heads to XCDs when B*H is a multiple of 8
 //    (a head's workgroups then share one L2 for their re-reads of Q and dO)
-//    and dispatches key blocks in order of decreasing work; the query-block
-//    grid uses the forward pass's mapping.
+//    and dispatches key blocks in order of decreasing work, which with one
+//    workgroup per CU already balances the causal triangle; the query-block
+//    grid uses the forward pass's mapping, causal query tiles in pairs
+//    (t, nqt-1-t) of equal total work.
 #include "fa_common.h"
 #include "fa_launch.h"
 
@@ -219,21 +221,25 @@ void bwd_dkdv_bf16_kernel(const bf16* __restrict__ Q, const bf16* __restrict__ K
           __builtin_amdgcn_sched_barrier(0);
         }
       }
-      const bool need_mask =
-          (qi0 + BR > Nq) || (kw0 + 32 > Nk) || (CAUSAL && (kw0 + 31 > qi0 + off));
+      // Lane holds key mykey and rows (i/4)*8 + half*4 + i%4 of the block.
+      // Rows past the end and, causal, rows before the key's diagonal get
+      // score -inf, hence P = 0 and dS = 0 (only blocks that cross the
+      // diagonal or an end need it).
+      if ((qi0 + BR > Nq) || (kw0 + 32 > Nk) || (CAUSAL && (kw0 + 31 > qi0 + off))) {
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+          const int q = qi0 + (i >> 2) * 8 + half * 4 + (i & 3);
+          const bool vis = (q < Nq) && (mykey < Nk) && (!CAUSAL || mykey <= q + off);
+          if (!vis) sacc[i] = -INFINITY;
+        }
+      }
       // P = exp2(S*c - L2) and dS = P * (dP - D) for the 8 rows of chunk kc
-      // (elements i = kc*8 .. kc*8+7); lane holds key mykey and rows
-      // (i/4)*8 + half*4 + i%4 of the block.
+      // (elements i = kc*8 .. kc*8+7).
       bf16x8 pf[2], dsf[2];
       auto pds = [&](int kc, int i) {
         const int i4 = i >> 2, e = i & 3;
         const int ql = i4 * 8 + half * 4 + e;
-        float p = fast_exp2(fmaf(sacc[i], c, -tLD[ql]));
-        if (need_mask) {
-          const int q = qi0 + ql;
-          const bool vis = (q < Nq) && (mykey < Nk) && (!CAUSAL || mykey <= q + off);
-          if (!vis) p = 0.f;
-        }
+        const float p = fast_exp2(fmaf(sacc[i], c, -tLD[ql]));
         const float ds = p * (dpacc[i] - tLD[BR + ql]);
         pf[kc][(i4 & 1) * 4 + e] = (bf16)p;
         dsf[kc][(i4 & 1) * 4 + e] = (bf16)ds;
@@ -261,6 +267,8 @@ void bwd_dkdv_bf16_kernel(const bf16* __restrict__ Q, const bf16* __restrict__ K
           if (overlap) {
 #pragma unroll
             for (int h = 0; h < 8 / NS; ++h) pds(kc + 1, (kc + 1) * 8 + st * (8 / NS) + h);
+            pin(pf[kc + 1]);
+            pin(dsf[kc + 1]);
           }
           __builtin_amdgcn_sched_barrier(0);
         }
@@ -324,142 +332,150 @@ void bwd_dq_bf16_kernel(const bf16* __restrict__ Q, const bf16* __restrict__ K,
   const int half = lane >> 5, l32 = lane & 31;
   const int g = lane >> 4, s16 = lane & 15;
 
+  // Causal: one workgroup per pair of query tiles (t, nqt-1-t), taken in
+  // turn, so that every workgroup carries the same number of key tiles.
+  const int nwg = CAUSAL ? (nqt + 1) / 2 : nqt;  // workgroups per head
   const int logical = xcd_remap(blockIdx.x, gridDim.x);
-  const int bh = logical / nqt;
-  const int t = logical - bh * nqt;
-  const int qt = CAUSAL ? (nqt - 1 - t) : t;
-  const int q0 = qt * BR;
+  const int bh = logical / nwg;
+  const int t = logical - bh * nwg;
   const size_t qbase = (size_t)bh * Nq * D;
   const bf16* Kh = K + (size_t)bh * Nk * D;
   const bf16* Vh = V + (size_t)bh * Nk * D;
 
-  // This lane's query row: Q^T and dO^T fragments (B operands), L and D.
-  const int qrow = q0 + wave * 32 + l32;
-  bf16x8 qf[NKK], dof[NKK];
-#pragma unroll
-  for (int kk = 0; kk < NKK; ++kk) {
-    const size_t o = qbase + (size_t)qrow * D + kk * 16 + half * 8;
-    qf[kk] = (qrow < Nq) ? *(const bf16x8*)(Q + o) : zero_bf16x8();
-    dof[kk] = (qrow < Nq) ? *(const bf16x8*)(dO + o) : zero_bf16x8();
-  }
-  const float l2 = (qrow < Nq) ? L[(size_t)bh * Nq + qrow] * kLog2e : INFINITY;
-  const float drow = (qrow < Nq) ? Dvec[(size_t)bh * Nq + qrow] : 0.f;
+  for (int pass = 0; pass < (CAUSAL ? 2 : 1); ++pass) {
+    const int qt = !CAUSAL ? t : (pass == 0 ? nqt - 1 - t : t);
+    if (CAUSAL && pass == 1 && t == nqt - 1 - t) break;  // odd count: the middle tile once
+    if (pass == 1) __syncthreads();  // the first tile's last LDS reads precede the new loads
+    const int q0 = qt * BR;
 
-  const int kend = CAUSAL ? min(Nk, q0 + BR + off) : Nk;
-  const int ntiles = (kend + BC - 1) / BC;
-  const int wrow_lo = q0 + wave * 32;
-
-  const int tr_row = (g >> 1) * 4 + (s16 >> 2);
-  const int tr_col = (g & 1) * 16 + (s16 & 3) * 4;
-  // S^T and dP^T for one 32-key half mt: 2 x NKK steps alternating the K
-  // (even step, S^T) and V (odd step, dP^T) row fragments.
-  const SwzRow<D> rowsw(l32, half);
-  const SwzTr<D> trsw(tr_row, tr_col);
-  auto sfrag = [&](const SwzRow<D>& rs, int mt, int st) {
-    const bf16* base = (st & 1) ? sV0 : sK0;
-    return *at_byte<bf16x8>(base, rs.off(mt * 32, (st >> 1) * 2));
-  };
-  // dQ^T += K^T dS^T for one 32-key half mt: 2 x NNT steps (16-key chunk
-  // kc = st / NNT of the half, head-dim tile st % NNT); K^T by transpose reads.
-  auto kt_frag = [&](const SwzTr<D>& ts, int mt, int st) {
-    const int rb = mt * 32 + (st / NNT) * 16, cb = (st % NNT) * 32;
-    return concat(lds_read_tr(to_lds(at_byte<bf16>(sK0, ts.off(rb, 0, cb)))),
-                  lds_read_tr(to_lds(at_byte<bf16>(sK0, ts.off(rb, 1, cb)))));
-  };
-  constexpr int SRING = 4, TRING = 3;
-
-  f32x16 dqacc[NNT];
-#pragma unroll
-  for (int nt = 0; nt < NNT; ++nt) dqacc[nt] = (f32x16){};
-
-  dma_tile<D, BC, kDqThreads>(Kh, 0, Nk, sK0, tid);
-  dma_tile<D, BC, kDqThreads>(Vh, 0, Nk, sV0, tid);
-  vm_wait_all();
-  __syncthreads();
-
-  for (int j = 0; j < ntiles; ++j) {
-    if (j + 1 < ntiles) {
-      dma_tile<D, BC, kDqThreads>(Kh, (j + 1) * BC, Nk, sK0 + ((j + 1) & 1) * TILE, tid);
-      dma_tile<D, BC, kDqThreads>(Vh, (j + 1) * BC, Nk, sV0 + ((j + 1) & 1) * TILE, tid);
+    // This lane's query row: Q^T and dO^T fragments (B operands), L and D.
+    const int qrow = q0 + wave * 32 + l32;
+    bf16x8 qf[NKK], dof[NKK];
+  #pragma unroll
+    for (int kk = 0; kk < NKK; ++kk) {
+      const size_t o = qbase + (size_t)qrow * D + kk * 16 + half * 8;
+      qf[kk] = (qrow < Nq) ? *(const bf16x8*)(Q + o) : zero_bf16x8();
+      dof[kk] = (qrow < Nq) ? *(const bf16x8*)(dO + o) : zero_bf16x8();
     }
-    const SwzRow<D> rs = rowsw.flipped((j & 1) * TB);
-    const SwzTr<D> ts = trsw.flipped((j & 1) * TB);
-    const int k0 = j * BC;
-    const bool need_mask = (k0 + BC > Nk) || (CAUSAL && (k0 + BC - 1 > wrow_lo + off));
+    const float l2 = (qrow < Nq) ? L[(size_t)bh * Nq + qrow] * kLog2e : INFINITY;
+    const float drow = (qrow < Nq) ? Dvec[(size_t)bh * Nq + qrow] : 0.f;
 
-    // dS^T for the 16 keys of element e of half mt: lane holds row qrow and
-    // keys k0 + mt*32 + (i/4)*8 + half*4 + i%4.
-    f32x16 sacc[2], dpacc[2];
-    bf16x8 dsf[4];
-    auto ds_elem = [&](int mt, int i) {
-      float p = fast_exp2(fmaf(sacc[mt][i], c, -l2));
-      if (need_mask) {
-        const int key = k0 + mt * 32 + (i >> 2) * 8 + half * 4 + (i & 3);
-        const bool vis = (key < Nk) && (!CAUSAL || key <= qrow + off);
-        if (!vis) p = 0.f;
-      }
-      dsf[mt * 2 + (i >> 3)][i & 7] = (bf16)(p * (dpacc[mt][i] - drow));
-    };
-    // S^T, dP^T of half mt (16 MFMAs); with `overlap`, the dS elements of half
-    // mt - 1 are computed between them.
-    auto sdp_half = [&](int mt, bool overlap) {
-      sacc[mt] = (f32x16){};
-      dpacc[mt] = (f32x16){};
-      bf16x8 ring[SRING];
-#pragma unroll
-      for (int st = 0; st < SRING; ++st) ring[st] = sfrag(rs, mt, st);
-#pragma unroll
-      for (int st = 0; st < 2 * NKK; ++st) {
-        const bf16x8 a = ring[st % SRING];
-        if (st + SRING < 2 * NKK) ring[st % SRING] = sfrag(rs, mt, st + SRING);
-        if (st & 1) dpacc[mt] = mfma32(a, dof[st >> 1], dpacc[mt]);
-        else sacc[mt] = mfma32(a, qf[st >> 1], sacc[mt]);
-        if (overlap) {
-#pragma unroll
-          for (int h = 0; h < 16 / (2 * NKK); ++h) ds_elem(mt - 1, st * (16 / (2 * NKK)) + h);
-        }
-        __builtin_amdgcn_sched_barrier(0);
-      }
-    };
-    // dQ^T += K^T dS^T over half mt (2*NNT MFMAs); with `overlap`, the dS
-    // elements of half mt + 1 are computed between them.
-    auto dq_half = [&](int mt, bool overlap) {
-      bf16x8 ring[TRING];
-#pragma unroll
-      for (int st = 0; st < TRING; ++st) ring[st] = kt_frag(ts, mt, st);
-#pragma unroll
-      for (int st = 0; st < 2 * NNT; ++st) {
-        const bf16x8 a = ring[st % TRING];
-        if (st + TRING < 2 * NNT) ring[st % TRING] = kt_frag(ts, mt, st + TRING);
-        dqacc[st % NNT] = mfma32(a, dsf[mt * 2 + st / NNT], dqacc[st % NNT]);
-        if (overlap) {
-#pragma unroll
-          for (int h = 0; h < 16 / (2 * NNT); ++h) ds_elem(mt + 1, st * (16 / (2 * NNT)) + h);
-        }
-        __builtin_amdgcn_sched_barrier(0);
-      }
-    };
-    sdp_half(0, false);
-    sdp_half(1, true);   // dS of half 0 overlaps the MFMAs of half 1
-    dq_half(0, true);    // dS of half 1 overlaps dQ of half 0
-    dq_half(1, false);
+    const int kend = CAUSAL ? min(Nk, q0 + BR + off) : Nk;
+    const int ntiles = (kend + BC - 1) / BC;
+    const int wrow_lo = q0 + wave * 32;
 
-    vm_wait_all();  // this wave's part of tile j+1 has landed
+    const int tr_row = (g >> 1) * 4 + (s16 >> 2);
+    const int tr_col = (g & 1) * 16 + (s16 & 3) * 4;
+    // S^T and dP^T for one 32-key half mt: 2 x NKK steps alternating the K
+    // (even step, S^T) and V (odd step, dP^T) row fragments.
+    const SwzRow<D> rowsw(l32, half);
+    const SwzTr<D> trsw(tr_row, tr_col);
+    auto sfrag = [&](const SwzRow<D>& rs, int mt, int st) {
+      const bf16* base = (st & 1) ? sV0 : sK0;
+      return *at_byte<bf16x8>(base, rs.off(mt * 32, (st >> 1) * 2));
+    };
+    // dQ^T += K^T dS^T for one 32-key half mt: 2 x NNT steps (16-key chunk
+    // kc = st / NNT of the half, head-dim tile st % NNT); K^T by transpose reads.
+    auto kt_frag = [&](const SwzTr<D>& ts, int mt, int st) {
+      const int rb = mt * 32 + (st / NNT) * 16, cb = (st % NNT) * 32;
+      return concat(lds_read_tr(to_lds(at_byte<bf16>(sK0, ts.off(rb, 0, cb)))),
+                    lds_read_tr(to_lds(at_byte<bf16>(sK0, ts.off(rb, 1, cb)))));
+    };
+    constexpr int SRING = 4, TRING = 3;
+
+    f32x16 dqacc[NNT];
+  #pragma unroll
+    for (int nt = 0; nt < NNT; ++nt) dqacc[nt] = (f32x16){};
+
+    dma_tile<D, BC, kDqThreads>(Kh, 0, Nk, sK0, tid);
+    dma_tile<D, BC, kDqThreads>(Vh, 0, Nk, sV0, tid);
+    vm_wait_all();
     __syncthreads();
-  }
 
-  // Epilogue: dQ = scale * dQ_acc; lane holds row qrow.
-  if (qrow < Nq) {
-    bf16* out = dQ + qbase + (size_t)qrow * D;
-#pragma unroll
-    for (int nt = 0; nt < NNT; ++nt)
-#pragma unroll
-      for (int gg = 0; gg < 4; ++gg) {
-        bf16x4 v;
-#pragma unroll
-        for (int e = 0; e < 4; ++e) v[e] = (bf16)(dqacc[nt][gg * 4 + e] * scale);
-        *(bf16x4*)(out + nt * 32 + gg * 8 + half * 4) = v;
+    for (int j = 0; j < ntiles; ++j) {
+      if (j + 1 < ntiles) {
+        dma_tile<D, BC, kDqThreads>(Kh, (j + 1) * BC, Nk, sK0 + ((j + 1) & 1) * TILE, tid);
+        dma_tile<D, BC, kDqThreads>(Vh, (j + 1) * BC, Nk, sV0 + ((j + 1) & 1) * TILE, tid);
       }
+      const SwzRow<D> rs = rowsw.flipped((j & 1) * TB);
+      const SwzTr<D> ts = trsw.flipped((j & 1) * TB);
+      const int k0 = j * BC;
+      const bool need_mask = (k0 + BC > Nk) || (CAUSAL && (k0 + BC - 1 > wrow_lo + off));
+
+      // dS^T for the 16 keys of element e of half mt: lane holds row qrow and
+      // keys k0 + mt*32 + (i/4)*8 + half*4 + i%4.
+      f32x16 sacc[2], dpacc[2];
+      bf16x8 dsf[4];
+      auto ds_elem = [&](int mt, int i) {
+        float p = fast_exp2(fmaf(sacc[mt][i], c, -l2));
+        if (need_mask) {
+          const int key = k0 + mt * 32 + (i >> 2) * 8 + half * 4 + (i & 3);
+          const bool vis = (key < Nk) && (!CAUSAL || key <= qrow + off);
+          if (!vis) p = 0.f;
+        }
+        dsf[mt * 2 + (i >> 3)][i & 7] = (bf16)(p * (dpacc[mt][i] - drow));
+      };
+      // S^T, dP^T of half mt (16 MFMAs); with `overlap`, the dS elements of half
+      // mt - 1 are computed between them.
+      auto sdp_half = [&](int mt, bool overlap) {
+        sacc[mt] = (f32x16){};
+        dpacc[mt] = (f32x16){};
+        bf16x8 ring[SRING];
+  #pragma unroll
+        for (int st = 0; st < SRING; ++st) ring[st] = sfrag(rs, mt, st);
+  #pragma unroll
+        for (int st = 0; st < 2 * NKK; ++st) {
+          const bf16x8 a = ring[st % SRING];
+          if (st + SRING < 2 * NKK) ring[st % SRING] = sfrag(rs, mt, st + SRING);
+          if (st & 1) dpacc[mt] = mfma32(a, dof[st >> 1], dpacc[mt]);
+          else sacc[mt] = mfma32(a, qf[st >> 1], sacc[mt]);
+          if (overlap) {
+  #pragma unroll
+            for (int h = 0; h < 16 / (2 * NKK); ++h) ds_elem(mt - 1, st * (16 / (2 * NKK)) + h);
+          }
+          __builtin_amdgcn_sched_barrier(0);
+        }
+      };
+      // dQ^T += K^T dS^T over half mt (2*NNT MFMAs); with `overlap`, the dS
+      // elements of half mt + 1 are computed between them.
+      auto dq_half = [&](int mt, bool overlap) {
+        bf16x8 ring[TRING];
+  #pragma unroll
+        for (int st = 0; st < TRING; ++st) ring[st] = kt_frag(ts, mt, st);
+  #pragma unroll
+        for (int st = 0; st < 2 * NNT; ++st) {
+          const bf16x8 a = ring[st % TRING];
+          if (st + TRING < 2 * NNT) ring[st % TRING] = kt_frag(ts, mt, st + TRING);
+          dqacc[st % NNT] = mfma32(a, dsf[mt * 2 + st / NNT], dqacc[st % NNT]);
+          if (overlap) {
+  #pragma unroll
+            for (int h = 0; h < 16 / (2 * NNT); ++h) ds_elem(mt + 1, st * (16 / (2 * NNT)) + h);
+          }
+          __builtin_amdgcn_sched_barrier(0);
+        }
+      };
+      sdp_half(0, false);
+      sdp_half(1, true);   // dS of half 0 overlaps the MFMAs of half 1
+      dq_half(0, true);    // dS of half 1 overlaps dQ of half 0
+      dq_half(1, false);
+
+      vm_wait_all();  // this wave's part of tile j+1 has landed
+      __syncthreads();
+    }
+
+    // Epilogue: dQ = scale * dQ_acc; lane holds row qrow.
+    if (qrow < Nq) {
+      bf16* out = dQ + qbase + (size_t)qrow * D;
+  #pragma unroll
+      for (int nt = 0; nt < NNT; ++nt)
+  #pragma unroll
+        for (int gg = 0; gg < 4; ++gg) {
+          bf16x4 v;
+  #pragma unroll
+          for (int e = 0; e < 4; ++e) v[e] = (bf16)(dqacc[nt][gg * 4 + e] * scale);
+          *(bf16x4*)(out + nt * 32 + gg * 8 + half * 4) = v;
+        }
+    }
   }
 }
 
@@ -611,7 +627,7 @@ hipError_t launch_bwd_bf16(const BwdArgs& a, int stages, hipStream_t s) {
   }
   if ((stages & 4) && a.Nq > 0) {
     const int nqt = (a.Nq + kDqBR - 1) / kDqBR;
-    const int nblocks = nqt * BH;
+    const int nblocks = (a.causal ? (nqt + 1) / 2 : nqt) * BH;  // causal: query tile pairs
 #define FA_DQ_LAUNCH(DD, CC)                                                                    \
   hipLaunchKernelGGL((bwd_dq_bf16_kernel<DD, CC>), dim3(nblocks), dim3(kDqThreads), 0, s, Q, K,  \
                      V, a.L, dO, a.Dvec, (bf16*)a.dQ, a.Nq, a.Nk, nqt, c, a.scale, off)

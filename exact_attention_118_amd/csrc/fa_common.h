@@ -139,29 +139,49 @@ __device__ __forceinline__ const T* at_byte(const void* base, unsigned off) {
 // LDS tile, with direct-to-LDS loads (global_load_lds_dwordx4: lane i of a
 // wave instruction writes 16 bytes at the instruction's LDS base + 16 i).
 // Rows at or beyond nvalid (>= 1) are read from row nvalid - 1 instead, so the
-// tile holds finite data that the caller masks.  All THREADS threads call it;
-// the data is in LDS once this wave has waited for vmcnt and the workgroup has
-// passed a barrier.
+// tile holds finite data that the caller masks.  The tile takes
+// ROWS * D / 8 / THREADS instructions per wave; dma_part issues instruction u
+// of the calling wave, so a kernel can spread them over its compute.  The data
+// is in LDS once every wave has waited for vmcnt and passed a barrier.
+template <int D, int ROWS, int THREADS>
+struct DmaTile {
+  static constexpr int CPR = D / 8;
+  static constexpr int PER = ROWS * CPR / THREADS;
+  static_assert(PER * THREADS == ROWS * CPR && THREADS % 64 == 0, "tile split");
+};
+
+template <int D, int ROWS, int THREADS>
+__device__ __forceinline__ void dma_part(const bf16* __restrict__ g, int row0, int nvalid,
+                                         bf16* lds, int tid, int u) {
+  using T = DmaTile<D, ROWS, THREADS>;
+  const int wave = tid >> 6, lane = tid & 63;
+  const int slot0 = (wave * T::PER + u) * 64;
+  const int slot = slot0 + lane;
+  const int r = slot / T::CPR, pch = slot % T::CPR;
+  const int grow = min(row0 + r, nvalid - 1);
+  const bf16* src = g + (size_t)grow * D + ((pch ^ swz<D>(r)) << 3);
+  __builtin_amdgcn_global_load_lds((const void*)src, (FA_LDS void*)(lds + slot0 * 8), 16, 0, 0);
+}
+
 template <int D, int ROWS, int THREADS>
 __device__ __forceinline__ void dma_tile(const bf16* __restrict__ g, int row0, int nvalid,
                                          bf16* lds, int tid) {
-  constexpr int CPR = D / 8;
-  constexpr int PER = ROWS * CPR / THREADS;
-  static_assert(PER * THREADS == ROWS * CPR && THREADS % 64 == 0, "tile split");
-  const int wave = tid >> 6, lane = tid & 63;
 #pragma unroll
-  for (int u = 0; u < PER; ++u) {
-    const int slot0 = (wave * PER + u) * 64;
-    const int slot = slot0 + lane;
-    const int r = slot / CPR, pch = slot % CPR;
-    const int grow = min(row0 + r, nvalid - 1);
-    const bf16* src = g + (size_t)grow * D + ((pch ^ swz<D>(r)) << 3);
-    __builtin_amdgcn_global_load_lds((const void*)src, (FA_LDS void*)(lds + slot0 * 8), 16, 0, 0);
-  }
+  for (int u = 0; u < DmaTile<D, ROWS, THREADS>::PER; ++u)
+    dma_part<D, ROWS, THREADS>(g, row0, nvalid, lds, tid, u);
 }
 
 // Wait for this wave's outstanding vector-memory operations (including the
 // direct-to-LDS loads above).
 __device__ __forceinline__ void vm_wait_all() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
+
+// Keeps the computation of v at this point of the instruction stream: the
+// empty volatile asm reads and rewrites v, so whatever produces v must come
+// before it, and the asm itself keeps its place among the other volatile
+// statements and scheduling barriers.  Without it the compiler sinks pure
+// arithmetic (exponentials, conversions) towards its first use, undoing an
+// interleave of vector-ALU work with MFMAs.
+template <typename T>
+__device__ __forceinline__ void pin(T& v) { asm volatile("" : "+v"(v)); }
 
 }  // namespace fa

@@ -21,15 +21,19 @@
 //  * O^T = V^T P^T reuses the S^T accumulator registers directly as the
 //    P operand (no LDS round trip); V^T is read from the row-major V tile with
 //    the LDS transpose read ds_read_b64_tr_b16.
-//  * K/V tiles of BC = 64 keys are staged in LDS; the next tile's global
-//    loads are issued before the current tile's math (register prefetch).
-//  * Causal: tiles beyond the diagonal are never loaded, the mask is applied
-//    only on tiles that straddle it (the 51CTO FlashAttention V1/V2 notes, "FlashAttention V2 相比V1有哪些改进"),
-//    and a wave whose rows see none of a tile skips its math.
+//  * K/V tiles of BC = 64 keys are staged in LDS, double-buffered and loaded
+//    straight from HBM into LDS (global_load_lds_dwordx4) in an XOR-swizzled
+//    layout that keeps both the row reads and the transpose reads free of
+//    bank conflicts; the loads of tiles j+1/j+2 are spread over tile j's
+//    MFMA steps, and tile j's exponentials over tile j+1's score MFMAs.
+//  * Causal: tiles beyond the diagonal are never loaded and the mask is
+//    applied only on tiles that straddle it (the 51CTO FlashAttention V1/V2
+//    notes, "FlashAttention V2 相比V1有哪些改进").
 //  * Grid: one workgroup per (Q tile, batch*head), remapped so each XCD gets a
 //    contiguous range of Q tiles of the same heads (K/V stay in that XCD's L2;
-//    the 51CTO FlashAttention V1/V2 notes, "Thread Block Level 并行", grid order with the Q tile fastest),
-//    causal tiles longest first.
+//    the 51CTO FlashAttention V1/V2 notes, "Thread Block Level 并行", grid order with the Q tile fastest).
+//    Causal: a workgroup takes Q tiles t and nqt-1-t in turn, so all carry
+//    the same number of key tiles and no CU idles half-empty at the end.
 #include "fa_common.h"
 #include "fa_launch.h"
 
@@ -64,192 +68,228 @@ void fwd_bf16_kernel(const bf16* __restrict__ Q, const bf16* __restrict__ K,
   const int half = lane >> 5, l32 = lane & 31;
   const int g = lane >> 4, s16 = lane & 15;
 
+  // Grid: one workgroup per (query tile, batch*head); causal, one per pair of
+  // query tiles (t, nqt-1-t) of a head, processed one after the other, so that
+  // every workgroup has the same number of key tiles (a query tile's count
+  // grows with its index) and the two workgroups sharing a CU finish together
+  // instead of leaving it half used.  Remapped so each XCD serves a contiguous
+  // range of workgroups of the same heads (K/V stay in that XCD's L2; the 51CTO
+  // notes, "Thread Block Level 并行", grid order with the query tile fastest).
+  const int nwg = CAUSAL ? (nqt + 1) / 2 : nqt;  // workgroups per head
   const int logical = xcd_remap(blockIdx.x, gridDim.x);
-  const int bh = logical / nqt;
-  const int t = logical - bh * nqt;
-  const int qt = CAUSAL ? (nqt - 1 - t) : t;
-  const int q0 = qt * BR;
+  const int bh = logical / nwg;
+  const int t = logical - bh * nwg;
   const size_t qbase = (size_t)bh * Nq * D;
   const bf16* Kh = K + (size_t)bh * Nk * D;
   const bf16* Vh = V + (size_t)bh * Nk * D;
 
-  // This lane's query row and its Q^T fragments (B operand of S^T = K Q^T).
-  const int qrow = q0 + wave * 32 + l32;
-  bf16x8 qf[NKK];
-#pragma unroll
-  for (int kk = 0; kk < NKK; ++kk)
-    qf[kk] = (qrow < Nq) ? *(const bf16x8*)(Q + qbase + (size_t)qrow * D + kk * 16 + half * 8)
-                         : zero_bf16x8();
+  for (int pass = 0; pass < (CAUSAL ? 2 : 1); ++pass) {
+    const int qt = !CAUSAL ? t : (pass == 0 ? nqt - 1 - t : t);
+    if (CAUSAL && pass == 1 && t == nqt - 1 - t) break;  // odd count: the middle tile once
+    if (pass == 1) __syncthreads();  // the first tile's last reads precede the new loads
+    const int q0 = qt * BR;
 
-  // Keys this workgroup needs: all, or (causal) up to the last row's diagonal.
-  const int kend = CAUSAL ? min(Nk, q0 + BR + off) : Nk;
-  const int ntiles = (kend + BC - 1) / BC;
-  const int wrow_lo = q0 + wave * 32;  // smallest query row of this wave
+    // This lane's query row and its Q^T fragments (B operand of S^T = K Q^T).
+    const int qrow = q0 + wave * 32 + l32;
+    bf16x8 qf[NKK];
+  #pragma unroll
+    for (int kk = 0; kk < NKK; ++kk)
+      qf[kk] = (qrow < Nq) ? *(const bf16x8*)(Q + qbase + (size_t)qrow * D + kk * 16 + half * 8)
+                           : zero_bf16x8();
 
-  // Lane-constant parts of the LDS reads.
-  const int tr_row = (g >> 1) * 4 + (s16 >> 2);      // transpose read: row in a 16-row chunk
-  const int tr_col = (g & 1) * 16 + (s16 & 3) * 4;   // and column in a 32-wide tile
-  // S^T = K Q^T for one K tile: 2 x NKK MFMA steps (step st: key half st & 1,
-  // head-dim chunk st >> 1); the A fragment of step st is K row (st&1)*32 + l32,
-  // columns (st>>1)*16 + half*8 .. +8.
-  const SwzRow<D> krow(l32, half);
-  const SwzTr<D> vtr(tr_row, tr_col);
-  auto kfrag = [&](const SwzRow<D>& kr, int st) {
-    return *at_byte<bf16x8>(sK0, kr.off((st & 1) * 32, (st >> 1) * 2));
-  };
-  // O^T += V^T P^T: 4 x NNT steps (step st: 16-key chunk st / NNT, head-dim tile
-  // st % NNT); the A fragment is V^T by two transpose reads.
-  auto vfrag = [&](const SwzTr<D>& vt, int st) {
-    const int rb = (st / NNT) * 16, cb = (st % NNT) * 32;
-    return concat(lds_read_tr(to_lds(at_byte<bf16>(sV0, vt.off(rb, 0, cb)))),
-                  lds_read_tr(to_lds(at_byte<bf16>(sV0, vt.off(rb, 1, cb)))));
-  };
-  constexpr int KRING = 4, VRING = 3;
+    // Keys this workgroup needs: all, or (causal) up to the last row's diagonal.
+    const int kend = CAUSAL ? min(Nk, q0 + BR + off) : Nk;
+    const int ntiles = (kend + BC - 1) / BC;
+    const int wrow_lo = q0 + wave * 32;  // smallest query row of this wave
 
-  float m_run = -INFINITY;  // reference of the exponentials (row max so far, log2 units)
-  float l_run = 0.f;        // running sum of this lane half's probabilities
-  f32x16 oacc[NNT];
-#pragma unroll
-  for (int nt = 0; nt < NNT; ++nt) oacc[nt] = (f32x16){};
+    // Lane-constant parts of the LDS reads.
+    const int tr_row = (g >> 1) * 4 + (s16 >> 2);      // transpose read: row in a 16-row chunk
+    const int tr_col = (g & 1) * 16 + (s16 & 3) * 4;   // and column in a 32-wide tile
+    // S^T = K Q^T for one K tile: 2 x NKK MFMA steps (step st: key half st & 1,
+    // head-dim chunk st >> 1); the A fragment of step st is K row (st&1)*32 + l32,
+    // columns (st>>1)*16 + half*8 .. +8.
+    const SwzRow<D> krow(l32, half);
+    const SwzTr<D> vtr(tr_row, tr_col);
+    auto kfrag = [&](const SwzRow<D>& kr, int st) {
+      return *at_byte<bf16x8>(sK0, kr.off((st & 1) * 32, (st >> 1) * 2));
+    };
+    // O^T += V^T P^T: 4 x NNT steps (step st: 16-key chunk st / NNT, head-dim tile
+    // st % NNT); the A fragment is V^T by two transpose reads.
+    auto vfrag = [&](const SwzTr<D>& vt, int st) {
+      const int rb = (st / NNT) * 16, cb = (st % NNT) * 32;
+      return concat(lds_read_tr(to_lds(at_byte<bf16>(sV0, vt.off(rb, 0, cb)))),
+                    lds_read_tr(to_lds(at_byte<bf16>(sV0, vt.off(rb, 1, cb)))));
+    };
+    constexpr int KRING = 4, VRING = 3;
 
-  // Prologue: K tiles 0 and 1, V tile 0; scores of tile 0.
-  dma_tile<D, BC, kFwdThreads>(Kh, 0, Nk, sK0, tid);
-  if (ntiles > 1) dma_tile<D, BC, kFwdThreads>(Kh, BC, Nk, sK0 + TILE, tid);
-  dma_tile<D, BC, kFwdThreads>(Vh, 0, Nk, sV0, tid);
-  vm_wait_all();
-  __syncthreads();
-  f32x16 snext[2] = {(f32x16){}, (f32x16){}};
-  {
-    bf16x8 ring[KRING];
-#pragma unroll
-    for (int st = 0; st < KRING; ++st) ring[st] = kfrag(krow, st);
-#pragma unroll
-    for (int st = 0; st < 2 * NKK; ++st) {
-      const bf16x8 a = ring[st % KRING];
-      if (st + KRING < 2 * NKK) ring[st % KRING] = kfrag(krow, st + KRING);
-      snext[st & 1] = mfma32(a, qf[st >> 1], snext[st & 1]);
-    }
-  }
-  __syncthreads();  // every wave is done with K tile 0 before tile 2 replaces it
+    float m_run = -INFINITY;  // reference of the exponentials (row max so far, log2 units)
+    float l_run = 0.f;        // running sum of this lane half's probabilities
+    f32x16 oacc[NNT];
+  #pragma unroll
+    for (int nt = 0; nt < NNT; ++nt) oacc[nt] = (f32x16){};
 
-  for (int j = 0; j < ntiles; ++j) {
-    // Start loading K tile j+2 (over tile j's buffer, last read for tile j's
-    // scores) and V tile j+1.
-    if (j + 2 < ntiles) dma_tile<D, BC, kFwdThreads>(Kh, (j + 2) * BC, Nk, sK0 + (j & 1) * TILE, tid);
-    if (j + 1 < ntiles)
-      dma_tile<D, BC, kFwdThreads>(Vh, (j + 1) * BC, Nk, sV0 + ((j + 1) & 1) * TILE, tid);
+    using KD = DmaTile<D, BC, kFwdThreads>;
+    // Keys past the end and, causal, keys after the row's diagonal get score
+    // -inf.  Only tiles that cross the diagonal or the end need it; lane holds
+    // row qrow, keys k0 + mt*32 + (i/4)*8 + half*4 + i%4.
+    auto mask_tile = [&](f32x16 (&sc)[2], int k0) {
+      if ((k0 + BC > Nk) || (CAUSAL && (k0 + BC - 1 > wrow_lo + off))) {
+  #pragma unroll
+        for (int mt = 0; mt < 2; ++mt)
+  #pragma unroll
+          for (int i = 0; i < 16; ++i) {
+            const int key = k0 + mt * 32 + (i >> 2) * 8 + half * 4 + (i & 3);
+            const bool vis = (key < Nk) && (!CAUSAL || key <= qrow + off);
+            if (!vis) sc[mt][i] = -INFINITY;
+          }
+      }
+    };
 
-    const int k0 = j * BC;
-    f32x16 scur[2] = {snext[0], snext[1]};
-    // Mask keys past the end and, causal, keys after the row's diagonal (only
-    // tiles that cross it); lane holds row qrow, keys k0 + mt*32 + (i/4)*8 +
-    // half*4 + i%4.
-    const bool need_mask = (k0 + BC > Nk) || (CAUSAL && (k0 + BC - 1 > wrow_lo + off));
-    if (need_mask) {
-#pragma unroll
-      for (int mt = 0; mt < 2; ++mt)
-#pragma unroll
-        for (int i = 0; i < 16; ++i) {
-          const int key = k0 + mt * 32 + (i >> 2) * 8 + half * 4 + (i & 3);
-          const bool vis = (key < Nk) && (!CAUSAL || key <= qrow + off);
-          if (!vis) scur[mt][i] = -INFINITY;
-        }
-    }
-    // Online softmax (the CSDN post "Flash Attention1", 例子说明: running max
-    // and running sum), normalised once in the epilogue.  The reference m_run
-    // of the exponentials moves to the new row max only when some row of the
-    // wave has grown by more than kRescaleSlack (log2 units); until then
-    // probabilities are taken against the older, smaller reference and stay
-    // below 2^kRescaleSlack, where fp32 sums and bf16 operands keep their full
-    // relative precision.  The result is the same in exact arithmetic, and
-    // most tiles skip rescaling the accumulators.
-    float mx = -INFINITY;
-#pragma unroll
-    for (int mt = 0; mt < 2; ++mt)
-#pragma unroll
-      for (int i = 0; i < 16; ++i) mx = fmaxf(mx, scur[mt][i]);
-    mx = fmaxf(mx, wave_shfl_xor(mx, 32));
-    const float m_tile = mx * c;
-    if (__builtin_amdgcn_ballot_w64(m_tile > m_run + kRescaleSlack) != 0) {
-      const float m_new = fmaxf(m_run, m_tile);
-      const float alpha = fast_exp2(m_run - (m_new == -INFINITY ? 0.f : m_new));
-      l_run *= alpha;
-#pragma unroll
-      for (int nt = 0; nt < NNT; ++nt) oacc[nt] *= alpha;
-      m_run = m_new;
-    }
-    const float m_ref = (m_run == -INFINITY) ? 0.f : m_run;
-
-    // Scores of tile j+1 on the MFMA pipe, interleaved step by step with the
-    // exponentials of tile j on the vector ALU.  Step st converts the pair of
-    // probabilities pf[st/4][2*(st%4) .. +1] (keys of chunk st/4).  The last
-    // iteration also computes scores, of a stale buffer, and discards them:
-    // one extra tile of S per workgroup keeps this block free of branches, so
-    // the two kinds of work stay interleaved.
-    bf16x8 pf[4];
-    float rs0 = 0.f, rs1 = 0.f;
+    // Prologue: K tiles 0 and 1, V tile 0; scores, mask and row max of tile 0.
+    dma_tile<D, BC, kFwdThreads>(Kh, 0, Nk, sK0, tid);
+    dma_tile<D, BC, kFwdThreads>(Kh, BC, Nk, sK0 + TILE, tid);
+    dma_tile<D, BC, kFwdThreads>(Vh, 0, Nk, sV0, tid);
+    vm_wait_all();
+    __syncthreads();
+    f32x16 snext[2] = {(f32x16){}, (f32x16){}};
     {
-      const SwzRow<D> kr = krow.flipped(((j + 1) & 1) * TB);
       bf16x8 ring[KRING];
-      snext[0] = (f32x16){};
-      snext[1] = (f32x16){};
-#pragma unroll
-      for (int st = 0; st < KRING; ++st) ring[st] = kfrag(kr, st);
-#pragma unroll
+  #pragma unroll
+      for (int st = 0; st < KRING; ++st) ring[st] = kfrag(krow, st);
+  #pragma unroll
       for (int st = 0; st < 2 * NKK; ++st) {
         const bf16x8 a = ring[st % KRING];
-        if (st + KRING < 2 * NKK) ring[st % KRING] = kfrag(kr, st + KRING);
+        if (st + KRING < 2 * NKK) ring[st % KRING] = kfrag(krow, st + KRING);
         snext[st & 1] = mfma32(a, qf[st >> 1], snext[st & 1]);
-#pragma unroll
-        for (int h = 0; h < 32 / (2 * NKK); h += 2) {
-          const int el = st * (32 / (2 * NKK)) + h;  // probability index 0..31
-          const int kc = el >> 3, e = el & 7;
-          const int mt = kc >> 1, i = (kc & 1) * 8 + e;
-          const float p0 = fast_exp2(fmaf(scur[mt][i], c, -m_ref));
-          const float p1 = fast_exp2(fmaf(scur[mt][i + 1], c, -m_ref));
-          rs0 += p0;
-          rs1 += p1;
-          pf[kc][e] = (bf16)p0;
-          pf[kc][e + 1] = (bf16)p1;
+      }
+    }
+    mask_tile(snext, 0);
+    float mx_next = -INFINITY;
+  #pragma unroll
+    for (int mt = 0; mt < 2; ++mt)
+  #pragma unroll
+      for (int i = 0; i < 16; ++i) mx_next = fmaxf(mx_next, snext[mt][i]);
+    mx_next = fmaxf(mx_next, wave_shfl_xor(mx_next, 32));
+    __syncthreads();  // every wave is done with K tile 0 before tile 2 replaces it
+
+    for (int j = 0; j < ntiles; ++j) {
+      const int k0 = j * BC;
+      f32x16 scur[2] = {snext[0], snext[1]};
+      // Online softmax (the CSDN post "Flash Attention1", 例子说明: running max
+      // and running sum), normalised once in the epilogue.  The reference m_run
+      // of the exponentials moves to the new row max only when some row of the
+      // wave has grown by more than kRescaleSlack (log2 units); until then
+      // probabilities are taken against the older, smaller reference and stay
+      // below 2^kRescaleSlack, where fp32 sums and bf16 operands keep their full
+      // relative precision.  The result is the same in exact arithmetic, and
+      // most tiles skip rescaling the accumulators.  The row max of tile j was
+      // taken while tile j-1's P V product ran.
+      const float m_tile = mx_next * c;
+      if (__builtin_amdgcn_ballot_w64(m_tile > m_run + kRescaleSlack) != 0) {
+        const float m_new = fmaxf(m_run, m_tile);
+        const float alpha = fast_exp2(m_run - (m_new == -INFINITY ? 0.f : m_new));
+        l_run *= alpha;
+  #pragma unroll
+        for (int nt = 0; nt < NNT; ++nt) oacc[nt] *= alpha;
+        m_run = m_new;
+      }
+      const float m_ref = (m_run == -INFINITY) ? 0.f : m_run;
+
+      // Scores of tile j+1 on the MFMA pipe, interleaved step by step with the
+      // exponentials of tile j on the vector ALU and with the direct-to-LDS
+      // loads of K tile j+2 (over tile j's buffer, last read for tile j's
+      // scores) and V tile j+1.  Step st converts the pair of probabilities
+      // pf[st/4][2*(st%4) .. +1] (keys of chunk st/4).  The last iterations
+      // also compute scores of a stale buffer and load clamped rows nobody
+      // reads: that extra work keeps this block free of branches, so the three
+      // kinds of work stay interleaved.
+      bf16x8 pf[4];
+      float rs0 = 0.f, rs1 = 0.f;
+      {
+        const SwzRow<D> kr = krow.flipped(((j + 1) & 1) * TB);
+        bf16x8 ring[KRING];
+        snext[0] = (f32x16){};
+        snext[1] = (f32x16){};
+  #pragma unroll
+        for (int st = 0; st < KRING; ++st) ring[st] = kfrag(kr, st);
+  #pragma unroll
+        for (int st = 0; st < 2 * NKK; ++st) {
+          const bf16x8 a = ring[st % KRING];
+          if (st + KRING < 2 * NKK) ring[st % KRING] = kfrag(kr, st + KRING);
+          snext[st & 1] = mfma32(a, qf[st >> 1], snext[st & 1]);
+          if ((st & 1) == 0) {
+            static_assert(2 * KD::PER == NKK, "one load every other step");
+            const int di = st >> 1;
+            if (di < KD::PER)
+              dma_part<D, BC, kFwdThreads>(Kh, k0 + 2 * BC, Nk, sK0 + (j & 1) * TILE, tid, di);
+            else
+              dma_part<D, BC, kFwdThreads>(Vh, k0 + BC, Nk, sV0 + ((j + 1) & 1) * TILE, tid,
+                                           di - KD::PER);
+          }
+  #pragma unroll
+          for (int h = 0; h < 32 / (2 * NKK); h += 2) {
+            const int el = st * (32 / (2 * NKK)) + h;  // probability index 0..31
+            const int kc = el >> 3, e = el & 7;
+            const int mt = kc >> 1, i = (kc & 1) * 8 + e;
+            const float p0 = fast_exp2(fmaf(scur[mt][i], c, -m_ref));
+            const float p1 = fast_exp2(fmaf(scur[mt][i + 1], c, -m_ref));
+            rs0 += p0;
+            rs1 += p1;
+            pf[kc][e] = (bf16)p0;
+            pf[kc][e + 1] = (bf16)p1;
+          }
+          pin(pf[(st * (32 / (2 * NKK))) >> 3]);
+          pin(rs0);
+          pin(rs1);
+          __builtin_amdgcn_sched_barrier(0);
         }
-        __builtin_amdgcn_sched_barrier(0);
       }
-    }
-    l_run += rs0 + rs1;
+      l_run += rs0 + rs1;
+      mask_tile(snext, k0 + BC);
 
-    // O^T += V^T P^T for tile j.
-    {
-      const SwzTr<D> vt = vtr.flipped((j & 1) * TB);
-      bf16x8 ring[VRING];
-#pragma unroll
-      for (int st = 0; st < VRING; ++st) ring[st] = vfrag(vt, st);
-#pragma unroll
-      for (int st = 0; st < 4 * NNT; ++st) {
-        const bf16x8 a = ring[st % VRING];
-        if (st + VRING < 4 * NNT) ring[st % VRING] = vfrag(vt, st + VRING);
-        oacc[st % NNT] = mfma32(a, pf[st / NNT], oacc[st % NNT]);
-        __builtin_amdgcn_sched_barrier(0);
+      // O^T += V^T P^T for tile j, interleaved with the row max of tile j+1.
+      {
+        const SwzTr<D> vt = vtr.flipped((j & 1) * TB);
+        bf16x8 ring[VRING];
+        float mxa = -INFINITY, mxb = -INFINITY;
+  #pragma unroll
+        for (int st = 0; st < VRING; ++st) ring[st] = vfrag(vt, st);
+  #pragma unroll
+        for (int st = 0; st < 4 * NNT; ++st) {
+          const bf16x8 a = ring[st % VRING];
+          if (st + VRING < 4 * NNT) ring[st % VRING] = vfrag(vt, st + VRING);
+          oacc[st % NNT] = mfma32(a, pf[st / NNT], oacc[st % NNT]);
+  #pragma unroll
+          for (int h = 0; h < 32 / (4 * NNT); h += 2) {
+            const int el = st * (32 / (4 * NNT)) + h;
+            mxa = fmaxf(mxa, snext[el >> 4][el & 15]);
+            mxb = fmaxf(mxb, snext[el >> 4][(el & 15) + 1]);
+          }
+          __builtin_amdgcn_sched_barrier(0);
+        }
+        mx_next = fmaxf(mxa, mxb);
+        mx_next = fmaxf(mx_next, wave_shfl_xor(mx_next, 32));
       }
+      vm_wait_all();  // this wave's part of tiles K j+2 and V j+1 has landed
+      __syncthreads();
     }
-    vm_wait_all();  // this wave's part of tiles K j+2 and V j+1 has landed
-    __syncthreads();
-  }
 
-  // Epilogue: O = O_acc / l, L = (m + log2 l) * ln 2.
-  const float l_tot = l_run + wave_shfl_xor(l_run, 32);
-  if (qrow < Nq) {
-    const float inv = 1.f / l_tot;
-    bf16* orow = O + qbase + (size_t)qrow * D;
-#pragma unroll
-    for (int nt = 0; nt < NNT; ++nt)
-#pragma unroll
-      for (int gg = 0; gg < 4; ++gg) {
-        bf16x4 v;
-#pragma unroll
-        for (int e = 0; e < 4; ++e) v[e] = (bf16)(oacc[nt][gg * 4 + e] * inv);
-        *(bf16x4*)(orow + nt * 32 + gg * 8 + half * 4) = v;
-      }
-    if (half == 0) L[(size_t)bh * Nq + qrow] = (m_run + log2f(l_tot)) * kLn2;
+    // Epilogue: O = O_acc / l, L = (m + log2 l) * ln 2.
+    const float l_tot = l_run + wave_shfl_xor(l_run, 32);
+    if (qrow < Nq) {
+      const float inv = 1.f / l_tot;
+      bf16* orow = O + qbase + (size_t)qrow * D;
+  #pragma unroll
+      for (int nt = 0; nt < NNT; ++nt)
+  #pragma unroll
+        for (int gg = 0; gg < 4; ++gg) {
+          bf16x4 v;
+  #pragma unroll
+          for (int e = 0; e < 4; ++e) v[e] = (bf16)(oacc[nt][gg * 4 + e] * inv);
+          *(bf16x4*)(orow + nt * 32 + gg * 8 + half * 4) = v;
+        }
+      if (half == 0) L[(size_t)bh * Nq + qrow] = (m_run + log2f(l_tot)) * kLn2;
+    }
   }
 }
 
@@ -328,7 +368,8 @@ __global__ __launch_bounds__(kF32Rows) void fwd_f32_kernel(
 hipError_t launch_fwd_bf16(const FwdArgs& a, hipStream_t s) {
   const int BH = a.B * a.H;
   const int nqt = (a.Nq + kFwdBR - 1) / kFwdBR;
-  const int nblocks = nqt * BH;
+  // Causal: one workgroup per pair of query tiles (t, nqt-1-t).
+  const int nblocks = (a.causal ? (nqt + 1) / 2 : nqt) * BH;
   const float c = a.scale * kLog2e;
   const int off = a.Nk - a.Nq;
   const bf16* Q = (const bf16*)a.Q;

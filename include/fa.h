@@ -62,7 +62,8 @@ typedef enum fa_dtype { FA_BF16 = 0, FA_FP32 = 1 } fa_dtype;
  *
  *  Q [B,H,Nq,d], K and V [B,H,Nk,d] (read); O [B,H,Nq,d] and L [B,H,Nq] fp32
  *  (written, every element).  scale is the score multiplier (usually
- *  1/sqrt(d)); causal != 0 applies the mask above.
+ *  1/sqrt(d)); it must be finite and > 0, else FA_ERR_UNSUPPORTED.
+ *  causal != 0 applies the mask above.
  *
  *  num_splits chooses the key-split ("Flash-Decoding", the 51CTO FlashAttention V1/V2 notes, last paragraph
  *  of "Sequence Parallel") path, available for Nq == 1 with FA_BF16:

@@ -80,6 +80,7 @@ def test_fwd_rejects_bad_arguments(lib):
     assert fwd(lib, Q=None, Nk=0) == fa.FA_ERR_SHAPE
     assert fwd(lib, Q=None, Nq=20, Nk=16, causal=1) == fa.FA_ERR_SHAPE
     assert fwd(lib, Q=None, scale=-1.0) == fa.FA_ERR_UNSUPPORTED
+    assert fwd(lib, Q=None, scale=0.0) == fa.FA_ERR_UNSUPPORTED
     assert fwd(lib, Q=None, scale=float("nan")) == fa.FA_ERR_UNSUPPORTED
     assert fwd(lib, Q=None, scale=float("inf")) == fa.FA_ERR_UNSUPPORTED
     assert fwd(lib, Q=None, B=1 << 20, H=1 << 12) == fa.FA_ERR_SHAPE
@@ -117,6 +118,7 @@ def test_bwd_rejects_bad_arguments(lib):
     assert bwd(lib, Nq=17, Nk=16, causal=1) == fa.FA_ERR_SHAPE
     assert bwd(lib, Nq=4, Nk=0) == fa.FA_ERR_SHAPE
     assert bwd(lib, scale=-0.5) == fa.FA_ERR_UNSUPPORTED
+    assert bwd(lib, scale=0.0) == fa.FA_ERR_UNSUPPORTED
     for bad in (0, 8, -1):
         assert lib.fa_bwd_stages(*([A] * 9), 1, 1, 16, 16, 64, 0.125, 0, fa.FA_BF16, A, need, None,
                                  bad) == fa.FA_ERR_UNSUPPORTED
