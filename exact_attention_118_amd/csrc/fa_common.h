@@ -171,6 +171,63 @@ __device__ __forceinline__ void dma_tile(const bf16* __restrict__ g, int row0, i
     dma_part<D, ROWS, THREADS>(g, row0, nvalid, lds, tid, u);
 }
 
+// gfx9 buffer descriptor, word 3: 32-bit data format, so that raw (untyped)
+// buffer loads are range-checked per dword against the record count.
+constexpr int kRsrcWord3 = 0x00020000;
+
+// Raw buffer resource over `bytes` bytes at base: a load at a byte offset at
+// or past `bytes` returns zeros and touches no memory.  (The resource type
+// exists only in the device pass; the host pass, which never runs these
+// functions, sees an empty body, since clang otherwise drops the host launch
+// stubs of some kernels that use it.)
+#if __HIP_DEVICE_COMPILE__
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, int bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, bytes, kRsrcWord3);
+}
+#endif
+
+// Direct-to-LDS tile loads through a buffer resource (buffer_load_dwordx4 with
+// the lds flag: lane i of a wave instruction writes 16 bytes at the
+// instruction's LDS base + 16 i).  Rows [row0, row0 + ROWS) of a row-major
+// [nvalid, D] bf16 matrix go into a tile swizzled as swz lays it out; rows at
+// or past nvalid read as zeros.  A lane keeps the byte offsets of its PER
+// chunks for the whole kernel; the row base, the row count and the LDS
+// address are wave-uniform (scalar registers), so a load costs no vector-ALU
+// instruction.  The data is in LDS once every wave has waited for vmcnt and
+// passed a barrier.
+template <int D, int ROWS, int THREADS>
+struct BufTile {
+  static constexpr int CPR = D / 8;                  // 16-byte chunks per row
+  static constexpr int PER = ROWS * CPR / THREADS;   // loads per wave per tile
+  static_assert(PER * THREADS == ROWS * CPR && THREADS % 64 == 0, "tile split");
+  unsigned voff[PER];
+  int wave;  // wave-uniform
+  __device__ __forceinline__ BufTile(int wave_uniform, int lane) : wave(wave_uniform) {
+#pragma unroll
+    for (int u = 0; u < PER; ++u) {
+      const int slot = (wave * PER + u) * 64 + lane;
+      const int r = slot / CPR, pch = slot % CPR;
+      voff[u] = (unsigned)(r * D * 2 + ((pch ^ swz<D>(r)) << 4));
+    }
+  }
+  // Load u (0 <= u < PER) of this wave for the tile at row0 into lds.
+  __device__ __forceinline__ void part(const bf16* g, int row0, int nvalid, bf16* lds,
+                                       int u) const {
+    // (readfirstlane: the clamp compiles to a vector instruction, and a
+    // resource in vector registers would need a loop over its distinct values)
+#if __HIP_DEVICE_COMPILE__
+    const int rows = __builtin_amdgcn_readfirstlane(min(max(nvalid - row0, 0), ROWS));
+    const __amdgpu_buffer_rsrc_t rs = make_rsrc(g + (size_t)min(row0, nvalid) * D, rows * D * 2);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (FA_LDS void*)(lds + (wave * PER + u) * 64 * 8),
+                                             16, voff[u], 0, 0, 0);
+#endif
+  }
+  __device__ __forceinline__ void tile(const bf16* g, int row0, int nvalid, bf16* lds) const {
+#pragma unroll
+    for (int u = 0; u < PER; ++u) part(g, row0, nvalid, lds, u);
+  }
+};
+
 // Wait for this wave's outstanding vector-memory operations (including the
 // direct-to-LDS loads above).
 __device__ __forceinline__ void vm_wait_all() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }

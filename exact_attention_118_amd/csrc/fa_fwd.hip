@@ -56,25 +56,26 @@ void fwd_bf16_kernel(const bf16* __restrict__ Q, const bf16* __restrict__ K,
   constexpr int NNT = D / 32;  // 32-wide output tiles over the head dim
   constexpr int TILE = BC * D;  // elements per K or V tile
 
-  constexpr unsigned TB = TILE * 2;  // bytes per tile (a power of two)
   // K tiles j+1 (read) and j+2 (loading) at buffers 0/1, V tiles j (read) and
-  // j+1 (loading) at buffers 2/3; all swizzled (see swz).
+  // j+1 (loading) at buffers 2/3; all swizzled (see swz).  Tile j's buffers
+  // are j & 1; the loop below is unrolled by two so that every LDS address
+  // offset is a compile-time constant.
   __shared__ __attribute__((aligned(1024))) bf16 smem[4 * TILE];
   bf16* const sK0 = smem;
   bf16* const sV0 = smem + 2 * TILE;
 
   const int tid = threadIdx.x;
-  const int lane = tid & 63, wave = tid >> 6;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int half = lane >> 5, l32 = lane & 31;
   const int g = lane >> 4, s16 = lane & 15;
 
   // Grid: one workgroup per (query tile, batch*head); causal, one per pair of
   // query tiles (t, nqt-1-t) of a head, processed one after the other, so that
   // every workgroup has the same number of key tiles (a query tile's count
-  // grows with its index) and the two workgroups sharing a CU finish together
-  // instead of leaving it half used.  Remapped so each XCD serves a contiguous
-  // range of workgroups of the same heads (K/V stay in that XCD's L2; the 51CTO
-  // notes, "Thread Block Level 并行", grid order with the query tile fastest).
+  // grows with its index).  Remapped so each XCD serves a contiguous range of
+  // workgroups of the same heads (K/V stay in that XCD's L2; the 51CTO notes,
+  // "Thread Block Level 并行", grid order with the query tile fastest).
   const int nwg = CAUSAL ? (nqt + 1) / 2 : nqt;  // workgroups per head
   const int logical = xcd_remap(blockIdx.x, gridDim.x);
   const int bh = logical / nwg;
@@ -83,16 +84,50 @@ void fwd_bf16_kernel(const bf16* __restrict__ Q, const bf16* __restrict__ K,
   const bf16* Kh = K + (size_t)bh * Nk * D;
   const bf16* Vh = V + (size_t)bh * Nk * D;
 
+  using KV = BufTile<D, BC, kFwdThreads>;
+  const KV kv(wave, lane);
+  static_assert(2 * KV::PER == NKK, "one tile load every other score step");
+
+  // Byte offsets, within a tile, of this lane's LDS operand reads; the row
+  // block and the buffer are added as instruction offsets.  S^T = K Q^T: the
+  // A fragment of step st is K row (st&1)*32 + l32, 16-byte chunk
+  // 2*(st>>1) + half.  O^T += V^T P^T: step st reads V^T for the 16 keys of
+  // chunk st / NNT and head-dim tile st % NNT, two transpose reads
+  // (hi = 0, 1) per fragment.
+  unsigned ka[NKK], va[2 * NNT];
+  {
+    const SwzRow<D> krow(l32, half);
+    const int tr_row = (g >> 1) * 4 + (s16 >> 2);     // row in a 16-row chunk
+    const int tr_col = (g & 1) * 16 + (s16 & 3) * 4;  // column in a 32-wide tile
+    const SwzTr<D> vtr(tr_row, tr_col);
+#pragma unroll
+    for (int i = 0; i < NKK; ++i) ka[i] = krow.off(0, 2 * i);
+#pragma unroll
+    for (int hi = 0; hi < 2; ++hi)
+#pragma unroll
+      for (int nt = 0; nt < NNT; ++nt) va[hi * NNT + nt] = vtr.off(0, hi, nt * 32);
+  }
+  auto kfrag = [&](int buf, int st) {
+    return *at_byte<bf16x8>(sK0 + buf * TILE, ka[st >> 1] + (st & 1) * 32 * 2 * D);
+  };
+  auto vfrag = [&](int buf, int st) {
+    const unsigned rb = (st / NNT) * 16 * 2 * D;
+    const bf16* base = sV0 + buf * TILE;
+    return concat(lds_read_tr(to_lds(at_byte<bf16>(base, va[st % NNT] + rb))),
+                  lds_read_tr(to_lds(at_byte<bf16>(base, va[NNT + st % NNT] + rb))));
+  };
+  constexpr int KRING = 4, VRING = 3;
+
   for (int pass = 0; pass < (CAUSAL ? 2 : 1); ++pass) {
     const int qt = !CAUSAL ? t : (pass == 0 ? nqt - 1 - t : t);
     if (CAUSAL && pass == 1 && t == nqt - 1 - t) break;  // odd count: the middle tile once
-    if (pass == 1) __syncthreads();  // the first tile's last reads precede the new loads
+    if (pass == 1) __syncthreads();  // the first tile's last LDS reads precede the new loads
     const int q0 = qt * BR;
 
     // This lane's query row and its Q^T fragments (B operand of S^T = K Q^T).
     const int qrow = q0 + wave * 32 + l32;
     bf16x8 qf[NKK];
-  #pragma unroll
+#pragma unroll
     for (int kk = 0; kk < NKK; ++kk)
       qf[kk] = (qrow < Nq) ? *(const bf16x8*)(Q + qbase + (size_t)qrow * D + kk * 16 + half * 8)
                            : zero_bf16x8();
@@ -102,41 +137,20 @@ void fwd_bf16_kernel(const bf16* __restrict__ Q, const bf16* __restrict__ K,
     const int ntiles = (kend + BC - 1) / BC;
     const int wrow_lo = q0 + wave * 32;  // smallest query row of this wave
 
-    // Lane-constant parts of the LDS reads.
-    const int tr_row = (g >> 1) * 4 + (s16 >> 2);      // transpose read: row in a 16-row chunk
-    const int tr_col = (g & 1) * 16 + (s16 & 3) * 4;   // and column in a 32-wide tile
-    // S^T = K Q^T for one K tile: 2 x NKK MFMA steps (step st: key half st & 1,
-    // head-dim chunk st >> 1); the A fragment of step st is K row (st&1)*32 + l32,
-    // columns (st>>1)*16 + half*8 .. +8.
-    const SwzRow<D> krow(l32, half);
-    const SwzTr<D> vtr(tr_row, tr_col);
-    auto kfrag = [&](const SwzRow<D>& kr, int st) {
-      return *at_byte<bf16x8>(sK0, kr.off((st & 1) * 32, (st >> 1) * 2));
-    };
-    // O^T += V^T P^T: 4 x NNT steps (step st: 16-key chunk st / NNT, head-dim tile
-    // st % NNT); the A fragment is V^T by two transpose reads.
-    auto vfrag = [&](const SwzTr<D>& vt, int st) {
-      const int rb = (st / NNT) * 16, cb = (st % NNT) * 32;
-      return concat(lds_read_tr(to_lds(at_byte<bf16>(sV0, vt.off(rb, 0, cb)))),
-                    lds_read_tr(to_lds(at_byte<bf16>(sV0, vt.off(rb, 1, cb)))));
-    };
-    constexpr int KRING = 4, VRING = 3;
-
     float m_run = -INFINITY;  // reference of the exponentials (row max so far, log2 units)
     float l_run = 0.f;        // running sum of this lane half's probabilities
     f32x16 oacc[NNT];
-  #pragma unroll
+#pragma unroll
     for (int nt = 0; nt < NNT; ++nt) oacc[nt] = (f32x16){};
 
-    using KD = DmaTile<D, BC, kFwdThreads>;
     // Keys past the end and, causal, keys after the row's diagonal get score
     // -inf.  Only tiles that cross the diagonal or the end need it; lane holds
     // row qrow, keys k0 + mt*32 + (i/4)*8 + half*4 + i%4.
     auto mask_tile = [&](f32x16 (&sc)[2], int k0) {
       if ((k0 + BC > Nk) || (CAUSAL && (k0 + BC - 1 > wrow_lo + off))) {
-  #pragma unroll
+#pragma unroll
         for (int mt = 0; mt < 2; ++mt)
-  #pragma unroll
+#pragma unroll
           for (int i = 0; i < 16; ++i) {
             const int key = k0 + mt * 32 + (i >> 2) * 8 + half * 4 + (i & 3);
             const bool vis = (key < Nk) && (!CAUSAL || key <= qrow + off);
@@ -144,37 +158,46 @@ void fwd_bf16_kernel(const bf16* __restrict__ Q, const bf16* __restrict__ K,
           }
       }
     };
-
-    // Prologue: K tiles 0 and 1, V tile 0; scores, mask and row max of tile 0.
-    dma_tile<D, BC, kFwdThreads>(Kh, 0, Nk, sK0, tid);
-    dma_tile<D, BC, kFwdThreads>(Kh, BC, Nk, sK0 + TILE, tid);
-    dma_tile<D, BC, kFwdThreads>(Vh, 0, Nk, sV0, tid);
-    vm_wait_all();
-    __syncthreads();
-    f32x16 snext[2] = {(f32x16){}, (f32x16){}};
-    {
+    // Scores of one K tile (2 x NKK MFMA steps) from LDS buffer buf.
+    auto scores = [&](int buf, f32x16 (&sc)[2]) {
       bf16x8 ring[KRING];
-  #pragma unroll
-      for (int st = 0; st < KRING; ++st) ring[st] = kfrag(krow, st);
-  #pragma unroll
+#pragma unroll
+      for (int st = 0; st < KRING; ++st) ring[st] = kfrag(buf, st);
+      sc[0] = (f32x16){};
+      sc[1] = (f32x16){};
+#pragma unroll
       for (int st = 0; st < 2 * NKK; ++st) {
         const bf16x8 a = ring[st % KRING];
-        if (st + KRING < 2 * NKK) ring[st % KRING] = kfrag(krow, st + KRING);
-        snext[st & 1] = mfma32(a, qf[st >> 1], snext[st & 1]);
+        if (st + KRING < 2 * NKK) ring[st % KRING] = kfrag(buf, st + KRING);
+        sc[st & 1] = mfma32(a, qf[st >> 1], sc[st & 1]);
       }
-    }
-    mask_tile(snext, 0);
-    float mx_next = -INFINITY;
-  #pragma unroll
-    for (int mt = 0; mt < 2; ++mt)
-  #pragma unroll
-      for (int i = 0; i < 16; ++i) mx_next = fmaxf(mx_next, snext[mt][i]);
-    mx_next = fmaxf(mx_next, wave_shfl_xor(mx_next, 32));
+    };
+    auto row_max = [&](const f32x16 (&sc)[2]) {
+      float mx = -INFINITY;
+#pragma unroll
+      for (int mt = 0; mt < 2; ++mt)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) mx = fmaxf(mx, sc[mt][i]);
+      return fmaxf(mx, wave_shfl_xor(mx, 32));
+    };
+
+    // Prologue: K tiles 0 and 1, V tile 0; scores, mask and row max of tile 0.
+    kv.tile(Kh, 0, Nk, sK0);
+    kv.tile(Kh, BC, Nk, sK0 + TILE);
+    kv.tile(Vh, 0, Nk, sV0);
+    vm_wait_all();
+    __syncthreads();
+    f32x16 sA[2], sB[2];
+    scores(0, sA);
+    mask_tile(sA, 0);
+    float mx_next = row_max(sA);
     __syncthreads();  // every wave is done with K tile 0 before tile 2 replaces it
 
-    for (int j = 0; j < ntiles; ++j) {
+    // One key tile j (P = buffer parity j & 1, a constant at both inlined
+    // call sites): scores of tile j are in scur, those of tile j+1 go to snext.
+    auto tile_step = [&](const int P, int j, f32x16 (&scur)[2], f32x16 (&snext)[2])
+                         __attribute__((always_inline)) {
       const int k0 = j * BC;
-      f32x16 scur[2] = {snext[0], snext[1]};
       // Online softmax (the CSDN post "Flash Attention1", 例子说明: running max
       // and running sum), normalised once in the epilogue.  The reference m_run
       // of the exponentials moves to the new row max only when some row of the
@@ -189,7 +212,7 @@ void fwd_bf16_kernel(const bf16* __restrict__ Q, const bf16* __restrict__ K,
         const float m_new = fmaxf(m_run, m_tile);
         const float alpha = fast_exp2(m_run - (m_new == -INFINITY ? 0.f : m_new));
         l_run *= alpha;
-  #pragma unroll
+#pragma unroll
         for (int nt = 0; nt < NNT; ++nt) oacc[nt] *= alpha;
         m_run = m_new;
       }
@@ -200,33 +223,30 @@ void fwd_bf16_kernel(const bf16* __restrict__ Q, const bf16* __restrict__ K,
       // loads of K tile j+2 (over tile j's buffer, last read for tile j's
       // scores) and V tile j+1.  Step st converts the pair of probabilities
       // pf[st/4][2*(st%4) .. +1] (keys of chunk st/4).  The last iterations
-      // also compute scores of a stale buffer and load clamped rows nobody
-      // reads: that extra work keeps this block free of branches, so the three
-      // kinds of work stay interleaved.
+      // also compute scores of a stale buffer and load rows past the end (as
+      // zeros): that extra work keeps this block free of branches, so the
+      // three kinds of work stay interleaved.
       bf16x8 pf[4];
       float rs0 = 0.f, rs1 = 0.f;
       {
-        const SwzRow<D> kr = krow.flipped(((j + 1) & 1) * TB);
         bf16x8 ring[KRING];
+#pragma unroll
+        for (int st = 0; st < KRING; ++st) ring[st] = kfrag(1 - P, st);
         snext[0] = (f32x16){};
         snext[1] = (f32x16){};
-  #pragma unroll
-        for (int st = 0; st < KRING; ++st) ring[st] = kfrag(kr, st);
-  #pragma unroll
+#pragma unroll
         for (int st = 0; st < 2 * NKK; ++st) {
           const bf16x8 a = ring[st % KRING];
-          if (st + KRING < 2 * NKK) ring[st % KRING] = kfrag(kr, st + KRING);
+          if (st + KRING < 2 * NKK) ring[st % KRING] = kfrag(1 - P, st + KRING);
           snext[st & 1] = mfma32(a, qf[st >> 1], snext[st & 1]);
           if ((st & 1) == 0) {
-            static_assert(2 * KD::PER == NKK, "one load every other step");
             const int di = st >> 1;
-            if (di < KD::PER)
-              dma_part<D, BC, kFwdThreads>(Kh, k0 + 2 * BC, Nk, sK0 + (j & 1) * TILE, tid, di);
+            if (di < KV::PER)
+              kv.part(Kh, k0 + 2 * BC, Nk, sK0 + P * TILE, di);
             else
-              dma_part<D, BC, kFwdThreads>(Vh, k0 + BC, Nk, sV0 + ((j + 1) & 1) * TILE, tid,
-                                           di - KD::PER);
+              kv.part(Vh, k0 + BC, Nk, sV0 + (1 - P) * TILE, di - KV::PER);
           }
-  #pragma unroll
+#pragma unroll
           for (int h = 0; h < 32 / (2 * NKK); h += 2) {
             const int el = st * (32 / (2 * NKK)) + h;  // probability index 0..31
             const int kc = el >> 3, e = el & 7;
@@ -249,17 +269,16 @@ void fwd_bf16_kernel(const bf16* __restrict__ Q, const bf16* __restrict__ K,
 
       // O^T += V^T P^T for tile j, interleaved with the row max of tile j+1.
       {
-        const SwzTr<D> vt = vtr.flipped((j & 1) * TB);
         bf16x8 ring[VRING];
         float mxa = -INFINITY, mxb = -INFINITY;
-  #pragma unroll
-        for (int st = 0; st < VRING; ++st) ring[st] = vfrag(vt, st);
-  #pragma unroll
+#pragma unroll
+        for (int st = 0; st < VRING; ++st) ring[st] = vfrag(P, st);
+#pragma unroll
         for (int st = 0; st < 4 * NNT; ++st) {
           const bf16x8 a = ring[st % VRING];
-          if (st + VRING < 4 * NNT) ring[st % VRING] = vfrag(vt, st + VRING);
+          if (st + VRING < 4 * NNT) ring[st % VRING] = vfrag(P, st + VRING);
           oacc[st % NNT] = mfma32(a, pf[st / NNT], oacc[st % NNT]);
-  #pragma unroll
+#pragma unroll
           for (int h = 0; h < 32 / (4 * NNT); h += 2) {
             const int el = st * (32 / (4 * NNT)) + h;
             mxa = fmaxf(mxa, snext[el >> 4][el & 15]);
@@ -272,6 +291,11 @@ void fwd_bf16_kernel(const bf16* __restrict__ Q, const bf16* __restrict__ K,
       }
       vm_wait_all();  // this wave's part of tiles K j+2 and V j+1 has landed
       __syncthreads();
+    };
+
+    for (int j = 0; j < ntiles; j += 2) {
+      tile_step(0, j, sA, sB);
+      if (j + 1 < ntiles) tile_step(1, j + 1, sB, sA);
     }
 
     // Epilogue: O = O_acc / l, L = (m + log2 l) * ln 2.
@@ -279,12 +303,12 @@ void fwd_bf16_kernel(const bf16* __restrict__ Q, const bf16* __restrict__ K,
     if (qrow < Nq) {
       const float inv = 1.f / l_tot;
       bf16* orow = O + qbase + (size_t)qrow * D;
-  #pragma unroll
+#pragma unroll
       for (int nt = 0; nt < NNT; ++nt)
-  #pragma unroll
+#pragma unroll
         for (int gg = 0; gg < 4; ++gg) {
           bf16x4 v;
-  #pragma unroll
+#pragma unroll
           for (int e = 0; e < 4; ++e) v[e] = (bf16)(oacc[nt][gg * 4 + e] * inv);
           *(bf16x4*)(orow + nt * 32 + gg * 8 + half * 4) = v;
         }
