@@ -81,6 +81,7 @@ SplitWs split_ws(int BH, int d, int splits) {
 }
 
 // Backward workspace: D [B*H*Nq] fp32, then L*log2(e) [B*H*Nq] fp32.
+// Backward workspace: the fp32 pairs (L*log2(e), D) of every query row.
 size_t bwd_ws_half(int BH, int Nq) { return round_up((size_t)BH * Nq * sizeof(float), kWsAlign); }
 size_t bwd_ws_bytes(int BH, int Nq) { return 2 * bwd_ws_half(BH, Nq); }
 
@@ -177,11 +178,8 @@ fa_status fa_bwd_stages(const void* Q, const void* K, const void* V, const void*
   if (Nq > 0 && (!workspace || workspace_bytes < bwd_ws_bytes(B * H, Nq))) return FA_ERR_WORKSPACE;
   if (Nq > 0 && !aligned(workspace)) return FA_ERR_ALIGN;
   fa::BwdArgs a{Q, K, V, O, L, dO, dQ, dK, dV, B, H, Nq, Nk, d, scale, causal != 0,
-                nullptr, nullptr};
-  if (Nq > 0) {
-    a.Dvec = static_cast<float*>(workspace);
-    a.L2 = reinterpret_cast<float*>(static_cast<char*>(workspace) + bwd_ws_half(B * H, Nq));
-  }
+                nullptr};
+  if (Nq > 0) a.LD = static_cast<float*>(workspace);
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
   const hipError_t e =
       (dtype == FA_BF16) ? fa::launch_bwd_bf16(a, stages, s) : fa::launch_bwd_f32(a, stages, s);

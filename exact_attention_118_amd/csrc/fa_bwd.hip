@@ -56,13 +56,13 @@ namespace fa {
 namespace {
 
 // D_i = sum_k dO_ik O_ik in fp32, and L2_i = L_i * log2(e) (the exponent
-// base of the kernels below).
+// base of the kernels below), stored as the pair LD[i] = (L2_i, D_i) so that
+// one load brings both.
 template <int D, typename T>
 __global__ __launch_bounds__(256) void bwd_pre_kernel(const T* __restrict__ O,
                                                       const T* __restrict__ dO,
                                                       const float* __restrict__ L,
-                                                      float* __restrict__ Dvec,
-                                                      float* __restrict__ L2, long rows) {
+                                                      float* __restrict__ LD, long rows) {
   constexpr int TPR = D / 8;  // threads per row, 8 elements each
   constexpr int RPB = 256 / TPR;
   const long row = (long)blockIdx.x * RPB + threadIdx.x / TPR;
@@ -76,8 +76,10 @@ __global__ __launch_bounds__(256) void bwd_pre_kernel(const T* __restrict__ O,
 #pragma unroll
   for (int msk = TPR / 2; msk >= 1; msk >>= 1) acc += __shfl_xor(acc, msk, 64);
   if (row < rows && part == 0) {
-    Dvec[row] = acc;
-    L2[row] = L[row] * kLog2e;
+    float2 v;
+    v.x = L[row] * kLog2e;
+    v.y = acc;
+    *(float2*)(LD + 2 * row) = v;
   }
 }
 
@@ -91,24 +93,26 @@ constexpr int kKvThreads = kKvWaves * 64;
 template <int D, bool CAUSAL>
 __global__ __launch_bounds__(kKvThreads, 1) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void bwd_dkdv_bf16_kernel(const bf16* __restrict__ Q, const bf16* __restrict__ K,
-                          const bf16* __restrict__ V, const float* __restrict__ L2vec,
-                          const bf16* __restrict__ dO, const float* __restrict__ Dvec,
-                          bf16* __restrict__ dK, bf16* __restrict__ dV, int Nq, int Nk, int nkt,
-                          int BH, int hpx, float c, float scale, int off) {
+                          const bf16* __restrict__ V, const bf16* __restrict__ dO,
+                          const float* __restrict__ LD, bf16* __restrict__ dK,
+                          bf16* __restrict__ dV, int Nq, int Nk, int nkt, int BH, int hpx,
+                          float c, float scale, int off) {
   constexpr int BC = kKvBC, BR = kKvBR;
   constexpr int CPR = D / 8;     // 16-byte chunks per row
   constexpr int NKK = D / 16;    // MFMA k-steps over the head dim
   constexpr int NNT = D / 32;    // 32-wide tiles over the head dim
   constexpr int KTILE = BC * D;  // elements of the K block
   constexpr int QTILE = BR * D;  // elements of one Q or dO tile
-  constexpr unsigned QB = QTILE * 2;           // bytes of one Q or dO tile (a power of two)
-  constexpr int NIQ = BR * CPR / 64;           // direct-to-LDS instructions per Q (or dO) tile
+  constexpr int NIQ = BR * CPR / 64;           // direct-to-LDS loads per Q (or dO) tile
   constexpr int IPW = 2 * NIQ / kKvWaves;      // ... per wave for both tiles
   static_assert(IPW * kKvWaves == 2 * NIQ && IPW >= 1, "query tile load split");
-  static_assert(2 * BR == 64, "one dword load per lane carries L2 and D of a block");
+  static_assert(2 * BR == 64, "one dword load per lane carries the (L2, D) pairs of a block");
+  static_assert(NIQ % IPW == 0, "a wave loads from one tile");
 
-  // [K block | Q buffers 0,1 | dO buffers 0,1], all swizzled (see swz); L2 and
-  // D of the query block per buffer.
+  // [K block | Q buffers 0,1 | dO buffers 0,1], all swizzled (see swz); the
+  // (L*log2 e, D) pairs of the query block per buffer.  Query block it uses
+  // buffers it & 1; the loop is unrolled by two so that their offsets are
+  // constants.
   __shared__ __attribute__((aligned(1024))) bf16 smem[KTILE + 4 * QTILE];
   __shared__ __attribute__((aligned(16))) float sLD[2][2 * BR];
   bf16* const sK = smem;
@@ -116,7 +120,8 @@ void bwd_dkdv_bf16_kernel(const bf16* __restrict__ Q, const bf16* __restrict__ K
   bf16* const sdO0 = smem + KTILE + 2 * QTILE;
 
   const int tid = threadIdx.x;
-  const int lane = tid & 63, wave = tid >> 6;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int half = lane >> 5, l32 = lane & 31;
   const int g = lane >> 4, s16 = lane & 15;
 
@@ -141,31 +146,43 @@ void bwd_dkdv_bf16_kernel(const bf16* __restrict__ Q, const bf16* __restrict__ K
   const int qb_first = CAUSAL ? max(0, k0 - off) / BR : 0;
   const int nloop = nqb - qb_first;
 
-  // Q and dO rows of query block qb into buffer buf (direct-to-LDS,
-  // swizzled), and its L2 and D (one dword per lane of the last wave).
+  // Direct-to-LDS loads of query block qb through buffer resources: this
+  // wave's IPW chunks of the Q (waves 0 .. 8/2-1) or dO tile, and (last
+  // wave) the 32 (L2, D) pairs; rows past Nq read as zeros.  Lane offsets
+  // are fixed; the rest is wave-uniform.
+  const int tsel = (wave * IPW) / NIQ;  // 0: Q, 1: dO
+  const bf16* const qsrc = (tsel ? dO : Q) + qbase;
+  bf16* const qdst0 = (tsel ? sdO0 : sQ0) + ((wave * IPW) % NIQ) * 64 * 8;
+  unsigned qoff[IPW];
+#pragma unroll
+  for (int u = 0; u < IPW; ++u) {
+    const int slot = ((wave * IPW) % NIQ + u) * 64 + lane;
+    const int r = slot / CPR, pch = slot % CPR;
+    qoff[u] = (unsigned)(r * D * 2 + ((pch ^ swz<D>(r)) << 4));
+  }
   auto load_block = [&](int qb, int buf) {
     const int qi0 = qb * BR;
+#if __HIP_DEVICE_COMPILE__
+    const int rows = __builtin_amdgcn_readfirstlane(min(Nq - qi0, BR));
+    const __amdgpu_buffer_rsrc_t rq = make_rsrc(qsrc + (size_t)qi0 * D, rows * D * 2);
 #pragma unroll
-    for (int u = 0; u < IPW; ++u) {
-      const int gi = wave * IPW + u;
-      const int tsel = gi / NIQ;  // 0: Q, 1: dO
-      const int slot0 = (gi - tsel * NIQ) * 64;
-      const int slot = slot0 + lane;
-      const int r = slot / CPR, pch = slot % CPR;
-      const int q = min(qi0 + r, Nq - 1);
-      const bf16* src = (tsel ? dO : Q) + qbase + (size_t)q * D + ((pch ^ swz<D>(r)) << 3);
-      bf16* dst = (tsel ? sdO0 : sQ0) + buf * QTILE + slot0 * 8;
-      __builtin_amdgcn_global_load_lds((const void*)src, (FA_LDS void*)dst, 16, 0, 0);
-    }
+    for (int u = 0; u < IPW; ++u)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(
+          rq, (FA_LDS void*)(qdst0 + buf * QTILE + u * 64 * 8), 16, qoff[u], 0, 0, 0);
     if (wave == kKvWaves - 1) {
-      const int q = min(qi0 + (lane & (BR - 1)), Nq - 1);
-      const float* src = (lane < BR ? L2vec : Dvec) + lbase + q;
-      __builtin_amdgcn_global_load_lds((const void*)src, (FA_LDS void*)&sLD[buf][0], 4, 0, 0);
+      const __amdgpu_buffer_rsrc_t rl = make_rsrc(LD + 2 * (lbase + qi0), rows * 8);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rl, (FA_LDS void*)&sLD[buf][0], 4, lane * 4, 0,
+                                               0, 0);
     }
+#endif
   };
 
-  // K block (rows clamped to Nk - 1) and the first query block.
-  dma_tile<D, BC, kKvThreads>(K + kbase, k0, Nk, sK, tid);
+  // K block (rows past Nk read as zeros) and the first query block.
+  {
+    using KB = BufTile<D, BC, kKvThreads>;
+    const KB kb(wave, lane);
+    kb.tile(K + kbase, k0, Nk, sK);
+  }
   if (nloop > 0) load_block(qb_first, 0);
   // This wave's V rows in registers (B operand of dP = dO V^T).
   bf16x8 vf[NKK];
@@ -182,32 +199,48 @@ void bwd_dkdv_bf16_kernel(const bf16* __restrict__ Q, const bf16* __restrict__ K
   vm_wait_all();
   __syncthreads();
 
-  const int tr_row = (g >> 1) * 4 + (s16 >> 2);
-  const int tr_col = (g & 1) * 16 + (s16 & 3) * 4;
-  const SwzRow<D> qrow_sw(l32, half);  // Q / dO rows l32 of a block
-  const SwzRow<D> krow_sw(SwzRow<D>(l32, half).x + (unsigned)(wave * 64 * D));  // K rows kw0 - k0 + l32
-  const SwzTr<D> tr_sw(tr_row, tr_col);
+  // Byte offsets, within a tile, of this lane's LDS operand reads (buffers
+  // and row blocks are instruction offsets): Q/dO rows l32 and K rows
+  // kw0 - k0 + l32, 16-byte chunk 2*kk + half; transpose reads of dO^T / Q^T.
+  unsigned qa[NKK], ka[NKK], ta[2 * NNT];
+  {
+    const SwzRow<D> qrow_sw(l32, half);
+    const SwzRow<D> krow_sw(SwzRow<D>(l32, half).x + (unsigned)(wave * 64 * D));
+    const int tr_row = (g >> 1) * 4 + (s16 >> 2);
+    const int tr_col = (g & 1) * 16 + (s16 & 3) * 4;
+    const SwzTr<D> tr_sw(tr_row, tr_col);
+#pragma unroll
+    for (int kk = 0; kk < NKK; ++kk) {
+      qa[kk] = qrow_sw.off(0, kk * 2);
+      ka[kk] = krow_sw.off(0, kk * 2);
+    }
+#pragma unroll
+    for (int hi = 0; hi < 2; ++hi)
+#pragma unroll
+      for (int nt = 0; nt < NNT; ++nt) ta[hi * NNT + nt] = tr_sw.off(0, hi, nt * 32);
+  }
 
-  for (int it = 0; it < nloop; ++it) {
-    const int buf = it & 1;
+  // One query block (P = buffer parity it & 1, a constant at both inlined
+  // call sites).
+  auto block_step = [&](const int P, int it) __attribute__((always_inline)) {
     const int qi0 = (qb_first + it) * BR;
-    if (it + 1 < nloop) load_block(qb_first + it + 1, buf ^ 1);
+    if (it + 1 < nloop) load_block(qb_first + it + 1, 1 - P);
 
     // Causal: a wave whose keys all lie after every row of the block has no work.
     const bool wave_idle = CAUSAL && (kw0 > qi0 + BR - 1 + off);
     if (!wave_idle) {
-      const SwzRow<D> qs = qrow_sw.flipped(buf * QB);
-      const SwzTr<D> ts = tr_sw.flipped(buf * QB);
-      const float* tLD = sLD[buf];
+      const bf16* const tQ = sQ0 + P * QTILE;
+      const bf16* const tdO = sdO0 + P * QTILE;
+      const float* tLD = sLD[P];
       // S = Q K^T and dP = dO V^T: 32 rows x this wave's 32 keys.  Step kk
       // needs the Q, K and dO fragments of head-dim chunk kk; those of step
       // kk + 1 are read before step kk's MFMAs are issued.
       f32x16 sacc = (f32x16){}, dpacc = (f32x16){};
       {
         auto ldstep = [&](int kk, bf16x8* f) {
-          f[0] = *at_byte<bf16x8>(sQ0, qs.off(0, kk * 2));
-          f[1] = *at_byte<bf16x8>(sK, krow_sw.off(0, kk * 2));
-          f[2] = *at_byte<bf16x8>(sdO0, qs.off(0, kk * 2));
+          f[0] = *at_byte<bf16x8>(tQ, qa[kk]);
+          f[1] = *at_byte<bf16x8>(sK, ka[kk]);
+          f[2] = *at_byte<bf16x8>(tdO, qa[kk]);
         };
         bf16x8 fa[3], fb[3];
         ldstep(0, fa);
@@ -233,29 +266,40 @@ void bwd_dkdv_bf16_kernel(const bf16* __restrict__ Q, const bf16* __restrict__ K
           if (!vis) sacc[i] = -INFINITY;
         }
       }
-      // P = exp2(S*c - L2) and dS = P * (dP - D) for the 8 rows of chunk kc
-      // (elements i = kc*8 .. kc*8+7).
+      // P = exp2(S*c - L2) and dS = P * (dP - D) for the pair of rows of
+      // elements i, i+1 (i even) of chunk kc = i / 8, in two halves: the
+      // probabilities, then dS and both conversions to bf16.
       bf16x8 pf[2], dsf[2];
-      auto pds = [&](int kc, int i) {
-        const int i4 = i >> 2, e = i & 3;
-        const int ql = i4 * 8 + half * 4 + e;
-        const float p = fast_exp2(fmaf(sacc[i], c, -tLD[ql]));
-        const float ds = p * (dpacc[i] - tLD[BR + ql]);
-        pf[kc][(i4 & 1) * 4 + e] = (bf16)p;
-        dsf[kc][(i4 & 1) * 4 + e] = (bf16)ds;
+      float pp[2];
+      auto pds_p = [&](int i) {
+        const int ql = (i >> 2) * 8 + half * 4 + (i & 3);  // rows ql, ql + 1
+        const float2 a = *(const float2*)(tLD + 2 * ql);
+        const float2 b = *(const float2*)(tLD + 2 * ql + 2);
+        pp[0] = fast_exp2(fmaf(sacc[i], c, -a.x));
+        pp[1] = fast_exp2(fmaf(sacc[i + 1], c, -b.x));
+        return make_float2(a.y, b.y);
+      };
+      auto pds_ds = [&](int i, float2 dd) {
+        const int kc = i >> 3, e = i & 7;
+        pf[kc][e] = (bf16)pp[0];
+        pf[kc][e + 1] = (bf16)pp[1];
+        dsf[kc][e] = (bf16)(pp[0] * (dpacc[i] - dd.x));
+        dsf[kc][e + 1] = (bf16)(pp[1] * (dpacc[i + 1] - dd.y));
       };
       // dV^T += dO^T P and dK^T += Q^T dS over the 16 rows of chunk kc
       // (2 * NNT MFMAs, A operands by transpose reads); with `overlap`, the
       // probabilities of chunk kc + 1 are computed between them.
       auto dvdk = [&](int kc, bool overlap) {
         auto afrag = [&](int st) {  // st: (head-dim tile st/2, dO^T if even else Q^T)
-          const bf16* base = (st & 1) ? sQ0 : sdO0;
-          const int cb = (st >> 1) * 32;
-          return concat(lds_read_tr(to_lds(at_byte<bf16>(base, ts.off(kc * 16, 0, cb)))),
-                        lds_read_tr(to_lds(at_byte<bf16>(base, ts.off(kc * 16, 1, cb)))));
+          const bf16* base = (st & 1) ? tQ : tdO;
+          const unsigned rb = kc * 16 * 2 * D;
+          return concat(lds_read_tr(to_lds(at_byte<bf16>(base, ta[st >> 1] + rb))),
+                        lds_read_tr(to_lds(at_byte<bf16>(base, ta[NNT + (st >> 1)] + rb))));
         };
         constexpr int NS = 2 * NNT, RING = 2;
+        static_assert(NS == 4 || NS == 8, "two or four probability pairs per chunk step pair");
         bf16x8 ring[RING];
+        float2 dd;
 #pragma unroll
         for (int st = 0; st < RING; ++st) ring[st] = afrag(st);
 #pragma unroll
@@ -265,21 +309,41 @@ void bwd_dkdv_bf16_kernel(const bf16* __restrict__ Q, const bf16* __restrict__ K
           if (st & 1) dkacc[st >> 1] = mfma32(a, dsf[kc], dkacc[st >> 1]);
           else dvacc[st >> 1] = mfma32(a, pf[kc], dvacc[st >> 1]);
           if (overlap) {
-#pragma unroll
-            for (int h = 0; h < 8 / NS; ++h) pds(kc + 1, (kc + 1) * 8 + st * (8 / NS) + h);
-            pin(pf[kc + 1]);
-            pin(dsf[kc + 1]);
+            // NS steps carry the 4 pairs of chunk kc + 1: D = 128 takes a
+            // pair per two steps (probabilities, then dS), D = 64 a pair per
+            // step.
+            if constexpr (NS == 8) {
+              const int i = (kc + 1) * 8 + (st >> 1) * 2;
+              if ((st & 1) == 0) {
+                dd = pds_p(i);
+                pin(pp[0]);
+                pin(pp[1]);
+              } else {
+                pds_ds(i, dd);
+                pin(pf[kc + 1]);
+                pin(dsf[kc + 1]);
+              }
+            } else {
+              const int i = (kc + 1) * 8 + st * 2;
+              pds_ds(i, pds_p(i));
+              pin(pf[kc + 1]);
+              pin(dsf[kc + 1]);
+            }
           }
           __builtin_amdgcn_sched_barrier(0);
         }
       };
 #pragma unroll
-      for (int i = 0; i < 8; ++i) pds(0, i);
+      for (int i = 0; i < 8; i += 2) pds_ds(i, pds_p(i));
       dvdk(0, true);   // probabilities of rows 16..31 overlap the MFMAs of rows 0..15
       dvdk(1, false);
     }
     vm_wait_all();  // this wave's part of the next query block has landed
     __syncthreads();
+  };
+  for (int it = 0; it < nloop; it += 2) {
+    block_step(0, it);
+    if (it + 1 < nloop) block_step(1, it + 1);
   }
 
   // Epilogue: dK = scale * dK_acc, dV = dV_acc; lane holds key mykey.
@@ -311,8 +375,8 @@ constexpr int kDqThreads = 256;
 template <int D, bool CAUSAL>
 __global__ __launch_bounds__(kDqThreads, 2) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void bwd_dq_bf16_kernel(const bf16* __restrict__ Q, const bf16* __restrict__ K,
-                        const bf16* __restrict__ V, const float* __restrict__ L,
-                        const bf16* __restrict__ dO, const float* __restrict__ Dvec,
+                        const bf16* __restrict__ V, const bf16* __restrict__ dO,
+                        const float* __restrict__ LD,
                         bf16* __restrict__ dQ, int Nq, int Nk, int nqt, float c, float scale,
                         int off) {
   constexpr int BR = kDqBR, BC = kDqBC;
@@ -320,15 +384,16 @@ void bwd_dq_bf16_kernel(const bf16* __restrict__ Q, const bf16* __restrict__ K,
   constexpr int NNT = D / 32;
   constexpr int TILE = BC * D;
 
-  constexpr unsigned TB = TILE * 2;  // bytes per tile (a power of two)
   // K tiles (buffers 0/1) and V tiles (buffers 2/3), swizzled (see swz) and
-  // double-buffered: tile j+1 loads while tile j is read.
+  // double-buffered: tile j+1 loads while tile j (buffers j & 1) is read.
+  // The key loop is unrolled by two so that buffer offsets are constants.
   __shared__ __attribute__((aligned(1024))) bf16 smem[4 * TILE];
   bf16* const sK0 = smem;
   bf16* const sV0 = smem + 2 * TILE;
 
   const int tid = threadIdx.x;
-  const int lane = tid & 63, wave = tid >> 6;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int half = lane >> 5, l32 = lane & 31;
   const int g = lane >> 4, s16 = lane & 15;
 
@@ -342,6 +407,40 @@ void bwd_dq_bf16_kernel(const bf16* __restrict__ Q, const bf16* __restrict__ K,
   const bf16* Kh = K + (size_t)bh * Nk * D;
   const bf16* Vh = V + (size_t)bh * Nk * D;
 
+  using KV = BufTile<D, BC, kDqThreads>;
+  const KV kv(wave, lane);
+  static_assert(2 * KV::PER <= 2 * NKK, "tile loads fit the first score half");
+
+  // Byte offsets, within a tile, of this lane's LDS operand reads (row
+  // blocks and buffers are instruction offsets).  S^T and dP^T: the A
+  // fragment of step st is row mt*32 + l32 of K (even st) or V (odd st),
+  // 16-byte chunk 2*(st>>1) + half.  dQ^T += K^T dS^T: step st reads K^T for
+  // the 16 keys of chunk st / NNT of half mt and head-dim tile st % NNT.
+  unsigned ra[NKK], ta[2 * NNT];
+  {
+    const SwzRow<D> rowsw(l32, half);
+    const int tr_row = (g >> 1) * 4 + (s16 >> 2);
+    const int tr_col = (g & 1) * 16 + (s16 & 3) * 4;
+    const SwzTr<D> trsw(tr_row, tr_col);
+#pragma unroll
+    for (int i = 0; i < NKK; ++i) ra[i] = rowsw.off(0, 2 * i);
+#pragma unroll
+    for (int hi = 0; hi < 2; ++hi)
+#pragma unroll
+      for (int nt = 0; nt < NNT; ++nt) ta[hi * NNT + nt] = trsw.off(0, hi, nt * 32);
+  }
+  auto sfrag = [&](int buf, int mt, int st) {
+    const bf16* base = ((st & 1) ? sV0 : sK0) + buf * TILE;
+    return *at_byte<bf16x8>(base, ra[st >> 1] + mt * 32 * 2 * D);
+  };
+  auto kt_frag = [&](int buf, int mt, int st) {
+    const unsigned rb = (mt * 32 + (st / NNT) * 16) * 2 * D;
+    const bf16* base = sK0 + buf * TILE;
+    return concat(lds_read_tr(to_lds(at_byte<bf16>(base, ta[st % NNT] + rb))),
+                  lds_read_tr(to_lds(at_byte<bf16>(base, ta[NNT + st % NNT] + rb))));
+  };
+  constexpr int SRING = 4, TRING = 3;
+
   for (int pass = 0; pass < (CAUSAL ? 2 : 1); ++pass) {
     const int qt = !CAUSAL ? t : (pass == 0 ? nqt - 1 - t : t);
     if (CAUSAL && pass == 1 && t == nqt - 1 - t) break;  // odd count: the middle tile once
@@ -351,87 +450,80 @@ void bwd_dq_bf16_kernel(const bf16* __restrict__ Q, const bf16* __restrict__ K,
     // This lane's query row: Q^T and dO^T fragments (B operands), L and D.
     const int qrow = q0 + wave * 32 + l32;
     bf16x8 qf[NKK], dof[NKK];
-  #pragma unroll
+#pragma unroll
     for (int kk = 0; kk < NKK; ++kk) {
       const size_t o = qbase + (size_t)qrow * D + kk * 16 + half * 8;
       qf[kk] = (qrow < Nq) ? *(const bf16x8*)(Q + o) : zero_bf16x8();
       dof[kk] = (qrow < Nq) ? *(const bf16x8*)(dO + o) : zero_bf16x8();
     }
-    const float l2 = (qrow < Nq) ? L[(size_t)bh * Nq + qrow] * kLog2e : INFINITY;
-    const float drow = (qrow < Nq) ? Dvec[(size_t)bh * Nq + qrow] : 0.f;
+    const float l2 = (qrow < Nq) ? LD[2 * ((size_t)bh * Nq + qrow)] : INFINITY;
+    const float drow = (qrow < Nq) ? LD[2 * ((size_t)bh * Nq + qrow) + 1] : 0.f;
 
     const int kend = CAUSAL ? min(Nk, q0 + BR + off) : Nk;
     const int ntiles = (kend + BC - 1) / BC;
     const int wrow_lo = q0 + wave * 32;
 
-    const int tr_row = (g >> 1) * 4 + (s16 >> 2);
-    const int tr_col = (g & 1) * 16 + (s16 & 3) * 4;
-    // S^T and dP^T for one 32-key half mt: 2 x NKK steps alternating the K
-    // (even step, S^T) and V (odd step, dP^T) row fragments.
-    const SwzRow<D> rowsw(l32, half);
-    const SwzTr<D> trsw(tr_row, tr_col);
-    auto sfrag = [&](const SwzRow<D>& rs, int mt, int st) {
-      const bf16* base = (st & 1) ? sV0 : sK0;
-      return *at_byte<bf16x8>(base, rs.off(mt * 32, (st >> 1) * 2));
-    };
-    // dQ^T += K^T dS^T for one 32-key half mt: 2 x NNT steps (16-key chunk
-    // kc = st / NNT of the half, head-dim tile st % NNT); K^T by transpose reads.
-    auto kt_frag = [&](const SwzTr<D>& ts, int mt, int st) {
-      const int rb = mt * 32 + (st / NNT) * 16, cb = (st % NNT) * 32;
-      return concat(lds_read_tr(to_lds(at_byte<bf16>(sK0, ts.off(rb, 0, cb)))),
-                    lds_read_tr(to_lds(at_byte<bf16>(sK0, ts.off(rb, 1, cb)))));
-    };
-    constexpr int SRING = 4, TRING = 3;
-
     f32x16 dqacc[NNT];
-  #pragma unroll
+#pragma unroll
     for (int nt = 0; nt < NNT; ++nt) dqacc[nt] = (f32x16){};
 
-    dma_tile<D, BC, kDqThreads>(Kh, 0, Nk, sK0, tid);
-    dma_tile<D, BC, kDqThreads>(Vh, 0, Nk, sV0, tid);
+    kv.tile(Kh, 0, Nk, sK0);
+    kv.tile(Vh, 0, Nk, sV0);
     vm_wait_all();
     __syncthreads();
 
-    for (int j = 0; j < ntiles; ++j) {
-      if (j + 1 < ntiles) {
-        dma_tile<D, BC, kDqThreads>(Kh, (j + 1) * BC, Nk, sK0 + ((j + 1) & 1) * TILE, tid);
-        dma_tile<D, BC, kDqThreads>(Vh, (j + 1) * BC, Nk, sV0 + ((j + 1) & 1) * TILE, tid);
-      }
-      const SwzRow<D> rs = rowsw.flipped((j & 1) * TB);
-      const SwzTr<D> ts = trsw.flipped((j & 1) * TB);
+    // One key tile j (P = buffer parity j & 1, a constant at both inlined
+    // call sites).
+    auto tile_step = [&](const int P, int j) __attribute__((always_inline)) {
       const int k0 = j * BC;
-      const bool need_mask = (k0 + BC > Nk) || (CAUSAL && (k0 + BC - 1 > wrow_lo + off));
-
       // dS^T for the 16 keys of element e of half mt: lane holds row qrow and
       // keys k0 + mt*32 + (i/4)*8 + half*4 + i%4.
       f32x16 sacc[2], dpacc[2];
       bf16x8 dsf[4];
       auto ds_elem = [&](int mt, int i) {
-        float p = fast_exp2(fmaf(sacc[mt][i], c, -l2));
-        if (need_mask) {
-          const int key = k0 + mt * 32 + (i >> 2) * 8 + half * 4 + (i & 3);
-          const bool vis = (key < Nk) && (!CAUSAL || key <= qrow + off);
-          if (!vis) p = 0.f;
-        }
+        const float p = fast_exp2(fmaf(sacc[mt][i], c, -l2));
         dsf[mt * 2 + (i >> 3)][i & 7] = (bf16)(p * (dpacc[mt][i] - drow));
       };
-      // S^T, dP^T of half mt (16 MFMAs); with `overlap`, the dS elements of half
-      // mt - 1 are computed between them.
+      // Keys past the end and, causal, keys after the row's diagonal get
+      // score -inf, hence P = 0 and dS = 0; only tiles that cross the
+      // diagonal or the end need it.
+      auto mask_half = [&](int mt) {
+        if ((k0 + BC > Nk) || (CAUSAL && (k0 + BC - 1 > wrow_lo + off))) {
+#pragma unroll
+          for (int i = 0; i < 16; ++i) {
+            const int key = k0 + mt * 32 + (i >> 2) * 8 + half * 4 + (i & 3);
+            const bool vis = (key < Nk) && (!CAUSAL || key <= qrow + off);
+            if (!vis) sacc[mt][i] = -INFINITY;
+          }
+        }
+      };
+      // S^T, dP^T of half mt (16 MFMAs); with `overlap`, the dS elements of
+      // half mt - 1 are computed between them; half 0 also issues the
+      // direct-to-LDS loads of K and V tile j+1 (rows past the end read as
+      // zeros; the last tile loads nothing anybody reads).
       auto sdp_half = [&](int mt, bool overlap) {
         sacc[mt] = (f32x16){};
         dpacc[mt] = (f32x16){};
         bf16x8 ring[SRING];
-  #pragma unroll
-        for (int st = 0; st < SRING; ++st) ring[st] = sfrag(rs, mt, st);
-  #pragma unroll
+#pragma unroll
+        for (int st = 0; st < SRING; ++st) ring[st] = sfrag(P, mt, st);
+#pragma unroll
         for (int st = 0; st < 2 * NKK; ++st) {
           const bf16x8 a = ring[st % SRING];
-          if (st + SRING < 2 * NKK) ring[st % SRING] = sfrag(rs, mt, st + SRING);
+          if (st + SRING < 2 * NKK) ring[st % SRING] = sfrag(P, mt, st + SRING);
           if (st & 1) dpacc[mt] = mfma32(a, dof[st >> 1], dpacc[mt]);
           else sacc[mt] = mfma32(a, qf[st >> 1], sacc[mt]);
+          if (mt == 0 && (st & 1) == 0 && (st >> 1) < 2 * KV::PER) {
+            const int di = st >> 1;
+            if (di < KV::PER)
+              kv.part(Kh, k0 + BC, Nk, sK0 + (1 - P) * TILE, di);
+            else
+              kv.part(Vh, k0 + BC, Nk, sV0 + (1 - P) * TILE, di - KV::PER);
+          }
           if (overlap) {
-  #pragma unroll
+#pragma unroll
             for (int h = 0; h < 16 / (2 * NKK); ++h) ds_elem(mt - 1, st * (16 / (2 * NKK)) + h);
+            pin(dsf[(mt - 1) * 2 + (st * (16 / (2 * NKK))) / 8]);
           }
           __builtin_amdgcn_sched_barrier(0);
         }
@@ -440,38 +532,45 @@ void bwd_dq_bf16_kernel(const bf16* __restrict__ Q, const bf16* __restrict__ K,
       // elements of half mt + 1 are computed between them.
       auto dq_half = [&](int mt, bool overlap) {
         bf16x8 ring[TRING];
-  #pragma unroll
-        for (int st = 0; st < TRING; ++st) ring[st] = kt_frag(ts, mt, st);
-  #pragma unroll
+#pragma unroll
+        for (int st = 0; st < TRING; ++st) ring[st] = kt_frag(P, mt, st);
+#pragma unroll
         for (int st = 0; st < 2 * NNT; ++st) {
           const bf16x8 a = ring[st % TRING];
-          if (st + TRING < 2 * NNT) ring[st % TRING] = kt_frag(ts, mt, st + TRING);
+          if (st + TRING < 2 * NNT) ring[st % TRING] = kt_frag(P, mt, st + TRING);
           dqacc[st % NNT] = mfma32(a, dsf[mt * 2 + st / NNT], dqacc[st % NNT]);
           if (overlap) {
-  #pragma unroll
+#pragma unroll
             for (int h = 0; h < 16 / (2 * NNT); ++h) ds_elem(mt + 1, st * (16 / (2 * NNT)) + h);
+            pin(dsf[(mt + 1) * 2 + (st * (16 / (2 * NNT))) / 8]);
           }
           __builtin_amdgcn_sched_barrier(0);
         }
       };
       sdp_half(0, false);
+      mask_half(0);
       sdp_half(1, true);   // dS of half 0 overlaps the MFMAs of half 1
+      mask_half(1);
       dq_half(0, true);    // dS of half 1 overlaps dQ of half 0
       dq_half(1, false);
 
       vm_wait_all();  // this wave's part of tile j+1 has landed
       __syncthreads();
+    };
+    for (int j = 0; j < ntiles; j += 2) {
+      tile_step(0, j);
+      if (j + 1 < ntiles) tile_step(1, j + 1);
     }
 
     // Epilogue: dQ = scale * dQ_acc; lane holds row qrow.
     if (qrow < Nq) {
       bf16* out = dQ + qbase + (size_t)qrow * D;
-  #pragma unroll
+#pragma unroll
       for (int nt = 0; nt < NNT; ++nt)
-  #pragma unroll
+#pragma unroll
         for (int gg = 0; gg < 4; ++gg) {
           bf16x4 v;
-  #pragma unroll
+#pragma unroll
           for (int e = 0; e < 4; ++e) v[e] = (bf16)(dqacc[nt][gg * 4 + e] * scale);
           *(bf16x4*)(out + nt * 32 + gg * 8 + half * 4) = v;
         }
@@ -487,7 +586,7 @@ constexpr int kF32BT = 64;
 template <int D, bool CAUSAL>
 __global__ __launch_bounds__(kF32BT) void bwd_dkdv_f32_kernel(
     const float* __restrict__ Q, const float* __restrict__ K, const float* __restrict__ V,
-    const float* __restrict__ L, const float* __restrict__ dO, const float* __restrict__ Dvec,
+    const float* __restrict__ L, const float* __restrict__ dO, const float* __restrict__ LD,
     float* __restrict__ dK, float* __restrict__ dV, int Nq, int Nk, int nkt, float scale,
     int off) {
   __shared__ float sq[D], sdo[D];
@@ -520,7 +619,7 @@ __global__ __launch_bounds__(kF32BT) void bwd_dkdv_f32_kernel(
       dp = fmaf(sdo[e], v[e], dp);
     }
     const float p = expf(s * scale - L[(size_t)bh * Nq + q]);
-    const float ds = p * (dp - Dvec[(size_t)bh * Nq + q]);
+    const float ds = p * (dp - LD[2 * ((size_t)bh * Nq + q) + 1]);
 #pragma unroll
     for (int e = 0; e < D; ++e) {
       dv[e] = fmaf(p, sdo[e], dv[e]);
@@ -539,7 +638,7 @@ __global__ __launch_bounds__(kF32BT) void bwd_dkdv_f32_kernel(
 template <int D, bool CAUSAL>
 __global__ __launch_bounds__(kF32BT) void bwd_dq_f32_kernel(
     const float* __restrict__ Q, const float* __restrict__ K, const float* __restrict__ V,
-    const float* __restrict__ L, const float* __restrict__ dO, const float* __restrict__ Dvec,
+    const float* __restrict__ L, const float* __restrict__ dO, const float* __restrict__ LD,
     float* __restrict__ dQ, int Nq, int Nk, int nqt, float scale, int off) {
   __shared__ float sk[D], sv[D];
   const int bh = blockIdx.x / nqt;
@@ -554,7 +653,7 @@ __global__ __launch_bounds__(kF32BT) void bwd_dq_f32_kernel(
     dq[e] = 0.f;
   }
   const float lq = (q < Nq) ? L[(size_t)bh * Nq + q] : 0.f;
-  const float dq_aux = (q < Nq) ? Dvec[(size_t)bh * Nq + q] : 0.f;
+  const float dq_aux = (q < Nq) ? LD[2 * ((size_t)bh * Nq + q) + 1] : 0.f;
   int kend = Nk;
   if (CAUSAL) kend = min(Nk, qt * kF32BT + kF32BT + off);
   for (int key = 0; key < kend; ++key) {
@@ -590,7 +689,7 @@ hipError_t launch_pre(const BwdArgs& a, hipStream_t s) {
   const long nb = (rows + RPB - 1) / RPB;
   if (nb == 0) return hipSuccess;
   hipLaunchKernelGGL((bwd_pre_kernel<D, T>), dim3((unsigned)nb), dim3(256), 0, s,
-                     (const T*)a.O, (const T*)a.dO, a.L, a.Dvec, a.L2, rows);
+                     (const T*)a.O, (const T*)a.dO, a.L, a.LD, rows);
   return hipGetLastError();
 }
 
@@ -614,7 +713,7 @@ hipError_t launch_bwd_bf16(const BwdArgs& a, int stages, hipStream_t s) {
     const int hpx = (BH % kNumXcd == 0) ? BH / kNumXcd : 0;
 #define FA_DKDV_LAUNCH(DD, CC)                                                                  \
   hipLaunchKernelGGL((bwd_dkdv_bf16_kernel<DD, CC>), dim3(nblocks), dim3(kKvThreads), 0, s, Q, K, \
-                     V, a.L2, dO, a.Dvec, (bf16*)a.dK, (bf16*)a.dV, a.Nq, a.Nk, nkt, BH, hpx, c, \
+                     V, dO, a.LD, (bf16*)a.dK, (bf16*)a.dV, a.Nq, a.Nk, nkt, BH, hpx, c,     \
                      a.scale, off)
     if (a.d == 128) {
       if (a.causal) FA_DKDV_LAUNCH(128, true); else FA_DKDV_LAUNCH(128, false);
@@ -630,7 +729,7 @@ hipError_t launch_bwd_bf16(const BwdArgs& a, int stages, hipStream_t s) {
     const int nblocks = (a.causal ? (nqt + 1) / 2 : nqt) * BH;  // causal: query tile pairs
 #define FA_DQ_LAUNCH(DD, CC)                                                                    \
   hipLaunchKernelGGL((bwd_dq_bf16_kernel<DD, CC>), dim3(nblocks), dim3(kDqThreads), 0, s, Q, K,  \
-                     V, a.L, dO, a.Dvec, (bf16*)a.dQ, a.Nq, a.Nk, nqt, c, a.scale, off)
+                     V, dO, a.LD, (bf16*)a.dQ, a.Nq, a.Nk, nqt, c, a.scale, off)
     if (a.d == 128) {
       if (a.causal) FA_DQ_LAUNCH(128, true); else FA_DQ_LAUNCH(128, false);
     } else {
@@ -658,7 +757,7 @@ hipError_t launch_bwd_f32(const BwdArgs& a, int stages, hipStream_t s) {
   if ((stages & 2) && nkt > 0) {
 #define FA_DKDV32_LAUNCH(DD, CC)                                                                \
   hipLaunchKernelGGL((bwd_dkdv_f32_kernel<DD, CC>), dim3(nkt * BH), dim3(kF32BT), 0, s, Q, K, V, \
-                     a.L, dO, a.Dvec, (float*)a.dK, (float*)a.dV, a.Nq, a.Nk, nkt, a.scale, off)
+                     a.L, dO, a.LD, (float*)a.dK, (float*)a.dV, a.Nq, a.Nk, nkt, a.scale, off)
     if (a.d == 128) {
       if (a.causal) FA_DKDV32_LAUNCH(128, true); else FA_DKDV32_LAUNCH(128, false);
     } else {
@@ -671,7 +770,7 @@ hipError_t launch_bwd_f32(const BwdArgs& a, int stages, hipStream_t s) {
   if ((stages & 4) && nqt > 0) {
 #define FA_DQ32_LAUNCH(DD, CC)                                                                \
   hipLaunchKernelGGL((bwd_dq_f32_kernel<DD, CC>), dim3(nqt * BH), dim3(kF32BT), 0, s, Q, K, V, \
-                     a.L, dO, a.Dvec, (float*)a.dQ, a.Nq, a.Nk, nqt, a.scale, off)
+                     a.L, dO, a.LD, (float*)a.dQ, a.Nq, a.Nk, nqt, a.scale, off)
     if (a.d == 128) {
       if (a.causal) FA_DQ32_LAUNCH(128, true); else FA_DQ32_LAUNCH(128, false);
     } else {

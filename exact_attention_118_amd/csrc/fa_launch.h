@@ -32,8 +32,7 @@ struct BwdArgs {
   int B, H, Nq, Nk, d;
   float scale;
   bool causal;
-  float* Dvec;  // [B*H*Nq] fp32 scratch (workspace): D = rowsum(dO * O)
-  float* L2;    // [B*H*Nq] fp32 scratch (workspace): L * log2(e)
+  float* LD;  // [B*H*Nq][2] fp32 scratch (workspace): per query row L * log2(e), then D = rowsum(dO * O)
 };
 
 // Tiled forward (Q-tile per workgroup, K/V streamed through LDS).
@@ -46,7 +45,7 @@ hipError_t launch_fwd_split_bf16(const FwdArgs& a, int splits, float* part_o, fl
                                  hipStream_t s);
 
 // Backward: D = rowsum(dO*O) and L*log2(e); dK and dV; dQ.
-// `stages`: bit 1 D and L2, bit 2 dK/dV kernel, bit 4 dQ kernel (2 and 4 read them).
+// `stages`: bit 1 the (L*log2 e, D) pairs, bit 2 dK/dV kernel, bit 4 dQ kernel (2 and 4 read them).
 hipError_t launch_bwd_bf16(const BwdArgs& a, int stages, hipStream_t s);
 hipError_t launch_bwd_f32(const BwdArgs& a, int stages, hipStream_t s);
 

@@ -87,10 +87,11 @@ fa_status fa_fwd(const void* Q, const void* K, const void* V, void* O, float* L,
  *
  *  Q, K, V, O (from fa_fwd), L (from fa_fwd), dO: read.  dQ [B,H,Nq,d],
  *  dK, dV [B,H,Nk,d]: overwritten, every element (not accumulated into).
- *  workspace: fa_bwd_workspace_size() bytes of device memory (D and
- *  L*log2(e), each [B,H,Nq] fp32), written by the first stage.  dK and dV are computed per key block and
- *  dQ per query block by a second kernel that recomputes P and dP, so there
- *  are no atomic operations and every output is deterministic.
+ *  workspace: fa_bwd_workspace_size() bytes of device memory, 16-byte
+ *  aligned, written by the first stage: per query row the fp32 pair
+ *  (L*log2(e), D), [B,H,Nq,2].  dK and dV are computed per key block and dQ
+ *  per query block by a second kernel that recomputes P and dP, so there are
+ *  no atomic operations and every output is deterministic.
  */
 fa_status fa_bwd(const void* Q, const void* K, const void* V, const void* O, const float* L,
                  const void* dO, void* dQ, void* dK, void* dV,
@@ -100,7 +101,7 @@ fa_status fa_bwd(const void* Q, const void* K, const void* V, const void* O, con
 /*
  * The backward pass as its three launches, for callers that schedule or time
  * them separately.  Same arguments as fa_bwd plus `stages`, a bit mask:
- *   FA_BWD_PREPROCESS (1): D = rowsum(dO * O) and L*log2(e) into the workspace;
+ *   FA_BWD_PREPROCESS (1): the (L*log2(e), D = rowsum(dO * O)) pairs into the workspace;
  *   FA_BWD_DKDV       (2): dK and dV written (reads the workspace);
  *   FA_BWD_DQ         (4): dQ written (reads the workspace).
  * fa_bwd(...) is fa_bwd_stages(..., FA_BWD_ALL).  Stages 2 and 4 need stage 1
