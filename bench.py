@@ -2,13 +2,18 @@
 """Throughput of the fused attention path on one MI355X.
 
 One step = the whole hot path on one batch: forward (fa_fwd) then backward
-(fa_bwd: preprocess, main kernel, dQ conversion) on the long-sequence
-workload B=1, H=32, N=8192, d=128, causal, bf16 (Q and K scaled by 3).
-Inputs are synthetic (seeded normal draws on the GPU) and resident in HBM
-before timing starts.  Prints ONE JSON line on stdout; progress goes to stderr.
+(fa_bwd: the (L*log2 e, D) preprocess, the dK/dV kernel, the dQ kernel) on
+the long-sequence workload B=1, H=32, N=8192, d=128, causal, bf16 (Q and K
+scaled by 3).  Inputs are synthetic (seeded normal draws on the GPU) and
+resident in HBM before timing starts.  Prints ONE JSON line on stdout;
+progress goes to stderr.
 
 FLOP convention: forward 2 GEMMs = 4*d per unmasked (query, key) pair,
 backward 5 GEMMs = 10*d per pair; pairs = N(N+1)/2 per head when causal.
+
+`--write-traffic FETCH_CSV WRITE_CSV` turns two rocprofv3 counter runs of this
+script (one with --pmc FETCH_SIZE, one with --pmc WRITE_SIZE, both with
+--copy-calibration-mib) into profiles/hbm_traffic.json and exits.
 """
 
 import argparse
@@ -42,9 +47,71 @@ def unmasked_pairs(Nq, Nk, causal):
     return part + max(0, Nq - full_from) * Nk
 
 
+KERNEL_SOURCES = {
+    "fwd_bf16_kernel": "fa_fwd.hip",
+    "bwd_dkdv_bf16_kernel": "fa_bwd.hip",
+    "bwd_dq_bf16_kernel": "fa_bwd.hip",
+    "bwd_pre_kernel": "fa_bwd.hip",
+}
+
+
 def source_sha(path):
-    with open(path, "rb") as f:
-        return hashlib.sha256(f.read()).hexdigest()
+    """sha256 over a kernel's source file and the device header it includes."""
+    h = hashlib.sha256()
+    for p in (path, os.path.join(os.path.dirname(path), "fa_common.h")):
+        with open(p, "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()
+
+
+def write_traffic(fetch_csv, write_csv, copy_mib):
+    """profiles/hbm_traffic.json from two rocprofv3 --pmc runs of this script.
+
+    Each counter is scaled by what it reads for the calibration copy (a plain
+    elementwise kernel reading and writing copy_mib MiB): HBM bytes per launch
+    = counter KiB * 1024 * (true copy bytes / counter bytes of the copy)."""
+    import csv
+    import re
+    import statistics
+
+    def per_kernel(path, counter):
+        vals = {}
+        for r in csv.DictReader(open(path)):
+            if r["Counter_Name"] != counter:
+                continue
+            m = re.search(r"(fwd_bf16_kernel|bwd_dkdv_bf16_kernel|bwd_dq_bf16_kernel|bwd_pre_kernel)",
+                          r["Kernel_Name"])
+            name = m.group(1) if m else ("copy" if int(r["Grid_Size"]) == (copy_mib << 20) // 16
+                                         else None)
+            if name:
+                vals.setdefault(name, []).append(float(r["Counter_Value"]))
+        return vals
+
+    fetch, write = per_kernel(fetch_csv, "FETCH_SIZE"), per_kernel(write_csv, "WRITE_SIZE")
+    copy_kib = float(copy_mib << 10)
+    fscale = copy_kib / max(fetch["copy"])  # max: the copy's source fill shares its grid size
+    wscale = copy_kib / max(write["copy"])
+    csrc = os.path.join(ROOT, "exact_attention_118_amd", "csrc")
+    kernels = {}
+    for name, src in KERNEL_SOURCES.items():
+        if name not in fetch or name not in write:
+            continue
+        fk, wk = statistics.mean(fetch[name]), statistics.mean(write[name])
+        kernels[name] = {"source": f"exact_attention_118_amd/csrc/{src} + fa_common.h",
+                         "source_sha256": source_sha(os.path.join(csrc, src)),
+                         "fetch_kib_raw": fk, "write_kib_raw": wk,
+                         "fetch_bytes": fk * 1024 * fscale, "write_bytes": wk * 1024 * wscale,
+                         "bytes_per_launch": fk * 1024 * fscale + wk * 1024 * wscale,
+                         "launches": len(fetch[name])}
+    rec = {"about": "HBM bytes per launch from rocprofv3 --pmc FETCH_SIZE and --pmc WRITE_SIZE "
+                    "(KiB per dispatch, mean over the launches), each scaled by what the same "
+                    f"counter reads for a plain elementwise copy of {copy_mib} MiB in the same run. "
+                    "A kernel's entry is valid while its source and fa_common.h hash to "
+                    "source_sha256.",
+           "fetch_scale": fscale, "write_scale": wscale, "kernels": kernels}
+    with open(TRAFFIC_FILE, "w") as f:
+        json.dump(rec, f, indent=1)
+    print(json.dumps({k: round(v["bytes_per_launch"] / 2**20, 1) for k, v in kernels.items()}))
 
 
 def measured_traffic(kernel_name, source):
@@ -129,7 +196,13 @@ def main():
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
                     help="after the timed steps, run one plain device-to-device copy of this many "
                          "MiB (reference point for HBM byte counters under rocprofv3 --pmc)")
+    ap.add_argument("--write-traffic", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
+                    help="write profiles/hbm_traffic.json from two rocprofv3 counter runs and exit")
     args = ap.parse_args()
+
+    if args.write_traffic:
+        write_traffic(*args.write_traffic, copy_mib=args.copy_calibration_mib or 1024)
+        return
 
     if args.gpus != 1:
         print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
@@ -207,7 +280,8 @@ def main():
     # pair) -- its recomputation of S and dP is overhead, not algorithmic work.
     csrc = os.path.join(ROOT, "exact_attention_118_amd", "csrc")
     kernels = {
-        "fwd_bf16_kernel": {"ms": fwd_ms, "flops": fwd_flops, "source": os.path.join(csrc, "fa_fwd.hip")},
+        "fwd_bf16_kernel": {"ms": fwd_ms, "flops": fwd_flops,
+                            "source": os.path.join(csrc, "fa_fwd.hip")},
         "bwd_dkdv_bf16_kernel": {"ms": dkdv_ms, "flops": 8 * w.d * pairs,
                                  "source": os.path.join(csrc, "fa_bwd.hip")},
         "bwd_dq_bf16_kernel": {"ms": dq_ms, "flops": 2 * w.d * pairs,
