@@ -218,26 +218,48 @@ void fwd_bf16_kernel(const bf16* __restrict__ Q, const bf16* __restrict__ K,
       }
       const float m_ref = (m_run == -INFINITY) ? 0.f : m_run;
 
-      // Scores of tile j+1 on the MFMA pipe, interleaved step by step with the
-      // exponentials of tile j on the vector ALU and with the direct-to-LDS
-      // loads of K tile j+2 (over tile j's buffer, last read for tile j's
-      // scores) and V tile j+1.  Step st converts the pair of probabilities
-      // pf[st/4][2*(st%4) .. +1] (keys of chunk st/4).  The last iterations
-      // also compute scores of a stale buffer and load rows past the end (as
-      // zeros): that extra work keeps this block free of branches, so the
-      // three kinds of work stay interleaved.
+      // The 32 probabilities of this lane's row in tile j, as 16 pairs (pair
+      // pr: probabilities 2pr, 2pr+1 of chunk pr/4, converted together).  The
+      // score block below is short of vector-ALU time and the P V block has
+      // spare: with D = 128 the first kPairsA pairs go with the score MFMAs
+      // and the rest with the first P V steps, which do not yet read them.
+      constexpr int NPAIR = 16;
+      constexpr int kPairsA = (D == 128) ? 8 : NPAIR;
+      static_assert(NPAIR - kPairsA <= 2 * NNT, "late pairs fit before chunk 2 is read");
       bf16x8 pf[4];
       float rs0 = 0.f, rs1 = 0.f;
+      auto prob_pair = [&](int pr) {
+        const int el = 2 * pr, kc = el >> 3, e = el & 7;
+        const int mt = kc >> 1, i = (kc & 1) * 8 + e;
+        const float p0 = fast_exp2(fmaf(scur[mt][i], c, -m_ref));
+        const float p1 = fast_exp2(fmaf(scur[mt][i + 1], c, -m_ref));
+        rs0 += p0;
+        rs1 += p1;
+        pf[kc][e] = (bf16)p0;
+        pf[kc][e + 1] = (bf16)p1;
+        pin(pf[kc]);
+        pin(rs0);
+        pin(rs1);
+      };
+
+      // Scores of tile j+1 on the MFMA pipe, interleaved step by step with
+      // exponentials of tile j on the vector ALU and with the direct-to-LDS
+      // loads of K tile j+2 (over tile j's buffer, last read for tile j's
+      // scores) and V tile j+1.  The last iterations also compute scores of a
+      // stale buffer and load rows past the end (as zeros): that extra work
+      // keeps this block free of branches, so the three kinds of work stay
+      // interleaved.
       {
+        constexpr int SA = 2 * NKK;
         bf16x8 ring[KRING];
 #pragma unroll
         for (int st = 0; st < KRING; ++st) ring[st] = kfrag(1 - P, st);
         snext[0] = (f32x16){};
         snext[1] = (f32x16){};
 #pragma unroll
-        for (int st = 0; st < 2 * NKK; ++st) {
+        for (int st = 0; st < SA; ++st) {
           const bf16x8 a = ring[st % KRING];
-          if (st + KRING < 2 * NKK) ring[st % KRING] = kfrag(1 - P, st + KRING);
+          if (st + KRING < SA) ring[st % KRING] = kfrag(1 - P, st + KRING);
           snext[st & 1] = mfma32(a, qf[st >> 1], snext[st & 1]);
           if ((st & 1) == 0) {
             const int di = st >> 1;
@@ -247,27 +269,16 @@ void fwd_bf16_kernel(const bf16* __restrict__ Q, const bf16* __restrict__ K,
               kv.part(Vh, k0 + BC, Nk, sV0 + (1 - P) * TILE, di - KV::PER);
           }
 #pragma unroll
-          for (int h = 0; h < 32 / (2 * NKK); h += 2) {
-            const int el = st * (32 / (2 * NKK)) + h;  // probability index 0..31
-            const int kc = el >> 3, e = el & 7;
-            const int mt = kc >> 1, i = (kc & 1) * 8 + e;
-            const float p0 = fast_exp2(fmaf(scur[mt][i], c, -m_ref));
-            const float p1 = fast_exp2(fmaf(scur[mt][i + 1], c, -m_ref));
-            rs0 += p0;
-            rs1 += p1;
-            pf[kc][e] = (bf16)p0;
-            pf[kc][e + 1] = (bf16)p1;
-          }
-          pin(pf[(st * (32 / (2 * NKK))) >> 3]);
-          pin(rs0);
-          pin(rs1);
+          for (int pr = 0; pr < kPairsA; ++pr)
+            if (pr * SA / kPairsA == st) prob_pair(pr);
           __builtin_amdgcn_sched_barrier(0);
         }
       }
-      l_run += rs0 + rs1;
       mask_tile(snext, k0 + BC);
 
-      // O^T += V^T P^T for tile j, interleaved with the row max of tile j+1.
+      // O^T += V^T P^T for tile j (step st reads chunk st / NNT of P),
+      // interleaved with the remaining probability pairs and the row max of
+      // tile j+1.
       {
         bf16x8 ring[VRING];
         float mxa = -INFINITY, mxb = -INFINITY;
@@ -278,6 +289,7 @@ void fwd_bf16_kernel(const bf16* __restrict__ Q, const bf16* __restrict__ K,
           const bf16x8 a = ring[st % VRING];
           if (st + VRING < 4 * NNT) ring[st % VRING] = vfrag(P, st + VRING);
           oacc[st % NNT] = mfma32(a, pf[st / NNT], oacc[st % NNT]);
+          if (kPairsA + st < NPAIR) prob_pair(kPairsA + st);
 #pragma unroll
           for (int h = 0; h < 32 / (4 * NNT); h += 2) {
             const int el = st * (32 / (4 * NNT)) + h;
@@ -289,6 +301,7 @@ void fwd_bf16_kernel(const bf16* __restrict__ Q, const bf16* __restrict__ K,
         mx_next = fmaxf(mxa, mxb);
         mx_next = fmaxf(mx_next, wave_shfl_xor(mx_next, 32));
       }
+      l_run += rs0 + rs1;
       vm_wait_all();  // this wave's part of tiles K j+2 and V j+1 has landed
       __syncthreads();
     };
