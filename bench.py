@@ -48,9 +48,9 @@ def unmasked_pairs(Nq, Nk, causal):
 
 
 KERNEL_SOURCES = {
-    "fwd_bf16_kernel": "fa_fwd.hip",
-    "bwd_dkdv_bf16_kernel": "fa_bwd.hip",
-    "bwd_dq_bf16_kernel": "fa_bwd.hip",
+    "fwd_kernel": "fa_fwd.hip",
+    "bwd_dkdv_kernel": "fa_bwd.hip",
+    "bwd_dq_kernel": "fa_bwd.hip",
     "bwd_pre_kernel": "fa_bwd.hip",
 }
 
@@ -79,7 +79,7 @@ def write_traffic(fetch_csv, write_csv, copy_mib):
         for r in csv.DictReader(open(path)):
             if r["Counter_Name"] != counter:
                 continue
-            m = re.search(r"(fwd_bf16_kernel|bwd_dkdv_bf16_kernel|bwd_dq_bf16_kernel|bwd_pre_kernel)",
+            m = re.search(r"(fwd_kernel|bwd_dkdv_kernel|bwd_dq_kernel|bwd_pre_kernel)",
                           r["Kernel_Name"])
             name = m.group(1) if m else ("copy" if int(r["Grid_Size"]) == (copy_mib << 20) // 16
                                          else None)
@@ -184,6 +184,35 @@ def bench_decode(fa, torch, steps):
             "algorithmic_bytes": all_bytes}
 
 
+def bench_fp16(fa, torch, w, x, ws, steps):
+    """The same forward and backward on fp16 copies of the inputs."""
+    Q, K, V, dO = (x[k].to(torch.float16) for k in ("Q", "K", "V", "dO"))
+    O = torch.empty_like(Q)
+    L = torch.empty(w.B, w.H, w.Nq, dtype=torch.float32, device="cuda")
+    dQ, dK, dV = torch.empty_like(Q), torch.empty_like(K), torch.empty_like(V)
+
+    def run(ev=None):
+        fa.fa_fwd(Q, K, V, O, L, w.scale, w.causal)
+        if ev is not None:
+            ev.record()
+        fa.fa_bwd(Q, K, V, O, L, dO, dQ, dK, dV, w.scale, w.causal, workspace=ws)
+
+    run()
+    torch.cuda.synchronize()
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(steps)]
+    for e in ev:
+        e[0].record()
+        run(e[1])
+        e[2].record()
+    torch.cuda.synchronize()
+    fwd_ms = sum(e[0].elapsed_time(e[1]) for e in ev) / steps
+    bwd_ms = sum(e[1].elapsed_time(e[2]) for e in ev) / steps
+    pairs = unmasked_pairs(w.Nq, w.Nk, w.causal) * w.B * w.H
+    return {"fwd_ms": fwd_ms, "bwd_ms": bwd_ms,
+            "fwd_TFLOP/s": 4 * w.d * pairs / (fwd_ms * 1e-3) / 1e12,
+            "bwd_TFLOP/s": 10 * w.d * pairs / (bwd_ms * 1e-3) / 1e12}
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__)
     ap.add_argument("--gpus", type=int, default=1)
@@ -193,6 +222,7 @@ def main():
     ap.add_argument("--cpu-heads", type=int, default=16,
                     help="heads of the workload the float64 oracle is timed on (0 = skip)")
     ap.add_argument("--no-decode", action="store_true", help="skip the decode-shaped forward")
+    ap.add_argument("--no-fp16", action="store_true", help="skip the fp16 forward and backward")
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
                     help="after the timed steps, run one plain device-to-device copy of this many "
                          "MiB (reference point for HBM byte counters under rocprofv3 --pmc)")
@@ -280,11 +310,11 @@ def main():
     # pair) -- its recomputation of S and dP is overhead, not algorithmic work.
     csrc = os.path.join(ROOT, "exact_attention_118_amd", "csrc")
     kernels = {
-        "fwd_bf16_kernel": {"ms": fwd_ms, "flops": fwd_flops,
+        "fwd_kernel": {"ms": fwd_ms, "flops": fwd_flops,
                             "source": os.path.join(csrc, "fa_fwd.hip")},
-        "bwd_dkdv_bf16_kernel": {"ms": dkdv_ms, "flops": 8 * w.d * pairs,
+        "bwd_dkdv_kernel": {"ms": dkdv_ms, "flops": 8 * w.d * pairs,
                                  "source": os.path.join(csrc, "fa_bwd.hip")},
-        "bwd_dq_bf16_kernel": {"ms": dq_ms, "flops": 2 * w.d * pairs,
+        "bwd_dq_kernel": {"ms": dq_ms, "flops": 2 * w.d * pairs,
                                "source": os.path.join(csrc, "fa_bwd.hip")},
     }
     dom_name = max(kernels, key=lambda k: kernels[k]["ms"])
@@ -317,7 +347,11 @@ def main():
                 "preprocess_ms": pre_ms, "dkdv_ms": dkdv_ms, "dq_ms": dq_ms,
                 "executed_mfma_frac": 14 * w.d * pairs / (bwd_ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS},
     }
-    del dQ, dK, dV, ws
+    del dQ, dK, dV
+    if not args.no_fp16:
+        log("fp16 inputs, same workload")
+        out["fp16"] = bench_fp16(fa, torch, w, x, ws, steps=max(3, args.steps // 2))
+    del ws
     if args.copy_calibration_mib > 0:
         n = args.copy_calibration_mib << 20
         src = torch.ones(n // 4, dtype=torch.float32, device="cuda")

@@ -16,12 +16,12 @@ __all__ = [
     "FAError", "load_library", "lib_path", "fa_fwd", "fa_bwd", "forward", "backward",
     "fwd_workspace_size", "bwd_workspace_size", "fwd_num_splits", "status_string", "version",
     "FA_OK", "FA_ERR_NULL", "FA_ERR_SHAPE", "FA_ERR_UNSUPPORTED", "FA_ERR_ALIGN",
-    "FA_ERR_WORKSPACE", "FA_ERR_HIP", "FA_BF16", "FA_FP32", "EXPORTED_SYMBOLS",
+    "FA_ERR_WORKSPACE", "FA_ERR_HIP", "FA_BF16", "FA_FP32", "FA_FP16", "EXPORTED_SYMBOLS",
     "FA_BWD_PREPROCESS", "FA_BWD_DKDV", "FA_BWD_DQ", "FA_BWD_ALL",
 ]
 
 FA_OK, FA_ERR_NULL, FA_ERR_SHAPE, FA_ERR_UNSUPPORTED, FA_ERR_ALIGN, FA_ERR_WORKSPACE, FA_ERR_HIP = range(7)
-FA_BF16, FA_FP32 = 0, 1
+FA_BF16, FA_FP32, FA_FP16 = 0, 1, 2
 
 FA_BWD_PREPROCESS, FA_BWD_DKDV, FA_BWD_DQ, FA_BWD_ALL = 1, 2, 4, 7
 
@@ -90,9 +90,11 @@ def _dtype_code(t) -> int:
     torch = _torch()
     if t.dtype == torch.bfloat16:
         return FA_BF16
+    if t.dtype == torch.float16:
+        return FA_FP16
     if t.dtype == torch.float32:
         return FA_FP32
-    raise TypeError(f"unsupported dtype {t.dtype}; libfa takes bfloat16 or float32")
+    raise TypeError(f"unsupported dtype {t.dtype}; libfa takes bfloat16, float16 or float32")
 
 
 def _ptr(t):

@@ -21,7 +21,8 @@ size_t round_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 
 bool aligned(const void* p) { return (reinterpret_cast<uintptr_t>(p) % kAlign) == 0; }
 
-bool dtype_ok(fa_dtype t) { return t == FA_BF16 || t == FA_FP32; }
+bool dtype_ok(fa_dtype t) { return t == FA_BF16 || t == FA_FP16 || t == FA_FP32; }
+bool is_mfma(fa_dtype t) { return t == FA_BF16 || t == FA_FP16; }
 
 // Common shape checks.  Returns FA_OK when the sizes are usable; sets *empty
 // when there is nothing to compute for the forward pass.
@@ -60,7 +61,7 @@ int effective_splits(int Nk, int s) {
 // 0: tiled path, >0: split path with that many splits, <0: unsupported combination.
 int choose_splits(int B, int H, int Nq, int Nk, fa_dtype dtype, int num_splits) {
   if (num_splits < 0) return -1;
-  if (Nq == 1 && dtype == FA_BF16) {
+  if (Nq == 1 && is_mfma(dtype)) {
     const int s = num_splits == 0 ? auto_splits(B * H, Nk) : num_splits;
     return effective_splits(Nk, s);
   }
@@ -145,9 +146,12 @@ fa_status fa_fwd(const void* Q, const void* K, const void* V, void* O, float* L,
     float* part_o = static_cast<float*>(workspace);
     float* part_l = reinterpret_cast<float*>(static_cast<char*>(workspace) + w.l_off);
     a.causal = false;  // one query row sees every key under bottom-right alignment
-    e = fa::launch_fwd_split_bf16(a, splits, part_o, part_l, s);
+    e = (dtype == FA_BF16) ? fa::launch_fwd_split_bf16(a, splits, part_o, part_l, s)
+                           : fa::launch_fwd_split_f16(a, splits, part_o, part_l, s);
   } else if (dtype == FA_BF16) {
     e = fa::launch_fwd_bf16(a, s);
+  } else if (dtype == FA_FP16) {
+    e = fa::launch_fwd_f16(a, s);
   } else {
     e = fa::launch_fwd_f32(a, s);
   }
@@ -182,7 +186,9 @@ fa_status fa_bwd_stages(const void* Q, const void* K, const void* V, const void*
   if (Nq > 0) a.LD = static_cast<float*>(workspace);
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
   const hipError_t e =
-      (dtype == FA_BF16) ? fa::launch_bwd_bf16(a, stages, s) : fa::launch_bwd_f32(a, stages, s);
+      (dtype == FA_BF16)   ? fa::launch_bwd_bf16(a, stages, s)
+      : (dtype == FA_FP16) ? fa::launch_bwd_f16(a, stages, s)
+                           : fa::launch_bwd_f32(a, stages, s);
   return e == hipSuccess ? FA_OK : FA_ERR_HIP;
 }
 

@@ -24,19 +24,19 @@
 // workspace beyond D, and every output is deterministic.
 //
 // gfx950 mapping:
-//  * bwd_dkdv_bf16_kernel: 512 threads = 8 waves, two per SIMD, so one wave's
+//  * bwd_dkdv_kernel: 512 threads = 8 waves, two per SIMD, so one wave's
 //    MFMAs overlap the other's LDS reads, exponentials and barrier waits.  A
 //    workgroup owns BC = 256 keys and each wave 32 of them, so dK and dV stay
 //    wave-private (the notes, "Warp Level 并行": with keys split across warps,
 //    dV, dS and dK need no cross-warp reduction).  Scores are laid out with the
-//    key along lanes (S = Q K^T on the 32x32x16 bf16 MFMA): rounded to bf16,
+//    key along lanes (S = Q K^T on the 32x32x16 bf16/fp16 MFMA): rounded to 16 bits,
 //    the fp32 accumulators of P and dS are directly the B operands of
 //    dV^T = dO^T P and dK^T = Q^T dS; dO^T and Q^T come from the row-major LDS
 //    tiles through the transpose read ds_read_b64_tr_b16.  K stays in LDS, the
 //    wave's 32 rows of V in registers; Q, dO, L, D of the next 32-row query
 //    block are loaded into registers while the current one is processed and
 //    are double-buffered in LDS, so one barrier per query block suffices.
-//  * bwd_dq_bf16_kernel: the forward pass's layout.  4 waves own 32 query rows
+//  * bwd_dq_kernel: the forward pass's layout.  4 waves own 32 query rows
 //    each (the notes' "sliced-Q": no cross-wave reduction); scores are computed
 //    transposed, S^T = K Q^T and dP^T = V dO^T, so each lane holds one query
 //    row and its L and D are scalars; dS^T feeds dQ^T = K^T dS^T from
@@ -90,13 +90,14 @@ constexpr int kKvBR = 32;   // query rows per inner iteration
 constexpr int kKvWaves = 8;
 constexpr int kKvThreads = kKvWaves * 64;
 
-template <int D, bool CAUSAL>
+template <typename T, int D, bool CAUSAL>
 __global__ __launch_bounds__(kKvThreads, 1) __attribute__((amdgpu_waves_per_eu(2, 2)))
-void bwd_dkdv_bf16_kernel(const bf16* __restrict__ Q, const bf16* __restrict__ K,
-                          const bf16* __restrict__ V, const bf16* __restrict__ dO,
-                          const float* __restrict__ LD, bf16* __restrict__ dK,
-                          bf16* __restrict__ dV, int Nq, int Nk, int nkt, int BH, int hpx,
-                          float c, float scale, int off) {
+void bwd_dkdv_kernel(const T* __restrict__ Q, const T* __restrict__ K, const T* __restrict__ V,
+                     const T* __restrict__ dO, const float* __restrict__ LD, T* __restrict__ dK,
+                     T* __restrict__ dV, int Nq, int Nk, int nkt, int BH, int hpx, float c,
+                     float scale, int off) {
+  typedef typename Vec<T>::x8 T8;
+  typedef typename Vec<T>::x4 T4;
   constexpr int BC = kKvBC, BR = kKvBR;
   constexpr int CPR = D / 8;     // 16-byte chunks per row
   constexpr int NKK = D / 16;    // MFMA k-steps over the head dim
@@ -113,11 +114,11 @@ void bwd_dkdv_bf16_kernel(const bf16* __restrict__ Q, const bf16* __restrict__ K
   // (L*log2 e, D) pairs of the query block per buffer.  Query block it uses
   // buffers it & 1; the loop is unrolled by two so that their offsets are
   // constants.
-  __shared__ __attribute__((aligned(1024))) bf16 smem[KTILE + 4 * QTILE];
+  __shared__ __attribute__((aligned(1024))) T smem[KTILE + 4 * QTILE];
   __shared__ __attribute__((aligned(16))) float sLD[2][2 * BR];
-  bf16* const sK = smem;
-  bf16* const sQ0 = smem + KTILE;
-  bf16* const sdO0 = smem + KTILE + 2 * QTILE;
+  T* const sK = smem;
+  T* const sQ0 = smem + KTILE;
+  T* const sdO0 = smem + KTILE + 2 * QTILE;
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -151,8 +152,8 @@ void bwd_dkdv_bf16_kernel(const bf16* __restrict__ Q, const bf16* __restrict__ K
   // wave) the 32 (L2, D) pairs; rows past Nq read as zeros.  Lane offsets
   // are fixed; the rest is wave-uniform.
   const int tsel = (wave * IPW) / NIQ;  // 0: Q, 1: dO
-  const bf16* const qsrc = (tsel ? dO : Q) + qbase;
-  bf16* const qdst0 = (tsel ? sdO0 : sQ0) + ((wave * IPW) % NIQ) * 64 * 8;
+  const T* const qsrc = (tsel ? dO : Q) + qbase;
+  T* const qdst0 = (tsel ? sdO0 : sQ0) + ((wave * IPW) % NIQ) * 64 * 8;
   unsigned qoff[IPW];
 #pragma unroll
   for (int u = 0; u < IPW; ++u) {
@@ -185,11 +186,11 @@ void bwd_dkdv_bf16_kernel(const bf16* __restrict__ Q, const bf16* __restrict__ K
   }
   if (nloop > 0) load_block(qb_first, 0);
   // This wave's V rows in registers (B operand of dP = dO V^T).
-  bf16x8 vf[NKK];
+  T8 vf[NKK];
 #pragma unroll
   for (int kk = 0; kk < NKK; ++kk)
-    vf[kk] = (mykey < Nk) ? *(const bf16x8*)(V + kbase + (size_t)mykey * D + kk * 16 + half * 8)
-                          : zero_bf16x8();
+    vf[kk] = (mykey < Nk) ? *(const T8*)(V + kbase + (size_t)mykey * D + kk * 16 + half * 8)
+                          : zero8<T8>();
   f32x16 dkacc[NNT], dvacc[NNT];
 #pragma unroll
   for (int nt = 0; nt < NNT; ++nt) {
@@ -229,25 +230,25 @@ void bwd_dkdv_bf16_kernel(const bf16* __restrict__ Q, const bf16* __restrict__ K
     // Causal: a wave whose keys all lie after every row of the block has no work.
     const bool wave_idle = CAUSAL && (kw0 > qi0 + BR - 1 + off);
     if (!wave_idle) {
-      const bf16* const tQ = sQ0 + P * QTILE;
-      const bf16* const tdO = sdO0 + P * QTILE;
+      const T* const tQ = sQ0 + P * QTILE;
+      const T* const tdO = sdO0 + P * QTILE;
       const float* tLD = sLD[P];
       // S = Q K^T and dP = dO V^T: 32 rows x this wave's 32 keys.  Step kk
       // needs the Q, K and dO fragments of head-dim chunk kk; those of step
       // kk + 1 are read before step kk's MFMAs are issued.
       f32x16 sacc = (f32x16){}, dpacc = (f32x16){};
       {
-        auto ldstep = [&](int kk, bf16x8* f) {
-          f[0] = *at_byte<bf16x8>(tQ, qa[kk]);
-          f[1] = *at_byte<bf16x8>(sK, ka[kk]);
-          f[2] = *at_byte<bf16x8>(tdO, qa[kk]);
+        auto ldstep = [&](int kk, T8* f) {
+          f[0] = *at_byte<T8>(tQ, qa[kk]);
+          f[1] = *at_byte<T8>(sK, ka[kk]);
+          f[2] = *at_byte<T8>(tdO, qa[kk]);
         };
-        bf16x8 fa[3], fb[3];
+        T8 fa[3], fb[3];
         ldstep(0, fa);
 #pragma unroll
         for (int kk = 0; kk < NKK; ++kk) {
-          bf16x8* cur = (kk & 1) ? fb : fa;
-          bf16x8* nxt = (kk & 1) ? fa : fb;
+          T8* cur = (kk & 1) ? fb : fa;
+          T8* nxt = (kk & 1) ? fa : fb;
           if (kk + 1 < NKK) ldstep(kk + 1, nxt);
           sacc = mfma32(cur[0], cur[1], sacc);
           dpacc = mfma32(cur[2], vf[kk], dpacc);
@@ -268,8 +269,8 @@ void bwd_dkdv_bf16_kernel(const bf16* __restrict__ Q, const bf16* __restrict__ K
       }
       // P = exp2(S*c - L2) and dS = P * (dP - D) for the pair of rows of
       // elements i, i+1 (i even) of chunk kc = i / 8, in two halves: the
-      // probabilities, then dS and both conversions to bf16.
-      bf16x8 pf[2], dsf[2];
+      // probabilities, then dS and both conversions to T.
+      T8 pf[2], dsf[2];
       float pp[2];
       auto pds_p = [&](int i) {
         const int ql = (i >> 2) * 8 + half * 4 + (i & 3);  // rows ql, ql + 1
@@ -281,30 +282,30 @@ void bwd_dkdv_bf16_kernel(const bf16* __restrict__ Q, const bf16* __restrict__ K
       };
       auto pds_ds = [&](int i, float2 dd) {
         const int kc = i >> 3, e = i & 7;
-        pf[kc][e] = (bf16)pp[0];
-        pf[kc][e + 1] = (bf16)pp[1];
-        dsf[kc][e] = (bf16)(pp[0] * (dpacc[i] - dd.x));
-        dsf[kc][e + 1] = (bf16)(pp[1] * (dpacc[i + 1] - dd.y));
+        pf[kc][e] = (T)pp[0];
+        pf[kc][e + 1] = (T)pp[1];
+        dsf[kc][e] = (T)(pp[0] * (dpacc[i] - dd.x));
+        dsf[kc][e + 1] = (T)(pp[1] * (dpacc[i + 1] - dd.y));
       };
       // dV^T += dO^T P and dK^T += Q^T dS over the 16 rows of chunk kc
       // (2 * NNT MFMAs, A operands by transpose reads); with `overlap`, the
       // probabilities of chunk kc + 1 are computed between them.
       auto dvdk = [&](int kc, bool overlap) {
         auto afrag = [&](int st) {  // st: (head-dim tile st/2, dO^T if even else Q^T)
-          const bf16* base = (st & 1) ? tQ : tdO;
+          const T* base = (st & 1) ? tQ : tdO;
           const unsigned rb = kc * 16 * 2 * D;
-          return concat(lds_read_tr(to_lds(at_byte<bf16>(base, ta[st >> 1] + rb))),
-                        lds_read_tr(to_lds(at_byte<bf16>(base, ta[NNT + (st >> 1)] + rb))));
+          return concat(lds_read_tr<T>(to_lds(at_byte<T>(base, ta[st >> 1] + rb))),
+                        lds_read_tr<T>(to_lds(at_byte<T>(base, ta[NNT + (st >> 1)] + rb))));
         };
         constexpr int NS = 2 * NNT, RING = 2;
         static_assert(NS == 4 || NS == 8, "two or four probability pairs per chunk step pair");
-        bf16x8 ring[RING];
+        T8 ring[RING];
         float2 dd;
 #pragma unroll
         for (int st = 0; st < RING; ++st) ring[st] = afrag(st);
 #pragma unroll
         for (int st = 0; st < NS; ++st) {
-          const bf16x8 a = ring[st % RING];
+          const T8 a = ring[st % RING];
           if (st + RING < NS) ring[st % RING] = afrag(st + RING);
           if (st & 1) dkacc[st >> 1] = mfma32(a, dsf[kc], dkacc[st >> 1]);
           else dvacc[st >> 1] = mfma32(a, pf[kc], dvacc[st >> 1]);
@@ -348,20 +349,20 @@ void bwd_dkdv_bf16_kernel(const bf16* __restrict__ Q, const bf16* __restrict__ K
 
   // Epilogue: dK = scale * dK_acc, dV = dV_acc; lane holds key mykey.
   if (mykey < Nk) {
-    bf16* dkrow = dK + kbase + (size_t)mykey * D;
-    bf16* dvrow = dV + kbase + (size_t)mykey * D;
+    T* dkrow = dK + kbase + (size_t)mykey * D;
+    T* dvrow = dV + kbase + (size_t)mykey * D;
 #pragma unroll
     for (int nt = 0; nt < NNT; ++nt)
 #pragma unroll
       for (int gg = 0; gg < 4; ++gg) {
-        bf16x4 vk, vv;
+        T4 vk, vv;
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
-          vk[e] = (bf16)(dkacc[nt][gg * 4 + e] * scale);
-          vv[e] = (bf16)(dvacc[nt][gg * 4 + e]);
+          vk[e] = (T)(dkacc[nt][gg * 4 + e] * scale);
+          vv[e] = (T)(dvacc[nt][gg * 4 + e]);
         }
-        *(bf16x4*)(dkrow + nt * 32 + gg * 8 + half * 4) = vk;
-        *(bf16x4*)(dvrow + nt * 32 + gg * 8 + half * 4) = vv;
+        *(T4*)(dkrow + nt * 32 + gg * 8 + half * 4) = vk;
+        *(T4*)(dvrow + nt * 32 + gg * 8 + half * 4) = vv;
       }
   }
 }
@@ -372,13 +373,13 @@ constexpr int kDqBR = 128;  // query rows per workgroup
 constexpr int kDqBC = 64;   // keys per K/V tile
 constexpr int kDqThreads = 256;
 
-template <int D, bool CAUSAL>
+template <typename T, int D, bool CAUSAL>
 __global__ __launch_bounds__(kDqThreads, 2) __attribute__((amdgpu_waves_per_eu(2, 2)))
-void bwd_dq_bf16_kernel(const bf16* __restrict__ Q, const bf16* __restrict__ K,
-                        const bf16* __restrict__ V, const bf16* __restrict__ dO,
-                        const float* __restrict__ LD,
-                        bf16* __restrict__ dQ, int Nq, int Nk, int nqt, float c, float scale,
-                        int off) {
+void bwd_dq_kernel(const T* __restrict__ Q, const T* __restrict__ K, const T* __restrict__ V,
+                   const T* __restrict__ dO, const float* __restrict__ LD, T* __restrict__ dQ,
+                   int Nq, int Nk, int nqt, float c, float scale, int off) {
+  typedef typename Vec<T>::x8 T8;
+  typedef typename Vec<T>::x4 T4;
   constexpr int BR = kDqBR, BC = kDqBC;
   constexpr int NKK = D / 16;
   constexpr int NNT = D / 32;
@@ -387,9 +388,9 @@ void bwd_dq_bf16_kernel(const bf16* __restrict__ Q, const bf16* __restrict__ K,
   // K tiles (buffers 0/1) and V tiles (buffers 2/3), swizzled (see swz) and
   // double-buffered: tile j+1 loads while tile j (buffers j & 1) is read.
   // The key loop is unrolled by two so that buffer offsets are constants.
-  __shared__ __attribute__((aligned(1024))) bf16 smem[4 * TILE];
-  bf16* const sK0 = smem;
-  bf16* const sV0 = smem + 2 * TILE;
+  __shared__ __attribute__((aligned(1024))) T smem[4 * TILE];
+  T* const sK0 = smem;
+  T* const sV0 = smem + 2 * TILE;
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -404,8 +405,8 @@ void bwd_dq_bf16_kernel(const bf16* __restrict__ Q, const bf16* __restrict__ K,
   const int bh = logical / nwg;
   const int t = logical - bh * nwg;
   const size_t qbase = (size_t)bh * Nq * D;
-  const bf16* Kh = K + (size_t)bh * Nk * D;
-  const bf16* Vh = V + (size_t)bh * Nk * D;
+  const T* Kh = K + (size_t)bh * Nk * D;
+  const T* Vh = V + (size_t)bh * Nk * D;
 
   using KV = BufTile<D, BC, kDqThreads>;
   const KV kv(wave, lane);
@@ -430,14 +431,14 @@ void bwd_dq_bf16_kernel(const bf16* __restrict__ Q, const bf16* __restrict__ K,
       for (int nt = 0; nt < NNT; ++nt) ta[hi * NNT + nt] = trsw.off(0, hi, nt * 32);
   }
   auto sfrag = [&](int buf, int mt, int st) {
-    const bf16* base = ((st & 1) ? sV0 : sK0) + buf * TILE;
-    return *at_byte<bf16x8>(base, ra[st >> 1] + mt * 32 * 2 * D);
+    const T* base = ((st & 1) ? sV0 : sK0) + buf * TILE;
+    return *at_byte<T8>(base, ra[st >> 1] + mt * 32 * 2 * D);
   };
   auto kt_frag = [&](int buf, int mt, int st) {
     const unsigned rb = (mt * 32 + (st / NNT) * 16) * 2 * D;
-    const bf16* base = sK0 + buf * TILE;
-    return concat(lds_read_tr(to_lds(at_byte<bf16>(base, ta[st % NNT] + rb))),
-                  lds_read_tr(to_lds(at_byte<bf16>(base, ta[NNT + st % NNT] + rb))));
+    const T* base = sK0 + buf * TILE;
+    return concat(lds_read_tr<T>(to_lds(at_byte<T>(base, ta[st % NNT] + rb))),
+                  lds_read_tr<T>(to_lds(at_byte<T>(base, ta[NNT + st % NNT] + rb))));
   };
   constexpr int SRING = 4, TRING = 3;
 
@@ -449,12 +450,12 @@ void bwd_dq_bf16_kernel(const bf16* __restrict__ Q, const bf16* __restrict__ K,
 
     // This lane's query row: Q^T and dO^T fragments (B operands), L and D.
     const int qrow = q0 + wave * 32 + l32;
-    bf16x8 qf[NKK], dof[NKK];
+    T8 qf[NKK], dof[NKK];
 #pragma unroll
     for (int kk = 0; kk < NKK; ++kk) {
       const size_t o = qbase + (size_t)qrow * D + kk * 16 + half * 8;
-      qf[kk] = (qrow < Nq) ? *(const bf16x8*)(Q + o) : zero_bf16x8();
-      dof[kk] = (qrow < Nq) ? *(const bf16x8*)(dO + o) : zero_bf16x8();
+      qf[kk] = (qrow < Nq) ? *(const T8*)(Q + o) : zero8<T8>();
+      dof[kk] = (qrow < Nq) ? *(const T8*)(dO + o) : zero8<T8>();
     }
     const float l2 = (qrow < Nq) ? LD[2 * ((size_t)bh * Nq + qrow)] : INFINITY;
     const float drow = (qrow < Nq) ? LD[2 * ((size_t)bh * Nq + qrow) + 1] : 0.f;
@@ -479,10 +480,10 @@ void bwd_dq_bf16_kernel(const bf16* __restrict__ Q, const bf16* __restrict__ K,
       // dS^T for the 16 keys of element e of half mt: lane holds row qrow and
       // keys k0 + mt*32 + (i/4)*8 + half*4 + i%4.
       f32x16 sacc[2], dpacc[2];
-      bf16x8 dsf[4];
+      T8 dsf[4];
       auto ds_elem = [&](int mt, int i) {
         const float p = fast_exp2(fmaf(sacc[mt][i], c, -l2));
-        dsf[mt * 2 + (i >> 3)][i & 7] = (bf16)(p * (dpacc[mt][i] - drow));
+        dsf[mt * 2 + (i >> 3)][i & 7] = (T)(p * (dpacc[mt][i] - drow));
       };
       // Keys past the end and, causal, keys after the row's diagonal get
       // score -inf, hence P = 0 and dS = 0; only tiles that cross the
@@ -504,12 +505,12 @@ void bwd_dq_bf16_kernel(const bf16* __restrict__ Q, const bf16* __restrict__ K,
       auto sdp_half = [&](int mt, bool overlap) {
         sacc[mt] = (f32x16){};
         dpacc[mt] = (f32x16){};
-        bf16x8 ring[SRING];
+        T8 ring[SRING];
 #pragma unroll
         for (int st = 0; st < SRING; ++st) ring[st] = sfrag(P, mt, st);
 #pragma unroll
         for (int st = 0; st < 2 * NKK; ++st) {
-          const bf16x8 a = ring[st % SRING];
+          const T8 a = ring[st % SRING];
           if (st + SRING < 2 * NKK) ring[st % SRING] = sfrag(P, mt, st + SRING);
           if (st & 1) dpacc[mt] = mfma32(a, dof[st >> 1], dpacc[mt]);
           else sacc[mt] = mfma32(a, qf[st >> 1], sacc[mt]);
@@ -531,12 +532,12 @@ void bwd_dq_bf16_kernel(const bf16* __restrict__ Q, const bf16* __restrict__ K,
       // dQ^T += K^T dS^T over half mt (2*NNT MFMAs); with `overlap`, the dS
       // elements of half mt + 1 are computed between them.
       auto dq_half = [&](int mt, bool overlap) {
-        bf16x8 ring[TRING];
+        T8 ring[TRING];
 #pragma unroll
         for (int st = 0; st < TRING; ++st) ring[st] = kt_frag(P, mt, st);
 #pragma unroll
         for (int st = 0; st < 2 * NNT; ++st) {
-          const bf16x8 a = ring[st % TRING];
+          const T8 a = ring[st % TRING];
           if (st + TRING < 2 * NNT) ring[st % TRING] = kt_frag(P, mt, st + TRING);
           dqacc[st % NNT] = mfma32(a, dsf[mt * 2 + st / NNT], dqacc[st % NNT]);
           if (overlap) {
@@ -564,15 +565,15 @@ void bwd_dq_bf16_kernel(const bf16* __restrict__ Q, const bf16* __restrict__ K,
 
     // Epilogue: dQ = scale * dQ_acc; lane holds row qrow.
     if (qrow < Nq) {
-      bf16* out = dQ + qbase + (size_t)qrow * D;
+      T* out = dQ + qbase + (size_t)qrow * D;
 #pragma unroll
       for (int nt = 0; nt < NNT; ++nt)
 #pragma unroll
         for (int gg = 0; gg < 4; ++gg) {
-          bf16x4 v;
+          T4 v;
 #pragma unroll
-          for (int e = 0; e < 4; ++e) v[e] = (bf16)(dqacc[nt][gg * 4 + e] * scale);
-          *(bf16x4*)(out + nt * 32 + gg * 8 + half * 4) = v;
+          for (int e = 0; e < 4; ++e) v[e] = (T)(dqacc[nt][gg * 4 + e] * scale);
+          *(T4*)(out + nt * 32 + gg * 8 + half * 4) = v;
         }
     }
   }
@@ -695,16 +696,19 @@ hipError_t launch_pre(const BwdArgs& a, hipStream_t s) {
 
 }  // namespace
 
-hipError_t launch_bwd_bf16(const BwdArgs& a, int stages, hipStream_t s) {
+namespace {
+
+template <typename T>
+hipError_t launch_bwd_mfma(const BwdArgs& a, int stages, hipStream_t s) {
   const int BH = a.B * a.H;
   const float c = a.scale * kLog2e;
   const int off = a.Nk - a.Nq;
-  const bf16* Q = (const bf16*)a.Q;
-  const bf16* K = (const bf16*)a.K;
-  const bf16* V = (const bf16*)a.V;
-  const bf16* dO = (const bf16*)a.dO;
+  const T* Q = (const T*)a.Q;
+  const T* K = (const T*)a.K;
+  const T* V = (const T*)a.V;
+  const T* dO = (const T*)a.dO;
   if (stages & 1) {
-    const hipError_t e = (a.d == 128) ? launch_pre<128, bf16>(a, s) : launch_pre<64, bf16>(a, s);
+    const hipError_t e = (a.d == 128) ? launch_pre<128, T>(a, s) : launch_pre<64, T>(a, s);
     if (e != hipSuccess) return e;
   }
   if ((stages & 2) && a.Nk > 0) {
@@ -712,9 +716,8 @@ hipError_t launch_bwd_bf16(const BwdArgs& a, int stages, hipStream_t s) {
     const int nblocks = nkt * BH;
     const int hpx = (BH % kNumXcd == 0) ? BH / kNumXcd : 0;
 #define FA_DKDV_LAUNCH(DD, CC)                                                                  \
-  hipLaunchKernelGGL((bwd_dkdv_bf16_kernel<DD, CC>), dim3(nblocks), dim3(kKvThreads), 0, s, Q, K, \
-                     V, dO, a.LD, (bf16*)a.dK, (bf16*)a.dV, a.Nq, a.Nk, nkt, BH, hpx, c,     \
-                     a.scale, off)
+  hipLaunchKernelGGL((bwd_dkdv_kernel<T, DD, CC>), dim3(nblocks), dim3(kKvThreads), 0, s, Q, K, \
+                     V, dO, a.LD, (T*)a.dK, (T*)a.dV, a.Nq, a.Nk, nkt, BH, hpx, c, a.scale, off)
     if (a.d == 128) {
       if (a.causal) FA_DKDV_LAUNCH(128, true); else FA_DKDV_LAUNCH(128, false);
     } else {
@@ -728,8 +731,8 @@ hipError_t launch_bwd_bf16(const BwdArgs& a, int stages, hipStream_t s) {
     const int nqt = (a.Nq + kDqBR - 1) / kDqBR;
     const int nblocks = (a.causal ? (nqt + 1) / 2 : nqt) * BH;  // causal: query tile pairs
 #define FA_DQ_LAUNCH(DD, CC)                                                                    \
-  hipLaunchKernelGGL((bwd_dq_bf16_kernel<DD, CC>), dim3(nblocks), dim3(kDqThreads), 0, s, Q, K,  \
-                     V, dO, a.LD, (bf16*)a.dQ, a.Nq, a.Nk, nqt, c, a.scale, off)
+  hipLaunchKernelGGL((bwd_dq_kernel<T, DD, CC>), dim3(nblocks), dim3(kDqThreads), 0, s, Q, K,  \
+                     V, dO, a.LD, (T*)a.dQ, a.Nq, a.Nk, nqt, c, a.scale, off)
     if (a.d == 128) {
       if (a.causal) FA_DQ_LAUNCH(128, true); else FA_DQ_LAUNCH(128, false);
     } else {
@@ -739,6 +742,15 @@ hipError_t launch_bwd_bf16(const BwdArgs& a, int stages, hipStream_t s) {
     return hipGetLastError();
   }
   return hipSuccess;
+}
+
+}  // namespace
+
+hipError_t launch_bwd_bf16(const BwdArgs& a, int stages, hipStream_t s) {
+  return launch_bwd_mfma<bf16>(a, stages, s);
+}
+hipError_t launch_bwd_f16(const BwdArgs& a, int stages, hipStream_t s) {
+  return launch_bwd_mfma<f16>(a, stages, s);
 }
 
 hipError_t launch_bwd_f32(const BwdArgs& a, int stages, hipStream_t s) {

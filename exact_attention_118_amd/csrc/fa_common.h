@@ -9,9 +9,24 @@ namespace fa {
 typedef __bf16 bf16;
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef _Float16 f16;
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x4 __attribute__((ext_vector_type(4)));
 typedef short i16x4 __attribute__((ext_vector_type(4)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
+
+// The MFMA kernels take 16-bit inputs, bf16 or fp16; Vec<T> names their
+// 8- and 4-element vectors.
+template <typename T> struct Vec;
+template <> struct Vec<bf16> {
+  typedef bf16x8 x8;
+  typedef bf16x4 x4;
+};
+template <> struct Vec<f16> {
+  typedef f16x8 x8;
+  typedef f16x4 x4;
+};
 
 #define FA_LDS __attribute__((address_space(3)))
 
@@ -19,12 +34,15 @@ constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
 constexpr int kNumXcd = 8;
 
-// 32x32x16 bf16 MFMA, fp32 accumulate.  Operand layout (lane l of 64):
+// 32x32x16 bf16 / fp16 MFMA, fp32 accumulate.  Operand layout (lane l of 64):
 //   A[m][k]: m = l % 32, k = (l / 32) * 8 + e      (e = vector element 0..7)
 //   B[k][n]: n = l % 32, k = (l / 32) * 8 + e
 //   C[m][n]: n = l % 32, m = (i / 4) * 8 + (l / 32) * 4 + i % 4   (i = 0..15)
 __device__ __forceinline__ f32x16 mfma32(bf16x8 a, bf16x8 b, f32x16 c) {
   return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+}
+__device__ __forceinline__ f32x16 mfma32(f16x8 a, f16x8 b, f32x16 c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_f16(a, b, c, 0, 0, 0);
 }
 
 // LDS transposed read of 16-bit data.  Within each group of 16 lanes, lane s
@@ -32,9 +50,10 @@ __device__ __forceinline__ f32x16 mfma32(bf16x8 a, bf16x8 b, f32x16 c) {
 // (r % 4) of the rows supplied by lanes r/4, r/4 + 4, r/4 + 8, r/4 + 12.
 // When lane s points at row (k0 + s/4), column (n0 + (s%4)*4) of a row-major
 // tile, lane r receives column n0 + r of rows k0 .. k0+3.
-__device__ __forceinline__ bf16x4 lds_read_tr(const FA_LDS void* p) {
+template <typename T = bf16>
+__device__ __forceinline__ typename Vec<T>::x4 lds_read_tr(const FA_LDS void* p) {
   i16x4 v = __builtin_amdgcn_ds_read_tr16_b64_v4i16((FA_LDS i16x4*)p);
-  return __builtin_bit_cast(bf16x4, v);
+  return __builtin_bit_cast(typename Vec<T>::x4, v);
 }
 
 template <typename T>
@@ -45,12 +64,15 @@ __device__ __forceinline__ const FA_LDS T* to_lds(const T* p) {
 __device__ __forceinline__ bf16x8 concat(bf16x4 a, bf16x4 b) {
   return __builtin_shufflevector(a, b, 0, 1, 2, 3, 4, 5, 6, 7);
 }
-
-__device__ __forceinline__ bf16x8 zero_bf16x8() {
-  return __builtin_bit_cast(bf16x8, (uint4){0u, 0u, 0u, 0u});
+__device__ __forceinline__ f16x8 concat(f16x4 a, f16x4 b) {
+  return __builtin_shufflevector(a, b, 0, 1, 2, 3, 4, 5, 6, 7);
 }
 
-__device__ __forceinline__ float bf2f(bf16 x) { return (float)x; }
+template <typename V8>
+__device__ __forceinline__ V8 zero8() {
+  return __builtin_bit_cast(V8, (uint4){0u, 0u, 0u, 0u});
+}
+__device__ __forceinline__ bf16x8 zero_bf16x8() { return zero8<bf16x8>(); }
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
@@ -135,42 +157,6 @@ __device__ __forceinline__ const T* at_byte(const void* base, unsigned off) {
   return (const T*)((const char*)base + off);
 }
 
-// Rows [row0, row0 + ROWS) of a row-major [*, D] bf16 matrix g into a swizzled
-// LDS tile, with direct-to-LDS loads (global_load_lds_dwordx4: lane i of a
-// wave instruction writes 16 bytes at the instruction's LDS base + 16 i).
-// Rows at or beyond nvalid (>= 1) are read from row nvalid - 1 instead, so the
-// tile holds finite data that the caller masks.  The tile takes
-// ROWS * D / 8 / THREADS instructions per wave; dma_part issues instruction u
-// of the calling wave, so a kernel can spread them over its compute.  The data
-// is in LDS once every wave has waited for vmcnt and passed a barrier.
-template <int D, int ROWS, int THREADS>
-struct DmaTile {
-  static constexpr int CPR = D / 8;
-  static constexpr int PER = ROWS * CPR / THREADS;
-  static_assert(PER * THREADS == ROWS * CPR && THREADS % 64 == 0, "tile split");
-};
-
-template <int D, int ROWS, int THREADS>
-__device__ __forceinline__ void dma_part(const bf16* __restrict__ g, int row0, int nvalid,
-                                         bf16* lds, int tid, int u) {
-  using T = DmaTile<D, ROWS, THREADS>;
-  const int wave = tid >> 6, lane = tid & 63;
-  const int slot0 = (wave * T::PER + u) * 64;
-  const int slot = slot0 + lane;
-  const int r = slot / T::CPR, pch = slot % T::CPR;
-  const int grow = min(row0 + r, nvalid - 1);
-  const bf16* src = g + (size_t)grow * D + ((pch ^ swz<D>(r)) << 3);
-  __builtin_amdgcn_global_load_lds((const void*)src, (FA_LDS void*)(lds + slot0 * 8), 16, 0, 0);
-}
-
-template <int D, int ROWS, int THREADS>
-__device__ __forceinline__ void dma_tile(const bf16* __restrict__ g, int row0, int nvalid,
-                                         bf16* lds, int tid) {
-#pragma unroll
-  for (int u = 0; u < DmaTile<D, ROWS, THREADS>::PER; ++u)
-    dma_part<D, ROWS, THREADS>(g, row0, nvalid, lds, tid, u);
-}
-
 // gfx9 buffer descriptor, word 3: 32-bit data format, so that raw (untyped)
 // buffer loads are range-checked per dword against the record count.
 constexpr int kRsrcWord3 = 0x00020000;
@@ -189,7 +175,7 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, in
 // Direct-to-LDS tile loads through a buffer resource (buffer_load_dwordx4 with
 // the lds flag: lane i of a wave instruction writes 16 bytes at the
 // instruction's LDS base + 16 i).  Rows [row0, row0 + ROWS) of a row-major
-// [nvalid, D] bf16 matrix go into a tile swizzled as swz lays it out; rows at
+// [nvalid, D] matrix of 16-bit elements go into a tile swizzled as swz lays it out; rows at
 // or past nvalid read as zeros.  A lane keeps the byte offsets of its PER
 // chunks for the whole kernel; the row base, the row count and the LDS
 // address are wave-uniform (scalar registers), so a load costs no vector-ALU
@@ -211,8 +197,9 @@ struct BufTile {
     }
   }
   // Load u (0 <= u < PER) of this wave for the tile at row0 into lds.
-  __device__ __forceinline__ void part(const bf16* g, int row0, int nvalid, bf16* lds,
-                                       int u) const {
+  template <typename T>
+  __device__ __forceinline__ void part(const T* g, int row0, int nvalid, T* lds, int u) const {
+    static_assert(sizeof(T) == 2, "16-bit elements");
     // (readfirstlane: the clamp compiles to a vector instruction, and a
     // resource in vector registers would need a loop over its distinct values)
 #if __HIP_DEVICE_COMPILE__
@@ -222,7 +209,8 @@ struct BufTile {
                                              16, voff[u], 0, 0, 0);
 #endif
   }
-  __device__ __forceinline__ void tile(const bf16* g, int row0, int nvalid, bf16* lds) const {
+  template <typename T>
+  __device__ __forceinline__ void tile(const T* g, int row0, int nvalid, T* lds) const {
 #pragma unroll
     for (int u = 0; u < PER; ++u) part(g, row0, nvalid, lds, u);
   }

@@ -11,11 +11,11 @@
 // pass (the 51CTO FlashAttention V1/V2 notes, "FlashAttention V2 相比V1有哪些改进").  The exponent uses
 // exp2 with scale*log2(e) folded on the host (the 51CTO FlashAttention V1/V2 notes, "指令级别的优化").
 //
-// gfx950 mapping (bf16 kernel):
+// gfx950 mapping (bf16 / fp16 kernel):
 //  * 256 threads = 4 waves; the workgroup owns BR = 128 query rows and each
 //    wave owns 32 of them ("sliced-Q", the 51CTO FlashAttention V1/V2 notes "Warp Level 并行": all waves
 //    read the same K/V tile, so no cross-wave reduction is needed).
-//  * Scores are computed transposed, S^T = K Q^T, with the 32x32x16 bf16
+//  * Scores are computed transposed, S^T = K Q^T, with the 32x32x16 bf16/fp16
 //    MFMA: each lane then holds 16 scores of ONE query row (its lane % 32), so
 //    row max / row sum are lane-local plus a single exchange with lane ^ 32.
 //  * O^T = V^T P^T reuses the S^T accumulator registers directly as the
@@ -46,11 +46,13 @@ constexpr int kFwdBC = 64;   // keys per K/V tile
 constexpr int kFwdThreads = 256;
 constexpr float kRescaleSlack = 8.f;  // see the online softmax below
 
-template <int D, bool CAUSAL>
+template <typename T, int D, bool CAUSAL>
 __global__ __launch_bounds__(kFwdThreads, 2) __attribute__((amdgpu_waves_per_eu(2, 2)))
-void fwd_bf16_kernel(const bf16* __restrict__ Q, const bf16* __restrict__ K,
-                     const bf16* __restrict__ V, bf16* __restrict__ O, float* __restrict__ L,
+void fwd_kernel(const T* __restrict__ Q, const T* __restrict__ K, const T* __restrict__ V,
+                T* __restrict__ O, float* __restrict__ L,
                      int Nq, int Nk, int nqt, float c, int off) {
+  typedef typename Vec<T>::x8 T8;
+  typedef typename Vec<T>::x4 T4;
   constexpr int BR = kFwdBR, BC = kFwdBC;
   constexpr int NKK = D / 16;  // MFMA k-steps over the head dim
   constexpr int NNT = D / 32;  // 32-wide output tiles over the head dim
@@ -60,9 +62,9 @@ void fwd_bf16_kernel(const bf16* __restrict__ Q, const bf16* __restrict__ K,
   // j+1 (loading) at buffers 2/3; all swizzled (see swz).  Tile j's buffers
   // are j & 1; the loop below is unrolled by two so that every LDS address
   // offset is a compile-time constant.
-  __shared__ __attribute__((aligned(1024))) bf16 smem[4 * TILE];
-  bf16* const sK0 = smem;
-  bf16* const sV0 = smem + 2 * TILE;
+  __shared__ __attribute__((aligned(1024))) T smem[4 * TILE];
+  T* const sK0 = smem;
+  T* const sV0 = smem + 2 * TILE;
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -81,8 +83,8 @@ void fwd_bf16_kernel(const bf16* __restrict__ Q, const bf16* __restrict__ K,
   const int bh = logical / nwg;
   const int t = logical - bh * nwg;
   const size_t qbase = (size_t)bh * Nq * D;
-  const bf16* Kh = K + (size_t)bh * Nk * D;
-  const bf16* Vh = V + (size_t)bh * Nk * D;
+  const T* Kh = K + (size_t)bh * Nk * D;
+  const T* Vh = V + (size_t)bh * Nk * D;
 
   using KV = BufTile<D, BC, kFwdThreads>;
   const KV kv(wave, lane);
@@ -108,13 +110,13 @@ void fwd_bf16_kernel(const bf16* __restrict__ Q, const bf16* __restrict__ K,
       for (int nt = 0; nt < NNT; ++nt) va[hi * NNT + nt] = vtr.off(0, hi, nt * 32);
   }
   auto kfrag = [&](int buf, int st) {
-    return *at_byte<bf16x8>(sK0 + buf * TILE, ka[st >> 1] + (st & 1) * 32 * 2 * D);
+    return *at_byte<T8>(sK0 + buf * TILE, ka[st >> 1] + (st & 1) * 32 * 2 * D);
   };
   auto vfrag = [&](int buf, int st) {
     const unsigned rb = (st / NNT) * 16 * 2 * D;
-    const bf16* base = sV0 + buf * TILE;
-    return concat(lds_read_tr(to_lds(at_byte<bf16>(base, va[st % NNT] + rb))),
-                  lds_read_tr(to_lds(at_byte<bf16>(base, va[NNT + st % NNT] + rb))));
+    const T* base = sV0 + buf * TILE;
+    return concat(lds_read_tr<T>(to_lds(at_byte<T>(base, va[st % NNT] + rb))),
+                  lds_read_tr<T>(to_lds(at_byte<T>(base, va[NNT + st % NNT] + rb))));
   };
   constexpr int KRING = 4, VRING = 3;
 
@@ -126,11 +128,11 @@ void fwd_bf16_kernel(const bf16* __restrict__ Q, const bf16* __restrict__ K,
 
     // This lane's query row and its Q^T fragments (B operand of S^T = K Q^T).
     const int qrow = q0 + wave * 32 + l32;
-    bf16x8 qf[NKK];
+    T8 qf[NKK];
 #pragma unroll
     for (int kk = 0; kk < NKK; ++kk)
-      qf[kk] = (qrow < Nq) ? *(const bf16x8*)(Q + qbase + (size_t)qrow * D + kk * 16 + half * 8)
-                           : zero_bf16x8();
+      qf[kk] = (qrow < Nq) ? *(const T8*)(Q + qbase + (size_t)qrow * D + kk * 16 + half * 8)
+                           : zero8<T8>();
 
     // Keys this workgroup needs: all, or (causal) up to the last row's diagonal.
     const int kend = CAUSAL ? min(Nk, q0 + BR + off) : Nk;
@@ -160,14 +162,14 @@ void fwd_bf16_kernel(const bf16* __restrict__ Q, const bf16* __restrict__ K,
     };
     // Scores of one K tile (2 x NKK MFMA steps) from LDS buffer buf.
     auto scores = [&](int buf, f32x16 (&sc)[2]) {
-      bf16x8 ring[KRING];
+      T8 ring[KRING];
 #pragma unroll
       for (int st = 0; st < KRING; ++st) ring[st] = kfrag(buf, st);
       sc[0] = (f32x16){};
       sc[1] = (f32x16){};
 #pragma unroll
       for (int st = 0; st < 2 * NKK; ++st) {
-        const bf16x8 a = ring[st % KRING];
+        const T8 a = ring[st % KRING];
         if (st + KRING < 2 * NKK) ring[st % KRING] = kfrag(buf, st + KRING);
         sc[st & 1] = mfma32(a, qf[st >> 1], sc[st & 1]);
       }
@@ -203,7 +205,7 @@ void fwd_bf16_kernel(const bf16* __restrict__ Q, const bf16* __restrict__ K,
       // of the exponentials moves to the new row max only when some row of the
       // wave has grown by more than kRescaleSlack (log2 units); until then
       // probabilities are taken against the older, smaller reference and stay
-      // below 2^kRescaleSlack, where fp32 sums and bf16 operands keep their full
+      // below 2^kRescaleSlack, where fp32 sums and 16-bit operands keep their full
       // relative precision.  The result is the same in exact arithmetic, and
       // most tiles skip rescaling the accumulators.  The row max of tile j was
       // taken while tile j-1's P V product ran.
@@ -226,7 +228,7 @@ void fwd_bf16_kernel(const bf16* __restrict__ Q, const bf16* __restrict__ K,
       constexpr int NPAIR = 16;
       constexpr int kPairsA = (D == 128) ? 8 : NPAIR;
       static_assert(NPAIR - kPairsA <= 2 * NNT, "late pairs fit before chunk 2 is read");
-      bf16x8 pf[4];
+      T8 pf[4];
       float rs0 = 0.f, rs1 = 0.f;
       auto prob_pair = [&](int pr) {
         const int el = 2 * pr, kc = el >> 3, e = el & 7;
@@ -235,8 +237,8 @@ void fwd_bf16_kernel(const bf16* __restrict__ Q, const bf16* __restrict__ K,
         const float p1 = fast_exp2(fmaf(scur[mt][i + 1], c, -m_ref));
         rs0 += p0;
         rs1 += p1;
-        pf[kc][e] = (bf16)p0;
-        pf[kc][e + 1] = (bf16)p1;
+        pf[kc][e] = (T)p0;
+        pf[kc][e + 1] = (T)p1;
         pin(pf[kc]);
         pin(rs0);
         pin(rs1);
@@ -251,14 +253,14 @@ void fwd_bf16_kernel(const bf16* __restrict__ Q, const bf16* __restrict__ K,
       // interleaved.
       {
         constexpr int SA = 2 * NKK;
-        bf16x8 ring[KRING];
+        T8 ring[KRING];
 #pragma unroll
         for (int st = 0; st < KRING; ++st) ring[st] = kfrag(1 - P, st);
         snext[0] = (f32x16){};
         snext[1] = (f32x16){};
 #pragma unroll
         for (int st = 0; st < SA; ++st) {
-          const bf16x8 a = ring[st % KRING];
+          const T8 a = ring[st % KRING];
           if (st + KRING < SA) ring[st % KRING] = kfrag(1 - P, st + KRING);
           snext[st & 1] = mfma32(a, qf[st >> 1], snext[st & 1]);
           if ((st & 1) == 0) {
@@ -280,13 +282,13 @@ void fwd_bf16_kernel(const bf16* __restrict__ Q, const bf16* __restrict__ K,
       // interleaved with the remaining probability pairs and the row max of
       // tile j+1.
       {
-        bf16x8 ring[VRING];
+        T8 ring[VRING];
         float mxa = -INFINITY, mxb = -INFINITY;
 #pragma unroll
         for (int st = 0; st < VRING; ++st) ring[st] = vfrag(P, st);
 #pragma unroll
         for (int st = 0; st < 4 * NNT; ++st) {
-          const bf16x8 a = ring[st % VRING];
+          const T8 a = ring[st % VRING];
           if (st + VRING < 4 * NNT) ring[st % VRING] = vfrag(P, st + VRING);
           oacc[st % NNT] = mfma32(a, pf[st / NNT], oacc[st % NNT]);
           if (kPairsA + st < NPAIR) prob_pair(kPairsA + st);
@@ -315,15 +317,15 @@ void fwd_bf16_kernel(const bf16* __restrict__ Q, const bf16* __restrict__ K,
     const float l_tot = l_run + wave_shfl_xor(l_run, 32);
     if (qrow < Nq) {
       const float inv = 1.f / l_tot;
-      bf16* orow = O + qbase + (size_t)qrow * D;
+      T* orow = O + qbase + (size_t)qrow * D;
 #pragma unroll
       for (int nt = 0; nt < NNT; ++nt)
 #pragma unroll
         for (int gg = 0; gg < 4; ++gg) {
-          bf16x4 v;
+          T4 v;
 #pragma unroll
-          for (int e = 0; e < 4; ++e) v[e] = (bf16)(oacc[nt][gg * 4 + e] * inv);
-          *(bf16x4*)(orow + nt * 32 + gg * 8 + half * 4) = v;
+          for (int e = 0; e < 4; ++e) v[e] = (T)(oacc[nt][gg * 4 + e] * inv);
+          *(T4*)(orow + nt * 32 + gg * 8 + half * 4) = v;
         }
       if (half == 0) L[(size_t)bh * Nq + qrow] = (m_run + log2f(l_tot)) * kLn2;
     }
@@ -402,19 +404,22 @@ __global__ __launch_bounds__(kF32Rows) void fwd_f32_kernel(
 
 }  // namespace
 
-hipError_t launch_fwd_bf16(const FwdArgs& a, hipStream_t s) {
+namespace {
+
+template <typename T>
+hipError_t launch_fwd_mfma(const FwdArgs& a, hipStream_t s) {
   const int BH = a.B * a.H;
   const int nqt = (a.Nq + kFwdBR - 1) / kFwdBR;
   // Causal: one workgroup per pair of query tiles (t, nqt-1-t).
   const int nblocks = (a.causal ? (nqt + 1) / 2 : nqt) * BH;
   const float c = a.scale * kLog2e;
   const int off = a.Nk - a.Nq;
-  const bf16* Q = (const bf16*)a.Q;
-  const bf16* K = (const bf16*)a.K;
-  const bf16* V = (const bf16*)a.V;
-  bf16* O = (bf16*)a.O;
+  const T* Q = (const T*)a.Q;
+  const T* K = (const T*)a.K;
+  const T* V = (const T*)a.V;
+  T* O = (T*)a.O;
 #define FA_FWD_LAUNCH(DD, CC)                                                                  \
-  hipLaunchKernelGGL((fwd_bf16_kernel<DD, CC>), dim3(nblocks), dim3(kFwdThreads), 0, s, Q, K, V, \
+  hipLaunchKernelGGL((fwd_kernel<T, DD, CC>), dim3(nblocks), dim3(kFwdThreads), 0, s, Q, K, V, \
                      O, a.L, a.Nq, a.Nk, nqt, c, off)
   if (a.d == 128) {
     if (a.causal) FA_FWD_LAUNCH(128, true); else FA_FWD_LAUNCH(128, false);
@@ -424,6 +429,11 @@ hipError_t launch_fwd_bf16(const FwdArgs& a, hipStream_t s) {
 #undef FA_FWD_LAUNCH
   return hipGetLastError();
 }
+
+}  // namespace
+
+hipError_t launch_fwd_bf16(const FwdArgs& a, hipStream_t s) { return launch_fwd_mfma<bf16>(a, s); }
+hipError_t launch_fwd_f16(const FwdArgs& a, hipStream_t s) { return launch_fwd_mfma<f16>(a, s); }
 
 hipError_t launch_fwd_f32(const FwdArgs& a, hipStream_t s) {
   const int BH = a.B * a.H;

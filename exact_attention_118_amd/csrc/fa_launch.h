@@ -37,16 +37,20 @@ struct BwdArgs {
 
 // Tiled forward (Q-tile per workgroup, K/V streamed through LDS).
 hipError_t launch_fwd_bf16(const FwdArgs& a, hipStream_t s);
+hipError_t launch_fwd_f16(const FwdArgs& a, hipStream_t s);
 hipError_t launch_fwd_f32(const FwdArgs& a, hipStream_t s);
 
 // Split-key forward for one query row per head, then the logsumexp combine.
 // part_o: [splits, B*H, d] fp32, part_l: [splits, B*H] fp32.
 hipError_t launch_fwd_split_bf16(const FwdArgs& a, int splits, float* part_o, float* part_l,
                                  hipStream_t s);
+hipError_t launch_fwd_split_f16(const FwdArgs& a, int splits, float* part_o, float* part_l,
+                                hipStream_t s);
 
 // Backward: D = rowsum(dO*O) and L*log2(e); dK and dV; dQ.
 // `stages`: bit 1 the (L*log2 e, D) pairs, bit 2 dK/dV kernel, bit 4 dQ kernel (2 and 4 read them).
 hipError_t launch_bwd_bf16(const BwdArgs& a, int stages, hipStream_t s);
+hipError_t launch_bwd_f16(const BwdArgs& a, int stages, hipStream_t s);
 hipError_t launch_bwd_f32(const BwdArgs& a, int stages, hipStream_t s);
 
 // Key-chunk length used by the split path for `splits` chunks of Nk keys.

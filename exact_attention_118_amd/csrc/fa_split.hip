@@ -29,9 +29,9 @@ namespace {
 constexpr int kSplitThreads = 256;
 constexpr int kSplitPasses = 8;
 
-template <int D>
-__global__ __launch_bounds__(kSplitThreads) void fwd_split_bf16_kernel(
-    const bf16* __restrict__ Q, const bf16* __restrict__ K, const bf16* __restrict__ V,
+template <typename T, int D>
+__global__ __launch_bounds__(kSplitThreads) void fwd_split_kernel(
+    const T* __restrict__ Q, const T* __restrict__ K, const T* __restrict__ V,
     float* __restrict__ part_o, float* __restrict__ part_l, int Nk, int splits, int chunk,
     int BH, float c) {
   constexpr int TPR = D / 8;          // lanes per key row
@@ -51,7 +51,7 @@ __global__ __launch_bounds__(kSplitThreads) void fwd_split_bf16_kernel(
 
   float q[8];
   {
-    const bf16x8 qv = *(const bf16x8*)(Q + (size_t)bh * D + dpart * 8);
+    const typename Vec<T>::x8 qv = *(const typename Vec<T>::x8*)(Q + (size_t)bh * D + dpart * 8);
 #pragma unroll
     for (int e = 0; e < 8; ++e) q[e] = (float)qv[e];
   }
@@ -61,16 +61,16 @@ __global__ __launch_bounds__(kSplitThreads) void fwd_split_bf16_kernel(
   for (int e = 0; e < 8; ++e) o[e] = 0.f;
 
   for (int base = kb + wave * KPW; base < ke; base += 4 * KPW) {
-    bf16x8 kv[kSplitPasses], vv[kSplitPasses];
+    typename Vec<T>::x8 kv[kSplitPasses], vv[kSplitPasses];
 #pragma unroll
     for (int p = 0; p < kSplitPasses; ++p) {
       const int key = base + p * KPP + kgrp;
       if (key < ke) {
-        kv[p] = *(const bf16x8*)(K + kbase + (size_t)key * D + dpart * 8);
-        vv[p] = *(const bf16x8*)(V + kbase + (size_t)key * D + dpart * 8);
+        kv[p] = *(const typename Vec<T>::x8*)(K + kbase + (size_t)key * D + dpart * 8);
+        vv[p] = *(const typename Vec<T>::x8*)(V + kbase + (size_t)key * D + dpart * 8);
       } else {
-        kv[p] = zero_bf16x8();
-        vv[p] = zero_bf16x8();
+        kv[p] = zero8<typename Vec<T>::x8>();
+        vv[p] = zero8<typename Vec<T>::x8>();
       }
     }
     float s[kSplitPasses];
@@ -135,10 +135,10 @@ __global__ __launch_bounds__(kSplitThreads) void fwd_split_bf16_kernel(
 }
 
 // One workgroup of D threads per head: L = log sum_s exp(L_s), O = sum_s exp(L_s - L) O_s.
-template <int D>
+template <typename T, int D>
 __global__ __launch_bounds__(D) void split_combine_kernel(const float* __restrict__ part_o,
                                                           const float* __restrict__ part_l,
-                                                          bf16* __restrict__ O,
+                                                          T* __restrict__ O,
                                                           float* __restrict__ L, int splits,
                                                           int BH) {
   const int bh = blockIdx.x, e = threadIdx.x;
@@ -150,7 +150,7 @@ __global__ __launch_bounds__(D) void split_combine_kernel(const float* __restric
   float acc = 0.f;
   for (int s = 0; s < splits; ++s)
     acc = fmaf(expf(part_l[(size_t)s * BH + bh] - Lt), part_o[((size_t)s * BH + bh) * D + e], acc);
-  O[(size_t)bh * D + e] = (bf16)acc;
+  O[(size_t)bh * D + e] = (T)acc;
   if (e == 0) L[bh] = Lt;
 }
 
@@ -158,31 +158,45 @@ __global__ __launch_bounds__(D) void split_combine_kernel(const float* __restric
 
 int split_chunk(int Nk, int splits) { return (Nk + splits - 1) / splits; }
 
-hipError_t launch_fwd_split_bf16(const FwdArgs& a, int splits, float* part_o, float* part_l,
-                                 hipStream_t s) {
+namespace {
+
+template <typename T>
+hipError_t launch_split(const FwdArgs& a, int splits, float* part_o, float* part_l,
+                        hipStream_t s) {
   const int BH = a.B * a.H;
   const int chunk = split_chunk(a.Nk, splits);
   const float c = a.scale * kLog2e;
   const unsigned nblocks = (unsigned)splits * (unsigned)BH;
   if (a.d == 128) {
-    hipLaunchKernelGGL((fwd_split_bf16_kernel<128>), dim3(nblocks), dim3(kSplitThreads), 0, s,
-                       (const bf16*)a.Q, (const bf16*)a.K, (const bf16*)a.V, part_o, part_l, a.Nk,
-                       splits, chunk, BH, c);
+    hipLaunchKernelGGL((fwd_split_kernel<T, 128>), dim3(nblocks), dim3(kSplitThreads), 0, s,
+                       (const T*)a.Q, (const T*)a.K, (const T*)a.V, part_o, part_l, a.Nk, splits,
+                       chunk, BH, c);
   } else {
-    hipLaunchKernelGGL((fwd_split_bf16_kernel<64>), dim3(nblocks), dim3(kSplitThreads), 0, s,
-                       (const bf16*)a.Q, (const bf16*)a.K, (const bf16*)a.V, part_o, part_l, a.Nk,
-                       splits, chunk, BH, c);
+    hipLaunchKernelGGL((fwd_split_kernel<T, 64>), dim3(nblocks), dim3(kSplitThreads), 0, s,
+                       (const T*)a.Q, (const T*)a.K, (const T*)a.V, part_o, part_l, a.Nk, splits,
+                       chunk, BH, c);
   }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   if (a.d == 128) {
-    hipLaunchKernelGGL((split_combine_kernel<128>), dim3(BH), dim3(128), 0, s, part_o, part_l,
-                       (bf16*)a.O, a.L, splits, BH);
+    hipLaunchKernelGGL((split_combine_kernel<T, 128>), dim3(BH), dim3(128), 0, s, part_o, part_l,
+                       (T*)a.O, a.L, splits, BH);
   } else {
-    hipLaunchKernelGGL((split_combine_kernel<64>), dim3(BH), dim3(64), 0, s, part_o, part_l,
-                       (bf16*)a.O, a.L, splits, BH);
+    hipLaunchKernelGGL((split_combine_kernel<T, 64>), dim3(BH), dim3(64), 0, s, part_o, part_l,
+                       (T*)a.O, a.L, splits, BH);
   }
   return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_fwd_split_bf16(const FwdArgs& a, int splits, float* part_o, float* part_l,
+                                 hipStream_t s) {
+  return launch_split<bf16>(a, splits, part_o, part_l, s);
+}
+hipError_t launch_fwd_split_f16(const FwdArgs& a, int splits, float* part_o, float* part_l,
+                                hipStream_t s) {
+  return launch_split<f16>(a, splits, part_o, part_l, s);
 }
 
 }  // namespace fa

@@ -47,6 +47,9 @@ WORKLOADS = {
     # forward+backward, bf16, B=2, H=16, N=4096, d=128, causal and non-causal
     "b2h16n4096d128_causal": Workload("b2h16n4096d128_causal", 2, 16, 4096, 4096, 128, True, torch.bfloat16),
     "b2h16n4096d128": Workload("b2h16n4096d128", 2, 16, 4096, 4096, 128, False, torch.bfloat16),
+    # the same causal shape with fp16 inputs
+    "b2h16n4096d128_causal_fp16": Workload("b2h16n4096d128_causal_fp16", 2, 16, 4096, 4096, 128, True,
+                                           torch.float16),
     # long sequence, bf16, B=1, H=32, N=8192, d=128, causal, Q and K scaled by 3
     "b1h32n8192d128_causal": Workload("b1h32n8192d128_causal", 1, 32, 8192, 8192, 128, True,
                                       torch.bfloat16, qk_mult=3.0),

@@ -29,8 +29,9 @@
  *    failed launch (hipGetLastError).  Faults inside a kernel surface at the
  *    caller's next synchronisation, as for any HIP kernel.
  *  - An empty problem (B*H*Nq == 0) returns FA_OK and launches nothing.
- *  - Supported: dtype FA_BF16 with d in {64, 128} for every entry point;
- *    dtype FA_FP32 with d in {64, 128} for fa_fwd (non-split) and fa_bwd.
+ *  - Supported: dtypes FA_BF16 and FA_FP16 with d in {64, 128} for every
+ *    entry point (MFMA kernels, fp32 accumulation and statistics); dtype
+ *    FA_FP32 with d in {64, 128} for fa_fwd (non-split) and fa_bwd.
  *  - Thread safety: no global mutable state; concurrent calls on different
  *    streams with disjoint buffers are safe.
  */
@@ -53,7 +54,7 @@ typedef enum fa_status {
   FA_ERR_HIP = 6          /* a kernel launch failed */
 } fa_status;
 
-typedef enum fa_dtype { FA_BF16 = 0, FA_FP32 = 1 } fa_dtype;
+typedef enum fa_dtype { FA_BF16 = 0, FA_FP32 = 1, FA_FP16 = 2 } fa_dtype;
 
 /*
  * Forward pass: O = softmax(scale * Q K^T + mask) V and L = logsumexp of each
@@ -66,7 +67,7 @@ typedef enum fa_dtype { FA_BF16 = 0, FA_FP32 = 1 } fa_dtype;
  *  causal != 0 applies the mask above.
  *
  *  num_splits chooses the key-split ("Flash-Decoding", the 51CTO FlashAttention V1/V2 notes, last paragraph
- *  of "Sequence Parallel") path, available for Nq == 1 with FA_BF16:
+ *  of "Sequence Parallel") path, available for Nq == 1 with FA_BF16 or FA_FP16:
  *    0  = automatic (split path for Nq == 1 and bf16, tiled path otherwise),
  *    1  = tiled path for Nq > 1; for Nq == 1 the split path with one split,
  *    >1 = split path with that many key chunks (Nq must be 1).

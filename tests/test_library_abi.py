@@ -144,6 +144,11 @@ def test_workspace_queries(lib):
     assert lib.fa_fwd_num_splits(1, 1, 1, 1000, 64, fa.FA_BF16, 3) == 3
     assert lib.fa_fwd_num_splits(1, 1, 1, 10, 64, fa.FA_BF16, 50) == 10
     assert lib.fa_fwd_num_splits(1, 1, 1, 10, 64, fa.FA_FP32, 0) == 1
+    # fp16 takes the same paths and workspaces as bf16
+    assert lib.fa_fwd_num_splits(16, 32, 1, 16384, 128, fa.FA_FP16, 0) == s
+    assert lib.fa_fwd_workspace_size(16, 32, 1, 16384, 128, fa.FA_FP16, 0) == \
+        lib.fa_fwd_workspace_size(16, 32, 1, 16384, 128, fa.FA_BF16, 0)
+    assert lib.fa_bwd_workspace_size(B, H, N, N, d, fa.FA_FP16) == 2 * up(B * H * N * 4)
 
 
 def test_binding_fails_loudly_without_the_library(monkeypatch, tmp_path):
