@@ -15,7 +15,11 @@ Conventions (the readings of the pages that this oracle fixes):
   the 51CTO FlashAttention V1/V2 notes describes when it skips the upper-right blocks).  Masked scores are
   -inf, so they get probability exactly 0.
 * L is the natural-log logsumexp of the scaled, masked score row.
-* All arithmetic is float64 on inputs converted exactly from bf16 or fp32.
+* Additive bias (the "+ mask" of the method's formula, taken in general): an
+  optional [nq, nk] matrix added to the scaled scores before the causal mask;
+  -inf entries remove keys.  It is a constant of the computation (no
+  gradient is formed for it).
+* All arithmetic is float64 on inputs converted exactly from bf16, fp16 or fp32.
 """
 
 from __future__ import annotations
@@ -42,15 +46,18 @@ def causal_visible(nq: int, nk: int) -> np.ndarray:
     return j <= i + (nk - nq)
 
 
-def scores(Q, K, scale: float, causal: bool) -> np.ndarray:
-    """S = scale * Q K^T with -inf at masked positions.  Q [nq, dk], K [nk, dk].
+def scores(Q, K, scale: float, causal: bool, bias=None) -> np.ndarray:
+    """S = scale * Q K^T (+ bias) with -inf at masked positions.  Q [nq, dk], K [nk, dk].
 
     The CSDN post "Flash Attention1", "Flash Attention" section, first line of the formula (S = Q K^T),
-    with the softmax scale applied to the product.
+    with the softmax scale applied to the product and the additive mask term
+    (``bias`` [nq, nk], optional) added to it.
     """
     Q = _as_f64(Q)
     K = _as_f64(K)
     S = scale * (Q @ K.T)
+    if bias is not None:
+        S = S + _as_f64(bias)
     if causal:
         S = np.where(causal_visible(Q.shape[0], K.shape[0]), S, -np.inf)
     return S
@@ -75,19 +82,19 @@ def softmax_with_lse(S) -> tuple[np.ndarray, np.ndarray]:
     return P, L
 
 
-def attention_forward(Q, K, V, scale: float, causal: bool):
+def attention_forward(Q, K, V, scale: float, causal: bool, bias=None):
     """Forward pass for one head: returns (O [nq, dv], L [nq]).
 
     The CSDN post "Flash Attention1", "Flash Attention" section: S = Q K^T, P = softmax(S), O = P V;
     L as defined in ``softmax_with_lse``.
     """
-    S = scores(Q, K, scale, causal)
+    S = scores(Q, K, scale, causal, bias)
     P, L = softmax_with_lse(S)
     O = P @ _as_f64(V)
     return O, L
 
 
-def attention_forward_rows(Q, K, V, rows, scale: float, causal: bool):
+def attention_forward_rows(Q, K, V, rows, scale: float, causal: bool, bias=None):
     """Forward pass for selected query rows of one head (same definition).
 
     Row i of O and L depends only on Q_i and all of K, V, so a sample of rows
@@ -99,6 +106,8 @@ def attention_forward_rows(Q, K, V, rows, scale: float, causal: bool):
     nq, nk = Q.shape[0], K.shape[0]
     rows = np.asarray(rows, dtype=np.int64)
     S = scale * (Q[rows] @ K.T)
+    if bias is not None:
+        S = S + _as_f64(bias)[rows]
     if causal:
         vis = np.arange(nk)[None, :] <= (rows[:, None] + (nk - nq))
         S = np.where(vis, S, -np.inf)
@@ -106,7 +115,8 @@ def attention_forward_rows(Q, K, V, rows, scale: float, causal: bool):
     return P @ V, L
 
 
-def attention_backward(Q, K, V, dO, scale: float, causal: bool, return_aux: bool = False):
+def attention_backward(Q, K, V, dO, scale: float, causal: bool, return_aux: bool = False,
+                       bias=None):
     """Gradients of f = sum(dO * O) for one head: returns (dQ, dK, dV).
 
     P is recomputed from the inputs (the Huawei Cloud post "FlashAttention", section 3: recomputation in the
@@ -130,7 +140,7 @@ def attention_backward(Q, K, V, dO, scale: float, causal: bool, return_aux: bool
     K = _as_f64(K)
     V = _as_f64(V)
     dO = _as_f64(dO)
-    S = scores(Q, K, scale, causal)
+    S = scores(Q, K, scale, causal, bias)
     P, L = softmax_with_lse(S)
     dV = P.T @ dO
     dP = dO @ V.T
@@ -149,38 +159,50 @@ def _heads(x):
     return x.reshape((-1,) + x.shape[-2:]), lead
 
 
-def attention_forward_batched(Q, K, V, scale: float, causal: bool, heads=None):
+def _head_bias(bias, lead):
+    """Per-head view of a bias of shape [B or 1, H or 1, nq, nk] (None stays None)."""
+    if bias is None:
+        return None
+    b = np.broadcast_to(_as_f64(bias), tuple(lead) + np.shape(bias)[-2:])
+    return b.reshape((-1,) + b.shape[-2:])
+
+
+def attention_forward_batched(Q, K, V, scale: float, causal: bool, heads=None, bias=None):
     """``attention_forward`` over leading [B, H] dims, one head at a time.
 
-    Q [B, H, nq, d], K and V [B, H, nk, d].  ``heads`` (flat b*H + h indices)
-    restricts the work to a sample of heads; the result then has shape
-    [len(heads), nq, d] and [len(heads), nq].
+    Q [B, H, nq, d], K and V [B, H, nk, d], bias (optional) [B or 1, H or 1,
+    nq, nk].  ``heads`` (flat b*H + h indices) restricts the work to a sample
+    of heads; the result then has shape [len(heads), nq, d] and [len(heads), nq].
     """
     q, lead = _heads(Q)
     k, _ = _heads(K)
     v, _ = _heads(V)
+    bh = _head_bias(bias, lead)
     idx = range(q.shape[0]) if heads is None else list(heads)
     O = np.empty((len(idx), q.shape[1], v.shape[2]))
     L = np.empty((len(idx), q.shape[1]))
     for n, h in enumerate(idx):
-        O[n], L[n] = attention_forward(q[h], k[h], v[h], scale, causal)
+        O[n], L[n] = attention_forward(q[h], k[h], v[h], scale, causal,
+                                       None if bh is None else bh[h])
     if heads is None:
         return O.reshape(lead + O.shape[1:]), L.reshape(lead + L.shape[1:])
     return O, L
 
 
-def attention_backward_batched(Q, K, V, dO, scale: float, causal: bool, heads=None):
+def attention_backward_batched(Q, K, V, dO, scale: float, causal: bool, heads=None, bias=None):
     """``attention_backward`` over leading [B, H] dims, one head at a time."""
     q, lead = _heads(Q)
     k, _ = _heads(K)
     v, _ = _heads(V)
     do, _ = _heads(dO)
+    bh = _head_bias(bias, lead)
     idx = range(q.shape[0]) if heads is None else list(heads)
     dQ = np.empty((len(idx),) + q.shape[1:])
     dK = np.empty((len(idx),) + k.shape[1:])
     dV = np.empty((len(idx),) + v.shape[1:])
     for n, h in enumerate(idx):
-        dQ[n], dK[n], dV[n] = attention_backward(q[h], k[h], v[h], do[h], scale, causal)
+        dQ[n], dK[n], dV[n] = attention_backward(q[h], k[h], v[h], do[h], scale, causal,
+                                                 bias=None if bh is None else bh[h])
     if heads is None:
         return (dQ.reshape(lead + dQ.shape[1:]), dK.reshape(lead + dK.shape[1:]),
                 dV.reshape(lead + dV.shape[1:]))

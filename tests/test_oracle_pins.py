@@ -13,7 +13,10 @@ Sources of truth used here:
 * softmax identities: rows of P sum to 1, invariance under a per-row shift
   of the scores (the 51CTO FlashAttention V1/V2 notes, "理解FlashAttention核心逻辑": softmax -> safe softmax);
 * central finite differences of f = sum(dO * O);
-* torch's float64 scaled_dot_product_attention and autograd on the CPU.
+* torch's float64 scaled_dot_product_attention and autograd on the CPU;
+* for the additive bias: a per-row constant only shifts L, a bias ln(w_j)
+  weights key j by w_j (brute force with math.exp), and -inf entries are the
+  same as removing those keys.
 """
 
 import json
@@ -268,9 +271,98 @@ def check_brute_force(fwd, bwd):
     return bool(ok)
 
 
+def check_bias_row_constant(fwd, bwd):
+    """A bias constant along each row leaves O and the gradients unchanged and
+    adds that constant to L (softmax is invariant to a per-row shift)."""
+    ok = True
+    for n, (nq, nk, causal) in enumerate([(6, 6, True), (4, 9, False), (5, 7, True)]):
+        r = _rng(500 + n)
+        Q, K, V, dO = r.standard_normal((nq, 4)), r.standard_normal((nk, 4)), \
+            r.standard_normal((nk, 3)), r.standard_normal((nq, 3))
+        c = r.standard_normal(nq) * 2.0
+        bias = np.repeat(c[:, None], nk, axis=1)
+        O0, L0 = fwd(Q, K, V, 0.6, causal)
+        O1, L1 = fwd(Q, K, V, 0.6, causal, bias=bias)
+        ok &= _close(O1, O0, 1e-12) and _close(L1, L0 + c, 1e-12)
+        g0 = bwd(Q, K, V, dO, 0.6, causal)
+        g1 = bwd(Q, K, V, dO, 0.6, causal, bias=bias)
+        ok &= all(_close(a, b, 1e-11) for a, b in zip(g1, g0))
+    return bool(ok)
+
+
+def check_bias_log_weights(fwd, bwd):
+    """bias_ij = ln w_j weights key j by w_j: brute force with math.exp."""
+    ok = True
+    for n, (nq, nk, causal) in enumerate([(3, 4, False), (4, 4, True), (2, 5, True)]):
+        r = _rng(520 + n)
+        Q, K, V = r.standard_normal((nq, 2)), r.standard_normal((nk, 2)), r.standard_normal((nk, 2))
+        w = r.random(nk) + 0.1
+        bias = np.tile(np.log(w)[None, :], (nq, 1))
+        O_ref, L_ref = np.zeros((nq, 2)), np.zeros(nq)
+        for i in range(nq):
+            e = [0.0 if (causal and j > i + (nk - nq)) else
+                 w[j] * math.exp(0.8 * sum(Q[i, t] * K[j, t] for t in range(2))) for j in range(nk)]
+            L_ref[i] = math.log(sum(e))
+            for j in range(nk):
+                O_ref[i] += e[j] / sum(e) * V[j]
+        O, L = fwd(Q, K, V, 0.8, causal, bias=bias)
+        ok &= _close(O, O_ref, 1e-13) and _close(L, L_ref, 1e-13)
+    return bool(ok)
+
+
+def check_bias_neg_inf_drops_keys(fwd, bwd):
+    """-inf bias entries on a set of keys give the attention over the other
+    keys; the removed keys get zero dK and dV."""
+    ok = True
+    r = _rng(540)
+    nq, nk = 5, 9
+    Q, K, V, dO = r.standard_normal((nq, 4)), r.standard_normal((nk, 4)), r.standard_normal((nk, 3)), \
+        r.standard_normal((nq, 3))
+    keep = np.array([1, 0, 1, 1, 0, 0, 1, 0, 1], dtype=bool)
+    bias = np.where(keep[None, :], 0.0, -np.inf) * np.ones((nq, 1))
+    O, L = fwd(Q, K, V, 0.5, False, bias=bias)
+    O_r, L_r = fwd(Q, K[keep], V[keep], 0.5, False)
+    ok &= _close(O, O_r, 1e-12) and _close(L, L_r, 1e-12)
+    dQ, dK, dV = bwd(Q, K, V, dO, 0.5, False, bias=bias)
+    dQ_r, dK_r, dV_r = bwd(Q, K[keep], V[keep], dO, 0.5, False)
+    ok &= _close(dQ, dQ_r, 1e-11) and _close(dK[keep], dK_r, 1e-11) and _close(dV[keep], dV_r, 1e-11)
+    ok &= bool(np.all(dK[~keep] == 0) and np.all(dV[~keep] == 0))
+    return bool(ok)
+
+
+def _torch_ref_bias(Q, K, V, dO, scale, causal, bias):
+    q, k, v = (torch.tensor(x, dtype=torch.float64, requires_grad=True) for x in (Q, K, V))
+    m = torch.tensor(bias, dtype=torch.float64)
+    if causal:
+        nq, nk = q.shape[0], k.shape[0]
+        vis = torch.ones(nq, nk, dtype=torch.bool).tril(diagonal=nk - nq)
+        m = m.masked_fill(~vis, float("-inf"))
+    o = torch.nn.functional.scaled_dot_product_attention(
+        q[None, None], k[None, None], v[None, None], attn_mask=m[None, None], scale=scale)[0, 0]
+    o.backward(torch.tensor(dO, dtype=torch.float64))
+    return o.detach().numpy(), q.grad.numpy(), k.grad.numpy(), v.grad.numpy()
+
+
+def check_bias_torch_library(fwd, bwd):
+    """torch's float64 attention with an additive float mask, and its autograd."""
+    ok = True
+    for n, (nq, nk, d, causal) in enumerate([(8, 8, 16, False), (8, 8, 16, True), (5, 12, 8, True)]):
+        r = _rng(560 + n)
+        Q, K, V, dO = (r.standard_normal(s) for s in ((nq, d), (nk, d), (nk, d), (nq, d)))
+        bias = r.standard_normal((nq, nk)) * 1.5
+        scale = 1.0 / math.sqrt(d)
+        O_t, dQ_t, dK_t, dV_t = _torch_ref_bias(Q, K, V, dO, scale, causal, bias)
+        O, _ = fwd(Q, K, V, scale, causal, bias=bias)
+        dQ, dK, dV = bwd(Q, K, V, dO, scale, causal, bias=bias)
+        ok &= _close(O, O_t, 1e-10) and _close(dQ, dQ_t, 1e-10)
+        ok &= _close(dK, dK_t, 1e-10) and _close(dV, dV_t, 1e-10)
+    return bool(ok)
+
+
 ALL_CHECKS = [check_golden, check_walkthrough, check_shift_invariance, check_closed_forms,
               check_finite_differences, check_gradient_identities, check_split_combine,
-              check_torch_library, check_brute_force]
+              check_torch_library, check_brute_force, check_bias_row_constant,
+              check_bias_log_weights, check_bias_neg_inf_drops_keys, check_bias_torch_library]
 
 
 # --------------------------------------------------------------------------- tests
@@ -340,20 +432,45 @@ def test_rows_and_batched_entry_points_agree_with_torch():
     assert _close(Or, O_t[rows], 1e-10) and _close(Lr, L[1, 2, rows], 1e-12)
 
 
+def test_batched_bias_broadcasts_over_batch_and_heads():
+    """Bias [1, H, nq, nk] and [B, 1, nq, nk] apply to every batch / head."""
+    r = _rng(13)
+    B, H, N, d = 2, 3, 7, 4
+    Q, K, V, dO = (r.standard_normal((B, H, N, d)) for _ in range(4))
+    for shape in ((1, H, N, N), (B, 1, N, N), (B, H, N, N)):
+        bias = r.standard_normal(shape)
+        O, L = oracle.attention_forward_batched(Q, K, V, 0.5, True, bias=bias)
+        dQ, dK, dV = oracle.attention_backward_batched(Q, K, V, dO, 0.5, True, bias=bias)
+        full = np.broadcast_to(bias, (B, H, N, N))
+        for b in range(B):
+            for h in range(H):
+                Oh, Lh = oracle.attention_forward(Q[b, h], K[b, h], V[b, h], 0.5, True, bias=full[b, h])
+                gh = oracle.attention_backward(Q[b, h], K[b, h], V[b, h], dO[b, h], 0.5, True,
+                                               bias=full[b, h])
+                assert np.array_equal(O[b, h], Oh) and np.array_equal(L[b, h], Lh)
+                assert all(np.array_equal(g[b, h], e) for g, e in zip((dQ, dK, dV), gh))
+
+
 # --------------------------------------------------------------------------- planted mistakes
 # Copies of the oracle with one plausible mistake each.  Every one must fail at
 # least one pin above.
 
-def _mut_fwd(scale_in_scores=True, visible=None, lse_without_max=False, pv_transposed=False):
-    def scores(Q, K, scale, causal):
+def _mut_fwd(scale_in_scores=True, visible=None, lse_without_max=False, pv_transposed=False,
+             bias_scaled=False, bias_transposed=False):
+    def scores(Q, K, scale, causal, bias=None):
         S = (scale if scale_in_scores else 1.0) * (Q @ K.T)
+        if bias is not None:
+            b = np.asarray(bias, float)
+            if bias_transposed and b.shape[0] == b.shape[1]:
+                b = b.T
+            S = S + (scale * b if bias_scaled else b)
         if causal:
             vis = (visible or A.causal_visible)(Q.shape[0], K.shape[0])
             S = np.where(vis, S, -np.inf)
         return S
 
-    def fwd(Q, K, V, scale, causal):
-        S = scores(np.asarray(Q, float), np.asarray(K, float), scale, causal)
+    def fwd(Q, K, V, scale, causal, bias=None):
+        S = scores(np.asarray(Q, float), np.asarray(K, float), scale, causal, bias)
         m = S.max(axis=1, keepdims=True)
         e = np.exp(S - m)
         l = e.sum(axis=1, keepdims=True)
@@ -366,10 +483,10 @@ def _mut_fwd(scale_in_scores=True, visible=None, lse_without_max=False, pv_trans
 
 
 def _mut_bwd(scores, dv_no_transpose=False, ds_sign=False, dq_no_scale=False,
-             dk_wrong_operand=False, d_from_wrong_axis=False):
-    def bwd(Q, K, V, dO, scale, causal):
+             dk_wrong_operand=False, d_from_wrong_axis=False, bias_ignored=False):
+    def bwd(Q, K, V, dO, scale, causal, bias=None):
         Q, K, V, dO = (np.asarray(x, float) for x in (Q, K, V, dO))
-        S = scores(Q, K, scale, causal)
+        S = scores(Q, K, scale, causal, None if bias_ignored else bias)
         P, _ = A.softmax_with_lse(S)
         dV = (P @ dO) if dv_no_transpose and P.shape[0] == P.shape[1] else P.T @ dO
         dP = dO @ V.T
@@ -406,6 +523,11 @@ def _mutants():
     yield "scale dropped from dQ", f_ok, _mut_bwd(s_ok, dq_no_scale=True)
     yield "dK = dS Q (not dS^T Q)", f_ok, _mut_bwd(s_ok, dk_wrong_operand=True)
     yield "D summed over the wrong axis", f_ok, _mut_bwd(s_ok, d_from_wrong_axis=True)
+    f, s = _mut_fwd(bias_scaled=True)
+    yield "bias multiplied by the scale", f, _mut_bwd(s)
+    f, s = _mut_fwd(bias_transposed=True)
+    yield "bias transposed", f, _mut_bwd(s)
+    yield "bias left out of the backward", f_ok, _mut_bwd(s_ok, bias_ignored=True)
 
 
 def test_unmutated_copy_passes_every_pin():
