@@ -184,18 +184,23 @@ def bench_decode(fa, torch, steps):
             "algorithmic_bytes": all_bytes}
 
 
-def bench_fp16(fa, torch, w, x, ws, steps):
-    """The same forward and backward on fp16 copies of the inputs."""
-    Q, K, V, dO = (x[k].to(torch.float16) for k in ("Q", "K", "V", "dO"))
+def _time_fwd_bwd(fa, torch, w, Q, K, V, dO, ws, steps, bias=None):
+    """Mean forward and backward milliseconds of fa_fwd(_bias) + fa_bwd(_bias)."""
     O = torch.empty_like(Q)
     L = torch.empty(w.B, w.H, w.Nq, dtype=torch.float32, device="cuda")
     dQ, dK, dV = torch.empty_like(Q), torch.empty_like(K), torch.empty_like(V)
 
     def run(ev=None):
-        fa.fa_fwd(Q, K, V, O, L, w.scale, w.causal)
+        if bias is None:
+            fa.fa_fwd(Q, K, V, O, L, w.scale, w.causal)
+        else:
+            fa.fa_fwd_bias(Q, K, V, bias, O, L, w.scale, w.causal)
         if ev is not None:
             ev.record()
-        fa.fa_bwd(Q, K, V, O, L, dO, dQ, dK, dV, w.scale, w.causal, workspace=ws)
+        if bias is None:
+            fa.fa_bwd(Q, K, V, O, L, dO, dQ, dK, dV, w.scale, w.causal, workspace=ws)
+        else:
+            fa.fa_bwd_bias(Q, K, V, bias, O, L, dO, dQ, dK, dV, w.scale, w.causal, workspace=ws)
 
     run()
     torch.cuda.synchronize()
@@ -213,6 +218,24 @@ def bench_fp16(fa, torch, w, x, ws, steps):
             "bwd_TFLOP/s": 10 * w.d * pairs / (bwd_ms * 1e-3) / 1e12}
 
 
+def bench_fp16(fa, torch, w, x, ws, steps):
+    """The same forward and backward on fp16 copies of the inputs."""
+    Q, K, V, dO = (x[k].to(torch.float16) for k in ("Q", "K", "V", "dO"))
+    return _time_fwd_bwd(fa, torch, w, Q, K, V, dO, ws, steps)
+
+
+def bench_bias(fa, torch, w, x, ws, steps):
+    """The same forward and backward with an additive bias [1, H, N, N] in the
+    input dtype (one score matrix per head, shared over the batch)."""
+    from exact_attention_118_amd import synth
+
+    bias = synth.make_bias(w.B, w.H, w.Nq, w.Nk, w.dtype, seed=11, device="cuda", per_batch=False)
+    r = _time_fwd_bwd(fa, torch, w, x["Q"], x["K"], x["V"], x["dO"], ws, steps, bias=bias)
+    r["bias_shape"] = list(bias.shape)
+    r["bias_GB"] = bias.numel() * bias.element_size() / 1e9
+    return r
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__)
     ap.add_argument("--gpus", type=int, default=1)
@@ -223,6 +246,8 @@ def main():
                     help="heads of the workload the float64 oracle is timed on (0 = skip)")
     ap.add_argument("--no-decode", action="store_true", help="skip the decode-shaped forward")
     ap.add_argument("--no-fp16", action="store_true", help="skip the fp16 forward and backward")
+    ap.add_argument("--no-bias", action="store_true",
+                    help="skip the forward and backward with an additive bias")
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
                     help="after the timed steps, run one plain device-to-device copy of this many "
                          "MiB (reference point for HBM byte counters under rocprofv3 --pmc)")
@@ -351,6 +376,9 @@ def main():
     if not args.no_fp16:
         log("fp16 inputs, same workload")
         out["fp16"] = bench_fp16(fa, torch, w, x, ws, steps=max(3, args.steps // 2))
+    if not args.no_bias:
+        log("additive bias [1, H, N, N], same workload")
+        out["bias"] = bench_bias(fa, torch, w, x, ws, steps=max(3, args.steps // 2))
     del ws
     if args.copy_calibration_mib > 0:
         n = args.copy_calibration_mib << 20

@@ -13,7 +13,8 @@ import math
 import os
 
 __all__ = [
-    "FAError", "load_library", "lib_path", "fa_fwd", "fa_bwd", "forward", "backward",
+    "FAError", "load_library", "lib_path", "fa_fwd", "fa_bwd", "fa_fwd_bias", "fa_bwd_bias",
+    "forward", "backward",
     "fwd_workspace_size", "bwd_workspace_size", "fwd_num_splits", "status_string", "version",
     "FA_OK", "FA_ERR_NULL", "FA_ERR_SHAPE", "FA_ERR_UNSUPPORTED", "FA_ERR_ALIGN",
     "FA_ERR_WORKSPACE", "FA_ERR_HIP", "FA_BF16", "FA_FP32", "FA_FP16", "EXPORTED_SYMBOLS",
@@ -25,8 +26,9 @@ FA_BF16, FA_FP32, FA_FP16 = 0, 1, 2
 
 FA_BWD_PREPROCESS, FA_BWD_DKDV, FA_BWD_DQ, FA_BWD_ALL = 1, 2, 4, 7
 
-EXPORTED_SYMBOLS = ("fa_fwd", "fa_bwd", "fa_bwd_stages", "fa_fwd_workspace_size",
-                    "fa_bwd_workspace_size", "fa_fwd_num_splits", "fa_status_string", "fa_version")
+EXPORTED_SYMBOLS = ("fa_fwd", "fa_bwd", "fa_bwd_stages", "fa_fwd_bias", "fa_bwd_bias",
+                    "fa_fwd_workspace_size", "fa_bwd_workspace_size", "fa_fwd_num_splits",
+                    "fa_status_string", "fa_version")
 
 _LIB = None
 
@@ -57,6 +59,12 @@ def load_library():
     lib.fa_bwd.restype = i
     lib.fa_bwd_stages.argtypes = lib.fa_bwd.argtypes + [i]
     lib.fa_bwd_stages.restype = i
+    ll = ctypes.c_longlong
+    lib.fa_fwd_bias.argtypes = [vp, vp, vp, vp, ll, ll, ll, vp, vp, i, i, i, i, i, f, i, i, vp]
+    lib.fa_fwd_bias.restype = i
+    lib.fa_bwd_bias.argtypes = [vp, vp, vp, vp, ll, ll, ll, vp, vp, vp, vp, vp, vp, i, i, i, i, i,
+                                f, i, i, vp, sz, vp]
+    lib.fa_bwd_bias.restype = i
     lib.fa_fwd_workspace_size.argtypes = [i, i, i, i, i, i, i]
     lib.fa_fwd_workspace_size.restype = sz
     lib.fa_bwd_workspace_size.argtypes = [i, i, i, i, i, i]
@@ -194,7 +202,71 @@ def fa_bwd(Q, K, V, O, L, dO, dQ, dK, dV, scale, causal, workspace=None, stream=
     return dQ, dK, dV
 
 
-def forward(Q, K, V, scale=None, causal=False, num_splits=0, stream=None):
+def _bias_strides(bias, B, H, Nq, Nk, dtype, device):
+    """Element strides (sb, sh, sq) of a bias viewable as [B or 1, H or 1, Nq, Nk]
+    whose last dim is contiguous; broadcast dims (size 1) get stride 0."""
+    if not bias.is_cuda or bias.device != device:
+        raise ValueError(f"bias must be a GPU tensor on {device}")
+    if bias.dtype != dtype:
+        raise ValueError(f"bias has dtype {bias.dtype}, expected {dtype}")
+    if bias.dim() != 4 or tuple(bias.shape[2:]) != (Nq, Nk) or bias.shape[0] not in (1, B) \
+            or bias.shape[1] not in (1, H):
+        raise ValueError(f"bias has shape {tuple(bias.shape)}, expected [B or 1, H or 1, {Nq}, {Nk}]")
+    if bias.stride(3) != 1:
+        raise ValueError("bias must be contiguous along keys")
+    sb = 0 if bias.shape[0] == 1 else bias.stride(0)
+    sh = 0 if bias.shape[1] == 1 else bias.stride(1)
+    return sb, sh, bias.stride(2)
+
+
+def fa_fwd_bias(Q, K, V, bias, O, L, scale, causal, stream=None):
+    """Call ``fa_fwd_bias``: attention with an additive bias [B or 1, H or 1, Nq, Nk]."""
+    lib = load_library()
+    B, H, Nq, d = Q.shape
+    Nk = K.shape[2]
+    dev = Q.device
+    _check_tensor("Q", Q, (B, H, Nq, d), Q.dtype, dev)
+    _check_tensor("K", K, (B, H, Nk, d), Q.dtype, dev)
+    _check_tensor("V", V, (B, H, Nk, d), Q.dtype, dev)
+    _check_tensor("O", O, (B, H, Nq, d), Q.dtype, dev)
+    _check_tensor("L", L, (B, H, Nq), _torch().float32, dev)
+    sb, sh, sq = _bias_strides(bias, B, H, Nq, Nk, Q.dtype, dev)
+    st = lib.fa_fwd_bias(_ptr(Q), _ptr(K), _ptr(V), _ptr(bias), sb, sh, sq, _ptr(O), _ptr(L), B, H,
+                         Nq, Nk, d, float(scale), int(bool(causal)), _dtype_code(Q),
+                         _stream_handle(dev, stream))
+    if st != FA_OK:
+        raise FAError(st, "fa_fwd_bias")
+    return O, L
+
+
+def fa_bwd_bias(Q, K, V, bias, O, L, dO, dQ, dK, dV, scale, causal, workspace=None, stream=None):
+    """Call ``fa_bwd_bias`` (dQ, dK, dV overwritten; no gradient for the bias)."""
+    lib = load_library()
+    B, H, Nq, d = Q.shape
+    Nk = K.shape[2]
+    dev = Q.device
+    for name, t, shp in (("Q", Q, (B, H, Nq, d)), ("K", K, (B, H, Nk, d)), ("V", V, (B, H, Nk, d)),
+                         ("O", O, (B, H, Nq, d)), ("dO", dO, (B, H, Nq, d)),
+                         ("dQ", dQ, (B, H, Nq, d)), ("dK", dK, (B, H, Nk, d)),
+                         ("dV", dV, (B, H, Nk, d))):
+        _check_tensor(name, t, shp, Q.dtype, dev)
+    _check_tensor("L", L, (B, H, Nq), _torch().float32, dev)
+    sb, sh, sq = _bias_strides(bias, B, H, Nq, Nk, Q.dtype, dev)
+    code = _dtype_code(Q)
+    need = lib.fa_bwd_workspace_size(B, H, Nq, Nk, d, code)
+    if workspace is None:
+        workspace = _alloc_workspace(need, dev)
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    st = lib.fa_bwd_bias(_ptr(Q), _ptr(K), _ptr(V), _ptr(bias), sb, sh, sq, _ptr(O), _ptr(L),
+                         _ptr(dO), _ptr(dQ), _ptr(dK), _ptr(dV), B, H, Nq, Nk, d, float(scale),
+                         int(bool(causal)), code, _ptr(workspace), ws_bytes,
+                         _stream_handle(dev, stream))
+    if st != FA_OK:
+        raise FAError(st, "fa_bwd_bias")
+    return dQ, dK, dV
+
+
+def forward(Q, K, V, scale=None, causal=False, num_splits=0, stream=None, bias=None):
     """Allocate O, L and run ``fa_fwd``.  Returns (O, L)."""
     torch = _torch()
     B, H, Nq, d = Q.shape
@@ -202,10 +274,12 @@ def forward(Q, K, V, scale=None, causal=False, num_splits=0, stream=None):
         scale = 1.0 / math.sqrt(d)
     O = torch.empty_like(Q)
     L = torch.empty((B, H, Nq), dtype=torch.float32, device=Q.device)
+    if bias is not None:
+        return fa_fwd_bias(Q, K, V, bias, O, L, scale, causal, stream=stream)
     return fa_fwd(Q, K, V, O, L, scale, causal, num_splits=num_splits, stream=stream)
 
 
-def backward(Q, K, V, O, L, dO, scale=None, causal=False, stream=None):
+def backward(Q, K, V, O, L, dO, scale=None, causal=False, stream=None, bias=None):
     """Allocate dQ, dK, dV and run ``fa_bwd``.  Returns (dQ, dK, dV)."""
     torch = _torch()
     d = Q.shape[-1]
@@ -214,4 +288,6 @@ def backward(Q, K, V, O, L, dO, scale=None, causal=False, stream=None):
     dQ = torch.empty_like(Q)
     dK = torch.empty_like(K)
     dV = torch.empty_like(V)
+    if bias is not None:
+        return fa_bwd_bias(Q, K, V, bias, O, L, dO, dQ, dK, dV, scale, causal, stream=stream)
     return fa_bwd(Q, K, V, O, L, dO, dQ, dK, dV, scale, causal, stream=stream)

@@ -125,18 +125,35 @@ size_t fa_bwd_workspace_size(int B, int H, int Nq, int Nk, int d, fa_dtype dtype
   return bwd_ws_bytes(B * H, Nq);
 }
 
-fa_status fa_fwd(const void* Q, const void* K, const void* V, void* O, float* L, int B, int H,
-                 int Nq, int Nk, int d, float scale, int causal, fa_dtype dtype, int num_splits,
-                 void* workspace, size_t workspace_bytes, void* stream) {
+}  // extern "C"
+
+namespace {
+
+// Additive-bias checks (see fa_fwd_bias): rows of at least Nk elements, 16-byte
+// aligned rows and head blocks, element offsets within a head below 2^30.
+fa_status check_bias(const void* bias, long long sb, long long sh, long long sq, int Nq, int Nk) {
+  if (!bias) return FA_ERR_NULL;
+  if (!aligned(bias)) return FA_ERR_ALIGN;
+  if (sb < 0 || sh < 0 || sq < Nk || sq < 1) return FA_ERR_SHAPE;
+  if (sq % 8 != 0 || sb % 8 != 0 || sh % 8 != 0) return FA_ERR_ALIGN;
+  if (Nq > 0 && (long long)(Nq - 1) * sq + Nk > (1LL << 30)) return FA_ERR_SHAPE;
+  return FA_OK;
+}
+
+fa_status fwd_impl(const void* Q, const void* K, const void* V, const fa::BiasArgs& bias, void* O,
+                   float* L, int B, int H, int Nq, int Nk, int d, float scale, int causal,
+                   fa_dtype dtype, int num_splits, void* workspace, size_t workspace_bytes,
+                   void* stream) {
   fa_status st = check_dims(B, H, Nq, Nk, d, scale, causal, dtype);
   if (st != FA_OK) return st;
   if (num_splits < 0) return FA_ERR_UNSUPPORTED;
   if ((long long)B * H * Nq == 0) return FA_OK;
   if (!Q || !K || !V || !O || !L) return FA_ERR_NULL;
   if (!aligned(Q) || !aligned(K) || !aligned(V) || !aligned(O) || !aligned(L)) return FA_ERR_ALIGN;
-  const int splits = choose_splits(B, H, Nq, Nk, dtype, num_splits);
+  const int splits = bias.ptr ? 0 : choose_splits(B, H, Nq, Nk, dtype, num_splits);
   if (splits < 0) return FA_ERR_UNSUPPORTED;
   fa::FwdArgs a{Q, K, V, O, L, B, H, Nq, Nk, d, scale, causal != 0};
+  a.bias = bias;
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
   hipError_t e;
   if (splits > 0) {
@@ -158,18 +175,10 @@ fa_status fa_fwd(const void* Q, const void* K, const void* V, void* O, float* L,
   return e == hipSuccess ? FA_OK : FA_ERR_HIP;
 }
 
-fa_status fa_bwd(const void* Q, const void* K, const void* V, const void* O, const float* L,
-                 const void* dO, void* dQ, void* dK, void* dV, int B, int H, int Nq, int Nk, int d,
-                 float scale, int causal, fa_dtype dtype, void* workspace, size_t workspace_bytes,
-                 void* stream) {
-  return fa_bwd_stages(Q, K, V, O, L, dO, dQ, dK, dV, B, H, Nq, Nk, d, scale, causal, dtype,
-                       workspace, workspace_bytes, stream, FA_BWD_ALL);
-}
-
-fa_status fa_bwd_stages(const void* Q, const void* K, const void* V, const void* O,
-                        const float* L, const void* dO, void* dQ, void* dK, void* dV, int B,
-                        int H, int Nq, int Nk, int d, float scale, int causal, fa_dtype dtype,
-                        void* workspace, size_t workspace_bytes, void* stream, int stages) {
+fa_status bwd_impl(const void* Q, const void* K, const void* V, const fa::BiasArgs& bias,
+                   const void* O, const float* L, const void* dO, void* dQ, void* dK, void* dV,
+                   int B, int H, int Nq, int Nk, int d, float scale, int causal, fa_dtype dtype,
+                   void* workspace, size_t workspace_bytes, void* stream, int stages) {
   if (stages <= 0 || stages > FA_BWD_ALL) return FA_ERR_UNSUPPORTED;
   fa_status st = check_dims(B, H, Nq, Nk, d, scale, causal, dtype);
   if (st != FA_OK) return st;
@@ -183,6 +192,7 @@ fa_status fa_bwd_stages(const void* Q, const void* K, const void* V, const void*
   if (Nq > 0 && !aligned(workspace)) return FA_ERR_ALIGN;
   fa::BwdArgs a{Q, K, V, O, L, dO, dQ, dK, dV, B, H, Nq, Nk, d, scale, causal != 0,
                 nullptr};
+  a.bias = bias;
   if (Nq > 0) a.LD = static_cast<float*>(workspace);
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
   const hipError_t e =
@@ -190,6 +200,72 @@ fa_status fa_bwd_stages(const void* Q, const void* K, const void* V, const void*
       : (dtype == FA_FP16) ? fa::launch_bwd_f16(a, stages, s)
                            : fa::launch_bwd_f32(a, stages, s);
   return e == hipSuccess ? FA_OK : FA_ERR_HIP;
+}
+
+}  // namespace
+
+extern "C" {
+
+fa_status fa_fwd(const void* Q, const void* K, const void* V, void* O, float* L, int B, int H,
+                 int Nq, int Nk, int d, float scale, int causal, fa_dtype dtype, int num_splits,
+                 void* workspace, size_t workspace_bytes, void* stream) {
+  return fwd_impl(Q, K, V, fa::BiasArgs{}, O, L, B, H, Nq, Nk, d, scale, causal, dtype, num_splits,
+                  workspace, workspace_bytes, stream);
+}
+
+fa_status fa_fwd_bias(const void* Q, const void* K, const void* V, const void* bias,
+                      long long bias_sb, long long bias_sh, long long bias_sq, void* O, float* L,
+                      int B, int H, int Nq, int Nk, int d, float scale, int causal, fa_dtype dtype,
+                      void* stream) {
+  fa_status st = check_dims(B, H, Nq, Nk, d, scale, causal, dtype);
+  if (st != FA_OK) return st;
+  if ((long long)B * H * Nq == 0) return FA_OK;
+  st = check_bias(bias, bias_sb, bias_sh, bias_sq, Nq, Nk);
+  if (st != FA_OK) return st;
+  fa::BiasArgs b;
+  b.ptr = bias;
+  b.sb = bias_sb;
+  b.sh = bias_sh;
+  b.sq = bias_sq;
+  return fwd_impl(Q, K, V, b, O, L, B, H, Nq, Nk, d, scale, causal, dtype, 1, nullptr, 0, stream);
+}
+
+fa_status fa_bwd_bias(const void* Q, const void* K, const void* V, const void* bias,
+                      long long bias_sb, long long bias_sh, long long bias_sq, const void* O,
+                      const float* L, const void* dO, void* dQ, void* dK, void* dV, int B, int H,
+                      int Nq, int Nk, int d, float scale, int causal, fa_dtype dtype,
+                      void* workspace, size_t workspace_bytes, void* stream) {
+  fa_status st = check_dims(B, H, Nq, Nk, d, scale, causal, dtype);
+  if (st != FA_OK) return st;
+  if ((long long)B * H == 0 || Nq == 0) {
+    return bwd_impl(Q, K, V, fa::BiasArgs{}, O, L, dO, dQ, dK, dV, B, H, Nq, Nk, d, scale, causal,
+                    dtype, workspace, workspace_bytes, stream, FA_BWD_ALL);
+  }
+  st = check_bias(bias, bias_sb, bias_sh, bias_sq, Nq, Nk);
+  if (st != FA_OK) return st;
+  fa::BiasArgs b;
+  b.ptr = bias;
+  b.sb = bias_sb;
+  b.sh = bias_sh;
+  b.sq = bias_sq;
+  return bwd_impl(Q, K, V, b, O, L, dO, dQ, dK, dV, B, H, Nq, Nk, d, scale, causal, dtype,
+                  workspace, workspace_bytes, stream, FA_BWD_ALL);
+}
+
+fa_status fa_bwd(const void* Q, const void* K, const void* V, const void* O, const float* L,
+                 const void* dO, void* dQ, void* dK, void* dV, int B, int H, int Nq, int Nk, int d,
+                 float scale, int causal, fa_dtype dtype, void* workspace, size_t workspace_bytes,
+                 void* stream) {
+  return fa_bwd_stages(Q, K, V, O, L, dO, dQ, dK, dV, B, H, Nq, Nk, d, scale, causal, dtype,
+                       workspace, workspace_bytes, stream, FA_BWD_ALL);
+}
+
+fa_status fa_bwd_stages(const void* Q, const void* K, const void* V, const void* O,
+                        const float* L, const void* dO, void* dQ, void* dK, void* dV, int B,
+                        int H, int Nq, int Nk, int d, float scale, int causal, fa_dtype dtype,
+                        void* workspace, size_t workspace_bytes, void* stream, int stages) {
+  return bwd_impl(Q, K, V, fa::BiasArgs{}, O, L, dO, dQ, dK, dV, B, H, Nq, Nk, d, scale, causal,
+                  dtype, workspace, workspace_bytes, stream, stages);
 }
 
 }  // extern "C"

@@ -90,12 +90,12 @@ constexpr int kKvBR = 32;   // query rows per inner iteration
 constexpr int kKvWaves = 8;
 constexpr int kKvThreads = kKvWaves * 64;
 
-template <typename T, int D, bool CAUSAL>
+template <typename T, int D, bool CAUSAL, bool BIAS>
 __global__ __launch_bounds__(kKvThreads, 1) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void bwd_dkdv_kernel(const T* __restrict__ Q, const T* __restrict__ K, const T* __restrict__ V,
                      const T* __restrict__ dO, const float* __restrict__ LD, T* __restrict__ dK,
                      T* __restrict__ dV, int Nq, int Nk, int nkt, int BH, int hpx, float c,
-                     float scale, int off) {
+                     float scale, int off, BiasDev bias) {
   typedef typename Vec<T>::x8 T8;
   typedef typename Vec<T>::x4 T4;
   constexpr int BC = kKvBC, BR = kKvBR;
@@ -141,6 +141,16 @@ void bwd_dkdv_kernel(const T* __restrict__ Q, const T* __restrict__ K, const T* 
   const size_t qbase = (size_t)bh * Nq * D;
   const size_t kbase = (size_t)bh * Nk * D;
   const size_t lbase = (size_t)bh * Nq;
+
+  // Additive bias (BIAS) of this head; this lane reads column mykey.
+  const T* bias_h = nullptr;
+  long long bias_n = 0;
+  if constexpr (BIAS) {
+    const int b = bh / bias.H, h = bh - b * bias.H;
+    bias_h = (const T*)bias.ptr + b * bias.sb + h * bias.sh;
+    bias_n = (long long)(Nq - 1) * bias.sq + Nk;
+  }
+  const BiasReader<T> br(bias_h, bias_n);
 
   // Query blocks that can see any key of this workgroup.
   const int nqb = (Nq + BR - 1) / BR;
@@ -237,6 +247,14 @@ void bwd_dkdv_kernel(const T* __restrict__ Q, const T* __restrict__ K, const T* 
       // needs the Q, K and dO fragments of head-dim chunk kk; those of step
       // kk + 1 are read before step kk's MFMAs are issued.
       f32x16 sacc = (f32x16){}, dpacc = (f32x16){};
+      // Bias of rows qi0 + (i/4)*8 + half*4 + i%4, key mykey (rows past Nq
+      // read zeros, keys past Nk are masked below), loaded before the MFMAs.
+      float bias_v[BIAS ? 16 : 1];
+      if constexpr (BIAS) {
+#pragma unroll
+        for (int i = 0; i < 16; ++i)
+          bias_v[i] = br.load1((unsigned)((qi0 + (i >> 2) * 8 + half * 4 + (i & 3)) * bias.sq + mykey));
+      }
       {
         auto ldstep = [&](int kk, T8* f) {
           f[0] = *at_byte<T8>(tQ, qa[kk]);
@@ -254,6 +272,10 @@ void bwd_dkdv_kernel(const T* __restrict__ Q, const T* __restrict__ K, const T* 
           dpacc = mfma32(cur[2], vf[kk], dpacc);
           __builtin_amdgcn_sched_barrier(0);
         }
+      }
+      if constexpr (BIAS) {
+#pragma unroll
+        for (int i = 0; i < 16; ++i) sacc[i] = fmaf(bias_v[i], bias.inv_scale, sacc[i]);
       }
       // Lane holds key mykey and rows (i/4)*8 + half*4 + i%4 of the block.
       // Rows past the end and, causal, rows before the key's diagonal get
@@ -373,11 +395,11 @@ constexpr int kDqBR = 128;  // query rows per workgroup
 constexpr int kDqBC = 64;   // keys per K/V tile
 constexpr int kDqThreads = 256;
 
-template <typename T, int D, bool CAUSAL>
+template <typename T, int D, bool CAUSAL, bool BIAS>
 __global__ __launch_bounds__(kDqThreads, 2) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void bwd_dq_kernel(const T* __restrict__ Q, const T* __restrict__ K, const T* __restrict__ V,
                    const T* __restrict__ dO, const float* __restrict__ LD, T* __restrict__ dQ,
-                   int Nq, int Nk, int nqt, float c, float scale, int off) {
+                   int Nq, int Nk, int nqt, float c, float scale, int off, BiasDev bias) {
   typedef typename Vec<T>::x8 T8;
   typedef typename Vec<T>::x4 T4;
   constexpr int BR = kDqBR, BC = kDqBC;
@@ -407,6 +429,17 @@ void bwd_dq_kernel(const T* __restrict__ Q, const T* __restrict__ K, const T* __
   const size_t qbase = (size_t)bh * Nq * D;
   const T* Kh = K + (size_t)bh * Nk * D;
   const T* Vh = V + (size_t)bh * Nk * D;
+
+  // Additive bias (BIAS) of this head: lane row qrow, keys along elements.
+  const T* bias_h = nullptr;
+  long long bias_n = 0;
+  if constexpr (BIAS) {
+    const int b = bh / bias.H, h = bh - b * bias.H;
+    bias_h = (const T*)bias.ptr + b * bias.sb + h * bias.sh;
+    bias_n = (long long)(Nq - 1) * bias.sq + Nk;
+  }
+  const BiasReader<T> br(bias_h, bias_n);
+  typedef typename Vec<T>::x4 BT4;
 
   using KV = BufTile<D, BC, kDqThreads>;
   const KV kv(wave, lane);
@@ -481,6 +514,24 @@ void bwd_dq_kernel(const T* __restrict__ Q, const T* __restrict__ K, const T* __
       // keys k0 + mt*32 + (i/4)*8 + half*4 + i%4.
       f32x16 sacc[2], dpacc[2];
       T8 dsf[4];
+      // Bias of this tile (BIAS): half mt, elements g*4 .. g*4+3 are keys
+      // k0 + mt*32 + g*8 + half*4 + 0..3; loaded first, added after each
+      // half's scores (rows past Nq read zeros, keys past Nk are masked).
+      BT4 bb[BIAS ? 8 : 1];
+      if constexpr (BIAS) {
+#pragma unroll
+        for (int q = 0; q < 8; ++q)
+          bb[q] = br.load4((unsigned)(qrow * bias.sq + k0 + (q >> 2) * 32 + (q & 3) * 8 + half * 4));
+      }
+      auto bias_half = [&](int mt) {
+        if constexpr (BIAS) {
+#pragma unroll
+          for (int g = 0; g < 4; ++g)
+#pragma unroll
+            for (int e = 0; e < 4; ++e)
+              sacc[mt][g * 4 + e] = fmaf((float)bb[mt * 4 + g][e], bias.inv_scale, sacc[mt][g * 4 + e]);
+        }
+      };
       auto ds_elem = [&](int mt, int i) {
         const float p = fast_exp2(fmaf(sacc[mt][i], c, -l2));
         dsf[mt * 2 + (i >> 3)][i & 7] = (T)(p * (dpacc[mt][i] - drow));
@@ -549,8 +600,10 @@ void bwd_dq_kernel(const T* __restrict__ Q, const T* __restrict__ K, const T* __
         }
       };
       sdp_half(0, false);
+      bias_half(0);
       mask_half(0);
       sdp_half(1, true);   // dS of half 0 overlaps the MFMAs of half 1
+      bias_half(1);
       mask_half(1);
       dq_half(0, true);    // dS of half 1 overlaps dQ of half 0
       dq_half(1, false);
@@ -589,12 +642,17 @@ __global__ __launch_bounds__(kF32BT) void bwd_dkdv_f32_kernel(
     const float* __restrict__ Q, const float* __restrict__ K, const float* __restrict__ V,
     const float* __restrict__ L, const float* __restrict__ dO, const float* __restrict__ LD,
     float* __restrict__ dK, float* __restrict__ dV, int Nq, int Nk, int nkt, float scale,
-    int off) {
+    int off, BiasDev bias) {
   __shared__ float sq[D], sdo[D];
   const int bh = blockIdx.x / nkt;
   const int kt = blockIdx.x - bh * nkt;
   const int key = kt * kF32BT + threadIdx.x;
   const size_t qbase = (size_t)bh * Nq * D, kbase = (size_t)bh * Nk * D;
+  const float* bias_h = nullptr;  // this head's additive bias, if any
+  if (bias.ptr) {
+    const int b = bh / bias.H, h = bh - b * bias.H;
+    bias_h = (const float*)bias.ptr + b * bias.sb + h * bias.sh;
+  }
   float k[D], v[D], dk[D], dv[D];
 #pragma unroll
   for (int e = 0; e < D; ++e) {
@@ -619,7 +677,8 @@ __global__ __launch_bounds__(kF32BT) void bwd_dkdv_f32_kernel(
       s = fmaf(sq[e], k[e], s);
       dp = fmaf(sdo[e], v[e], dp);
     }
-    const float p = expf(s * scale - L[(size_t)bh * Nq + q]);
+    const float b = bias_h ? bias_h[(long long)q * bias.sq + key] : 0.f;
+    const float p = expf(s * scale + b - L[(size_t)bh * Nq + q]);
     const float ds = p * (dp - LD[2 * ((size_t)bh * Nq + q) + 1]);
 #pragma unroll
     for (int e = 0; e < D; ++e) {
@@ -640,12 +699,17 @@ template <int D, bool CAUSAL>
 __global__ __launch_bounds__(kF32BT) void bwd_dq_f32_kernel(
     const float* __restrict__ Q, const float* __restrict__ K, const float* __restrict__ V,
     const float* __restrict__ L, const float* __restrict__ dO, const float* __restrict__ LD,
-    float* __restrict__ dQ, int Nq, int Nk, int nqt, float scale, int off) {
+    float* __restrict__ dQ, int Nq, int Nk, int nqt, float scale, int off, BiasDev bias) {
   __shared__ float sk[D], sv[D];
   const int bh = blockIdx.x / nqt;
   const int qt = blockIdx.x - bh * nqt;
   const int q = qt * kF32BT + threadIdx.x;
   const size_t qbase = (size_t)bh * Nq * D, kbase = (size_t)bh * Nk * D;
+  const float* brow = nullptr;  // this row's additive bias, if any
+  if (bias.ptr && q < Nq) {
+    const int b = bh / bias.H, h = bh - b * bias.H;
+    brow = (const float*)bias.ptr + b * bias.sb + h * bias.sh + (long long)q * bias.sq;
+  }
   float qv[D], dov[D], dq[D];
 #pragma unroll
   for (int e = 0; e < D; ++e) {
@@ -672,7 +736,7 @@ __global__ __launch_bounds__(kF32BT) void bwd_dq_f32_kernel(
       s = fmaf(qv[e], sk[e], s);
       dp = fmaf(dov[e], sv[e], dp);
     }
-    const float p = expf(s * scale - lq);
+    const float p = expf(s * scale + (brow ? brow[key] : 0.f) - lq);
     const float ds = p * (dp - dq_aux);
 #pragma unroll
     for (int e = 0; e < D; ++e) dq[e] = fmaf(ds, sk[e], dq[e]);
@@ -698,7 +762,7 @@ hipError_t launch_pre(const BwdArgs& a, hipStream_t s) {
 
 namespace {
 
-template <typename T>
+template <typename T, bool BIAS>
 hipError_t launch_bwd_mfma(const BwdArgs& a, int stages, hipStream_t s) {
   const int BH = a.B * a.H;
   const float c = a.scale * kLog2e;
@@ -707,6 +771,7 @@ hipError_t launch_bwd_mfma(const BwdArgs& a, int stages, hipStream_t s) {
   const T* K = (const T*)a.K;
   const T* V = (const T*)a.V;
   const T* dO = (const T*)a.dO;
+  const BiasDev bias{a.bias.ptr, a.bias.sb, a.bias.sh, a.bias.sq, a.H, 1.f / a.scale};
   if (stages & 1) {
     const hipError_t e = (a.d == 128) ? launch_pre<128, T>(a, s) : launch_pre<64, T>(a, s);
     if (e != hipSuccess) return e;
@@ -716,8 +781,9 @@ hipError_t launch_bwd_mfma(const BwdArgs& a, int stages, hipStream_t s) {
     const int nblocks = nkt * BH;
     const int hpx = (BH % kNumXcd == 0) ? BH / kNumXcd : 0;
 #define FA_DKDV_LAUNCH(DD, CC)                                                                  \
-  hipLaunchKernelGGL((bwd_dkdv_kernel<T, DD, CC>), dim3(nblocks), dim3(kKvThreads), 0, s, Q, K, \
-                     V, dO, a.LD, (T*)a.dK, (T*)a.dV, a.Nq, a.Nk, nkt, BH, hpx, c, a.scale, off)
+  hipLaunchKernelGGL((bwd_dkdv_kernel<T, DD, CC, BIAS>), dim3(nblocks), dim3(kKvThreads), 0, s, \
+                     Q, K, V, dO, a.LD, (T*)a.dK, (T*)a.dV, a.Nq, a.Nk, nkt, BH, hpx, c, a.scale, \
+                     off, bias)
     if (a.d == 128) {
       if (a.causal) FA_DKDV_LAUNCH(128, true); else FA_DKDV_LAUNCH(128, false);
     } else {
@@ -731,8 +797,8 @@ hipError_t launch_bwd_mfma(const BwdArgs& a, int stages, hipStream_t s) {
     const int nqt = (a.Nq + kDqBR - 1) / kDqBR;
     const int nblocks = (a.causal ? (nqt + 1) / 2 : nqt) * BH;  // causal: query tile pairs
 #define FA_DQ_LAUNCH(DD, CC)                                                                    \
-  hipLaunchKernelGGL((bwd_dq_kernel<T, DD, CC>), dim3(nblocks), dim3(kDqThreads), 0, s, Q, K,  \
-                     V, dO, a.LD, (T*)a.dQ, a.Nq, a.Nk, nqt, c, a.scale, off)
+  hipLaunchKernelGGL((bwd_dq_kernel<T, DD, CC, BIAS>), dim3(nblocks), dim3(kDqThreads), 0, s, Q, \
+                     K, V, dO, a.LD, (T*)a.dQ, a.Nq, a.Nk, nqt, c, a.scale, off, bias)
     if (a.d == 128) {
       if (a.causal) FA_DQ_LAUNCH(128, true); else FA_DQ_LAUNCH(128, false);
     } else {
@@ -747,10 +813,12 @@ hipError_t launch_bwd_mfma(const BwdArgs& a, int stages, hipStream_t s) {
 }  // namespace
 
 hipError_t launch_bwd_bf16(const BwdArgs& a, int stages, hipStream_t s) {
-  return launch_bwd_mfma<bf16>(a, stages, s);
+  return a.bias.ptr ? launch_bwd_mfma<bf16, true>(a, stages, s)
+                    : launch_bwd_mfma<bf16, false>(a, stages, s);
 }
 hipError_t launch_bwd_f16(const BwdArgs& a, int stages, hipStream_t s) {
-  return launch_bwd_mfma<f16>(a, stages, s);
+  return a.bias.ptr ? launch_bwd_mfma<f16, true>(a, stages, s)
+                    : launch_bwd_mfma<f16, false>(a, stages, s);
 }
 
 hipError_t launch_bwd_f32(const BwdArgs& a, int stages, hipStream_t s) {
@@ -766,10 +834,12 @@ hipError_t launch_bwd_f32(const BwdArgs& a, int stages, hipStream_t s) {
   const float* K = (const float*)a.K;
   const float* V = (const float*)a.V;
   const float* dO = (const float*)a.dO;
+  const BiasDev bias{a.bias.ptr, a.bias.sb, a.bias.sh, a.bias.sq, a.H, 1.f / a.scale};
   if ((stages & 2) && nkt > 0) {
 #define FA_DKDV32_LAUNCH(DD, CC)                                                                \
   hipLaunchKernelGGL((bwd_dkdv_f32_kernel<DD, CC>), dim3(nkt * BH), dim3(kF32BT), 0, s, Q, K, V, \
-                     a.L, dO, a.LD, (float*)a.dK, (float*)a.dV, a.Nq, a.Nk, nkt, a.scale, off)
+                     a.L, dO, a.LD, (float*)a.dK, (float*)a.dV, a.Nq, a.Nk, nkt, a.scale, off,  \
+                     bias)
     if (a.d == 128) {
       if (a.causal) FA_DKDV32_LAUNCH(128, true); else FA_DKDV32_LAUNCH(128, false);
     } else {
@@ -782,7 +852,7 @@ hipError_t launch_bwd_f32(const BwdArgs& a, int stages, hipStream_t s) {
   if ((stages & 4) && nqt > 0) {
 #define FA_DQ32_LAUNCH(DD, CC)                                                                \
   hipLaunchKernelGGL((bwd_dq_f32_kernel<DD, CC>), dim3(nqt * BH), dim3(kF32BT), 0, s, Q, K, V, \
-                     a.L, dO, a.LD, (float*)a.dQ, a.Nq, a.Nk, nqt, a.scale, off)
+                     a.L, dO, a.LD, (float*)a.dQ, a.Nq, a.Nk, nqt, a.scale, off, bias)
     if (a.d == 128) {
       if (a.causal) FA_DQ32_LAUNCH(128, true); else FA_DQ32_LAUNCH(128, false);
     } else {

@@ -216,6 +216,60 @@ struct BufTile {
   }
 };
 
+// Additive bias as the kernels take it: element (b, h, i, j) of the bias at
+// ptr[b*sb + h*sh + i*sq + j] (16-bit elements; sq a multiple of 8), folded
+// into the raw scores as bias * inv_scale so that the exponent stays
+// s * scale * log2(e) - m.
+struct BiasDev {
+  const void* ptr;
+  long long sb, sh, sq;
+  int H;
+  float inv_scale;
+};
+
+// Reads of an additive bias through a buffer descriptor over one head's bias
+// block of `nelem` 16-bit elements (element offsets below 2^30): loads past
+// the block return zeros and touch no memory.  Lanes read different rows, so
+// the offsets are per lane; the descriptor is wave-uniform.
+template <typename T>
+struct BiasReader {
+  static_assert(sizeof(T) == 2, "16-bit elements");
+#if __HIP_DEVICE_COMPILE__
+  __amdgpu_buffer_rsrc_t rs;
+#endif
+  __device__ __forceinline__ BiasReader(const T* base, long long nelem) {
+#if __HIP_DEVICE_COMPILE__
+    // The range check of a buffer load works on whole dwords: a dword that
+    // runs past the range reads as zero even where its first half is in it.
+    // The range is therefore rounded up to the 16-byte block that holds the
+    // last element; with a 16-byte aligned base that block lies in the page
+    // of a valid byte, so reading it cannot fault.  Callers keep nelem <=
+    // 2^30, so the range fits the 32-bit field.
+    const unsigned long long bytes = ((unsigned long long)nelem * 2 + 15) & ~15ull;
+    rs = make_rsrc(base, (int)(unsigned)(bytes < 0xfffffff0ull ? bytes : 0xfffffff0ull));
+#endif
+  }
+  // Elements e .. e+3 (e a multiple of 4), packed as loaded.
+  __device__ __forceinline__ typename Vec<T>::x4 load4(unsigned e) const {
+    typename Vec<T>::x4 r = {};
+#if __HIP_DEVICE_COMPILE__
+    typedef unsigned u32x2 __attribute__((ext_vector_type(2)));
+    const u32x2 v = __builtin_amdgcn_raw_buffer_load_b64(rs, (int)(e * 2), 0, 0);
+    r = __builtin_bit_cast(typename Vec<T>::x4, v);
+#endif
+    return r;
+  }
+  // Element e, as fp32.
+  __device__ __forceinline__ float load1(unsigned e) const {
+    float r = 0.f;
+#if __HIP_DEVICE_COMPILE__
+    const unsigned short v = __builtin_amdgcn_raw_buffer_load_b16(rs, (int)(e * 2), 0, 0);
+    r = (float)__builtin_bit_cast(T, v);
+#endif
+    return r;
+  }
+};
+
 // Wait for this wave's outstanding vector-memory operations (including the
 // direct-to-LDS loads above).
 __device__ __forceinline__ void vm_wait_all() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }

@@ -46,11 +46,11 @@ constexpr int kFwdBC = 64;   // keys per K/V tile
 constexpr int kFwdThreads = 256;
 constexpr float kRescaleSlack = 8.f;  // see the online softmax below
 
-template <typename T, int D, bool CAUSAL>
+template <typename T, int D, bool CAUSAL, bool BIAS>
 __global__ __launch_bounds__(kFwdThreads, 2) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void fwd_kernel(const T* __restrict__ Q, const T* __restrict__ K, const T* __restrict__ V,
-                T* __restrict__ O, float* __restrict__ L,
-                     int Nq, int Nk, int nqt, float c, int off) {
+                T* __restrict__ O, float* __restrict__ L, int Nq, int Nk, int nqt, float c,
+                int off, BiasDev bias) {
   typedef typename Vec<T>::x8 T8;
   typedef typename Vec<T>::x4 T4;
   constexpr int BR = kFwdBR, BC = kFwdBC;
@@ -85,6 +85,16 @@ void fwd_kernel(const T* __restrict__ Q, const T* __restrict__ K, const T* __res
   const size_t qbase = (size_t)bh * Nq * D;
   const T* Kh = K + (size_t)bh * Nk * D;
   const T* Vh = V + (size_t)bh * Nk * D;
+
+  // Additive bias (BIAS) of this head: lane row qrow, keys along elements.
+  const T* bias_h = nullptr;
+  long long bias_n = 0;
+  if constexpr (BIAS) {
+    const int b = bh / bias.H, h = bh - b * bias.H;
+    bias_h = (const T*)bias.ptr + b * bias.sb + h * bias.sh;
+    bias_n = (long long)(Nq - 1) * bias.sq + Nk;
+  }
+  const BiasReader<T> br(bias_h, bias_n);
 
   using KV = BufTile<D, BC, kFwdThreads>;
   const KV kv(wave, lane);
@@ -174,6 +184,22 @@ void fwd_kernel(const T* __restrict__ Q, const T* __restrict__ K, const T* __res
         sc[st & 1] = mfma32(a, qf[st >> 1], sc[st & 1]);
       }
     };
+    // Bias of the score tile at key k0b: lane row qrow holds keys
+    // k0b + mt*32 + g*8 + half*4 + 0..3 in elements i = g*4 .. g*4+3 of sc[mt];
+    // rows past Nq read zeros, keys past Nk are masked afterwards.
+    typedef typename Vec<T>::x4 BT4;
+    auto bias_load = [&](BT4 (&bb)[8], int k0b) {
+#pragma unroll
+      for (int q = 0; q < 8; ++q)
+        bb[q] = br.load4((unsigned)(qrow * bias.sq + k0b + (q >> 2) * 32 + (q & 3) * 8 + half * 4));
+    };
+    auto bias_add = [&](f32x16 (&sc)[2], const BT4 (&bb)[8]) {
+#pragma unroll
+      for (int q = 0; q < 8; ++q)
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+          sc[q >> 2][(q & 3) * 4 + e] = fmaf((float)bb[q][e], bias.inv_scale, sc[q >> 2][(q & 3) * 4 + e]);
+    };
     auto row_max = [&](const f32x16 (&sc)[2]) {
       float mx = -INFINITY;
 #pragma unroll
@@ -191,6 +217,11 @@ void fwd_kernel(const T* __restrict__ Q, const T* __restrict__ K, const T* __res
     __syncthreads();
     f32x16 sA[2], sB[2];
     scores(0, sA);
+    if constexpr (BIAS) {
+      BT4 bb[8];
+      bias_load(bb, 0);
+      bias_add(sA, bb);
+    }
     mask_tile(sA, 0);
     float mx_next = row_max(sA);
     __syncthreads();  // every wave is done with K tile 0 before tile 2 replaces it
@@ -250,7 +281,10 @@ void fwd_kernel(const T* __restrict__ Q, const T* __restrict__ K, const T* __res
       // scores) and V tile j+1.  The last iterations also compute scores of a
       // stale buffer and load rows past the end (as zeros): that extra work
       // keeps this block free of branches, so the three kinds of work stay
-      // interleaved.
+      // interleaved.  With a bias, its values for tile j+1 are loaded first
+      // and added once the scores are complete.
+      BT4 bnext[8];
+      if constexpr (BIAS) bias_load(bnext, k0 + BC);
       {
         constexpr int SA = 2 * NKK;
         T8 ring[KRING];
@@ -276,6 +310,7 @@ void fwd_kernel(const T* __restrict__ Q, const T* __restrict__ K, const T* __res
           __builtin_amdgcn_sched_barrier(0);
         }
       }
+      if constexpr (BIAS) bias_add(snext, bnext);
       mask_tile(snext, k0 + BC);
 
       // O^T += V^T P^T for tile j (step st reads chunk st / NNT of P),
@@ -341,7 +376,8 @@ constexpr int kF32Keys = 16;
 template <int D, bool CAUSAL>
 __global__ __launch_bounds__(kF32Rows) void fwd_f32_kernel(
     const float* __restrict__ Q, const float* __restrict__ K, const float* __restrict__ V,
-    float* __restrict__ O, float* __restrict__ L, int Nq, int Nk, int nqt, float scale, int off) {
+    float* __restrict__ O, float* __restrict__ L, int Nq, int Nk, int nqt, float scale, int off,
+    BiasDev bias) {
   __shared__ float sK[kF32Keys][D];
   __shared__ float sV[kF32Keys][D];
   const int bh = blockIdx.x / nqt;
@@ -349,6 +385,11 @@ __global__ __launch_bounds__(kF32Rows) void fwd_f32_kernel(
   const int tid = threadIdx.x;
   const int row = qt * kF32Rows + tid;
   const size_t qbase = (size_t)bh * Nq * D, kbase = (size_t)bh * Nk * D;
+  const float* brow = nullptr;  // this row's additive bias, if any
+  if (bias.ptr && row < Nq) {
+    const int b = bh / bias.H, h = bh - b * bias.H;
+    brow = (const float*)bias.ptr + b * bias.sb + h * bias.sh + (long long)row * bias.sq;
+  }
   float q[D], o[D];
 #pragma unroll
   for (int e = 0; e < D; ++e) {
@@ -375,7 +416,7 @@ __global__ __launch_bounds__(kF32Rows) void fwd_f32_kernel(
       for (int e = 0; e < D; ++e) acc = fmaf(q[e], sK[jj][e], acc);
       const int key = k0 + jj;
       const bool vis = key < Nk && (!CAUSAL || key <= row + off);
-      s[jj] = vis ? acc * scale : -INFINITY;
+      s[jj] = vis ? acc * scale + (brow ? brow[key] : 0.f) : -INFINITY;
       mx = fmaxf(mx, s[jj]);
     }
     const float m_new = fmaxf(m_run, mx);
@@ -406,7 +447,7 @@ __global__ __launch_bounds__(kF32Rows) void fwd_f32_kernel(
 
 namespace {
 
-template <typename T>
+template <typename T, bool BIAS>
 hipError_t launch_fwd_mfma(const FwdArgs& a, hipStream_t s) {
   const int BH = a.B * a.H;
   const int nqt = (a.Nq + kFwdBR - 1) / kFwdBR;
@@ -418,9 +459,10 @@ hipError_t launch_fwd_mfma(const FwdArgs& a, hipStream_t s) {
   const T* K = (const T*)a.K;
   const T* V = (const T*)a.V;
   T* O = (T*)a.O;
+  const BiasDev bias{a.bias.ptr, a.bias.sb, a.bias.sh, a.bias.sq, a.H, 1.f / a.scale};
 #define FA_FWD_LAUNCH(DD, CC)                                                                  \
-  hipLaunchKernelGGL((fwd_kernel<T, DD, CC>), dim3(nblocks), dim3(kFwdThreads), 0, s, Q, K, V, \
-                     O, a.L, a.Nq, a.Nk, nqt, c, off)
+  hipLaunchKernelGGL((fwd_kernel<T, DD, CC, BIAS>), dim3(nblocks), dim3(kFwdThreads), 0, s, Q, \
+                     K, V, O, a.L, a.Nq, a.Nk, nqt, c, off, bias)
   if (a.d == 128) {
     if (a.causal) FA_FWD_LAUNCH(128, true); else FA_FWD_LAUNCH(128, false);
   } else {
@@ -432,8 +474,12 @@ hipError_t launch_fwd_mfma(const FwdArgs& a, hipStream_t s) {
 
 }  // namespace
 
-hipError_t launch_fwd_bf16(const FwdArgs& a, hipStream_t s) { return launch_fwd_mfma<bf16>(a, s); }
-hipError_t launch_fwd_f16(const FwdArgs& a, hipStream_t s) { return launch_fwd_mfma<f16>(a, s); }
+hipError_t launch_fwd_bf16(const FwdArgs& a, hipStream_t s) {
+  return a.bias.ptr ? launch_fwd_mfma<bf16, true>(a, s) : launch_fwd_mfma<bf16, false>(a, s);
+}
+hipError_t launch_fwd_f16(const FwdArgs& a, hipStream_t s) {
+  return a.bias.ptr ? launch_fwd_mfma<f16, true>(a, s) : launch_fwd_mfma<f16, false>(a, s);
+}
 
 hipError_t launch_fwd_f32(const FwdArgs& a, hipStream_t s) {
   const int BH = a.B * a.H;
@@ -444,9 +490,10 @@ hipError_t launch_fwd_f32(const FwdArgs& a, hipStream_t s) {
   const float* K = (const float*)a.K;
   const float* V = (const float*)a.V;
   float* O = (float*)a.O;
+  const BiasDev bias{a.bias.ptr, a.bias.sb, a.bias.sh, a.bias.sq, a.H, 1.f / a.scale};
 #define FA_FWD32_LAUNCH(DD, CC)                                                               \
   hipLaunchKernelGGL((fwd_f32_kernel<DD, CC>), dim3(nblocks), dim3(kF32Rows), 0, s, Q, K, V, O, \
-                     a.L, a.Nq, a.Nk, nqt, a.scale, off)
+                     a.L, a.Nq, a.Nk, nqt, a.scale, off, bias)
   if (a.d == 128) {
     if (a.causal) FA_FWD32_LAUNCH(128, true); else FA_FWD32_LAUNCH(128, false);
   } else {

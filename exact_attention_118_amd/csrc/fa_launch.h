@@ -8,6 +8,13 @@
 
 namespace fa {
 
+// Optional additive bias: element (b, h, i, j) at ptr[b*sb + h*sh + i*sq + j]
+// (ptr == nullptr: none).  Same element type as Q.
+struct BiasArgs {
+  const void* ptr = nullptr;
+  long long sb = 0, sh = 0, sq = 0;
+};
+
 struct FwdArgs {
   const void* Q;
   const void* K;
@@ -17,6 +24,7 @@ struct FwdArgs {
   int B, H, Nq, Nk, d;
   float scale;
   bool causal;
+  BiasArgs bias;
 };
 
 struct BwdArgs {
@@ -33,6 +41,7 @@ struct BwdArgs {
   float scale;
   bool causal;
   float* LD;  // [B*H*Nq][2] fp32 scratch (workspace): per query row L * log2(e), then D = rowsum(dO * O)
+  BiasArgs bias;
 };
 
 // Tiled forward (Q-tile per workgroup, K/V streamed through LDS).

@@ -85,3 +85,32 @@ def make_inputs(w: Workload, seed: int = 0, device="cpu", with_grad_out: bool | 
     if with_grad_out:
         out["dO"] = draw(w.Nq).to(w.dtype).contiguous()
     return out
+
+
+def make_bias(B: int, H: int, Nq: int, Nk: int, dtype, seed: int = 0, device="cpu",
+              per_batch: bool = True, per_head: bool = True, row_stride: int | None = None,
+              drop: float = 0.0, pad_value: float = float("nan")):
+    """Seeded additive bias, returned as a view of shape [B or 1, H or 1, Nq, Nk].
+
+    Recipe: a ``torch.Generator`` on ``device`` seeded with ``seed``; an i.i.d.
+    standard normal float32 tensor of shape [B', H', Nq, row_stride] (B' = B if
+    ``per_batch`` else 1, H' likewise; row_stride defaults to Nk); then, when
+    ``drop`` > 0, a second uniform draw of the same shape sets each entry with
+    u < drop to -inf, except key 0 of every row, so that every row keeps a
+    finite entry; the columns past Nk are set to ``pad_value`` (NaN by
+    default: they are not part of the problem); cast to ``dtype``.  A
+    dimension of size 1 is meant to broadcast.
+    """
+    sq = Nk if row_stride is None else row_stride
+    if sq < Nk:
+        raise ValueError("row_stride must be >= Nk")
+    g = torch.Generator(device=device)
+    g.manual_seed(seed)
+    shape = (B if per_batch else 1, H if per_head else 1, Nq, sq)
+    b = torch.randn(shape, generator=g, device=device, dtype=torch.float32)
+    if drop > 0.0:
+        u = torch.rand(shape, generator=g, device=device, dtype=torch.float32)
+        u[..., 0] = 1.0
+        b[u < drop] = float("-inf")
+    b[..., Nk:] = pad_value
+    return b.to(dtype)[..., :Nk]

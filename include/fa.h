@@ -116,6 +116,39 @@ fa_status fa_bwd_stages(const void* Q, const void* K, const void* V, const void*
                         fa_dtype dtype, void* workspace, size_t workspace_bytes, void* stream,
                         int stages);
 
+/*
+ * Forward and backward passes with an additive bias -- the mask term of the
+ * method's formula taken in general: O = softmax(scale * Q K^T + bias
+ * (+ causal mask)) V (the CSDN post "Flash Attention1", section "Flash
+ * Attention", the score line of the formula; the 51CTO FlashAttention V1/V2
+ * notes name custom masks among the reasons to write one's own kernel).
+ *
+ *  bias: element type `dtype` (the same as Q); element (b, h, i, j) is
+ *  bias[b*bias_sb + h*bias_sh + i*bias_sq + j].  bias_sb and bias_sh may be 0
+ *  to broadcast over batches or heads.  A NULL bias is FA_ERR_NULL; bias_sb,
+ *  bias_sh >= 0 and bias_sq >= Nk, else FA_ERR_SHAPE; bias_sb, bias_sh and
+ *  bias_sq are multiples of 8 elements and the pointer is 16-byte aligned,
+ *  else FA_ERR_ALIGN; (Nq - 1) * bias_sq + Nk <= 2^30, else FA_ERR_SHAPE.
+ *  Only entries at rows < Nq and keys < Nk enter the result; the kernels may
+ *  also read the rest of a 16-byte aligned block that holds such an entry.
+ *  -inf entries remove keys; every score row must keep at least one finite
+ *  entry, or that row of O is NaN.  The bias is a constant of the
+ *  computation: fa_bwd_bias forms no gradient for it, and fa_bwd_bias must be
+ *  given the bias that fa_fwd_bias used (it recomputes P with it).
+ *  fa_fwd_bias always takes the tiled path and needs no workspace; the other
+ *  arguments, rules and errors are those of fa_fwd and fa_bwd.
+ */
+fa_status fa_fwd_bias(const void* Q, const void* K, const void* V, const void* bias,
+                      long long bias_sb, long long bias_sh, long long bias_sq, void* O, float* L,
+                      int B, int H, int Nq, int Nk, int d, float scale, int causal,
+                      fa_dtype dtype, void* stream);
+
+fa_status fa_bwd_bias(const void* Q, const void* K, const void* V, const void* bias,
+                      long long bias_sb, long long bias_sh, long long bias_sq, const void* O,
+                      const float* L, const void* dO, void* dQ, void* dK, void* dV, int B, int H,
+                      int Nq, int Nk, int d, float scale, int causal, fa_dtype dtype,
+                      void* workspace, size_t workspace_bytes, void* stream);
+
 /* Workspace bytes fa_fwd needs for these arguments (0 when none). */
 size_t fa_fwd_workspace_size(int B, int H, int Nq, int Nk, int d, fa_dtype dtype, int num_splits);
 

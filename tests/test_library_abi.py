@@ -126,6 +126,48 @@ def test_bwd_rejects_bad_arguments(lib):
                              fa.FA_BWD_DKDV) == fa.FA_ERR_WORKSPACE
 
 
+def fwd_bias(lib, bias=A, sb=0, sh=0, sq=16, Q=A, B=1, H=1, Nq=16, Nk=16, d=64, scale=0.125,
+             causal=0, dtype=fa.FA_BF16):
+    return lib.fa_fwd_bias(Q, A, A, bias, sb, sh, sq, A, A, B, H, Nq, Nk, d, scale, causal, dtype,
+                           None)
+
+
+def bwd_bias(lib, bias=A, sb=0, sh=0, sq=16, Nq=16, Nk=16, ws=None, ws_bytes=0, Q=A, B=1):
+    return lib.fa_bwd_bias(Q, A, A, bias, sb, sh, sq, A, A, A, A, A, A, B, 1, Nq, Nk, 64, 0.125, 0,
+                           fa.FA_BF16, ws, ws_bytes, None)
+
+
+def test_bias_entry_points_reject_bad_arguments(lib):
+    assert fwd_bias(lib, bias=None) == fa.FA_ERR_NULL
+    assert fwd_bias(lib, bias=MIS) == fa.FA_ERR_ALIGN
+    assert fwd_bias(lib, sq=8) == fa.FA_ERR_SHAPE          # row stride shorter than Nk
+    assert fwd_bias(lib, sq=20, Nk=20) == fa.FA_ERR_ALIGN  # not a multiple of 8 elements
+    assert fwd_bias(lib, sb=-16) == fa.FA_ERR_SHAPE
+    assert fwd_bias(lib, sh=-8) == fa.FA_ERR_SHAPE
+    assert fwd_bias(lib, sb=12) == fa.FA_ERR_ALIGN
+    assert fwd_bias(lib, sh=4) == fa.FA_ERR_ALIGN
+    assert fwd_bias(lib, Nq=1 << 15, Nk=1 << 15, sq=(1 << 15) + 8) == fa.FA_ERR_SHAPE  # > 2^30
+    assert fwd_bias(lib, Q=None) == fa.FA_ERR_NULL
+    # the shared checks of fa_fwd still apply, before the bias is looked at
+    assert fwd_bias(lib, bias=None, d=96) == fa.FA_ERR_UNSUPPORTED
+    assert fwd_bias(lib, bias=None, scale=0.0) == fa.FA_ERR_UNSUPPORTED
+    assert fwd_bias(lib, bias=None, Nq=20, Nk=16, causal=1) == fa.FA_ERR_SHAPE
+    need = lib.fa_bwd_workspace_size(1, 1, 16, 16, 64, fa.FA_BF16)
+    assert bwd_bias(lib, bias=None, ws=A, ws_bytes=need) == fa.FA_ERR_NULL
+    assert bwd_bias(lib, bias=MIS, ws=A, ws_bytes=need) == fa.FA_ERR_ALIGN
+    assert bwd_bias(lib, sq=8, ws=A, ws_bytes=need) == fa.FA_ERR_SHAPE
+    assert bwd_bias(lib, sh=-8, ws=A, ws_bytes=need) == fa.FA_ERR_SHAPE
+    assert bwd_bias(lib) == fa.FA_ERR_WORKSPACE
+    assert bwd_bias(lib, Q=None, ws=A, ws_bytes=need) == fa.FA_ERR_NULL
+
+
+def test_bias_entry_points_accept_empty_problems(lib):
+    assert fwd_bias(lib, bias=None, Q=None, B=0) == fa.FA_OK
+    assert fwd_bias(lib, bias=None, Q=None, Nq=0) == fa.FA_OK
+    assert lib.fa_bwd_bias(*([None] * 4), 0, 0, 16, *([None] * 6), 1, 1, 0, 0, 64, 0.125, 0,
+                           fa.FA_BF16, None, 0, None) == fa.FA_OK
+
+
 def test_workspace_queries(lib):
     B, H, N, d = 2, 3, 100, 128
     # backward: D and L*log2(e), each [B,H,N] fp32 padded to 256 bytes
