@@ -13,6 +13,10 @@ P materialised, exactly what the fused kernels compute tile by tile:
 * backward -- dQ, dK, dV of f = sum(dO * O), recomputing P from the inputs
   (the Huawei Cloud post "FlashAttention", section 3 "Recomputation"; the 51CTO FlashAttention V1/V2 notes names the auxiliary row vector D).
 
+Dropout's random bits come from Philox4x32-10 (``oracle.philox``), written
+from its published definition and pinned by the generator authors' known-answer
+vectors (tests/golden/philox4x32_kat.json).
+
 Every function is pinned by CPU tests against facts that do not come from this
 code: hand-derived closed forms (tests/golden), the page-1 online-softmax
 walk-through re-implemented independently, finite differences, algebraic
@@ -28,4 +32,11 @@ from .attention import (  # noqa: F401
     causal_visible,
     scores,
     softmax_with_lse,
+)
+from .philox import (  # noqa: F401
+    dropout_bytes,
+    dropout_multiplier,
+    dropout_multiplier_batched,
+    keep_threshold,
+    philox4x32,
 )

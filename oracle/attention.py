@@ -19,6 +19,10 @@ Conventions (the readings of the pages that this oracle fixes):
   optional [nq, nk] matrix added to the scaled scores before the causal mask;
   -inf entries remove keys.  It is a constant of the computation (no
   gradient is formed for it).
+* Dropout (optional): a multiplier matrix Z [nq, nk] (0 for a dropped score,
+  1/keep-probability for a kept one, from ``oracle.philox``) applied to the
+  normalised probabilities, O = (P * Z) V.  L stays the logsumexp of the
+  scores: dropout acts after the softmax.
 * All arithmetic is float64 on inputs converted exactly from bf16, fp16 or fp32.
 """
 
@@ -82,19 +86,23 @@ def softmax_with_lse(S) -> tuple[np.ndarray, np.ndarray]:
     return P, L
 
 
-def attention_forward(Q, K, V, scale: float, causal: bool, bias=None):
+def attention_forward(Q, K, V, scale: float, causal: bool, bias=None, dropout=None):
     """Forward pass for one head: returns (O [nq, dv], L [nq]).
 
     The CSDN post "Flash Attention1", "Flash Attention" section: S = Q K^T, P = softmax(S), O = P V;
-    L as defined in ``softmax_with_lse``.
+    L as defined in ``softmax_with_lse``.  With ``dropout`` (the multiplier
+    matrix Z), O = (P * Z) V: the dropout on P of the V1 algorithm in the
+    51CTO FlashAttention V1/V2 notes ("FlashAttention V2 相比 V1 有哪些改进").
     """
     S = scores(Q, K, scale, causal, bias)
     P, L = softmax_with_lse(S)
+    if dropout is not None:
+        P = P * _as_f64(dropout)
     O = P @ _as_f64(V)
     return O, L
 
 
-def attention_forward_rows(Q, K, V, rows, scale: float, causal: bool, bias=None):
+def attention_forward_rows(Q, K, V, rows, scale: float, causal: bool, bias=None, dropout=None):
     """Forward pass for selected query rows of one head (same definition).
 
     Row i of O and L depends only on Q_i and all of K, V, so a sample of rows
@@ -112,11 +120,13 @@ def attention_forward_rows(Q, K, V, rows, scale: float, causal: bool, bias=None)
         vis = np.arange(nk)[None, :] <= (rows[:, None] + (nk - nq))
         S = np.where(vis, S, -np.inf)
     P, L = softmax_with_lse(S)
+    if dropout is not None:
+        P = P * _as_f64(dropout)[rows]
     return P @ V, L
 
 
 def attention_backward(Q, K, V, dO, scale: float, causal: bool, return_aux: bool = False,
-                       bias=None):
+                       bias=None, dropout=None):
     """Gradients of f = sum(dO * O) for one head: returns (dQ, dK, dV).
 
     P is recomputed from the inputs (the Huawei Cloud post "FlashAttention", section 3: recomputation in the
@@ -134,6 +144,11 @@ def attention_backward(Q, K, V, dO, scale: float, causal: bool, return_aux: bool
 
     D is formed from P and dP, not from the shortcut dO_i . O_i that a kernel
     uses; the two agree because O_i = sum_j P_ij V_j.
+
+    With ``dropout`` (Z), O = (P * Z) V, so the chain rule gives
+    dV = (P * Z)^T dO and dP = (dO V^T) * Z (the gradient with respect to the
+    undropped P); D, dS, dQ and dK then follow as above, and D_i still equals
+    dO_i . O_i.
     With ``return_aux`` also returns a dict holding P, L, dP, D and dS.
     """
     Q = _as_f64(Q)
@@ -142,8 +157,11 @@ def attention_backward(Q, K, V, dO, scale: float, causal: bool, return_aux: bool
     dO = _as_f64(dO)
     S = scores(Q, K, scale, causal, bias)
     P, L = softmax_with_lse(S)
-    dV = P.T @ dO
+    Z = None if dropout is None else _as_f64(dropout)
+    dV = (P if Z is None else P * Z).T @ dO
     dP = dO @ V.T
+    if Z is not None:
+        dP = dP * Z
     D = (P * dP).sum(axis=1, keepdims=True)
     dS = P * (dP - D)
     dQ = scale * (dS @ K)
@@ -167,42 +185,49 @@ def _head_bias(bias, lead):
     return b.reshape((-1,) + b.shape[-2:])
 
 
-def attention_forward_batched(Q, K, V, scale: float, causal: bool, heads=None, bias=None):
+def attention_forward_batched(Q, K, V, scale: float, causal: bool, heads=None, bias=None,
+                              dropout=None):
     """``attention_forward`` over leading [B, H] dims, one head at a time.
 
     Q [B, H, nq, d], K and V [B, H, nk, d], bias (optional) [B or 1, H or 1,
-    nq, nk].  ``heads`` (flat b*H + h indices) restricts the work to a sample
+    nq, nk], dropout (optional) Z [B, H, nq, nk].  ``heads`` (flat b*H + h
+    indices) restricts the work to a sample
     of heads; the result then has shape [len(heads), nq, d] and [len(heads), nq].
     """
     q, lead = _heads(Q)
     k, _ = _heads(K)
     v, _ = _heads(V)
     bh = _head_bias(bias, lead)
+    zh = _head_bias(dropout, lead)
     idx = range(q.shape[0]) if heads is None else list(heads)
     O = np.empty((len(idx), q.shape[1], v.shape[2]))
     L = np.empty((len(idx), q.shape[1]))
     for n, h in enumerate(idx):
         O[n], L[n] = attention_forward(q[h], k[h], v[h], scale, causal,
-                                       None if bh is None else bh[h])
+                                       None if bh is None else bh[h],
+                                       None if zh is None else zh[h])
     if heads is None:
         return O.reshape(lead + O.shape[1:]), L.reshape(lead + L.shape[1:])
     return O, L
 
 
-def attention_backward_batched(Q, K, V, dO, scale: float, causal: bool, heads=None, bias=None):
+def attention_backward_batched(Q, K, V, dO, scale: float, causal: bool, heads=None, bias=None,
+                               dropout=None):
     """``attention_backward`` over leading [B, H] dims, one head at a time."""
     q, lead = _heads(Q)
     k, _ = _heads(K)
     v, _ = _heads(V)
     do, _ = _heads(dO)
     bh = _head_bias(bias, lead)
+    zh = _head_bias(dropout, lead)
     idx = range(q.shape[0]) if heads is None else list(heads)
     dQ = np.empty((len(idx),) + q.shape[1:])
     dK = np.empty((len(idx),) + k.shape[1:])
     dV = np.empty((len(idx),) + v.shape[1:])
     for n, h in enumerate(idx):
         dQ[n], dK[n], dV[n] = attention_backward(q[h], k[h], v[h], do[h], scale, causal,
-                                                 bias=None if bh is None else bh[h])
+                                                 bias=None if bh is None else bh[h],
+                                                 dropout=None if zh is None else zh[h])
     if heads is None:
         return (dQ.reshape(lead + dQ.shape[1:]), dK.reshape(lead + dK.shape[1:]),
                 dV.reshape(lead + dV.shape[1:]))

@@ -16,7 +16,12 @@ Sources of truth used here:
 * torch's float64 scaled_dot_product_attention and autograd on the CPU;
 * for the additive bias: a per-row constant only shifts L, a bias ln(w_j)
   weights key j by w_j (brute force with math.exp), and -inf entries are the
-  same as removing those keys.
+  same as removing those keys;
+* for dropout: finite differences and torch's float64 autograd through
+  softmax, the multiplier Z and the product with V; the expectation over
+  masks drawn by the generator equals the attention without dropout; and the
+  generator itself (Philox4x32-10) against the known-answer vectors published
+  with its reference implementation (tests/golden/philox4x32_kat.json).
 """
 
 import json
@@ -32,6 +37,7 @@ import oracle
 from oracle import attention as A
 
 GOLDEN = os.path.join(os.path.dirname(__file__), "golden", "hand_derived_attention.json")
+PHILOX_KAT = os.path.join(os.path.dirname(__file__), "golden", "philox4x32_kat.json")
 
 
 # --------------------------------------------------------------------------- helpers
@@ -359,10 +365,90 @@ def check_bias_torch_library(fwd, bwd):
     return bool(ok)
 
 
+def _mask(r, nq, nk, keep=0.6):
+    """A dropout multiplier with both kept (1/keep) and dropped (0) entries."""
+    return np.where(r.random((nq, nk)) < keep, 1.0 / keep, 0.0)
+
+
+def check_dropout_finite_differences(fwd, bwd):
+    """With the multiplier Z fixed, the backward is the gradient of sum(dO * O)."""
+    ok = True
+    h = 1e-6
+    for n, (nq, nk, d, causal) in enumerate([(3, 3, 2, False), (4, 4, 2, True), (3, 5, 3, True)]):
+        r = _rng(700 + n)
+        Q, K, V, dO = (r.standard_normal(s) for s in ((nq, d), (nk, d), (nk, d), (nq, d)))
+        Z = _mask(r, nq, nk)
+        scale = 0.7
+        got = bwd(Q, K, V, dO, scale, causal, dropout=Z)
+        for which, X in enumerate((Q, K, V)):
+            num = np.zeros_like(X)
+            for idx in np.ndindex(X.shape):
+                args = [Q.copy(), K.copy(), V.copy()]
+                args[which][idx] += h
+                fp = float((fwd(*args, scale, causal, dropout=Z)[0] * dO).sum())
+                args[which][idx] -= 2 * h
+                fm = float((fwd(*args, scale, causal, dropout=Z)[0] * dO).sum())
+                num[idx] = (fp - fm) / (2 * h)
+            err = np.abs(np.asarray(got[which]) - num).max() / max(np.abs(num).max(), 1e-30)
+            ok &= err <= 1e-6
+    return bool(ok)
+
+
+def _torch_ref_dropout(Q, K, V, dO, scale, causal, Z):
+    q, k, v = (torch.tensor(x, dtype=torch.float64, requires_grad=True) for x in (Q, K, V))
+    s = scale * (q @ k.T)
+    if causal:
+        nq, nk = s.shape
+        vis = torch.ones(nq, nk, dtype=torch.bool).tril(diagonal=nk - nq)
+        s = s.masked_fill(~vis, float("-inf"))
+    lse = torch.logsumexp(s, dim=1)
+    o = (torch.softmax(s, dim=1) * torch.tensor(Z, dtype=torch.float64)) @ v
+    o.backward(torch.tensor(dO, dtype=torch.float64))
+    return (o.detach().numpy(), lse.detach().numpy(), q.grad.numpy(), k.grad.numpy(),
+            v.grad.numpy())
+
+
+def check_dropout_torch_library(fwd, bwd):
+    """torch's float64 softmax, the multiplier and the product with V, with autograd."""
+    ok = True
+    for n, (nq, nk, d, causal) in enumerate([(8, 8, 16, False), (8, 8, 16, True), (5, 12, 8, True)]):
+        r = _rng(720 + n)
+        Q, K, V, dO = (r.standard_normal(s) for s in ((nq, d), (nk, d), (nk, d), (nq, d)))
+        Z = _mask(r, nq, nk, keep=0.75)
+        scale = 1.0 / math.sqrt(d)
+        O_t, L_t, dQ_t, dK_t, dV_t = _torch_ref_dropout(Q, K, V, dO, scale, causal, Z)
+        O, L = fwd(Q, K, V, scale, causal, dropout=Z)
+        dQ, dK, dV = bwd(Q, K, V, dO, scale, causal, dropout=Z)
+        ok &= _close(O, O_t, 1e-10) and _close(L, L_t, 1e-10) and _close(dQ, dQ_t, 1e-10)
+        ok &= _close(dK, dK_t, 1e-10) and _close(dV, dV_t, 1e-10)
+    return bool(ok)
+
+
+def check_dropout_expectation(fwd, bwd):
+    """Averaged over masks drawn by the generator, O and the gradients are those
+    without dropout (the multiplier 256/T makes each kept score unbiased)."""
+    nq, nk, d, p, n = 4, 8, 3, 0.5, 4000
+    r = _rng(740)
+    Q, K, V, dO = (r.standard_normal(s) for s in ((nq, d), (nk, d), (nk, d), (nq, d)))
+    Zs = np.stack([oracle.dropout_multiplier(nq, nk, p, seed=1234, offset=t, bh=0)
+                   for t in range(n)])
+    O0, L0 = fwd(Q, K, V, 0.5, False)
+    g0 = bwd(Q, K, V, dO, 0.5, False)
+    Os = np.stack([fwd(Q, K, V, 0.5, False, dropout=Z)[0] for Z in Zs])
+    gs = [np.stack(x) for x in zip(*(bwd(Q, K, V, dO, 0.5, False, dropout=Z) for Z in Zs))]
+    ok = True
+    for mean_of, samples, exact in [(Os.mean(0), Os, O0)] + [(g.mean(0), g, e) for g, e in zip(gs, g0)]:
+        sem = samples.std(0) / math.sqrt(n)  # standard error of the mean, per element
+        ok &= bool(np.all(np.abs(mean_of - exact) <= 5.0 * sem + 1e-12))
+    return bool(ok)
+
+
 ALL_CHECKS = [check_golden, check_walkthrough, check_shift_invariance, check_closed_forms,
               check_finite_differences, check_gradient_identities, check_split_combine,
               check_torch_library, check_brute_force, check_bias_row_constant,
-              check_bias_log_weights, check_bias_neg_inf_drops_keys, check_bias_torch_library]
+              check_bias_log_weights, check_bias_neg_inf_drops_keys, check_bias_torch_library,
+              check_dropout_finite_differences, check_dropout_torch_library,
+              check_dropout_expectation]
 
 
 # --------------------------------------------------------------------------- tests
@@ -456,7 +542,8 @@ def test_batched_bias_broadcasts_over_batch_and_heads():
 # least one pin above.
 
 def _mut_fwd(scale_in_scores=True, visible=None, lse_without_max=False, pv_transposed=False,
-             bias_scaled=False, bias_transposed=False):
+             bias_scaled=False, bias_transposed=False, drop_unscaled=False, drop_renormalised=False,
+             drop_in_lse=False):
     def scores(Q, K, scale, causal, bias=None):
         S = (scale if scale_in_scores else 1.0) * (Q @ K.T)
         if bias is not None:
@@ -469,13 +556,22 @@ def _mut_fwd(scale_in_scores=True, visible=None, lse_without_max=False, pv_trans
             S = np.where(vis, S, -np.inf)
         return S
 
-    def fwd(Q, K, V, scale, causal, bias=None):
+    def fwd(Q, K, V, scale, causal, bias=None, dropout=None):
         S = scores(np.asarray(Q, float), np.asarray(K, float), scale, causal, bias)
         m = S.max(axis=1, keepdims=True)
         e = np.exp(S - m)
         l = e.sum(axis=1, keepdims=True)
         P = e / l
         L = np.log(l)[:, 0] if lse_without_max else (m + np.log(l))[:, 0]
+        if dropout is not None:
+            Z = np.asarray(dropout, float)
+            if drop_unscaled:
+                Z = (Z > 0).astype(float)
+            P = P * Z
+            if drop_renormalised:
+                P = P / P.sum(axis=1, keepdims=True)
+            if drop_in_lse:
+                L = (m + np.log((e * Z).sum(axis=1, keepdims=True)))[:, 0]
         V = np.asarray(V, float)
         O = (P @ V) if not pv_transposed else (P @ V[::-1])
         return O, L
@@ -483,13 +579,18 @@ def _mut_fwd(scale_in_scores=True, visible=None, lse_without_max=False, pv_trans
 
 
 def _mut_bwd(scores, dv_no_transpose=False, ds_sign=False, dq_no_scale=False,
-             dk_wrong_operand=False, d_from_wrong_axis=False, bias_ignored=False):
-    def bwd(Q, K, V, dO, scale, causal, bias=None):
+             dk_wrong_operand=False, d_from_wrong_axis=False, bias_ignored=False,
+             drop_not_in_dp=False, drop_not_in_dv=False):
+    def bwd(Q, K, V, dO, scale, causal, bias=None, dropout=None):
         Q, K, V, dO = (np.asarray(x, float) for x in (Q, K, V, dO))
         S = scores(Q, K, scale, causal, None if bias_ignored else bias)
         P, _ = A.softmax_with_lse(S)
-        dV = (P @ dO) if dv_no_transpose and P.shape[0] == P.shape[1] else P.T @ dO
+        Z = np.ones_like(P) if dropout is None else np.asarray(dropout, float)
+        Pd = P if drop_not_in_dv else P * Z
+        dV = (Pd @ dO) if dv_no_transpose and P.shape[0] == P.shape[1] else Pd.T @ dO
         dP = dO @ V.T
+        if not drop_not_in_dp:
+            dP = dP * Z
         D = (P * dP).sum(axis=0 if d_from_wrong_axis and P.shape[0] == P.shape[1] else 1,
                          keepdims=True)
         if d_from_wrong_axis and P.shape[0] == P.shape[1]:
@@ -528,6 +629,11 @@ def _mutants():
     f, s = _mut_fwd(bias_transposed=True)
     yield "bias transposed", f, _mut_bwd(s)
     yield "bias left out of the backward", f_ok, _mut_bwd(s_ok, bias_ignored=True)
+    yield "dropout mask not scaled by 1/keep", _mut_fwd(drop_unscaled=True)[0], _mut_bwd(s_ok)
+    yield "probabilities renormalised after dropout", _mut_fwd(drop_renormalised=True)[0], _mut_bwd(s_ok)
+    yield "logsumexp of the dropped probabilities", _mut_fwd(drop_in_lse=True)[0], _mut_bwd(s_ok)
+    yield "dropout left out of dP", f_ok, _mut_bwd(s_ok, drop_not_in_dp=True)
+    yield "dropout left out of dV", f_ok, _mut_bwd(s_ok, drop_not_in_dv=True)
 
 
 def test_unmutated_copy_passes_every_pin():
@@ -548,3 +654,108 @@ def test_planted_mistakes_are_caught(name, fwd, bwd):
         if not passed:
             failed.append(check.__name__)
     assert failed, f"no pin caught the planted mistake: {name}"
+
+
+# --------------------------------------------------------------------------- the dropout generator
+
+def _kat_cases():
+    with open(PHILOX_KAT) as f:
+        rec = json.load(f)
+    return [([int(x, 16) for x in c["counter"]], [int(x, 16) for x in c["key"]],
+             [int(x, 16) for x in c["out"]]) for c in rec["cases"]]
+
+
+def _philox_passes_kat(fn):
+    for ctr, key, out in _kat_cases():
+        got = [int(np.asarray(w)) for w in fn(ctr, key)]
+        if got != out:
+            return False
+    return True
+
+
+def test_philox_known_answer_vectors():
+    assert _philox_passes_kat(oracle.philox4x32)
+
+
+def test_philox_vectorised_over_counters():
+    """A batch of counters gives what the counters give one at a time."""
+    ctrs = [np.array([0, 5, 0xFFFFFFFF]), np.array([1, 2, 3]), np.array([7, 0, 9]), 4]
+    batch = oracle.philox4x32(ctrs, (11, 12))
+    for n in range(3):
+        one = oracle.philox4x32([int(ctrs[0][n]), int(ctrs[1][n]), int(ctrs[2][n]), 4], (11, 12))
+        assert [int(b[n]) for b in batch] == [int(np.asarray(w)) for w in one]
+
+
+def _philox_mutant(kind):
+    def fn(counter, key, rounds=10):
+        c = [int(x) & 0xFFFFFFFF for x in counter]
+        k0, k1 = int(key[0]), int(key[1])
+        m0, m1 = (0xCD9E8D57, 0xD2511F53) if kind == "multipliers swapped" else (0xD2511F53, 0xCD9E8D57)
+        for _ in range(rounds - (1 if kind == "nine rounds" else 0)):
+            p0, p1 = m0 * c[0], m1 * c[2]
+            hi0, lo0, hi1, lo1 = p0 >> 32, p0 & 0xFFFFFFFF, p1 >> 32, p1 & 0xFFFFFFFF
+            if kind == "output words reordered":
+                c = [hi0 ^ c[3] ^ k1, lo0, hi1 ^ c[1] ^ k0, lo1]
+            else:
+                c = [hi1 ^ c[1] ^ k0, lo1, hi0 ^ c[3] ^ k1, lo0]
+            if kind != "key not bumped":
+                k0, k1 = (k0 + 0x9E3779B9) & 0xFFFFFFFF, (k1 + 0xBB67AE85) & 0xFFFFFFFF
+        return c
+    return fn
+
+
+@pytest.mark.parametrize("kind", ["multipliers swapped", "nine rounds", "output words reordered",
+                                  "key not bumped"])
+def test_planted_generator_mistakes_fail_the_known_answers(kind):
+    assert _philox_passes_kat(_philox_mutant("none"))
+    assert not _philox_passes_kat(_philox_mutant(kind))
+
+
+def test_dropout_bytes_follow_the_block_layout():
+    """Score (i, j) takes byte j mod 4 of word i mod 4 of the call with counter
+    (j div 4, i div 4, bh, offset), key (seed low, seed high)."""
+    seed, offset, bh = 0x0123456789ABCDEF, 77, 5
+    by = oracle.dropout_bytes(9, 11, seed, offset, bh)
+    for i in range(9):
+        for j in range(11):
+            w = oracle.philox4x32([j // 4, i // 4, bh, offset], (seed & 0xFFFFFFFF, seed >> 32))
+            assert int(by[i, j]) == (int(np.asarray(w[i % 4])) >> (8 * (j % 4))) & 0xFF
+
+
+def test_keep_threshold():
+    assert oracle.keep_threshold(0.0) == 256
+    assert oracle.keep_threshold(0.5) == 128
+    assert oracle.keep_threshold(0.1) == 230      # round(230.4)
+    assert oracle.keep_threshold(0.998) == 1      # round(0.512)
+    for bad in (-0.1, 1.0, 0.999, float("nan")):
+        with pytest.raises(ValueError):
+            oracle.keep_threshold(bad)
+
+
+def test_dropout_bytes_are_uniform_and_the_keep_rate_is_t_over_256():
+    by = oracle.dropout_bytes(256, 512, seed=42, offset=0, bh=3).ravel()
+    n = by.size
+    counts = np.bincount(by, minlength=256)
+    chi2 = float(((counts - n / 256) ** 2 / (n / 256)).sum())
+    assert 150 < chi2 < 370  # 255 degrees of freedom: mean 255, sd 22.6
+    for p in (0.1, 0.3, 0.5):
+        t = oracle.keep_threshold(p)
+        frac = float((by < t).mean())
+        q = t / 256
+        assert abs(frac - q) <= 5 * math.sqrt(q * (1 - q) / n)
+    Z = oracle.dropout_multiplier(256, 512, 0.3, seed=42, offset=0, bh=3)
+    assert set(np.unique(Z)) == {0.0, 256.0 / oracle.keep_threshold(0.3)}
+
+
+def test_dropout_masks_differ_across_heads_offsets_and_seeds():
+    a = oracle.dropout_bytes(16, 16, 1, 0, 0)
+    for other in (oracle.dropout_bytes(16, 16, 1, 0, 1), oracle.dropout_bytes(16, 16, 1, 1, 0),
+                  oracle.dropout_bytes(16, 16, 2, 0, 0), oracle.dropout_bytes(16, 16, 1 << 32, 0, 0)):
+        assert (a != other).mean() > 0.9
+
+
+def test_batched_dropout_uses_the_flat_head_index():
+    Z = oracle.dropout_multiplier_batched(2, 3, 5, 9, 0.25, seed=9, offset=4)
+    for b in range(2):
+        for h in range(3):
+            assert np.array_equal(Z[b, h], oracle.dropout_multiplier(5, 9, 0.25, 9, 4, b * 3 + h))
