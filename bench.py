@@ -184,20 +184,26 @@ def bench_decode(fa, torch, steps):
             "algorithmic_bytes": all_bytes}
 
 
-def _time_fwd_bwd(fa, torch, w, Q, K, V, dO, ws, steps, bias=None):
-    """Mean forward and backward milliseconds of fa_fwd(_bias) + fa_bwd(_bias)."""
+def _time_fwd_bwd(fa, torch, w, Q, K, V, dO, ws, steps, bias=None, dropout_p=0.0):
+    """Mean forward and backward milliseconds of fa_fwd + fa_bwd (the bias or
+    the dropout entry points when given)."""
     O = torch.empty_like(Q)
     L = torch.empty(w.B, w.H, w.Nq, dtype=torch.float32, device="cuda")
     dQ, dK, dV = torch.empty_like(Q), torch.empty_like(K), torch.empty_like(V)
 
     def run(ev=None):
-        if bias is None:
+        if dropout_p:
+            fa.fa_fwd_ex(Q, K, V, O, L, w.scale, w.causal, bias=bias, dropout_p=dropout_p, seed=1)
+        elif bias is None:
             fa.fa_fwd(Q, K, V, O, L, w.scale, w.causal)
         else:
             fa.fa_fwd_bias(Q, K, V, bias, O, L, w.scale, w.causal)
         if ev is not None:
             ev.record()
-        if bias is None:
+        if dropout_p:
+            fa.fa_bwd_ex(Q, K, V, O, L, dO, dQ, dK, dV, w.scale, w.causal, bias=bias,
+                         dropout_p=dropout_p, seed=1, workspace=ws)
+        elif bias is None:
             fa.fa_bwd(Q, K, V, O, L, dO, dQ, dK, dV, w.scale, w.causal, workspace=ws)
         else:
             fa.fa_bwd_bias(Q, K, V, bias, O, L, dO, dQ, dK, dV, w.scale, w.causal, workspace=ws)
@@ -236,6 +242,14 @@ def bench_bias(fa, torch, w, x, ws, steps):
     return r
 
 
+def bench_dropout(fa, torch, w, x, ws, steps, p=0.1):
+    """The same forward and backward with dropout p on the probabilities
+    (Philox mask drawn in the kernels, forward and backward)."""
+    r = _time_fwd_bwd(fa, torch, w, x["Q"], x["K"], x["V"], x["dO"], ws, steps, dropout_p=p)
+    r["dropout_p"] = p
+    return r
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__)
     ap.add_argument("--gpus", type=int, default=1)
@@ -248,6 +262,8 @@ def main():
     ap.add_argument("--no-fp16", action="store_true", help="skip the fp16 forward and backward")
     ap.add_argument("--no-bias", action="store_true",
                     help="skip the forward and backward with an additive bias")
+    ap.add_argument("--no-dropout", action="store_true",
+                    help="skip the forward and backward with dropout")
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
                     help="after the timed steps, run one plain device-to-device copy of this many "
                          "MiB (reference point for HBM byte counters under rocprofv3 --pmc)")
@@ -379,6 +395,9 @@ def main():
     if not args.no_bias:
         log("additive bias [1, H, N, N], same workload")
         out["bias"] = bench_bias(fa, torch, w, x, ws, steps=max(3, args.steps // 2))
+    if not args.no_dropout:
+        log("dropout p = 0.1, same workload")
+        out["dropout"] = bench_dropout(fa, torch, w, x, ws, steps=max(3, args.steps // 2))
     del ws
     if args.copy_calibration_mib > 0:
         n = args.copy_calibration_mib << 20

@@ -14,6 +14,7 @@ import os
 
 __all__ = [
     "FAError", "load_library", "lib_path", "fa_fwd", "fa_bwd", "fa_fwd_bias", "fa_bwd_bias",
+    "fa_fwd_ex", "fa_bwd_ex",
     "forward", "backward",
     "fwd_workspace_size", "bwd_workspace_size", "fwd_num_splits", "status_string", "version",
     "FA_OK", "FA_ERR_NULL", "FA_ERR_SHAPE", "FA_ERR_UNSUPPORTED", "FA_ERR_ALIGN",
@@ -27,6 +28,7 @@ FA_BF16, FA_FP32, FA_FP16 = 0, 1, 2
 FA_BWD_PREPROCESS, FA_BWD_DKDV, FA_BWD_DQ, FA_BWD_ALL = 1, 2, 4, 7
 
 EXPORTED_SYMBOLS = ("fa_fwd", "fa_bwd", "fa_bwd_stages", "fa_fwd_bias", "fa_bwd_bias",
+                    "fa_fwd_ex", "fa_bwd_ex",
                     "fa_fwd_workspace_size", "fa_bwd_workspace_size", "fa_fwd_num_splits",
                     "fa_status_string", "fa_version")
 
@@ -65,6 +67,13 @@ def load_library():
     lib.fa_bwd_bias.argtypes = [vp, vp, vp, vp, ll, ll, ll, vp, vp, vp, vp, vp, vp, i, i, i, i, i,
                                 f, i, i, vp, sz, vp]
     lib.fa_bwd_bias.restype = i
+    ull, u = ctypes.c_ulonglong, ctypes.c_uint
+    lib.fa_fwd_ex.argtypes = [vp, vp, vp, vp, ll, ll, ll, f, ull, u, vp, vp, i, i, i, i, i, f, i, i,
+                              vp]
+    lib.fa_fwd_ex.restype = i
+    lib.fa_bwd_ex.argtypes = [vp, vp, vp, vp, ll, ll, ll, f, ull, u, vp, vp, vp, vp, vp, vp, i, i,
+                              i, i, i, f, i, i, vp, sz, vp]
+    lib.fa_bwd_ex.restype = i
     lib.fa_fwd_workspace_size.argtypes = [i, i, i, i, i, i, i]
     lib.fa_fwd_workspace_size.restype = sz
     lib.fa_bwd_workspace_size.argtypes = [i, i, i, i, i, i]
@@ -266,21 +275,87 @@ def fa_bwd_bias(Q, K, V, bias, O, L, dO, dQ, dK, dV, scale, causal, workspace=No
     return dQ, dK, dV
 
 
-def forward(Q, K, V, scale=None, causal=False, num_splits=0, stream=None, bias=None):
-    """Allocate O, L and run ``fa_fwd``.  Returns (O, L)."""
+def _check_dropout(dropout_p, seed, offset):
+    if not (0.0 <= float(dropout_p) < 1.0):
+        raise ValueError(f"dropout_p must lie in [0, 1), got {dropout_p}")
+    if not (0 <= int(seed) < 2**64) or not (0 <= int(offset) < 2**32):
+        raise ValueError("seed must fit 64 bits and offset 32 bits")
+
+
+def fa_fwd_ex(Q, K, V, O, L, scale, causal, bias=None, dropout_p=0.0, seed=0, offset=0,
+              stream=None):
+    """Call ``fa_fwd_ex``: optional additive bias and optional dropout on P."""
+    lib = load_library()
+    B, H, Nq, d = Q.shape
+    Nk = K.shape[2]
+    dev = Q.device
+    _check_tensor("Q", Q, (B, H, Nq, d), Q.dtype, dev)
+    _check_tensor("K", K, (B, H, Nk, d), Q.dtype, dev)
+    _check_tensor("V", V, (B, H, Nk, d), Q.dtype, dev)
+    _check_tensor("O", O, (B, H, Nq, d), Q.dtype, dev)
+    _check_tensor("L", L, (B, H, Nq), _torch().float32, dev)
+    _check_dropout(dropout_p, seed, offset)
+    sb, sh, sq = (0, 0, 0) if bias is None else _bias_strides(bias, B, H, Nq, Nk, Q.dtype, dev)
+    st = lib.fa_fwd_ex(_ptr(Q), _ptr(K), _ptr(V), None if bias is None else _ptr(bias), sb, sh, sq,
+                       float(dropout_p), int(seed), int(offset), _ptr(O), _ptr(L), B, H, Nq, Nk, d,
+                       float(scale), int(bool(causal)), _dtype_code(Q), _stream_handle(dev, stream))
+    if st != FA_OK:
+        raise FAError(st, "fa_fwd_ex")
+    return O, L
+
+
+def fa_bwd_ex(Q, K, V, O, L, dO, dQ, dK, dV, scale, causal, bias=None, dropout_p=0.0, seed=0,
+              offset=0, workspace=None, stream=None):
+    """Call ``fa_bwd_ex`` with the bias and dropout arguments the forward pass used."""
+    lib = load_library()
+    B, H, Nq, d = Q.shape
+    Nk = K.shape[2]
+    dev = Q.device
+    for name, t, shp in (("Q", Q, (B, H, Nq, d)), ("K", K, (B, H, Nk, d)), ("V", V, (B, H, Nk, d)),
+                         ("O", O, (B, H, Nq, d)), ("dO", dO, (B, H, Nq, d)),
+                         ("dQ", dQ, (B, H, Nq, d)), ("dK", dK, (B, H, Nk, d)),
+                         ("dV", dV, (B, H, Nk, d))):
+        _check_tensor(name, t, shp, Q.dtype, dev)
+    _check_tensor("L", L, (B, H, Nq), _torch().float32, dev)
+    _check_dropout(dropout_p, seed, offset)
+    sb, sh, sq = (0, 0, 0) if bias is None else _bias_strides(bias, B, H, Nq, Nk, Q.dtype, dev)
+    code = _dtype_code(Q)
+    need = lib.fa_bwd_workspace_size(B, H, Nq, Nk, d, code)
+    if workspace is None:
+        workspace = _alloc_workspace(need, dev)
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    st = lib.fa_bwd_ex(_ptr(Q), _ptr(K), _ptr(V), None if bias is None else _ptr(bias), sb, sh, sq,
+                       float(dropout_p), int(seed), int(offset), _ptr(O), _ptr(L), _ptr(dO),
+                       _ptr(dQ), _ptr(dK), _ptr(dV), B, H, Nq, Nk, d, float(scale),
+                       int(bool(causal)), code, _ptr(workspace), ws_bytes,
+                       _stream_handle(dev, stream))
+    if st != FA_OK:
+        raise FAError(st, "fa_bwd_ex")
+    return dQ, dK, dV
+
+
+def forward(Q, K, V, scale=None, causal=False, num_splits=0, stream=None, bias=None,
+            dropout_p=0.0, seed=0, offset=0):
+    """Allocate O, L and run ``fa_fwd`` (``fa_fwd_bias`` with a bias, ``fa_fwd_ex``
+    with dropout).  Returns (O, L)."""
     torch = _torch()
     B, H, Nq, d = Q.shape
     if scale is None:
         scale = 1.0 / math.sqrt(d)
     O = torch.empty_like(Q)
     L = torch.empty((B, H, Nq), dtype=torch.float32, device=Q.device)
+    if dropout_p:
+        return fa_fwd_ex(Q, K, V, O, L, scale, causal, bias=bias, dropout_p=dropout_p, seed=seed,
+                         offset=offset, stream=stream)
     if bias is not None:
         return fa_fwd_bias(Q, K, V, bias, O, L, scale, causal, stream=stream)
     return fa_fwd(Q, K, V, O, L, scale, causal, num_splits=num_splits, stream=stream)
 
 
-def backward(Q, K, V, O, L, dO, scale=None, causal=False, stream=None, bias=None):
-    """Allocate dQ, dK, dV and run ``fa_bwd``.  Returns (dQ, dK, dV)."""
+def backward(Q, K, V, O, L, dO, scale=None, causal=False, stream=None, bias=None, dropout_p=0.0,
+             seed=0, offset=0):
+    """Allocate dQ, dK, dV and run ``fa_bwd`` (or the bias / dropout entry point
+    matching the forward call).  Returns (dQ, dK, dV)."""
     torch = _torch()
     d = Q.shape[-1]
     if scale is None:
@@ -288,6 +363,9 @@ def backward(Q, K, V, O, L, dO, scale=None, causal=False, stream=None, bias=None
     dQ = torch.empty_like(Q)
     dK = torch.empty_like(K)
     dV = torch.empty_like(V)
+    if dropout_p:
+        return fa_bwd_ex(Q, K, V, O, L, dO, dQ, dK, dV, scale, causal, bias=bias,
+                         dropout_p=dropout_p, seed=seed, offset=offset, stream=stream)
     if bias is not None:
         return fa_bwd_bias(Q, K, V, bias, O, L, dO, dQ, dK, dV, scale, causal, stream=stream)
     return fa_bwd(Q, K, V, O, L, dO, dQ, dK, dV, scale, causal, stream=stream)

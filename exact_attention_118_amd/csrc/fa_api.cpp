@@ -140,20 +140,45 @@ fa_status check_bias(const void* bias, long long sb, long long sh, long long sq,
   return FA_OK;
 }
 
-fa_status fwd_impl(const void* Q, const void* K, const void* V, const fa::BiasArgs& bias, void* O,
+// Dropout probability p -> keep threshold T = round((1 - p) * 256) (ties to
+// even, in double): a score is kept iff its random byte is below T, and kept
+// probabilities are scaled by 256 / T.  T = 256 (p below 1/512) keeps every
+// score, which is the path without dropout.
+fa_status make_dropout(float p, unsigned long long seed, unsigned offset, fa::DropArgs* out) {
+  if (!(p >= 0.f && p < 1.f)) return FA_ERR_UNSUPPORTED;
+  const int t = (int)std::nearbyint((1.0 - (double)p) * 256.0);
+  if (t < 1) return FA_ERR_UNSUPPORTED;
+  fa::DropArgs d;
+  d.on = t < 256;
+  d.seed_lo = (unsigned)(seed & 0xFFFFFFFFull);
+  d.seed_hi = (unsigned)(seed >> 32);
+  d.offset = offset;
+  d.thresh = (unsigned)t;
+  d.inv_keep = (float)(256.0 / t);
+  *out = d;
+  return FA_OK;
+}
+
+// The forward pass behind every forward entry point; num_splits as fa_fwd
+// takes it, or -1 for the tiled path only (the bias and dropout entry points).
+fa_status fwd_impl(const void* Q, const void* K, const void* V, const fa::BiasArgs& bias,
+                   const fa::DropArgs& drop, void* O,
                    float* L, int B, int H, int Nq, int Nk, int d, float scale, int causal,
                    fa_dtype dtype, int num_splits, void* workspace, size_t workspace_bytes,
                    void* stream) {
   fa_status st = check_dims(B, H, Nq, Nk, d, scale, causal, dtype);
   if (st != FA_OK) return st;
-  if (num_splits < 0) return FA_ERR_UNSUPPORTED;
   if ((long long)B * H * Nq == 0) return FA_OK;
   if (!Q || !K || !V || !O || !L) return FA_ERR_NULL;
   if (!aligned(Q) || !aligned(K) || !aligned(V) || !aligned(O) || !aligned(L)) return FA_ERR_ALIGN;
-  const int splits = bias.ptr ? 0 : choose_splits(B, H, Nq, Nk, dtype, num_splits);
+  // num_splits < 0 here: the tiled path only (the bias and dropout entry points)
+  const int splits = (num_splits < 0 || bias.ptr || drop.on)
+                         ? 0
+                         : choose_splits(B, H, Nq, Nk, dtype, num_splits);
   if (splits < 0) return FA_ERR_UNSUPPORTED;
   fa::FwdArgs a{Q, K, V, O, L, B, H, Nq, Nk, d, scale, causal != 0};
   a.bias = bias;
+  a.drop = drop;
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
   hipError_t e;
   if (splits > 0) {
@@ -176,7 +201,7 @@ fa_status fwd_impl(const void* Q, const void* K, const void* V, const fa::BiasAr
 }
 
 fa_status bwd_impl(const void* Q, const void* K, const void* V, const fa::BiasArgs& bias,
-                   const void* O, const float* L, const void* dO, void* dQ, void* dK, void* dV,
+                   const fa::DropArgs& drop, const void* O, const float* L, const void* dO, void* dQ, void* dK, void* dV,
                    int B, int H, int Nq, int Nk, int d, float scale, int causal, fa_dtype dtype,
                    void* workspace, size_t workspace_bytes, void* stream, int stages) {
   if (stages <= 0 || stages > FA_BWD_ALL) return FA_ERR_UNSUPPORTED;
@@ -193,6 +218,7 @@ fa_status bwd_impl(const void* Q, const void* K, const void* V, const fa::BiasAr
   fa::BwdArgs a{Q, K, V, O, L, dO, dQ, dK, dV, B, H, Nq, Nk, d, scale, causal != 0,
                 nullptr};
   a.bias = bias;
+  a.drop = drop;
   if (Nq > 0) a.LD = static_cast<float*>(workspace);
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
   const hipError_t e =
@@ -209,7 +235,12 @@ extern "C" {
 fa_status fa_fwd(const void* Q, const void* K, const void* V, void* O, float* L, int B, int H,
                  int Nq, int Nk, int d, float scale, int causal, fa_dtype dtype, int num_splits,
                  void* workspace, size_t workspace_bytes, void* stream) {
-  return fwd_impl(Q, K, V, fa::BiasArgs{}, O, L, B, H, Nq, Nk, d, scale, causal, dtype, num_splits,
+  if (num_splits < 0) {
+    const fa_status st = check_dims(B, H, Nq, Nk, d, scale, causal, dtype);
+    return st != FA_OK ? st : FA_ERR_UNSUPPORTED;
+  }
+  return fwd_impl(Q, K, V, fa::BiasArgs{}, fa::DropArgs{}, O, L, B, H, Nq, Nk, d, scale, causal,
+                  dtype, num_splits,
                   workspace, workspace_bytes, stream);
 }
 
@@ -227,7 +258,8 @@ fa_status fa_fwd_bias(const void* Q, const void* K, const void* V, const void* b
   b.sb = bias_sb;
   b.sh = bias_sh;
   b.sq = bias_sq;
-  return fwd_impl(Q, K, V, b, O, L, B, H, Nq, Nk, d, scale, causal, dtype, 1, nullptr, 0, stream);
+  return fwd_impl(Q, K, V, b, fa::DropArgs{}, O, L, B, H, Nq, Nk, d, scale, causal, dtype, -1,
+                  nullptr, 0, stream);
 }
 
 fa_status fa_bwd_bias(const void* Q, const void* K, const void* V, const void* bias,
@@ -238,8 +270,8 @@ fa_status fa_bwd_bias(const void* Q, const void* K, const void* V, const void* b
   fa_status st = check_dims(B, H, Nq, Nk, d, scale, causal, dtype);
   if (st != FA_OK) return st;
   if ((long long)B * H == 0 || Nq == 0) {
-    return bwd_impl(Q, K, V, fa::BiasArgs{}, O, L, dO, dQ, dK, dV, B, H, Nq, Nk, d, scale, causal,
-                    dtype, workspace, workspace_bytes, stream, FA_BWD_ALL);
+    return bwd_impl(Q, K, V, fa::BiasArgs{}, fa::DropArgs{}, O, L, dO, dQ, dK, dV, B, H, Nq, Nk,
+                    d, scale, causal, dtype, workspace, workspace_bytes, stream, FA_BWD_ALL);
   }
   st = check_bias(bias, bias_sb, bias_sh, bias_sq, Nq, Nk);
   if (st != FA_OK) return st;
@@ -248,7 +280,54 @@ fa_status fa_bwd_bias(const void* Q, const void* K, const void* V, const void* b
   b.sb = bias_sb;
   b.sh = bias_sh;
   b.sq = bias_sq;
-  return bwd_impl(Q, K, V, b, O, L, dO, dQ, dK, dV, B, H, Nq, Nk, d, scale, causal, dtype,
+  return bwd_impl(Q, K, V, b, fa::DropArgs{}, O, L, dO, dQ, dK, dV, B, H, Nq, Nk, d, scale,
+                  causal, dtype, workspace, workspace_bytes, stream, FA_BWD_ALL);
+}
+
+fa_status fa_fwd_ex(const void* Q, const void* K, const void* V, const void* bias,
+                    long long bias_sb, long long bias_sh, long long bias_sq, float dropout_p,
+                    unsigned long long seed, unsigned int offset, void* O, float* L, int B, int H,
+                    int Nq, int Nk, int d, float scale, int causal, fa_dtype dtype, void* stream) {
+  fa_status st = check_dims(B, H, Nq, Nk, d, scale, causal, dtype);
+  if (st != FA_OK) return st;
+  fa::DropArgs dr;
+  st = make_dropout(dropout_p, seed, offset, &dr);
+  if (st != FA_OK) return st;
+  if ((long long)B * H * Nq == 0) return FA_OK;
+  fa::BiasArgs b;
+  if (bias) {
+    st = check_bias(bias, bias_sb, bias_sh, bias_sq, Nq, Nk);
+    if (st != FA_OK) return st;
+    b.ptr = bias;
+    b.sb = bias_sb;
+    b.sh = bias_sh;
+    b.sq = bias_sq;
+  }
+  return fwd_impl(Q, K, V, b, dr, O, L, B, H, Nq, Nk, d, scale, causal, dtype, -1, nullptr, 0,
+                  stream);
+}
+
+fa_status fa_bwd_ex(const void* Q, const void* K, const void* V, const void* bias,
+                    long long bias_sb, long long bias_sh, long long bias_sq, float dropout_p,
+                    unsigned long long seed, unsigned int offset, const void* O, const float* L,
+                    const void* dO, void* dQ, void* dK, void* dV, int B, int H, int Nq, int Nk,
+                    int d, float scale, int causal, fa_dtype dtype, void* workspace,
+                    size_t workspace_bytes, void* stream) {
+  fa_status st = check_dims(B, H, Nq, Nk, d, scale, causal, dtype);
+  if (st != FA_OK) return st;
+  fa::DropArgs dr;
+  st = make_dropout(dropout_p, seed, offset, &dr);
+  if (st != FA_OK) return st;
+  fa::BiasArgs b;
+  if (bias && (long long)B * H > 0 && Nq > 0) {
+    st = check_bias(bias, bias_sb, bias_sh, bias_sq, Nq, Nk);
+    if (st != FA_OK) return st;
+    b.ptr = bias;
+    b.sb = bias_sb;
+    b.sh = bias_sh;
+    b.sq = bias_sq;
+  }
+  return bwd_impl(Q, K, V, b, dr, O, L, dO, dQ, dK, dV, B, H, Nq, Nk, d, scale, causal, dtype,
                   workspace, workspace_bytes, stream, FA_BWD_ALL);
 }
 
@@ -264,8 +343,8 @@ fa_status fa_bwd_stages(const void* Q, const void* K, const void* V, const void*
                         const float* L, const void* dO, void* dQ, void* dK, void* dV, int B,
                         int H, int Nq, int Nk, int d, float scale, int causal, fa_dtype dtype,
                         void* workspace, size_t workspace_bytes, void* stream, int stages) {
-  return bwd_impl(Q, K, V, fa::BiasArgs{}, O, L, dO, dQ, dK, dV, B, H, Nq, Nk, d, scale, causal,
-                  dtype, workspace, workspace_bytes, stream, stages);
+  return bwd_impl(Q, K, V, fa::BiasArgs{}, fa::DropArgs{}, O, L, dO, dQ, dK, dV, B, H, Nq, Nk, d,
+                  scale, causal, dtype, workspace, workspace_bytes, stream, stages);
 }
 
 }  // extern "C"

@@ -90,12 +90,12 @@ constexpr int kKvBR = 32;   // query rows per inner iteration
 constexpr int kKvWaves = 8;
 constexpr int kKvThreads = kKvWaves * 64;
 
-template <typename T, int D, bool CAUSAL, bool BIAS>
+template <typename T, int D, bool CAUSAL, bool BIAS, bool DROP>
 __global__ __launch_bounds__(kKvThreads, 1) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void bwd_dkdv_kernel(const T* __restrict__ Q, const T* __restrict__ K, const T* __restrict__ V,
                      const T* __restrict__ dO, const float* __restrict__ LD, T* __restrict__ dK,
                      T* __restrict__ dV, int Nq, int Nk, int nkt, int BH, int hpx, float c,
-                     float scale, int off, BiasDev bias) {
+                     float scale, int off, BiasDev bias, DropDev drop) {
   typedef typename Vec<T>::x8 T8;
   typedef typename Vec<T>::x4 T4;
   constexpr int BC = kKvBC, BR = kKvBR;
@@ -294,6 +294,12 @@ void bwd_dkdv_kernel(const T* __restrict__ Q, const T* __restrict__ K, const T* 
       // probabilities, then dS and both conversions to T.
       T8 pf[2], dsf[2];
       float pp[2];
+      // Dropout (DROP): byte r of rbk[g] is the random byte of row
+      // qi0 + 8g + half*4 + r and key mykey.  P times the mask goes into dV
+      // (1 / keep-probability applied at the end); dP is masked and scaled
+      // before dS = P (dP - D).
+      unsigned rbk[4];
+      if constexpr (DROP) drop_bytes_keys(rbk, drop, bh, mykey, qi0 + half * 4, lane);
       auto pds_p = [&](int i) {
         const int ql = (i >> 2) * 8 + half * 4 + (i & 3);  // rows ql, ql + 1
         const float2 a = *(const float2*)(tLD + 2 * ql);
@@ -304,10 +310,19 @@ void bwd_dkdv_kernel(const T* __restrict__ Q, const T* __restrict__ K, const T* 
       };
       auto pds_ds = [&](int i, float2 dd) {
         const int kc = i >> 3, e = i & 7;
-        pf[kc][e] = (T)pp[0];
-        pf[kc][e + 1] = (T)pp[1];
-        dsf[kc][e] = (T)(pp[0] * (dpacc[i] - dd.x));
-        dsf[kc][e + 1] = (T)(pp[1] * (dpacc[i + 1] - dd.y));
+        if constexpr (DROP) {
+          const bool k0 = drop_keep(rbk[i >> 2], i & 3, drop.thresh);
+          const bool k1 = drop_keep(rbk[i >> 2], (i + 1) & 3, drop.thresh);
+          pf[kc][e] = (T)(k0 ? pp[0] : 0.f);
+          pf[kc][e + 1] = (T)(k1 ? pp[1] : 0.f);
+          dsf[kc][e] = (T)(pp[0] * ((k0 ? dpacc[i] * drop.inv_keep : 0.f) - dd.x));
+          dsf[kc][e + 1] = (T)(pp[1] * ((k1 ? dpacc[i + 1] * drop.inv_keep : 0.f) - dd.y));
+        } else {
+          pf[kc][e] = (T)pp[0];
+          pf[kc][e + 1] = (T)pp[1];
+          dsf[kc][e] = (T)(pp[0] * (dpacc[i] - dd.x));
+          dsf[kc][e + 1] = (T)(pp[1] * (dpacc[i + 1] - dd.y));
+        }
       };
       // dV^T += dO^T P and dK^T += Q^T dS over the 16 rows of chunk kc
       // (2 * NNT MFMAs, A operands by transpose reads); with `overlap`, the
@@ -369,7 +384,9 @@ void bwd_dkdv_kernel(const T* __restrict__ Q, const T* __restrict__ K, const T* 
     if (it + 1 < nloop) block_step(1, it + 1);
   }
 
-  // Epilogue: dK = scale * dK_acc, dV = dV_acc; lane holds key mykey.
+  // Epilogue: dK = scale * dK_acc, dV = dV_acc (times 1 / keep-probability
+  // with dropout); lane holds key mykey.
+  const float vscale = DROP ? drop.inv_keep : 1.f;
   if (mykey < Nk) {
     T* dkrow = dK + kbase + (size_t)mykey * D;
     T* dvrow = dV + kbase + (size_t)mykey * D;
@@ -381,7 +398,7 @@ void bwd_dkdv_kernel(const T* __restrict__ Q, const T* __restrict__ K, const T* 
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
           vk[e] = (T)(dkacc[nt][gg * 4 + e] * scale);
-          vv[e] = (T)(dvacc[nt][gg * 4 + e]);
+          vv[e] = (T)(dvacc[nt][gg * 4 + e] * vscale);
         }
         *(T4*)(dkrow + nt * 32 + gg * 8 + half * 4) = vk;
         *(T4*)(dvrow + nt * 32 + gg * 8 + half * 4) = vv;
@@ -395,11 +412,12 @@ constexpr int kDqBR = 128;  // query rows per workgroup
 constexpr int kDqBC = 64;   // keys per K/V tile
 constexpr int kDqThreads = 256;
 
-template <typename T, int D, bool CAUSAL, bool BIAS>
+template <typename T, int D, bool CAUSAL, bool BIAS, bool DROP>
 __global__ __launch_bounds__(kDqThreads, 2) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void bwd_dq_kernel(const T* __restrict__ Q, const T* __restrict__ K, const T* __restrict__ V,
                    const T* __restrict__ dO, const float* __restrict__ LD, T* __restrict__ dQ,
-                   int Nq, int Nk, int nqt, float c, float scale, int off, BiasDev bias) {
+                   int Nq, int Nk, int nqt, float c, float scale, int off, BiasDev bias,
+                   DropDev drop) {
   typedef typename Vec<T>::x8 T8;
   typedef typename Vec<T>::x4 T4;
   constexpr int BR = kDqBR, BC = kDqBC;
@@ -532,9 +550,17 @@ void bwd_dq_kernel(const T* __restrict__ Q, const T* __restrict__ K, const T* __
               sacc[mt][g * 4 + e] = fmaf((float)bb[mt * 4 + g][e], bias.inv_scale, sacc[mt][g * 4 + e]);
         }
       };
+      // Dropout (DROP): byte e of rb[mt][c] is the random byte of row qrow
+      // and key k0 + mt*32 + c*8 + half*4 + e; dP is masked and scaled before
+      // dS = P (dP - D).
+      unsigned rb[2][4];
+      if constexpr (DROP) drop_bytes_rows(rb, drop, bh, qrow, k0 + half * 4, lane);
       auto ds_elem = [&](int mt, int i) {
         const float p = fast_exp2(fmaf(sacc[mt][i], c, -l2));
-        dsf[mt * 2 + (i >> 3)][i & 7] = (T)(p * (dpacc[mt][i] - drow));
+        float dp = dpacc[mt][i];
+        if constexpr (DROP)
+          dp = drop_keep(rb[mt][i >> 2], i & 3, drop.thresh) ? dp * drop.inv_keep : 0.f;
+        dsf[mt * 2 + (i >> 3)][i & 7] = (T)(p * (dp - drow));
       };
       // Keys past the end and, causal, keys after the row's diagonal get
       // score -inf, hence P = 0 and dS = 0; only tiles that cross the
@@ -637,12 +663,12 @@ void bwd_dq_kernel(const T* __restrict__ Q, const T* __restrict__ K, const T* __
 // thread per query row for dQ; plain fp32 FMAs and expf.
 constexpr int kF32BT = 64;
 
-template <int D, bool CAUSAL>
+template <int D, bool CAUSAL, bool DROP>
 __global__ __launch_bounds__(kF32BT) void bwd_dkdv_f32_kernel(
     const float* __restrict__ Q, const float* __restrict__ K, const float* __restrict__ V,
     const float* __restrict__ L, const float* __restrict__ dO, const float* __restrict__ LD,
     float* __restrict__ dK, float* __restrict__ dV, int Nq, int Nk, int nkt, float scale,
-    int off, BiasDev bias) {
+    int off, BiasDev bias, DropDev drop) {
   __shared__ float sq[D], sdo[D];
   const int bh = blockIdx.x / nkt;
   const int kt = blockIdx.x - bh * nkt;
@@ -679,10 +705,15 @@ __global__ __launch_bounds__(kF32BT) void bwd_dkdv_f32_kernel(
     }
     const float b = bias_h ? bias_h[(long long)q * bias.sq + key] : 0.f;
     const float p = expf(s * scale + b - L[(size_t)bh * Nq + q]);
-    const float ds = p * (dp - LD[2 * ((size_t)bh * Nq + q) + 1]);
+    // Dropout (DROP): the kept probability times 1/keep feeds dV and the
+    // masked, scaled dP feeds dS.
+    const bool kept = !DROP || drop_byte(drop, bh, q, key) < drop.thresh;
+    const float pd = kept ? (DROP ? p * drop.inv_keep : p) : 0.f;
+    const float dpd = kept ? (DROP ? dp * drop.inv_keep : dp) : 0.f;
+    const float ds = p * (dpd - LD[2 * ((size_t)bh * Nq + q) + 1]);
 #pragma unroll
     for (int e = 0; e < D; ++e) {
-      dv[e] = fmaf(p, sdo[e], dv[e]);
+      dv[e] = fmaf(pd, sdo[e], dv[e]);
       dk[e] = fmaf(ds, sq[e], dk[e]);
     }
   }
@@ -695,11 +726,12 @@ __global__ __launch_bounds__(kF32BT) void bwd_dkdv_f32_kernel(
   }
 }
 
-template <int D, bool CAUSAL>
+template <int D, bool CAUSAL, bool DROP>
 __global__ __launch_bounds__(kF32BT) void bwd_dq_f32_kernel(
     const float* __restrict__ Q, const float* __restrict__ K, const float* __restrict__ V,
     const float* __restrict__ L, const float* __restrict__ dO, const float* __restrict__ LD,
-    float* __restrict__ dQ, int Nq, int Nk, int nqt, float scale, int off, BiasDev bias) {
+    float* __restrict__ dQ, int Nq, int Nk, int nqt, float scale, int off, BiasDev bias,
+    DropDev drop) {
   __shared__ float sk[D], sv[D];
   const int bh = blockIdx.x / nqt;
   const int qt = blockIdx.x - bh * nqt;
@@ -737,7 +769,8 @@ __global__ __launch_bounds__(kF32BT) void bwd_dq_f32_kernel(
       dp = fmaf(dov[e], sv[e], dp);
     }
     const float p = expf(s * scale + (brow ? brow[key] : 0.f) - lq);
-    const float ds = p * (dp - dq_aux);
+    const bool kept = !DROP || drop_byte(drop, bh, q, key) < drop.thresh;
+    const float ds = p * ((kept ? (DROP ? dp * drop.inv_keep : dp) : 0.f) - dq_aux);
 #pragma unroll
     for (int e = 0; e < D; ++e) dq[e] = fmaf(ds, sk[e], dq[e]);
   }
@@ -762,7 +795,11 @@ hipError_t launch_pre(const BwdArgs& a, hipStream_t s) {
 
 namespace {
 
-template <typename T, bool BIAS>
+DropDev drop_dev(const DropArgs& d) {
+  return DropDev{d.seed_lo, d.seed_hi, d.offset, d.on ? d.thresh : 256u, d.on ? d.inv_keep : 1.f};
+}
+
+template <typename T, bool BIAS, bool DROP>
 hipError_t launch_bwd_mfma(const BwdArgs& a, int stages, hipStream_t s) {
   const int BH = a.B * a.H;
   const float c = a.scale * kLog2e;
@@ -772,6 +809,7 @@ hipError_t launch_bwd_mfma(const BwdArgs& a, int stages, hipStream_t s) {
   const T* V = (const T*)a.V;
   const T* dO = (const T*)a.dO;
   const BiasDev bias{a.bias.ptr, a.bias.sb, a.bias.sh, a.bias.sq, a.H, 1.f / a.scale};
+  const DropDev drop = drop_dev(a.drop);
   if (stages & 1) {
     const hipError_t e = (a.d == 128) ? launch_pre<128, T>(a, s) : launch_pre<64, T>(a, s);
     if (e != hipSuccess) return e;
@@ -780,10 +818,10 @@ hipError_t launch_bwd_mfma(const BwdArgs& a, int stages, hipStream_t s) {
     const int nkt = (a.Nk + kKvBC - 1) / kKvBC;
     const int nblocks = nkt * BH;
     const int hpx = (BH % kNumXcd == 0) ? BH / kNumXcd : 0;
-#define FA_DKDV_LAUNCH(DD, CC)                                                                  \
-  hipLaunchKernelGGL((bwd_dkdv_kernel<T, DD, CC, BIAS>), dim3(nblocks), dim3(kKvThreads), 0, s, \
-                     Q, K, V, dO, a.LD, (T*)a.dK, (T*)a.dV, a.Nq, a.Nk, nkt, BH, hpx, c, a.scale, \
-                     off, bias)
+#define FA_DKDV_LAUNCH(DD, CC)                                                                 \
+  hipLaunchKernelGGL((bwd_dkdv_kernel<T, DD, CC, BIAS, DROP>), dim3(nblocks), dim3(kKvThreads), \
+                     0, s, Q, K, V, dO, a.LD, (T*)a.dK, (T*)a.dV, a.Nq, a.Nk, nkt, BH, hpx, c,  \
+                     a.scale, off, bias, drop)
     if (a.d == 128) {
       if (a.causal) FA_DKDV_LAUNCH(128, true); else FA_DKDV_LAUNCH(128, false);
     } else {
@@ -796,9 +834,9 @@ hipError_t launch_bwd_mfma(const BwdArgs& a, int stages, hipStream_t s) {
   if ((stages & 4) && a.Nq > 0) {
     const int nqt = (a.Nq + kDqBR - 1) / kDqBR;
     const int nblocks = (a.causal ? (nqt + 1) / 2 : nqt) * BH;  // causal: query tile pairs
-#define FA_DQ_LAUNCH(DD, CC)                                                                    \
-  hipLaunchKernelGGL((bwd_dq_kernel<T, DD, CC, BIAS>), dim3(nblocks), dim3(kDqThreads), 0, s, Q, \
-                     K, V, dO, a.LD, (T*)a.dQ, a.Nq, a.Nk, nqt, c, a.scale, off, bias)
+#define FA_DQ_LAUNCH(DD, CC)                                                                   \
+  hipLaunchKernelGGL((bwd_dq_kernel<T, DD, CC, BIAS, DROP>), dim3(nblocks), dim3(kDqThreads), 0, \
+                     s, Q, K, V, dO, a.LD, (T*)a.dQ, a.Nq, a.Nk, nqt, c, a.scale, off, bias, drop)
     if (a.d == 128) {
       if (a.causal) FA_DQ_LAUNCH(128, true); else FA_DQ_LAUNCH(128, false);
     } else {
@@ -810,15 +848,22 @@ hipError_t launch_bwd_mfma(const BwdArgs& a, int stages, hipStream_t s) {
   return hipSuccess;
 }
 
+template <typename T>
+hipError_t launch_bwd_typed(const BwdArgs& a, int stages, hipStream_t s) {
+  if (a.drop.on)
+    return a.bias.ptr ? launch_bwd_mfma<T, true, true>(a, stages, s)
+                      : launch_bwd_mfma<T, false, true>(a, stages, s);
+  return a.bias.ptr ? launch_bwd_mfma<T, true, false>(a, stages, s)
+                    : launch_bwd_mfma<T, false, false>(a, stages, s);
+}
+
 }  // namespace
 
 hipError_t launch_bwd_bf16(const BwdArgs& a, int stages, hipStream_t s) {
-  return a.bias.ptr ? launch_bwd_mfma<bf16, true>(a, stages, s)
-                    : launch_bwd_mfma<bf16, false>(a, stages, s);
+  return launch_bwd_typed<bf16>(a, stages, s);
 }
 hipError_t launch_bwd_f16(const BwdArgs& a, int stages, hipStream_t s) {
-  return a.bias.ptr ? launch_bwd_mfma<f16, true>(a, stages, s)
-                    : launch_bwd_mfma<f16, false>(a, stages, s);
+  return launch_bwd_typed<f16>(a, stages, s);
 }
 
 hipError_t launch_bwd_f32(const BwdArgs& a, int stages, hipStream_t s) {
@@ -835,11 +880,19 @@ hipError_t launch_bwd_f32(const BwdArgs& a, int stages, hipStream_t s) {
   const float* V = (const float*)a.V;
   const float* dO = (const float*)a.dO;
   const BiasDev bias{a.bias.ptr, a.bias.sb, a.bias.sh, a.bias.sq, a.H, 1.f / a.scale};
+  const DropDev drop = drop_dev(a.drop);
   if ((stages & 2) && nkt > 0) {
-#define FA_DKDV32_LAUNCH(DD, CC)                                                                \
-  hipLaunchKernelGGL((bwd_dkdv_f32_kernel<DD, CC>), dim3(nkt * BH), dim3(kF32BT), 0, s, Q, K, V, \
-                     a.L, dO, a.LD, (float*)a.dK, (float*)a.dV, a.Nq, a.Nk, nkt, a.scale, off,  \
-                     bias)
+#define FA_DKDV32_LAUNCH(DD, CC)                                                             \
+  do {                                                                                       \
+    if (a.drop.on)                                                                           \
+      hipLaunchKernelGGL((bwd_dkdv_f32_kernel<DD, CC, true>), dim3(nkt * BH), dim3(kF32BT), 0, \
+                         s, Q, K, V, a.L, dO, a.LD, (float*)a.dK, (float*)a.dV, a.Nq, a.Nk,  \
+                         nkt, a.scale, off, bias, drop);                                     \
+    else                                                                                     \
+      hipLaunchKernelGGL((bwd_dkdv_f32_kernel<DD, CC, false>), dim3(nkt * BH), dim3(kF32BT),  \
+                         0, s, Q, K, V, a.L, dO, a.LD, (float*)a.dK, (float*)a.dV, a.Nq,     \
+                         a.Nk, nkt, a.scale, off, bias, drop);                               \
+  } while (0)
     if (a.d == 128) {
       if (a.causal) FA_DKDV32_LAUNCH(128, true); else FA_DKDV32_LAUNCH(128, false);
     } else {
@@ -850,9 +903,17 @@ hipError_t launch_bwd_f32(const BwdArgs& a, int stages, hipStream_t s) {
     if (e != hipSuccess) return e;
   }
   if ((stages & 4) && nqt > 0) {
-#define FA_DQ32_LAUNCH(DD, CC)                                                                \
-  hipLaunchKernelGGL((bwd_dq_f32_kernel<DD, CC>), dim3(nqt * BH), dim3(kF32BT), 0, s, Q, K, V, \
-                     a.L, dO, a.LD, (float*)a.dQ, a.Nq, a.Nk, nqt, a.scale, off, bias)
+#define FA_DQ32_LAUNCH(DD, CC)                                                               \
+  do {                                                                                       \
+    if (a.drop.on)                                                                           \
+      hipLaunchKernelGGL((bwd_dq_f32_kernel<DD, CC, true>), dim3(nqt * BH), dim3(kF32BT), 0,  \
+                         s, Q, K, V, a.L, dO, a.LD, (float*)a.dQ, a.Nq, a.Nk, nqt, a.scale,  \
+                         off, bias, drop);                                                   \
+    else                                                                                     \
+      hipLaunchKernelGGL((bwd_dq_f32_kernel<DD, CC, false>), dim3(nqt * BH), dim3(kF32BT), 0, \
+                         s, Q, K, V, a.L, dO, a.LD, (float*)a.dQ, a.Nq, a.Nk, nqt, a.scale,  \
+                         off, bias, drop);                                                   \
+  } while (0)
     if (a.d == 128) {
       if (a.causal) FA_DQ32_LAUNCH(128, true); else FA_DQ32_LAUNCH(128, false);
     } else {

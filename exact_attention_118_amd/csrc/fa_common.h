@@ -270,6 +270,129 @@ struct BiasReader {
   }
 };
 
+// Dropout on the normalised probabilities (the V1 algorithm in the 51CTO
+// FlashAttention V1/V2 notes, "FlashAttention V2 相比 V1 有哪些改进", applies it
+// inside the loop).  The bits come from Philox4x32-10 (Salmon, Moraes, Dror
+// and Shaw, "Parallel Random Numbers: As Easy as 1, 2, 3", SC 2011, section
+// 3.2), one call per block of 4 query rows x 4 keys: key (seed_lo, seed_hi),
+// counter (key / 4, row / 4, b*H + h, offset); word row % 4 holds the block's
+// row and byte key % 4 of that word the score.  A score is kept iff its byte
+// is below thresh (1..255), and kept probabilities are scaled by inv_keep =
+// 256 / thresh.
+struct DropDev {
+  unsigned seed_lo, seed_hi, offset, thresh;
+  float inv_keep;
+};
+
+// Philox4x32-10 of counter x, in place.  Per round: the two products
+// M0 * x0 and M1 * x2 (32 x 32 -> 64 bits); the new words are (hi1 ^ x1 ^ k0,
+// lo1, hi0 ^ x3 ^ k1, lo0); the round key then advances by the Weyl
+// constants.  k0, k1 are wave-uniform, so the key schedule is scalar work.
+__device__ __forceinline__ void philox4x32_10(unsigned (&x)[4], unsigned k0, unsigned k1) {
+#pragma unroll
+  for (int r = 0; r < 10; ++r) {
+    const unsigned long long p0 = (unsigned long long)0xD2511F53u * x[0];
+    const unsigned long long p1 = (unsigned long long)0xCD9E8D57u * x[2];
+    const unsigned hi0 = (unsigned)(p0 >> 32), lo0 = (unsigned)p0;
+    const unsigned hi1 = (unsigned)(p1 >> 32), lo1 = (unsigned)p1;
+    x[0] = hi1 ^ x[1] ^ k0;
+    x[1] = lo1;
+    x[2] = hi0 ^ x[3] ^ k1;
+    x[3] = lo0;
+    k0 += 0x9E3779B9u;
+    k1 += 0xBB67AE85u;
+  }
+}
+
+// 4 x 4 transpose of dwords across the 4 lanes of a quad (lanes 4a .. 4a+3):
+// on entry lane t holds x[0..3]; on exit x[c] of lane t is what x[t] of lane
+// c held.  Two butterfly stages of quad-permute moves (DPP) and selects.
+__device__ __forceinline__ unsigned quad_xor1(unsigned v) {
+  return (unsigned)__builtin_amdgcn_update_dpp(0, (int)v, 0xB1, 0xF, 0xF, false);  // [1,0,3,2]
+}
+__device__ __forceinline__ unsigned quad_xor2(unsigned v) {
+  return (unsigned)__builtin_amdgcn_update_dpp(0, (int)v, 0x4E, 0xF, 0xF, false);  // [2,3,0,1]
+}
+__device__ __forceinline__ void quad_transpose(unsigned (&x)[4], int lane) {
+  const bool odd = lane & 1, upper = lane & 2;
+  const unsigned a0 = quad_xor1(x[1]), a1 = quad_xor1(x[0]);
+  const unsigned a2 = quad_xor1(x[3]), a3 = quad_xor1(x[2]);
+  x[0] = odd ? a0 : x[0];
+  x[1] = odd ? x[1] : a1;
+  x[2] = odd ? a2 : x[2];
+  x[3] = odd ? x[3] : a3;
+  const unsigned b0 = quad_xor2(x[2]), b1 = quad_xor2(x[3]);
+  const unsigned b2 = quad_xor2(x[0]), b3 = quad_xor2(x[1]);
+  x[0] = upper ? b0 : x[0];
+  x[1] = upper ? b1 : x[1];
+  x[2] = upper ? x[2] : b2;
+  x[3] = upper ? x[3] : b3;
+}
+
+// 4 x 4 transpose of the bytes of x[0..3] within a lane: byte r of x[e] on
+// exit is byte e of x[r] on entry.
+__device__ __forceinline__ void byte_transpose(unsigned (&x)[4]) {
+  const unsigned a0 = __builtin_amdgcn_perm(x[1], x[0], 0x06020400u);
+  const unsigned a1 = __builtin_amdgcn_perm(x[1], x[0], 0x07030501u);
+  const unsigned a2 = __builtin_amdgcn_perm(x[3], x[2], 0x06020400u);
+  const unsigned a3 = __builtin_amdgcn_perm(x[3], x[2], 0x07030501u);
+  x[0] = __builtin_amdgcn_perm(a2, a0, 0x05040100u);
+  x[1] = __builtin_amdgcn_perm(a3, a1, 0x05040100u);
+  x[2] = __builtin_amdgcn_perm(a2, a0, 0x07060302u);
+  x[3] = __builtin_amdgcn_perm(a3, a1, 0x07060302u);
+}
+
+// Random bytes for a lane that holds query row `row` and keys
+// key0 + s*32 + c*8 + e (s = 0, 1; c, e = 0..3; key0 a multiple of 4), the
+// lanes of its quad holding rows 4a .. 4a+3 and the same keys: each lane
+// makes two of the quad's eight calls, then the quad exchanges words.  On
+// exit byte e of x[s][c] belongs to (row, key0 + s*32 + c*8 + e).
+__device__ __forceinline__ void drop_bytes_rows(unsigned (&x)[2][4], const DropDev& dr, int bh,
+                                                int row, int key0, int lane) {
+  const int t = lane & 3;
+#pragma unroll
+  for (int sblk = 0; sblk < 2; ++sblk) {
+    unsigned w[4] = {(unsigned)(key0 + sblk * 32 + t * 8) >> 2, (unsigned)row >> 2,
+                     (unsigned)bh, dr.offset};
+    philox4x32_10(w, dr.seed_lo, dr.seed_hi);
+    quad_transpose(w, lane);
+#pragma unroll
+    for (int c = 0; c < 4; ++c) x[sblk][c] = w[c];
+  }
+}
+
+// Random bytes for a lane that holds key `key` and query rows
+// row0 + 8g + r (g, r = 0..3; row0 a multiple of 4), the lanes of its quad
+// holding keys 4b .. 4b+3 and the same rows: each lane makes one of the
+// quad's four calls, transposes its bytes, then the quad exchanges words.
+// On exit byte r of x[g] belongs to (row0 + 8g + r, key).
+__device__ __forceinline__ void drop_bytes_keys(unsigned (&x)[4], const DropDev& dr, int bh,
+                                                int key, int row0, int lane) {
+  const int t = lane & 3;
+  x[0] = (unsigned)key >> 2;
+  x[1] = (unsigned)(row0 + 8 * t) >> 2;
+  x[2] = (unsigned)bh;
+  x[3] = dr.offset;
+  philox4x32_10(x, dr.seed_lo, dr.seed_hi);
+  byte_transpose(x);
+  quad_transpose(x, lane);
+}
+
+// The random byte of one score (row, key) of flat head bh, from its own call
+// (the fp32 kernels, which hold one row or one key per thread).
+__device__ __forceinline__ unsigned drop_byte(const DropDev& dr, int bh, int row, int key) {
+  unsigned w[4] = {(unsigned)key >> 2, (unsigned)row >> 2, (unsigned)bh, dr.offset};
+  philox4x32_10(w, dr.seed_lo, dr.seed_hi);
+  const int r = row & 3;
+  const unsigned word = r == 0 ? w[0] : r == 1 ? w[1] : r == 2 ? w[2] : w[3];
+  return (word >> (8 * (key & 3))) & 0xFFu;
+}
+
+// Keep decision for byte b (0..3) of a word of random bytes.
+__device__ __forceinline__ bool drop_keep(unsigned word, int b, unsigned thresh) {
+  return ((word >> (8 * b)) & 0xFFu) < thresh;
+}
+
 // Wait for this wave's outstanding vector-memory operations (including the
 // direct-to-LDS loads above).
 __device__ __forceinline__ void vm_wait_all() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }

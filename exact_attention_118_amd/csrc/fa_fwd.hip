@@ -46,11 +46,11 @@ constexpr int kFwdBC = 64;   // keys per K/V tile
 constexpr int kFwdThreads = 256;
 constexpr float kRescaleSlack = 8.f;  // see the online softmax below
 
-template <typename T, int D, bool CAUSAL, bool BIAS>
+template <typename T, int D, bool CAUSAL, bool BIAS, bool DROP>
 __global__ __launch_bounds__(kFwdThreads, 2) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void fwd_kernel(const T* __restrict__ Q, const T* __restrict__ K, const T* __restrict__ V,
                 T* __restrict__ O, float* __restrict__ L, int Nq, int Nk, int nqt, float c,
-                int off, BiasDev bias) {
+                int off, BiasDev bias, DropDev drop) {
   typedef typename Vec<T>::x8 T8;
   typedef typename Vec<T>::x4 T4;
   constexpr int BR = kFwdBR, BC = kFwdBC;
@@ -261,6 +261,11 @@ void fwd_kernel(const T* __restrict__ Q, const T* __restrict__ K, const T* __res
       static_assert(NPAIR - kPairsA <= 2 * NNT, "late pairs fit before chunk 2 is read");
       T8 pf[4];
       float rs0 = 0.f, rs1 = 0.f;
+      // Dropout (DROP): the random bytes of this lane's 32 scores of tile j;
+      // the row sums take the probabilities before dropout, P V after it
+      // (the 1 / keep-probability factor is applied with 1 / l at the end).
+      unsigned rb[2][4];
+      if constexpr (DROP) drop_bytes_rows(rb, drop, bh, qrow, k0 + half * 4, lane);
       auto prob_pair = [&](int pr) {
         const int el = 2 * pr, kc = el >> 3, e = el & 7;
         const int mt = kc >> 1, i = (kc & 1) * 8 + e;
@@ -268,8 +273,13 @@ void fwd_kernel(const T* __restrict__ Q, const T* __restrict__ K, const T* __res
         const float p1 = fast_exp2(fmaf(scur[mt][i + 1], c, -m_ref));
         rs0 += p0;
         rs1 += p1;
-        pf[kc][e] = (T)p0;
-        pf[kc][e + 1] = (T)p1;
+        if constexpr (DROP) {
+          pf[kc][e] = (T)(drop_keep(rb[mt][i >> 2], i & 3, drop.thresh) ? p0 : 0.f);
+          pf[kc][e + 1] = (T)(drop_keep(rb[mt][i >> 2], (i + 1) & 3, drop.thresh) ? p1 : 0.f);
+        } else {
+          pf[kc][e] = (T)p0;
+          pf[kc][e + 1] = (T)p1;
+        }
         pin(pf[kc]);
         pin(rs0);
         pin(rs1);
@@ -348,10 +358,11 @@ void fwd_kernel(const T* __restrict__ Q, const T* __restrict__ K, const T* __res
       if (j + 1 < ntiles) tile_step(1, j + 1, sB, sA);
     }
 
-    // Epilogue: O = O_acc / l, L = (m + log2 l) * ln 2.
+    // Epilogue: O = O_acc / l (times 1 / keep-probability with dropout),
+    // L = (m + log2 l) * ln 2.
     const float l_tot = l_run + wave_shfl_xor(l_run, 32);
     if (qrow < Nq) {
-      const float inv = 1.f / l_tot;
+      const float inv = (DROP ? drop.inv_keep : 1.f) / l_tot;
       T* orow = O + qbase + (size_t)qrow * D;
 #pragma unroll
       for (int nt = 0; nt < NNT; ++nt)
@@ -373,11 +384,11 @@ void fwd_kernel(const T* __restrict__ Q, const T* __restrict__ K, const T* __res
 constexpr int kF32Rows = 64;
 constexpr int kF32Keys = 16;
 
-template <int D, bool CAUSAL>
+template <int D, bool CAUSAL, bool DROP>
 __global__ __launch_bounds__(kF32Rows) void fwd_f32_kernel(
     const float* __restrict__ Q, const float* __restrict__ K, const float* __restrict__ V,
     float* __restrict__ O, float* __restrict__ L, int Nq, int Nk, int nqt, float scale, int off,
-    BiasDev bias) {
+    BiasDev bias, DropDev drop) {
   __shared__ float sK[kF32Keys][D];
   __shared__ float sV[kF32Keys][D];
   const int bh = blockIdx.x / nqt;
@@ -425,18 +436,32 @@ __global__ __launch_bounds__(kF32Rows) void fwd_f32_kernel(
     l_run *= alpha;
 #pragma unroll
     for (int e = 0; e < D; ++e) o[e] *= alpha;
+    // Dropout (DROP): one Philox call per 4 keys of this row; word row % 4
+    // holds the row's 4 bytes.
+    unsigned rbyte[kF32Keys / 4];
+    if constexpr (DROP) {
+#pragma unroll
+      for (int kb = 0; kb < kF32Keys / 4; ++kb) {
+        unsigned w[4] = {(unsigned)(k0 + 4 * kb) >> 2, (unsigned)row >> 2, (unsigned)bh,
+                         drop.offset};
+        philox4x32_10(w, drop.seed_lo, drop.seed_hi);
+        const int r = row & 3;
+        rbyte[kb] = r == 0 ? w[0] : r == 1 ? w[1] : r == 2 ? w[2] : w[3];
+      }
+    }
 #pragma unroll
     for (int jj = 0; jj < kF32Keys; ++jj) {
       const float p = expf(s[jj] - m_base);
       l_run += p;
+      const float pd = (DROP && !drop_keep(rbyte[jj >> 2], jj & 3, drop.thresh)) ? 0.f : p;
 #pragma unroll
-      for (int e = 0; e < D; ++e) o[e] = fmaf(p, sV[jj][e], o[e]);
+      for (int e = 0; e < D; ++e) o[e] = fmaf(pd, sV[jj][e], o[e]);
     }
     m_run = m_new;
     __syncthreads();
   }
   if (row < Nq) {
-    const float inv = 1.f / l_run;
+    const float inv = (DROP ? drop.inv_keep : 1.f) / l_run;
 #pragma unroll
     for (int e = 0; e < D; ++e) O[qbase + (size_t)row * D + e] = o[e] * inv;
     L[(size_t)bh * Nq + row] = m_run + logf(l_run);
@@ -447,7 +472,11 @@ __global__ __launch_bounds__(kF32Rows) void fwd_f32_kernel(
 
 namespace {
 
-template <typename T, bool BIAS>
+DropDev drop_dev(const DropArgs& d) {
+  return DropDev{d.seed_lo, d.seed_hi, d.offset, d.on ? d.thresh : 256u, d.on ? d.inv_keep : 1.f};
+}
+
+template <typename T, bool BIAS, bool DROP>
 hipError_t launch_fwd_mfma(const FwdArgs& a, hipStream_t s) {
   const int BH = a.B * a.H;
   const int nqt = (a.Nq + kFwdBR - 1) / kFwdBR;
@@ -460,9 +489,10 @@ hipError_t launch_fwd_mfma(const FwdArgs& a, hipStream_t s) {
   const T* V = (const T*)a.V;
   T* O = (T*)a.O;
   const BiasDev bias{a.bias.ptr, a.bias.sb, a.bias.sh, a.bias.sq, a.H, 1.f / a.scale};
+  const DropDev drop = drop_dev(a.drop);
 #define FA_FWD_LAUNCH(DD, CC)                                                                  \
-  hipLaunchKernelGGL((fwd_kernel<T, DD, CC, BIAS>), dim3(nblocks), dim3(kFwdThreads), 0, s, Q, \
-                     K, V, O, a.L, a.Nq, a.Nk, nqt, c, off, bias)
+  hipLaunchKernelGGL((fwd_kernel<T, DD, CC, BIAS, DROP>), dim3(nblocks), dim3(kFwdThreads), 0, \
+                     s, Q, K, V, O, a.L, a.Nq, a.Nk, nqt, c, off, bias, drop)
   if (a.d == 128) {
     if (a.causal) FA_FWD_LAUNCH(128, true); else FA_FWD_LAUNCH(128, false);
   } else {
@@ -472,14 +502,17 @@ hipError_t launch_fwd_mfma(const FwdArgs& a, hipStream_t s) {
   return hipGetLastError();
 }
 
+template <typename T>
+hipError_t launch_fwd_typed(const FwdArgs& a, hipStream_t s) {
+  if (a.drop.on)
+    return a.bias.ptr ? launch_fwd_mfma<T, true, true>(a, s) : launch_fwd_mfma<T, false, true>(a, s);
+  return a.bias.ptr ? launch_fwd_mfma<T, true, false>(a, s) : launch_fwd_mfma<T, false, false>(a, s);
+}
+
 }  // namespace
 
-hipError_t launch_fwd_bf16(const FwdArgs& a, hipStream_t s) {
-  return a.bias.ptr ? launch_fwd_mfma<bf16, true>(a, s) : launch_fwd_mfma<bf16, false>(a, s);
-}
-hipError_t launch_fwd_f16(const FwdArgs& a, hipStream_t s) {
-  return a.bias.ptr ? launch_fwd_mfma<f16, true>(a, s) : launch_fwd_mfma<f16, false>(a, s);
-}
+hipError_t launch_fwd_bf16(const FwdArgs& a, hipStream_t s) { return launch_fwd_typed<bf16>(a, s); }
+hipError_t launch_fwd_f16(const FwdArgs& a, hipStream_t s) { return launch_fwd_typed<f16>(a, s); }
 
 hipError_t launch_fwd_f32(const FwdArgs& a, hipStream_t s) {
   const int BH = a.B * a.H;
@@ -491,9 +524,16 @@ hipError_t launch_fwd_f32(const FwdArgs& a, hipStream_t s) {
   const float* V = (const float*)a.V;
   float* O = (float*)a.O;
   const BiasDev bias{a.bias.ptr, a.bias.sb, a.bias.sh, a.bias.sq, a.H, 1.f / a.scale};
-#define FA_FWD32_LAUNCH(DD, CC)                                                               \
-  hipLaunchKernelGGL((fwd_f32_kernel<DD, CC>), dim3(nblocks), dim3(kF32Rows), 0, s, Q, K, V, O, \
-                     a.L, a.Nq, a.Nk, nqt, a.scale, off, bias)
+  const DropDev drop = drop_dev(a.drop);
+#define FA_FWD32_LAUNCH(DD, CC)                                                              \
+  do {                                                                                       \
+    if (a.drop.on)                                                                           \
+      hipLaunchKernelGGL((fwd_f32_kernel<DD, CC, true>), dim3(nblocks), dim3(kF32Rows), 0, s, \
+                         Q, K, V, O, a.L, a.Nq, a.Nk, nqt, a.scale, off, bias, drop);        \
+    else                                                                                     \
+      hipLaunchKernelGGL((fwd_f32_kernel<DD, CC, false>), dim3(nblocks), dim3(kF32Rows), 0,   \
+                         s, Q, K, V, O, a.L, a.Nq, a.Nk, nqt, a.scale, off, bias, drop);     \
+  } while (0)
   if (a.d == 128) {
     if (a.causal) FA_FWD32_LAUNCH(128, true); else FA_FWD32_LAUNCH(128, false);
   } else {

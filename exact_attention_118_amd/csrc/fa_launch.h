@@ -15,6 +15,15 @@ struct BiasArgs {
   long long sb = 0, sh = 0, sq = 0;
 };
 
+// Optional dropout on the normalised probabilities (on == false: none).  A
+// score is kept iff its Philox byte is below thresh (1..255); kept
+// probabilities are scaled by inv_keep = 256 / thresh.
+struct DropArgs {
+  bool on = false;
+  unsigned seed_lo = 0, seed_hi = 0, offset = 0, thresh = 256;
+  float inv_keep = 1.f;
+};
+
 struct FwdArgs {
   const void* Q;
   const void* K;
@@ -25,6 +34,7 @@ struct FwdArgs {
   float scale;
   bool causal;
   BiasArgs bias;
+  DropArgs drop;
 };
 
 struct BwdArgs {
@@ -42,6 +52,7 @@ struct BwdArgs {
   bool causal;
   float* LD;  // [B*H*Nq][2] fp32 scratch (workspace): per query row L * log2(e), then D = rowsum(dO * O)
   BiasArgs bias;
+  DropArgs drop;
 };
 
 // Tiled forward (Q-tile per workgroup, K/V streamed through LDS).

@@ -149,6 +149,43 @@ fa_status fa_bwd_bias(const void* Q, const void* K, const void* V, const void* b
                       int Nq, int Nk, int d, float scale, int causal, fa_dtype dtype,
                       void* workspace, size_t workspace_bytes, void* stream);
 
+/*
+ * Forward and backward passes with an optional additive bias (as
+ * fa_fwd_bias / fa_bwd_bias take it; bias == NULL: none) and optional
+ * dropout on the normalised probabilities, O = (P * Z) V (the 51CTO
+ * FlashAttention V1/V2 notes, section "FlashAttention V2 相比 V1 有哪些改进": the
+ * V1 algorithm draws dropout on P inside its loop).
+ *
+ *  dropout_p: probability of dropping a score, 0 <= p < 1 (else
+ *  FA_ERR_UNSUPPORTED).  The keep threshold is T = round((1 - p) * 256),
+ *  rounded half to even in double precision from the float p; T = 0 is
+ *  FA_ERR_UNSUPPORTED and T = 256 (p < 1/512) means no dropout.  A score is
+ *  kept iff its random byte is below T, and Z = 256 / T where kept, 0 where
+ *  dropped, so E[Z] = 1.  L stays the logsumexp of the scores before
+ *  dropout.
+ *  Random bytes: Philox4x32-10 (Salmon, Moraes, Dror and Shaw, "Parallel
+ *  Random Numbers: As Easy as 1, 2, 3", SC 2011) with key (seed mod 2^32,
+ *  seed div 2^32) and counter (j div 4, i div 4, b*H + h, offset) for the
+ *  score of query row i and key j of head (b, h); byte j mod 4 of output
+ *  word i mod 4 is that score's byte.  A new offset (or seed) gives a new
+ *  mask; fa_bwd_ex must be given the dropout_p, seed and offset (and bias)
+ *  that fa_fwd_ex used, and regenerates the mask from them.
+ *  Both always take the tiled path (no key splits; fa_fwd_ex needs no
+ *  workspace); the other arguments, rules and errors are those of fa_fwd,
+ *  fa_bwd and fa_fwd_bias.
+ */
+fa_status fa_fwd_ex(const void* Q, const void* K, const void* V, const void* bias,
+                    long long bias_sb, long long bias_sh, long long bias_sq, float dropout_p,
+                    unsigned long long seed, unsigned int offset, void* O, float* L, int B, int H,
+                    int Nq, int Nk, int d, float scale, int causal, fa_dtype dtype, void* stream);
+
+fa_status fa_bwd_ex(const void* Q, const void* K, const void* V, const void* bias,
+                    long long bias_sb, long long bias_sh, long long bias_sq, float dropout_p,
+                    unsigned long long seed, unsigned int offset, const void* O, const float* L,
+                    const void* dO, void* dQ, void* dK, void* dV, int B, int H, int Nq, int Nk,
+                    int d, float scale, int causal, fa_dtype dtype, void* workspace,
+                    size_t workspace_bytes, void* stream);
+
 /* Workspace bytes fa_fwd needs for these arguments (0 when none). */
 size_t fa_fwd_workspace_size(int B, int H, int Nq, int Nk, int d, fa_dtype dtype, int num_splits);
 

@@ -168,6 +168,42 @@ def test_bias_entry_points_accept_empty_problems(lib):
                            fa.FA_BF16, None, 0, None) == fa.FA_OK
 
 
+def fwd_ex(lib, bias=None, sq=16, p=0.0, seed=1, offset=0, Q=A, B=1, Nq=16, Nk=16, d=64,
+           scale=0.125, causal=0):
+    return lib.fa_fwd_ex(Q, A, A, bias, 0, 0, sq, p, seed, offset, A, A, B, 1, Nq, Nk, d, scale,
+                         causal, fa.FA_BF16, None)
+
+
+def bwd_ex(lib, bias=None, sq=16, p=0.0, ws=None, ws_bytes=0, Q=A, B=1, Nq=16):
+    return lib.fa_bwd_ex(Q, A, A, bias, 0, 0, sq, p, 1, 0, A, A, A, A, A, A, B, 1, Nq, 16, 64,
+                         0.125, 0, fa.FA_BF16, ws, ws_bytes, None)
+
+
+def test_ex_entry_points_reject_bad_arguments(lib):
+    for bad in (-0.1, 1.0, 1.5, float("nan"), float("inf"), 0.999):  # 0.999: T = round(0.256) = 0
+        assert fwd_ex(lib, p=bad, Q=None) == fa.FA_ERR_UNSUPPORTED, bad
+        assert bwd_ex(lib, p=bad, Q=None) == fa.FA_ERR_UNSUPPORTED, bad
+    assert fwd_ex(lib, p=0.998, Q=None) == fa.FA_ERR_NULL  # T = 1: accepted
+    assert fwd_ex(lib, p=0.5, Q=None) == fa.FA_ERR_NULL
+    assert fwd_ex(lib, p=0.0, Q=None) == fa.FA_ERR_NULL
+    assert fwd_ex(lib, p=0.5, bias=MIS) == fa.FA_ERR_ALIGN
+    assert fwd_ex(lib, p=0.5, bias=A, sq=8) == fa.FA_ERR_SHAPE
+    assert fwd_ex(lib, p=0.5, d=96, Q=None) == fa.FA_ERR_UNSUPPORTED
+    assert fwd_ex(lib, p=0.5, Nq=20, causal=1, Q=None) == fa.FA_ERR_SHAPE
+    need = lib.fa_bwd_workspace_size(1, 1, 16, 16, 64, fa.FA_BF16)
+    assert bwd_ex(lib, p=0.5) == fa.FA_ERR_WORKSPACE
+    assert bwd_ex(lib, p=0.5, ws=A, ws_bytes=need, Q=None) == fa.FA_ERR_NULL
+    assert bwd_ex(lib, p=0.5, ws=A, ws_bytes=need, bias=MIS) == fa.FA_ERR_ALIGN
+    assert bwd_ex(lib, p=0.5, ws=A, ws_bytes=need, bias=A, sq=8) == fa.FA_ERR_SHAPE
+
+
+def test_ex_entry_points_accept_empty_problems(lib):
+    assert fwd_ex(lib, p=0.5, Q=None, B=0) == fa.FA_OK
+    assert fwd_ex(lib, p=0.5, Q=None, Nq=0) == fa.FA_OK
+    assert lib.fa_bwd_ex(*([None] * 4), 0, 0, 0, 0.5, 1, 0, *([None] * 6), 0, 1, 16, 16, 64, 0.125,
+                         0, fa.FA_BF16, None, 0, None) == fa.FA_OK
+
+
 def test_workspace_queries(lib):
     B, H, N, d = 2, 3, 100, 128
     # backward: D and L*log2(e), each [B,H,N] fp32 padded to 256 bytes
