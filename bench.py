@@ -184,6 +184,37 @@ def bench_decode(fa, torch, steps):
             "algorithmic_bytes": all_bytes}
 
 
+def bench_rows_split(fa, torch, steps):
+    """A few query rows against a long key range (B=4, H=32, Nq=16, Nk=16384,
+    d=128, causal): the key-split path against the tiled path (num_splits=1)."""
+    from exact_attention_118_amd import synth
+
+    w = synth.Workload("rows_b4h32q16k16384d128_causal", 4, 32, 16, 16384, 128, True,
+                       torch.bfloat16, backward=False)
+    x = synth.make_inputs(w, seed=0, device="cuda")
+    O = torch.empty_like(x["Q"])
+    L = torch.empty(w.B, w.H, w.Nq, dtype=torch.float32, device="cuda")
+    out = {"workload": w.name}
+    kv_bytes = 2 * w.B * w.H * w.Nk * w.d * 2
+    for label, ns in (("split", 0), ("tiled", 1)):
+        nsplit = fa.fwd_num_splits(w.B, w.H, w.Nq, w.Nk, w.d, fa.FA_BF16, ns)
+        nb = fa.fwd_workspace_size(w.B, w.H, w.Nq, w.Nk, w.d, fa.FA_BF16, ns)
+        ws = torch.empty(nb, dtype=torch.uint8, device="cuda") if nb else None
+        for _ in range(2):
+            fa.fa_fwd(x["Q"], x["K"], x["V"], O, L, w.scale, True, num_splits=ns, workspace=ws)
+        torch.cuda.synchronize()
+        ev = [torch.cuda.Event(enable_timing=True) for _ in range(steps + 1)]
+        ev[0].record()
+        for i in range(steps):
+            fa.fa_fwd(x["Q"], x["K"], x["V"], O, L, w.scale, True, num_splits=ns, workspace=ws)
+            ev[i + 1].record()
+        torch.cuda.synchronize()
+        ms = ev[0].elapsed_time(ev[-1]) / steps
+        out[label] = {"ms": ms, "splits": nsplit, "kv_GB/s": kv_bytes / (ms * 1e-3) / 1e9}
+    del x
+    return out
+
+
 def _time_fwd_bwd(fa, torch, w, Q, K, V, dO, ws, steps, bias=None, dropout_p=0.0):
     """Mean forward and backward milliseconds of fa_fwd + fa_bwd (the bias or
     the dropout entry points when given)."""
@@ -411,6 +442,8 @@ def main():
     if not args.no_decode:
         log("decode-shaped forward")
         out["decode"] = bench_decode(fa, torch, steps=10)
+        log("a few query rows: key splits against the tiled path")
+        out["rows_split"] = bench_rows_split(fa, torch, steps=10)
     if args.cpu_heads > 0:
         log(f"float64 oracle on {args.cpu_heads} heads")
         out["cpu_baseline"] = cpu_baseline(w, x, args.cpu_heads)

@@ -16,6 +16,12 @@ constexpr size_t kAlign = 16;
 constexpr size_t kWsAlign = 256;
 constexpr int kSplitTargetBlocks = 2048;  // aim for ~8 workgroups per CU on the split path
 constexpr int kSplitMinKeys = 256;        // do not split below this many keys per chunk
+// Key splits for a few query rows (1 < Nq <= kRowsSplitMaxNq: one 128-row
+// query tile per head): the tiled kernel per (query tile, key chunk).
+constexpr int kRowsSplitMaxNq = 128;
+constexpr int kRowsSplitTarget = 1024;  // workgroups (4 waves each) to aim for
+constexpr int kRowsSplitMinKeys = 512;  // keys per chunk at least (8 key tiles)
+constexpr int kRowsSplitAlign = 128;    // chunks are whole pairs of 64-key tiles
 
 size_t round_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 
@@ -58,12 +64,35 @@ int effective_splits(int Nk, int s) {
   return (Nk + chunk - 1) / chunk;
 }
 
+// Chunk length of the row-split path: ceil(Nk / s) rounded up to whole tile pairs.
+int rows_split_chunk(int Nk, int s) {
+  const int c = (Nk + s - 1) / s;
+  return (c + kRowsSplitAlign - 1) / kRowsSplitAlign * kRowsSplitAlign;
+}
+
+int rows_auto_splits(int BH, int Nk) {
+  int s = (kRowsSplitTarget + BH - 1) / BH;
+  const int by_keys = Nk / kRowsSplitMinKeys;
+  if (s > by_keys) s = by_keys;
+  return s < 1 ? 1 : s;
+}
+
 // 0: tiled path, >0: split path with that many splits, <0: unsupported combination.
 int choose_splits(int B, int H, int Nq, int Nk, fa_dtype dtype, int num_splits) {
   if (num_splits < 0) return -1;
   if (Nq == 1 && is_mfma(dtype)) {
     const int s = num_splits == 0 ? auto_splits(B * H, Nk) : num_splits;
     return effective_splits(Nk, s);
+  }
+  if (Nq > 1 && Nq <= kRowsSplitMaxNq && is_mfma(dtype)) {
+    int s = num_splits == 0 ? rows_auto_splits(B * H, Nk) : num_splits;
+    if (s > Nk) s = Nk;
+    if (s <= 1) return 0;  // one chunk: the tiled path
+    const int chunk = rows_split_chunk(Nk, s);
+    const int eff = (Nk + chunk - 1) / chunk;
+    // partial rows (B*H*Nq per split) are indexed with 32-bit counts
+    if ((long long)B * H * Nq * eff > INT_MAX / 128) return 0;
+    return eff > 1 ? eff : 0;
   }
   if (num_splits > 1) return -1;
   return 0;
@@ -117,7 +146,7 @@ size_t fa_fwd_workspace_size(int B, int H, int Nq, int Nk, int d, fa_dtype dtype
   if ((long long)B * H * Nq == 0) return 0;
   const int s = choose_splits(B, H, Nq, Nk, dtype, num_splits);
   if (s <= 0) return 0;
-  return split_ws(B * H, d, s).total;
+  return split_ws(B * H * Nq, d, s).total;
 }
 
 size_t fa_bwd_workspace_size(int B, int H, int Nq, int Nk, int d, fa_dtype dtype) {
@@ -182,14 +211,24 @@ fa_status fwd_impl(const void* Q, const void* K, const void* V, const fa::BiasAr
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
   hipError_t e;
   if (splits > 0) {
-    const SplitWs w = split_ws(B * H, d, splits);
+    const SplitWs w = split_ws(B * H * Nq, d, splits);
     if (!workspace || workspace_bytes < w.total) return FA_ERR_WORKSPACE;
     if (!aligned(workspace)) return FA_ERR_ALIGN;
     float* part_o = static_cast<float*>(workspace);
     float* part_l = reinterpret_cast<float*>(static_cast<char*>(workspace) + w.l_off);
-    a.causal = false;  // one query row sees every key under bottom-right alignment
-    e = (dtype == FA_BF16) ? fa::launch_fwd_split_bf16(a, splits, part_o, part_l, s)
-                           : fa::launch_fwd_split_f16(a, splits, part_o, part_l, s);
+    if (Nq == 1) {
+      a.causal = false;  // one query row sees every key under bottom-right alignment
+      e = (dtype == FA_BF16) ? fa::launch_fwd_split_bf16(a, splits, part_o, part_l, s)
+                             : fa::launch_fwd_split_f16(a, splits, part_o, part_l, s);
+    } else {
+      const int chunk = rows_split_chunk(Nk, splits);
+      e = (dtype == FA_BF16)
+              ? fa::launch_fwd_rows_split_bf16(a, splits, chunk, part_o, part_l, s)
+              : fa::launch_fwd_rows_split_f16(a, splits, chunk, part_o, part_l, s);
+      if (e == hipSuccess)
+        e = (dtype == FA_BF16) ? fa::launch_split_combine_bf16(a, splits, part_o, part_l, s)
+                               : fa::launch_split_combine_f16(a, splits, part_o, part_l, s);
+    }
   } else if (dtype == FA_BF16) {
     e = fa::launch_fwd_bf16(a, s);
   } else if (dtype == FA_FP16) {

@@ -46,11 +46,24 @@ constexpr int kFwdBC = 64;   // keys per K/V tile
 constexpr int kFwdThreads = 256;
 constexpr float kRescaleSlack = 8.f;  // see the online softmax below
 
-template <typename T, int D, bool CAUSAL, bool BIAS, bool DROP>
+// Key splits (SPLIT): each workgroup takes one query tile and one chunk of
+// `chunk` keys (a multiple of 2 * BC), and writes its normalised partial
+// output and logsumexp in fp32 to part_o [splits, rows, D] and part_l
+// [splits, rows] (rows = B*H*Nq) for the combine kernel (the 51CTO notes,
+// "Sequence Length 并行" and the end of "Sequence Parallel": Flash-Decoding
+// splits the keys when the query length gives too few workgroups).  A row
+// that sees no key of its chunk writes 0 and -inf.
+struct SplitDev {
+  float* part_o;
+  float* part_l;
+  int splits, chunk, rows;
+};
+
+template <typename T, int D, bool CAUSAL, bool BIAS, bool DROP, bool SPLIT>
 __global__ __launch_bounds__(kFwdThreads, 2) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void fwd_kernel(const T* __restrict__ Q, const T* __restrict__ K, const T* __restrict__ V,
                 T* __restrict__ O, float* __restrict__ L, int Nq, int Nk, int nqt, float c,
-                int off, BiasDev bias, DropDev drop) {
+                int off, BiasDev bias, DropDev drop, SplitDev split) {
   typedef typename Vec<T>::x8 T8;
   typedef typename Vec<T>::x4 T4;
   constexpr int BR = kFwdBR, BC = kFwdBC;
@@ -78,8 +91,14 @@ void fwd_kernel(const T* __restrict__ Q, const T* __restrict__ K, const T* __res
   // grows with its index).  Remapped so each XCD serves a contiguous range of
   // workgroups of the same heads (K/V stay in that XCD's L2; the 51CTO notes,
   // "Thread Block Level 并行", grid order with the query tile fastest).
-  const int nwg = CAUSAL ? (nqt + 1) / 2 : nqt;  // workgroups per head
-  const int logical = xcd_remap(blockIdx.x, gridDim.x);
+  constexpr bool PAIRED = CAUSAL && !SPLIT;
+  const int nwg = PAIRED ? (nqt + 1) / 2 : nqt;  // workgroups per head (and split)
+  int logical = xcd_remap(blockIdx.x, gridDim.x);
+  int sp = 0;  // key split (SPLIT)
+  if constexpr (SPLIT) {
+    sp = logical % split.splits;
+    logical /= split.splits;
+  }
   const int bh = logical / nwg;
   const int t = logical - bh * nwg;
   const size_t qbase = (size_t)bh * Nq * D;
@@ -130,9 +149,9 @@ void fwd_kernel(const T* __restrict__ Q, const T* __restrict__ K, const T* __res
   };
   constexpr int KRING = 4, VRING = 3;
 
-  for (int pass = 0; pass < (CAUSAL ? 2 : 1); ++pass) {
-    const int qt = !CAUSAL ? t : (pass == 0 ? nqt - 1 - t : t);
-    if (CAUSAL && pass == 1 && t == nqt - 1 - t) break;  // odd count: the middle tile once
+  for (int pass = 0; pass < (PAIRED ? 2 : 1); ++pass) {
+    const int qt = !PAIRED ? t : (pass == 0 ? nqt - 1 - t : t);
+    if (PAIRED && pass == 1 && t == nqt - 1 - t) break;  // odd count: the middle tile once
     if (pass == 1) __syncthreads();  // the first tile's last LDS reads precede the new loads
     const int q0 = qt * BR;
 
@@ -145,8 +164,12 @@ void fwd_kernel(const T* __restrict__ Q, const T* __restrict__ K, const T* __res
                            : zero8<T8>();
 
     // Keys this workgroup needs: all, or (causal) up to the last row's diagonal.
-    const int kend = CAUSAL ? min(Nk, q0 + BR + off) : Nk;
+    // With SPLIT, only the keys of chunk sp: tiles jbeg .. ntiles-1 (jbeg even,
+    // so tile j still uses buffers j & 1).
+    const int kbeg = SPLIT ? sp * split.chunk : 0;
+    const int kend = min(CAUSAL ? min(Nk, q0 + BR + off) : Nk, SPLIT ? kbeg + split.chunk : Nk);
     const int ntiles = (kend + BC - 1) / BC;
+    const int jbeg = kbeg / BC;
     const int wrow_lo = q0 + wave * 32;  // smallest query row of this wave
 
     float m_run = -INFINITY;  // reference of the exponentials (row max so far, log2 units)
@@ -210,19 +233,19 @@ void fwd_kernel(const T* __restrict__ Q, const T* __restrict__ K, const T* __res
     };
 
     // Prologue: K tiles 0 and 1, V tile 0; scores, mask and row max of tile 0.
-    kv.tile(Kh, 0, Nk, sK0);
-    kv.tile(Kh, BC, Nk, sK0 + TILE);
-    kv.tile(Vh, 0, Nk, sV0);
+    kv.tile(Kh, kbeg, Nk, sK0);
+    kv.tile(Kh, kbeg + BC, Nk, sK0 + TILE);
+    kv.tile(Vh, kbeg, Nk, sV0);
     vm_wait_all();
     __syncthreads();
     f32x16 sA[2], sB[2];
     scores(0, sA);
     if constexpr (BIAS) {
       BT4 bb[8];
-      bias_load(bb, 0);
+      bias_load(bb, kbeg);
       bias_add(sA, bb);
     }
-    mask_tile(sA, 0);
+    mask_tile(sA, kbeg);
     float mx_next = row_max(sA);
     __syncthreads();  // every wave is done with K tile 0 before tile 2 replaces it
 
@@ -353,7 +376,7 @@ void fwd_kernel(const T* __restrict__ Q, const T* __restrict__ K, const T* __res
       __syncthreads();
     };
 
-    for (int j = 0; j < ntiles; j += 2) {
+    for (int j = jbeg; j < ntiles; j += 2) {
       tile_step(0, j, sA, sB);
       if (j + 1 < ntiles) tile_step(1, j + 1, sB, sA);
     }
@@ -361,7 +384,24 @@ void fwd_kernel(const T* __restrict__ Q, const T* __restrict__ K, const T* __res
     // Epilogue: O = O_acc / l (times 1 / keep-probability with dropout),
     // L = (m + log2 l) * ln 2.
     const float l_tot = l_run + wave_shfl_xor(l_run, 32);
-    if (qrow < Nq) {
+    if constexpr (SPLIT) {
+      if (qrow < Nq) {
+        const size_t prow = (size_t)sp * split.rows + (size_t)bh * Nq + qrow;
+        const bool any = l_tot > 0.f;  // some key of the chunk is visible to this row
+        const float inv = any ? 1.f / l_tot : 0.f;
+        float* po = split.part_o + prow * D;
+#pragma unroll
+        for (int nt = 0; nt < NNT; ++nt)
+#pragma unroll
+          for (int gg = 0; gg < 4; ++gg) {
+            f32x4 v;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) v[e] = oacc[nt][gg * 4 + e] * inv;
+            *(f32x4*)(po + nt * 32 + gg * 8 + half * 4) = v;
+          }
+        if (half == 0) split.part_l[prow] = any ? (m_run + log2f(l_tot)) * kLn2 : -INFINITY;
+      }
+    } else if (qrow < Nq) {
       const float inv = (DROP ? drop.inv_keep : 1.f) / l_tot;
       T* orow = O + qbase + (size_t)qrow * D;
 #pragma unroll
@@ -490,15 +530,46 @@ hipError_t launch_fwd_mfma(const FwdArgs& a, hipStream_t s) {
   T* O = (T*)a.O;
   const BiasDev bias{a.bias.ptr, a.bias.sb, a.bias.sh, a.bias.sq, a.H, 1.f / a.scale};
   const DropDev drop = drop_dev(a.drop);
-#define FA_FWD_LAUNCH(DD, CC)                                                                  \
-  hipLaunchKernelGGL((fwd_kernel<T, DD, CC, BIAS, DROP>), dim3(nblocks), dim3(kFwdThreads), 0, \
-                     s, Q, K, V, O, a.L, a.Nq, a.Nk, nqt, c, off, bias, drop)
+  const SplitDev nosplit{nullptr, nullptr, 1, 0, 0};
+#define FA_FWD_LAUNCH(DD, CC)                                                                 \
+  hipLaunchKernelGGL((fwd_kernel<T, DD, CC, BIAS, DROP, false>), dim3(nblocks),               \
+                     dim3(kFwdThreads), 0, s, Q, K, V, O, a.L, a.Nq, a.Nk, nqt, c, off, bias, \
+                     drop, nosplit)
   if (a.d == 128) {
     if (a.causal) FA_FWD_LAUNCH(128, true); else FA_FWD_LAUNCH(128, false);
   } else {
     if (a.causal) FA_FWD_LAUNCH(64, true); else FA_FWD_LAUNCH(64, false);
   }
 #undef FA_FWD_LAUNCH
+  return hipGetLastError();
+}
+
+// Key splits for a few query rows: (query tile, key chunk, batch*head) per
+// workgroup into the partial buffers; the caller runs the combine.
+template <typename T>
+hipError_t launch_fwd_rows_split(const FwdArgs& a, int splits, int chunk, float* part_o,
+                                 float* part_l, hipStream_t s) {
+  const int BH = a.B * a.H;
+  const int nqt = (a.Nq + kFwdBR - 1) / kFwdBR;
+  const int nblocks = nqt * BH * splits;
+  const float c = a.scale * kLog2e;
+  const int off = a.Nk - a.Nq;
+  const T* Q = (const T*)a.Q;
+  const T* K = (const T*)a.K;
+  const T* V = (const T*)a.V;
+  const BiasDev nobias{nullptr, 0, 0, 0, a.H, 1.f};
+  const DropDev nodrop = drop_dev(DropArgs{});
+  const SplitDev split{part_o, part_l, splits, chunk, BH * a.Nq};
+#define FA_FWD_SPLIT_LAUNCH(DD, CC)                                                           \
+  hipLaunchKernelGGL((fwd_kernel<T, DD, CC, false, false, true>), dim3(nblocks),              \
+                     dim3(kFwdThreads), 0, s, Q, K, V, (T*)a.O, a.L, a.Nq, a.Nk, nqt, c, off, \
+                     nobias, nodrop, split)
+  if (a.d == 128) {
+    if (a.causal) FA_FWD_SPLIT_LAUNCH(128, true); else FA_FWD_SPLIT_LAUNCH(128, false);
+  } else {
+    if (a.causal) FA_FWD_SPLIT_LAUNCH(64, true); else FA_FWD_SPLIT_LAUNCH(64, false);
+  }
+#undef FA_FWD_SPLIT_LAUNCH
   return hipGetLastError();
 }
 
@@ -513,6 +584,15 @@ hipError_t launch_fwd_typed(const FwdArgs& a, hipStream_t s) {
 
 hipError_t launch_fwd_bf16(const FwdArgs& a, hipStream_t s) { return launch_fwd_typed<bf16>(a, s); }
 hipError_t launch_fwd_f16(const FwdArgs& a, hipStream_t s) { return launch_fwd_typed<f16>(a, s); }
+
+hipError_t launch_fwd_rows_split_bf16(const FwdArgs& a, int splits, int chunk, float* part_o,
+                                      float* part_l, hipStream_t s) {
+  return launch_fwd_rows_split<bf16>(a, splits, chunk, part_o, part_l, s);
+}
+hipError_t launch_fwd_rows_split_f16(const FwdArgs& a, int splits, int chunk, float* part_o,
+                                     float* part_l, hipStream_t s) {
+  return launch_fwd_rows_split<f16>(a, splits, chunk, part_o, part_l, s);
+}
 
 hipError_t launch_fwd_f32(const FwdArgs& a, hipStream_t s) {
   const int BH = a.B * a.H;

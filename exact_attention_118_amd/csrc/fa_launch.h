@@ -73,6 +73,18 @@ hipError_t launch_bwd_bf16(const BwdArgs& a, int stages, hipStream_t s);
 hipError_t launch_bwd_f16(const BwdArgs& a, int stages, hipStream_t s);
 hipError_t launch_bwd_f32(const BwdArgs& a, int stages, hipStream_t s);
 
+// Key splits for a few query rows (1 < Nq <= 128): the tiled forward kernel on
+// (query tile, chunk of `chunk` keys), partials as above with B*H*Nq rows,
+// then the combine of those partials into O and L.
+hipError_t launch_fwd_rows_split_bf16(const FwdArgs& a, int splits, int chunk, float* part_o,
+                                      float* part_l, hipStream_t s);
+hipError_t launch_fwd_rows_split_f16(const FwdArgs& a, int splits, int chunk, float* part_o,
+                                     float* part_l, hipStream_t s);
+hipError_t launch_split_combine_bf16(const FwdArgs& a, int splits, const float* part_o,
+                                     const float* part_l, hipStream_t s);
+hipError_t launch_split_combine_f16(const FwdArgs& a, int splits, const float* part_o,
+                                    const float* part_l, hipStream_t s);
+
 // Key-chunk length used by the split path for `splits` chunks of Nk keys.
 int split_chunk(int Nk, int splits);
 

@@ -134,24 +134,39 @@ __global__ __launch_bounds__(kSplitThreads) void fwd_split_kernel(
   }
 }
 
-// One workgroup of D threads per head: L = log sum_s exp(L_s), O = sum_s exp(L_s - L) O_s.
+// One workgroup of D threads per output row (rows = B*H*Nq, row-major like O):
+// L = log sum_s exp(L_s), O = sum_s exp(L_s - L) O_s.  A split that saw no key
+// of the row has L_s = -inf and weight 0; every row sees some key overall.
 template <typename T, int D>
 __global__ __launch_bounds__(D) void split_combine_kernel(const float* __restrict__ part_o,
                                                           const float* __restrict__ part_l,
                                                           T* __restrict__ O,
                                                           float* __restrict__ L, int splits,
-                                                          int BH) {
-  const int bh = blockIdx.x, e = threadIdx.x;
+                                                          int rows) {
+  const int r = blockIdx.x, e = threadIdx.x;
   float M = -INFINITY;
-  for (int s = 0; s < splits; ++s) M = fmaxf(M, part_l[(size_t)s * BH + bh]);
+  for (int s = 0; s < splits; ++s) M = fmaxf(M, part_l[(size_t)s * rows + r]);
   float sum = 0.f;
-  for (int s = 0; s < splits; ++s) sum += expf(part_l[(size_t)s * BH + bh] - M);
+  for (int s = 0; s < splits; ++s) sum += expf(part_l[(size_t)s * rows + r] - M);
   const float Lt = M + logf(sum);
   float acc = 0.f;
   for (int s = 0; s < splits; ++s)
-    acc = fmaf(expf(part_l[(size_t)s * BH + bh] - Lt), part_o[((size_t)s * BH + bh) * D + e], acc);
-  O[(size_t)bh * D + e] = (T)acc;
-  if (e == 0) L[bh] = Lt;
+    acc = fmaf(expf(part_l[(size_t)s * rows + r] - Lt), part_o[((size_t)s * rows + r) * D + e], acc);
+  O[(size_t)r * D + e] = (T)acc;
+  if (e == 0) L[r] = Lt;
+}
+
+template <typename T>
+hipError_t launch_combine(const FwdArgs& a, int splits, int rows, const float* part_o,
+                          const float* part_l, hipStream_t s) {
+  if (a.d == 128) {
+    hipLaunchKernelGGL((split_combine_kernel<T, 128>), dim3(rows), dim3(128), 0, s, part_o, part_l,
+                       (T*)a.O, a.L, splits, rows);
+  } else {
+    hipLaunchKernelGGL((split_combine_kernel<T, 64>), dim3(rows), dim3(64), 0, s, part_o, part_l,
+                       (T*)a.O, a.L, splits, rows);
+  }
+  return hipGetLastError();
 }
 
 }  // namespace
@@ -178,14 +193,7 @@ hipError_t launch_split(const FwdArgs& a, int splits, float* part_o, float* part
   }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  if (a.d == 128) {
-    hipLaunchKernelGGL((split_combine_kernel<T, 128>), dim3(BH), dim3(128), 0, s, part_o, part_l,
-                       (T*)a.O, a.L, splits, BH);
-  } else {
-    hipLaunchKernelGGL((split_combine_kernel<T, 64>), dim3(BH), dim3(64), 0, s, part_o, part_l,
-                       (T*)a.O, a.L, splits, BH);
-  }
-  return hipGetLastError();
+  return launch_combine<T>(a, splits, BH, part_o, part_l, s);
 }
 
 }  // namespace
@@ -197,6 +205,15 @@ hipError_t launch_fwd_split_bf16(const FwdArgs& a, int splits, float* part_o, fl
 hipError_t launch_fwd_split_f16(const FwdArgs& a, int splits, float* part_o, float* part_l,
                                 hipStream_t s) {
   return launch_split<f16>(a, splits, part_o, part_l, s);
+}
+
+hipError_t launch_split_combine_bf16(const FwdArgs& a, int splits, const float* part_o,
+                                     const float* part_l, hipStream_t s) {
+  return launch_combine<bf16>(a, splits, a.B * a.H * a.Nq, part_o, part_l, s);
+}
+hipError_t launch_split_combine_f16(const FwdArgs& a, int splits, const float* part_o,
+                                    const float* part_l, hipStream_t s) {
+  return launch_combine<f16>(a, splits, a.B * a.H * a.Nq, part_o, part_l, s);
 }
 
 }  // namespace fa

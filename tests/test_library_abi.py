@@ -84,8 +84,10 @@ def test_fwd_rejects_bad_arguments(lib):
     assert fwd(lib, Q=None, scale=float("nan")) == fa.FA_ERR_UNSUPPORTED
     assert fwd(lib, Q=None, scale=float("inf")) == fa.FA_ERR_UNSUPPORTED
     assert fwd(lib, Q=None, B=1 << 20, H=1 << 12) == fa.FA_ERR_SHAPE
-    # key splits need a single query row (bf16); fp32 never splits
-    assert fwd(lib, splits=2) == fa.FA_ERR_UNSUPPORTED
+    # key splits need at most 128 query rows (bf16, fp16); fp32 never splits
+    assert fwd(lib, Nq=200, Nk=256, splits=2) == fa.FA_ERR_UNSUPPORTED
+    assert fwd(lib, Nq=16, Nk=4096, splits=2) == fa.FA_ERR_WORKSPACE  # allowed, needs workspace
+    assert fwd(lib, Nq=16, dtype=fa.FA_FP32, splits=2) == fa.FA_ERR_UNSUPPORTED
     assert fwd(lib, splits=-1) == fa.FA_ERR_UNSUPPORTED
     assert fwd(lib, Nq=1, dtype=fa.FA_FP32, splits=3) == fa.FA_ERR_UNSUPPORTED
     # the split path needs its workspace
@@ -227,6 +229,16 @@ def test_workspace_queries(lib):
     assert lib.fa_fwd_workspace_size(16, 32, 1, 16384, 128, fa.FA_FP16, 0) == \
         lib.fa_fwd_workspace_size(16, 32, 1, 16384, 128, fa.FA_BF16, 0)
     assert lib.fa_bwd_workspace_size(B, H, N, N, d, fa.FA_FP16) == 2 * up(B * H * N * 4)
+    # a few query rows: chunks of whole 128-key tile pairs, partials per row
+    assert lib.fa_fwd_num_splits(2, 4, 16, 8192, 128, fa.FA_BF16, 0) == 16
+    assert lib.fa_fwd_workspace_size(2, 4, 16, 8192, 128, fa.FA_BF16, 0) == \
+        up(16 * 128 * 128 * 4) + up(16 * 128 * 4)
+    assert lib.fa_fwd_num_splits(1, 1, 16, 1000, 64, fa.FA_BF16, 3) == 3    # chunk 384
+    assert lib.fa_fwd_num_splits(1, 1, 16, 200, 64, fa.FA_BF16, 3) == 2     # chunk 128
+    assert lib.fa_fwd_num_splits(1, 1, 16, 100, 64, fa.FA_BF16, 2) == 1     # one chunk: tiled
+    assert lib.fa_fwd_workspace_size(1, 1, 16, 100, 64, fa.FA_BF16, 2) == 0
+    assert lib.fa_fwd_num_splits(64, 16, 64, 4096, 128, fa.FA_BF16, 0) == 1  # grid full already
+    assert lib.fa_fwd_num_splits(1, 1, 129, 8192, 64, fa.FA_BF16, 0) == 1   # over 128 rows
 
 
 def test_binding_fails_loudly_without_the_library(monkeypatch, tmp_path):

@@ -248,6 +248,63 @@ def test_split_path_small(gpu_lib, d, nk, dt):
         assert max_abs(f64(L), L_ref) <= tl
 
 
+ROW_SPLIT_CASES = [
+    # Nq, Nk, causal, forced splits (0: automatic)
+    (16, 1000, False, 3),
+    (7, 4100, True, 0),
+    (128, 2048, True, 4),
+    (2, 300, False, 2),
+    (100, 777, True, 5),
+    (33, 1536, False, 64),   # more splits than 128-key chunks: clamped
+]
+
+
+@pytest.mark.parametrize("dt", [torch.bfloat16, torch.float16])
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("case", ROW_SPLIT_CASES, ids=lambda c: f"q{c[0]}k{c[1]}{'c' if c[2] else ''}s{c[3]}")
+def test_row_split_path_small(gpu_lib, case, d, dt):
+    """A few query rows, keys split across workgroups and combined: against the
+    oracle, and against the tiled path (num_splits = 1)."""
+    fa = gpu_lib
+    Nq, Nk, causal, ns = case
+    B, H = 2, 3
+    eff = fa.fwd_num_splits(B, H, Nq, Nk, d, 0 if dt == torch.bfloat16 else 2, ns)
+    say(f"row split {dt} d={d} Nq={Nq} Nk={Nk} causal={causal} ns={ns} -> {eff}")
+    x = make(B, H, Nq, Nk, d, dt, seed=14)
+    scale = 1.0 / math.sqrt(d)
+    O, L = fa.forward(x["Q"], x["K"], x["V"], scale, causal, num_splits=ns)
+    O1, L1 = fa.forward(x["Q"], x["K"], x["V"], scale, causal, num_splits=1)
+    torch.cuda.synchronize()
+    O_ref, L_ref = oracle.attention_forward_batched(f64(x["Q"]), f64(x["K"]), f64(x["V"]), scale,
+                                                    causal)
+    to, tl, _ = tolerances(dt)
+    assert max_abs(f64(O), O_ref) <= to
+    assert max_abs(f64(L), L_ref) <= tl
+    assert max_abs(f64(O1), O_ref) <= to
+    assert max_abs(f64(L), f64(L1)) <= tl
+
+
+def test_row_split_b4h32q16k16384d128_causal(gpu_lib):
+    """B=4, H=32, 16 query rows against 16384 keys, causal, bf16: automatic
+    split; sampled heads against the oracle, every head against the tiled path."""
+    fa = gpu_lib
+    w = synth.Workload("rows", 4, 32, 16, 16384, 128, True, torch.bfloat16)
+    x = synth.make_inputs(w, seed=0, device="cuda", with_grad_out=False)
+    ns = fa.fwd_num_splits(w.B, w.H, w.Nq, w.Nk, w.d, 0, 0)
+    say(f"row split b4h32q16k16384d128 causal, {ns} splits")
+    assert ns > 1
+    O, L = fa.forward(x["Q"], x["K"], x["V"], w.scale, True)
+    O1, L1 = fa.forward(x["Q"], x["K"], x["V"], w.scale, True, num_splits=1)
+    torch.cuda.synchronize()
+    for b, h in ((0, 0), (1, 7), (3, 31)):
+        O_ref, L_ref = oracle.attention_forward(f64(x["Q"][b, h]), f64(x["K"][b, h]),
+                                                f64(x["V"][b, h]), w.scale, True)
+        assert max_abs(f64(O[b, h]), O_ref) <= BF16_O, (b, h)
+        assert max_abs(f64(L[b, h]), L_ref) <= BF16_L, (b, h)
+    assert float((O.float() - O1.float()).abs().max()) <= 2 * BF16_O
+    assert float((L - L1).abs().max()) <= BF16_L
+
+
 # --------------------------------------------------------------------------- guards and edge cases
 
 @pytest.mark.parametrize("dt", [torch.bfloat16, torch.float16, torch.float32])
