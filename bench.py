@@ -215,7 +215,7 @@ def bench_rows_split(fa, torch, steps):
     return out
 
 
-def _time_fwd_bwd(fa, torch, w, Q, K, V, dO, ws, steps, bias=None, dropout_p=0.0):
+def _time_fwd_bwd(fa, torch, w, Q, K, V, dO, ws, steps, bias=None, dropout_p=0.0, tile_map=None):
     """Mean forward and backward milliseconds of fa_fwd + fa_bwd (the bias or
     the dropout entry points when given)."""
     O = torch.empty_like(Q)
@@ -223,17 +223,18 @@ def _time_fwd_bwd(fa, torch, w, Q, K, V, dO, ws, steps, bias=None, dropout_p=0.0
     dQ, dK, dV = torch.empty_like(Q), torch.empty_like(K), torch.empty_like(V)
 
     def run(ev=None):
-        if dropout_p:
-            fa.fa_fwd_ex(Q, K, V, O, L, w.scale, w.causal, bias=bias, dropout_p=dropout_p, seed=1)
+        if dropout_p or tile_map is not None:
+            fa.fa_fwd_ex(Q, K, V, O, L, w.scale, w.causal, bias=bias, dropout_p=dropout_p, seed=1,
+                         tile_map=tile_map)
         elif bias is None:
             fa.fa_fwd(Q, K, V, O, L, w.scale, w.causal)
         else:
             fa.fa_fwd_bias(Q, K, V, bias, O, L, w.scale, w.causal)
         if ev is not None:
             ev.record()
-        if dropout_p:
+        if dropout_p or tile_map is not None:
             fa.fa_bwd_ex(Q, K, V, O, L, dO, dQ, dK, dV, w.scale, w.causal, bias=bias,
-                         dropout_p=dropout_p, seed=1, workspace=ws)
+                         dropout_p=dropout_p, seed=1, workspace=ws, tile_map=tile_map)
         elif bias is None:
             fa.fa_bwd(Q, K, V, O, L, dO, dQ, dK, dV, w.scale, w.causal, workspace=ws)
         else:
@@ -271,6 +272,33 @@ def bench_bias(fa, torch, w, x, ws, steps):
     r["bias_shape"] = list(bias.shape)
     r["bias_GB"] = bias.numel() * bias.element_size() / 1e9
     return r
+
+
+def bench_window(fa, torch, w, x, ws, steps, window=1024):
+    """A block-sparse bias: keys more than `window` before the diagonal get
+    -inf ([1, 1, N, N] bf16), with and without its tile map (the map's own
+    build time reported apart)."""
+    i = torch.arange(w.Nq, device="cuda")[:, None] + (w.Nk - w.Nq)
+    j = torch.arange(w.Nk, device="cuda")[None, :]
+    b = torch.zeros((w.Nq, w.Nk), dtype=torch.float32, device="cuda")
+    b[(i - j) > window] = float("-inf")
+    bias = b.to(w.dtype).view(1, 1, w.Nq, w.Nk)
+    del b, i, j
+    tmap = fa.fa_bias_tile_map(bias, w.B, w.H, w.Nq, w.Nk)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(steps):
+        fa.fa_bias_tile_map(bias, w.B, w.H, w.Nq, w.Nk, tile_map=tmap)
+    e1.record()
+    torch.cuda.synchronize()
+    out = {"window": window, "map_ms": e0.elapsed_time(e1) / steps,
+           "map_bytes": int(tmap.numel()),
+           "map_active_frac": float(tmap.float().mean())}
+    args = (fa, torch, w, x["Q"], x["K"], x["V"], x["dO"], ws, steps)
+    out["with_map"] = _time_fwd_bwd(*args, bias=bias, tile_map=tmap)
+    out["without_map"] = _time_fwd_bwd(*args, bias=bias)
+    return out
 
 
 def bench_dropout(fa, torch, w, x, ws, steps, p=0.1):
@@ -426,6 +454,9 @@ def main():
     if not args.no_bias:
         log("additive bias [1, H, N, N], same workload")
         out["bias"] = bench_bias(fa, torch, w, x, ws, steps=max(3, args.steps // 2))
+    if not args.no_bias:
+        log("block-sparse bias (1024-key window) with and without its tile map")
+        out["window_bias"] = bench_window(fa, torch, w, x, ws, steps=max(3, args.steps // 2))
     if not args.no_dropout:
         log("dropout p = 0.1, same workload")
         out["dropout"] = bench_dropout(fa, torch, w, x, ws, steps=max(3, args.steps // 2))

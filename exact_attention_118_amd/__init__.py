@@ -14,7 +14,7 @@ import os
 
 __all__ = [
     "FAError", "load_library", "lib_path", "fa_fwd", "fa_bwd", "fa_fwd_bias", "fa_bwd_bias",
-    "fa_fwd_ex", "fa_bwd_ex",
+    "fa_fwd_ex", "fa_bwd_ex", "fa_bias_tile_map",
     "forward", "backward",
     "fwd_workspace_size", "bwd_workspace_size", "fwd_num_splits", "status_string", "version",
     "FA_OK", "FA_ERR_NULL", "FA_ERR_SHAPE", "FA_ERR_UNSUPPORTED", "FA_ERR_ALIGN",
@@ -28,7 +28,7 @@ FA_BF16, FA_FP32, FA_FP16 = 0, 1, 2
 FA_BWD_PREPROCESS, FA_BWD_DKDV, FA_BWD_DQ, FA_BWD_ALL = 1, 2, 4, 7
 
 EXPORTED_SYMBOLS = ("fa_fwd", "fa_bwd", "fa_bwd_stages", "fa_fwd_bias", "fa_bwd_bias",
-                    "fa_fwd_ex", "fa_bwd_ex",
+                    "fa_fwd_ex", "fa_bwd_ex", "fa_bias_tile_map", "fa_bias_tile_map_size",
                     "fa_fwd_workspace_size", "fa_bwd_workspace_size", "fa_fwd_num_splits",
                     "fa_status_string", "fa_version")
 
@@ -68,12 +68,16 @@ def load_library():
                                 f, i, i, vp, sz, vp]
     lib.fa_bwd_bias.restype = i
     ull, u = ctypes.c_ulonglong, ctypes.c_uint
-    lib.fa_fwd_ex.argtypes = [vp, vp, vp, vp, ll, ll, ll, f, ull, u, vp, vp, i, i, i, i, i, f, i, i,
-                              vp]
+    lib.fa_fwd_ex.argtypes = [vp, vp, vp, vp, ll, ll, ll, vp, f, ull, u, vp, vp, i, i, i, i, i, f,
+                              i, i, vp]
     lib.fa_fwd_ex.restype = i
-    lib.fa_bwd_ex.argtypes = [vp, vp, vp, vp, ll, ll, ll, f, ull, u, vp, vp, vp, vp, vp, vp, i, i,
-                              i, i, i, f, i, i, vp, sz, vp]
+    lib.fa_bwd_ex.argtypes = [vp, vp, vp, vp, ll, ll, ll, vp, f, ull, u, vp, vp, vp, vp, vp, vp, i,
+                              i, i, i, i, f, i, i, vp, sz, vp]
     lib.fa_bwd_ex.restype = i
+    lib.fa_bias_tile_map_size.argtypes = [ll, ll, i, i, i, i]
+    lib.fa_bias_tile_map_size.restype = sz
+    lib.fa_bias_tile_map.argtypes = [vp, ll, ll, ll, i, i, i, i, i, vp, sz, vp]
+    lib.fa_bias_tile_map.restype = i
     lib.fa_fwd_workspace_size.argtypes = [i, i, i, i, i, i, i]
     lib.fa_fwd_workspace_size.restype = sz
     lib.fa_bwd_workspace_size.argtypes = [i, i, i, i, i, i]
@@ -282,8 +286,27 @@ def _check_dropout(dropout_p, seed, offset):
         raise ValueError("seed must fit 64 bits and offset 32 bits")
 
 
+def fa_bias_tile_map(bias, B, H, Nq, Nk, tile_map=None, stream=None):
+    """Call ``fa_bias_tile_map``: the uint8 map of the bias's 128 x 64 tiles
+    that hold an entry above -inf (allocated when not given)."""
+    lib = load_library()
+    torch = _torch()
+    dev = bias.device
+    if bias.dtype not in (torch.bfloat16, torch.float16):
+        raise ValueError("tile maps are built for bf16 or fp16 biases")
+    sb, sh, sq = _bias_strides(bias, B, H, Nq, Nk, bias.dtype, dev)
+    n = lib.fa_bias_tile_map_size(sb, sh, B, H, Nq, Nk)
+    if tile_map is None:
+        tile_map = torch.empty(max(n, 1), dtype=torch.uint8, device=dev)
+    st = lib.fa_bias_tile_map(_ptr(bias), sb, sh, sq, B, H, Nq, Nk, _dtype_code(bias),
+                              _ptr(tile_map), tile_map.numel(), _stream_handle(dev, stream))
+    if st != FA_OK:
+        raise FAError(st, "fa_bias_tile_map")
+    return tile_map
+
+
 def fa_fwd_ex(Q, K, V, O, L, scale, causal, bias=None, dropout_p=0.0, seed=0, offset=0,
-              stream=None):
+              stream=None, tile_map=None):
     """Call ``fa_fwd_ex``: optional additive bias and optional dropout on P."""
     lib = load_library()
     B, H, Nq, d = Q.shape
@@ -297,6 +320,7 @@ def fa_fwd_ex(Q, K, V, O, L, scale, causal, bias=None, dropout_p=0.0, seed=0, of
     _check_dropout(dropout_p, seed, offset)
     sb, sh, sq = (0, 0, 0) if bias is None else _bias_strides(bias, B, H, Nq, Nk, Q.dtype, dev)
     st = lib.fa_fwd_ex(_ptr(Q), _ptr(K), _ptr(V), None if bias is None else _ptr(bias), sb, sh, sq,
+                       None if tile_map is None else _ptr(tile_map),
                        float(dropout_p), int(seed), int(offset), _ptr(O), _ptr(L), B, H, Nq, Nk, d,
                        float(scale), int(bool(causal)), _dtype_code(Q), _stream_handle(dev, stream))
     if st != FA_OK:
@@ -305,7 +329,7 @@ def fa_fwd_ex(Q, K, V, O, L, scale, causal, bias=None, dropout_p=0.0, seed=0, of
 
 
 def fa_bwd_ex(Q, K, V, O, L, dO, dQ, dK, dV, scale, causal, bias=None, dropout_p=0.0, seed=0,
-              offset=0, workspace=None, stream=None):
+              offset=0, workspace=None, stream=None, tile_map=None):
     """Call ``fa_bwd_ex`` with the bias and dropout arguments the forward pass used."""
     lib = load_library()
     B, H, Nq, d = Q.shape
@@ -325,6 +349,7 @@ def fa_bwd_ex(Q, K, V, O, L, dO, dQ, dK, dV, scale, causal, bias=None, dropout_p
         workspace = _alloc_workspace(need, dev)
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     st = lib.fa_bwd_ex(_ptr(Q), _ptr(K), _ptr(V), None if bias is None else _ptr(bias), sb, sh, sq,
+                       None if tile_map is None else _ptr(tile_map),
                        float(dropout_p), int(seed), int(offset), _ptr(O), _ptr(L), _ptr(dO),
                        _ptr(dQ), _ptr(dK), _ptr(dV), B, H, Nq, Nk, d, float(scale),
                        int(bool(causal)), code, _ptr(workspace), ws_bytes,
@@ -335,7 +360,7 @@ def fa_bwd_ex(Q, K, V, O, L, dO, dQ, dK, dV, scale, causal, bias=None, dropout_p
 
 
 def forward(Q, K, V, scale=None, causal=False, num_splits=0, stream=None, bias=None,
-            dropout_p=0.0, seed=0, offset=0):
+            dropout_p=0.0, seed=0, offset=0, tile_map=None):
     """Allocate O, L and run ``fa_fwd`` (``fa_fwd_bias`` with a bias, ``fa_fwd_ex``
     with dropout).  Returns (O, L)."""
     torch = _torch()
@@ -344,16 +369,16 @@ def forward(Q, K, V, scale=None, causal=False, num_splits=0, stream=None, bias=N
         scale = 1.0 / math.sqrt(d)
     O = torch.empty_like(Q)
     L = torch.empty((B, H, Nq), dtype=torch.float32, device=Q.device)
-    if dropout_p:
+    if dropout_p or tile_map is not None:
         return fa_fwd_ex(Q, K, V, O, L, scale, causal, bias=bias, dropout_p=dropout_p, seed=seed,
-                         offset=offset, stream=stream)
+                         offset=offset, stream=stream, tile_map=tile_map)
     if bias is not None:
         return fa_fwd_bias(Q, K, V, bias, O, L, scale, causal, stream=stream)
     return fa_fwd(Q, K, V, O, L, scale, causal, num_splits=num_splits, stream=stream)
 
 
 def backward(Q, K, V, O, L, dO, scale=None, causal=False, stream=None, bias=None, dropout_p=0.0,
-             seed=0, offset=0):
+             seed=0, offset=0, tile_map=None):
     """Allocate dQ, dK, dV and run ``fa_bwd`` (or the bias / dropout entry point
     matching the forward call).  Returns (dQ, dK, dV)."""
     torch = _torch()
@@ -363,9 +388,10 @@ def backward(Q, K, V, O, L, dO, scale=None, causal=False, stream=None, bias=None
     dQ = torch.empty_like(Q)
     dK = torch.empty_like(K)
     dV = torch.empty_like(V)
-    if dropout_p:
+    if dropout_p or tile_map is not None:
         return fa_bwd_ex(Q, K, V, O, L, dO, dQ, dK, dV, scale, causal, bias=bias,
-                         dropout_p=dropout_p, seed=seed, offset=offset, stream=stream)
+                         dropout_p=dropout_p, seed=seed, offset=offset, stream=stream,
+                         tile_map=tile_map)
     if bias is not None:
         return fa_bwd_bias(Q, K, V, bias, O, L, dO, dQ, dK, dV, scale, causal, stream=stream)
     return fa_bwd(Q, K, V, O, L, dO, dQ, dK, dV, scale, causal, stream=stream)

@@ -15,7 +15,7 @@ INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(PKG, "libfa.so")
 OBJDIR = os.path.join(PKG, "_build")
 
-SOURCES = ["fa_api.cpp", "fa_fwd.hip", "fa_bwd.hip", "fa_split.hip"]
+SOURCES = ["fa_api.cpp", "fa_fwd.hip", "fa_bwd.hip", "fa_split.hip", "fa_tilemap.hip"]
 ARCH = os.environ.get("FA_OFFLOAD_ARCH", "gfx950")
 
 COMMON_FLAGS = [

@@ -160,6 +160,34 @@ namespace {
 
 // Additive-bias checks (see fa_fwd_bias): rows of at least Nk elements, 16-byte
 // aligned rows and head blocks, element offsets within a head below 2^30.
+// Geometry of a bias tile map: Bb x Hb heads of nqt rows of nkt4 bytes.
+struct MapGeom {
+  long long Bb, Hb, nqt, nkt4;
+  long long bytes() const { return Bb * Hb * nqt * nkt4; }
+};
+MapGeom map_geom(long long sb, long long sh, int B, int H, int Nq, int Nk) {
+  MapGeom g;
+  g.Bb = sb ? B : 1;
+  g.Hb = sh ? H : 1;
+  g.nqt = (Nq + 127) / 128;
+  g.nkt4 = ((Nk + 63) / 64 + 3) / 4 * 4;
+  return g;
+}
+
+// Attach a caller's tile map to the bias arguments (bias already checked).
+fa_status attach_map(const unsigned char* map, int B, int H, int Nq, int Nk, fa_dtype dtype,
+                     fa::BiasArgs* b) {
+  if (!map) return FA_OK;
+  if (!b->ptr || dtype == FA_FP32) return FA_ERR_UNSUPPORTED;
+  if (!aligned(map)) return FA_ERR_ALIGN;
+  const MapGeom g = map_geom(b->sb, b->sh, B, H, Nq, Nk);
+  b->tmap = map;
+  b->nkt4 = (int)g.nkt4;
+  b->tm_sh = b->sh ? g.nqt * g.nkt4 : 0;
+  b->tm_sb = b->sb ? g.Hb * g.nqt * g.nkt4 : 0;
+  return FA_OK;
+}
+
 fa_status check_bias(const void* bias, long long sb, long long sh, long long sq, int Nq, int Nk) {
   if (!bias) return FA_ERR_NULL;
   if (!aligned(bias)) return FA_ERR_ALIGN;
@@ -324,9 +352,10 @@ fa_status fa_bwd_bias(const void* Q, const void* K, const void* V, const void* b
 }
 
 fa_status fa_fwd_ex(const void* Q, const void* K, const void* V, const void* bias,
-                    long long bias_sb, long long bias_sh, long long bias_sq, float dropout_p,
-                    unsigned long long seed, unsigned int offset, void* O, float* L, int B, int H,
-                    int Nq, int Nk, int d, float scale, int causal, fa_dtype dtype, void* stream) {
+                    long long bias_sb, long long bias_sh, long long bias_sq,
+                    const unsigned char* bias_tile_map, float dropout_p, unsigned long long seed,
+                    unsigned int offset, void* O, float* L, int B, int H, int Nq, int Nk, int d,
+                    float scale, int causal, fa_dtype dtype, void* stream) {
   fa_status st = check_dims(B, H, Nq, Nk, d, scale, causal, dtype);
   if (st != FA_OK) return st;
   fa::DropArgs dr;
@@ -342,13 +371,16 @@ fa_status fa_fwd_ex(const void* Q, const void* K, const void* V, const void* bia
     b.sh = bias_sh;
     b.sq = bias_sq;
   }
+  st = attach_map(bias_tile_map, B, H, Nq, Nk, dtype, &b);
+  if (st != FA_OK) return st;
   return fwd_impl(Q, K, V, b, dr, O, L, B, H, Nq, Nk, d, scale, causal, dtype, -1, nullptr, 0,
                   stream);
 }
 
 fa_status fa_bwd_ex(const void* Q, const void* K, const void* V, const void* bias,
-                    long long bias_sb, long long bias_sh, long long bias_sq, float dropout_p,
-                    unsigned long long seed, unsigned int offset, const void* O, const float* L,
+                    long long bias_sb, long long bias_sh, long long bias_sq,
+                    const unsigned char* bias_tile_map, float dropout_p, unsigned long long seed,
+                    unsigned int offset, const void* O, const float* L,
                     const void* dO, void* dQ, void* dK, void* dV, int B, int H, int Nq, int Nk,
                     int d, float scale, int causal, fa_dtype dtype, void* workspace,
                     size_t workspace_bytes, void* stream) {
@@ -365,9 +397,41 @@ fa_status fa_bwd_ex(const void* Q, const void* K, const void* V, const void* bia
     b.sb = bias_sb;
     b.sh = bias_sh;
     b.sq = bias_sq;
+    st = attach_map(bias_tile_map, B, H, Nq, Nk, dtype, &b);
+    if (st != FA_OK) return st;
+  } else if (bias_tile_map && !bias) {
+    return FA_ERR_UNSUPPORTED;
   }
   return bwd_impl(Q, K, V, b, dr, O, L, dO, dQ, dK, dV, B, H, Nq, Nk, d, scale, causal, dtype,
                   workspace, workspace_bytes, stream, FA_BWD_ALL);
+}
+
+size_t fa_bias_tile_map_size(long long bias_sb, long long bias_sh, int B, int H, int Nq,
+                             int Nk) {
+  if (B < 0 || H < 0 || Nq < 0 || Nk < 0) return 0;
+  return (size_t)map_geom(bias_sb, bias_sh, B, H, Nq, Nk).bytes();
+}
+
+fa_status fa_bias_tile_map(const void* bias, long long bias_sb, long long bias_sh,
+                           long long bias_sq, int B, int H, int Nq, int Nk, fa_dtype dtype,
+                           unsigned char* tile_map, size_t tile_map_bytes, void* stream) {
+  if (!dtype_ok(dtype) || dtype == FA_FP32) return FA_ERR_UNSUPPORTED;
+  if (B < 0 || H < 0 || Nq < 0 || Nk < 0) return FA_ERR_SHAPE;
+  const MapGeom g = map_geom(bias_sb, bias_sh, B, H, Nq, Nk);
+  if (g.bytes() == 0) return FA_OK;
+  if (g.bytes() > INT_MAX) return FA_ERR_SHAPE;
+  fa_status st = check_bias(bias, bias_sb, bias_sh, bias_sq, Nq, Nk);
+  if (st != FA_OK) return st;
+  if (!tile_map) return FA_ERR_NULL;
+  if (tile_map_bytes < (size_t)g.bytes()) return FA_ERR_WORKSPACE;
+  fa::BiasArgs b;
+  b.ptr = bias;
+  b.sb = bias_sb;
+  b.sh = bias_sh;
+  b.sq = bias_sq;
+  const hipError_t e = fa::launch_bias_tile_map(b, B, H, Nq, Nk, dtype == FA_FP16, tile_map,
+                                                reinterpret_cast<hipStream_t>(stream));
+  return e == hipSuccess ? FA_OK : FA_ERR_HIP;
 }
 
 fa_status fa_bwd(const void* Q, const void* K, const void* V, const void* O, const float* L,

@@ -55,6 +55,11 @@ namespace fa {
 
 namespace {
 
+BiasDev bias_dev(const BiasArgs& b, int H, float scale) {
+  return BiasDev{b.ptr, b.sb, b.sh, b.sq, H, 1.f / scale, b.tmap, b.tm_sb, b.tm_sh, b.nkt4};
+}
+
+
 // D_i = sum_k dO_ik O_ik in fp32, and L2_i = L_i * log2(e) (the exponent
 // base of the kernels below), stored as the pair LD[i] = (L2_i, D_i) so that
 // one load brings both.
@@ -153,8 +158,26 @@ void bwd_dkdv_kernel(const T* __restrict__ Q, const T* __restrict__ K, const T* 
   const BiasReader<T> br(bias_h, bias_n);
 
   // Query blocks that can see any key of this workgroup.
-  const int nqb = (Nq + BR - 1) / BR;
-  const int qb_first = CAUSAL ? max(0, k0 - off) / BR : 0;
+  int nqb = (Nq + BR - 1) / BR;
+  int qb_first = CAUSAL ? max(0, k0 - off) / BR : 0;
+  // Bias tile map (BIAS): only the query blocks from the first to the last
+  // 128-row tile that holds an entry above -inf for one of this workgroup's
+  // four 64-key tiles.
+  if constexpr (BIAS) {
+    static_assert(BC == 4 * kMapKeys && kMapRows % BR == 0, "tile map granularity");
+    if (bias.tmap) {
+      const int b = bh / bias.H, h = bh - b * bias.H;
+      int lo, hi;
+      map_range_cols(bias.tmap + b * bias.tm_sb + h * bias.tm_sh, (Nq + kMapRows - 1) / kMapRows,
+                     bias.nkt4, k0 / kMapKeys, lane, lo, hi);
+      if (lo > hi) {
+        nqb = qb_first;
+      } else {
+        qb_first = max(qb_first, lo * (kMapRows / BR));
+        nqb = min(nqb, (hi + 1) * (kMapRows / BR));
+      }
+    }
+  }
   const int nloop = nqb - qb_first;
 
   // Direct-to-LDS loads of query block qb through buffer resources: this
@@ -512,15 +535,34 @@ void bwd_dq_kernel(const T* __restrict__ Q, const T* __restrict__ K, const T* __
     const float drow = (qrow < Nq) ? LD[2 * ((size_t)bh * Nq + qrow) + 1] : 0.f;
 
     const int kend = CAUSAL ? min(Nk, q0 + BR + off) : Nk;
-    const int ntiles = (kend + BC - 1) / BC;
+    int ntiles = (kend + BC - 1) / BC;
+    int jbeg = 0;
+    // Bias tile map (BIAS): only the key tiles from the first to the last that
+    // hold an entry above -inf for this query tile (jbeg stays even, so tile
+    // j keeps buffers j & 1).
+    if constexpr (BIAS) {
+      static_assert(BR == kMapRows && BC == kMapKeys, "tile map granularity");
+      if (bias.tmap) {
+        const int b = bh / bias.H, h = bh - b * bias.H;
+        int lo, hi;
+        map_range(bias.tmap + b * bias.tm_sb + h * bias.tm_sh + (size_t)qt * bias.nkt4,
+                  (Nk + BC - 1) / BC, lane, lo, hi);
+        if (lo > hi) {
+          ntiles = 0;
+        } else {
+          jbeg = lo & ~1;
+          ntiles = min(ntiles, hi + 1);
+        }
+      }
+    }
     const int wrow_lo = q0 + wave * 32;
 
     f32x16 dqacc[NNT];
 #pragma unroll
     for (int nt = 0; nt < NNT; ++nt) dqacc[nt] = (f32x16){};
 
-    kv.tile(Kh, 0, Nk, sK0);
-    kv.tile(Vh, 0, Nk, sV0);
+    kv.tile(Kh, jbeg * BC, Nk, sK0);
+    kv.tile(Vh, jbeg * BC, Nk, sV0);
     vm_wait_all();
     __syncthreads();
 
@@ -637,7 +679,7 @@ void bwd_dq_kernel(const T* __restrict__ Q, const T* __restrict__ K, const T* __
       vm_wait_all();  // this wave's part of tile j+1 has landed
       __syncthreads();
     };
-    for (int j = 0; j < ntiles; j += 2) {
+    for (int j = jbeg; j < ntiles; j += 2) {
       tile_step(0, j);
       if (j + 1 < ntiles) tile_step(1, j + 1);
     }
@@ -808,7 +850,7 @@ hipError_t launch_bwd_mfma(const BwdArgs& a, int stages, hipStream_t s) {
   const T* K = (const T*)a.K;
   const T* V = (const T*)a.V;
   const T* dO = (const T*)a.dO;
-  const BiasDev bias{a.bias.ptr, a.bias.sb, a.bias.sh, a.bias.sq, a.H, 1.f / a.scale};
+  const BiasDev bias = bias_dev(a.bias, a.H, a.scale);
   const DropDev drop = drop_dev(a.drop);
   if (stages & 1) {
     const hipError_t e = (a.d == 128) ? launch_pre<128, T>(a, s) : launch_pre<64, T>(a, s);
@@ -879,7 +921,7 @@ hipError_t launch_bwd_f32(const BwdArgs& a, int stages, hipStream_t s) {
   const float* K = (const float*)a.K;
   const float* V = (const float*)a.V;
   const float* dO = (const float*)a.dO;
-  const BiasDev bias{a.bias.ptr, a.bias.sb, a.bias.sh, a.bias.sq, a.H, 1.f / a.scale};
+  const BiasDev bias = bias_dev(a.bias, a.H, a.scale);
   const DropDev drop = drop_dev(a.drop);
   if ((stages & 2) && nkt > 0) {
 #define FA_DKDV32_LAUNCH(DD, CC)                                                             \

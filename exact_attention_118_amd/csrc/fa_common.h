@@ -220,12 +220,58 @@ struct BufTile {
 // ptr[b*sb + h*sh + i*sq + j] (16-bit elements; sq a multiple of 8), folded
 // into the raw scores as bias * inv_scale so that the exponent stays
 // s * scale * log2(e) - m.
+//
+// Optional tile map of the bias (tmap != nullptr): one byte per 128-row x
+// 64-key tile of each bias head, nonzero iff the tile holds an entry above
+// -inf; tile (b, h, qt, kt) at tmap[b*tm_sb + h*tm_sh + qt*nkt4 + kt], rows
+// padded with zeros to nkt4 (a multiple of 4) bytes.  The kernels visit only
+// the tiles between the first and the last nonzero byte of their row (or
+// column) of the map: all-masked tiles contribute exact zeros.
+constexpr int kMapRows = 128;
+constexpr int kMapKeys = 64;
+
 struct BiasDev {
   const void* ptr;
   long long sb, sh, sq;
   int H;
   float inv_scale;
+  const unsigned char* tmap;
+  long long tm_sb, tm_sh;
+  int nkt4;
 };
+
+// First and last nonzero byte of row[0 .. n) (lo > hi when none), over the
+// wave: lane i reads bytes i, i + 64, ...; the result is wave-uniform.
+__device__ __forceinline__ void map_range(const unsigned char* row, int n, int lane, int& lo,
+                                          int& hi) {
+  lo = 0x7fffffff;
+  hi = -1;
+  for (int base = 0; base < n; base += 64) {
+    const int i = base + lane;
+    const unsigned long long m = __builtin_amdgcn_ballot_w64(i < n && row[i] != 0);
+    if (m != 0ull) {
+      lo = min(lo, base + (int)__builtin_ctzll(m));
+      hi = base + 63 - (int)__builtin_clzll(m);
+    }
+  }
+}
+
+// First and last query tile qt in [0, nqt) whose bytes kt0 .. kt0+3 of the
+// map (a 4-byte aligned word) are not all zero; lo > hi when none.
+__device__ __forceinline__ void map_range_cols(const unsigned char* head, int nqt, int nkt4,
+                                               int kt0, int lane, int& lo, int& hi) {
+  lo = 0x7fffffff;
+  hi = -1;
+  for (int base = 0; base < nqt; base += 64) {
+    const int qt = base + lane;
+    const unsigned w = qt < nqt ? *(const unsigned*)(head + (size_t)qt * nkt4 + kt0) : 0u;
+    const unsigned long long m = __builtin_amdgcn_ballot_w64(w != 0u);
+    if (m != 0ull) {
+      lo = min(lo, base + (int)__builtin_ctzll(m));
+      hi = base + 63 - (int)__builtin_clzll(m);
+    }
+  }
+}
 
 // Reads of an additive bias through a buffer descriptor over one head's bias
 // block of `nelem` 16-bit elements (element offsets below 2^30): loads past

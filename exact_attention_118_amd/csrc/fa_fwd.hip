@@ -41,6 +41,11 @@ namespace fa {
 
 namespace {
 
+BiasDev bias_dev(const BiasArgs& b, int H, float scale) {
+  return BiasDev{b.ptr, b.sb, b.sh, b.sq, H, 1.f / scale, b.tmap, b.tm_sb, b.tm_sh, b.nkt4};
+}
+
+
 constexpr int kFwdBR = 128;  // query rows per workgroup
 constexpr int kFwdBC = 64;   // keys per K/V tile
 constexpr int kFwdThreads = 256;
@@ -168,8 +173,26 @@ void fwd_kernel(const T* __restrict__ Q, const T* __restrict__ K, const T* __res
     // so tile j still uses buffers j & 1).
     const int kbeg = SPLIT ? sp * split.chunk : 0;
     const int kend = min(CAUSAL ? min(Nk, q0 + BR + off) : Nk, SPLIT ? kbeg + split.chunk : Nk);
-    const int ntiles = (kend + BC - 1) / BC;
-    const int jbeg = kbeg / BC;
+    int ntiles = (kend + BC - 1) / BC;
+    int jbeg = kbeg / BC;
+    // Bias tile map (BIAS): only the key tiles from the first to the last that
+    // hold an entry above -inf for this query tile (jbeg stays even).
+    if constexpr (BIAS) {
+      static_assert(BR == kMapRows && BC == kMapKeys, "tile map granularity");
+      if (bias.tmap) {
+        const int b = bh / bias.H, h = bh - b * bias.H;
+        int lo, hi;
+        map_range(bias.tmap + b * bias.tm_sb + h * bias.tm_sh + (size_t)qt * bias.nkt4,
+                  (Nk + BC - 1) / BC, lane, lo, hi);
+        if (lo > hi) {
+          ntiles = jbeg;
+        } else {
+          jbeg = max(jbeg, lo & ~1);
+          ntiles = min(ntiles, hi + 1);
+        }
+      }
+    }
+    const int kfirst = jbeg * BC;
     const int wrow_lo = q0 + wave * 32;  // smallest query row of this wave
 
     float m_run = -INFINITY;  // reference of the exponentials (row max so far, log2 units)
@@ -233,19 +256,19 @@ void fwd_kernel(const T* __restrict__ Q, const T* __restrict__ K, const T* __res
     };
 
     // Prologue: K tiles 0 and 1, V tile 0; scores, mask and row max of tile 0.
-    kv.tile(Kh, kbeg, Nk, sK0);
-    kv.tile(Kh, kbeg + BC, Nk, sK0 + TILE);
-    kv.tile(Vh, kbeg, Nk, sV0);
+    kv.tile(Kh, kfirst, Nk, sK0);
+    kv.tile(Kh, kfirst + BC, Nk, sK0 + TILE);
+    kv.tile(Vh, kfirst, Nk, sV0);
     vm_wait_all();
     __syncthreads();
     f32x16 sA[2], sB[2];
     scores(0, sA);
     if constexpr (BIAS) {
       BT4 bb[8];
-      bias_load(bb, kbeg);
+      bias_load(bb, kfirst);
       bias_add(sA, bb);
     }
-    mask_tile(sA, kbeg);
+    mask_tile(sA, kfirst);
     float mx_next = row_max(sA);
     __syncthreads();  // every wave is done with K tile 0 before tile 2 replaces it
 
@@ -528,7 +551,7 @@ hipError_t launch_fwd_mfma(const FwdArgs& a, hipStream_t s) {
   const T* K = (const T*)a.K;
   const T* V = (const T*)a.V;
   T* O = (T*)a.O;
-  const BiasDev bias{a.bias.ptr, a.bias.sb, a.bias.sh, a.bias.sq, a.H, 1.f / a.scale};
+  const BiasDev bias = bias_dev(a.bias, a.H, a.scale);
   const DropDev drop = drop_dev(a.drop);
   const SplitDev nosplit{nullptr, nullptr, 1, 0, 0};
 #define FA_FWD_LAUNCH(DD, CC)                                                                 \
@@ -557,7 +580,7 @@ hipError_t launch_fwd_rows_split(const FwdArgs& a, int splits, int chunk, float*
   const T* Q = (const T*)a.Q;
   const T* K = (const T*)a.K;
   const T* V = (const T*)a.V;
-  const BiasDev nobias{nullptr, 0, 0, 0, a.H, 1.f};
+  const BiasDev nobias = bias_dev(BiasArgs{}, a.H, 1.f);
   const DropDev nodrop = drop_dev(DropArgs{});
   const SplitDev split{part_o, part_l, splits, chunk, BH * a.Nq};
 #define FA_FWD_SPLIT_LAUNCH(DD, CC)                                                           \
@@ -603,7 +626,7 @@ hipError_t launch_fwd_f32(const FwdArgs& a, hipStream_t s) {
   const float* K = (const float*)a.K;
   const float* V = (const float*)a.V;
   float* O = (float*)a.O;
-  const BiasDev bias{a.bias.ptr, a.bias.sb, a.bias.sh, a.bias.sq, a.H, 1.f / a.scale};
+  const BiasDev bias = bias_dev(a.bias, a.H, a.scale);
   const DropDev drop = drop_dev(a.drop);
 #define FA_FWD32_LAUNCH(DD, CC)                                                              \
   do {                                                                                       \

@@ -10,9 +10,15 @@ namespace fa {
 
 // Optional additive bias: element (b, h, i, j) at ptr[b*sb + h*sh + i*sq + j]
 // (ptr == nullptr: none).  Same element type as Q.
+// Optional tile map of that bias (tmap == nullptr: none): byte (b, h, qt, kt)
+// at tmap[b*tm_sb + h*tm_sh + qt*nkt4 + kt], nonzero iff the 128-row x 64-key
+// tile holds an entry above -inf.
 struct BiasArgs {
   const void* ptr = nullptr;
   long long sb = 0, sh = 0, sq = 0;
+  const unsigned char* tmap = nullptr;
+  long long tm_sb = 0, tm_sh = 0;
+  int nkt4 = 0;
 };
 
 // Optional dropout on the normalised probabilities (on == false: none).  A
@@ -84,6 +90,11 @@ hipError_t launch_split_combine_bf16(const FwdArgs& a, int splits, const float* 
                                      const float* part_l, hipStream_t s);
 hipError_t launch_split_combine_f16(const FwdArgs& a, int splits, const float* part_o,
                                     const float* part_l, hipStream_t s);
+
+// Tile map of a bias (16-bit dtypes): one byte per 128-row x 64-key tile of
+// each bias head (Bb = sb ? B : 1, Hb = sh ? H : 1 heads), rows of nkt4 bytes.
+hipError_t launch_bias_tile_map(const BiasArgs& bias, int B, int H, int Nq, int Nk, bool fp16,
+                                unsigned char* tmap, hipStream_t s);
 
 // Key-chunk length used by the split path for `splits` chunks of Nk keys.
 int split_chunk(int Nk, int splits);

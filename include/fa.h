@@ -170,21 +170,47 @@ fa_status fa_bwd_bias(const void* Q, const void* K, const void* V, const void* b
  *  word i mod 4 is that score's byte.  A new offset (or seed) gives a new
  *  mask; fa_bwd_ex must be given the dropout_p, seed and offset (and bias)
  *  that fa_fwd_ex used, and regenerates the mask from them.
+ *  bias_tile_map: NULL, or the map that fa_bias_tile_map wrote for this
+ *  bias and these B, H, Nq, Nk (16-byte aligned; it needs a bias and a
+ *  16-bit dtype, else FA_ERR_UNSUPPORTED).  With it the kernels skip the
+ *  tiles of all -inf entries at the ends of each query tile's key range and
+ *  of each key block's query range; the results are the same as without it.
  *  Both always take the tiled path (no key splits; fa_fwd_ex needs no
  *  workspace); the other arguments, rules and errors are those of fa_fwd,
  *  fa_bwd and fa_fwd_bias.
  */
 fa_status fa_fwd_ex(const void* Q, const void* K, const void* V, const void* bias,
-                    long long bias_sb, long long bias_sh, long long bias_sq, float dropout_p,
-                    unsigned long long seed, unsigned int offset, void* O, float* L, int B, int H,
-                    int Nq, int Nk, int d, float scale, int causal, fa_dtype dtype, void* stream);
+                    long long bias_sb, long long bias_sh, long long bias_sq,
+                    const unsigned char* bias_tile_map, float dropout_p, unsigned long long seed,
+                    unsigned int offset, void* O, float* L, int B, int H, int Nq, int Nk, int d,
+                    float scale, int causal, fa_dtype dtype, void* stream);
 
 fa_status fa_bwd_ex(const void* Q, const void* K, const void* V, const void* bias,
-                    long long bias_sb, long long bias_sh, long long bias_sq, float dropout_p,
-                    unsigned long long seed, unsigned int offset, const void* O, const float* L,
-                    const void* dO, void* dQ, void* dK, void* dV, int B, int H, int Nq, int Nk,
-                    int d, float scale, int causal, fa_dtype dtype, void* workspace,
-                    size_t workspace_bytes, void* stream);
+                    long long bias_sb, long long bias_sh, long long bias_sq,
+                    const unsigned char* bias_tile_map, float dropout_p, unsigned long long seed,
+                    unsigned int offset, const void* O, const float* L, const void* dO, void* dQ,
+                    void* dK, void* dV, int B, int H, int Nq, int Nk, int d, float scale,
+                    int causal, fa_dtype dtype, void* workspace, size_t workspace_bytes,
+                    void* stream);
+
+/*
+ * Tile map of an additive bias, for skipping all-masked tiles: one byte per
+ * tile of 128 query rows x 64 keys of each bias head, 1 iff the tile holds an
+ * entry above -inf (NaN counts as present), else 0.  Layout [Bb][Hb][nqt][nkt4]
+ * with Bb = (bias_sb ? B : 1), Hb = (bias_sh ? H : 1), nqt = ceil(Nq / 128),
+ * nkt4 = ceil(Nk / 64) rounded up to a multiple of 4 (padding bytes 0).  A
+ * block-sparse bias (a band, blocks along the diagonal, key padding) is the
+ * intended use: the custom masks the 51CTO FlashAttention V1/V2 notes cite as
+ * a reason for one's own kernel.  The kernel reads the bias once; compute the
+ * map once per bias and pass it to every fa_fwd_ex / fa_bwd_ex call with it.
+ * bias arguments as for fa_fwd_bias; bf16 or fp16 only (FA_ERR_UNSUPPORTED
+ * otherwise); tile_map_bytes below fa_bias_tile_map_size: FA_ERR_WORKSPACE.
+ */
+size_t fa_bias_tile_map_size(long long bias_sb, long long bias_sh, int B, int H, int Nq, int Nk);
+
+fa_status fa_bias_tile_map(const void* bias, long long bias_sb, long long bias_sh,
+                           long long bias_sq, int B, int H, int Nq, int Nk, fa_dtype dtype,
+                           unsigned char* tile_map, size_t tile_map_bytes, void* stream);
 
 /* Workspace bytes fa_fwd needs for these arguments (0 when none). */
 size_t fa_fwd_workspace_size(int B, int H, int Nq, int Nk, int d, fa_dtype dtype, int num_splits);

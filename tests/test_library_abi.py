@@ -171,13 +171,13 @@ def test_bias_entry_points_accept_empty_problems(lib):
 
 
 def fwd_ex(lib, bias=None, sq=16, p=0.0, seed=1, offset=0, Q=A, B=1, Nq=16, Nk=16, d=64,
-           scale=0.125, causal=0):
-    return lib.fa_fwd_ex(Q, A, A, bias, 0, 0, sq, p, seed, offset, A, A, B, 1, Nq, Nk, d, scale,
-                         causal, fa.FA_BF16, None)
+           scale=0.125, causal=0, tmap=None, dtype=fa.FA_BF16):
+    return lib.fa_fwd_ex(Q, A, A, bias, 0, 0, sq, tmap, p, seed, offset, A, A, B, 1, Nq, Nk, d,
+                         scale, causal, dtype, None)
 
 
-def bwd_ex(lib, bias=None, sq=16, p=0.0, ws=None, ws_bytes=0, Q=A, B=1, Nq=16):
-    return lib.fa_bwd_ex(Q, A, A, bias, 0, 0, sq, p, 1, 0, A, A, A, A, A, A, B, 1, Nq, 16, 64,
+def bwd_ex(lib, bias=None, sq=16, p=0.0, ws=None, ws_bytes=0, Q=A, B=1, Nq=16, tmap=None):
+    return lib.fa_bwd_ex(Q, A, A, bias, 0, 0, sq, tmap, p, 1, 0, A, A, A, A, A, A, B, 1, Nq, 16, 64,
                          0.125, 0, fa.FA_BF16, ws, ws_bytes, None)
 
 
@@ -199,11 +199,35 @@ def test_ex_entry_points_reject_bad_arguments(lib):
     assert bwd_ex(lib, p=0.5, ws=A, ws_bytes=need, bias=A, sq=8) == fa.FA_ERR_SHAPE
 
 
+def test_tile_map_arguments(lib):
+    # the map needs a bias and a 16-bit dtype, 16-byte aligned
+    assert fwd_ex(lib, bias=None, tmap=A, p=0.5) == fa.FA_ERR_UNSUPPORTED
+    assert fwd_ex(lib, bias=A, tmap=A, dtype=fa.FA_FP32) == fa.FA_ERR_UNSUPPORTED
+    assert fwd_ex(lib, bias=A, tmap=MIS) == fa.FA_ERR_ALIGN
+    need = lib.fa_bwd_workspace_size(1, 1, 16, 16, 64, fa.FA_BF16)
+    assert bwd_ex(lib, bias=None, tmap=A, ws=A, ws_bytes=need) == fa.FA_ERR_UNSUPPORTED
+    assert bwd_ex(lib, bias=A, tmap=MIS, ws=A, ws_bytes=need) == fa.FA_ERR_ALIGN
+    # size: [Bb][Hb][ceil(Nq/128)][ceil(Nk/64) rounded up to 4]
+    assert lib.fa_bias_tile_map_size(0, 0, 2, 3, 300, 1000) == 1 * 1 * 3 * 16
+    assert lib.fa_bias_tile_map_size(8, 8, 2, 3, 128, 64) == 2 * 3 * 1 * 4
+    assert lib.fa_bias_tile_map_size(0, 8, 2, 3, 129, 257) == 1 * 3 * 2 * 8
+    assert lib.fa_bias_tile_map_size(0, 0, 1, 1, 0, 64) == 0
+    tm = lambda **k: lib.fa_bias_tile_map(k.get("bias", A), 0, 0, k.get("sq", 16), 1, 1, 16,
+                                          k.get("Nk", 16), k.get("dtype", fa.FA_BF16),
+                                          k.get("map", A), k.get("nbytes", 4), None)
+    assert tm(dtype=fa.FA_FP32) == fa.FA_ERR_UNSUPPORTED
+    assert tm(bias=None) == fa.FA_ERR_NULL
+    assert tm(bias=MIS) == fa.FA_ERR_ALIGN
+    assert tm(sq=8) == fa.FA_ERR_SHAPE
+    assert tm(map=None) == fa.FA_ERR_NULL
+    assert tm(nbytes=3) == fa.FA_ERR_WORKSPACE
+
+
 def test_ex_entry_points_accept_empty_problems(lib):
     assert fwd_ex(lib, p=0.5, Q=None, B=0) == fa.FA_OK
     assert fwd_ex(lib, p=0.5, Q=None, Nq=0) == fa.FA_OK
-    assert lib.fa_bwd_ex(*([None] * 4), 0, 0, 0, 0.5, 1, 0, *([None] * 6), 0, 1, 16, 16, 64, 0.125,
-                         0, fa.FA_BF16, None, 0, None) == fa.FA_OK
+    assert lib.fa_bwd_ex(*([None] * 4), 0, 0, 0, None, 0.5, 1, 0, *([None] * 6), 0, 1, 16, 16, 64,
+                         0.125, 0, fa.FA_BF16, None, 0, None) == fa.FA_OK
 
 
 def test_workspace_queries(lib):
