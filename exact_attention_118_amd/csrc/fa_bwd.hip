@@ -147,15 +147,38 @@ void bwd_dkdv_kernel(const T* __restrict__ Q, const T* __restrict__ K, const T* 
   const size_t kbase = (size_t)bh * Nk * D;
   const size_t lbase = (size_t)bh * Nq;
 
-  // Additive bias (BIAS) of this head; this lane reads column mykey.
+  // Additive bias (BIAS) of this head, staged per query block: a tile of
+  // BR rows x BC keys per buffer, double-buffered like Q and dO and filled by
+  // the same direct-to-LDS loads (rows past Nq read as zeros; keys past Nk
+  // are masked).  Row r keeps its 16-byte chunk c at c ^ 2*(r & 3), so the
+  // transposed reads below (4 rows x 16 keys per 16 lanes) hit distinct
+  // banks.  Lane offsets are fixed; block offsets go into the descriptor.
+  constexpr int BTILE = BR * BC;                 // elements of one bias tile
+  constexpr int NIB = BTILE * 2 / 16 / 64;       // direct-to-LDS loads per bias tile
+  constexpr int IPB = NIB / kKvWaves;            // ... per wave
+  static_assert(IPB * kKvWaves == NIB, "bias tile load split");
+  __shared__ __attribute__((aligned(1024))) T sBias[BIAS ? 2 * BTILE : 8];
   const T* bias_h = nullptr;
-  long long bias_n = 0;
+  unsigned boff[IPB];
+  unsigned bread = 0;  // byte offset of this lane's transposed read of row group 0
   if constexpr (BIAS) {
     const int b = bh / bias.H, h = bh - b * bias.H;
     bias_h = (const T*)bias.ptr + b * bias.sb + h * bias.sh;
-    bias_n = (long long)(Nq - 1) * bias.sq + Nk;
+#pragma unroll
+    for (int u = 0; u < IPB; ++u) {
+      const int slot = (wave * IPB + u) * 64 + lane;
+      const int r = slot / (BC / 8), pch = slot % (BC / 8);
+      // wraps only for rows past Nq, whose reads fall outside the descriptor
+      boff[u] = (unsigned)((long long)r * bias.sq * 2) + (unsigned)((pch ^ (2 * (r & 3))) << 4);
+    }
+    // Lane l receives key kw0 + l%32 of rows 8g + 4*half + 0..3 (g = 0..3)
+    // when lane s of each 16-lane group m points at row 4*(m/2) + s/4 (+8g),
+    // keys wave*32 + (m%2)*16 + (s%4)*4 .. +3 of the tile.
+    const int m = lane >> 4;
+    const int row = 4 * (m >> 1) + (s16 >> 2);
+    const int col = wave * 32 + (m & 1) * 16 + (s16 & 3) * 4;
+    bread = (unsigned)(row * BC * 2 + (((col >> 3) ^ (2 * (row & 3))) << 4) + (col & 7) * 2);
   }
-  const BiasReader<T> br(bias_h, bias_n);
 
   // Query blocks that can see any key of this workgroup.
   int nqb = (Nq + BR - 1) / BR;
@@ -207,6 +230,20 @@ void bwd_dkdv_kernel(const T* __restrict__ Q, const T* __restrict__ K, const T* 
       const __amdgpu_buffer_rsrc_t rl = make_rsrc(LD + 2 * (lbase + qi0), rows * 8);
       __builtin_amdgcn_raw_ptr_buffer_load_lds(rl, (FA_LDS void*)&sLD[buf][0], 4, lane * 4, 0,
                                                0, 0);
+    }
+    if constexpr (BIAS) {
+      // the block's bias from row qi0, key k0 on: (Nq-1-qi0)*sq + Nk-k0 elements,
+      // the range rounded up to 16 bytes as in BiasReader
+      const long long ext = (long long)(Nq - 1 - qi0) * bias.sq + (Nk - k0);
+      const unsigned long long nb = ((unsigned long long)ext * 2 + 15) & ~15ull;
+      const __amdgpu_buffer_rsrc_t rb =
+          make_rsrc(bias_h + (size_t)qi0 * bias.sq + k0,
+                    (int)(unsigned)(nb < 0xfffffff0ull ? nb : 0xfffffff0ull));
+#pragma unroll
+      for (int u = 0; u < IPB; ++u)
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(
+            rb, (FA_LDS void*)(sBias + buf * BTILE + (wave * IPB + u) * 64 * 8), 16, boff[u], 0,
+            0, 0);
     }
 #endif
   };
@@ -270,13 +307,15 @@ void bwd_dkdv_kernel(const T* __restrict__ Q, const T* __restrict__ K, const T* 
       // needs the Q, K and dO fragments of head-dim chunk kk; those of step
       // kk + 1 are read before step kk's MFMAs are issued.
       f32x16 sacc = (f32x16){}, dpacc = (f32x16){};
-      // Bias of rows qi0 + (i/4)*8 + half*4 + i%4, key mykey (rows past Nq
-      // read zeros, keys past Nk are masked below), loaded before the MFMAs.
-      float bias_v[BIAS ? 16 : 1];
+      // Bias of rows qi0 + 8g + half*4 + 0..3, key mykey, from the staged
+      // tile (rows past Nq read zeros, keys past Nk are masked below), read
+      // before the MFMAs.
+      typename Vec<T>::x4 bq[BIAS ? 4 : 1];
       if constexpr (BIAS) {
+        const T* tb = sBias + P * BTILE;
 #pragma unroll
-        for (int i = 0; i < 16; ++i)
-          bias_v[i] = br.load1((unsigned)((qi0 + (i >> 2) * 8 + half * 4 + (i & 3)) * bias.sq + mykey));
+        for (int gq = 0; gq < 4; ++gq)
+          bq[gq] = lds_read_tr<T>(to_lds(at_byte<T>(tb, bread + gq * 8 * BC * 2)));
       }
       {
         auto ldstep = [&](int kk, T8* f) {
@@ -298,7 +337,8 @@ void bwd_dkdv_kernel(const T* __restrict__ Q, const T* __restrict__ K, const T* 
       }
       if constexpr (BIAS) {
 #pragma unroll
-        for (int i = 0; i < 16; ++i) sacc[i] = fmaf(bias_v[i], bias.inv_scale, sacc[i]);
+        for (int i = 0; i < 16; ++i)
+          sacc[i] = fmaf((float)bq[i >> 2][i & 3], bias.inv_scale, sacc[i]);
       }
       // Lane holds key mykey and rows (i/4)*8 + half*4 + i%4 of the block.
       // Rows past the end and, causal, rows before the key's diagonal get
