@@ -635,8 +635,8 @@ void bwd_dq_kernel(const T* __restrict__ Q, const T* __restrict__ K, const T* __
       // Dropout (DROP): byte e of rb[mt][c] is the random byte of row qrow
       // and key k0 + mt*32 + c*8 + half*4 + e; dP is masked and scaled before
       // dS = P (dP - D).
+      // Each half's bytes are made just before its dS elements.
       unsigned rb[2][4];
-      if constexpr (DROP) drop_bytes_rows(rb, drop, bh, qrow, k0 + half * 4, lane);
       auto ds_elem = [&](int mt, int i) {
         const float p = fast_exp2(fmaf(sacc[mt][i], c, -l2));
         float dp = dpacc[mt][i];
@@ -710,9 +710,11 @@ void bwd_dq_kernel(const T* __restrict__ Q, const T* __restrict__ K, const T* __
       sdp_half(0, false);
       bias_half(0);
       mask_half(0);
+      if constexpr (DROP) drop_bytes_rows(rb[0], drop, bh, qrow, k0 + half * 4, lane);
       sdp_half(1, true);   // dS of half 0 overlaps the MFMAs of half 1
       bias_half(1);
       mask_half(1);
+      if constexpr (DROP) drop_bytes_rows(rb[1], drop, bh, qrow, k0 + 32 + half * 4, lane);
       dq_half(0, true);    // dS of half 1 overlaps dQ of half 0
       dq_half(1, false);
 

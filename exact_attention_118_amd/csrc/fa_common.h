@@ -389,22 +389,19 @@ __device__ __forceinline__ void byte_transpose(unsigned (&x)[4]) {
 }
 
 // Random bytes for a lane that holds query row `row` and keys
-// key0 + s*32 + c*8 + e (s = 0, 1; c, e = 0..3; key0 a multiple of 4), the
-// lanes of its quad holding rows 4a .. 4a+3 and the same keys: each lane
-// makes two of the quad's eight calls, then the quad exchanges words.  On
-// exit byte e of x[s][c] belongs to (row, key0 + s*32 + c*8 + e).
-__device__ __forceinline__ void drop_bytes_rows(unsigned (&x)[2][4], const DropDev& dr, int bh,
+// key0 + c*8 + e (c, e = 0..3; key0 a multiple of 4), the lanes of its quad
+// holding rows 4a .. 4a+3 and the same keys: each lane makes one of the
+// quad's four calls (key block (key0 + 8t) / 4 for quad lane t), then the quad
+// exchanges words.  On exit byte e of x[c] belongs to (row, key0 + c*8 + e).
+__device__ __forceinline__ void drop_bytes_rows(unsigned (&x)[4], const DropDev& dr, int bh,
                                                 int row, int key0, int lane) {
   const int t = lane & 3;
-#pragma unroll
-  for (int sblk = 0; sblk < 2; ++sblk) {
-    unsigned w[4] = {(unsigned)(key0 + sblk * 32 + t * 8) >> 2, (unsigned)row >> 2,
-                     (unsigned)bh, dr.offset};
-    philox4x32_10(w, dr.seed_lo, dr.seed_hi);
-    quad_transpose(w, lane);
-#pragma unroll
-    for (int c = 0; c < 4; ++c) x[sblk][c] = w[c];
-  }
+  x[0] = (unsigned)(key0 + t * 8) >> 2;
+  x[1] = (unsigned)row >> 2;
+  x[2] = (unsigned)bh;
+  x[3] = dr.offset;
+  philox4x32_10(x, dr.seed_lo, dr.seed_hi);
+  quad_transpose(x, lane);
 }
 
 // Random bytes for a lane that holds key `key` and query rows

@@ -307,11 +307,16 @@ void fwd_kernel(const T* __restrict__ Q, const T* __restrict__ K, const T* __res
       static_assert(NPAIR - kPairsA <= 2 * NNT, "late pairs fit before chunk 2 is read");
       T8 pf[4];
       float rs0 = 0.f, rs1 = 0.f;
-      // Dropout (DROP): the random bytes of this lane's 32 scores of tile j;
-      // the row sums take the probabilities before dropout, P V after it
-      // (the 1 / keep-probability factor is applied with 1 / l at the end).
+      // Dropout (DROP): the random bytes of this lane's scores of tile j,
+      // keys k0 + mt*32 + ... in rb[mt], each made just before its pairs (the
+      // second half after the score block when its pairs go with P V); the
+      // row sums take the probabilities before dropout, P V after it (the
+      // 1 / keep-probability factor is applied with 1 / l at the end).
       unsigned rb[2][4];
-      if constexpr (DROP) drop_bytes_rows(rb, drop, bh, qrow, k0 + half * 4, lane);
+      if constexpr (DROP) {
+        drop_bytes_rows(rb[0], drop, bh, qrow, k0 + half * 4, lane);
+        if constexpr (kPairsA > 8) drop_bytes_rows(rb[1], drop, bh, qrow, k0 + 32 + half * 4, lane);
+      }
       auto prob_pair = [&](int pr) {
         const int el = 2 * pr, kc = el >> 3, e = el & 7;
         const int mt = kc >> 1, i = (kc & 1) * 8 + e;
@@ -368,6 +373,8 @@ void fwd_kernel(const T* __restrict__ Q, const T* __restrict__ K, const T* __res
       }
       if constexpr (BIAS) bias_add(snext, bnext);
       mask_tile(snext, k0 + BC);
+      if constexpr (DROP && kPairsA <= 8)
+        drop_bytes_rows(rb[1], drop, bh, qrow, k0 + 32 + half * 4, lane);
 
       // O^T += V^T P^T for tile j (step st reads chunk st / NNT of P),
       // interleaved with the remaining probability pairs and the row max of

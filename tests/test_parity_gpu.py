@@ -305,6 +305,67 @@ def test_row_split_b4h32q16k16384d128_causal(gpu_lib):
     assert float((L - L1).abs().max()) <= BF16_L
 
 
+# --------------------------------------------------------------------------- maximum sizes
+
+def test_max_length_b1h2n65536d128_causal(gpu_lib):
+    """N = 65536 (offsets past 2^31 bytes per tensor row range): forward rows
+    sampled from both heads against the oracle, and the backward's gradient
+    identities on every head."""
+    fa = gpu_lib
+    w = synth.Workload("n64k", 1, 2, 65536, 65536, 128, True, torch.bfloat16)
+    say("max length b1h2n65536d128 causal")
+    x = synth.make_inputs(w, seed=0, device="cuda")
+    O, L = fa.forward(x["Q"], x["K"], x["V"], w.scale, True)
+    dQ, dK, dV = fa.backward(x["Q"], x["K"], x["V"], O, L, x["dO"], w.scale, True)
+    torch.cuda.synchronize()
+    rows = np.array([0, 1, 127, 128, 40000, 65535])
+    r = torch.as_tensor(rows, device="cuda")
+    for h in range(2):
+        Or, Lr = oracle.attention_forward_rows(f64(x["Q"][0, h]), f64(x["K"][0, h]),
+                                               f64(x["V"][0, h]), rows, w.scale, True)
+        assert max_abs(f64(O[0, h][r]), Or) <= BF16_O, h
+        assert max_abs(f64(L[0, h][r]), Lr) <= BF16_L, h
+    assert bool(torch.isfinite(dQ).all() and torch.isfinite(dK).all() and torch.isfinite(dV).all())
+    _gradient_sums(w, x, dK, dV)
+
+
+def test_many_heads_b256h64n130d64(gpu_lib):
+    """B*H = 16384 heads of 130 rows: sampled heads (first, last, middle) of the
+    forward and backward against the oracle."""
+    fa = gpu_lib
+    w = synth.Workload("bh16k", 256, 64, 130, 130, 64, True, torch.bfloat16)
+    say("many heads b256h64n130d64 causal")
+    x = synth.make_inputs(w, seed=0, device="cuda")
+    O, L = fa.forward(x["Q"], x["K"], x["V"], w.scale, True)
+    dQ, dK, dV = fa.backward(x["Q"], x["K"], x["V"], O, L, x["dO"], w.scale, True)
+    torch.cuda.synchronize()
+    for b, h in ((0, 0), (127, 33), (255, 63)):
+        Q, K, V, dO = (f64(x[k][b, h]) for k in ("Q", "K", "V", "dO"))
+        O_ref, L_ref = oracle.attention_forward(Q, K, V, w.scale, True)
+        assert max_abs(f64(O[b, h]), O_ref) <= BF16_O, (b, h)
+        assert max_abs(f64(L[b, h]), L_ref) <= BF16_L, (b, h)
+        ref = oracle.attention_backward(Q, K, V, dO, w.scale, True)
+        for name, got, want in zip(("dQ", "dK", "dV"), (dQ, dK, dV), ref):
+            assert rel_l2(f64(got[b, h]), want) <= BF16_G, (b, h, name)
+
+
+def test_decode_one_million_keys(gpu_lib):
+    """One query row against 2^20 keys (B=1, H=8, d=128): the automatic split
+    path against the oracle on every head."""
+    fa = gpu_lib
+    w = synth.Workload("k1m", 1, 8, 1, 1 << 20, 128, False, torch.bfloat16, backward=False)
+    ns = fa.fwd_num_splits(w.B, w.H, 1, w.Nk, w.d, 0, 0)
+    say(f"decode 2^20 keys, {ns} splits")
+    x = synth.make_inputs(w, seed=0, device="cuda")
+    O, L = fa.forward(x["Q"], x["K"], x["V"], w.scale, False)
+    torch.cuda.synchronize()
+    for h in range(w.H):
+        O_ref, L_ref = oracle.attention_forward(f64(x["Q"][0, h]), f64(x["K"][0, h]),
+                                                f64(x["V"][0, h]), w.scale, False)
+        assert max_abs(f64(O[0, h]), O_ref) <= BF16_O, h
+        assert max_abs(f64(L[0, h]), L_ref) <= BF16_L, h
+
+
 # --------------------------------------------------------------------------- guards and edge cases
 
 @pytest.mark.parametrize("dt", [torch.bfloat16, torch.float16, torch.float32])
