@@ -66,13 +66,20 @@ typedef enum fa_dtype { FA_BF16 = 0, FA_FP32 = 1, FA_FP16 = 2 } fa_dtype;
  *  1/sqrt(d)); it must be finite and > 0, else FA_ERR_UNSUPPORTED.
  *  causal != 0 applies the mask above.
  *
- *  num_splits chooses the key-split ("Flash-Decoding", the 51CTO FlashAttention V1/V2 notes, last paragraph
- *  of "Sequence Parallel") path, available for Nq == 1 with FA_BF16 or FA_FP16:
- *    0  = automatic (split path for Nq == 1 and bf16, tiled path otherwise),
+ *  num_splits chooses the key-split ("Flash-Decoding", the 51CTO FlashAttention
+ *  V1/V2 notes, "Sequence Length 并行" and the last paragraph of "Sequence
+ *  Parallel") path, available for Nq <= 128 with FA_BF16 or FA_FP16:
+ *    0  = automatic: Nq == 1 always splits; 1 < Nq <= 128 splits when the
+ *         query tiles alone give few workgroups and the keys are many;
+ *         otherwise the tiled path,
  *    1  = tiled path for Nq > 1; for Nq == 1 the split path with one split,
- *    >1 = split path with that many key chunks (Nq must be 1).
- *  The split path needs a workspace of fa_fwd_workspace_size() bytes (fp32
- *  partial outputs and logsumexps); the tiled path needs none (pass NULL, 0).
+ *    >1 = split path with at most that many key chunks (Nq <= 128, else
+ *         FA_ERR_UNSUPPORTED; for Nq > 1 chunks are whole multiples of 128
+ *         keys, so fewer may be used, and one chunk means the tiled path).
+ *  fa_fwd_num_splits reports the count that will be used.  The split path
+ *  needs a workspace of fa_fwd_workspace_size() bytes (fp32 partial outputs
+ *  and logsumexps per split and query row); the tiled path needs none (pass
+ *  NULL, 0).
  */
 fa_status fa_fwd(const void* Q, const void* K, const void* V, void* O, float* L,
                  int B, int H, int Nq, int Nk, int d, float scale, int causal,
