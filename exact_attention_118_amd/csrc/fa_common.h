@@ -333,21 +333,24 @@ struct DropDev {
 // Philox4x32-10 of counter x, in place.  Per round: the two products
 // M0 * x0 and M1 * x2 (32 x 32 -> 64 bits); the new words are (hi1 ^ x1 ^ k0,
 // lo1, hi0 ^ x3 ^ k1, lo0); the round key then advances by the Weyl
-// constants.  k0, k1 are wave-uniform, so the key schedule is scalar work.
+// constants W0, W1, so round r uses (seed_lo + r * W0, seed_hi + r * W1)
+// mod 2^32.  The keys are wave-uniform (scalar work), and a call may be split
+// into its rounds so that they run between other work.
+__device__ __forceinline__ void philox_round(unsigned (&x)[4], unsigned k0, unsigned k1) {
+  const unsigned long long p0 = (unsigned long long)0xD2511F53u * x[0];
+  const unsigned long long p1 = (unsigned long long)0xCD9E8D57u * x[2];
+  const unsigned hi0 = (unsigned)(p0 >> 32), lo0 = (unsigned)p0;
+  const unsigned hi1 = (unsigned)(p1 >> 32), lo1 = (unsigned)p1;
+  x[0] = hi1 ^ x[1] ^ k0;
+  x[1] = lo1;
+  x[2] = hi0 ^ x[3] ^ k1;
+  x[3] = lo0;
+}
+constexpr unsigned kPhiloxW0 = 0x9E3779B9u, kPhiloxW1 = 0xBB67AE85u;
+
 __device__ __forceinline__ void philox4x32_10(unsigned (&x)[4], unsigned k0, unsigned k1) {
 #pragma unroll
-  for (int r = 0; r < 10; ++r) {
-    const unsigned long long p0 = (unsigned long long)0xD2511F53u * x[0];
-    const unsigned long long p1 = (unsigned long long)0xCD9E8D57u * x[2];
-    const unsigned hi0 = (unsigned)(p0 >> 32), lo0 = (unsigned)p0;
-    const unsigned hi1 = (unsigned)(p1 >> 32), lo1 = (unsigned)p1;
-    x[0] = hi1 ^ x[1] ^ k0;
-    x[1] = lo1;
-    x[2] = hi0 ^ x[3] ^ k1;
-    x[3] = lo0;
-    k0 += 0x9E3779B9u;
-    k1 += 0xBB67AE85u;
-  }
+  for (int r = 0; r < 10; ++r) philox_round(x, k0 + r * kPhiloxW0, k1 + r * kPhiloxW1);
 }
 
 // 4 x 4 transpose of dwords across the 4 lanes of a quad (lanes 4a .. 4a+3):
@@ -393,13 +396,17 @@ __device__ __forceinline__ void byte_transpose(unsigned (&x)[4]) {
 // holding rows 4a .. 4a+3 and the same keys: each lane makes one of the
 // quad's four calls (key block (key0 + 8t) / 4 for quad lane t), then the quad
 // exchanges words.  On exit byte e of x[c] belongs to (row, key0 + c*8 + e).
-__device__ __forceinline__ void drop_bytes_rows(unsigned (&x)[4], const DropDev& dr, int bh,
-                                                int row, int key0, int lane) {
+__device__ __forceinline__ void drop_counter_rows(unsigned (&x)[4], const DropDev& dr, int bh,
+                                                  int row, int key0, int lane) {
   const int t = lane & 3;
   x[0] = (unsigned)(key0 + t * 8) >> 2;
   x[1] = (unsigned)row >> 2;
   x[2] = (unsigned)bh;
   x[3] = dr.offset;
+}
+__device__ __forceinline__ void drop_bytes_rows(unsigned (&x)[4], const DropDev& dr, int bh,
+                                                int row, int key0, int lane) {
+  drop_counter_rows(x, dr, bh, row, key0, lane);
   philox4x32_10(x, dr.seed_lo, dr.seed_hi);
   quad_transpose(x, lane);
 }
@@ -409,13 +416,17 @@ __device__ __forceinline__ void drop_bytes_rows(unsigned (&x)[4], const DropDev&
 // holding keys 4b .. 4b+3 and the same rows: each lane makes one of the
 // quad's four calls, transposes its bytes, then the quad exchanges words.
 // On exit byte r of x[g] belongs to (row0 + 8g + r, key).
-__device__ __forceinline__ void drop_bytes_keys(unsigned (&x)[4], const DropDev& dr, int bh,
-                                                int key, int row0, int lane) {
+__device__ __forceinline__ void drop_counter_keys(unsigned (&x)[4], const DropDev& dr, int bh,
+                                                  int key, int row0, int lane) {
   const int t = lane & 3;
   x[0] = (unsigned)key >> 2;
   x[1] = (unsigned)(row0 + 8 * t) >> 2;
   x[2] = (unsigned)bh;
   x[3] = dr.offset;
+}
+__device__ __forceinline__ void drop_bytes_keys(unsigned (&x)[4], const DropDev& dr, int bh,
+                                                int key, int row0, int lane) {
+  drop_counter_keys(x, dr, bh, key, row0, lane);
   philox4x32_10(x, dr.seed_lo, dr.seed_hi);
   byte_transpose(x);
   quad_transpose(x, lane);
