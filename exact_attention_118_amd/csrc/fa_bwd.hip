@@ -491,13 +491,18 @@ void bwd_dq_kernel(const T* __restrict__ Q, const T* __restrict__ K, const T* __
   // K tiles (buffers 0/1) and V tiles (buffers 2/3), swizzled (see swz) and
   // double-buffered: tile j+1 loads while tile j (buffers j & 1) is read.
   // The key loop is unrolled by two so that buffer offsets are constants.
-  __shared__ __attribute__((aligned(1024))) T smem[4 * TILE];
+  // Bias staging (BIAS), after the tiles: 32 rows x BC keys per wave, rows
+  // of 8 chunks of 16 bytes, chunk c of row r at c ^ ((r / 2) % 8) (reads of
+  // one chunk per row take the minimum two LDS passes).
+  constexpr int BSTAGE = BIAS ? (kDqThreads / 64) * 32 * BC : 0;
+  __shared__ __attribute__((aligned(1024))) T smem[4 * TILE + BSTAGE];
   T* const sK0 = smem;
   T* const sV0 = smem + 2 * TILE;
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  T* const sBw = smem + 4 * TILE + wave * 32 * BC;  // this wave's bias region (BIAS)
   const int half = lane >> 5, l32 = lane & 31;
   const int g = lane >> 4, s16 = lane & 15;
 
@@ -519,7 +524,10 @@ void bwd_dq_kernel(const T* __restrict__ Q, const T* __restrict__ K, const T* __
     bias_h = (const T*)bias.ptr + b * bias.sb + h * bias.sh;
     bias_n = (long long)(Nq - 1) * bias.sq + Nk;
   }
-  const BiasReader<T> br(bias_h, bias_n);
+  // the head's bias as buffer descriptor words, range rounded up to 16 bytes
+  // as in BiasReader
+  const i32x4 brw = rsrc_words(
+      bias_h, (unsigned)min(((unsigned long long)bias_n * 2 + 15) & ~15ull, 0xfffffff0ull));
   typedef typename Vec<T>::x4 BT4;
 
   using KV = BufTile<D, BC, kDqThreads>;
@@ -606,6 +614,34 @@ void bwd_dq_kernel(const T* __restrict__ Q, const T* __restrict__ K, const T* __
     vm_wait_all();
     __syncthreads();
 
+    // Bias (BIAS): each wave stages its 32 rows x BC keys of a tile in its own
+    // region with four direct-to-LDS loads of whole 128-byte rows, issued one
+    // tile ahead (after the current tile's bias was read), and reads its
+    // lanes' pieces back; rows past Nq read zeros, keys past Nk are masked.
+    // Load u, lane l: row 8u + l/8 of the wave's 32, stored chunk l%8, which
+    // holds chunk (l%8) ^ ((row / 2) % 8) of the row, i.e. c0 for even u and
+    // c0 ^ 4 for odd u.  One per-lane base (wraps only for rows past Nq, whose
+    // loads fall outside the descriptor); the row step is scalar.
+    const unsigned bbase =
+        BIAS ? (unsigned)((long long)(q0 + wave * 32 + (lane >> 3)) * bias.sq * 2) : 0u;
+    const unsigned bstep = BIAS ? (unsigned)(bias.sq * 16) : 0u;  // 8 rows, in bytes
+    const unsigned bc0 = (unsigned)(((lane & 7) ^ (lane >> 4)) << 4);
+    auto bias_issue = [&](int k0b) {
+#pragma unroll
+      for (int u = 0; u < 4; ++u)
+        lds_dma16_asm(brw, bbase + u * bstep + ((u & 1) ? (bc0 ^ 64u) : bc0) + (unsigned)k0b * 2,
+                      (const FA_LDS void*)(sBw + u * 64 * 8));
+    };
+    // Chunks q0b .. q0b+3 (keys q*8 + half*4 .. +3 of this lane's row).
+    auto bias_fetch = [&](BT4 (&bb)[8], int q0b) {
+      const unsigned rowb = (unsigned)l32 * (BC * 2) + (unsigned)half * 8;
+      const unsigned x = (unsigned)(l32 >> 1) & 7u;
+#pragma unroll
+      for (int q = q0b; q < q0b + 4; ++q)
+        bb[q] = *at_byte<BT4>(sBw, rowb + (((unsigned)q ^ x) << 4));
+    };
+    if constexpr (BIAS) bias_issue(jbeg * BC);
+
     // One key tile j (P = buffer parity j & 1, a constant at both inlined
     // call sites).
     auto tile_step = [&](const int P, int j) __attribute__((always_inline)) {
@@ -615,14 +651,9 @@ void bwd_dq_kernel(const T* __restrict__ Q, const T* __restrict__ K, const T* __
       f32x16 sacc[2], dpacc[2];
       T8 dsf[4];
       // Bias of this tile (BIAS): half mt, elements g*4 .. g*4+3 are keys
-      // k0 + mt*32 + g*8 + half*4 + 0..3; loaded first, added after each
-      // half's scores (rows past Nq read zeros, keys past Nk are masked).
+      // k0 + mt*32 + g*8 + half*4 + 0..3, read from the staged region before
+      // half 0's scores are complete and added after each half's scores.
       BT4 bb[BIAS ? 8 : 1];
-      if constexpr (BIAS) {
-#pragma unroll
-        for (int q = 0; q < 8; ++q)
-          bb[q] = br.load4((unsigned)(qrow * bias.sq + k0 + (q >> 2) * 32 + (q & 3) * 8 + half * 4));
-      }
       auto bias_half = [&](int mt) {
         if constexpr (BIAS) {
 #pragma unroll
@@ -708,23 +739,35 @@ void bwd_dq_kernel(const T* __restrict__ Q, const T* __restrict__ K, const T* __
         }
       };
       sdp_half(0, false);
+      if constexpr (BIAS) {
+        // the 2 * KV::PER tile loads of half 0 were issued after this tile's
+        // bias loads and complete in order
+        asm volatile("s_waitcnt vmcnt(%0)" ::"n"(2 * KV::PER) : "memory");
+        bias_fetch(bb, 0);
+      }
       bias_half(0);
       mask_half(0);
       if constexpr (DROP) drop_bytes_rows(rb[0], drop, bh, qrow, k0 + half * 4, lane);
       sdp_half(1, true);   // dS of half 0 overlaps the MFMAs of half 1
+      if constexpr (BIAS) bias_fetch(bb, 4);
       bias_half(1);
+      if constexpr (BIAS) bias_issue(k0 + BC);  // the region is free: stage tile j+1
       mask_half(1);
       if constexpr (DROP) drop_bytes_rows(rb[1], drop, bh, qrow, k0 + 32 + half * 4, lane);
       dq_half(0, true);    // dS of half 1 overlaps dQ of half 0
       dq_half(1, false);
 
-      vm_wait_all();  // this wave's part of tile j+1 has landed
+      // this wave's part of tile j+1 has landed (with a bias, the 4 bias
+      // loads of tile j+1, issued last, may still be in flight)
+      if constexpr (BIAS) asm volatile("s_waitcnt vmcnt(4)" ::: "memory");
+      else vm_wait_all();
       __syncthreads();
     };
     for (int j = jbeg; j < ntiles; j += 2) {
       tile_step(0, j);
       if (j + 1 < ntiles) tile_step(1, j + 1);
     }
+    if constexpr (BIAS) vm_wait_all();  // the last, unused bias loads
 
     // Epilogue: dQ = scale * dQ_acc; lane holds row qrow.
     if (qrow < Nq) {

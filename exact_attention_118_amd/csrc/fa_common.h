@@ -72,7 +72,6 @@ template <typename V8>
 __device__ __forceinline__ V8 zero8() {
   return __builtin_bit_cast(V8, (uint4){0u, 0u, 0u, 0u});
 }
-__device__ __forceinline__ bf16x8 zero_bf16x8() { return zero8<bf16x8>(); }
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
@@ -171,6 +170,27 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, in
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, bytes, kRsrcWord3);
 }
 #endif
+
+// A 16-byte direct-to-LDS load (lane i writes at lds + 16 i) issued from
+// inline assembly, with its buffer descriptor as four scalar words.  The
+// compiler's wait-count tracking does not see it, so the caller waits for it
+// explicitly (s_waitcnt vmcnt); in exchange its target does not join the
+// LDS regions that the compiler tracks for its own direct-to-LDS loads,
+// which would otherwise make it wait for those after each one.
+typedef int i32x4 __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ i32x4 rsrc_words(const void* base, unsigned bytes) {
+  const unsigned long long a = (unsigned long long)base;
+  i32x4 r;
+  r[0] = __builtin_amdgcn_readfirstlane((int)(unsigned)a);
+  r[1] = __builtin_amdgcn_readfirstlane((int)(unsigned)(a >> 32));
+  r[2] = __builtin_amdgcn_readfirstlane((int)bytes);
+  r[3] = (int)kRsrcWord3;
+  return r;
+}
+__device__ __forceinline__ void lds_dma16_asm(i32x4 rsrc, unsigned voff, const FA_LDS void* lds) {
+  asm volatile("s_mov_b32 m0, %2\n\tbuffer_load_dwordx4 %0, %1, 0 offen lds"
+               :: "v"(voff), "s"(rsrc), "s"((unsigned)(size_t)lds) : "m0", "memory");
+}
 
 // Direct-to-LDS tile loads through a buffer resource (buffer_load_dwordx4 with
 // the lds flag: lane i of a wave instruction writes 16 bytes at the
@@ -302,15 +322,6 @@ struct BiasReader {
     typedef unsigned u32x2 __attribute__((ext_vector_type(2)));
     const u32x2 v = __builtin_amdgcn_raw_buffer_load_b64(rs, (int)(e * 2), 0, 0);
     r = __builtin_bit_cast(typename Vec<T>::x4, v);
-#endif
-    return r;
-  }
-  // Element e, as fp32.
-  __device__ __forceinline__ float load1(unsigned e) const {
-    float r = 0.f;
-#if __HIP_DEVICE_COMPILE__
-    const unsigned short v = __builtin_amdgcn_raw_buffer_load_b16(rs, (int)(e * 2), 0, 0);
-    r = (float)__builtin_bit_cast(T, v);
 #endif
     return r;
   }

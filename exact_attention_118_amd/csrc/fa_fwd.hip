@@ -80,13 +80,18 @@ void fwd_kernel(const T* __restrict__ Q, const T* __restrict__ K, const T* __res
   // j+1 (loading) at buffers 2/3; all swizzled (see swz).  Tile j's buffers
   // are j & 1; the loop below is unrolled by two so that every LDS address
   // offset is a compile-time constant.
-  __shared__ __attribute__((aligned(1024))) T smem[4 * TILE];
+  // Bias staging (BIAS), after the tiles: a region of 32 rows x BC keys per
+  // wave, rows of 8 chunks of 16 bytes, chunk c of row r at c ^ ((r / 2) % 8)
+  // so that a read of one chunk per row takes the minimum two LDS passes.
+  constexpr int BSTAGE = BIAS ? (kFwdThreads / 64) * 32 * BC : 0;
+  __shared__ __attribute__((aligned(1024))) T smem[4 * TILE + BSTAGE];
   T* const sK0 = smem;
   T* const sV0 = smem + 2 * TILE;
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  T* const sBw = smem + 4 * TILE + wave * 32 * BC;  // this wave's bias region (BIAS)
   const int half = lane >> 5, l32 = lane & 31;
   const int g = lane >> 4, s16 = lane & 15;
 
@@ -118,7 +123,10 @@ void fwd_kernel(const T* __restrict__ Q, const T* __restrict__ K, const T* __res
     bias_h = (const T*)bias.ptr + b * bias.sb + h * bias.sh;
     bias_n = (long long)(Nq - 1) * bias.sq + Nk;
   }
-  const BiasReader<T> br(bias_h, bias_n);
+  // the head's bias as buffer descriptor words, range rounded up to 16 bytes
+  // as in BiasReader
+  const i32x4 brw = rsrc_words(
+      bias_h, (unsigned)min(((unsigned long long)bias_n * 2 + 15) & ~15ull, 0xfffffff0ull));
 
   using KV = BufTile<D, BC, kFwdThreads>;
   const KV kv(wave, lane);
@@ -232,12 +240,32 @@ void fwd_kernel(const T* __restrict__ Q, const T* __restrict__ K, const T* __res
     };
     // Bias of the score tile at key k0b: lane row qrow holds keys
     // k0b + mt*32 + g*8 + half*4 + 0..3 in elements i = g*4 .. g*4+3 of sc[mt];
-    // rows past Nq read zeros, keys past Nk are masked afterwards.
+    // rows past Nq read zeros, keys past Nk are masked afterwards.  Each wave
+    // stages its 32 rows x BC keys in its own LDS region with four
+    // direct-to-LDS loads of whole 128-byte rows (bias_issue), then reads its
+    // lanes' pieces back (bias_fetch); no other wave touches the region.
     typedef typename Vec<T>::x4 BT4;
-    auto bias_load = [&](BT4 (&bb)[8], int k0b) {
+    // Load u, lane l: row 8u + l/8 of the wave's 32, stored chunk l%8, which
+    // holds chunk (l%8) ^ ((row / 2) % 8) of the row, i.e. c0 for even u and
+    // c0 ^ 4 for odd u.  One per-lane base (wraps only for rows past Nq, whose
+    // loads fall outside the descriptor); the row step is scalar.
+    const unsigned bbase =
+        BIAS ? (unsigned)((long long)(q0 + wave * 32 + (lane >> 3)) * bias.sq * 2) : 0u;
+    const unsigned bstep = BIAS ? (unsigned)(bias.sq * 16) : 0u;  // 8 rows, in bytes
+    const unsigned bc0 = (unsigned)(((lane & 7) ^ (lane >> 4)) << 4);
+    auto bias_issue = [&](int k0b) {
 #pragma unroll
-      for (int q = 0; q < 8; ++q)
-        bb[q] = br.load4((unsigned)(qrow * bias.sq + k0b + (q >> 2) * 32 + (q & 3) * 8 + half * 4));
+      for (int u = 0; u < 4; ++u)
+        lds_dma16_asm(brw, bbase + u * bstep + ((u & 1) ? (bc0 ^ 64u) : bc0) + (unsigned)k0b * 2,
+                      (const FA_LDS void*)(sBw + u * 64 * 8));
+    };
+    // Chunks q0b .. q0b+3 (keys q*8 + half*4 .. +3 of this lane's row).
+    auto bias_fetch = [&](BT4 (&bb)[8], int q0b) {
+      const unsigned rowb = (unsigned)l32 * (BC * 2) + (unsigned)half * 8;
+      const unsigned x = (unsigned)(l32 >> 1) & 7u;
+#pragma unroll
+      for (int q = q0b; q < q0b + 4; ++q)
+        bb[q] = *at_byte<BT4>(sBw, rowb + (((unsigned)q ^ x) << 4));
     };
     auto bias_add = [&](f32x16 (&sc)[2], const BT4 (&bb)[8]) {
 #pragma unroll
@@ -262,10 +290,13 @@ void fwd_kernel(const T* __restrict__ Q, const T* __restrict__ K, const T* __res
     vm_wait_all();
     __syncthreads();
     f32x16 sA[2], sB[2];
+    if constexpr (BIAS) bias_issue(kfirst);
     scores(0, sA);
     if constexpr (BIAS) {
       BT4 bb[8];
-      bias_load(bb, kfirst);
+      vm_wait_all();
+      bias_fetch(bb, 0);
+      bias_fetch(bb, 4);
       bias_add(sA, bb);
     }
     mask_tile(sA, kfirst);
@@ -344,8 +375,7 @@ void fwd_kernel(const T* __restrict__ Q, const T* __restrict__ K, const T* __res
       // keeps this block free of branches, so the three kinds of work stay
       // interleaved.  With a bias, its values for tile j+1 are loaded first
       // and added once the scores are complete.
-      BT4 bnext[8];
-      if constexpr (BIAS) bias_load(bnext, k0 + BC);
+      if constexpr (BIAS) bias_issue(k0 + BC);
       {
         constexpr int SA = 2 * NKK;
         T8 ring[KRING];
@@ -371,7 +401,15 @@ void fwd_kernel(const T* __restrict__ Q, const T* __restrict__ K, const T* __res
           __builtin_amdgcn_sched_barrier(0);
         }
       }
-      if constexpr (BIAS) bias_add(snext, bnext);
+      if constexpr (BIAS) {
+        // the NKK tile loads of this block were issued after the bias loads
+        // and complete in order: waiting for all but NKK waits for the bias
+        asm volatile("s_waitcnt vmcnt(%0)" ::"n"(NKK) : "memory");
+        BT4 bnext[8];
+        bias_fetch(bnext, 0);
+        bias_fetch(bnext, 4);
+        bias_add(snext, bnext);
+      }
       mask_tile(snext, k0 + BC);
       if constexpr (DROP && kPairsA <= 8)
         drop_bytes_rows(rb[1], drop, bh, qrow, k0 + 32 + half * 4, lane);
