@@ -192,6 +192,13 @@ __device__ __forceinline__ void lds_dma16_asm(i32x4 rsrc, unsigned voff, const F
                :: "v"(voff), "s"(rsrc), "s"((unsigned)(size_t)lds) : "m0", "memory");
 }
 
+// Before direct-to-LDS loads overwrite a region that this wave has just
+// read: the reads must have returned.  The compiler places its wait for a
+// read just before the first use of the value, and plain arithmetic on the
+// value may be scheduled after the loads' inline assembly, so the wait is
+// made explicit.
+__device__ __forceinline__ void lds_reads_done() { asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory"); }
+
 // Direct-to-LDS tile loads through a buffer resource (buffer_load_dwordx4 with
 // the lds flag: lane i of a wave instruction writes 16 bytes at the
 // instruction's LDS base + 16 i).  Rows [row0, row0 + ROWS) of a row-major

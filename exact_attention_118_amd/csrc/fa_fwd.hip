@@ -254,6 +254,7 @@ void fwd_kernel(const T* __restrict__ Q, const T* __restrict__ K, const T* __res
     const unsigned bstep = BIAS ? (unsigned)(bias.sq * 16) : 0u;  // 8 rows, in bytes
     const unsigned bc0 = (unsigned)(((lane & 7) ^ (lane >> 4)) << 4);
     auto bias_issue = [&](int k0b) {
+      lds_reads_done();  // the region's previous contents have been read
 #pragma unroll
       for (int u = 0; u < 4; ++u)
         lds_dma16_asm(brw, bbase + u * bstep + ((u & 1) ? (bc0 ^ 64u) : bc0) + (unsigned)k0b * 2,
