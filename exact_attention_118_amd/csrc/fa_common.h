@@ -90,6 +90,22 @@ __device__ __forceinline__ float wave_shfl_xor(float v, int mask) {
   return __shfl_xor(v, mask, 64);
 }
 
+// Combine v with its value in lane l ^ 32 (the other half of the wave), for
+// every lane l.  v_permlane32_swap exchanges the two halves of its operands,
+// which leaves each lane holding v_l and v_{l^32}; the operations below are
+// commutative, so both halves get the same result bit for bit.  A vector-ALU
+// exchange, where __shfl_xor would go through the LDS crossbar.
+__device__ __forceinline__ float xor32_max(float v) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false,
+                                                  false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float xor32_sum(float v) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false,
+                                                  false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
 // Swizzled LDS tiles.  A [rows][D] bf16 tile is stored without padding, each
 // row's 16-byte chunks permuted: logical chunk c of row r sits at physical
 // chunk c ^ swz<D>(r).  The permutation makes both access patterns of the

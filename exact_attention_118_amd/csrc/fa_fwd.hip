@@ -49,7 +49,17 @@ BiasDev bias_dev(const BiasArgs& b, int H, float scale) {
 constexpr int kFwdBR = 128;  // query rows per workgroup
 constexpr int kFwdBC = 64;   // keys per K/V tile
 constexpr int kFwdThreads = 256;
-constexpr float kRescaleSlack = 8.f;  // see the online softmax below
+// The exponentials of the online softmax are taken against a reference that
+// lags the row max (see the tile step): every probability stays at or below
+// prob_limit<T>().  Floating point keeps its relative precision at any
+// magnitude, so the limit only has to keep P, O and l finite: 2^40 for bf16
+// (sums of 2^40-sized terms over any key count stay far below the fp32
+// range), 2^15 for fp16, whose largest finite value is 65504.  The higher the
+// limit, the more rarely the reference has to move.
+template <typename T>
+constexpr float prob_limit() {
+  return std::is_same<T, f16>::value ? 32768.f : 1099511627776.f;
+}
 
 // Key splits (SPLIT): each workgroup takes one query tile and one chunk of
 // `chunk` keys (a multiple of 2 * BC), and writes its normalised partial
@@ -75,6 +85,7 @@ void fwd_kernel(const T* __restrict__ Q, const T* __restrict__ K, const T* __res
   constexpr int NKK = D / 16;  // MFMA k-steps over the head dim
   constexpr int NNT = D / 32;  // 32-wide output tiles over the head dim
   constexpr int TILE = BC * D;  // elements per K or V tile
+  constexpr float kProbLimit = prob_limit<T>();
 
   // K tiles j+1 (read) and j+2 (loading) at buffers 0/1, V tiles j (read) and
   // j+1 (loading) at buffers 2/3; all swizzled (see swz).  Tile j's buffers
@@ -281,7 +292,7 @@ void fwd_kernel(const T* __restrict__ Q, const T* __restrict__ K, const T* __res
       for (int mt = 0; mt < 2; ++mt)
 #pragma unroll
         for (int i = 0; i < 16; ++i) mx = fmaxf(mx, sc[mt][i]);
-      return fmaxf(mx, wave_shfl_xor(mx, 32));
+      return xor32_max(mx);
     };
 
     // Prologue: K tiles 0 and 1, V tile 0; scores, mask and row max of tile 0.
@@ -301,7 +312,7 @@ void fwd_kernel(const T* __restrict__ Q, const T* __restrict__ K, const T* __res
       bias_add(sA, bb);
     }
     mask_tile(sA, kfirst);
-    float mx_next = row_max(sA);
+    m_run = row_max(sA) * c;  // the reference starts at tile 0's row max
     __syncthreads();  // every wave is done with K tile 0 before tile 2 replaces it
 
     // One key tile j (P = buffer parity j & 1, a constant at both inlined
@@ -310,24 +321,29 @@ void fwd_kernel(const T* __restrict__ Q, const T* __restrict__ K, const T* __res
                          __attribute__((always_inline)) {
       const int k0 = j * BC;
       // Online softmax (the CSDN post "Flash Attention1", 例子说明: running max
-      // and running sum), normalised once in the epilogue.  The reference m_run
-      // of the exponentials moves to the new row max only when some row of the
-      // wave has grown by more than kRescaleSlack (log2 units); until then
-      // probabilities are taken against the older, smaller reference and stay
-      // below 2^kRescaleSlack, where fp32 sums and 16-bit operands keep their full
-      // relative precision.  The result is the same in exact arithmetic, and
-      // most tiles skip rescaling the accumulators.  The row max of tile j was
-      // taken while tile j-1's P V product ran.
-      const float m_tile = mx_next * c;
-      if (__builtin_amdgcn_ballot_w64(m_tile > m_run + kRescaleSlack) != 0) {
-        const float m_new = fmaxf(m_run, m_tile);
+      // and running sum), normalised once in the epilogue.  The exponentials
+      // are taken against a reference m_run, which only has to bound them:
+      // the result is the same in exact arithmetic for any reference, since
+      // O and l are both scaled by 2^-m_run.  So the reference is not moved
+      // to each tile's row max.  Instead the row sums of the tile's
+      // probabilities (two halves, each checked before its 16-bit values
+      // enter P V) show whether any probability of the wave exceeds
+      // kProbLimit; only then is the reference moved to the tile's row max,
+      // what was accumulated rescaled, and that half recomputed.  A row that
+      // has seen no finite score yet (m_run = -inf) always takes that path, so
+      // that its first finite scores set the reference.
+      float m_ref = (m_run == -INFINITY) ? 0.f : m_run;
+      auto rebase = [&](float& part0, float& part1) {
+        const float m_new = fmaxf(m_run, row_max(scur) * c);
         const float alpha = fast_exp2(m_run - (m_new == -INFINITY ? 0.f : m_new));
         l_run *= alpha;
+        part0 *= alpha;
+        part1 *= alpha;
 #pragma unroll
         for (int nt = 0; nt < NNT; ++nt) oacc[nt] *= alpha;
         m_run = m_new;
-      }
-      const float m_ref = (m_run == -INFINITY) ? 0.f : m_run;
+        m_ref = (m_run == -INFINITY) ? 0.f : m_run;
+      };
 
       // The 32 probabilities of this lane's row in tile j, as 16 pairs (pair
       // pr: probabilities 2pr, 2pr+1 of chunk pr/4, converted together).  The
@@ -338,7 +354,9 @@ void fwd_kernel(const T* __restrict__ Q, const T* __restrict__ K, const T* __res
       constexpr int kPairsA = (D == 128) ? 8 : NPAIR;
       static_assert(NPAIR - kPairsA <= 2 * NNT, "late pairs fit before chunk 2 is read");
       T8 pf[4];
-      float rs0 = 0.f, rs1 = 0.f;
+      // row sums of this lane's probabilities: rs[0..1] the early pairs,
+      // rs[2..3] the late ones (two accumulators each)
+      float rs[4] = {0.f, 0.f, 0.f, 0.f};
       // Dropout (DROP): the random bytes of this lane's scores of tile j,
       // keys k0 + mt*32 + ... in rb[mt], each made just before its pairs (the
       // second half after the score block when its pairs go with P V); the
@@ -354,8 +372,10 @@ void fwd_kernel(const T* __restrict__ Q, const T* __restrict__ K, const T* __res
         const int mt = kc >> 1, i = (kc & 1) * 8 + e;
         const float p0 = fast_exp2(fmaf(scur[mt][i], c, -m_ref));
         const float p1 = fast_exp2(fmaf(scur[mt][i + 1], c, -m_ref));
-        rs0 += p0;
-        rs1 += p1;
+        float& ra = rs[pr < kPairsA ? 0 : 2];
+        float& rb_ = rs[pr < kPairsA ? 1 : 3];
+        ra += p0;
+        rb_ += p1;
         if constexpr (DROP) {
           pf[kc][e] = (T)(drop_keep(rb[mt][i >> 2], i & 3, drop.thresh) ? p0 : 0.f);
           pf[kc][e + 1] = (T)(drop_keep(rb[mt][i >> 2], (i + 1) & 3, drop.thresh) ? p1 : 0.f);
@@ -364,8 +384,8 @@ void fwd_kernel(const T* __restrict__ Q, const T* __restrict__ K, const T* __res
           pf[kc][e + 1] = (T)p1;
         }
         pin(pf[kc]);
-        pin(rs0);
-        pin(rs1);
+        pin(ra);
+        pin(rb_);
       };
 
       // Scores of tile j+1 on the MFMA pipe, interleaved step by step with
@@ -402,6 +422,15 @@ void fwd_kernel(const T* __restrict__ Q, const T* __restrict__ K, const T* __res
           __builtin_amdgcn_sched_barrier(0);
         }
       }
+      // The early pairs, about to enter P V: redo them against the tile's row
+      // max if some lane's sum of them exceeds the limit (nothing of tile j
+      // has been accumulated yet).
+      if (__builtin_amdgcn_ballot_w64(rs[0] + rs[1] > kProbLimit || m_run == -INFINITY) != 0) {
+        rebase(rs[0], rs[1]);
+        rs[0] = rs[1] = 0.f;
+#pragma unroll
+        for (int pr = 0; pr < kPairsA; ++pr) prob_pair(pr);
+      }
       if constexpr (BIAS) {
         // the NKK tile loads of this block were issued after the bias loads
         // and complete in order: waiting for all but NKK waits for the bias
@@ -416,31 +445,31 @@ void fwd_kernel(const T* __restrict__ Q, const T* __restrict__ K, const T* __res
         drop_bytes_rows(rb[1], drop, bh, qrow, k0 + 32 + half * 4, lane);
 
       // O^T += V^T P^T for tile j (step st reads chunk st / NNT of P),
-      // interleaved with the remaining probability pairs and the row max of
-      // tile j+1.
+      // interleaved with the remaining probability pairs.
       {
         T8 ring[VRING];
-        float mxa = -INFINITY, mxb = -INFINITY;
 #pragma unroll
         for (int st = 0; st < VRING; ++st) ring[st] = vfrag(P, st);
 #pragma unroll
         for (int st = 0; st < 4 * NNT; ++st) {
+          if (kPairsA < NPAIR && st == NPAIR - kPairsA) {
+            // The late pairs are complete and their chunks not yet read: the
+            // same check, now rescaling the early pairs' share of O and l.
+            if (__builtin_amdgcn_ballot_w64(rs[2] + rs[3] > kProbLimit) != 0) {
+              rebase(rs[0], rs[1]);
+              rs[2] = rs[3] = 0.f;
+#pragma unroll
+              for (int pr = kPairsA; pr < NPAIR; ++pr) prob_pair(pr);
+            }
+          }
           const T8 a = ring[st % VRING];
           if (st + VRING < 4 * NNT) ring[st % VRING] = vfrag(P, st + VRING);
           oacc[st % NNT] = mfma32(a, pf[st / NNT], oacc[st % NNT]);
           if (kPairsA + st < NPAIR) prob_pair(kPairsA + st);
-#pragma unroll
-          for (int h = 0; h < 32 / (4 * NNT); h += 2) {
-            const int el = st * (32 / (4 * NNT)) + h;
-            mxa = fmaxf(mxa, snext[el >> 4][el & 15]);
-            mxb = fmaxf(mxb, snext[el >> 4][(el & 15) + 1]);
-          }
           __builtin_amdgcn_sched_barrier(0);
         }
-        mx_next = fmaxf(mxa, mxb);
-        mx_next = fmaxf(mx_next, wave_shfl_xor(mx_next, 32));
       }
-      l_run += rs0 + rs1;
+      l_run += (rs[0] + rs[1]) + (rs[2] + rs[3]);
       vm_wait_all();  // this wave's part of tiles K j+2 and V j+1 has landed
       __syncthreads();
     };
@@ -452,7 +481,7 @@ void fwd_kernel(const T* __restrict__ Q, const T* __restrict__ K, const T* __res
 
     // Epilogue: O = O_acc / l (times 1 / keep-probability with dropout),
     // L = (m + log2 l) * ln 2.
-    const float l_tot = l_run + wave_shfl_xor(l_run, 32);
+    const float l_tot = xor32_sum(l_run);
     if constexpr (SPLIT) {
       if (qrow < Nq) {
         const size_t prow = (size_t)sp * split.rows + (size_t)bh * Nq + qrow;

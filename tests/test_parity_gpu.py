@@ -442,3 +442,31 @@ def test_large_scores_and_uniform_keys(gpu_lib):
     V = f64(x["V"])
     prefix = np.cumsum(V, axis=2) / np.arange(1, 334)[None, None, :, None]
     assert max_abs(f64(O), prefix) <= BF16_O
+
+
+@pytest.mark.parametrize("dt", [torch.bfloat16, torch.float16])
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("slope", [1.0, -1.0])
+def test_scores_rising_or_falling_along_keys(gpu_lib, dt, causal, slope):
+    """Scores that rise (or fall) by about 0.5 log2 units per key, i.e. ~33 per
+    64-key tile and ~16 per half tile: the forward kernel's reference for its
+    exponentials has to move between tiles and between the two halves of a
+    tile (bf16 and fp16 bound the probabilities differently), or never moves
+    and later tiles underflow; O and L still match the oracle."""
+    fa = gpu_lib
+    say(f"rising/falling scores slope={slope} causal={causal} {dt}")
+    g = torch.Generator().manual_seed(11)
+    B, H, N, d = 1, 2, 700, 128
+    Q = torch.randn(B, H, N, d, generator=g) * 0.5
+    K = torch.randn(B, H, N, d, generator=g) * 0.5
+    V = torch.randn(B, H, N, d, generator=g)
+    Q[..., 0] = 4.0
+    K[..., 0] = slope * torch.arange(N, dtype=torch.float32)
+    Q, K, V = (t.to(dt).cuda() for t in (Q, K, V))
+    scale = 1 / math.sqrt(d)
+    O, L = fa.forward(Q, K, V, scale, causal)
+    torch.cuda.synchronize()
+    O_ref, L_ref = oracle.attention_forward_batched(f64(Q), f64(K), f64(V), scale, causal)
+    to, tl, _ = tolerances(dt)
+    assert max_abs(f64(O), O_ref) <= to
+    assert max_abs(f64(L), L_ref) <= tl
