@@ -115,15 +115,18 @@ void bwd_dkdv_kernel(const T* __restrict__ Q, const T* __restrict__ K, const T* 
   static_assert(2 * BR == 64, "one dword load per lane carries the (L2, D) pairs of a block");
   static_assert(NIQ % IPW == 0, "a wave loads from one tile");
 
-  // [K block | Q buffers 0,1 | dO buffers 0,1], all swizzled (see swz); the
+  // [Q buffers 0,1 | dO buffers 0,1 | K block], all swizzled (see swz); the
   // (L*log2 e, D) pairs of the query block per buffer.  Query block it uses
   // buffers it & 1; the loop is unrolled by two so that their offsets are
-  // constants.
-  __shared__ __attribute__((aligned(1024))) T smem[KTILE + 4 * QTILE];
+  // constants.  The query tiles come first: their many reads then carry the
+  // buffer offset in the 16-bit offset field of the LDS instruction, which
+  // offsets past the 64 KB K block would not fit (each read would need an
+  // address add).
+  __shared__ __attribute__((aligned(1024))) T smem[4 * QTILE + KTILE];
   __shared__ __attribute__((aligned(16))) float sLD[2][2 * BR];
-  T* const sK = smem;
-  T* const sQ0 = smem + KTILE;
-  T* const sdO0 = smem + KTILE + 2 * QTILE;
+  T* const sQ0 = smem;
+  T* const sdO0 = smem + 2 * QTILE;
+  T* const sK = smem + 4 * QTILE;
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
