@@ -24,9 +24,11 @@
 // workspace beyond D, and every output is deterministic.
 //
 // gfx950 mapping:
-//  * bwd_dkdv_kernel: 512 threads = 8 waves, two per SIMD, so one wave's
-//    MFMAs overlap the other's LDS reads, exponentials and barrier waits.  A
-//    workgroup owns BC = 256 keys and each wave 32 of them, so dK and dV stay
+//  * bwd_dkdv_kernel: 256 threads = 4 waves, two workgroups per CU (two
+//    waves per SIMD), so one wave's MFMAs overlap the other's LDS reads,
+//    exponentials and barrier waits, and the two workgroups' barriers are
+//    independent.  A workgroup owns BC = 128 keys and each wave 32 of them
+//    (64 KB of LDS: the K block and two Q and dO buffers), so dK and dV stay
 //    wave-private (the notes, "Warp Level 并行": with keys split across warps,
 //    dV, dS and dK need no cross-warp reduction).  Scores are laid out with the
 //    key along lanes (S = Q K^T on the 32x32x16 bf16/fp16 MFMA): rounded to 16 bits,
@@ -44,8 +46,8 @@
 //    tiles of 64 keys are loaded straight into LDS (swizzled, double-buffered).
 //  * Grids: the key-block grid pins heads to XCDs when B*H is a multiple of 8
 //    (a head's workgroups then share one L2 for their re-reads of Q and dO)
-//    and dispatches key blocks in order of decreasing work, which with one
-//    workgroup per CU already balances the causal triangle; the query-block
+//    and dispatches key blocks in order of decreasing work, which already
+//    balances the causal triangle; the query-block
 //    grid uses the forward pass's mapping, causal query tiles in pairs
 //    (t, nqt-1-t) of equal total work.
 #include "fa_common.h"
@@ -89,14 +91,14 @@ __global__ __launch_bounds__(256) void bwd_pre_kernel(const T* __restrict__ O,
 }
 
 // ---------------------------------------------------------------------------
-// dK and dV: one workgroup per (key block of 256, batch*head).
-constexpr int kKvBC = 256;  // keys per workgroup
+// dK and dV: one workgroup per (key block of 128, batch*head).
+constexpr int kKvBC = 128;  // keys per workgroup
 constexpr int kKvBR = 32;   // query rows per inner iteration
-constexpr int kKvWaves = 8;
+constexpr int kKvWaves = 4;
 constexpr int kKvThreads = kKvWaves * 64;
 
 template <typename T, int D, bool CAUSAL, bool BIAS, bool DROP>
-__global__ __launch_bounds__(kKvThreads, 1) __attribute__((amdgpu_waves_per_eu(2, 2)))
+__global__ __launch_bounds__(kKvThreads, 2) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void bwd_dkdv_kernel(const T* __restrict__ Q, const T* __restrict__ K, const T* __restrict__ V,
                      const T* __restrict__ dO, const float* __restrict__ LD, T* __restrict__ dK,
                      T* __restrict__ dV, int Nq, int Nk, int nkt, int BH, int hpx, float c,
@@ -188,13 +190,13 @@ void bwd_dkdv_kernel(const T* __restrict__ Q, const T* __restrict__ K, const T* 
   int qb_first = CAUSAL ? max(0, k0 - off) / BR : 0;
   // Bias tile map (BIAS): only the query blocks from the first to the last
   // 128-row tile that holds an entry above -inf for one of this workgroup's
-  // four 64-key tiles.
+  // two 64-key tiles.
   if constexpr (BIAS) {
-    static_assert(BC == 4 * kMapKeys && kMapRows % BR == 0, "tile map granularity");
+    static_assert(BC % kMapKeys == 0 && kMapRows % BR == 0, "tile map granularity");
     if (bias.tmap) {
       const int b = bh / bias.H, h = bh - b * bias.H;
       int lo, hi;
-      map_range_cols(bias.tmap + b * bias.tm_sb + h * bias.tm_sh, (Nq + kMapRows - 1) / kMapRows,
+      map_range_cols<BC / kMapKeys>(bias.tmap + b * bias.tm_sb + h * bias.tm_sh, (Nq + kMapRows - 1) / kMapRows,
                      bias.nkt4, k0 / kMapKeys, lane, lo, hi);
       if (lo > hi) {
         nqb = qb_first;

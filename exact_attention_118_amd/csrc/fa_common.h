@@ -4,6 +4,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <type_traits>
+
 namespace fa {
 
 typedef __bf16 bf16;
@@ -299,15 +301,19 @@ __device__ __forceinline__ void map_range(const unsigned char* row, int n, int l
   }
 }
 
-// First and last query tile qt in [0, nqt) whose bytes kt0 .. kt0+3 of the
-// map (a 4-byte aligned word) are not all zero; lo > hi when none.
+// First and last query tile qt in [0, nqt) whose NB bytes kt0 .. kt0+NB-1 of
+// the map are not all zero (NB = 2 or 4, kt0 a multiple of NB: one aligned
+// load per row, inside the row's padding to nkt4 bytes); lo > hi when none.
+template <int NB>
 __device__ __forceinline__ void map_range_cols(const unsigned char* head, int nqt, int nkt4,
                                                int kt0, int lane, int& lo, int& hi) {
+  static_assert(NB == 2 || NB == 4, "two or four map bytes per workgroup");
+  typedef typename std::conditional<NB == 4, unsigned, unsigned short>::type W;
   lo = 0x7fffffff;
   hi = -1;
   for (int base = 0; base < nqt; base += 64) {
     const int qt = base + lane;
-    const unsigned w = qt < nqt ? *(const unsigned*)(head + (size_t)qt * nkt4 + kt0) : 0u;
+    const unsigned w = qt < nqt ? (unsigned)*(const W*)(head + (size_t)qt * nkt4 + kt0) : 0u;
     const unsigned long long m = __builtin_amdgcn_ballot_w64(w != 0u);
     if (m != 0ull) {
       lo = min(lo, base + (int)__builtin_ctzll(m));
