@@ -28,7 +28,8 @@
 //    waves per SIMD), so one wave's MFMAs overlap the other's LDS reads,
 //    exponentials and barrier waits, and the two workgroups' barriers are
 //    independent.  A workgroup owns BC = 128 keys and each wave 32 of them
-//    (64 KB of LDS: the K block and two Q and dO buffers), so dK and dV stay
+//    (64 KB of LDS: the K block and two Q and dO buffers; with a bias, 8
+//    waves and 256 keys, one workgroup per CU), so dK and dV stay
 //    wave-private (the notes, "Warp Level 并行": with keys split across warps,
 //    dV, dS and dK need no cross-warp reduction).  Scores are laid out with the
 //    key along lanes (S = Q K^T on the 32x32x16 bf16/fp16 MFMA): rounded to 16 bits,
@@ -91,21 +92,30 @@ __global__ __launch_bounds__(256) void bwd_pre_kernel(const T* __restrict__ O,
 }
 
 // ---------------------------------------------------------------------------
-// dK and dV: one workgroup per (key block of 128, batch*head).
-constexpr int kKvBC = 128;  // keys per workgroup
-constexpr int kKvBR = 32;   // query rows per inner iteration
-constexpr int kKvWaves = 4;
-constexpr int kKvThreads = kKvWaves * 64;
+// dK and dV: one workgroup per (key block, batch*head), 32 keys per wave.
+// Without a bias: 4 waves and 128 keys, 64 KB of LDS, two workgroups per CU.
+// With a bias, whose double-buffered tiles would take a pair of such
+// workgroups just past the 160 KB of a CU: 8 waves and 256 keys, one per CU.
+template <bool BIAS>
+struct KvShape {
+  static constexpr int kWaves = BIAS ? 8 : 4;
+  static constexpr int kThreads = kWaves * 64;
+  static constexpr int kBC = kWaves * 32;  // keys per workgroup
+  static constexpr int kPerCU = BIAS ? 1 : 2;
+};
+constexpr int kKvBR = 32;  // query rows per inner iteration
 
 template <typename T, int D, bool CAUSAL, bool BIAS, bool DROP>
-__global__ __launch_bounds__(kKvThreads, 2) __attribute__((amdgpu_waves_per_eu(2, 2)))
+__global__ __launch_bounds__(KvShape<BIAS>::kThreads, KvShape<BIAS>::kPerCU)
+__attribute__((amdgpu_waves_per_eu(2, 2)))
 void bwd_dkdv_kernel(const T* __restrict__ Q, const T* __restrict__ K, const T* __restrict__ V,
                      const T* __restrict__ dO, const float* __restrict__ LD, T* __restrict__ dK,
                      T* __restrict__ dV, int Nq, int Nk, int nkt, int BH, int hpx, float c,
                      float scale, int off, BiasDev bias, DropDev drop) {
   typedef typename Vec<T>::x8 T8;
   typedef typename Vec<T>::x4 T4;
-  constexpr int BC = kKvBC, BR = kKvBR;
+  constexpr int kKvWaves = KvShape<BIAS>::kWaves, kKvThreads = KvShape<BIAS>::kThreads;
+  constexpr int BC = KvShape<BIAS>::kBC, BR = kKvBR;
   constexpr int CPR = D / 8;     // 16-byte chunks per row
   constexpr int NKK = D / 16;    // MFMA k-steps over the head dim
   constexpr int NNT = D / 32;    // 32-wide tiles over the head dim
@@ -948,11 +958,13 @@ hipError_t launch_bwd_mfma(const BwdArgs& a, int stages, hipStream_t s) {
     if (e != hipSuccess) return e;
   }
   if ((stages & 2) && a.Nk > 0) {
+    constexpr int kKvBC = KvShape<BIAS>::kBC;
     const int nkt = (a.Nk + kKvBC - 1) / kKvBC;
     const int nblocks = nkt * BH;
     const int hpx = (BH % kNumXcd == 0) ? BH / kNumXcd : 0;
 #define FA_DKDV_LAUNCH(DD, CC)                                                                 \
-  hipLaunchKernelGGL((bwd_dkdv_kernel<T, DD, CC, BIAS, DROP>), dim3(nblocks), dim3(kKvThreads), \
+  hipLaunchKernelGGL((bwd_dkdv_kernel<T, DD, CC, BIAS, DROP>), dim3(nblocks),                    \
+                     dim3(KvShape<BIAS>::kThreads),                                             \
                      0, s, Q, K, V, dO, a.LD, (T*)a.dK, (T*)a.dV, a.Nq, a.Nk, nkt, BH, hpx, c,  \
                      a.scale, off, bias, drop)
     if (a.d == 128) {
