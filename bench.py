@@ -177,11 +177,24 @@ def bench_decode(fa, torch, steps):
     ms = ev[0].elapsed_time(ev[-1]) / steps
     kv_bytes = 2 * w.B * w.H * w.Nk * w.d * 2
     all_bytes = kv_bytes + 2 * w.B * w.H * w.d * 2 + w.B * w.H * 4
-    del x
+    # What the HBM delivers to a plain device copy of the same K (2 GiB read,
+    # 2 GiB written) in this run: a reference rate for the split path.
+    buf = torch.empty_like(x["K"])
+    buf.copy_(x["K"])
+    torch.cuda.synchronize()
+    ev[0].record()
+    for i in range(steps):
+        buf.copy_(x["K"])
+        ev[i + 1].record()
+    torch.cuda.synchronize()
+    copy_ms = ev[0].elapsed_time(ev[-1]) / steps
+    copy_gbs = 2 * x["K"].numel() * x["K"].element_size() / (copy_ms * 1e-3) / 1e9
+    del x, buf
     return {"workload": w.name, "ms": ms, "splits": splits,
             "GB/s": all_bytes / (ms * 1e-3) / 1e9,
             "hbm_frac": all_bytes / (ms * 1e-3) / 1e9 / PEAK_HBM_GBS,
-            "algorithmic_bytes": all_bytes}
+            "algorithmic_bytes": all_bytes,
+            "reference_copy_GB/s": copy_gbs}
 
 
 def bench_rows_split(fa, torch, steps):
