@@ -275,6 +275,32 @@ def bench_fp16(fa, torch, w, x, ws, steps):
     return _time_fwd_bwd(fa, torch, w, Q, K, V, dO, ws, steps)
 
 
+def bench_other_configs(fa, torch, steps):
+    """Forward and backward of the other bf16 workloads, each against both
+    roofs: MFMA (4*d and 10*d flop per unmasked pair) and HBM (algorithmic
+    bytes: Q, K, V read and O, L written forward; Q, K, V, O, dO, L, D read
+    and dQ, dK, dV written backward)."""
+    from exact_attention_118_amd import synth
+
+    out = {}
+    for name in ("b4h16n1024d64_causal", "b2h16n4096d128_causal", "b2h16n4096d128"):
+        w = synth.WORKLOADS[name]
+        x = synth.make_inputs(w, seed=0, device="cuda")
+        ws = torch.empty(fa.bwd_workspace_size(w.B, w.H, w.Nq, w.Nk, w.d, fa.FA_BF16),
+                         dtype=torch.uint8, device="cuda")
+        r = _time_fwd_bwd(fa, torch, w, x["Q"], x["K"], x["V"], x["dO"], ws, steps)
+        t = w.B * w.H * w.Nq * w.d * 2  # bytes of one bf16 tensor
+        rows = w.B * w.H * w.Nq
+        fwd_bytes, bwd_bytes = 4 * t + 4 * rows, 8 * t + 8 * rows
+        r["fwd_mfma_frac"] = r["fwd_TFLOP/s"] / PEAK_BF16_TFLOPS
+        r["bwd_mfma_frac"] = r["bwd_TFLOP/s"] / PEAK_BF16_TFLOPS
+        r["fwd_hbm_frac"] = fwd_bytes / (r["fwd_ms"] * 1e-3) / 1e9 / PEAK_HBM_GBS
+        r["bwd_hbm_frac"] = bwd_bytes / (r["bwd_ms"] * 1e-3) / 1e9 / PEAK_HBM_GBS
+        out[name] = r
+        del x, ws
+    return out
+
+
 def bench_bias(fa, torch, w, x, ws, steps):
     """The same forward and backward with an additive bias [1, H, N, N] in the
     input dtype (one score matrix per head, shared over the batch)."""
@@ -331,6 +357,8 @@ def main():
     ap.add_argument("--cpu-heads", type=int, default=16,
                     help="heads of the workload the float64 oracle is timed on (0 = skip)")
     ap.add_argument("--no-decode", action="store_true", help="skip the decode-shaped forward")
+    ap.add_argument("--no-configs", action="store_true",
+                    help="skip the forward and backward of the other bf16 workloads")
     ap.add_argument("--no-fp16", action="store_true", help="skip the fp16 forward and backward")
     ap.add_argument("--no-bias", action="store_true",
                     help="skip the forward and backward with an additive bias")
@@ -461,6 +489,9 @@ def main():
                 "executed_mfma_frac": 14 * w.d * pairs / (bwd_ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS},
     }
     del dQ, dK, dV
+    if not args.no_configs:
+        log("other bf16 workloads")
+        out["configs"] = bench_other_configs(fa, torch, steps=10)
     if not args.no_fp16:
         log("fp16 inputs, same workload")
         out["fp16"] = bench_fp16(fa, torch, w, x, ws, steps=max(3, args.steps // 2))
