@@ -194,7 +194,11 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, in
 // compiler's wait-count tracking does not see it, so the caller waits for it
 // explicitly (s_waitcnt vmcnt); in exchange its target does not join the
 // LDS regions that the compiler tracks for its own direct-to-LDS loads,
-// which would otherwise make it wait for those after each one.
+// which would otherwise make it wait for those after each one.  The load
+// takes its LDS address from m0, a register the compiler reserves for
+// itself: the sequence saves m0, sets it, leaves the one wait state that an
+// m0 write needs before a direct-to-LDS load reads it (the gfx9 hazard
+// rule), issues the load and restores m0, so the compiler sees m0 unchanged.
 typedef int i32x4 __attribute__((ext_vector_type(4)));
 __device__ __forceinline__ i32x4 rsrc_words(const void* base, unsigned bytes) {
   const unsigned long long a = (unsigned long long)base;
@@ -206,8 +210,16 @@ __device__ __forceinline__ i32x4 rsrc_words(const void* base, unsigned bytes) {
   return r;
 }
 __device__ __forceinline__ void lds_dma16_asm(i32x4 rsrc, unsigned voff, const FA_LDS void* lds) {
-  asm volatile("s_mov_b32 m0, %2\n\tbuffer_load_dwordx4 %0, %1, 0 offen lds"
-               :: "v"(voff), "s"(rsrc), "s"((unsigned)(size_t)lds) : "m0", "memory");
+  unsigned saved;
+  asm volatile(
+      "s_mov_b32 %0, m0\n\t"
+      "s_mov_b32 m0, %3\n\t"
+      "s_nop 0\n\t"
+      "buffer_load_dwordx4 %1, %2, 0 offen lds\n\t"
+      "s_mov_b32 m0, %0"
+      : "=&s"(saved)
+      : "v"(voff), "s"(rsrc), "s"((unsigned)(size_t)lds)
+      : "memory");
 }
 
 // Before direct-to-LDS loads overwrite a region that this wave has just
