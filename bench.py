@@ -275,6 +275,53 @@ def bench_fp16(fa, torch, w, x, ws, steps):
     return _time_fwd_bwd(fa, torch, w, Q, K, V, dO, ws, steps)
 
 
+def _time_fwd_bwd_graph(fa, torch, w, Q, K, V, dO, ws, reps):
+    """Mean forward and backward milliseconds of fa_fwd + fa_bwd, each captured
+    `reps` times into a HIP graph and replayed, so that host-side launch
+    latency does not count: a kernel of a few microseconds would otherwise wait
+    for the host between launches."""
+    O = torch.empty_like(Q)
+    L = torch.empty(w.B, w.H, w.Nq, dtype=torch.float32, device="cuda")
+    dQ, dK, dV = torch.empty_like(Q), torch.empty_like(K), torch.empty_like(V)
+
+    def fwd():
+        fa.fa_fwd(Q, K, V, O, L, w.scale, w.causal)
+
+    def bwd():
+        fa.fa_bwd(Q, K, V, O, L, dO, dQ, dK, dV, w.scale, w.causal, workspace=ws)
+
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        fwd()
+        bwd()
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    graphs = []
+    for fn in (fwd, bwd):
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            for _ in range(reps):
+                fn()
+        graphs.append(g)
+    ms = []
+    for g in graphs:
+        g.replay()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        g.replay()
+        e1.record()
+        torch.cuda.synchronize()
+        ms.append(e0.elapsed_time(e1) / reps)
+    del graphs
+    pairs = unmasked_pairs(w.Nq, w.Nk, w.causal) * w.B * w.H
+    return {"fwd_ms": ms[0], "bwd_ms": ms[1],
+            "fwd_TFLOP/s": 4 * w.d * pairs / (ms[0] * 1e-3) / 1e12,
+            "bwd_TFLOP/s": 10 * w.d * pairs / (ms[1] * 1e-3) / 1e12,
+            "timing": f"HIP graph of {reps} calls, replayed"}
+
+
 def bench_other_configs(fa, torch, steps):
     """Forward and backward of the other bf16 workloads, each against both
     roofs: MFMA (4*d and 10*d flop per unmasked pair) and HBM (algorithmic
@@ -288,7 +335,7 @@ def bench_other_configs(fa, torch, steps):
         x = synth.make_inputs(w, seed=0, device="cuda")
         ws = torch.empty(fa.bwd_workspace_size(w.B, w.H, w.Nq, w.Nk, w.d, fa.FA_BF16),
                          dtype=torch.uint8, device="cuda")
-        r = _time_fwd_bwd(fa, torch, w, x["Q"], x["K"], x["V"], x["dO"], ws, steps)
+        r = _time_fwd_bwd_graph(fa, torch, w, x["Q"], x["K"], x["V"], x["dO"], ws, steps)
         t = w.B * w.H * w.Nq * w.d * 2  # bytes of one bf16 tensor
         rows = w.B * w.H * w.Nq
         fwd_bytes, bwd_bytes = 4 * t + 4 * rows, 8 * t + 8 * rows
