@@ -229,6 +229,11 @@ __device__ __forceinline__ void lds_dma16_asm(i32x4 rsrc, unsigned voff, const F
 // made explicit.
 __device__ __forceinline__ void lds_reads_done() { asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory"); }
 
+// Cache-policy operand of a buffer load that marks it non-temporal (the nt
+// bit of the gfx940-family policy: sc0 = 1, nt = 2, sc1 = 16): for streams
+// that no other workgroup reads again, which then pass the caches by.
+constexpr int kLoadNonTemporal = 2;
+
 // Direct-to-LDS tile loads through a buffer resource (buffer_load_dwordx4 with
 // the lds flag: lane i of a wave instruction writes 16 bytes at the
 // instruction's LDS base + 16 i).  Rows [row0, row0 + ROWS) of a row-major
@@ -253,8 +258,10 @@ struct BufTile {
       voff[u] = (unsigned)(r * D * 2 + ((pch ^ swz<D>(r)) << 4));
     }
   }
-  // Load u (0 <= u < PER) of this wave for the tile at row0 into lds.
-  template <typename T>
+  // Load u (0 <= u < PER) of this wave for the tile at row0 into lds.  AUX
+  // is the load's cache policy: 0, or kLoadNonTemporal for data that no other
+  // workgroup reads again.
+  template <int AUX = 0, typename T>
   __device__ __forceinline__ void part(const T* g, int row0, int nvalid, T* lds, int u) const {
     static_assert(sizeof(T) == 2, "16-bit elements");
     // (readfirstlane: the clamp compiles to a vector instruction, and a
@@ -263,13 +270,13 @@ struct BufTile {
     const int rows = __builtin_amdgcn_readfirstlane(min(max(nvalid - row0, 0), ROWS));
     const __amdgpu_buffer_rsrc_t rs = make_rsrc(g + (size_t)min(row0, nvalid) * D, rows * D * 2);
     __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (FA_LDS void*)(lds + (wave * PER + u) * 64 * 8),
-                                             16, voff[u], 0, 0, 0);
+                                             16, voff[u], 0, 0, AUX);
 #endif
   }
-  template <typename T>
+  template <int AUX = 0, typename T>
   __device__ __forceinline__ void tile(const T* g, int row0, int nvalid, T* lds) const {
 #pragma unroll
-    for (int u = 0; u < PER; ++u) part(g, row0, nvalid, lds, u);
+    for (int u = 0; u < PER; ++u) part<AUX>(g, row0, nvalid, lds, u);
   }
 };
 
