@@ -58,8 +58,8 @@ namespace fa {
 
 namespace {
 
-BiasDev bias_dev(const BiasArgs& b, int H, float scale) {
-  return BiasDev{b.ptr, b.sb, b.sh, b.sq, H, 1.f / scale, b.tmap, b.tm_sb, b.tm_sh, b.nkt4};
+BiasDev bias_dev(const BiasArgs& b, int B, int H, float scale) {
+  return make_bias_dev(b.ptr, b.sb, b.sh, b.sq, B, H, scale, b.tmap, b.tm_sb, b.tm_sh, b.nkt4);
 }
 
 
@@ -254,11 +254,19 @@ void bwd_dkdv_kernel(const T* __restrict__ Q, const T* __restrict__ K, const T* 
       const __amdgpu_buffer_rsrc_t rb =
           make_rsrc(bias_h + (size_t)qi0 * bias.sq + k0,
                     (int)(unsigned)(nb < 0xfffffff0ull ? nb : 0xfffffff0ull));
+      if (bias.stream) {
 #pragma unroll
-      for (int u = 0; u < IPB; ++u)
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(
-            rb, (FA_LDS void*)(sBias + buf * BTILE + (wave * IPB + u) * 64 * 8), 16, boff[u], 0,
-            0, 0);
+        for (int u = 0; u < IPB; ++u)
+          __builtin_amdgcn_raw_ptr_buffer_load_lds(
+              rb, (FA_LDS void*)(sBias + buf * BTILE + (wave * IPB + u) * 64 * 8), 16, boff[u],
+              0, 0, kLoadNonTemporal);
+      } else {
+#pragma unroll
+        for (int u = 0; u < IPB; ++u)
+          __builtin_amdgcn_raw_ptr_buffer_load_lds(
+              rb, (FA_LDS void*)(sBias + buf * BTILE + (wave * IPB + u) * 64 * 8), 16, boff[u],
+              0, 0, 0);
+      }
     }
 #endif
   };
@@ -649,10 +657,17 @@ void bwd_dq_kernel(const T* __restrict__ Q, const T* __restrict__ K, const T* __
     const unsigned bc0 = (unsigned)(((lane & 7) ^ (lane >> 4)) << 4);
     auto bias_issue = [&](int k0b) {
       lds_reads_done();  // the region's previous contents have been read
+      if (bias.stream) {
 #pragma unroll
-      for (int u = 0; u < 4; ++u)
-        lds_dma16_asm(brw, bbase + u * bstep + ((u & 1) ? (bc0 ^ 64u) : bc0) + (unsigned)k0b * 2,
-                      (const FA_LDS void*)(sBw + u * 64 * 8));
+        for (int u = 0; u < 4; ++u)
+          lds_dma16_asm<true>(brw, bbase + u * bstep + ((u & 1) ? (bc0 ^ 64u) : bc0) + (unsigned)k0b * 2,
+                              (const FA_LDS void*)(sBw + u * 64 * 8));
+      } else {
+#pragma unroll
+        for (int u = 0; u < 4; ++u)
+          lds_dma16_asm<false>(brw, bbase + u * bstep + ((u & 1) ? (bc0 ^ 64u) : bc0) + (unsigned)k0b * 2,
+                               (const FA_LDS void*)(sBw + u * 64 * 8));
+      }
     };
     // Chunks q0b .. q0b+3 (keys q*8 + half*4 .. +3 of this lane's row).
     auto bias_fetch = [&](BT4 (&bb)[8], int q0b) {
@@ -957,7 +972,7 @@ hipError_t launch_bwd_mfma(const BwdArgs& a, int stages, hipStream_t s) {
   const T* K = (const T*)a.K;
   const T* V = (const T*)a.V;
   const T* dO = (const T*)a.dO;
-  const BiasDev bias = bias_dev(a.bias, a.H, a.scale);
+  const BiasDev bias = bias_dev(a.bias, a.B, a.H, a.scale);
   const DropDev drop = drop_dev(a.drop);
   if (stages & 1) {
     const hipError_t e = (a.d == 128) ? launch_pre<128, T>(a, s) : launch_pre<64, T>(a, s);
@@ -1030,7 +1045,7 @@ hipError_t launch_bwd_f32(const BwdArgs& a, int stages, hipStream_t s) {
   const float* K = (const float*)a.K;
   const float* V = (const float*)a.V;
   const float* dO = (const float*)a.dO;
-  const BiasDev bias = bias_dev(a.bias, a.H, a.scale);
+  const BiasDev bias = bias_dev(a.bias, a.B, a.H, a.scale);
   const DropDev drop = drop_dev(a.drop);
   if ((stages & 2) && nkt > 0) {
 #define FA_DKDV32_LAUNCH(DD, CC)                                                             \

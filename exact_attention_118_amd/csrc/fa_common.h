@@ -209,17 +209,32 @@ __device__ __forceinline__ i32x4 rsrc_words(const void* base, unsigned bytes) {
   r[3] = (int)kRsrcWord3;
   return r;
 }
+// NT: the load is non-temporal (the nt cache-policy bit), for data that no
+// other workgroup reads again.
+template <bool NT>
 __device__ __forceinline__ void lds_dma16_asm(i32x4 rsrc, unsigned voff, const FA_LDS void* lds) {
   unsigned saved;
-  asm volatile(
-      "s_mov_b32 %0, m0\n\t"
-      "s_mov_b32 m0, %3\n\t"
-      "s_nop 0\n\t"
-      "buffer_load_dwordx4 %1, %2, 0 offen lds\n\t"
-      "s_mov_b32 m0, %0"
-      : "=&s"(saved)
-      : "v"(voff), "s"(rsrc), "s"((unsigned)(size_t)lds)
-      : "memory");
+  if constexpr (NT) {
+    asm volatile(
+        "s_mov_b32 %0, m0\n\t"
+        "s_mov_b32 m0, %3\n\t"
+        "s_nop 0\n\t"
+        "buffer_load_dwordx4 %1, %2, 0 offen nt lds\n\t"
+        "s_mov_b32 m0, %0"
+        : "=&s"(saved)
+        : "v"(voff), "s"(rsrc), "s"((unsigned)(size_t)lds)
+        : "memory");
+  } else {
+    asm volatile(
+        "s_mov_b32 %0, m0\n\t"
+        "s_mov_b32 m0, %3\n\t"
+        "s_nop 0\n\t"
+        "buffer_load_dwordx4 %1, %2, 0 offen lds\n\t"
+        "s_mov_b32 m0, %0"
+        : "=&s"(saved)
+        : "v"(voff), "s"(rsrc), "s"((unsigned)(size_t)lds)
+        : "memory");
+  }
 }
 
 // Before direct-to-LDS loads overwrite a region that this wave has just
@@ -302,7 +317,21 @@ struct BiasDev {
   const unsigned char* tmap;
   long long tm_sb, tm_sh;
   int nkt4;
+  // Nonzero when every bias element is read by one head of one batch only
+  // (no broadcast with a zero stride over more than one head or batch): its
+  // loads are then non-temporal.  A broadcast bias is re-read by the other
+  // heads and keeps cached loads.
+  int stream;
 };
+
+// BiasDev of a bias with element strides sb (batch), sh (head), sq (row),
+// for B batches of H heads.
+inline BiasDev make_bias_dev(const void* ptr, long long sb, long long sh, long long sq, int B,
+                             int H, float scale, const unsigned char* tmap, long long tm_sb,
+                             long long tm_sh, int nkt4) {
+  const bool reused = (sh == 0 && H > 1) || (sb == 0 && B > 1);
+  return BiasDev{ptr, sb, sh, sq, H, 1.f / scale, tmap, tm_sb, tm_sh, nkt4, reused ? 0 : 1};
+}
 
 // First and last nonzero byte of row[0 .. n) (lo > hi when none), over the
 // wave: lane i reads bytes i, i + 64, ...; the result is wave-uniform.

@@ -41,8 +41,8 @@ namespace fa {
 
 namespace {
 
-BiasDev bias_dev(const BiasArgs& b, int H, float scale) {
-  return BiasDev{b.ptr, b.sb, b.sh, b.sq, H, 1.f / scale, b.tmap, b.tm_sb, b.tm_sh, b.nkt4};
+BiasDev bias_dev(const BiasArgs& b, int B, int H, float scale) {
+  return make_bias_dev(b.ptr, b.sb, b.sh, b.sq, B, H, scale, b.tmap, b.tm_sb, b.tm_sh, b.nkt4);
 }
 
 
@@ -271,10 +271,17 @@ void fwd_kernel(const T* __restrict__ Q, const T* __restrict__ K, const T* __res
     const unsigned bc0 = (unsigned)(((lane & 7) ^ (lane >> 4)) << 4);
     auto bias_issue = [&](int k0b) {
       lds_reads_done();  // the region's previous contents have been read
+      if (bias.stream) {
 #pragma unroll
-      for (int u = 0; u < 4; ++u)
-        lds_dma16_asm(brw, bbase + u * bstep + ((u & 1) ? (bc0 ^ 64u) : bc0) + (unsigned)k0b * 2,
-                      (const FA_LDS void*)(sBw + u * 64 * 8));
+        for (int u = 0; u < 4; ++u)
+          lds_dma16_asm<true>(brw, bbase + u * bstep + ((u & 1) ? (bc0 ^ 64u) : bc0) + (unsigned)k0b * 2,
+                              (const FA_LDS void*)(sBw + u * 64 * 8));
+      } else {
+#pragma unroll
+        for (int u = 0; u < 4; ++u)
+          lds_dma16_asm<false>(brw, bbase + u * bstep + ((u & 1) ? (bc0 ^ 64u) : bc0) + (unsigned)k0b * 2,
+                               (const FA_LDS void*)(sBw + u * 64 * 8));
+      }
     };
     // Chunks q0b .. q0b+3 (keys q*8 + half*4 .. +3 of this lane's row).
     auto bias_fetch = [&](BT4 (&bb)[8], int q0b) {
@@ -637,7 +644,7 @@ hipError_t launch_fwd_mfma(const FwdArgs& a, hipStream_t s) {
   const T* K = (const T*)a.K;
   const T* V = (const T*)a.V;
   T* O = (T*)a.O;
-  const BiasDev bias = bias_dev(a.bias, a.H, a.scale);
+  const BiasDev bias = bias_dev(a.bias, a.B, a.H, a.scale);
   const DropDev drop = drop_dev(a.drop);
   const SplitDev nosplit{nullptr, nullptr, 1, 0, 0};
 #define FA_FWD_LAUNCH(DD, CC)                                                                 \
@@ -666,7 +673,7 @@ hipError_t launch_fwd_rows_split(const FwdArgs& a, int splits, int chunk, float*
   const T* Q = (const T*)a.Q;
   const T* K = (const T*)a.K;
   const T* V = (const T*)a.V;
-  const BiasDev nobias = bias_dev(BiasArgs{}, a.H, 1.f);
+  const BiasDev nobias = bias_dev(BiasArgs{}, a.B, a.H, 1.f);
   const DropDev nodrop = drop_dev(DropArgs{});
   const SplitDev split{part_o, part_l, splits, chunk, BH * a.Nq};
 #define FA_FWD_SPLIT_LAUNCH(DD, CC)                                                           \
@@ -712,7 +719,7 @@ hipError_t launch_fwd_f32(const FwdArgs& a, hipStream_t s) {
   const float* K = (const float*)a.K;
   const float* V = (const float*)a.V;
   float* O = (float*)a.O;
-  const BiasDev bias = bias_dev(a.bias, a.H, a.scale);
+  const BiasDev bias = bias_dev(a.bias, a.B, a.H, a.scale);
   const DropDev drop = drop_dev(a.drop);
 #define FA_FWD32_LAUNCH(DD, CC)                                                              \
   do {                                                                                       \
