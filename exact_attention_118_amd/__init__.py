@@ -68,11 +68,11 @@ def load_library():
                                 f, i, i, vp, sz, vp]
     lib.fa_bwd_bias.restype = i
     ull, u = ctypes.c_ulonglong, ctypes.c_uint
-    lib.fa_fwd_ex.argtypes = [vp, vp, vp, vp, ll, ll, ll, vp, f, ull, u, vp, vp, i, i, i, i, i, f,
-                              i, i, vp]
+    lib.fa_fwd_ex.argtypes = [vp, vp, vp, vp, ll, ll, ll, vp, sz, f, ull, u, vp, vp, i, i, i, i, i,
+                              f, i, i, vp]
     lib.fa_fwd_ex.restype = i
-    lib.fa_bwd_ex.argtypes = [vp, vp, vp, vp, ll, ll, ll, vp, f, ull, u, vp, vp, vp, vp, vp, vp, i,
-                              i, i, i, i, f, i, i, vp, sz, vp]
+    lib.fa_bwd_ex.argtypes = [vp, vp, vp, vp, ll, ll, ll, vp, sz, f, ull, u, vp, vp, vp, vp, vp, vp,
+                              i, i, i, i, i, f, i, i, vp, sz, vp]
     lib.fa_bwd_ex.restype = i
     lib.fa_bias_tile_map_size.argtypes = [ll, ll, i, i, i, i]
     lib.fa_bias_tile_map_size.restype = sz
@@ -122,10 +122,13 @@ def _ptr(t):
     return None if t is None else ctypes.c_void_p(t.data_ptr())
 
 
+def _stream(device, stream):
+    """The torch stream a call is enqueued on: `stream`, else the current one."""
+    return stream if stream is not None else _torch().cuda.current_stream(device)
+
+
 def _stream_handle(device, stream):
-    torch = _torch()
-    s = stream if stream is not None else torch.cuda.current_stream(device)
-    return ctypes.c_void_p(s.cuda_stream)
+    return ctypes.c_void_p(_stream(device, stream).cuda_stream)
 
 
 def _check_tensor(name, t, shape, dtype, device):
@@ -153,11 +156,38 @@ def fwd_num_splits(B, H, Nq, Nk, d, dtype_code, num_splits=0) -> int:
     return load_library().fa_fwd_num_splits(B, H, Nq, Nk, d, dtype_code, num_splits)
 
 
-def _alloc_workspace(nbytes, device):
+def _alloc_workspace(nbytes, device, stream):
+    """A workspace for a call enqueued on `stream` (None: the current stream).
+
+    The block is allocated on that stream, so torch's caching allocator hands
+    it to no other stream's allocation after it is freed here, while the
+    call's kernels may still be using it."""
     torch = _torch()
     if nbytes == 0:
         return None
-    return torch.empty(nbytes, dtype=torch.uint8, device=device)
+    with torch.cuda.stream(_stream(device, stream)):
+        return torch.empty(nbytes, dtype=torch.uint8, device=device)
+
+
+def _tile_map_arg(lib, tile_map, bias, sb, sh, B, H, Nq, Nk, device):
+    """(pointer, bytes) of a tile map after the checks that keep the kernels
+    inside it: a contiguous uint8 GPU tensor on the inputs' device holding at
+    least fa_bias_tile_map_size() bytes for this bias geometry."""
+    if tile_map is None:
+        return None, 0
+    torch = _torch()
+    if bias is None:
+        raise ValueError("tile_map needs the bias it was built from")
+    if not tile_map.is_cuda or tile_map.device != device:
+        raise ValueError(f"tile_map must be a GPU tensor on {device}")
+    if tile_map.dtype != torch.uint8:
+        raise ValueError(f"tile_map has dtype {tile_map.dtype}, expected torch.uint8")
+    if not tile_map.is_contiguous():
+        raise ValueError("tile_map must be contiguous")
+    need = lib.fa_bias_tile_map_size(sb, sh, B, H, Nq, Nk)
+    if tile_map.numel() < need:
+        raise ValueError(f"tile_map holds {tile_map.numel()} bytes; this bias needs {need}")
+    return _ptr(tile_map), tile_map.numel()
 
 
 def fa_fwd(Q, K, V, O, L, scale, causal, num_splits=0, workspace=None, stream=None):
@@ -174,7 +204,7 @@ def fa_fwd(Q, K, V, O, L, scale, causal, num_splits=0, workspace=None, stream=No
     code = _dtype_code(Q)
     need = lib.fa_fwd_workspace_size(B, H, Nq, Nk, d, code, num_splits)
     if workspace is None:
-        workspace = _alloc_workspace(need, dev)
+        workspace = _alloc_workspace(need, dev, stream)
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     st = lib.fa_fwd(_ptr(Q), _ptr(K), _ptr(V), _ptr(O), _ptr(L), B, H, Nq, Nk, d, float(scale),
                     int(bool(causal)), code, int(num_splits), _ptr(workspace), ws_bytes,
@@ -201,7 +231,7 @@ def fa_bwd(Q, K, V, O, L, dO, dQ, dK, dV, scale, causal, workspace=None, stream=
     code = _dtype_code(Q)
     need = lib.fa_bwd_workspace_size(B, H, Nq, Nk, d, code)
     if workspace is None:
-        workspace = _alloc_workspace(need, dev)
+        workspace = _alloc_workspace(need, dev, stream)
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     args = (_ptr(Q), _ptr(K), _ptr(V), _ptr(O), _ptr(L), _ptr(dO), _ptr(dQ), _ptr(dK), _ptr(dV),
             B, H, Nq, Nk, d, float(scale), int(bool(causal)), code, _ptr(workspace), ws_bytes,
@@ -268,7 +298,7 @@ def fa_bwd_bias(Q, K, V, bias, O, L, dO, dQ, dK, dV, scale, causal, workspace=No
     code = _dtype_code(Q)
     need = lib.fa_bwd_workspace_size(B, H, Nq, Nk, d, code)
     if workspace is None:
-        workspace = _alloc_workspace(need, dev)
+        workspace = _alloc_workspace(need, dev, stream)
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     st = lib.fa_bwd_bias(_ptr(Q), _ptr(K), _ptr(V), _ptr(bias), sb, sh, sq, _ptr(O), _ptr(L),
                          _ptr(dO), _ptr(dQ), _ptr(dK), _ptr(dV), B, H, Nq, Nk, d, float(scale),
@@ -297,7 +327,11 @@ def fa_bias_tile_map(bias, B, H, Nq, Nk, tile_map=None, stream=None):
     sb, sh, sq = _bias_strides(bias, B, H, Nq, Nk, bias.dtype, dev)
     n = lib.fa_bias_tile_map_size(sb, sh, B, H, Nq, Nk)
     if tile_map is None:
-        tile_map = torch.empty(max(n, 1), dtype=torch.uint8, device=dev)
+        with torch.cuda.stream(_stream(dev, stream)):
+            tile_map = torch.empty(max(n, 1), dtype=torch.uint8, device=dev)
+    elif (not tile_map.is_cuda or tile_map.device != dev or tile_map.dtype != torch.uint8
+          or not tile_map.is_contiguous()):
+        raise ValueError(f"tile_map must be a contiguous uint8 GPU tensor on {dev}")
     st = lib.fa_bias_tile_map(_ptr(bias), sb, sh, sq, B, H, Nq, Nk, _dtype_code(bias),
                               _ptr(tile_map), tile_map.numel(), _stream_handle(dev, stream))
     if st != FA_OK:
@@ -319,9 +353,9 @@ def fa_fwd_ex(Q, K, V, O, L, scale, causal, bias=None, dropout_p=0.0, seed=0, of
     _check_tensor("L", L, (B, H, Nq), _torch().float32, dev)
     _check_dropout(dropout_p, seed, offset)
     sb, sh, sq = (0, 0, 0) if bias is None else _bias_strides(bias, B, H, Nq, Nk, Q.dtype, dev)
+    map_ptr, map_bytes = _tile_map_arg(lib, tile_map, bias, sb, sh, B, H, Nq, Nk, dev)
     st = lib.fa_fwd_ex(_ptr(Q), _ptr(K), _ptr(V), None if bias is None else _ptr(bias), sb, sh, sq,
-                       None if tile_map is None else _ptr(tile_map),
-                       float(dropout_p), int(seed), int(offset), _ptr(O), _ptr(L), B, H, Nq, Nk, d,
+                       map_ptr, map_bytes, float(dropout_p), int(seed), int(offset), _ptr(O), _ptr(L), B, H, Nq, Nk, d,
                        float(scale), int(bool(causal)), _dtype_code(Q), _stream_handle(dev, stream))
     if st != FA_OK:
         raise FAError(st, "fa_fwd_ex")
@@ -343,14 +377,14 @@ def fa_bwd_ex(Q, K, V, O, L, dO, dQ, dK, dV, scale, causal, bias=None, dropout_p
     _check_tensor("L", L, (B, H, Nq), _torch().float32, dev)
     _check_dropout(dropout_p, seed, offset)
     sb, sh, sq = (0, 0, 0) if bias is None else _bias_strides(bias, B, H, Nq, Nk, Q.dtype, dev)
+    map_ptr, map_bytes = _tile_map_arg(lib, tile_map, bias, sb, sh, B, H, Nq, Nk, dev)
     code = _dtype_code(Q)
     need = lib.fa_bwd_workspace_size(B, H, Nq, Nk, d, code)
     if workspace is None:
-        workspace = _alloc_workspace(need, dev)
+        workspace = _alloc_workspace(need, dev, stream)
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     st = lib.fa_bwd_ex(_ptr(Q), _ptr(K), _ptr(V), None if bias is None else _ptr(bias), sb, sh, sq,
-                       None if tile_map is None else _ptr(tile_map),
-                       float(dropout_p), int(seed), int(offset), _ptr(O), _ptr(L), _ptr(dO),
+                       map_ptr, map_bytes, float(dropout_p), int(seed), int(offset), _ptr(O), _ptr(L), _ptr(dO),
                        _ptr(dQ), _ptr(dK), _ptr(dV), B, H, Nq, Nk, d, float(scale),
                        int(bool(causal)), code, _ptr(workspace), ws_bytes,
                        _stream_handle(dev, stream))

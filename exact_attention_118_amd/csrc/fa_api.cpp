@@ -11,7 +11,7 @@
 
 namespace {
 
-constexpr int kVersion = 1 * 10000 + 0 * 100 + 0;
+constexpr int kVersion = 2 * 10000 + 0 * 100 + 0;
 constexpr size_t kAlign = 16;
 constexpr size_t kWsAlign = 256;
 constexpr int kSplitTargetBlocks = 2048;  // aim for ~8 workgroups per CU on the split path
@@ -174,13 +174,17 @@ MapGeom map_geom(long long sb, long long sh, int B, int H, int Nq, int Nk) {
   return g;
 }
 
-// Attach a caller's tile map to the bias arguments (bias already checked).
-fa_status attach_map(const unsigned char* map, int B, int H, int Nq, int Nk, fa_dtype dtype,
-                     fa::BiasArgs* b) {
+// Attach a caller's tile map of map_bytes bytes to the bias arguments (bias
+// already checked): the kernels read every byte of the geometry below, so a
+// smaller buffer is refused.
+fa_status attach_map(const unsigned char* map, size_t map_bytes, int B, int H, int Nq, int Nk,
+                     fa_dtype dtype, fa::BiasArgs* b) {
   if (!map) return FA_OK;
   if (!b->ptr || dtype == FA_FP32) return FA_ERR_UNSUPPORTED;
   if (!aligned(map)) return FA_ERR_ALIGN;
   const MapGeom g = map_geom(b->sb, b->sh, B, H, Nq, Nk);
+  if (g.bytes() > INT_MAX) return FA_ERR_SHAPE;
+  if (map_bytes < (size_t)g.bytes()) return FA_ERR_WORKSPACE;
   b->tmap = map;
   b->nkt4 = (int)g.nkt4;
   b->tm_sh = b->sh ? g.nqt * g.nkt4 : 0;
@@ -353,9 +357,10 @@ fa_status fa_bwd_bias(const void* Q, const void* K, const void* V, const void* b
 
 fa_status fa_fwd_ex(const void* Q, const void* K, const void* V, const void* bias,
                     long long bias_sb, long long bias_sh, long long bias_sq,
-                    const unsigned char* bias_tile_map, float dropout_p, unsigned long long seed,
-                    unsigned int offset, void* O, float* L, int B, int H, int Nq, int Nk, int d,
-                    float scale, int causal, fa_dtype dtype, void* stream) {
+                    const unsigned char* bias_tile_map, size_t bias_tile_map_bytes,
+                    float dropout_p, unsigned long long seed, unsigned int offset, void* O,
+                    float* L, int B, int H, int Nq, int Nk, int d, float scale, int causal,
+                    fa_dtype dtype, void* stream) {
   fa_status st = check_dims(B, H, Nq, Nk, d, scale, causal, dtype);
   if (st != FA_OK) return st;
   fa::DropArgs dr;
@@ -371,7 +376,7 @@ fa_status fa_fwd_ex(const void* Q, const void* K, const void* V, const void* bia
     b.sh = bias_sh;
     b.sq = bias_sq;
   }
-  st = attach_map(bias_tile_map, B, H, Nq, Nk, dtype, &b);
+  st = attach_map(bias_tile_map, bias_tile_map_bytes, B, H, Nq, Nk, dtype, &b);
   if (st != FA_OK) return st;
   return fwd_impl(Q, K, V, b, dr, O, L, B, H, Nq, Nk, d, scale, causal, dtype, -1, nullptr, 0,
                   stream);
@@ -379,8 +384,9 @@ fa_status fa_fwd_ex(const void* Q, const void* K, const void* V, const void* bia
 
 fa_status fa_bwd_ex(const void* Q, const void* K, const void* V, const void* bias,
                     long long bias_sb, long long bias_sh, long long bias_sq,
-                    const unsigned char* bias_tile_map, float dropout_p, unsigned long long seed,
-                    unsigned int offset, const void* O, const float* L,
+                    const unsigned char* bias_tile_map, size_t bias_tile_map_bytes,
+                    float dropout_p, unsigned long long seed, unsigned int offset,
+                    const void* O, const float* L,
                     const void* dO, void* dQ, void* dK, void* dV, int B, int H, int Nq, int Nk,
                     int d, float scale, int causal, fa_dtype dtype, void* workspace,
                     size_t workspace_bytes, void* stream) {
@@ -397,7 +403,7 @@ fa_status fa_bwd_ex(const void* Q, const void* K, const void* V, const void* bia
     b.sb = bias_sb;
     b.sh = bias_sh;
     b.sq = bias_sq;
-    st = attach_map(bias_tile_map, B, H, Nq, Nk, dtype, &b);
+    st = attach_map(bias_tile_map, bias_tile_map_bytes, B, H, Nq, Nk, dtype, &b);
     if (st != FA_OK) return st;
   } else if (bias_tile_map && !bias) {
     return FA_ERR_UNSUPPORTED;

@@ -35,6 +35,7 @@ template <> struct Vec<f16> {
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
 constexpr int kNumXcd = 8;
+constexpr int kNumCu = 256;  // compute units of an MI355X
 
 // 32x32x16 bf16 / fp16 MFMA, fp32 accumulate.  Operand layout (lane l of 64):
 //   A[m][k]: m = l % 32, k = (l / 32) * 8 + e      (e = vector element 0..7)
@@ -76,6 +77,23 @@ __device__ __forceinline__ V8 zero8() {
 }
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+
+// acc + a + b for two 16-bit values as they are rounded (one v_dot2c_f32_bf16
+// or v_dot2c_f32_f16 against the pair (1, 1)): the sum of the probabilities
+// that enter the P V product, so that the output's normaliser carries the
+// same rounding as its numerator.
+__device__ __forceinline__ float add_pair(bf16 a, bf16 b, float acc) {
+  typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+  const bf16x2 v = {a, b};
+  const bf16x2 one = {(bf16)1.f, (bf16)1.f};
+  return __builtin_amdgcn_fdot2_f32_bf16(v, one, acc, false);
+}
+__device__ __forceinline__ float add_pair(f16 a, f16 b, float acc) {
+  typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
+  const f16x2 v = {a, b};
+  const f16x2 one = {(f16)1.f, (f16)1.f};
+  return __builtin_amdgcn_fdot2(v, one, acc, false);
+}
 
 // Workgroups are dispatched round-robin over the XCDs (block b runs on XCD
 // b % 8).  Map the hardware block index to a logical index so that each XCD

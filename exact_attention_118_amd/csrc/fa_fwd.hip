@@ -46,9 +46,11 @@ BiasDev bias_dev(const BiasArgs& b, int B, int H, float scale) {
 }
 
 
-constexpr int kFwdBR = 128;  // query rows per workgroup
+// A workgroup of NW waves owns 32 * NW query rows: NW = 4 (128 rows, two
+// workgroups per CU) or NW = 8 (256 rows, one per CU: each K/V tile staged
+// in LDS then serves twice the rows, halving the L2 -> LDS traffic per MFMA).
 constexpr int kFwdBC = 64;   // keys per K/V tile
-constexpr int kFwdThreads = 256;
+constexpr int kFwdBR4 = 128;  // query rows of the 4-wave shape (bias tile-map granularity)
 // The exponentials of the online softmax are taken against a reference that
 // lags the row max (see the tile step): every probability stays at or below
 // prob_limit<T>().  Floating point keeps its relative precision at any
@@ -74,14 +76,16 @@ struct SplitDev {
   int splits, chunk, rows;
 };
 
-template <typename T, int D, bool CAUSAL, bool BIAS, bool DROP, bool SPLIT>
-__global__ __launch_bounds__(kFwdThreads, 2) __attribute__((amdgpu_waves_per_eu(2, 2)))
+template <typename T, int D, bool CAUSAL, bool BIAS, bool DROP, bool SPLIT, int NW>
+__global__ __launch_bounds__(64 * NW, NW == 8 ? 1 : 2) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void fwd_kernel(const T* __restrict__ Q, const T* __restrict__ K, const T* __restrict__ V,
                 T* __restrict__ O, float* __restrict__ L, int Nq, int Nk, int nqt, float c,
                 int off, BiasDev bias, DropDev drop, SplitDev split) {
   typedef typename Vec<T>::x8 T8;
   typedef typename Vec<T>::x4 T4;
-  constexpr int BR = kFwdBR, BC = kFwdBC;
+  static_assert(NW == 4 || NW == 8, "4 or 8 waves");
+  constexpr int kFwdThreads = 64 * NW;
+  constexpr int BR = 32 * NW, BC = kFwdBC;
   constexpr int NKK = D / 16;  // MFMA k-steps over the head dim
   constexpr int NNT = D / 32;  // 32-wide output tiles over the head dim
   constexpr int TILE = BC * D;  // elements per K or V tile
@@ -141,7 +145,7 @@ void fwd_kernel(const T* __restrict__ Q, const T* __restrict__ K, const T* __res
 
   using KV = BufTile<D, BC, kFwdThreads>;
   const KV kv(wave, lane);
-  static_assert(2 * KV::PER == NKK, "one tile load every other score step");
+  static_assert(2 * KV::PER <= NKK, "tile loads fit the even score steps");
   // With key splits (a few query rows against many keys) each K/V tile is
   // read by one workgroup only: its loads are non-temporal (B4 H32 Nq16
   // Nk16384: 209 -> 178 us).  The tiled path re-reads every tile once per
@@ -220,7 +224,11 @@ void fwd_kernel(const T* __restrict__ Q, const T* __restrict__ K, const T* __res
     const int wrow_lo = q0 + wave * 32;  // smallest query row of this wave
 
     float m_run = -INFINITY;  // reference of the exponentials (row max so far, log2 units)
-    float l_run = 0.f;        // running sum of this lane half's probabilities
+    float l_run = 0.f;        // running sum of this lane half's probabilities (fp32, for L)
+    // running sum of the same probabilities as rounded to T for P V: O is
+    // normalised by it, so a dominant probability's rounding cancels between
+    // numerator and denominator (fp32 l would leave up to 2^-9 of it in O)
+    float lq_run = 0.f;
     f32x16 oacc[NNT];
 #pragma unroll
     for (int nt = 0; nt < NNT; ++nt) oacc[nt] = (f32x16){};
@@ -345,12 +353,14 @@ void fwd_kernel(const T* __restrict__ Q, const T* __restrict__ K, const T* __res
       // has seen no finite score yet (m_run = -inf) always takes that path, so
       // that its first finite scores set the reference.
       float m_ref = (m_run == -INFINITY) ? 0.f : m_run;
-      auto rebase = [&](float& part0, float& part1) {
+      auto rebase = [&](float& part0, float& part1, float& partq) {
         const float m_new = fmaxf(m_run, row_max(scur) * c);
         const float alpha = fast_exp2(m_run - (m_new == -INFINITY ? 0.f : m_new));
         l_run *= alpha;
+        lq_run *= alpha;
         part0 *= alpha;
         part1 *= alpha;
+        partq *= alpha;
 #pragma unroll
         for (int nt = 0; nt < NNT; ++nt) oacc[nt] *= alpha;
         m_run = m_new;
@@ -369,6 +379,8 @@ void fwd_kernel(const T* __restrict__ Q, const T* __restrict__ K, const T* __res
       // row sums of this lane's probabilities: rs[0..1] the early pairs,
       // rs[2..3] the late ones (two accumulators each)
       float rs[4] = {0.f, 0.f, 0.f, 0.f};
+      // the same sums over the rounded probabilities: rq[0] early, rq[1] late
+      float rq[2] = {0.f, 0.f};
       // Dropout (DROP): the random bytes of this lane's scores of tile j,
       // keys k0 + mt*32 + ... in rb[mt], each made just before its pairs (the
       // second half after the score block when its pairs go with P V); the
@@ -386,18 +398,20 @@ void fwd_kernel(const T* __restrict__ Q, const T* __restrict__ K, const T* __res
         const float p1 = fast_exp2(fmaf(scur[mt][i + 1], c, -m_ref));
         float& ra = rs[pr < kPairsA ? 0 : 2];
         float& rb_ = rs[pr < kPairsA ? 1 : 3];
+        float& rq_ = rq[pr < kPairsA ? 0 : 1];
         ra += p0;
         rb_ += p1;
+        pf[kc][e] = (T)p0;
+        pf[kc][e + 1] = (T)p1;
+        rq_ = add_pair(pf[kc][e], pf[kc][e + 1], rq_);
         if constexpr (DROP) {
-          pf[kc][e] = (T)(drop_keep(rb[mt][i >> 2], i & 3, drop.thresh) ? p0 : 0.f);
-          pf[kc][e + 1] = (T)(drop_keep(rb[mt][i >> 2], (i + 1) & 3, drop.thresh) ? p1 : 0.f);
-        } else {
-          pf[kc][e] = (T)p0;
-          pf[kc][e + 1] = (T)p1;
+          if (!drop_keep(rb[mt][i >> 2], i & 3, drop.thresh)) pf[kc][e] = (T)0.f;
+          if (!drop_keep(rb[mt][i >> 2], (i + 1) & 3, drop.thresh)) pf[kc][e + 1] = (T)0.f;
         }
         pin(pf[kc]);
         pin(ra);
         pin(rb_);
+        pin(rq_);
       };
 
       // Scores of tile j+1 on the MFMA pipe, interleaved step by step with
@@ -425,7 +439,7 @@ void fwd_kernel(const T* __restrict__ Q, const T* __restrict__ K, const T* __res
             const int di = st >> 1;
             if (di < KV::PER)
               kv.template part<KV_AUX>(Kh, k0 + 2 * BC, Nk, sK0 + P * TILE, di);
-            else
+            else if (di < 2 * KV::PER)
               kv.template part<KV_AUX>(Vh, k0 + BC, Nk, sV0 + (1 - P) * TILE, di - KV::PER);
           }
 #pragma unroll
@@ -438,8 +452,9 @@ void fwd_kernel(const T* __restrict__ Q, const T* __restrict__ K, const T* __res
       // max if some lane's sum of them exceeds the limit (nothing of tile j
       // has been accumulated yet).
       if (__builtin_amdgcn_ballot_w64(rs[0] + rs[1] > kProbLimit || m_run == -INFINITY) != 0) {
-        rebase(rs[0], rs[1]);
+        rebase(rs[0], rs[1], rq[0]);
         rs[0] = rs[1] = 0.f;
+        rq[0] = 0.f;
 #pragma unroll
         for (int pr = 0; pr < kPairsA; ++pr) prob_pair(pr);
       }
@@ -473,8 +488,9 @@ void fwd_kernel(const T* __restrict__ Q, const T* __restrict__ K, const T* __res
             // The late pairs are complete and their chunks not yet read: the
             // same check, now rescaling the early pairs' share of O and l.
             if (__builtin_amdgcn_ballot_w64(rs[2] + rs[3] > kProbLimit) != 0) {
-              rebase(rs[0], rs[1]);
+              rebase(rs[0], rs[1], rq[0]);
               rs[2] = rs[3] = 0.f;
+              rq[1] = 0.f;
 #pragma unroll
               for (int pr = kPairsA; pr < NPAIR; ++pr) prob_pair(pr);
             }
@@ -488,6 +504,7 @@ void fwd_kernel(const T* __restrict__ Q, const T* __restrict__ K, const T* __res
       }
       __builtin_amdgcn_s_setprio(0);
       l_run += (rs[0] + rs[1]) + (rs[2] + rs[3]);
+      lq_run += rq[0] + rq[1];
       vm_wait_all();  // this wave's part of tiles K j+2 and V j+1 has landed
       __syncthreads();
     };
@@ -497,14 +514,16 @@ void fwd_kernel(const T* __restrict__ Q, const T* __restrict__ K, const T* __res
       if (j + 1 < ntiles) tile_step(1, j + 1, sB, sA);
     }
 
-    // Epilogue: O = O_acc / l (times 1 / keep-probability with dropout),
-    // L = (m + log2 l) * ln 2.
+    // Epilogue: O = O_acc / lq (times 1 / keep-probability with dropout), lq
+    // the sum of the rounded probabilities; L = (m + log2 l) * ln 2 with the
+    // fp32 sum l.
     const float l_tot = xor32_sum(l_run);
+    const float lq_tot = xor32_sum(lq_run);
     if constexpr (SPLIT) {
       if (qrow < Nq) {
         const size_t prow = (size_t)sp * split.rows + (size_t)bh * Nq + qrow;
         const bool any = l_tot > 0.f;  // some key of the chunk is visible to this row
-        const float inv = any ? 1.f / l_tot : 0.f;
+        const float inv = any ? 1.f / lq_tot : 0.f;
         float* po = split.part_o + prow * D;
 #pragma unroll
         for (int nt = 0; nt < NNT; ++nt)
@@ -518,7 +537,7 @@ void fwd_kernel(const T* __restrict__ Q, const T* __restrict__ K, const T* __res
         if (half == 0) split.part_l[prow] = any ? (m_run + log2f(l_tot)) * kLn2 : -INFINITY;
       }
     } else if (qrow < Nq) {
-      const float inv = (DROP ? drop.inv_keep : 1.f) / l_tot;
+      const float inv = (DROP ? drop.inv_keep : 1.f) / lq_tot;
       T* orow = O + qbase + (size_t)qrow * D;
 #pragma unroll
       for (int nt = 0; nt < NNT; ++nt)
@@ -632,12 +651,17 @@ DropDev drop_dev(const DropArgs& d) {
   return DropDev{d.seed_lo, d.seed_hi, d.offset, d.on ? d.thresh : 256u, d.on ? d.inv_keep : 1.f};
 }
 
-template <typename T, bool BIAS, bool DROP>
-hipError_t launch_fwd_mfma(const FwdArgs& a, hipStream_t s) {
-  const int BH = a.B * a.H;
-  const int nqt = (a.Nq + kFwdBR - 1) / kFwdBR;
+// Workgroup count of the tiled forward grid with NW-wave workgroups.
+int fwd_blocks(const FwdArgs& a, int nw) {
+  const int nqt = (a.Nq + 32 * nw - 1) / (32 * nw);
   // Causal: one workgroup per pair of query tiles (t, nqt-1-t).
-  const int nblocks = (a.causal ? (nqt + 1) / 2 : nqt) * BH;
+  return (a.causal ? (nqt + 1) / 2 : nqt) * a.B * a.H;
+}
+
+template <typename T, bool BIAS, bool DROP, int NW>
+hipError_t launch_fwd_mfma(const FwdArgs& a, hipStream_t s) {
+  const int nqt = (a.Nq + 32 * NW - 1) / (32 * NW);
+  const int nblocks = fwd_blocks(a, NW);
   const float c = a.scale * kLog2e;
   const int off = a.Nk - a.Nq;
   const T* Q = (const T*)a.Q;
@@ -648,8 +672,8 @@ hipError_t launch_fwd_mfma(const FwdArgs& a, hipStream_t s) {
   const DropDev drop = drop_dev(a.drop);
   const SplitDev nosplit{nullptr, nullptr, 1, 0, 0};
 #define FA_FWD_LAUNCH(DD, CC)                                                                 \
-  hipLaunchKernelGGL((fwd_kernel<T, DD, CC, BIAS, DROP, false>), dim3(nblocks),               \
-                     dim3(kFwdThreads), 0, s, Q, K, V, O, a.L, a.Nq, a.Nk, nqt, c, off, bias, \
+  hipLaunchKernelGGL((fwd_kernel<T, DD, CC, BIAS, DROP, false, NW>), dim3(nblocks),           \
+                     dim3(64 * NW), 0, s, Q, K, V, O, a.L, a.Nq, a.Nk, nqt, c, off, bias,     \
                      drop, nosplit)
   if (a.d == 128) {
     if (a.causal) FA_FWD_LAUNCH(128, true); else FA_FWD_LAUNCH(128, false);
@@ -660,13 +684,23 @@ hipError_t launch_fwd_mfma(const FwdArgs& a, hipStream_t s) {
   return hipGetLastError();
 }
 
+// 8-wave workgroups when they still give every CU one (the bias path keeps
+// 4 waves: its tile map and staging regions are laid out for 128-row tiles).
+template <typename T, bool BIAS, bool DROP>
+hipError_t launch_fwd_shape(const FwdArgs& a, hipStream_t s) {
+  if constexpr (!BIAS) {
+    if (fwd_blocks(a, 8) >= kNumCu) return launch_fwd_mfma<T, BIAS, DROP, 8>(a, s);
+  }
+  return launch_fwd_mfma<T, BIAS, DROP, 4>(a, s);
+}
+
 // Key splits for a few query rows: (query tile, key chunk, batch*head) per
 // workgroup into the partial buffers; the caller runs the combine.
 template <typename T>
 hipError_t launch_fwd_rows_split(const FwdArgs& a, int splits, int chunk, float* part_o,
                                  float* part_l, hipStream_t s) {
   const int BH = a.B * a.H;
-  const int nqt = (a.Nq + kFwdBR - 1) / kFwdBR;
+  const int nqt = (a.Nq + kFwdBR4 - 1) / kFwdBR4;
   const int nblocks = nqt * BH * splits;
   const float c = a.scale * kLog2e;
   const int off = a.Nk - a.Nq;
@@ -677,8 +711,8 @@ hipError_t launch_fwd_rows_split(const FwdArgs& a, int splits, int chunk, float*
   const DropDev nodrop = drop_dev(DropArgs{});
   const SplitDev split{part_o, part_l, splits, chunk, BH * a.Nq};
 #define FA_FWD_SPLIT_LAUNCH(DD, CC)                                                           \
-  hipLaunchKernelGGL((fwd_kernel<T, DD, CC, false, false, true>), dim3(nblocks),              \
-                     dim3(kFwdThreads), 0, s, Q, K, V, (T*)a.O, a.L, a.Nq, a.Nk, nqt, c, off, \
+  hipLaunchKernelGGL((fwd_kernel<T, DD, CC, false, false, true, 4>), dim3(nblocks),           \
+                     dim3(256), 0, s, Q, K, V, (T*)a.O, a.L, a.Nq, a.Nk, nqt, c, off, \
                      nobias, nodrop, split)
   if (a.d == 128) {
     if (a.causal) FA_FWD_SPLIT_LAUNCH(128, true); else FA_FWD_SPLIT_LAUNCH(128, false);
@@ -692,8 +726,8 @@ hipError_t launch_fwd_rows_split(const FwdArgs& a, int splits, int chunk, float*
 template <typename T>
 hipError_t launch_fwd_typed(const FwdArgs& a, hipStream_t s) {
   if (a.drop.on)
-    return a.bias.ptr ? launch_fwd_mfma<T, true, true>(a, s) : launch_fwd_mfma<T, false, true>(a, s);
-  return a.bias.ptr ? launch_fwd_mfma<T, true, false>(a, s) : launch_fwd_mfma<T, false, false>(a, s);
+    return a.bias.ptr ? launch_fwd_shape<T, true, true>(a, s) : launch_fwd_shape<T, false, true>(a, s);
+  return a.bias.ptr ? launch_fwd_shape<T, true, false>(a, s) : launch_fwd_shape<T, false, false>(a, s);
 }
 
 }  // namespace

@@ -179,7 +179,11 @@ fa_status fa_bwd_bias(const void* Q, const void* K, const void* V, const void* b
  *  that fa_fwd_ex used, and regenerates the mask from them.
  *  bias_tile_map: NULL, or the map that fa_bias_tile_map wrote for this
  *  bias and these B, H, Nq, Nk (16-byte aligned; it needs a bias and a
- *  16-bit dtype, else FA_ERR_UNSUPPORTED).  With it the kernels skip the
+ *  16-bit dtype, else FA_ERR_UNSUPPORTED), in device memory of
+ *  bias_tile_map_bytes bytes: fewer than fa_bias_tile_map_size() for these
+ *  bias strides and sizes is FA_ERR_WORKSPACE (0 with a NULL map).  The map's
+ *  contents are trusted: a map built for another bias gives wrong results
+ *  (never an access outside the map or the bias).  With it the kernels skip the
  *  tiles of all -inf entries at the ends of each query tile's key range and
  *  of each key block's query range; the results are the same as without it.
  *  Both always take the tiled path (no key splits; fa_fwd_ex needs no
@@ -188,14 +192,16 @@ fa_status fa_bwd_bias(const void* Q, const void* K, const void* V, const void* b
  */
 fa_status fa_fwd_ex(const void* Q, const void* K, const void* V, const void* bias,
                     long long bias_sb, long long bias_sh, long long bias_sq,
-                    const unsigned char* bias_tile_map, float dropout_p, unsigned long long seed,
-                    unsigned int offset, void* O, float* L, int B, int H, int Nq, int Nk, int d,
-                    float scale, int causal, fa_dtype dtype, void* stream);
+                    const unsigned char* bias_tile_map, size_t bias_tile_map_bytes,
+                    float dropout_p, unsigned long long seed, unsigned int offset, void* O,
+                    float* L, int B, int H, int Nq, int Nk, int d, float scale, int causal,
+                    fa_dtype dtype, void* stream);
 
 fa_status fa_bwd_ex(const void* Q, const void* K, const void* V, const void* bias,
                     long long bias_sb, long long bias_sh, long long bias_sq,
-                    const unsigned char* bias_tile_map, float dropout_p, unsigned long long seed,
-                    unsigned int offset, const void* O, const float* L, const void* dO, void* dQ,
+                    const unsigned char* bias_tile_map, size_t bias_tile_map_bytes,
+                    float dropout_p, unsigned long long seed, unsigned int offset,
+                    const void* O, const float* L, const void* dO, void* dQ,
                     void* dK, void* dV, int B, int H, int Nq, int Nk, int d, float scale,
                     int causal, fa_dtype dtype, void* workspace, size_t workspace_bytes,
                     void* stream);

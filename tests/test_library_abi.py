@@ -48,7 +48,7 @@ def test_status_strings_and_version(lib):
         assert s.startswith(["FA_OK", "FA_ERR_NULL", "FA_ERR_SHAPE", "FA_ERR_UNSUPPORTED",
                              "FA_ERR_ALIGN", "FA_ERR_WORKSPACE", "FA_ERR_HIP"][code])
     assert "unknown" in fa.status_string(99)
-    assert fa.version() == 10000
+    assert fa.version() == 20000
 
 
 # Fake device addresses: only ever passed in combinations that validation rejects.
@@ -171,14 +171,19 @@ def test_bias_entry_points_accept_empty_problems(lib):
 
 
 def fwd_ex(lib, bias=None, sq=16, p=0.0, seed=1, offset=0, Q=A, B=1, Nq=16, Nk=16, d=64,
-           scale=0.125, causal=0, tmap=None, dtype=fa.FA_BF16):
-    return lib.fa_fwd_ex(Q, A, A, bias, 0, 0, sq, tmap, p, seed, offset, A, A, B, 1, Nq, Nk, d,
-                         scale, causal, dtype, None)
+           scale=0.125, causal=0, tmap=None, tmap_bytes=None, dtype=fa.FA_BF16):
+    if tmap_bytes is None:  # enough for the map of a broadcast bias of these sizes
+        tmap_bytes = 0 if tmap is None else lib.fa_bias_tile_map_size(0, 0, B, 1, Nq, Nk)
+    return lib.fa_fwd_ex(Q, A, A, bias, 0, 0, sq, tmap, tmap_bytes, p, seed, offset, A, A, B, 1, Nq,
+                         Nk, d, scale, causal, dtype, None)
 
 
-def bwd_ex(lib, bias=None, sq=16, p=0.0, ws=None, ws_bytes=0, Q=A, B=1, Nq=16, tmap=None):
-    return lib.fa_bwd_ex(Q, A, A, bias, 0, 0, sq, tmap, p, 1, 0, A, A, A, A, A, A, B, 1, Nq, 16, 64,
-                         0.125, 0, fa.FA_BF16, ws, ws_bytes, None)
+def bwd_ex(lib, bias=None, sq=16, p=0.0, ws=None, ws_bytes=0, Q=A, B=1, Nq=16, tmap=None,
+           tmap_bytes=None):
+    if tmap_bytes is None:
+        tmap_bytes = 0 if tmap is None else lib.fa_bias_tile_map_size(0, 0, B, 1, Nq, 16)
+    return lib.fa_bwd_ex(Q, A, A, bias, 0, 0, sq, tmap, tmap_bytes, p, 1, 0, A, A, A, A, A, A, B, 1,
+                         Nq, 16, 64, 0.125, 0, fa.FA_BF16, ws, ws_bytes, None)
 
 
 def test_ex_entry_points_reject_bad_arguments(lib):
@@ -207,6 +212,11 @@ def test_tile_map_arguments(lib):
     need = lib.fa_bwd_workspace_size(1, 1, 16, 16, 64, fa.FA_BF16)
     assert bwd_ex(lib, bias=None, tmap=A, ws=A, ws_bytes=need) == fa.FA_ERR_UNSUPPORTED
     assert bwd_ex(lib, bias=A, tmap=MIS, ws=A, ws_bytes=need) == fa.FA_ERR_ALIGN
+    # a map buffer smaller than the bias geometry needs is refused before any launch
+    # (Nq = 300, Nk = 16: 3 query tiles x 4 bytes)
+    assert fwd_ex(lib, bias=A, tmap=A, Nq=300, tmap_bytes=11) == fa.FA_ERR_WORKSPACE
+    assert fwd_ex(lib, bias=A, tmap=A, Nq=300, tmap_bytes=0) == fa.FA_ERR_WORKSPACE
+    assert bwd_ex(lib, bias=A, tmap=A, ws=A, ws_bytes=need, tmap_bytes=3) == fa.FA_ERR_WORKSPACE
     # size: [Bb][Hb][ceil(Nq/128)][ceil(Nk/64) rounded up to 4]
     assert lib.fa_bias_tile_map_size(0, 0, 2, 3, 300, 1000) == 1 * 1 * 3 * 16
     assert lib.fa_bias_tile_map_size(8, 8, 2, 3, 128, 64) == 2 * 3 * 1 * 4
@@ -226,8 +236,8 @@ def test_tile_map_arguments(lib):
 def test_ex_entry_points_accept_empty_problems(lib):
     assert fwd_ex(lib, p=0.5, Q=None, B=0) == fa.FA_OK
     assert fwd_ex(lib, p=0.5, Q=None, Nq=0) == fa.FA_OK
-    assert lib.fa_bwd_ex(*([None] * 4), 0, 0, 0, None, 0.5, 1, 0, *([None] * 6), 0, 1, 16, 16, 64,
-                         0.125, 0, fa.FA_BF16, None, 0, None) == fa.FA_OK
+    assert lib.fa_bwd_ex(*([None] * 4), 0, 0, 0, None, 0, 0.5, 1, 0, *([None] * 6), 0, 1, 16, 16,
+                         64, 0.125, 0, fa.FA_BF16, None, 0, None) == fa.FA_OK
 
 
 def test_workspace_queries(lib):
@@ -280,3 +290,43 @@ def test_product_code_does_not_touch_the_oracle():
                 text = open(os.path.join(dirpath, f), encoding="utf-8").read()
                 assert not re.search(r"^\s*(import|from)\s+oracle\b", text, re.M), f
                 assert "import_module(\"oracle" not in text, f
+
+
+class _FakeMap:
+    """Stands in for a torch tensor in the binding's tile-map checks (no GPU here)."""
+
+    def __init__(self, n, dtype=None, cuda=True, contiguous=True, device="cuda:0"):
+        import torch
+        self.is_cuda = cuda
+        self.device = torch.device(device)
+        self.dtype = torch.uint8 if dtype is None else dtype
+        self._n, self._c = n, contiguous
+
+    def numel(self):
+        return self._n
+
+    def is_contiguous(self):
+        return self._c
+
+    def data_ptr(self):
+        return 16
+
+
+def test_binding_checks_the_tile_map_before_any_call(lib):
+    import torch
+    dev = torch.device("cuda:0")
+    B, H, Nq, Nk = 2, 3, 300, 1000
+    need = lib.fa_bias_tile_map_size(0, 8, B, H, Nq, Nk)  # head-wise bias: 3 x 3 x 16 bytes
+    assert need == 3 * 3 * 16
+    bias = object()
+    ptr, n = fa._tile_map_arg(lib, _FakeMap(need), bias, 0, 8, B, H, Nq, Nk, dev)
+    assert n == need and ptr.value == 16
+    assert fa._tile_map_arg(lib, None, bias, 0, 8, B, H, Nq, Nk, dev) == (None, 0)
+    bad = [(_FakeMap(need - 1), "needs"), (_FakeMap(need, dtype=torch.int8), "uint8"),
+           (_FakeMap(need, cuda=False), "GPU tensor"), (_FakeMap(need, contiguous=False), "contiguous"),
+           (_FakeMap(need, device="cuda:1"), "GPU tensor")]
+    for m, msg in bad:
+        with pytest.raises(ValueError, match=msg):
+            fa._tile_map_arg(lib, m, bias, 0, 8, B, H, Nq, Nk, dev)
+    with pytest.raises(ValueError, match="needs the bias"):
+        fa._tile_map_arg(lib, _FakeMap(need), None, 0, 8, B, H, Nq, Nk, dev)

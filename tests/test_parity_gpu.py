@@ -195,14 +195,21 @@ def _gradient_sums(w, x, dK, dV):
     assert float((sdk.abs() / (adk + 1e-3)).max()) <= 1e-2
 
 
+# The backward kernels pin flat head bh to XCD bh % 8 when B*H is a multiple of
+# 8, so heads 0..7 cover every XCD's share of the grid; the full-oracle check
+# runs on those and on the last head.
+XCD_HEADS = list(range(8))
+
+
 @pytest.mark.parametrize("name", ["b2h16n4096d128_causal", "b2h16n4096d128", "b2h16n4096d128_causal_fp16"])
 def test_b2h16n4096d128_full(gpu_lib, name):
-    w, x, dK, dV = _sampled_head_check(gpu_lib, name, heads=[0, 31])
+    w, x, dK, dV = _sampled_head_check(gpu_lib, name, heads=XCD_HEADS + [31])
     _gradient_sums(w, x, dK, dV)
 
 
 def test_b1h32n8192d128_causal_full(gpu_lib):
-    w, x, dK, dV = _sampled_head_check(gpu_lib, "b1h32n8192d128_causal", heads=[5], rows_per_head=24)
+    w, x, dK, dV = _sampled_head_check(gpu_lib, "b1h32n8192d128_causal", heads=XCD_HEADS + [31],
+                                       rows_per_head=24)
     _gradient_sums(w, x, dK, dV)
 
 
@@ -435,7 +442,18 @@ def test_large_scores_and_uniform_keys(gpu_lib):
     torch.cuda.synchronize()
     O_ref, L_ref = oracle.attention_forward_batched(f64(x["Q"]), f64(x["K"]), f64(x["V"]), scale, True)
     assert max_abs(f64(O), O_ref) <= BF16_O
-    assert max_abs(f64(L), L_ref) <= 4 * BF16_L  # |L| ~ 100 here: fp32 score rounding
+    # L tracks the row's largest scores, which the kernel forms as fp32 sums of
+    # d = 128 exact bf16 products.  Recursive summation of n terms is off by at
+    # most n * 2^-24 * sum_k |q_k k_k| (Higham, Accuracy and Stability of
+    # Numerical Algorithms, section 4.2), and the logsumexp moves by at most the
+    # largest score error, so row i may differ from the float64 value by
+    # scale * 128 * 2^-24 * max_j sum_k |Q_ik K_jk| beyond the 1e-3 that holds
+    # at the workloads' score magnitudes.  Here the scores reach ~100.
+    Qa, Ka = np.abs(f64(x["Q"])), np.abs(f64(x["K"]))
+    rows_bound = scale * 128 * 2.0**-24 * np.max(Qa @ np.swapaxes(Ka, -1, -2), axis=-1)
+    err = np.abs(f64(L) - L_ref)
+    say(f"large scores: max |L - L_ref| = {err.max():.2e}, max rounding bound {rows_bound.max():.2e}")
+    assert np.all(err <= BF16_L + rows_bound)
     K = x["K"][:, :, :1].expand(-1, -1, 333, -1).contiguous()
     O, L = fa.forward(x["Q"], K, x["V"], scale, True)
     torch.cuda.synchronize()

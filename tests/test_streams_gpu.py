@@ -1,0 +1,62 @@
+"""Calls enqueued on a side stream (the `stream` argument of the binding).
+
+The workspaces the binding allocates for such a call (split-path partials,
+the backward pass's per-row pairs) must stay reserved for that stream until
+its kernels have used them; the results are checked against the float64
+oracle after synchronising.  Other allocations on the current stream run in
+between, so a workspace handed to them too early would be overwritten.
+"""
+
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from exact_attention_118_amd import synth
+
+pytestmark = pytest.mark.gpu
+
+
+def f64(t):
+    return t.detach().float().cpu().double().numpy()
+
+
+def test_side_stream_split_forward_and_backward(gpu_lib):
+    fa = gpu_lib
+    print("side stream: split forward, backward", flush=True)
+    scale = 1 / math.sqrt(128)
+    dec = synth.make_inputs(synth.Workload("dec", 4, 8, 1, 4100, 128, False, torch.bfloat16),
+                            seed=21, device="cpu")
+    x = synth.make_inputs(synth.Workload("bwd", 2, 4, 700, 700, 128, True, torch.bfloat16),
+                          seed=22, device="cpu")
+    dec = {k: v.cuda() for k, v in dec.items()}
+    x = {k: v.cuda() for k, v in x.items()}
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        O0, L0 = fa.forward(x["Q"], x["K"], x["V"], scale, True)
+    side.synchronize()
+    outs = []
+    for _ in range(3):
+        # a long kernel first, so the calls below are still queued when the
+        # binding drops its workspaces and the current stream allocates again
+        busy = torch.empty(64 << 20, dtype=torch.uint8, device="cuda")
+        with torch.cuda.stream(side):
+            torch.cuda._sleep(20_000_000)
+        Od, Ld = fa.forward(dec["Q"], dec["K"], dec["V"], scale, False, num_splits=3, stream=side)
+        g = fa.backward(x["Q"], x["K"], x["V"], O0, L0, x["dO"], scale, True, stream=side)
+        junk = [torch.full((1 << 20,), 7.0, device="cuda") for _ in range(32)]
+        outs.append((Od, Ld, g))
+        del busy, junk
+    side.synchronize()
+    torch.cuda.synchronize()
+    Or, Lr = oracle.attention_forward_batched(f64(dec["Q"]), f64(dec["K"]), f64(dec["V"]), scale, False)
+    ref = oracle.attention_backward_batched(f64(x["Q"]), f64(x["K"]), f64(x["V"]), f64(x["dO"]),
+                                            scale, True)
+    for Od, Ld, g in outs:
+        assert float(np.max(np.abs(f64(Od) - Or))) <= 2e-2
+        assert float(np.max(np.abs(f64(Ld) - Lr))) <= 1e-3
+        for got, want in zip(g, ref):
+            assert np.linalg.norm(f64(got) - want) / np.linalg.norm(want) <= 1e-2
