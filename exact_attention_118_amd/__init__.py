@@ -14,7 +14,7 @@ import os
 
 __all__ = [
     "FAError", "load_library", "lib_path", "fa_fwd", "fa_bwd", "fa_fwd_bias", "fa_bwd_bias",
-    "fa_fwd_ex", "fa_bwd_ex", "fa_bias_tile_map",
+    "fa_fwd_ex", "fa_bwd_ex", "fa_bias_tile_map", "fa_bwd_noalloc", "bwd_noalloc_max_rows",
     "forward", "backward",
     "fwd_workspace_size", "bwd_workspace_size", "fwd_num_splits", "status_string", "version",
     "FA_OK", "FA_ERR_NULL", "FA_ERR_SHAPE", "FA_ERR_UNSUPPORTED", "FA_ERR_ALIGN",
@@ -30,7 +30,7 @@ FA_BWD_PREPROCESS, FA_BWD_DKDV, FA_BWD_DQ, FA_BWD_ALL = 1, 2, 4, 7
 EXPORTED_SYMBOLS = ("fa_fwd", "fa_bwd", "fa_bwd_stages", "fa_fwd_bias", "fa_bwd_bias",
                     "fa_fwd_ex", "fa_bwd_ex", "fa_bias_tile_map", "fa_bias_tile_map_size",
                     "fa_fwd_workspace_size", "fa_bwd_workspace_size", "fa_fwd_num_splits",
-                    "fa_status_string", "fa_version")
+                    "fa_status_string", "fa_version", "fa_bwd_noalloc", "fa_bwd_noalloc_max_rows")
 
 _LIB = None
 
@@ -61,6 +61,10 @@ def load_library():
     lib.fa_bwd.restype = i
     lib.fa_bwd_stages.argtypes = lib.fa_bwd.argtypes + [i]
     lib.fa_bwd_stages.restype = i
+    lib.fa_bwd_noalloc.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, i, i, i, i, i, f, i, i, vp]
+    lib.fa_bwd_noalloc.restype = i
+    lib.fa_bwd_noalloc_max_rows.argtypes = []
+    lib.fa_bwd_noalloc_max_rows.restype = sz
     ll = ctypes.c_longlong
     lib.fa_fwd_bias.argtypes = [vp, vp, vp, vp, ll, ll, ll, vp, vp, i, i, i, i, i, f, i, i, vp]
     lib.fa_fwd_bias.restype = i
@@ -242,6 +246,32 @@ def fa_bwd(Q, K, V, O, L, dO, dQ, dK, dV, scale, causal, workspace=None, stream=
         st = lib.fa_bwd_stages(*args, int(stages))
     if st != FA_OK:
         raise FAError(st, "fa_bwd")
+    return dQ, dK, dV
+
+
+def bwd_noalloc_max_rows() -> int:
+    return load_library().fa_bwd_noalloc_max_rows()
+
+
+def fa_bwd_noalloc(Q, K, V, O, L, dO, dQ, dK, dV, scale, causal, stream=None):
+    """Call ``fa_bwd_noalloc``: ``fa_bwd`` with the library's own scratch
+    array instead of a workspace (nothing is allocated; calls that overlap on
+    one GPU race)."""
+    lib = load_library()
+    B, H, Nq, d = Q.shape
+    Nk = K.shape[2]
+    dev = Q.device
+    for name, t, shp in (("Q", Q, (B, H, Nq, d)), ("K", K, (B, H, Nk, d)), ("V", V, (B, H, Nk, d)),
+                         ("O", O, (B, H, Nq, d)), ("dO", dO, (B, H, Nq, d)),
+                         ("dQ", dQ, (B, H, Nq, d)), ("dK", dK, (B, H, Nk, d)),
+                         ("dV", dV, (B, H, Nk, d))):
+        _check_tensor(name, t, shp, Q.dtype, dev)
+    _check_tensor("L", L, (B, H, Nq), _torch().float32, dev)
+    st = lib.fa_bwd_noalloc(_ptr(Q), _ptr(K), _ptr(V), _ptr(O), _ptr(L), _ptr(dO), _ptr(dQ),
+                            _ptr(dK), _ptr(dV), B, H, Nq, Nk, d, float(scale), int(bool(causal)),
+                            _dtype_code(Q), _stream_handle(dev, stream))
+    if st != FA_OK:
+        raise FAError(st, "fa_bwd_noalloc")
     return dQ, dK, dV
 
 

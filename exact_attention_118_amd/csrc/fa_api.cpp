@@ -6,6 +6,7 @@
 #include <climits>
 #include <cmath>
 #include <cstdint>
+#include <mutex>
 
 #include "fa_launch.h"
 
@@ -114,6 +115,33 @@ SplitWs split_ws(int BH, int d, int splits) {
 // Backward workspace: the fp32 pairs (L*log2(e), D) of every query row.
 size_t bwd_ws_half(int BH, int Nq) { return round_up((size_t)BH * Nq * sizeof(float), kWsAlign); }
 size_t bwd_ws_bytes(int BH, int Nq) { return 2 * bwd_ws_half(BH, Nq); }
+
+// Scratch of fa_bwd_noalloc: the per-row (L*log2(e), D) pairs that fa_bwd
+// keeps in the caller's workspace.  One copy per GPU, held until the process
+// ends; every call on a GPU shares it.  In host code `scratch` names a
+// host-side stand-in, never the device memory: the kernels get the device
+// address that hipGetSymbolAddress returns for the current device.
+constexpr size_t kNoAllocScratchBytes = size_t(16) << 20;
+__device__ __align__(256) unsigned char scratch[kNoAllocScratchBytes];
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+// Device address of `scratch` on the current device, looked up once per device.
+fa_status scratch_address(void** out) {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess) return FA_ERR_HIP;
+  if (dev < 0 || dev >= kMaxDevices) return FA_ERR_UNSUPPORTED;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* p = nullptr;
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p) return FA_ERR_HIP;
+    g_scratch_ptr[dev] = p;
+  }
+  *out = g_scratch_ptr[dev];
+  return FA_OK;
+}
 
 }  // namespace
 
@@ -447,6 +475,26 @@ fa_status fa_bwd(const void* Q, const void* K, const void* V, const void* O, con
   return fa_bwd_stages(Q, K, V, O, L, dO, dQ, dK, dV, B, H, Nq, Nk, d, scale, causal, dtype,
                        workspace, workspace_bytes, stream, FA_BWD_ALL);
 }
+
+fa_status fa_bwd_noalloc(const void* Q, const void* K, const void* V, const void* O,
+                         const float* L, const void* dO, void* dQ, void* dK, void* dV, int B,
+                         int H, int Nq, int Nk, int d, float scale, int causal, fa_dtype dtype,
+                         void* stream) {
+  const fa_status st = check_dims(B, H, Nq, Nk, d, scale, causal, dtype);
+  if (st != FA_OK) return st;
+  if ((long long)B * H == 0 || Nq == 0) {
+    return bwd_impl(Q, K, V, fa::BiasArgs{}, fa::DropArgs{}, O, L, dO, dQ, dK, dV, B, H, Nq, Nk,
+                    d, scale, causal, dtype, nullptr, 0, stream, FA_BWD_ALL);
+  }
+  if (bwd_ws_bytes(B * H, Nq) > kNoAllocScratchBytes) return FA_ERR_WORKSPACE;
+  void* ws = nullptr;
+  const fa_status sa = scratch_address(&ws);
+  if (sa != FA_OK) return sa;
+  return bwd_impl(Q, K, V, fa::BiasArgs{}, fa::DropArgs{}, O, L, dO, dQ, dK, dV, B, H, Nq, Nk, d,
+                  scale, causal, dtype, ws, kNoAllocScratchBytes, stream, FA_BWD_ALL);
+}
+
+size_t fa_bwd_noalloc_max_rows(void) { return kNoAllocScratchBytes / 8; }
 
 fa_status fa_bwd_stages(const void* Q, const void* K, const void* V, const void* O,
                         const float* L, const void* dO, void* dQ, void* dK, void* dV, int B,

@@ -32,8 +32,9 @@
  *  - Supported: dtypes FA_BF16 and FA_FP16 with d in {64, 128} for every
  *    entry point (MFMA kernels, fp32 accumulation and statistics); dtype
  *    FA_FP32 with d in {64, 128} for fa_fwd (non-split) and fa_bwd.
- *  - Thread safety: no global mutable state; concurrent calls on different
- *    streams with disjoint buffers are safe.
+ *  - Thread safety: the only global mutable state is fa_bwd_noalloc's scratch
+ *    array; other concurrent calls on different streams with disjoint
+ *    buffers are safe.
  */
 #ifndef FA_H_
 #define FA_H_
@@ -122,6 +123,26 @@ fa_status fa_bwd_stages(const void* Q, const void* K, const void* V, const void*
                         int B, int H, int Nq, int Nk, int d, float scale, int causal,
                         fa_dtype dtype, void* workspace, size_t workspace_bytes, void* stream,
                         int stages);
+
+/*
+ * fa_bwd for callers that cannot allocate device memory (code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc): the same
+ * arguments and results as fa_bwd without the workspace.  The per-row
+ * (L*log2(e), D) pairs go to a scratch array inside the library instead, one
+ * per GPU, of fa_bwd_noalloc_max_rows() rows (16 MiB; held until the process
+ * ends).  B*H*Nq rows beyond that return FA_ERR_WORKSPACE before any launch.
+ * The first call on a GPU looks up the array's address there; no call
+ * allocates or frees memory.  Calls on one GPU share the array, so calls
+ * that overlap on one GPU (different streams, or threads) race: serialise
+ * them.  Every row the kernels read is written earlier in the same call.
+ */
+fa_status fa_bwd_noalloc(const void* Q, const void* K, const void* V, const void* O,
+                         const float* L, const void* dO, void* dQ, void* dK, void* dV,
+                         int B, int H, int Nq, int Nk, int d, float scale, int causal,
+                         fa_dtype dtype, void* stream);
+
+/* Largest B*H*Nq that fa_bwd_noalloc accepts. */
+size_t fa_bwd_noalloc_max_rows(void);
 
 /*
  * Forward and backward passes with an additive bias -- the mask term of the

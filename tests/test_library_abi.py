@@ -330,3 +330,16 @@ def test_binding_checks_the_tile_map_before_any_call(lib):
             fa._tile_map_arg(lib, m, bias, 0, 8, B, H, Nq, Nk, dev)
     with pytest.raises(ValueError, match="needs the bias"):
         fa._tile_map_arg(lib, _FakeMap(need), None, 0, 8, B, H, Nq, Nk, dev)
+
+
+def test_noalloc_backward_rejects_before_any_launch(lib):
+    rows = lib.fa_bwd_noalloc_max_rows()
+    assert rows == (16 << 20) // 8
+    args = lambda B, H, N, d=64, scale=0.125: (A, A, A, A, A, A, A, A, A, B, H, N, N, d, scale, 0,
+                                               fa.FA_BF16, None)
+    # one row past the scratch array: refused without touching the GPU
+    assert lib.fa_bwd_noalloc(*args(1, 2, rows // 2 + 8)) == fa.FA_ERR_WORKSPACE
+    assert lib.fa_bwd_noalloc(*args(1, 1, 16, d=96)) == fa.FA_ERR_UNSUPPORTED
+    assert lib.fa_bwd_noalloc(*args(1, 1, 16, scale=-1.0)) == fa.FA_ERR_UNSUPPORTED
+    assert lib.fa_bwd_noalloc(*args(-1, 1, 16)) == fa.FA_ERR_SHAPE
+    assert lib.fa_bwd_noalloc(*args(0, 4, 16)) == fa.FA_OK
