@@ -395,6 +395,158 @@ def bench_dropout(fa, torch, w, x, ws, steps, p=0.1):
     return r
 
 
+class PowerSampler:
+    """Board power and shader clock sampled through amdsmi in a background
+    thread; windows of samples are attributed to the probe running then.  Does
+    nothing (and reports None) where amdsmi or its device is unavailable."""
+
+    def __init__(self, period_s=0.004):
+        import threading
+        self.samples, self.ok, self.note = [], False, None
+        try:
+            import amdsmi
+            amdsmi.amdsmi_init()
+            handles = amdsmi.amdsmi_get_processor_handles()
+            self.h = handles[0]
+            try:
+                import torch
+                bus = getattr(torch.cuda.get_device_properties(0), "pci_bus_id", None)
+                for h in handles:
+                    bdf = amdsmi.amdsmi_get_gpu_device_bdf(h)
+                    if bus is not None and int(bdf.split(":")[1], 16) == int(bus):
+                        self.h = h
+            except Exception:
+                pass
+            self.amdsmi = amdsmi
+            self._read()
+            self.ok = True
+            self.note = f"{len(handles)} device(s) listed by amdsmi"
+        except Exception as e:  # no amdsmi, no device access
+            self.note = f"amdsmi unavailable: {type(e).__name__}: {e}"
+        self.stop = threading.Event()
+        if self.ok:
+            self.thread = threading.Thread(target=self._run, args=(period_s,), daemon=True)
+            self.thread.start()
+
+    def _read(self):
+        a = self.amdsmi
+        p = a.amdsmi_get_power_info(self.h)
+        c = a.amdsmi_get_clock_info(self.h, a.AmdSmiClkType.GFX)
+        watts = p.get("current_socket_power", p.get("average_socket_power"))
+        return float(watts), float(c.get("clk")), p.get("power_limit")
+
+    def _run(self, period_s):
+        while not self.stop.is_set():
+            try:
+                w, mhz, lim = self._read()
+                self.samples.append((time.perf_counter(), w, mhz, lim))
+            except Exception:
+                pass
+            time.sleep(period_s)
+
+    def window(self, t0, t1):
+        xs = [s for s in self.samples if t0 <= s[0] <= t1]
+        if not xs:
+            return {"power_W": None, "gfx_clock_MHz": None, "samples": 0}
+        return {"power_W": sum(s[1] for s in xs) / len(xs),
+                "gfx_clock_MHz": sum(s[2] for s in xs) / len(xs),
+                "power_limit": xs[-1][3], "samples": len(xs)}
+
+    def close(self):
+        self.stop.set()
+
+
+def run_probes(seconds):
+    """Machine probes (libfa_probe.so) and the attention kernels, each run in a
+    loop for `seconds` while board power and shader clock are sampled:
+    MFMA loops with constant or random operands, with 1 KB of LDS reads and/or
+    one exponential and four FMAs per MFMA; the forward, dK/dV and dQ kernels
+    on the long-sequence workload; fp32 atomic adds against plain stores in the
+    pattern of an MFMA result tile.  Prints one JSON line."""
+    import ctypes
+
+    import torch
+
+    import exact_attention_118_amd as fa
+    from exact_attention_118_amd import synth
+
+    plib = ctypes.CDLL(os.path.join(ROOT, "exact_attention_118_amd", "libfa_probe.so"))
+    plib.fa_probe_mfma.argtypes = [ctypes.c_int] * 3 + [ctypes.c_void_p] * 2
+    plib.fa_probe_adds.argtypes = [ctypes.c_int, ctypes.c_void_p] + [ctypes.c_int] * 3 + [ctypes.c_void_p]
+    fa.load_library()
+    sampler = PowerSampler()
+    stream = torch.cuda.current_stream()
+    results = []
+
+    def timed(name, launch, work, unit):
+        for _ in range(2):
+            launch()
+        torch.cuda.synchronize()
+        evs = []
+        t0 = time.perf_counter()
+        while time.perf_counter() - t0 < seconds or len(evs) < 3:
+            e = (torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+            e[0].record()
+            launch()
+            e[1].record()
+            evs.append(e)
+            if len(evs) % 8 == 0:
+                evs[-1][1].synchronize()
+        torch.cuda.synchronize()
+        t1 = time.perf_counter()
+        ms = sorted(a.elapsed_time(b) for a, b in evs)
+        med = ms[len(ms) // 2]
+        r = {"probe": name, "launches": len(evs), "median_ms": med, unit: work / (med * 1e-3)}
+        r.update(sampler.window(t0 + 0.25 * (t1 - t0), t1))
+        log(f"{name:44s} {med * 1e3:9.1f} us  {r[unit]:.4g} {unit}  "
+            f"power {r['power_W']} W  clock {r['gfx_clock_MHz']} MHz")
+        results.append(r)
+
+    blocks, iters = 256, 512
+    out = torch.empty(blocks * 512, dtype=torch.float32, device="cuda")
+    mfma_flops = blocks * 8 * iters * 32 * 32768.0
+    for mode, label in ((0, "MFMA, constant operands"), (1, "MFMA, random operands"),
+                        (3, "random MFMA + 1 KB LDS reads per MFMA"),
+                        (5, "random MFMA + 1 exp + 4 FMA per MFMA"),
+                        (7, "random MFMA + LDS reads + exp/FMA")):
+        timed(label, lambda m=mode: plib.fa_probe_mfma(m, blocks, iters, ctypes.c_void_p(out.data_ptr()),
+                                                       ctypes.c_void_p(stream.cuda_stream)),
+              mfma_flops / 1e12, "TFLOP/s")
+
+    w = synth.WORKLOADS["b1h32n8192d128_causal"]
+    x = synth.make_inputs(w, seed=0, device="cuda")
+    O = torch.empty_like(x["Q"])
+    L = torch.empty(w.B, w.H, w.Nq, dtype=torch.float32, device="cuda")
+    g = [torch.empty_like(x["Q"]) for _ in range(3)]
+    ws = torch.empty(fa.bwd_workspace_size(w.B, w.H, w.Nq, w.Nk, w.d, fa.FA_BF16), dtype=torch.uint8,
+                     device="cuda")
+    pairs = unmasked_pairs(w.Nq, w.Nk, w.causal) * w.B * w.H
+    fa.fa_fwd(x["Q"], x["K"], x["V"], O, L, w.scale, w.causal)
+    fa.fa_bwd(x["Q"], x["K"], x["V"], O, L, x["dO"], *g, w.scale, w.causal, workspace=ws,
+              stages=fa.FA_BWD_PREPROCESS)
+    timed("fwd_kernel (4*d flop per pair)",
+          lambda: fa.fa_fwd(x["Q"], x["K"], x["V"], O, L, w.scale, w.causal), 4 * w.d * pairs / 1e12,
+          "TFLOP/s")
+    timed("bwd_dkdv_kernel (8*d flop per pair)",
+          lambda: fa.fa_bwd(x["Q"], x["K"], x["V"], O, L, x["dO"], *g, w.scale, w.causal, workspace=ws,
+                            stages=fa.FA_BWD_DKDV), 8 * w.d * pairs / 1e12, "TFLOP/s")
+    timed("bwd_dq_kernel (6*d flop per pair executed)",
+          lambda: fa.fa_bwd(x["Q"], x["K"], x["V"], O, L, x["dO"], *g, w.scale, w.causal, workspace=ws,
+                            stages=fa.FA_BWD_DQ), 6 * w.d * pairs / 1e12, "TFLOP/s")
+    del x, O, L, g, ws
+
+    nrb, ablocks, aiters = 8192, 2048, 16  # a 128 MiB buffer
+    buf = torch.zeros(nrb * 32 * 128, dtype=torch.float32, device="cuda")
+    adds = ablocks * aiters * 4096
+    for atomic, label in ((0, "fp32 stores, MFMA-tile pattern"), (1, "fp32 atomic adds (device scope)")):
+        timed(label, lambda a=atomic: plib.fa_probe_adds(a, ctypes.c_void_p(buf.data_ptr()), nrb, ablocks,
+                                                         aiters, ctypes.c_void_p(stream.cuda_stream)),
+              adds / 1e9, "G values/s")
+    sampler.close()
+    print(json.dumps({"probes": results, "power_sampling": sampler.note, "seconds_per_probe": seconds}),
+          flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__)
     ap.add_argument("--gpus", type=int, default=1)
@@ -416,7 +568,13 @@ def main():
                          "MiB (reference point for HBM byte counters under rocprofv3 --pmc)")
     ap.add_argument("--write-traffic", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
                     help="write profiles/hbm_traffic.json from two rocprofv3 counter runs and exit")
+    ap.add_argument("--probes", type=float, default=0.0, metavar="SECONDS",
+                    help="run the machine probes and the attention kernels, each for SECONDS, "
+                         "sampling board power and clock, print one JSON line and exit")
     args = ap.parse_args()
+    if args.probes > 0:
+        run_probes(args.probes)
+        return
 
     if args.write_traffic:
         write_traffic(*args.write_traffic, copy_mib=args.copy_calibration_mib or 1024)

@@ -13,6 +13,9 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(PKG, "libfa.so")
+# measurement probes for bench.py --probes (no part of the attention path)
+PROBE_LIB = os.path.join(PKG, "libfa_probe.so")
+PROBE_SOURCES = ["fa_probe.hip"]
 OBJDIR = os.path.join(PKG, "_build")
 
 SOURCES = ["fa_api.cpp", "fa_fwd.hip", "fa_bwd.hip", "fa_split.hip", "fa_tilemap.hip"]
@@ -28,8 +31,6 @@ COMMON_FLAGS = [
     # packed fp32 instructions stay off (the compiler would otherwise form
     # v_pk_{add,mul,fma}_f32 from float2 code)
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
-    # let fp32 atomic adds lower to the hardware global_atomic_add_f32
-    "-munsafe-fp-atomics",
     f"-I{INCLUDE}",
     f"-I{CSRC}",
 ]
@@ -59,19 +60,26 @@ def _compile(src: str, verbose: bool) -> str:
     return obj
 
 
-def build(verbose: bool = False) -> str:
-    """Compile every source and link libfa.so next to this file; returns its path."""
-    os.makedirs(OBJDIR, exist_ok=True)
-    with ThreadPoolExecutor(max_workers=min(len(SOURCES), os.cpu_count() or 4)) as ex:
-        objs = list(ex.map(lambda s: _compile(s, verbose), SOURCES))
-    tmp = LIB + ".tmp"
+def _link(objs, out, verbose):
+    tmp = out + ".tmp"
     cmd = [hipcc(), f"--offload-arch={ARCH}", "-shared", "-fPIC", *objs, "-o", tmp]
     if verbose:
         print(" ".join(cmd), flush=True)
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"link failed:\n{r.stdout}{r.stderr}")
-    os.replace(tmp, LIB)
+    os.replace(tmp, out)
+
+
+def build(verbose: bool = False) -> str:
+    """Compile every source and link libfa.so (and the probe library)
+    next to this file; returns the path of libfa.so."""
+    os.makedirs(OBJDIR, exist_ok=True)
+    srcs = SOURCES + PROBE_SOURCES
+    with ThreadPoolExecutor(max_workers=min(len(srcs), os.cpu_count() or 4)) as ex:
+        objs = dict(zip(srcs, ex.map(lambda s: _compile(s, verbose), srcs)))
+    _link([objs[s] for s in SOURCES], LIB, verbose)
+    _link([objs[s] for s in PROBE_SOURCES], PROBE_LIB, verbose)
     return LIB
 
 

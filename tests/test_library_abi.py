@@ -343,3 +343,18 @@ def test_noalloc_backward_rejects_before_any_launch(lib):
     assert lib.fa_bwd_noalloc(*args(1, 1, 16, scale=-1.0)) == fa.FA_ERR_UNSUPPORTED
     assert lib.fa_bwd_noalloc(*args(-1, 1, 16)) == fa.FA_ERR_SHAPE
     assert lib.fa_bwd_noalloc(*args(0, 4, 16)) == fa.FA_OK
+
+
+def test_probe_library_exports_and_checks_arguments():
+    """bench.py --probes loads libfa_probe.so; its entry points refuse bad
+    arguments before any launch."""
+    import ctypes
+    path = os.path.join(ROOT, "exact_attention_118_amd", "libfa_probe.so")
+    plib = ctypes.CDLL(path)
+    plib.fa_probe_mfma.argtypes = [ctypes.c_int] * 3 + [ctypes.c_void_p] * 2
+    plib.fa_probe_adds.argtypes = [ctypes.c_int, ctypes.c_void_p] + [ctypes.c_int] * 3 + [ctypes.c_void_p]
+    assert plib.fa_probe_mfma(8, 1, 1, 16, None) != 0      # no such mode
+    assert plib.fa_probe_mfma(0, 0, 1, 16, None) != 0      # no blocks
+    assert plib.fa_probe_mfma(0, 1, 1, None, None) != 0    # no output
+    assert plib.fa_probe_adds(1, None, 1, 1, 1, None) != 0
+    assert plib.fa_probe_adds(1, 16, 0, 1, 1, None) != 0
