@@ -509,9 +509,25 @@ void fwd_kernel(const T* __restrict__ Q, const T* __restrict__ K, const T* __res
       __syncthreads();
     };
 
-    for (int j = jbeg; j < ntiles; j += 2) {
+    // Causal: tiles whose first key lies past the diagonal of this wave's
+    // last row contribute nothing to its rows (with 256-row workgroups the
+    // first waves reach them up to three tiles before the last ones).  The
+    // wave runs the tile steps up to its last useful tile, then only takes
+    // its part in the loads and barriers of the workgroup's remaining tiles.
+    const int jact = (CAUSAL && !BIAS) ? min(ntiles, (wrow_lo + 31 + off) / BC + 1) : ntiles;
+    for (int j = jbeg; j < jact; j += 2) {
       tile_step(0, j, sA, sB);
-      if (j + 1 < ntiles) tile_step(1, j + 1, sB, sA);
+      if (j + 1 < jact) tile_step(1, j + 1, sB, sA);
+    }
+    for (int j = max(jact, jbeg); j < ntiles; ++j) {
+      const int P = (j - jbeg) & 1;
+#pragma unroll
+      for (int di = 0; di < KV::PER; ++di) {
+        kv.template part<KV_AUX>(Kh, (j + 2) * BC, Nk, sK0 + P * TILE, di);
+        kv.template part<KV_AUX>(Vh, (j + 1) * BC, Nk, sV0 + (1 - P) * TILE, di);
+      }
+      vm_wait_all();
+      __syncthreads();
     }
 
     // Epilogue: O = O_acc / lq (times 1 / keep-probability with dropout), lq
