@@ -800,9 +800,23 @@ void bwd_dq_kernel(const T* __restrict__ Q, const T* __restrict__ K, const T* __
       else vm_wait_all();
       __syncthreads();
     };
-    for (int j = jbeg; j < ntiles; j += 2) {
+    // Causal: tiles whose first key lies past the diagonal of this wave's
+    // last row contribute nothing to its rows; after its last useful tile the
+    // wave only takes its part in the loads and barriers of the rest.
+    const int jact = (CAUSAL && !BIAS) ? min(ntiles, (wrow_lo + 31 + off) / BC + 1) : ntiles;
+    for (int j = jbeg; j < jact; j += 2) {
       tile_step(0, j);
-      if (j + 1 < ntiles) tile_step(1, j + 1);
+      if (j + 1 < jact) tile_step(1, j + 1);
+    }
+    for (int j = max(jact, jbeg); j < ntiles; ++j) {
+      const int P = (j - jbeg) & 1;
+#pragma unroll
+      for (int di = 0; di < KV::PER; ++di) {
+        kv.part(Kh, (j + 1) * BC, Nk, sK0 + (1 - P) * TILE, di);
+        kv.part(Vh, (j + 1) * BC, Nk, sV0 + (1 - P) * TILE, di);
+      }
+      vm_wait_all();
+      __syncthreads();
     }
     if constexpr (BIAS) vm_wait_all();  // the last, unused bias loads
 
