@@ -539,9 +539,14 @@ def run_probes(seconds):
     buf = torch.zeros(nrb * 32 * 128, dtype=torch.float32, device="cuda")
     adds = ablocks * aiters * 4096
     for atomic, label in ((0, "fp32 stores, MFMA-tile pattern"), (1, "fp32 atomic adds (device scope)")):
+        buf.zero_()
         timed(label, lambda a=atomic: plib.fa_probe_adds(a, ctypes.c_void_p(buf.data_ptr()), nrb, ablocks,
                                                          aiters, ctypes.c_void_p(stream.cuda_stream)),
               adds / 1e9, "G values/s")
+        if atomic:
+            # every add of 1.0 landed: each element's count stays far below 2^24
+            launches = results[-1]["launches"] + 2
+            results[-1]["sum_exact"] = bool(buf.double().sum().item() == float(launches) * adds)
     sampler.close()
     print(json.dumps({"probes": results, "power_sampling": sampler.note, "seconds_per_probe": seconds}),
           flush=True)
