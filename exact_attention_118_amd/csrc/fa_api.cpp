@@ -111,7 +111,6 @@ SplitWs split_ws(int BH, int d, int splits) {
   return w;
 }
 
-// Backward workspace: D [B*H*Nq] fp32, then L*log2(e) [B*H*Nq] fp32.
 // Backward workspace: the fp32 pairs (L*log2(e), D) of every query row.
 size_t bwd_ws_half(int BH, int Nq) { return round_up((size_t)BH * Nq * sizeof(float), kWsAlign); }
 size_t bwd_ws_bytes(int BH, int Nq) { return 2 * bwd_ws_half(BH, Nq); }
