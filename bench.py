@@ -49,10 +49,12 @@ def unmasked_pairs(Nq, Nk, causal):
 
 KERNEL_SOURCES = {
     "fwd_kernel": "fa_fwd.hip",
+    "bwd_fused_kernel": "fa_bwd.hip",
     "bwd_dkdv_kernel": "fa_bwd.hip",
     "bwd_dq_kernel": "fa_bwd.hip",
     "bwd_pre_kernel": "fa_bwd.hip",
 }
+KERNEL_RE = r"(fwd_kernel|bwd_fused_kernel|bwd_dkdv_kernel|bwd_dq_kernel|bwd_pre_kernel)"
 
 
 def source_sha(path):
@@ -79,8 +81,7 @@ def write_traffic(fetch_csv, write_csv, copy_mib):
         for r in csv.DictReader(open(path)):
             if r["Counter_Name"] != counter:
                 continue
-            m = re.search(r"(fwd_kernel|bwd_dkdv_kernel|bwd_dq_kernel|bwd_pre_kernel)",
-                          r["Kernel_Name"])
+            m = re.search(KERNEL_RE, r["Kernel_Name"])
             name = m.group(1) if m else ("copy" if int(r["Grid_Size"]) == (copy_mib << 20) // 16
                                          else None)
             if name:
@@ -533,6 +534,9 @@ def run_probes(seconds):
     timed("bwd_dq_kernel (6*d flop per pair executed)",
           lambda: fa.fa_bwd(x["Q"], x["K"], x["V"], O, L, x["dO"], *g, w.scale, w.causal, workspace=ws,
                             stages=fa.FA_BWD_DQ), 6 * w.d * pairs / 1e12, "TFLOP/s")
+    timed("bwd_fused_kernel (14*d flop per pair executed)",
+          lambda: fa.fa_bwd(x["Q"], x["K"], x["V"], O, L, x["dO"], *g, w.scale, w.causal, workspace=ws,
+                            stages=fa.FA_BWD_DKDV | fa.FA_BWD_DQ), 14 * w.d * pairs / 1e12, "TFLOP/s")
     del x, O, L, g, ws
 
     nrb, ablocks, aiters = 8192, 2048, 16  # a 128 MiB buffer
@@ -620,21 +624,18 @@ def main():
                   stages=fa.FA_BWD_PREPROCESS)
         if ev is not None:
             ev[2].record()
+        # dK/dV and dQ: one launch (bwd_fused_kernel), as fa_bwd runs them
         fa.fa_bwd(Q, K, V, O, L, dO, dQ, dK, dV, w.scale, w.causal, workspace=ws,
-                  stages=fa.FA_BWD_DKDV)
+                  stages=fa.FA_BWD_DKDV | fa.FA_BWD_DQ)
         if ev is not None:
             ev[3].record()
-        fa.fa_bwd(Q, K, V, O, L, dO, dQ, dK, dV, w.scale, w.causal, workspace=ws,
-                  stages=fa.FA_BWD_DQ)
-        if ev is not None:
-            ev[4].record()
 
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
     log(f"warmup {args.warmup} done")
 
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(5)] for _ in range(args.steps)]
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
     start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     t0 = time.perf_counter()
@@ -650,23 +651,37 @@ def main():
     def mean_ms(a, b):
         return sum(e[a].elapsed_time(e[b]) for e in evs) / len(evs)
 
-    fwd_ms, pre_ms, dkdv_ms, dq_ms = mean_ms(0, 1), mean_ms(1, 2), mean_ms(2, 3), mean_ms(3, 4)
-    bwd_ms = pre_ms + dkdv_ms + dq_ms
+    fwd_ms, pre_ms, main_ms = mean_ms(0, 1), mean_ms(1, 2), mean_ms(2, 3)
+    bwd_ms = pre_ms + main_ms
     pairs = unmasked_pairs(w.Nq, w.Nk, w.causal) * w.B * w.H
     fwd_flops, bwd_flops = 4 * w.d * pairs, 10 * w.d * pairs
     value = (fwd_flops + bwd_flops) / (ms_per_step * 1e-3) / 1e12
 
-    # Algorithmic flops per kernel: the forward's 2 GEMMs; the dK/dV kernel's
-    # S, dP, dV and dK GEMMs (8*d per pair); the dQ kernel's dQ GEMM (2*d per
-    # pair) -- its recomputation of S and dP is overhead, not algorithmic work.
+    # The two kernels of the fused launch, each launched alone (outside the
+    # timed steps): how the backward's time splits between dK/dV and dQ.
+    def alone(stages, reps=5):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        fa.fa_bwd(Q, K, V, O, L, dO, dQ, dK, dV, w.scale, w.causal, workspace=ws, stages=stages)
+        e0.record()
+        for _ in range(reps):
+            fa.fa_bwd(Q, K, V, O, L, dO, dQ, dK, dV, w.scale, w.causal, workspace=ws,
+                      stages=stages)
+        e1.record()
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / reps
+
+    dkdv_ms, dq_ms = alone(fa.FA_BWD_DKDV), alone(fa.FA_BWD_DQ)
+
+    # Algorithmic flops per launch: the forward's 2 GEMMs; the fused backward
+    # launch's S, dP, dV and dK GEMMs of the dK/dV workgroups (8*d per pair)
+    # and the dQ GEMM of the dQ workgroups (2*d per pair) -- their
+    # recomputation of S and dP (4*d per pair) is overhead, not algorithmic.
     csrc = os.path.join(ROOT, "exact_attention_118_amd", "csrc")
     kernels = {
         "fwd_kernel": {"ms": fwd_ms, "flops": fwd_flops,
-                            "source": os.path.join(csrc, "fa_fwd.hip")},
-        "bwd_dkdv_kernel": {"ms": dkdv_ms, "flops": 8 * w.d * pairs,
-                                 "source": os.path.join(csrc, "fa_bwd.hip")},
-        "bwd_dq_kernel": {"ms": dq_ms, "flops": 2 * w.d * pairs,
-                               "source": os.path.join(csrc, "fa_bwd.hip")},
+                       "source": os.path.join(csrc, "fa_fwd.hip")},
+        "bwd_fused_kernel": {"ms": main_ms, "flops": 10 * w.d * pairs,
+                             "source": os.path.join(csrc, "fa_bwd.hip")},
     }
     dom_name = max(kernels, key=lambda k: kernels[k]["ms"])
     dom = kernels[dom_name]
@@ -695,7 +710,9 @@ def main():
                 "mfma_frac": fwd_flops / (fwd_ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS},
         "bwd": {"ms": bwd_ms, "TFLOP/s": bwd_flops / (bwd_ms * 1e-3) / 1e12,
                 "mfma_frac": bwd_flops / (bwd_ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS,
-                "preprocess_ms": pre_ms, "dkdv_ms": dkdv_ms, "dq_ms": dq_ms,
+                "preprocess_ms": pre_ms, "dkdv_dq_ms": main_ms,
+                "alone": {"dkdv_ms": dkdv_ms, "dq_ms": dq_ms,
+                          "dkdv_TFLOP/s": 8 * w.d * pairs / (dkdv_ms * 1e-3) / 1e12},
                 "executed_mfma_frac": 14 * w.d * pairs / (bwd_ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS},
     }
     del dQ, dK, dV

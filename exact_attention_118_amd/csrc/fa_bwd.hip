@@ -51,6 +51,11 @@
 //    balances the causal triangle; the query-block
 //    grid uses the forward pass's mapping, causal query tiles in pairs
 //    (t, nqt-1-t) of equal total work.
+//  * bwd_fused_kernel (no bias): both grids in one launch, the key blocks
+//    first.  The dQ workgroups start on the CUs that the short key blocks
+//    free near the end of the dK/dV grid, and on short sequences, where a
+//    few long key-block chains set the time, the two grids run side by side
+//    (B4 H16 N1024 d64 causal: 63.5 -> 54.6 us for the backward pass).
 #include "fa_common.h"
 #include "fa_launch.h"
 
@@ -105,13 +110,24 @@ struct KvShape {
 };
 constexpr int kKvBR = 32;  // query rows per inner iteration
 
+// LDS of a dK/dV workgroup: [Q buffers 0,1 | dO buffers 0,1 | K block], all
+// swizzled (see swz); the (L*log2 e, D) pairs of the query block per buffer;
+// the bias tiles (BIAS).
+template <typename T, int D, bool BIAS>
+struct DkdvLds {
+  static constexpr int BC = KvShape<BIAS>::kBC, BR = kKvBR;
+  __attribute__((aligned(1024))) T smem[4 * BR * D + BC * D];
+  __attribute__((aligned(16))) float sLD[2][2 * BR];
+  alignas(BIAS ? 1024 : 16) T sBias[BIAS ? 2 * BR * BC : 8];
+};
+
+// Block `bid` of the key-block grid (the kernel's blockIdx.x).
 template <typename T, int D, bool CAUSAL, bool BIAS, bool DROP>
-__global__ __launch_bounds__(KvShape<BIAS>::kThreads, KvShape<BIAS>::kPerCU)
-__attribute__((amdgpu_waves_per_eu(2, 2)))
-void bwd_dkdv_kernel(const T* __restrict__ Q, const T* __restrict__ K, const T* __restrict__ V,
-                     const T* __restrict__ dO, const float* __restrict__ LD, T* __restrict__ dK,
-                     T* __restrict__ dV, int Nq, int Nk, int nkt, int BH, int hpx, float c,
-                     float scale, int off, BiasDev bias, DropDev drop) {
+__device__ __forceinline__ void dkdv_body(
+    const T* __restrict__ Q, const T* __restrict__ K, const T* __restrict__ V,
+    const T* __restrict__ dO, const float* __restrict__ LD, T* __restrict__ dK,
+    T* __restrict__ dV, int Nq, int Nk, int nkt, int BH, int hpx, float c, float scale, int off,
+    BiasDev bias, DropDev drop, DkdvLds<T, D, BIAS>& lds, int bid) {
   typedef typename Vec<T>::x8 T8;
   typedef typename Vec<T>::x4 T4;
   constexpr int kKvWaves = KvShape<BIAS>::kWaves, kKvThreads = KvShape<BIAS>::kThreads;
@@ -127,15 +143,14 @@ void bwd_dkdv_kernel(const T* __restrict__ Q, const T* __restrict__ K, const T* 
   static_assert(2 * BR == 64, "one dword load per lane carries the (L2, D) pairs of a block");
   static_assert(NIQ % IPW == 0, "a wave loads from one tile");
 
-  // [Q buffers 0,1 | dO buffers 0,1 | K block], all swizzled (see swz); the
-  // (L*log2 e, D) pairs of the query block per buffer.  Query block it uses
-  // buffers it & 1; the loop is unrolled by two so that their offsets are
-  // constants.  The query tiles come first: their many reads then carry the
-  // buffer offset in the 16-bit offset field of the LDS instruction, which
-  // offsets past the 64 KB K block would not fit (each read would need an
-  // address add).
-  __shared__ __attribute__((aligned(1024))) T smem[4 * QTILE + KTILE];
-  __shared__ __attribute__((aligned(16))) float sLD[2][2 * BR];
+  // Query block it uses buffers it & 1; the loop is unrolled by two so that
+  // their offsets are constants.  The query tiles come first: their many
+  // reads then carry the buffer offset in the 16-bit offset field of the LDS
+  // instruction, which offsets past the 64 KB K block would not fit (each
+  // read would need an address add).
+  static_assert(sizeof(lds.smem) == (4 * QTILE + KTILE) * sizeof(T), "LDS layout");
+  T* const smem = lds.smem;
+  float (&sLD)[2][2 * BR] = lds.sLD;
   T* const sQ0 = smem;
   T* const sdO0 = smem + 2 * QTILE;
   T* const sK = smem + 4 * QTILE;
@@ -148,12 +163,12 @@ void bwd_dkdv_kernel(const T* __restrict__ Q, const T* __restrict__ K, const T* 
 
   int bh, kt;
   if (hpx > 0) {  // B*H = 8 * hpx: head bh runs on XCD bh % 8
-    const int x = blockIdx.x % kNumXcd, slot = blockIdx.x / kNumXcd;
+    const int x = bid % kNumXcd, slot = bid / kNumXcd;
     bh = x + kNumXcd * (slot % hpx);
     kt = slot / hpx;
   } else {
-    kt = blockIdx.x / BH;
-    bh = blockIdx.x - kt * BH;
+    kt = bid / BH;
+    bh = bid - kt * BH;
   }
   const int k0 = kt * BC;
   const int kw0 = k0 + wave * 32;  // this wave's first key
@@ -172,7 +187,7 @@ void bwd_dkdv_kernel(const T* __restrict__ Q, const T* __restrict__ K, const T* 
   constexpr int NIB = BTILE * 2 / 16 / 64;       // direct-to-LDS loads per bias tile
   constexpr int IPB = NIB / kKvWaves;            // ... per wave
   static_assert(IPB * kKvWaves == NIB, "bias tile load split");
-  __shared__ __attribute__((aligned(1024))) T sBias[BIAS ? 2 * BTILE : 8];
+  T* const sBias = lds.sBias;
   const T* bias_h = nullptr;
   unsigned boff[IPB];
   unsigned bread = 0;  // byte offset of this lane's transposed read of row group 0
@@ -498,18 +513,39 @@ void bwd_dkdv_kernel(const T* __restrict__ Q, const T* __restrict__ K, const T* 
   }
 }
 
+template <typename T, int D, bool CAUSAL, bool BIAS, bool DROP>
+__global__ __launch_bounds__(KvShape<BIAS>::kThreads, KvShape<BIAS>::kPerCU)
+__attribute__((amdgpu_waves_per_eu(2, 2)))
+void bwd_dkdv_kernel(const T* __restrict__ Q, const T* __restrict__ K, const T* __restrict__ V,
+                     const T* __restrict__ dO, const float* __restrict__ LD, T* __restrict__ dK,
+                     T* __restrict__ dV, int Nq, int Nk, int nkt, int BH, int hpx, float c,
+                     float scale, int off, BiasDev bias, DropDev drop) {
+  __shared__ DkdvLds<T, D, BIAS> lds;
+  dkdv_body<T, D, CAUSAL, BIAS, DROP>(Q, K, V, dO, LD, dK, dV, Nq, Nk, nkt, BH, hpx, c, scale,
+                                      off, bias, drop, lds, blockIdx.x);
+}
+
 // ---------------------------------------------------------------------------
 // dQ: one workgroup per (query tile of 128, batch*head), key tiles streamed.
 constexpr int kDqBR = 128;  // query rows per workgroup
 constexpr int kDqBC = 64;   // keys per K/V tile
 constexpr int kDqThreads = 256;
 
+// LDS of a dQ workgroup: K tiles (buffers 0/1), V tiles (buffers 2/3), then
+// the bias staging (BIAS).
+template <typename T, int D, bool BIAS>
+struct DqLds {
+  __attribute__((aligned(1024))) T smem[4 * kDqBC * D + (BIAS ? (kDqThreads / 64) * 32 * kDqBC : 0)];
+};
+
+// Block `bid` of a grid of `nblk` query-tile workgroups.
 template <typename T, int D, bool CAUSAL, bool BIAS, bool DROP>
-__global__ __launch_bounds__(kDqThreads, 2) __attribute__((amdgpu_waves_per_eu(2, 2)))
-void bwd_dq_kernel(const T* __restrict__ Q, const T* __restrict__ K, const T* __restrict__ V,
-                   const T* __restrict__ dO, const float* __restrict__ LD, T* __restrict__ dQ,
-                   int Nq, int Nk, int nqt, float c, float scale, int off, BiasDev bias,
-                   DropDev drop) {
+__device__ __forceinline__ void dq_body(const T* __restrict__ Q, const T* __restrict__ K,
+                                        const T* __restrict__ V, const T* __restrict__ dO,
+                                        const float* __restrict__ LD, T* __restrict__ dQ, int Nq,
+                                        int Nk, int nqt, float c, float scale, int off,
+                                        BiasDev bias, DropDev drop, DqLds<T, D, BIAS>& lds,
+                                        int bid, int nblk) {
   typedef typename Vec<T>::x8 T8;
   typedef typename Vec<T>::x4 T4;
   constexpr int BR = kDqBR, BC = kDqBC;
@@ -524,7 +560,8 @@ void bwd_dq_kernel(const T* __restrict__ Q, const T* __restrict__ K, const T* __
   // of 8 chunks of 16 bytes, chunk c of row r at c ^ ((r / 2) % 8) (reads of
   // one chunk per row take the minimum two LDS passes).
   constexpr int BSTAGE = BIAS ? (kDqThreads / 64) * 32 * BC : 0;
-  __shared__ __attribute__((aligned(1024))) T smem[4 * TILE + BSTAGE];
+  static_assert(sizeof(lds.smem) == (4 * TILE + BSTAGE) * sizeof(T), "LDS layout");
+  T* const smem = lds.smem;
   T* const sK0 = smem;
   T* const sV0 = smem + 2 * TILE;
 
@@ -538,7 +575,7 @@ void bwd_dq_kernel(const T* __restrict__ Q, const T* __restrict__ K, const T* __
   // Causal: one workgroup per pair of query tiles (t, nqt-1-t), taken in
   // turn, so that every workgroup carries the same number of key tiles.
   const int nwg = CAUSAL ? (nqt + 1) / 2 : nqt;  // workgroups per head
-  const int logical = xcd_remap(blockIdx.x, gridDim.x);
+  const int logical = xcd_remap(bid, nblk);
   const int bh = logical / nwg;
   const int t = logical - bh * nwg;
   const size_t qbase = (size_t)bh * Nq * D;
@@ -836,6 +873,43 @@ void bwd_dq_kernel(const T* __restrict__ Q, const T* __restrict__ K, const T* __
   }
 }
 
+template <typename T, int D, bool CAUSAL, bool BIAS, bool DROP>
+__global__ __launch_bounds__(kDqThreads, 2) __attribute__((amdgpu_waves_per_eu(2, 2)))
+void bwd_dq_kernel(const T* __restrict__ Q, const T* __restrict__ K, const T* __restrict__ V,
+                   const T* __restrict__ dO, const float* __restrict__ LD, T* __restrict__ dQ,
+                   int Nq, int Nk, int nqt, float c, float scale, int off, BiasDev bias,
+                   DropDev drop) {
+  __shared__ DqLds<T, D, BIAS> lds;
+  dq_body<T, D, CAUSAL, BIAS, DROP>(Q, K, V, dO, LD, dQ, Nq, Nk, nqt, c, scale, off, bias, drop,
+                                    lds, blockIdx.x, gridDim.x);
+}
+
+// dK/dV and dQ in one launch (no bias: both then run 256-thread workgroups,
+// two per CU): blocks 0 .. nkv-1 are the key-block grid, the rest the
+// query-tile grid, sharing one LDS allocation.  Workgroups start in block
+// order, so the dQ workgroups fill the CUs that the dK/dV grid's short key
+// blocks free near its end, and two dependent launches become one.
+template <typename T, int D, bool CAUSAL, bool DROP>
+__global__ __launch_bounds__(kDqThreads, 2) __attribute__((amdgpu_waves_per_eu(2, 2)))
+void bwd_fused_kernel(const T* __restrict__ Q, const T* __restrict__ K, const T* __restrict__ V,
+                      const T* __restrict__ dO, const float* __restrict__ LD,
+                      T* __restrict__ dQ, T* __restrict__ dK, T* __restrict__ dV, int Nq,
+                      int Nk, int nkt, int BH, int hpx, int nkv, int nqt, float c, float scale,
+                      int off, BiasDev bias, DropDev drop) {
+  static_assert(KvShape<false>::kThreads == kDqThreads, "one workgroup size");
+  __shared__ union {
+    DkdvLds<T, D, false> kv;
+    DqLds<T, D, false> q;
+  } lds;
+  const int b = blockIdx.x;
+  if (b < nkv)
+    dkdv_body<T, D, CAUSAL, false, DROP>(Q, K, V, dO, LD, dK, dV, Nq, Nk, nkt, BH, hpx, c, scale,
+                                         off, bias, drop, lds.kv, b);
+  else
+    dq_body<T, D, CAUSAL, false, DROP>(Q, K, V, dO, LD, dQ, Nq, Nk, nqt, c, scale, off, bias,
+                                       drop, lds.q, b - nkv, (int)gridDim.x - nkv);
+}
+
 // ---------------------------------------------------------------------------
 // fp32 backward (correctness path): one thread per key row for dK/dV, one
 // thread per query row for dQ; plain fp32 FMAs and expf.
@@ -991,6 +1065,27 @@ hipError_t launch_bwd_mfma(const BwdArgs& a, int stages, hipStream_t s) {
   if (stages & 1) {
     const hipError_t e = (a.d == 128) ? launch_pre<128, T>(a, s) : launch_pre<64, T>(a, s);
     if (e != hipSuccess) return e;
+  }
+  if constexpr (!BIAS) {
+    if ((stages & 6) == 6 && a.Nk > 0 && a.Nq > 0) {
+      constexpr int kKvBC = KvShape<false>::kBC;
+      const int nkt = (a.Nk + kKvBC - 1) / kKvBC;
+      const int nkv = nkt * BH;
+      const int hpx = (BH % kNumXcd == 0) ? BH / kNumXcd : 0;
+      const int nqt = (a.Nq + kDqBR - 1) / kDqBR;
+      const int nq = (a.causal ? (nqt + 1) / 2 : nqt) * BH;
+#define FA_FUSED_LAUNCH(DD, CC)                                                                 \
+  hipLaunchKernelGGL((bwd_fused_kernel<T, DD, CC, DROP>), dim3(nkv + nq), dim3(kDqThreads), 0,  \
+                     s, Q, K, V, dO, a.LD, (T*)a.dQ, (T*)a.dK, (T*)a.dV, a.Nq, a.Nk, nkt, BH,  \
+                     hpx, nkv, nqt, c, a.scale, off, bias, drop)
+      if (a.d == 128) {
+        if (a.causal) FA_FUSED_LAUNCH(128, true); else FA_FUSED_LAUNCH(128, false);
+      } else {
+        if (a.causal) FA_FUSED_LAUNCH(64, true); else FA_FUSED_LAUNCH(64, false);
+      }
+#undef FA_FUSED_LAUNCH
+      return hipGetLastError();
+    }
   }
   if ((stages & 2) && a.Nk > 0) {
     constexpr int kKvBC = KvShape<BIAS>::kBC;

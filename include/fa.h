@@ -99,8 +99,9 @@ fa_status fa_fwd(const void* Q, const void* K, const void* V, void* O, float* L,
  *  workspace: fa_bwd_workspace_size() bytes of device memory, 16-byte
  *  aligned, written by the first stage: per query row the fp32 pair
  *  (L*log2(e), D), [B,H,Nq,2].  dK and dV are computed per key block and dQ
- *  per query block by a second kernel that recomputes P and dP, so there are
- *  no atomic operations and every output is deterministic.
+ *  per query block by workgroups that recompute P and dP for their rows, so
+ *  there are no atomic operations and every output is deterministic.  Both
+ *  kinds of workgroup run in one launch after the preprocess launch.
  */
 fa_status fa_bwd(const void* Q, const void* K, const void* V, const void* O, const float* L,
                  const void* dO, void* dQ, void* dK, void* dV,
@@ -108,14 +109,15 @@ fa_status fa_bwd(const void* Q, const void* K, const void* V, const void* O, con
                  fa_dtype dtype, void* workspace, size_t workspace_bytes, void* stream);
 
 /*
- * The backward pass as its three launches, for callers that schedule or time
- * them separately.  Same arguments as fa_bwd plus `stages`, a bit mask:
+ * The backward pass in stages, for callers that schedule or time them
+ * separately.  Same arguments as fa_bwd plus `stages`, a bit mask:
  *   FA_BWD_PREPROCESS (1): the (L*log2(e), D = rowsum(dO * O)) pairs into the workspace;
  *   FA_BWD_DKDV       (2): dK and dV written (reads the workspace);
  *   FA_BWD_DQ         (4): dQ written (reads the workspace).
  * fa_bwd(...) is fa_bwd_stages(..., FA_BWD_ALL).  Stages 2 and 4 need stage 1
  * to have run on the same workspace; a mask of 0 or above 7 returns
- * FA_ERR_UNSUPPORTED.
+ * FA_ERR_UNSUPPORTED.  Stages 2 and 4 in one mask run as one launch (as two
+ * with a bias); the results are the same bit for bit either way.
  */
 enum { FA_BWD_PREPROCESS = 1, FA_BWD_DKDV = 2, FA_BWD_DQ = 4, FA_BWD_ALL = 7 };
 fa_status fa_bwd_stages(const void* Q, const void* K, const void* V, const void* O,

@@ -417,6 +417,32 @@ def test_forward_and_backward_are_deterministic(gpu_lib):
     assert torch.equal(a[2], b[2]) and torch.equal(a[3], b[3]) and torch.equal(a[4], b[4])
 
 
+@pytest.mark.parametrize("case", [(2, 3, 257, 257, 64, True, torch.bfloat16),
+                                  (1, 2, 600, 700, 128, True, torch.bfloat16),
+                                  (2, 1, 129, 77, 128, False, torch.bfloat16),
+                                  (1, 3, 300, 1000, 64, True, torch.float16),
+                                  (8, 8, 512, 512, 128, True, torch.bfloat16)],
+                         ids=lambda c: f"b{c[0]}h{c[1]}q{c[2]}k{c[3]}d{c[4]}{'c' if c[5] else ''}")
+def test_fused_backward_launch_matches_separate_launches(gpu_lib, case):
+    """fa_bwd runs the dK/dV and dQ workgroups as one launch; the stage mask
+    can run them as two.  Both compute every output with the same code, so the
+    results agree bit for bit."""
+    fa = gpu_lib
+    B, H, Nq, Nk, d, causal, dt = case
+    x = make(B, H, Nq, Nk, d, dt, seed=11)
+    O, L = fa.forward(x["Q"], x["K"], x["V"], d ** -0.5, causal)
+    dQ, dK, dV = fa.backward(x["Q"], x["K"], x["V"], O, L, x["dO"], d ** -0.5, causal)
+    sep = [torch.full_like(t, float("nan")) for t in (dQ, dK, dV)]
+    ws = torch.empty(fa.bwd_workspace_size(B, H, Nq, Nk, d, fa.FA_BF16 if dt == torch.bfloat16 else fa.FA_FP16),
+                     dtype=torch.uint8, device="cuda")
+    for stages in (fa.FA_BWD_PREPROCESS, fa.FA_BWD_DKDV, fa.FA_BWD_DQ):
+        fa.fa_bwd(x["Q"], x["K"], x["V"], O, L, x["dO"], *sep, d ** -0.5, causal, workspace=ws,
+                  stages=stages)
+    torch.cuda.synchronize()
+    for name, a, b in zip(("dQ", "dK", "dV"), (dQ, dK, dV), sep):
+        assert torch.equal(a.view(torch.int16), b.view(torch.int16)), name
+
+
 def test_no_query_rows_gives_zero_key_gradients(gpu_lib):
     fa = gpu_lib
     K = torch.randn(1, 2, 50, 64, device="cuda").bfloat16()
