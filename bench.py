@@ -401,9 +401,9 @@ class PowerSampler:
     thread; windows of samples are attributed to the probe running then.  Does
     nothing (and reports None) where amdsmi or its device is unavailable."""
 
-    def __init__(self, period_s=0.004):
+    def __init__(self, period_s=0.004, start=True):
         import threading
-        self.samples, self.ok, self.note = [], False, None
+        self.samples, self.ok, self.note, self.period_s = [], False, None, period_s
         try:
             import amdsmi
             amdsmi.amdsmi_init()
@@ -425,8 +425,14 @@ class PowerSampler:
         except Exception as e:  # no amdsmi, no device access
             self.note = f"amdsmi unavailable: {type(e).__name__}: {e}"
         self.stop = threading.Event()
-        if self.ok:
-            self.thread = threading.Thread(target=self._run, args=(period_s,), daemon=True)
+        self.thread = None
+        if start:
+            self.start()
+
+    def start(self):
+        import threading
+        if self.ok and self.thread is None:
+            self.thread = threading.Thread(target=self._run, args=(self.period_s,), daemon=True)
             self.thread.start()
 
     def _read(self):
@@ -506,6 +512,13 @@ def run_probes(seconds):
     blocks, iters = 256, 512
     out = torch.empty(blocks * 512, dtype=torch.float32, device="cuda")
     mfma_flops = blocks * 8 * iters * 32 * 32768.0
+    # one second of the first probe, untimed: amdsmi's power average lags, and
+    # the chip starts from idle
+    ts = time.perf_counter()
+    while time.perf_counter() - ts < 1.0:
+        plib.fa_probe_mfma(0, blocks, iters, ctypes.c_void_p(out.data_ptr()),
+                           ctypes.c_void_p(stream.cuda_stream))
+        torch.cuda.synchronize()
     for mode, label in ((0, "MFMA, constant operands"), (1, "MFMA, random operands"),
                         (3, "random MFMA + 1 KB LDS reads per MFMA"),
                         (5, "random MFMA + 1 exp + 4 FMA per MFMA"),
@@ -630,6 +643,7 @@ def main():
         if ev is not None:
             ev[3].record()
 
+    sampler = PowerSampler(start=False)  # amdsmi set up now; it samples after the timed steps
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
@@ -644,8 +658,27 @@ def main():
         step(evs[k])
     end.record()
     torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
+    t1 = time.perf_counter()
+    wall = t1 - t0
     ms_per_step = start.elapsed_time(end) / args.steps
+
+    # Board power and GFX clock (amdsmi) while the same step repeats for about
+    # 2.5 s after the timed steps: amdsmi's readings trail the chip by up to a
+    # second, far longer than the timed steps last, so only the last 60% of
+    # that window counts.  Gives the fraction of the peak at the clock the
+    # chip actually ran.
+    clock = {"note": sampler.note}
+    if sampler.ok:
+        sampler.start()
+        reps = max(1, int(2.5e3 / ms_per_step))
+        c0 = time.perf_counter()
+        for _ in range(reps):
+            step()
+        torch.cuda.synchronize()
+        c1 = time.perf_counter()
+        clock = sampler.window(c0 + 0.4 * (c1 - c0), c1)
+        clock["window_s"] = 0.6 * (c1 - c0)
+    sampler.close()
     log(f"timed {args.steps} steps: {ms_per_step:.3f} ms/step (wall {wall * 1e3 / args.steps:.3f})")
 
     def mean_ms(a, b):
@@ -689,6 +722,10 @@ def main():
     roofline = {"bound": "mfma", "achieved": achieved, "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
                 "frac": achieved / PEAK_BF16_TFLOPS, "traffic": measured_traffic(dom_name, dom["source"]),
                 "kernel": dom_name, "kernel_ms": dom["ms"]}
+    mhz = clock.get("gfx_clock_MHz")
+    if mhz:
+        # the same peak scaled to the mean GFX clock amdsmi reported over the timed steps
+        roofline["frac_at_measured_clock"] = achieved / (PEAK_BF16_TFLOPS * mhz / 2400.0)
 
     out = {
         "metric": METRIC,
@@ -706,6 +743,7 @@ def main():
         "config": {"workload": w.name, "B": w.B, "H": w.H, "N": w.Nq, "d": w.d,
                    "causal": w.causal, "qk_mult": w.qk_mult, "pass": "fwd+bwd"},
         "roofline": roofline,
+        "clock": clock,
         "fwd": {"ms": fwd_ms, "TFLOP/s": fwd_flops / (fwd_ms * 1e-3) / 1e12,
                 "mfma_frac": fwd_flops / (fwd_ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS},
         "bwd": {"ms": bwd_ms, "TFLOP/s": bwd_flops / (bwd_ms * 1e-3) / 1e12,
