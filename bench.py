@@ -521,6 +521,7 @@ def run_probes(seconds):
         torch.cuda.synchronize()
     for mode, label in ((0, "MFMA, constant operands"), (1, "MFMA, random operands"),
                         (3, "random MFMA + 1 KB LDS reads per MFMA"),
+                        (11, "random MFMA + 1 KB transposed LDS reads per MFMA"),
                         (5, "random MFMA + 1 exp + 4 FMA per MFMA"),
                         (7, "random MFMA + LDS reads + exp/FMA")):
         timed(label, lambda m=mode: plib.fa_probe_mfma(m, blocks, iters, ctypes.c_void_p(out.data_ptr()),

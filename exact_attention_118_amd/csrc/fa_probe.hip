@@ -15,6 +15,7 @@
 namespace {
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef short i16x4 __attribute__((ext_vector_type(4)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
 
@@ -37,13 +38,30 @@ __device__ __forceinline__ bf16x8 operand(unsigned seed) {
   return __builtin_bit_cast(bf16x8, u);
 }
 
+// A operand as the attention kernels read a transposed fragment: two
+// ds_read_b64_tr_b16 (8 bytes per lane each), lane l supplying row l/4 (and
+// row l/4 + 4 for the second) and 8-byte column group l%4 of a tile with
+// 288-byte rows (a 32-byte pad per 256-byte row spreads the four rows of a
+// 16-lane group over distinct banks).  `base` is a byte offset into the tile.
+__device__ __forceinline__ bf16x8 tr_pair(const __attribute__((address_space(3))) char* tile,
+                                          unsigned base) {
+  const unsigned l = threadIdx.x & 63;
+  const unsigned o = base + (l >> 2) * 288 + (l & 3) * 8;
+  const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+      (__attribute__((address_space(3))) i16x4*)(tile + o));
+  const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+      (__attribute__((address_space(3))) i16x4*)(tile + o + 4 * 288));
+  return __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+}
+
 // 8 waves per workgroup, one workgroup per CU (two waves per SIMD).  Per loop
 // step a wave issues 32 MFMAs (v_mfma_f32_32x32x16_bf16 into four
 // accumulators) with A operands cycling through 8 registers (LDS = false) or
-// read from LDS just before (LDS = true: one 16-byte read per lane, 1 KB per
-// wave, four steps ahead), B from 8 registers; VALU adds one v_exp_f32 and
-// four v_fma_f32 on independent registers after each MFMA.
-template <bool RANDOM, bool LDS, bool VALU>
+// read from LDS just before (LDS = true: 1 KB per wave, four steps ahead: one
+// 16-byte read per lane, or with TR two 8-byte transposed reads per lane),
+// B from 8 registers; VALU adds one v_exp_f32 and four v_fma_f32 on
+// independent registers after each MFMA.
+template <bool RANDOM, bool LDS, bool VALU, bool TR>
 __global__ __launch_bounds__(512, 1) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void mfma_probe(float* out, int iters) {
   __shared__ bf16x8 tile[4096];  // 64 KB
@@ -69,16 +87,18 @@ void mfma_probe(float* out, int iters) {
   }
   for (int it = 0; it < iters; ++it) {
     bf16x8 ring[4];
+    const __attribute__((address_space(3))) char* tl =
+        (const __attribute__((address_space(3))) char*)tile;
     if (LDS) {
 #pragma unroll
-      for (int m = 0; m < 4; ++m) ring[m] = tile[off[m]];
+      for (int m = 0; m < 4; ++m) ring[m] = TR ? tr_pair(tl, m * 8192u) : tile[off[m]];
     }
 #pragma unroll
     for (int m = 0; m < 32; ++m) {
       bf16x8 x = a[m & 7];
       if (LDS) {
         x = ring[m & 3];
-        ring[m & 3] = tile[off[(m + 4) & 7]];
+        ring[m & 3] = TR ? tr_pair(tl, ((m + 4) & 7) * 8192u) : tile[off[(m + 4) & 7]];
       }
       acc[m & 3] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(x, b[(m * 3) & 7], acc[m & 3], 0, 0, 0);
       if (VALU) {
@@ -130,19 +150,23 @@ __global__ __launch_bounds__(256) void add_probe(float* buf, int nrb, int iters)
 extern "C" {
 
 // mode bit 0: random operands; bit 1: 1 KB of LDS reads per MFMA; bit 2: one
-// exponential and four FMAs per MFMA.  `out` holds blocks * 512 floats.  Each
+// exponential and four FMAs per MFMA; bit 3 (with bit 1): the LDS reads as
+// pairs of 8-byte transposed reads.  `out` holds blocks * 512 floats.  Each
 // launch issues blocks * 8 * iters * 32 MFMAs of 32768 flop.
 int fa_probe_mfma(int mode, int blocks, int iters, float* out, void* stream) {
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
-  if (blocks <= 0 || iters <= 0 || !out || mode < 0 || mode > 7) return (int)hipErrorInvalidValue;
+  const bool tr_ok = (mode & 8) == 0 || (mode & 2) != 0;  // transposed reads need LDS reads
+  if (blocks <= 0 || iters <= 0 || !out || mode < 0 || mode > 15 || !tr_ok)
+    return (int)hipErrorInvalidValue;
 #define FA_PROBE_CASE(M)                                                                        \
   case M:                                                                                       \
-    hipLaunchKernelGGL((mfma_probe<(M & 1) != 0, (M & 2) != 0, (M & 4) != 0>), dim3(blocks),     \
-                       dim3(512), 0, s, out, iters);                                            \
+    hipLaunchKernelGGL((mfma_probe<(M & 1) != 0, (M & 2) != 0, (M & 4) != 0, (M & 8) != 0>),      \
+                       dim3(blocks), dim3(512), 0, s, out, iters);                              \
     break;
   switch (mode) {
     FA_PROBE_CASE(0) FA_PROBE_CASE(1) FA_PROBE_CASE(2) FA_PROBE_CASE(3)
     FA_PROBE_CASE(4) FA_PROBE_CASE(5) FA_PROBE_CASE(6) FA_PROBE_CASE(7)
+    FA_PROBE_CASE(10) FA_PROBE_CASE(11) FA_PROBE_CASE(14) FA_PROBE_CASE(15)
   }
 #undef FA_PROBE_CASE
   return (int)hipGetLastError();

@@ -353,7 +353,8 @@ def test_probe_library_exports_and_checks_arguments():
     plib = ctypes.CDLL(path)
     plib.fa_probe_mfma.argtypes = [ctypes.c_int] * 3 + [ctypes.c_void_p] * 2
     plib.fa_probe_adds.argtypes = [ctypes.c_int, ctypes.c_void_p] + [ctypes.c_int] * 3 + [ctypes.c_void_p]
-    assert plib.fa_probe_mfma(8, 1, 1, 16, None) != 0      # no such mode
+    assert plib.fa_probe_mfma(8, 1, 1, 16, None) != 0      # transposed reads without LDS reads
+    assert plib.fa_probe_mfma(16, 1, 1, 16, None) != 0     # no such mode
     assert plib.fa_probe_mfma(0, 0, 1, 16, None) != 0      # no blocks
     assert plib.fa_probe_mfma(0, 1, 1, None, None) != 0    # no output
     assert plib.fa_probe_adds(1, None, 1, 1, 1, None) != 0
