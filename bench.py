@@ -523,7 +523,11 @@ def run_probes(seconds):
                         (3, "random MFMA + 1 KB LDS reads per MFMA"),
                         (11, "random MFMA + 1 KB transposed LDS reads per MFMA"),
                         (5, "random MFMA + 1 exp + 4 FMA per MFMA"),
-                        (7, "random MFMA + LDS reads + exp/FMA")):
+                        (7, "random MFMA + LDS reads + exp/FMA"),
+                        (39, "random MFMA + 0.5 KB LDS reads + exp/FMA"),
+                        (17, "one wave per SIMD: random MFMA"),
+                        (23, "one wave per SIMD: random MFMA + LDS reads + exp/FMA"),
+                        (55, "one wave per SIMD: random MFMA + 0.5 KB LDS reads + exp/FMA")):
         timed(label, lambda m=mode: plib.fa_probe_mfma(m, blocks, iters, ctypes.c_void_p(out.data_ptr()),
                                                        ctypes.c_void_p(stream.cuda_stream)),
               mfma_flops / 1e12, "TFLOP/s")

@@ -54,18 +54,22 @@ __device__ __forceinline__ bf16x8 tr_pair(const __attribute__((address_space(3))
   return __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
 }
 
-// 8 waves per workgroup, one workgroup per CU (two waves per SIMD).  Per loop
-// step a wave issues 32 MFMAs (v_mfma_f32_32x32x16_bf16 into four
-// accumulators) with A operands cycling through 8 registers (LDS = false) or
-// read from LDS just before (LDS = true: 1 KB per wave, four steps ahead: one
-// 16-byte read per lane, or with TR two 8-byte transposed reads per lane),
-// B from 8 registers; VALU adds one v_exp_f32 and four v_fma_f32 on
-// independent registers after each MFMA.
-template <bool RANDOM, bool LDS, bool VALU, bool TR>
-__global__ __launch_bounds__(512, 1) __attribute__((amdgpu_waves_per_eu(2, 2)))
+// 8 waves per workgroup, one workgroup per CU (two waves per SIMD); with ONE,
+// 4 waves and 96 KB of LDS per workgroup, so that one fits a CU (one wave per
+// SIMD, up to 512 registers each).  Per loop step a wave issues 32 MFMAs
+// (v_mfma_f32_32x32x16_bf16 into four accumulators) with A operands cycling
+// through 8 registers (LDS = false) or read from LDS just before (LDS = true:
+// 1 KB per wave, four steps ahead: one 16-byte read per lane, or with TR two
+// 8-byte transposed reads per lane; with HALF only every other MFMA's A comes
+// from LDS, 0.5 KB per MFMA), B from 8 registers; VALU adds one v_exp_f32 and
+// four v_fma_f32 on independent registers after each MFMA.
+template <bool RANDOM, bool LDS, bool VALU, bool TR, bool ONE, bool HALF>
+__global__ __launch_bounds__(ONE ? 256 : 512, 1)
+__attribute__((amdgpu_waves_per_eu(ONE ? 1 : 2, ONE ? 1 : 2)))
 void mfma_probe(float* out, int iters) {
-  __shared__ bf16x8 tile[4096];  // 64 KB
-  for (int i = threadIdx.x; i < 4096; i += 512) tile[i] = operand<RANDOM>(i * 977u + blockIdx.x);
+  constexpr int kTile = ONE ? 6144 : 4096;  // 96 or 64 KB
+  __shared__ bf16x8 tile[kTile];
+  for (int i = threadIdx.x; i < kTile; i += blockDim.x) tile[i] = operand<RANDOM>(i * 977u + blockIdx.x);
   __syncthreads();
   bf16x8 a[8], b[8];
 #pragma unroll
@@ -75,7 +79,7 @@ void mfma_probe(float* out, int iters) {
   }
   unsigned off[8];  // per-lane LDS element offsets, fixed for the kernel
 #pragma unroll
-  for (int k = 0; k < 8; ++k) off[k] = (threadIdx.x + 512u * k) & 4095u;
+  for (int k = 0; k < 8; ++k) off[k] = (threadIdx.x + 512u * k) & 4095u;  // in every tile size
   f32x16 acc[4];
 #pragma unroll
   for (int k = 0; k < 4; ++k) acc[k] = (f32x16){};
@@ -96,9 +100,10 @@ void mfma_probe(float* out, int iters) {
 #pragma unroll
     for (int m = 0; m < 32; ++m) {
       bf16x8 x = a[m & 7];
-      if (LDS) {
-        x = ring[m & 3];
-        ring[m & 3] = TR ? tr_pair(tl, ((m + 4) & 7) * 8192u) : tile[off[(m + 4) & 7]];
+      if (LDS && (!HALF || (m & 1) == 0)) {
+        const int r = HALF ? (m >> 1) : m;
+        x = ring[r & 3];
+        ring[r & 3] = TR ? tr_pair(tl, ((r + 4) & 7) * 8192u) : tile[off[(r + 4) & 7]];
       }
       acc[m & 3] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(x, b[(m * 3) & 7], acc[m & 3], 0, 0, 0);
       if (VALU) {
@@ -151,22 +156,27 @@ extern "C" {
 
 // mode bit 0: random operands; bit 1: 1 KB of LDS reads per MFMA; bit 2: one
 // exponential and four FMAs per MFMA; bit 3 (with bit 1): the LDS reads as
-// pairs of 8-byte transposed reads.  `out` holds blocks * 512 floats.  Each
-// launch issues blocks * 8 * iters * 32 MFMAs of 32768 flop.
+// pairs of 8-byte transposed reads; bit 4: one wave per SIMD (2 * blocks
+// workgroups of 4 waves, one per CU at a time); bit 5 (with bit 1): LDS reads
+// for every other MFMA only (0.5 KB per MFMA).  `out` holds blocks * 512
+// floats.  Each launch issues blocks * 8 * iters * 32 MFMAs of 32768 flop.
 int fa_probe_mfma(int mode, int blocks, int iters, float* out, void* stream) {
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
-  const bool tr_ok = (mode & 8) == 0 || (mode & 2) != 0;  // transposed reads need LDS reads
-  if (blocks <= 0 || iters <= 0 || !out || mode < 0 || mode > 15 || !tr_ok)
-    return (int)hipErrorInvalidValue;
+  if (blocks <= 0 || iters <= 0 || !out) return (int)hipErrorInvalidValue;
 #define FA_PROBE_CASE(M)                                                                        \
   case M:                                                                                       \
-    hipLaunchKernelGGL((mfma_probe<(M & 1) != 0, (M & 2) != 0, (M & 4) != 0, (M & 8) != 0>),      \
-                       dim3(blocks), dim3(512), 0, s, out, iters);                              \
+    hipLaunchKernelGGL((mfma_probe<(M & 1) != 0, (M & 2) != 0, (M & 4) != 0, (M & 8) != 0,       \
+                                   (M & 16) != 0, (M & 32) != 0>),                              \
+                       dim3((M & 16) ? 2 * blocks : blocks), dim3((M & 16) ? 256 : 512), 0, s,  \
+                       out, iters);                                                             \
     break;
   switch (mode) {
     FA_PROBE_CASE(0) FA_PROBE_CASE(1) FA_PROBE_CASE(2) FA_PROBE_CASE(3)
     FA_PROBE_CASE(4) FA_PROBE_CASE(5) FA_PROBE_CASE(6) FA_PROBE_CASE(7)
     FA_PROBE_CASE(10) FA_PROBE_CASE(11) FA_PROBE_CASE(14) FA_PROBE_CASE(15)
+    FA_PROBE_CASE(17) FA_PROBE_CASE(23) FA_PROBE_CASE(39) FA_PROBE_CASE(55)
+    default:
+      return (int)hipErrorInvalidValue;  // combinations not built
   }
 #undef FA_PROBE_CASE
   return (int)hipGetLastError();
