@@ -156,6 +156,21 @@ def cpu_baseline(w, x, heads):
                       f"(float64 numpy, {dt:.1f} s)", "seconds": dt}
 
 
+SETTLE_S = 0.3  # seconds of untimed repetitions before each measurement
+
+
+def settle(torch, fn, seconds=SETTLE_S):
+    """Run fn repeatedly for about `seconds` before a measurement: after a
+    pause the GPU needs a few hundred milliseconds of load before its clock
+    and power settle (a forward timed after 3 warm-up steps ran 4-5% slower
+    than after 100 on the long-sequence workload), and a training loop keeps
+    it under load."""
+    t0 = time.perf_counter()
+    while time.perf_counter() - t0 < seconds:
+        fn()
+        torch.cuda.synchronize()
+
+
 def bench_decode(fa, torch, steps):
     from exact_attention_118_amd import synth
 
@@ -166,9 +181,7 @@ def bench_decode(fa, torch, steps):
     splits = fa.fwd_num_splits(w.B, w.H, 1, w.Nk, w.d, fa.FA_BF16, 0)
     ws = torch.empty(fa.fwd_workspace_size(w.B, w.H, 1, w.Nk, w.d, fa.FA_BF16, 0),
                      dtype=torch.uint8, device="cuda")
-    for _ in range(2):
-        fa.fa_fwd(x["Q"], x["K"], x["V"], O, L, w.scale, False, workspace=ws)
-    torch.cuda.synchronize()
+    settle(torch, lambda: fa.fa_fwd(x["Q"], x["K"], x["V"], O, L, w.scale, False, workspace=ws))
     ev = [torch.cuda.Event(enable_timing=True) for _ in range(steps + 1)]
     ev[0].record()
     for i in range(steps):
@@ -181,8 +194,7 @@ def bench_decode(fa, torch, steps):
     # What the HBM delivers to a plain device copy of the same K (2 GiB read,
     # 2 GiB written) in this run: a reference rate for the split path.
     buf = torch.empty_like(x["K"])
-    buf.copy_(x["K"])
-    torch.cuda.synchronize()
+    settle(torch, lambda: buf.copy_(x["K"]))
     ev[0].record()
     for i in range(steps):
         buf.copy_(x["K"])
@@ -214,9 +226,8 @@ def bench_rows_split(fa, torch, steps):
         nsplit = fa.fwd_num_splits(w.B, w.H, w.Nq, w.Nk, w.d, fa.FA_BF16, ns)
         nb = fa.fwd_workspace_size(w.B, w.H, w.Nq, w.Nk, w.d, fa.FA_BF16, ns)
         ws = torch.empty(nb, dtype=torch.uint8, device="cuda") if nb else None
-        for _ in range(2):
-            fa.fa_fwd(x["Q"], x["K"], x["V"], O, L, w.scale, True, num_splits=ns, workspace=ws)
-        torch.cuda.synchronize()
+        settle(torch, lambda: fa.fa_fwd(x["Q"], x["K"], x["V"], O, L, w.scale, True, num_splits=ns,
+                                        workspace=ws))
         ev = [torch.cuda.Event(enable_timing=True) for _ in range(steps + 1)]
         ev[0].record()
         for i in range(steps):
@@ -254,8 +265,7 @@ def _time_fwd_bwd(fa, torch, w, Q, K, V, dO, ws, steps, bias=None, dropout_p=0.0
         else:
             fa.fa_bwd_bias(Q, K, V, bias, O, L, dO, dQ, dK, dV, w.scale, w.causal, workspace=ws)
 
-    run()
-    torch.cuda.synchronize()
+    settle(torch, run)
     ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(steps)]
     for e in ev:
         e[0].record()
@@ -276,11 +286,12 @@ def bench_fp16(fa, torch, w, x, ws, steps):
     return _time_fwd_bwd(fa, torch, w, Q, K, V, dO, ws, steps)
 
 
-def _time_fwd_bwd_graph(fa, torch, w, Q, K, V, dO, ws, reps):
+def _time_fwd_bwd_graph(fa, torch, w, Q, K, V, dO, ws, reps, replays=20):
     """Mean forward and backward milliseconds of fa_fwd + fa_bwd, each captured
-    `reps` times into a HIP graph and replayed, so that host-side launch
-    latency does not count: a kernel of a few microseconds would otherwise wait
-    for the host between launches."""
+    `reps` times into a HIP graph and replayed (`replays` times back to back,
+    after settling), so that host-side launch latency does not count: a
+    kernel of a few microseconds would otherwise wait for the host between
+    launches."""
     O = torch.empty_like(Q)
     L = torch.empty(w.B, w.H, w.Nq, dtype=torch.float32, device="cuda")
     dQ, dK, dV = torch.empty_like(Q), torch.empty_like(K), torch.empty_like(V)
@@ -307,20 +318,20 @@ def _time_fwd_bwd_graph(fa, torch, w, Q, K, V, dO, ws, reps):
         graphs.append(g)
     ms = []
     for g in graphs:
-        g.replay()
-        torch.cuda.synchronize()
+        settle(torch, g.replay)
         e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         e0.record()
-        g.replay()
+        for _ in range(replays):
+            g.replay()
         e1.record()
         torch.cuda.synchronize()
-        ms.append(e0.elapsed_time(e1) / reps)
+        ms.append(e0.elapsed_time(e1) / (reps * replays))
     del graphs
     pairs = unmasked_pairs(w.Nq, w.Nk, w.causal) * w.B * w.H
     return {"fwd_ms": ms[0], "bwd_ms": ms[1],
             "fwd_TFLOP/s": 4 * w.d * pairs / (ms[0] * 1e-3) / 1e12,
             "bwd_TFLOP/s": 10 * w.d * pairs / (ms[1] * 1e-3) / 1e12,
-            "timing": f"HIP graph of {reps} calls, replayed"}
+            "timing": f"HIP graph of {reps} calls, replayed {replays} times after {SETTLE_S} s of replays"}
 
 
 def bench_other_configs(fa, torch, steps):
@@ -578,7 +589,7 @@ def main():
     ap = argparse.ArgumentParser(description=__doc__)
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
-    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--warmup", type=int, default=50)
     ap.add_argument("--workload", default="b1h32n8192d128_causal")
     ap.add_argument("--cpu-heads", type=int, default=16,
                     help="heads of the workload the float64 oracle is timed on (0 = skip)")
