@@ -885,8 +885,10 @@ void bwd_dq_kernel(const T* __restrict__ Q, const T* __restrict__ K, const T* __
 }
 
 // dK/dV and dQ in one launch (no bias: both then run 256-thread workgroups,
-// two per CU): blocks 0 .. nkv-1 are the key-block grid, the rest the
-// query-tile grid, sharing one LDS allocation.  Workgroups start in block
+// two per CU): blocks 0 .. nkv-1 are the key-block grid, blocks from nkv
+// rounded up to a multiple of 8 on the query-tile grid (so that its XCD
+// remap sees block b on XCD b % 8; the few blocks between return at once),
+// sharing one LDS allocation.  Workgroups start in block
 // order, so the dQ workgroups fill the CUs that the dK/dV grid's short key
 // blocks free near its end, and two dependent launches become one.
 template <typename T, int D, bool CAUSAL, bool DROP>
@@ -894,7 +896,8 @@ __global__ __launch_bounds__(kDqThreads, 2) __attribute__((amdgpu_waves_per_eu(2
 void bwd_fused_kernel(const T* __restrict__ Q, const T* __restrict__ K, const T* __restrict__ V,
                       const T* __restrict__ dO, const float* __restrict__ LD,
                       T* __restrict__ dQ, T* __restrict__ dK, T* __restrict__ dV, int Nq,
-                      int Nk, int nkt, int BH, int hpx, int nkv, int nqt, float c, float scale,
+                      int Nk, int nkt, int BH, int hpx, int nkv, int nq0, int nqt, float c,
+                      float scale,
                       int off, BiasDev bias, DropDev drop) {
   static_assert(KvShape<false>::kThreads == kDqThreads, "one workgroup size");
   __shared__ union {
@@ -905,9 +908,9 @@ void bwd_fused_kernel(const T* __restrict__ Q, const T* __restrict__ K, const T*
   if (b < nkv)
     dkdv_body<T, D, CAUSAL, false, DROP>(Q, K, V, dO, LD, dK, dV, Nq, Nk, nkt, BH, hpx, c, scale,
                                          off, bias, drop, lds.kv, b);
-  else
+  else if (b >= nq0)
     dq_body<T, D, CAUSAL, false, DROP>(Q, K, V, dO, LD, dQ, Nq, Nk, nqt, c, scale, off, bias,
-                                       drop, lds.q, b - nkv, (int)gridDim.x - nkv);
+                                       drop, lds.q, b - nq0, (int)gridDim.x - nq0);
 }
 
 // ---------------------------------------------------------------------------
@@ -1071,13 +1074,14 @@ hipError_t launch_bwd_mfma(const BwdArgs& a, int stages, hipStream_t s) {
       constexpr int kKvBC = KvShape<false>::kBC;
       const int nkt = (a.Nk + kKvBC - 1) / kKvBC;
       const int nkv = nkt * BH;
+      const int nq0 = (nkv + kNumXcd - 1) / kNumXcd * kNumXcd;  // first dQ block
       const int hpx = (BH % kNumXcd == 0) ? BH / kNumXcd : 0;
       const int nqt = (a.Nq + kDqBR - 1) / kDqBR;
       const int nq = (a.causal ? (nqt + 1) / 2 : nqt) * BH;
 #define FA_FUSED_LAUNCH(DD, CC)                                                                 \
-  hipLaunchKernelGGL((bwd_fused_kernel<T, DD, CC, DROP>), dim3(nkv + nq), dim3(kDqThreads), 0,  \
+  hipLaunchKernelGGL((bwd_fused_kernel<T, DD, CC, DROP>), dim3(nq0 + nq), dim3(kDqThreads), 0,  \
                      s, Q, K, V, dO, a.LD, (T*)a.dQ, (T*)a.dK, (T*)a.dV, a.Nq, a.Nk, nkt, BH,  \
-                     hpx, nkv, nqt, c, a.scale, off, bias, drop)
+                     hpx, nkv, nq0, nqt, c, a.scale, off, bias, drop)
       if (a.d == 128) {
         if (a.causal) FA_FUSED_LAUNCH(128, true); else FA_FUSED_LAUNCH(128, false);
       } else {
