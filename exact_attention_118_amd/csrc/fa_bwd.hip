@@ -885,19 +885,23 @@ void bwd_dq_kernel(const T* __restrict__ Q, const T* __restrict__ K, const T* __
 }
 
 // dK/dV and dQ in one launch (no bias: both then run 256-thread workgroups,
-// two per CU): blocks 0 .. nkv-1 are the key-block grid, blocks from nkv
-// rounded up to a multiple of 8 on the query-tile grid (so that its XCD
-// remap sees block b on XCD b % 8; the few blocks between return at once),
-// sharing one LDS allocation.  Workgroups start in block
-// order, so the dQ workgroups fill the CUs that the dK/dV grid's short key
-// blocks free near its end, and two dependent launches become one.
+// two per CU), sharing one LDS allocation.  Workgroups start in block order,
+// and both grids already list their workgroups longest first, so the launch
+// merges them by expected length: blocks 0 .. n1-1 are the first key blocks
+// (those longer than a dQ workgroup), the next nqpad blocks the query-tile
+// grid (nq workgroups; the few blocks past it return at once), the rest the
+// remaining key blocks.  n1 and nqpad are multiples of 8, so that each grid's
+// XCD mapping still sees block b on XCD b % 8.  The dQ workgroups thus fill
+// CUs as the long key blocks finish and the short key blocks come last: on
+// short sequences, where a few long chains set the time, the two grids run
+// side by side, and two dependent launches become one.
 template <typename T, int D, bool CAUSAL, bool DROP>
 __global__ __launch_bounds__(kDqThreads, 2) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void bwd_fused_kernel(const T* __restrict__ Q, const T* __restrict__ K, const T* __restrict__ V,
                       const T* __restrict__ dO, const float* __restrict__ LD,
                       T* __restrict__ dQ, T* __restrict__ dK, T* __restrict__ dV, int Nq,
-                      int Nk, int nkt, int BH, int hpx, int nkv, int nq0, int nqt, float c,
-                      float scale,
+                      int Nk, int nkt, int BH, int hpx, int n1, int nqpad, int nq, int nqt,
+                      float c, float scale,
                       int off, BiasDev bias, DropDev drop) {
   static_assert(KvShape<false>::kThreads == kDqThreads, "one workgroup size");
   __shared__ union {
@@ -905,12 +909,13 @@ void bwd_fused_kernel(const T* __restrict__ Q, const T* __restrict__ K, const T*
     DqLds<T, D, false> q;
   } lds;
   const int b = blockIdx.x;
-  if (b < nkv)
+  if (b < n1 || b >= n1 + nqpad) {
     dkdv_body<T, D, CAUSAL, false, DROP>(Q, K, V, dO, LD, dK, dV, Nq, Nk, nkt, BH, hpx, c, scale,
-                                         off, bias, drop, lds.kv, b);
-  else if (b >= nq0)
+                                         off, bias, drop, lds.kv, b < n1 ? b : b - nqpad);
+  } else if (b - n1 < nq) {
     dq_body<T, D, CAUSAL, false, DROP>(Q, K, V, dO, LD, dQ, Nq, Nk, nqt, c, scale, off, bias,
-                                       drop, lds.q, b - nq0, (int)gridDim.x - nq0);
+                                       drop, lds.q, b - n1, nq);
+  }
 }
 
 // ---------------------------------------------------------------------------
@@ -1054,6 +1059,29 @@ DropDev drop_dev(const DropArgs& d) {
   return DropDev{d.seed_lo, d.seed_hi, d.offset, d.on ? d.thresh : 256u, d.on ? d.inv_keep : 1.f};
 }
 
+// Key blocks that go before the dQ workgroups in the fused launch: those whose
+// chain of 32-row query blocks is longer than a dQ workgroup's key tiles, in
+// units of a dK/dV query block.  A dK/dV wave spends 32 MFMAs (d = 128; 16 at
+// d = 64) and 16 exponentials on a query block, a dQ wave 48 (24) and 32 on a
+// 64-key tile: about 1.5x at d = 128, where the MFMAs dominate, and 1.07x at
+// d = 64 (measured per step on one head).  Without a causal mask every key
+// block is longer than every dQ workgroup.
+int fused_split(const BwdArgs& a, int nkt, int nqt, int kv_bc) {
+  if (!a.causal) return nkt;
+  const int off = a.Nk - a.Nq;
+  const double r = (a.d == 128) ? 1.5 : 1.07;
+  auto tiles = [&](int t) {  // 64-key tiles of 128-row query tile t
+    return (std::min(a.Nk, (t + 1) * kDqBR + off) + kDqBC - 1) / kDqBC;
+  };
+  const double dq_len = r * (tiles(0) + (nqt > 1 ? tiles(nqt - 1) : 0));
+  const int nqb = (a.Nq + kKvBR - 1) / kKvBR;
+  for (int kt = 0; kt < nkt; ++kt) {
+    const int first = std::max(0, kt * kv_bc - off) / kKvBR;
+    if (nqb - first < dq_len) return kt;
+  }
+  return nkt;
+}
+
 template <typename T, bool BIAS, bool DROP>
 hipError_t launch_bwd_mfma(const BwdArgs& a, int stages, hipStream_t s) {
   const int BH = a.B * a.H;
@@ -1074,14 +1102,15 @@ hipError_t launch_bwd_mfma(const BwdArgs& a, int stages, hipStream_t s) {
       constexpr int kKvBC = KvShape<false>::kBC;
       const int nkt = (a.Nk + kKvBC - 1) / kKvBC;
       const int nkv = nkt * BH;
-      const int nq0 = (nkv + kNumXcd - 1) / kNumXcd * kNumXcd;  // first dQ block
       const int hpx = (BH % kNumXcd == 0) ? BH / kNumXcd : 0;
       const int nqt = (a.Nq + kDqBR - 1) / kDqBR;
       const int nq = (a.causal ? (nqt + 1) / 2 : nqt) * BH;
+      const int nqpad = (nq + kNumXcd - 1) / kNumXcd * kNumXcd;
+      const int n1 = fused_split(a, nkt, nqt, kKvBC) * BH / kNumXcd * kNumXcd;
 #define FA_FUSED_LAUNCH(DD, CC)                                                                 \
-  hipLaunchKernelGGL((bwd_fused_kernel<T, DD, CC, DROP>), dim3(nq0 + nq), dim3(kDqThreads), 0,  \
+  hipLaunchKernelGGL((bwd_fused_kernel<T, DD, CC, DROP>), dim3(nkv + nqpad), dim3(kDqThreads), 0,\
                      s, Q, K, V, dO, a.LD, (T*)a.dQ, (T*)a.dK, (T*)a.dV, a.Nq, a.Nk, nkt, BH,  \
-                     hpx, nkv, nq0, nqt, c, a.scale, off, bias, drop)
+                     hpx, n1, nqpad, nq, nqt, c, a.scale, off, bias, drop)
       if (a.d == 128) {
         if (a.causal) FA_FUSED_LAUNCH(128, true); else FA_FUSED_LAUNCH(128, false);
       } else {
