@@ -51,11 +51,12 @@
 //    balances the causal triangle; the query-block
 //    grid uses the forward pass's mapping, causal query tiles in pairs
 //    (t, nqt-1-t) of equal total work.
-//  * bwd_fused_kernel (no bias): both grids in one launch, the key blocks
-//    first.  The dQ workgroups start on the CUs that the short key blocks
-//    free near the end of the dK/dV grid, and on short sequences, where a
-//    few long key-block chains set the time, the two grids run side by side
-//    (B4 H16 N1024 d64 causal: 63.5 -> 54.6 us for the backward pass).
+//  * bwd_fused_kernel (no bias): both grids in one launch, merged by expected
+//    workgroup length (long key blocks, then the dQ workgroups, then the short
+//    key blocks), so that the dQ workgroups fill the CUs the long key blocks
+//    leave, and on short sequences, where a few long key-block chains set the
+//    time, the two grids run side by side (B4 H16 N1024 d64 causal:
+//    63.5 -> 52.4 us for the backward pass).
 #include "fa_common.h"
 #include "fa_launch.h"
 
