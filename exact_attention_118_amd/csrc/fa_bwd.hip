@@ -787,9 +787,16 @@ __device__ __forceinline__ void dq_body(const T* __restrict__ Q, const T* __rest
               kv.part(Vh, k0 + BC, Nk, sV0 + (1 - P) * TILE, di - KV::PER);
           }
           if (overlap) {
-#pragma unroll
-            for (int h = 0; h < 16 / (2 * NKK); ++h) ds_elem(mt - 1, st * (16 / (2 * NKK)) + h);
-            pin(dsf[(mt - 1) * 2 + (st * (16 / (2 * NKK))) / 8]);
+            // the 16 dS elements of half mt - 1 in pairs, so that each pair
+            // takes one packed conversion: a pair per step (D = 64) or per
+            // two steps (D = 128)
+            constexpr int SPP = (2 * NKK) / 8;
+            if ((st + 1) % SPP == 0) {
+              const int i = (st / SPP) * 2;
+              ds_elem(mt - 1, i);
+              ds_elem(mt - 1, i + 1);
+              pin(dsf[(mt - 1) * 2 + i / 8]);
+            }
           }
           __builtin_amdgcn_sched_barrier(0);
         }
