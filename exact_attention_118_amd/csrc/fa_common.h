@@ -48,6 +48,17 @@ __device__ __forceinline__ f32x16 mfma32(f16x8 a, f16x8 b, f32x16 c) {
   return __builtin_amdgcn_mfma_f32_32x32x16_f16(a, b, c, 0, 0, 0);
 }
 
+// 16x16x32 bf16 / fp16 MFMA, fp32 accumulate.  Operand layout (lane l of 64):
+//   A[m][k]: m = l % 16, k = (l / 16) * 8 + e      (e = vector element 0..7)
+//   B[k][n]: n = l % 16, k = (l / 16) * 8 + e
+//   C[m][n]: n = l % 16, m = (l / 16) * 4 + i      (i = 0..3)
+__device__ __forceinline__ f32x4 mfma16(bf16x8 a, bf16x8 b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+__device__ __forceinline__ f32x4 mfma16(f16x8 a, f16x8 b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, 0, 0, 0);
+}
+
 // LDS transposed read of 16-bit data.  Within each group of 16 lanes, lane s
 // supplies the address of 4 consecutive elements; lane r receives element
 // (r % 4) of the rows supplied by lanes r/4, r/4 + 4, r/4 + 8, r/4 + 12.

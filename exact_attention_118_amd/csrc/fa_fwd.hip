@@ -152,6 +152,26 @@ void fwd_kernel(const T* __restrict__ Q, const T* __restrict__ K, const T* __res
   // query tile from the L2, where non-temporal loads cost 7%.
   constexpr int KV_AUX = SPLIT ? kLoadNonTemporal : 0;
 
+  // The sums of the rounded probabilities that normalise O (see lq_run),
+  // without dropout formed on the matrix cores: one 16x16x32 MFMA per
+  // 16-key chunk of P, P as the B operand (lane l: row l % 32, one half of
+  // the chunk's keys) and as the A operand ones in rows 0 and 8 of k-blocks
+  // 0 and 2 and in rows 4 and 12 of k-blocks 1 and 3.  Element 0 of every
+  // lane's result is then the chunk's sum for the lane's own row, both
+  // halves included, in place of 16 v_dot2c per tile.  With a bias, whose
+  // kernels are short of registers, the operand is made per tile instead of
+  // being kept.
+  auto make_asel = [](int ln) {
+    const int m16 = ln & 15, kb = ln >> 4;
+    const bool one = (m16 & 3) == 0 && ((m16 >> 2) & 1) == (kb & 1);
+    T8 a;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) a[j] = one ? (T)1.f : (T)0.f;
+    return a;
+  };
+  [[maybe_unused]] T8 asel_kept;
+  if constexpr (!BIAS) asel_kept = make_asel(lane);
+
   // Byte offsets, within a tile, of this lane's LDS operand reads; the row
   // block and the buffer are added as instruction offsets.  S^T = K Q^T: the
   // A fragment of step st is K row (st&1)*32 + l32, 16-byte chunk
@@ -180,7 +200,8 @@ void fwd_kernel(const T* __restrict__ Q, const T* __restrict__ K, const T* __res
     return concat(lds_read_tr<T>(to_lds(at_byte<T>(base, va[st % NNT] + rb))),
                   lds_read_tr<T>(to_lds(at_byte<T>(base, va[NNT + st % NNT] + rb))));
   };
-  constexpr int KRING = 4, VRING = 3;
+  // LDS fragments read ahead of their MFMAs (shallower with a bias, for registers)
+  constexpr int KRING = BIAS ? 3 : 4, VRING = BIAS ? 2 : 3;
 
   for (int pass = 0; pass < (PAIRED ? 2 : 1); ++pass) {
     const int qt = !PAIRED ? t : (pass == 0 ? nqt - 1 - t : t);
@@ -228,7 +249,10 @@ void fwd_kernel(const T* __restrict__ Q, const T* __restrict__ K, const T* __res
     // running sum of the same probabilities as rounded to T for P V: O is
     // normalised by it, so a dominant probability's rounding cancels between
     // numerator and denominator (fp32 l would leave up to 2^-9 of it in O)
-    float lq_run = 0.f;
+    // (kept here with dropout, whose sums are taken before the mask; without
+    // dropout element 0 of lacc holds it, from the matrix cores)
+    [[maybe_unused]] float lq_run = 0.f;
+    f32x4 lacc = (f32x4){};
     f32x16 oacc[NNT];
 #pragma unroll
     for (int nt = 0; nt < NNT; ++nt) oacc[nt] = (f32x16){};
@@ -299,9 +323,9 @@ void fwd_kernel(const T* __restrict__ Q, const T* __restrict__ K, const T* __res
       for (int q = q0b; q < q0b + 4; ++q)
         bb[q] = *at_byte<BT4>(sBw, rowb + (((unsigned)q ^ x) << 4));
     };
-    auto bias_add = [&](f32x16 (&sc)[2], const BT4 (&bb)[8]) {
+    auto bias_add = [&](f32x16 (&sc)[2], const BT4 (&bb)[8], int q0b) {
 #pragma unroll
-      for (int q = 0; q < 8; ++q)
+      for (int q = q0b; q < q0b + 4; ++q)
 #pragma unroll
         for (int e = 0; e < 4; ++e)
           sc[q >> 2][(q & 3) * 4 + e] = fmaf((float)bb[q][e], bias.inv_scale, sc[q >> 2][(q & 3) * 4 + e]);
@@ -328,8 +352,9 @@ void fwd_kernel(const T* __restrict__ Q, const T* __restrict__ K, const T* __res
       BT4 bb[8];
       vm_wait_all();
       bias_fetch(bb, 0);
+      bias_add(sA, bb, 0);
       bias_fetch(bb, 4);
-      bias_add(sA, bb);
+      bias_add(sA, bb, 4);
     }
     mask_tile(sA, kfirst);
     m_run = row_max(sA) * c;  // the reference starts at tile 0's row max
@@ -358,6 +383,7 @@ void fwd_kernel(const T* __restrict__ Q, const T* __restrict__ K, const T* __res
         const float alpha = fast_exp2(m_run - (m_new == -INFINITY ? 0.f : m_new));
         l_run *= alpha;
         lq_run *= alpha;
+        lacc *= alpha;
         part0 *= alpha;
         part1 *= alpha;
         partq *= alpha;
@@ -379,7 +405,8 @@ void fwd_kernel(const T* __restrict__ Q, const T* __restrict__ K, const T* __res
       // row sums of this lane's probabilities: rs[0..1] the early pairs,
       // rs[2..3] the late ones (two accumulators each)
       float rs[4] = {0.f, 0.f, 0.f, 0.f};
-      // the same sums over the rounded probabilities: rq[0] early, rq[1] late
+      // with dropout, the same sums over the rounded probabilities: rq[0]
+      // early, rq[1] late
       float rq[2] = {0.f, 0.f};
       // Dropout (DROP): the random bytes of this lane's scores of tile j,
       // keys k0 + mt*32 + ... in rb[mt], each made just before its pairs (the
@@ -399,11 +426,14 @@ void fwd_kernel(const T* __restrict__ Q, const T* __restrict__ K, const T* __res
         float& ra = rs[pr < kPairsA ? 0 : 2];
         float& rb_ = rs[pr < kPairsA ? 1 : 3];
         float& rq_ = rq[pr < kPairsA ? 0 : 1];
-        ra += p0;
-        rb_ += p1;
+        // the first pair of each group starts its sums (0 + p = p exactly for
+        // p >= 0), without an add into a zeroed register
+        const bool first = (pr == 0 || pr == kPairsA);
+        ra = first ? p0 : ra + p0;
+        rb_ = first ? p1 : rb_ + p1;
         pf[kc][e] = (T)p0;
         pf[kc][e + 1] = (T)p1;
-        rq_ = add_pair(pf[kc][e], pf[kc][e + 1], rq_);
+        if constexpr (DROP) rq_ = add_pair(pf[kc][e], pf[kc][e + 1], first ? 0.f : rq_);
         if constexpr (DROP) {
           if (!drop_keep(rb[mt][i >> 2], i & 3, drop.thresh)) pf[kc][e] = (T)0.f;
           if (!drop_keep(rb[mt][i >> 2], (i + 1) & 3, drop.thresh)) pf[kc][e + 1] = (T)0.f;
@@ -411,7 +441,7 @@ void fwd_kernel(const T* __restrict__ Q, const T* __restrict__ K, const T* __res
         pin(pf[kc]);
         pin(ra);
         pin(rb_);
-        pin(rq_);
+        if constexpr (DROP) pin(rq_);
       };
 
       // Scores of tile j+1 on the MFMA pipe, interleaved step by step with
@@ -464,8 +494,10 @@ void fwd_kernel(const T* __restrict__ Q, const T* __restrict__ K, const T* __res
         asm volatile("s_waitcnt vmcnt(%0)" ::"n"(NKK) : "memory");
         BT4 bnext[8];
         bias_fetch(bnext, 0);
+        bias_add(snext, bnext, 0);
+        __builtin_amdgcn_sched_barrier(0);  // half the bias registers live at a time
         bias_fetch(bnext, 4);
-        bias_add(snext, bnext);
+        bias_add(snext, bnext, 4);
       }
       mask_tile(snext, k0 + BC);
       if constexpr (DROP && kPairsA <= 8)
@@ -479,6 +511,14 @@ void fwd_kernel(const T* __restrict__ Q, const T* __restrict__ K, const T* __res
         // the other the exponentials of its score block (about 2% faster
         // than equal priorities, measured on the long-sequence forward).
         __builtin_amdgcn_s_setprio(1);
+        T8 asel;
+        if constexpr (BIAS) {
+          int ln = lane;
+          pin(ln);  // made here, not kept across the tiles
+          asel = make_asel(ln);
+        } else {
+          asel = asel_kept;
+        }
         T8 ring[VRING];
 #pragma unroll
         for (int st = 0; st < VRING; ++st) ring[st] = vfrag(P, st);
@@ -498,13 +538,16 @@ void fwd_kernel(const T* __restrict__ Q, const T* __restrict__ K, const T* __res
           const T8 a = ring[st % VRING];
           if (st + VRING < 4 * NNT) ring[st % VRING] = vfrag(P, st + VRING);
           oacc[st % NNT] = mfma32(a, pf[st / NNT], oacc[st % NNT]);
+          if constexpr (!DROP) {
+            if (st % NNT == 0) lacc = mfma16(asel, pf[st / NNT], lacc);
+          }
           if (kPairsA + st < NPAIR) prob_pair(kPairsA + st);
           __builtin_amdgcn_sched_barrier(0);
         }
       }
       __builtin_amdgcn_s_setprio(0);
       l_run += (rs[0] + rs[1]) + (rs[2] + rs[3]);
-      lq_run += rq[0] + rq[1];
+      if constexpr (DROP) lq_run += rq[0] + rq[1];
       vm_wait_all();  // this wave's part of tiles K j+2 and V j+1 has landed
       __syncthreads();
     };
@@ -534,7 +577,7 @@ void fwd_kernel(const T* __restrict__ Q, const T* __restrict__ K, const T* __res
     // the sum of the rounded probabilities; L = (m + log2 l) * ln 2 with the
     // fp32 sum l.
     const float l_tot = xor32_sum(l_run);
-    const float lq_tot = xor32_sum(lq_run);
+    const float lq_tot = DROP ? xor32_sum(lq_run) : lacc[0];
     if constexpr (SPLIT) {
       if (qrow < Nq) {
         const size_t prow = (size_t)sp * split.rows + (size_t)bh * Nq + qrow;
