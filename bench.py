@@ -2,7 +2,7 @@
 """Throughput of the fused attention path on one MI355X.
 
 One step = the whole hot path on one batch: forward (fa_fwd) then backward
-(fa_bwd: the (L*log2 e, D) preprocess, the dK/dV kernel, the dQ kernel) on
+(fa_bwd: the (L*log2 e, -D) preprocess, the dK/dV kernel, the dQ kernel) on
 the long-sequence workload B=1, H=32, N=8192, d=128, causal, bf16 (Q and K
 scaled by 3).  Inputs are synthetic (seeded normal draws on the GPU) and
 resident in HBM before timing starts.  Prints ONE JSON line on stdout;

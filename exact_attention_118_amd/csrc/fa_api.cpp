@@ -111,12 +111,14 @@ SplitWs split_ws(int BH, int d, int splits) {
   return w;
 }
 
-// Backward workspace: the fp32 pairs (L*log2(e), D) of every query row.
-size_t bwd_ws_half(int BH, int Nq) { return round_up((size_t)BH * Nq * sizeof(float), kWsAlign); }
-size_t bwd_ws_bytes(int BH, int Nq) { return 2 * bwd_ws_half(BH, Nq); }
+// Backward workspace: per head and block of 32 query rows, the rows' fp32
+// L*log2(e) and then their -D (rows past Nq zero).
+size_t bwd_ws_bytes(int BH, int Nq) {
+  return round_up((size_t)BH * ((Nq + 31) / 32) * 64 * sizeof(float), kWsAlign);
+}
 
-// Scratch of fa_bwd_noalloc: the per-row (L*log2(e), D) pairs that fa_bwd
-// keeps in the caller's workspace.  One copy per GPU, held until the process
+// Scratch of fa_bwd_noalloc: the per-row L*log2(e) and -D that fa_bwd keeps
+// in the caller's workspace (8 bytes per query row, rows padded to 32 per head).  One copy per GPU, held until the process
 // ends; every call on a GPU shares it.  In host code `scratch` names a
 // host-side stand-in, never the device memory: the kernels get the device
 // address that hipGetSymbolAddress returns for the current device.

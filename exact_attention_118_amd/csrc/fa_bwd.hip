@@ -69,31 +69,50 @@ BiasDev bias_dev(const BiasArgs& b, int B, int H, float scale) {
 }
 
 
-// D_i = sum_k dO_ik O_ik in fp32, and L2_i = L_i * log2(e) (the exponent
-// base of the kernels below), stored as the pair LD[i] = (L2_i, D_i) so that
-// one load brings both.
-template <int D, typename T>
+// The backward workspace LD holds, per head and block of kLdRows query
+// rows (64 floats), the rows' L2 = L * log2(e) (the exponent base of the
+// kernels below) and -D, D = sum_k dO_ik O_ik in fp32; rows past Nq hold
+// zeros.  Without dropout the block is [L2 x 32 | -D x 32]: one 16-byte read
+// of -D fills four elements of a dP accumulator, which dK/dV then starts
+// from -D instead of zero (dS = P (dP - D)).  With dropout, whose dP is
+// masked and scaled before -D is added, the rows are interleaved,
+// (L2_r, -D_r) for r = 0..31, so that one 16-byte read brings both values of
+// two rows.  ld_index gives a row's L2; its -D is ld_nd_off floats on.
+constexpr int kLdRows = 32;
+template <bool DROP>
+__host__ __device__ __forceinline__ size_t ld_index(int bh, int row, int nblk) {
+  const int r = row % kLdRows;
+  return ((size_t)bh * nblk + row / kLdRows) * (2 * kLdRows) + (DROP ? 2 * r : r);
+}
+template <bool DROP>
+constexpr int ld_nd_off() { return DROP ? 1 : kLdRows; }
+
+template <int D, typename T, bool DROP>
 __global__ __launch_bounds__(256) void bwd_pre_kernel(const T* __restrict__ O,
                                                       const T* __restrict__ dO,
                                                       const float* __restrict__ L,
-                                                      float* __restrict__ LD, long rows) {
+                                                      float* __restrict__ LD, int BH, int Nq,
+                                                      int nblk) {
   constexpr int TPR = D / 8;  // threads per row, 8 elements each
   constexpr int RPB = 256 / TPR;
-  const long row = (long)blockIdx.x * RPB + threadIdx.x / TPR;
+  const long rpad = (long)nblk * kLdRows;  // rows per head, padded
+  const long prow = (long)blockIdx.x * RPB + threadIdx.x / TPR;
+  const int bh = (int)(prow / rpad);
+  const int r = (int)(prow - bh * rpad);
+  const bool valid = bh < BH && r < Nq;
   const int part = threadIdx.x % TPR;
   float acc = 0.f;
-  if (row < rows) {
-    const size_t base = (size_t)row * D + part * 8;
+  if (valid) {
+    const size_t base = ((size_t)bh * Nq + r) * D + part * 8;
 #pragma unroll
     for (int e = 0; e < 8; ++e) acc = fmaf((float)O[base + e], (float)dO[base + e], acc);
   }
 #pragma unroll
   for (int msk = TPR / 2; msk >= 1; msk >>= 1) acc += __shfl_xor(acc, msk, 64);
-  if (row < rows && part == 0) {
-    float2 v;
-    v.x = L[row] * kLog2e;
-    v.y = acc;
-    *(float2*)(LD + 2 * row) = v;
+  if (bh < BH && part == 0) {
+    const size_t i = ld_index<DROP>(bh, r, nblk);
+    LD[i] = valid ? L[(size_t)bh * Nq + r] * kLog2e : 0.f;
+    LD[i + ld_nd_off<DROP>()] = valid ? -acc : 0.f;
   }
 }
 
@@ -112,7 +131,7 @@ struct KvShape {
 constexpr int kKvBR = 32;  // query rows per inner iteration
 
 // LDS of a dK/dV workgroup: [Q buffers 0,1 | dO buffers 0,1 | K block], all
-// swizzled (see swz); the (L*log2 e, D) pairs of the query block per buffer;
+// swizzled (see swz); the (L2, -D) block of the query block per buffer;
 // the bias tiles (BIAS).
 template <typename T, int D, bool BIAS>
 struct DkdvLds {
@@ -141,7 +160,7 @@ __device__ __forceinline__ void dkdv_body(
   constexpr int NIQ = BR * CPR / 64;           // direct-to-LDS loads per Q (or dO) tile
   constexpr int IPW = 2 * NIQ / kKvWaves;      // ... per wave for both tiles
   static_assert(IPW * kKvWaves == 2 * NIQ && IPW >= 1, "query tile load split");
-  static_assert(2 * BR == 64, "one dword load per lane carries the (L2, D) pairs of a block");
+  static_assert(2 * BR == 64, "one dword load per lane carries the (L2, -D) block");
   static_assert(NIQ % IPW == 0, "a wave loads from one tile");
 
   // Query block it uses buffers it & 1; the loop is unrolled by two so that
@@ -176,7 +195,8 @@ __device__ __forceinline__ void dkdv_body(
   const int mykey = kw0 + l32;     // the key of this lane's accumulator column
   const size_t qbase = (size_t)bh * Nq * D;
   const size_t kbase = (size_t)bh * Nk * D;
-  const size_t lbase = (size_t)bh * Nq;
+  const int nqb_ld = (Nq + BR - 1) / BR;  // blocks per head of the (L2, -D) workspace
+  static_assert(BR == kLdRows, "one (L2, -D) block per query block");
 
   // Additive bias (BIAS) of this head, staged per query block: a tile of
   // BR rows x BC keys per buffer, double-buffered like Q and dO and filled by
@@ -236,7 +256,7 @@ __device__ __forceinline__ void dkdv_body(
 
   // Direct-to-LDS loads of query block qb through buffer resources: this
   // wave's IPW chunks of the Q (waves 0 .. 8/2-1) or dO tile, and (last
-  // wave) the 32 (L2, D) pairs; rows past Nq read as zeros.  Lane offsets
+  // wave) the (L2, -D) block; rows past Nq read as zeros.  Lane offsets
   // are fixed; the rest is wave-uniform.
   const int tsel = (wave * IPW) / NIQ;  // 0: Q, 1: dO
   const T* const qsrc = (tsel ? dO : Q) + qbase;
@@ -258,7 +278,7 @@ __device__ __forceinline__ void dkdv_body(
       __builtin_amdgcn_raw_ptr_buffer_load_lds(
           rq, (FA_LDS void*)(qdst0 + buf * QTILE + u * 64 * 8), 16, qoff[u], 0, 0, 0);
     if (wave == kKvWaves - 1) {
-      const __amdgpu_buffer_rsrc_t rl = make_rsrc(LD + 2 * (lbase + qi0), rows * 8);
+      const __amdgpu_buffer_rsrc_t rl = make_rsrc(LD + ld_index<DROP>(bh, qi0, nqb_ld), 2 * BR * 4);
       __builtin_amdgcn_raw_ptr_buffer_load_lds(rl, (FA_LDS void*)&sLD[buf][0], 4, lane * 4, 0,
                                                0, 0);
     }
@@ -345,7 +365,20 @@ __device__ __forceinline__ void dkdv_body(
       // S = Q K^T and dP = dO V^T: 32 rows x this wave's 32 keys.  Step kk
       // needs the Q, K and dO fragments of head-dim chunk kk; those of step
       // kk + 1 are read before step kk's MFMAs are issued.
-      f32x16 sacc = (f32x16){}, dpacc = (f32x16){};
+      // dP starts from -D of its row (element i: row (i/4)*8 + half*4 + i%4),
+      // so that dS = P (dP - D) needs no subtraction; with dropout, whose dP
+      // is masked and scaled first, from zero.
+      f32x16 sacc = (f32x16){}, dpacc;
+      if constexpr (DROP) {
+        dpacc = (f32x16){};
+      } else {
+#pragma unroll
+        for (int gq = 0; gq < 4; ++gq) {
+          const f32x4 nd = *(const f32x4*)(tLD + kLdRows + gq * 8 + half * 4);
+#pragma unroll
+          for (int e = 0; e < 4; ++e) dpacc[gq * 4 + e] = nd[e];
+        }
+      }
       // Bias of rows qi0 + 8g + half*4 + 0..3, key mykey, from the staged
       // tile (rows past Nq read zeros, keys past Nk are masked below), read
       // before the MFMAs.
@@ -402,13 +435,20 @@ __device__ __forceinline__ void dkdv_body(
       // before dS = P (dP - D).
       unsigned rbk[4];
       if constexpr (DROP) drop_bytes_keys(rbk, drop, bh, mykey, qi0 + half * 4, lane);
+      // (with dropout pds_p returns -D of the two rows, read with their L2)
       auto pds_p = [&](int i) {
-        const int ql = (i >> 2) * 8 + half * 4 + (i & 3);  // rows ql, ql + 1
-        const float2 a = *(const float2*)(tLD + 2 * ql);
-        const float2 b = *(const float2*)(tLD + 2 * ql + 2);
-        pp[0] = fast_exp2(fmaf(sacc[i], c, -a.x));
-        pp[1] = fast_exp2(fmaf(sacc[i + 1], c, -b.x));
-        return make_float2(a.y, b.y);
+        const int ql = (i >> 2) * 8 + half * 4 + (i & 3);  // rows ql, ql + 1 (ql even)
+        float2 l2, nd = make_float2(0.f, 0.f);
+        if constexpr (DROP) {
+          const f32x4 v = *(const f32x4*)(tLD + 2 * ql);  // (L2, -D) of both rows
+          l2 = make_float2(v[0], v[2]);
+          nd = make_float2(v[1], v[3]);
+        } else {
+          l2 = *(const float2*)(tLD + ql);
+        }
+        pp[0] = fast_exp2(fmaf(sacc[i], c, -l2.x));
+        pp[1] = fast_exp2(fmaf(sacc[i + 1], c, -l2.y));
+        return nd;
       };
       auto pds_ds = [&](int i, float2 dd) {
         const int kc = i >> 3, e = i & 7;
@@ -417,13 +457,13 @@ __device__ __forceinline__ void dkdv_body(
           const bool k1 = drop_keep(rbk[i >> 2], (i + 1) & 3, drop.thresh);
           pf[kc][e] = (T)(k0 ? pp[0] : 0.f);
           pf[kc][e + 1] = (T)(k1 ? pp[1] : 0.f);
-          dsf[kc][e] = (T)(pp[0] * ((k0 ? dpacc[i] * drop.inv_keep : 0.f) - dd.x));
-          dsf[kc][e + 1] = (T)(pp[1] * ((k1 ? dpacc[i + 1] * drop.inv_keep : 0.f) - dd.y));
+          dsf[kc][e] = (T)(pp[0] * ((k0 ? dpacc[i] * drop.inv_keep : 0.f) + dd.x));
+          dsf[kc][e + 1] = (T)(pp[1] * ((k1 ? dpacc[i + 1] * drop.inv_keep : 0.f) + dd.y));
         } else {
           pf[kc][e] = (T)pp[0];
           pf[kc][e + 1] = (T)pp[1];
-          dsf[kc][e] = (T)(pp[0] * (dpacc[i] - dd.x));
-          dsf[kc][e + 1] = (T)(pp[1] * (dpacc[i + 1] - dd.y));
+          dsf[kc][e] = (T)(pp[0] * dpacc[i]);  // dpacc = dP - D
+          dsf[kc][e + 1] = (T)(pp[1] * dpacc[i + 1]);
         }
       };
       // dV^T += dO^T P and dK^T += Q^T dS over the 16 rows of chunk kc
@@ -646,8 +686,10 @@ __device__ __forceinline__ void dq_body(const T* __restrict__ Q, const T* __rest
       qf[kk] = (qrow < Nq) ? *(const T8*)(Q + o) : zero8<T8>();
       dof[kk] = (qrow < Nq) ? *(const T8*)(dO + o) : zero8<T8>();
     }
-    const float l2 = (qrow < Nq) ? LD[2 * ((size_t)bh * Nq + qrow)] : INFINITY;
-    const float drow = (qrow < Nq) ? LD[2 * ((size_t)bh * Nq + qrow) + 1] : 0.f;
+    const int nqb_ld = (Nq + kLdRows - 1) / kLdRows;
+    const size_t li = ld_index<DROP>(bh, qrow, nqb_ld);
+    const float l2 = (qrow < Nq) ? LD[li] : INFINITY;
+    const float ndrow = (qrow < Nq) ? LD[li + ld_nd_off<DROP>()] : 0.f;  // -D
 
     const int kend = CAUSAL ? min(Nk, q0 + BR + off) : Nk;
     int ntiles = (kend + BC - 1) / BC;
@@ -748,7 +790,7 @@ __device__ __forceinline__ void dq_body(const T* __restrict__ Q, const T* __rest
         float dp = dpacc[mt][i];
         if constexpr (DROP)
           dp = drop_keep(rb[mt][i >> 2], i & 3, drop.thresh) ? dp * drop.inv_keep : 0.f;
-        dsf[mt * 2 + (i >> 3)][i & 7] = (T)(p * (dp - drow));
+        dsf[mt * 2 + (i >> 3)][i & 7] = (T)(p * (dp + ndrow));
       };
       // Keys past the end and, causal, keys after the row's diagonal get
       // score -inf, hence P = 0 and dS = 0; only tiles that cross the
@@ -978,7 +1020,8 @@ __global__ __launch_bounds__(kF32BT) void bwd_dkdv_f32_kernel(
     const bool kept = !DROP || drop_byte(drop, bh, q, key) < drop.thresh;
     const float pd = kept ? (DROP ? p * drop.inv_keep : p) : 0.f;
     const float dpd = kept ? (DROP ? dp * drop.inv_keep : dp) : 0.f;
-    const float ds = p * (dpd - LD[2 * ((size_t)bh * Nq + q) + 1]);
+    const float ds =
+        p * (dpd + LD[ld_index<DROP>(bh, q, (Nq + kLdRows - 1) / kLdRows) + ld_nd_off<DROP>()]);
 #pragma unroll
     for (int e = 0; e < D; ++e) {
       dv[e] = fmaf(pd, sdo[e], dv[e]);
@@ -1018,7 +1061,8 @@ __global__ __launch_bounds__(kF32BT) void bwd_dq_f32_kernel(
     dq[e] = 0.f;
   }
   const float lq = (q < Nq) ? L[(size_t)bh * Nq + q] : 0.f;
-  const float dq_aux = (q < Nq) ? LD[2 * ((size_t)bh * Nq + q) + 1] : 0.f;
+  const float ndq =  // -D
+      (q < Nq) ? LD[ld_index<DROP>(bh, q, (Nq + kLdRows - 1) / kLdRows) + ld_nd_off<DROP>()] : 0.f;
   int kend = Nk;
   if (CAUSAL) kend = min(Nk, qt * kF32BT + kF32BT + off);
   for (int key = 0; key < kend; ++key) {
@@ -1038,7 +1082,7 @@ __global__ __launch_bounds__(kF32BT) void bwd_dq_f32_kernel(
     }
     const float p = expf(s * scale + (brow ? brow[key] : 0.f) - lq);
     const bool kept = !DROP || drop_byte(drop, bh, q, key) < drop.thresh;
-    const float ds = p * ((kept ? (DROP ? dp * drop.inv_keep : dp) : 0.f) - dq_aux);
+    const float ds = p * ((kept ? (DROP ? dp * drop.inv_keep : dp) : 0.f) + ndq);
 #pragma unroll
     for (int e = 0; e < D; ++e) dq[e] = fmaf(ds, sk[e], dq[e]);
   }
@@ -1050,12 +1094,19 @@ __global__ __launch_bounds__(kF32BT) void bwd_dq_f32_kernel(
 
 template <int D, typename T>
 hipError_t launch_pre(const BwdArgs& a, hipStream_t s) {
-  const long rows = (long)a.B * a.H * a.Nq;
+  const int BH = a.B * a.H;
+  const int nblk = (a.Nq + kLdRows - 1) / kLdRows;
+  const long rows = (long)BH * nblk * kLdRows;  // padded rows
   constexpr int RPB = 256 / (D / 8);
   const long nb = (rows + RPB - 1) / RPB;
   if (nb == 0) return hipSuccess;
-  hipLaunchKernelGGL((bwd_pre_kernel<D, T>), dim3((unsigned)nb), dim3(256), 0, s,
-                     (const T*)a.O, (const T*)a.dO, a.L, a.LD, rows);
+  // the layout of the (L2, -D) blocks follows the kernels that read them
+  if (a.drop.on)
+    hipLaunchKernelGGL((bwd_pre_kernel<D, T, true>), dim3((unsigned)nb), dim3(256), 0, s,
+                       (const T*)a.O, (const T*)a.dO, a.L, a.LD, BH, a.Nq, nblk);
+  else
+    hipLaunchKernelGGL((bwd_pre_kernel<D, T, false>), dim3((unsigned)nb), dim3(256), 0, s,
+                       (const T*)a.O, (const T*)a.dO, a.L, a.LD, BH, a.Nq, nblk);
   return hipGetLastError();
 }
 

@@ -56,7 +56,7 @@ struct BwdArgs {
   int B, H, Nq, Nk, d;
   float scale;
   bool causal;
-  float* LD;  // [B*H*Nq][2] fp32 scratch (workspace): per query row L * log2(e), then D = rowsum(dO * O)
+  float* LD;  // fp32 workspace: per head and block of 32 query rows, L * log2(e) and -D, D = rowsum(dO * O)
   BiasArgs bias;
   DropArgs drop;
 };
@@ -74,7 +74,7 @@ hipError_t launch_fwd_split_f16(const FwdArgs& a, int splits, float* part_o, flo
                                 hipStream_t s);
 
 // Backward: D = rowsum(dO*O) and L*log2(e); dK and dV; dQ.
-// `stages`: bit 1 the (L*log2 e, D) pairs, bit 2 dK/dV kernel, bit 4 dQ kernel (2 and 4 read them).
+// `stages`: bit 1 the (L*log2 e, -D) blocks, bit 2 dK/dV kernel, bit 4 dQ kernel (2 and 4 read them).
 hipError_t launch_bwd_bf16(const BwdArgs& a, int stages, hipStream_t s);
 hipError_t launch_bwd_f16(const BwdArgs& a, int stages, hipStream_t s);
 hipError_t launch_bwd_f32(const BwdArgs& a, int stages, hipStream_t s);

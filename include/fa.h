@@ -97,8 +97,10 @@ fa_status fa_fwd(const void* Q, const void* K, const void* V, void* O, float* L,
  *  Q, K, V, O (from fa_fwd), L (from fa_fwd), dO: read.  dQ [B,H,Nq,d],
  *  dK, dV [B,H,Nk,d]: overwritten, every element (not accumulated into).
  *  workspace: fa_bwd_workspace_size() bytes of device memory, 16-byte
- *  aligned, written by the first stage: per query row the fp32 pair
- *  (L*log2(e), D), [B,H,Nq,2].  dK and dV are computed per key block and dQ
+ *  aligned, written by the first stage: per head and block of 32 query rows
+ *  64 fp32, the rows' L*log2(e) and -D, D = rowsum(dO * O) (rows past Nq
+ *  zero), laid out for the kernels that read them (by row pair with dropout,
+ *  as two runs of 32 without).  dK and dV are computed per key block and dQ
  *  per query block by workgroups that recompute P and dP for their rows, so
  *  there are no atomic operations and every output is deterministic.  Both
  *  kinds of workgroup run in one launch after the preprocess launch.
@@ -111,7 +113,7 @@ fa_status fa_bwd(const void* Q, const void* K, const void* V, const void* O, con
 /*
  * The backward pass in stages, for callers that schedule or time them
  * separately.  Same arguments as fa_bwd plus `stages`, a bit mask:
- *   FA_BWD_PREPROCESS (1): the (L*log2(e), D = rowsum(dO * O)) pairs into the workspace;
+ *   FA_BWD_PREPROCESS (1): L*log2(e) and -D, D = rowsum(dO * O), into the workspace;
  *   FA_BWD_DKDV       (2): dK and dV written (reads the workspace);
  *   FA_BWD_DQ         (4): dQ written (reads the workspace).
  * fa_bwd(...) is fa_bwd_stages(..., FA_BWD_ALL).  Stages 2 and 4 need stage 1
@@ -130,9 +132,10 @@ fa_status fa_bwd_stages(const void* Q, const void* K, const void* V, const void*
  * fa_bwd for callers that cannot allocate device memory (code under HIP graph
  * capture, tight serving loops, harnesses that forbid hipMalloc): the same
  * arguments and results as fa_bwd without the workspace.  The per-row
- * (L*log2(e), D) pairs go to a scratch array inside the library instead, one
- * per GPU, of fa_bwd_noalloc_max_rows() rows (16 MiB; held until the process
- * ends).  B*H*Nq rows beyond that return FA_ERR_WORKSPACE before any launch.
+ * L*log2(e) and -D go to a scratch array inside the library instead, one per
+ * GPU, of fa_bwd_noalloc_max_rows() rows (16 MiB; held until the process
+ * ends).  B*H*ceil(Nq/32)*32 rows (each head's rows padded to a multiple of
+ * 32) beyond that return FA_ERR_WORKSPACE before any launch.
  * The first call on a GPU looks up the array's address there; no call
  * allocates or frees memory.  Calls on one GPU share the array, so calls
  * that overlap on one GPU (different streams, or threads) race: serialise

@@ -242,10 +242,12 @@ def test_ex_entry_points_accept_empty_problems(lib):
 
 def test_workspace_queries(lib):
     B, H, N, d = 2, 3, 100, 128
-    # backward: D and L*log2(e), each [B,H,N] fp32 padded to 256 bytes
+    # backward: L*log2(e) and -D of every query row, fp32, rows padded to
+    # blocks of 32 per head, the whole padded to 256 bytes
     def up(x):
         return (x + 255) // 256 * 256
-    assert lib.fa_bwd_workspace_size(B, H, N, N, d, fa.FA_BF16) == 2 * up(B * H * N * 4)
+    assert lib.fa_bwd_workspace_size(B, H, N, N, d, fa.FA_BF16) == \
+        up(B * H * ((N + 31) // 32) * 32 * 2 * 4)
     # tiled forward needs none; the split path holds per-split outputs and logsumexps
     assert lib.fa_fwd_workspace_size(B, H, N, N, d, fa.FA_BF16, 0) == 0
     assert lib.fa_fwd_num_splits(B, H, N, N, d, fa.FA_BF16, 0) == 1
@@ -262,7 +264,8 @@ def test_workspace_queries(lib):
     assert lib.fa_fwd_num_splits(16, 32, 1, 16384, 128, fa.FA_FP16, 0) == s
     assert lib.fa_fwd_workspace_size(16, 32, 1, 16384, 128, fa.FA_FP16, 0) == \
         lib.fa_fwd_workspace_size(16, 32, 1, 16384, 128, fa.FA_BF16, 0)
-    assert lib.fa_bwd_workspace_size(B, H, N, N, d, fa.FA_FP16) == 2 * up(B * H * N * 4)
+    assert lib.fa_bwd_workspace_size(B, H, N, N, d, fa.FA_FP16) == \
+        lib.fa_bwd_workspace_size(B, H, N, N, d, fa.FA_BF16)
     # a few query rows: chunks of whole 128-key tile pairs, partials per row
     assert lib.fa_fwd_num_splits(2, 4, 16, 8192, 128, fa.FA_BF16, 0) == 16
     assert lib.fa_fwd_workspace_size(2, 4, 16, 8192, 128, fa.FA_BF16, 0) == \

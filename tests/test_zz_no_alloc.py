@@ -1,7 +1,7 @@
 """fa_bwd_noalloc (the backward pass without a caller workspace) against fa_bwd.
 
 Both run the same kernels; the allocation-free entry point keeps the per-row
-(L*log2(e), D) pairs in the library's scratch array.  Two calls in a row, the
+L*log2(e) and -D in the library's scratch array.  Two calls in a row, the
 second on a smaller problem, must each equal fa_bwd bit for bit (the array
 keeps the first call's rows; nothing of them may leak into the second).
 """
