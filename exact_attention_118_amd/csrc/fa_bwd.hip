@@ -91,15 +91,14 @@ template <int D, typename T, bool DROP>
 __global__ __launch_bounds__(256) void bwd_pre_kernel(const T* __restrict__ O,
                                                       const T* __restrict__ dO,
                                                       const float* __restrict__ L,
-                                                      float* __restrict__ LD, int BH, int Nq,
-                                                      int nblk) {
-  constexpr int TPR = D / 8;  // threads per row, 8 elements each
-  constexpr int RPB = 256 / TPR;
-  const long rpad = (long)nblk * kLdRows;  // rows per head, padded
-  const long prow = (long)blockIdx.x * RPB + threadIdx.x / TPR;
-  const int bh = (int)(prow / rpad);
-  const int r = (int)(prow - bh * rpad);
-  const bool valid = bh < BH && r < Nq;
+                                                      float* __restrict__ LD, int Nq, int nblk) {
+  constexpr int TPR = D / 8;      // threads per row, 8 elements each
+  constexpr int RPB = 256 / TPR;  // rows per workgroup, all in one block of a head
+  static_assert(kLdRows % RPB == 0, "a workgroup's rows lie in one block");
+  const int wph = nblk * (kLdRows / RPB);  // workgroups per head (the grid has B*H * wph)
+  const int bh = blockIdx.x / wph;
+  const int r = (blockIdx.x - bh * wph) * RPB + threadIdx.x / TPR;  // row, padded
+  const bool valid = r < Nq;
   const int part = threadIdx.x % TPR;
   float acc = 0.f;
   if (valid) {
@@ -109,7 +108,7 @@ __global__ __launch_bounds__(256) void bwd_pre_kernel(const T* __restrict__ O,
   }
 #pragma unroll
   for (int msk = TPR / 2; msk >= 1; msk >>= 1) acc += __shfl_xor(acc, msk, 64);
-  if (bh < BH && part == 0) {
+  if (part == 0) {
     const size_t i = ld_index<DROP>(bh, r, nblk);
     LD[i] = valid ? L[(size_t)bh * Nq + r] * kLog2e : 0.f;
     LD[i + ld_nd_off<DROP>()] = valid ? -acc : 0.f;
@@ -1096,17 +1095,16 @@ template <int D, typename T>
 hipError_t launch_pre(const BwdArgs& a, hipStream_t s) {
   const int BH = a.B * a.H;
   const int nblk = (a.Nq + kLdRows - 1) / kLdRows;
-  const long rows = (long)BH * nblk * kLdRows;  // padded rows
   constexpr int RPB = 256 / (D / 8);
-  const long nb = (rows + RPB - 1) / RPB;
+  const long nb = (long)BH * nblk * (kLdRows / RPB);  // workgroups (rows padded per head)
   if (nb == 0) return hipSuccess;
   // the layout of the (L2, -D) blocks follows the kernels that read them
   if (a.drop.on)
     hipLaunchKernelGGL((bwd_pre_kernel<D, T, true>), dim3((unsigned)nb), dim3(256), 0, s,
-                       (const T*)a.O, (const T*)a.dO, a.L, a.LD, BH, a.Nq, nblk);
+                       (const T*)a.O, (const T*)a.dO, a.L, a.LD, a.Nq, nblk);
   else
     hipLaunchKernelGGL((bwd_pre_kernel<D, T, false>), dim3((unsigned)nb), dim3(256), 0, s,
-                       (const T*)a.O, (const T*)a.dO, a.L, a.LD, BH, a.Nq, nblk);
+                       (const T*)a.O, (const T*)a.dO, a.L, a.LD, a.Nq, nblk);
   return hipGetLastError();
 }
 

@@ -12,15 +12,18 @@
 // exp2 with scale*log2(e) folded on the host (the 51CTO FlashAttention V1/V2 notes, "指令级别的优化").
 //
 // gfx950 mapping (bf16 / fp16 kernel):
-//  * 256 threads = 4 waves; the workgroup owns BR = 128 query rows and each
-//    wave owns 32 of them ("sliced-Q", the 51CTO FlashAttention V1/V2 notes "Warp Level 并行": all waves
-//    read the same K/V tile, so no cross-wave reduction is needed).
+//  * 256 or 512 threads = 4 or 8 waves; the workgroup owns BR = 128 or 256
+//    query rows and each wave owns 32 of them ("sliced-Q", the 51CTO
+//    FlashAttention V1/V2 notes "Warp Level 并行": all waves read the same K/V
+//    tile, so no cross-wave reduction is needed).
 //  * Scores are computed transposed, S^T = K Q^T, with the 32x32x16 bf16/fp16
 //    MFMA: each lane then holds 16 scores of ONE query row (its lane % 32), so
 //    row max / row sum are lane-local plus a single exchange with lane ^ 32.
 //  * O^T = V^T P^T reuses the S^T accumulator registers directly as the
 //    P operand (no LDS round trip); V^T is read from the row-major V tile with
-//    the LDS transpose read ds_read_b64_tr_b16.
+//    the LDS transpose read ds_read_b64_tr_b16.  The row sums of the rounded
+//    P that normalise O come from one 16x16x32 MFMA per 16-key chunk, not
+//    from vector instructions.
 //  * K/V tiles of BC = 64 keys are staged in LDS, double-buffered and loaded
 //    straight from HBM into LDS (global_load_lds_dwordx4) in an XOR-swizzled
 //    layout that keeps both the row reads and the transpose reads free of
