@@ -842,9 +842,10 @@ __device__ __forceinline__ void dq_body(const T* __restrict__ Q, const T* __rest
           __builtin_amdgcn_sched_barrier(0);
         }
       };
-      // dQ^T += K^T dS^T over half mt (2*NNT MFMAs); with `overlap`, the dS
-      // elements of half mt + 1 are computed between them.
-      auto dq_half = [&](int mt, bool overlap) {
+      // dQ^T += K^T dS^T over half mt (2*NNT MFMAs), with the ne dS elements
+      // e0 .. e0+ne-1 of half 1 computed between them, a pair at a time,
+      // spread over the first `window` steps.
+      auto dq_half = [&](int mt, int e0, int ne, int window) {
         T8 ring[TRING];
 #pragma unroll
         for (int st = 0; st < TRING; ++st) ring[st] = kt_frag(P, mt, st);
@@ -853,11 +854,13 @@ __device__ __forceinline__ void dq_body(const T* __restrict__ Q, const T* __rest
           const T8 a = ring[st % TRING];
           if (st + TRING < 2 * NNT) ring[st % TRING] = kt_frag(P, mt, st + TRING);
           dqacc[st % NNT] = mfma32(a, dsf[mt * 2 + st / NNT], dqacc[st % NNT]);
-          if (overlap) {
 #pragma unroll
-            for (int h = 0; h < 16 / (2 * NNT); ++h) ds_elem(mt + 1, st * (16 / (2 * NNT)) + h);
-            pin(dsf[(mt + 1) * 2 + (st * (16 / (2 * NNT))) / 8]);
-          }
+          for (int q = 0; q < ne / 2; ++q)
+            if (q * window / (ne / 2) == st) {
+              ds_elem(1, e0 + 2 * q);
+              ds_elem(1, e0 + 2 * q + 1);
+              pin(dsf[2 + (e0 + 2 * q) / 8]);
+            }
           __builtin_amdgcn_sched_barrier(0);
         }
       };
@@ -877,8 +880,13 @@ __device__ __forceinline__ void dq_body(const T* __restrict__ Q, const T* __rest
       if constexpr (BIAS) bias_issue(k0 + BC);  // the region is free: stage tile j+1
       mask_half(1);
       if constexpr (DROP) drop_bytes_rows(rb[1], drop, bh, qrow, k0 + 32 + half * 4, lane);
-      dq_half(0, true);    // dS of half 1 overlaps dQ of half 0
-      dq_half(1, false);
+      if constexpr (D == 128) {
+        dq_half(0, 0, 8, 2 * NNT);  // half 1's first chunk of dS overlaps dQ of half 0
+        dq_half(1, 8, 8, NNT);      // its second chunk the steps that read the first
+      } else {
+        dq_half(0, 0, 16, 2 * NNT);
+        dq_half(1, 0, 0, 1);
+      }
 
       // this wave's part of tile j+1 has landed (with a bias, the 4 bias
       // loads of tile j+1, issued last, may still be in flight)
