@@ -2,8 +2,9 @@
 """Throughput of the fused attention path on one MI355X.
 
 One step = the whole hot path on one batch: forward (fa_fwd) then backward
-(fa_bwd: the (L*log2 e, -D) preprocess, the dK/dV kernel, the dQ kernel) on
-the long-sequence workload B=1, H=32, N=8192, d=128, causal, bf16 (Q and K
+(fa_bwd: the (L*log2 e, -D) preprocess, the dK/dV kernel, which also stores
+dS on this workload, and the dQ kernel, which reads it) on the long-sequence
+workload B=1, H=32, N=8192, d=128, causal, bf16 (Q and K
 scaled by 3).  Inputs are synthetic (seeded normal draws on the GPU) and
 resident in HBM before timing starts.  Prints ONE JSON line on stdout;
 progress goes to stderr.
@@ -52,9 +53,18 @@ KERNEL_SOURCES = {
     "bwd_fused_kernel": "fa_bwd.hip",
     "bwd_dkdv_kernel": "fa_bwd.hip",
     "bwd_dq_kernel": "fa_bwd.hip",
+    "bwd_dq_ds_kernel": "fa_bwd.hip",
     "bwd_pre_kernel": "fa_bwd.hip",
 }
-KERNEL_RE = r"(fwd_kernel|bwd_fused_kernel|bwd_dkdv_kernel|bwd_dq_kernel|bwd_pre_kernel)"
+KERNEL_RE = r"(fwd_kernel|bwd_fused_kernel|bwd_dkdv_kernel|bwd_dq_kernel|bwd_dq_ds_kernel|bwd_pre_kernel)"
+
+
+def stores_ds(fa, w, code):
+    """True where fa_bwd takes the stored-dS path: its workspace then holds
+    the dS buffer after the per-row block."""
+    lib = fa.load_library()
+    return (lib.fa_bwd_workspace_size(w.B, w.H, w.Nq, w.Nk, w.d, code)
+            > lib.fa_bwd_bias_workspace_size(w.B, w.H, w.Nq, w.Nk, w.d, code))
 
 
 def source_sha(path):
@@ -557,15 +567,22 @@ def run_probes(seconds):
     timed("fwd_kernel (4*d flop per pair)",
           lambda: fa.fa_fwd(x["Q"], x["K"], x["V"], O, L, w.scale, w.causal), 4 * w.d * pairs / 1e12,
           "TFLOP/s")
+    sds = stores_ds(fa, w, fa.FA_BF16)
     timed("bwd_dkdv_kernel (8*d flop per pair)",
           lambda: fa.fa_bwd(x["Q"], x["K"], x["V"], O, L, x["dO"], *g, w.scale, w.causal, workspace=ws,
                             stages=fa.FA_BWD_DKDV), 8 * w.d * pairs / 1e12, "TFLOP/s")
-    timed("bwd_dq_kernel (6*d flop per pair executed)",
-          lambda: fa.fa_bwd(x["Q"], x["K"], x["V"], O, L, x["dO"], *g, w.scale, w.causal, workspace=ws,
-                            stages=fa.FA_BWD_DQ), 6 * w.d * pairs / 1e12, "TFLOP/s")
-    timed("bwd_fused_kernel (14*d flop per pair executed)",
-          lambda: fa.fa_bwd(x["Q"], x["K"], x["V"], O, L, x["dO"], *g, w.scale, w.causal, workspace=ws,
-                            stages=fa.FA_BWD_DKDV | fa.FA_BWD_DQ), 14 * w.d * pairs / 1e12, "TFLOP/s")
+    if sds:  # dQ = scale * dS K from the stored dS: one GEMM
+        timed("bwd_dq_ds_kernel (2*d flop per pair)",
+              lambda: fa.fa_bwd(x["Q"], x["K"], x["V"], O, L, x["dO"], *g, w.scale, w.causal,
+                                workspace=ws, stages=fa.FA_BWD_DQ), 2 * w.d * pairs / 1e12, "TFLOP/s")
+    else:
+        timed("bwd_dq_kernel (6*d flop per pair executed)",
+              lambda: fa.fa_bwd(x["Q"], x["K"], x["V"], O, L, x["dO"], *g, w.scale, w.causal,
+                                workspace=ws, stages=fa.FA_BWD_DQ), 6 * w.d * pairs / 1e12, "TFLOP/s")
+        timed("bwd_fused_kernel (14*d flop per pair executed)",
+              lambda: fa.fa_bwd(x["Q"], x["K"], x["V"], O, L, x["dO"], *g, w.scale, w.causal,
+                                workspace=ws, stages=fa.FA_BWD_DKDV | fa.FA_BWD_DQ),
+              14 * w.d * pairs / 1e12, "TFLOP/s")
     del x, O, L, g, ws
 
     nrb, ablocks, aiters = 8192, 2048, 16  # a 128 MiB buffer
@@ -642,6 +659,8 @@ def main():
     dQ, dK, dV = torch.empty_like(Q), torch.empty_like(K), torch.empty_like(V)
     ws = torch.empty(fa.bwd_workspace_size(w.B, w.H, w.Nq, w.Nk, w.d, fa.FA_BF16),
                      dtype=torch.uint8, device="cuda")
+    sds = stores_ds(fa, w, fa.FA_BF16)
+    log(f"backward path: {'stored dS' if sds else 'recomputed dQ'}")
 
     def step(ev=None):
         if ev is not None:
@@ -653,11 +672,22 @@ def main():
                   stages=fa.FA_BWD_PREPROCESS)
         if ev is not None:
             ev[2].record()
-        # dK/dV and dQ: one launch (bwd_fused_kernel), as fa_bwd runs them
-        fa.fa_bwd(Q, K, V, O, L, dO, dQ, dK, dV, w.scale, w.causal, workspace=ws,
-                  stages=fa.FA_BWD_DKDV | fa.FA_BWD_DQ)
+        if sds:
+            # as fa_bwd runs them: dK/dV (storing dS), then dQ from dS
+            fa.fa_bwd(Q, K, V, O, L, dO, dQ, dK, dV, w.scale, w.causal, workspace=ws,
+                      stages=fa.FA_BWD_DKDV)
+            if ev is not None:
+                ev[3].record()
+            fa.fa_bwd(Q, K, V, O, L, dO, dQ, dK, dV, w.scale, w.causal, workspace=ws,
+                      stages=fa.FA_BWD_DQ)
+        else:
+            # dK/dV and dQ: one launch (bwd_fused_kernel), as fa_bwd runs them
+            fa.fa_bwd(Q, K, V, O, L, dO, dQ, dK, dV, w.scale, w.causal, workspace=ws,
+                      stages=fa.FA_BWD_DKDV | fa.FA_BWD_DQ)
+            if ev is not None:
+                ev[3].record()
         if ev is not None:
-            ev[3].record()
+            ev[4].record()
 
     sampler = PowerSampler(start=False)  # amdsmi set up now; it samples after the timed steps
     for _ in range(args.warmup):
@@ -665,7 +695,7 @@ def main():
     torch.cuda.synchronize()
     log(f"warmup {args.warmup} done")
 
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(5)] for _ in range(args.steps)]
     start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     t0 = time.perf_counter()
@@ -700,14 +730,16 @@ def main():
     def mean_ms(a, b):
         return sum(e[a].elapsed_time(e[b]) for e in evs) / len(evs)
 
-    fwd_ms, pre_ms, main_ms = mean_ms(0, 1), mean_ms(1, 2), mean_ms(2, 3)
+    fwd_ms, pre_ms, main_ms = mean_ms(0, 1), mean_ms(1, 2), mean_ms(2, 4)
+    kv_ms, q_ms = mean_ms(2, 3), mean_ms(3, 4)  # stored dS: the dK/dV and dQ launches
     bwd_ms = pre_ms + main_ms
     pairs = unmasked_pairs(w.Nq, w.Nk, w.causal) * w.B * w.H
     fwd_flops, bwd_flops = 4 * w.d * pairs, 10 * w.d * pairs
     value = (fwd_flops + bwd_flops) / (ms_per_step * 1e-3) / 1e12
 
-    # The two kernels of the fused launch, each launched alone (outside the
-    # timed steps): how the backward's time splits between dK/dV and dQ.
+    # The dK/dV and dQ stages, each launched alone (outside the timed steps):
+    # how the backward's time splits between them (the halves of the fused
+    # launch where dQ is recomputed).
     def alone(stages, reps=5):
         e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         fa.fa_bwd(Q, K, V, O, L, dO, dQ, dK, dV, w.scale, w.causal, workspace=ws, stages=stages)
@@ -721,17 +753,19 @@ def main():
 
     dkdv_ms, dq_ms = alone(fa.FA_BWD_DKDV), alone(fa.FA_BWD_DQ)
 
-    # Algorithmic flops per launch: the forward's 2 GEMMs; the fused backward
-    # launch's S, dP, dV and dK GEMMs of the dK/dV workgroups (8*d per pair)
-    # and the dQ GEMM of the dQ workgroups (2*d per pair) -- their
-    # recomputation of S and dP (4*d per pair) is overhead, not algorithmic.
+    # Algorithmic flops per launch: the forward's 2 GEMMs; the S, dP, dV and
+    # dK GEMMs of the dK/dV kernel (8*d per pair) and the dQ GEMM (2*d per
+    # pair), in two launches with stored dS, else in one fused launch whose
+    # dQ workgroups also recompute S and dP (4*d per pair, not algorithmic).
     csrc = os.path.join(ROOT, "exact_attention_118_amd", "csrc")
-    kernels = {
-        "fwd_kernel": {"ms": fwd_ms, "flops": fwd_flops,
-                       "source": os.path.join(csrc, "fa_fwd.hip")},
-        "bwd_fused_kernel": {"ms": main_ms, "flops": 10 * w.d * pairs,
-                             "source": os.path.join(csrc, "fa_bwd.hip")},
-    }
+    src_b = os.path.join(csrc, "fa_bwd.hip")
+    kernels = {"fwd_kernel": {"ms": fwd_ms, "flops": fwd_flops,
+                              "source": os.path.join(csrc, "fa_fwd.hip")}}
+    if sds:
+        kernels["bwd_dkdv_kernel"] = {"ms": kv_ms, "flops": 8 * w.d * pairs, "source": src_b}
+        kernels["bwd_dq_ds_kernel"] = {"ms": q_ms, "flops": 2 * w.d * pairs, "source": src_b}
+    else:
+        kernels["bwd_fused_kernel"] = {"ms": main_ms, "flops": 10 * w.d * pairs, "source": src_b}
     dom_name = max(kernels, key=lambda k: kernels[k]["ms"])
     dom = kernels[dom_name]
     achieved = dom["flops"] / (dom["ms"] * 1e-3) / 1e12
@@ -764,10 +798,13 @@ def main():
                 "mfma_frac": fwd_flops / (fwd_ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS},
         "bwd": {"ms": bwd_ms, "TFLOP/s": bwd_flops / (bwd_ms * 1e-3) / 1e12,
                 "mfma_frac": bwd_flops / (bwd_ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS,
+                "path": "stored dS" if sds else "recomputed dQ",
                 "preprocess_ms": pre_ms, "dkdv_dq_ms": main_ms,
+                **({"dkdv_ms": kv_ms, "dq_ms": q_ms} if sds else {}),
                 "alone": {"dkdv_ms": dkdv_ms, "dq_ms": dq_ms,
                           "dkdv_TFLOP/s": 8 * w.d * pairs / (dkdv_ms * 1e-3) / 1e12},
-                "executed_mfma_frac": 14 * w.d * pairs / (bwd_ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS},
+                "executed_mfma_frac": (10 if sds else 14) * w.d * pairs / (bwd_ms * 1e-3) / 1e12
+                / PEAK_BF16_TFLOPS},
     }
     del dQ, dK, dV
     if not args.no_configs:

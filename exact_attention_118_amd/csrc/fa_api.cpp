@@ -117,6 +117,24 @@ size_t bwd_ws_bytes(int BH, int Nq) {
   return round_up((size_t)BH * ((Nq + 31) / 32) * 64 * sizeof(float), kWsAlign);
 }
 
+// After it, the dS buffer of the stored-dS backward, where that path runs:
+// the dK/dV kernel stores dS and dQ = dS K reads it, instead of a dQ kernel
+// that recomputes S and dP (two of its three GEMMs).  The buffer holds 2
+// bytes per (query, key) pair, padded to 32 x 32 blocks, so it grows with
+// Nq * Nk.  The path runs for bf16 and fp16 at d = 128, without a bias, with
+// Nq and Nk of at least kDsMinLen and a buffer of at most kDsMaxBytes.
+// Measured against recomputation (same process, steady state): 4-9% faster
+// at d = 128 for N = 2048-8192; slower at d = 64, where the recomputed GEMMs
+// cost half as much and the dS traffic the same, and on short sequences,
+// where the fused recomputing launch runs dQ beside the key blocks' chains.
+constexpr size_t kDsMaxBytes = size_t(8) << 30;
+constexpr int kDsMinLen = 2048;
+size_t bwd_ds_ws_bytes(int BH, int Nq, int Nk, int d, fa_dtype dtype) {
+  if (dtype == FA_FP32 || d != 128 || BH <= 0 || Nq < kDsMinLen || Nk < kDsMinLen) return 0;
+  const size_t b = fa::bwd_ds_bytes(BH, Nq, Nk);
+  return b <= kDsMaxBytes ? round_up(b, kWsAlign) : 0;
+}
+
 // Scratch of fa_bwd_noalloc: the per-row L*log2(e) and -D that fa_bwd keeps
 // in the caller's workspace (8 bytes per query row, rows padded to 32 per head).  One copy per GPU, held until the process
 // ends; every call on a GPU shares it.  In host code `scratch` names a
@@ -179,6 +197,11 @@ size_t fa_fwd_workspace_size(int B, int H, int Nq, int Nk, int d, fa_dtype dtype
 }
 
 size_t fa_bwd_workspace_size(int B, int H, int Nq, int Nk, int d, fa_dtype dtype) {
+  if (check_dims(B, H, Nq, Nk, d, 1.f, 0, dtype) != FA_OK) return 0;
+  return bwd_ws_bytes(B * H, Nq) + bwd_ds_ws_bytes(B * H, Nq, Nk, d, dtype);
+}
+
+size_t fa_bwd_bias_workspace_size(int B, int H, int Nq, int Nk, int d, fa_dtype dtype) {
   if (check_dims(B, H, Nq, Nk, d, 1.f, 0, dtype) != FA_OK) return 0;
   return bwd_ws_bytes(B * H, Nq);
 }
@@ -303,7 +326,8 @@ fa_status fwd_impl(const void* Q, const void* K, const void* V, const fa::BiasAr
 fa_status bwd_impl(const void* Q, const void* K, const void* V, const fa::BiasArgs& bias,
                    const fa::DropArgs& drop, const void* O, const float* L, const void* dO, void* dQ, void* dK, void* dV,
                    int B, int H, int Nq, int Nk, int d, float scale, int causal, fa_dtype dtype,
-                   void* workspace, size_t workspace_bytes, void* stream, int stages) {
+                   void* workspace, size_t workspace_bytes, void* stream, int stages,
+                   bool allow_ds = true) {
   if (stages <= 0 || stages > FA_BWD_ALL) return FA_ERR_UNSUPPORTED;
   fa_status st = check_dims(B, H, Nq, Nk, d, scale, causal, dtype);
   if (st != FA_OK) return st;
@@ -313,13 +337,17 @@ fa_status bwd_impl(const void* Q, const void* K, const void* V, const fa::BiasAr
   if (!aligned(K) || !aligned(V) || !aligned(dK) || !aligned(dV)) return FA_ERR_ALIGN;
   if (Nq > 0 && (!aligned(Q) || !aligned(O) || !aligned(L) || !aligned(dO) || !aligned(dQ)))
     return FA_ERR_ALIGN;
-  if (Nq > 0 && (!workspace || workspace_bytes < bwd_ws_bytes(B * H, Nq))) return FA_ERR_WORKSPACE;
+  // stored dS without a bias, when its buffer is within the limit
+  const size_t ws_ld = bwd_ws_bytes(B * H, Nq);
+  const size_t ws_ds = (allow_ds && !bias.ptr) ? bwd_ds_ws_bytes(B * H, Nq, Nk, d, dtype) : 0;
+  if (Nq > 0 && (!workspace || workspace_bytes < ws_ld + ws_ds)) return FA_ERR_WORKSPACE;
   if (Nq > 0 && !aligned(workspace)) return FA_ERR_ALIGN;
   fa::BwdArgs a{Q, K, V, O, L, dO, dQ, dK, dV, B, H, Nq, Nk, d, scale, causal != 0,
                 nullptr};
   a.bias = bias;
   a.drop = drop;
   if (Nq > 0) a.LD = static_cast<float*>(workspace);
+  if (ws_ds > 0) a.dS = static_cast<char*>(workspace) + ws_ld;
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
   const hipError_t e =
       (dtype == FA_BF16)   ? fa::launch_bwd_bf16(a, stages, s)
@@ -492,7 +520,8 @@ fa_status fa_bwd_noalloc(const void* Q, const void* K, const void* V, const void
   const fa_status sa = scratch_address(&ws);
   if (sa != FA_OK) return sa;
   return bwd_impl(Q, K, V, fa::BiasArgs{}, fa::DropArgs{}, O, L, dO, dQ, dK, dV, B, H, Nq, Nk, d,
-                  scale, causal, dtype, ws, kNoAllocScratchBytes, stream, FA_BWD_ALL);
+                  scale, causal, dtype, ws, kNoAllocScratchBytes, stream, FA_BWD_ALL,
+                  /*allow_ds=*/false);
 }
 
 size_t fa_bwd_noalloc_max_rows(void) { return kNoAllocScratchBytes / 8; }

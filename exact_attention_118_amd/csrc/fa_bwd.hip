@@ -16,12 +16,17 @@
 // over query blocks.  dQ needs a sum over every key block.  The notes
 // ("Sequence Parallel") weigh global atomic adds, which are slow, against
 // per-key-block dQ buffers reduced afterwards, whose size grows with N^2 / BC.
-// On MI355X fp32 atomic adds run at about a fifth of the store bandwidth, so
-// this library takes a third route: a second kernel, gridded over query
-// blocks like the forward pass, recomputes S and dP for its rows and
-// accumulates dQ in registers.  That costs two extra GEMMs per pair (seven in
-// all instead of five) but needs no atomics, no fp32 accumulator and no
-// workspace beyond D, and every output is deterministic.
+// On MI355X fp32 atomic adds run at about a fifth of the store bandwidth.
+// This library forms dQ per query block instead, in registers, with no
+// atomics and no fp32 accumulator (every output is deterministic), one of two
+// ways:
+//  * stored dS (bf16/fp16, d = 128, long sequences; the host picks it): the
+//    dK/dV kernel also writes its dS blocks, 2 bytes per pair, and
+//    bwd_dq_ds_kernel, gridded over query blocks, forms dQ = scale * dS K from
+//    them: the five GEMMs of the notes, for 4 bytes of HBM traffic per pair;
+//  * otherwise bwd_dq_kernel recomputes S and dP for its rows (two extra
+//    GEMMs per pair, seven in all) and needs no workspace beyond D; it runs in
+//    one launch with the dK/dV workgroups (bwd_fused_kernel below).
 //
 // gfx950 mapping:
 //  * bwd_dkdv_kernel: 256 threads = 4 waves, two workgroups per CU (two
@@ -51,6 +56,12 @@
 //    balances the causal triangle; the query-block
 //    grid uses the forward pass's mapping, causal query tiles in pairs
 //    (t, nqt-1-t) of equal total work.
+//  * bwd_dq_ds_kernel: the dQ kernel's grid and wave layout without its
+//    softmax: per 64-key tile a wave stages its two 2 KB dS chunks in LDS and
+//    issues 16 MFMAs (d = 128) reading K^T and dS^T by transpose reads; bound
+//    by the HBM reads of dS (both the dS stores and these reads carry the
+//    non-temporal hint: 5-7% faster than cached accesses on the long-sequence
+//    backward, whose 2 GiB of dS would otherwise pass through the caches).
 //  * bwd_fused_kernel (no bias): both grids in one launch, merged by expected
 //    workgroup length (long key blocks, then the dQ workgroups, then the short
 //    key blocks), so that the dQ workgroups fill the CUs the long key blocks
@@ -86,6 +97,22 @@ __host__ __device__ __forceinline__ size_t ld_index(int bh, int row, int nblk) {
 }
 template <bool DROP>
 constexpr int ld_nd_off() { return DROP ? 1 : kLdRows; }
+
+// dS buffer of the stored-dS backward (dK/dV kernel writes, dQ kernel reads):
+// per head and 32-row query block, one 2 KB chunk per group of 32 keys (the
+// keys of one dK/dV wave), 4 groups per 128-key block; the chunks of a query
+// block are consecutive.  A chunk holds the 16-bit dS of its 32 x 32 block as
+// 64 16-byte slots: slot (kc, h, k) has the dS of key k of the group for the
+// rows kc*16 + (e/4)*8 + h*4 + e%4 of the block (e = 0..7, one element each),
+// i.e. what lane h*32 + k of the dK/dV wave holds as the MFMA operand of row
+// chunk kc.  The slot lies at byte kc*1024 + h*512 + (k ^ 4(2kc + h))*16:
+// each dK/dV store fills 1 KB in one piece, and the XOR spreads the dQ
+// kernel's transposed reads of a chunk over all LDS banks.
+constexpr int kDsChunk = 1024;  // elements per chunk
+__host__ __device__ __forceinline__ int ds_chunks_per_row(int Nk) { return ((Nk + 127) / 128) * 4; }
+__host__ __device__ __forceinline__ unsigned ds_chunk_off(int kc, int h, int k) {
+  return (unsigned)(kc * 1024 + h * 512 + ((k ^ (4 * (2 * kc + h))) * 16));
+}
 
 template <int D, typename T, bool DROP>
 __global__ __launch_bounds__(256) void bwd_pre_kernel(const T* __restrict__ O,
@@ -140,13 +167,16 @@ struct DkdvLds {
   alignas(BIAS ? 1024 : 16) T sBias[BIAS ? 2 * BR * BC : 8];
 };
 
-// Block `bid` of the key-block grid (the kernel's blockIdx.x).
-template <typename T, int D, bool CAUSAL, bool BIAS, bool DROP>
+// Block `bid` of the key-block grid (the kernel's blockIdx.x).  DS: each
+// wave also stores the dS of every query block it runs, as a 2 KB chunk of
+// the dS buffer (layout at ds_chunk_off; two 16-byte non-temporal stores per
+// lane, chunk half kc as soon as its 16 rows are formed), for bwd_dq_ds_kernel.
+template <typename T, int D, bool CAUSAL, bool BIAS, bool DROP, bool DS = false>
 __device__ __forceinline__ void dkdv_body(
     const T* __restrict__ Q, const T* __restrict__ K, const T* __restrict__ V,
     const T* __restrict__ dO, const float* __restrict__ LD, T* __restrict__ dK,
     T* __restrict__ dV, int Nq, int Nk, int nkt, int BH, int hpx, float c, float scale, int off,
-    BiasDev bias, DropDev drop, DkdvLds<T, D, BIAS>& lds, int bid) {
+    BiasDev bias, DropDev drop, DkdvLds<T, D, BIAS>& lds, int bid, T* __restrict__ dSg = nullptr) {
   typedef typename Vec<T>::x8 T8;
   typedef typename Vec<T>::x4 T4;
   constexpr int kKvWaves = KvShape<BIAS>::kWaves, kKvThreads = KvShape<BIAS>::kThreads;
@@ -196,6 +226,18 @@ __device__ __forceinline__ void dkdv_body(
   const size_t kbase = (size_t)bh * Nk * D;
   const int nqb_ld = (Nq + BR - 1) / BR;  // blocks per head of the (L2, -D) workspace
   static_assert(BR == kLdRows, "one (L2, -D) block per query block");
+  // DS: this wave's chunk of query block 0 and this lane's two 16-byte slots
+  // in a chunk (elements); query block qb adds qb * ds_row.
+  [[maybe_unused]] T* ds_wave = nullptr;
+  [[maybe_unused]] size_t ds_row = 0;
+  [[maybe_unused]] unsigned ds_lane[2] = {0u, 0u};
+  if constexpr (DS) {
+    static_assert(BIAS == false && BR == 32, "dS chunks: 32 x 32 blocks of the 4-wave shape");
+    ds_row = (size_t)ds_chunks_per_row(Nk) * kDsChunk;
+    ds_wave = dSg + (size_t)bh * nqb_ld * ds_row + (size_t)(kw0 / 32) * kDsChunk;
+    ds_lane[0] = ds_chunk_off(0, half, l32) / 2;
+    ds_lane[1] = ds_chunk_off(1, half, l32) / 2;
+  }
 
   // Additive bias (BIAS) of this head, staged per query block: a tile of
   // BR rows x BC keys per buffer, double-buffered like Q and dO and filled by
@@ -355,8 +397,10 @@ __device__ __forceinline__ void dkdv_body(
     const int qi0 = (qb_first + it) * BR;
     if (it + 1 < nloop) load_block(qb_first + it + 1, 1 - P);
 
-    // Causal: a wave whose keys all lie after every row of the block has no work.
-    const bool wave_idle = CAUSAL && (kw0 > qi0 + BR - 1 + off);
+    // Causal: a wave whose keys all lie after every row of the block has no
+    // work.  (DS: it runs the block all the same, masked to zeros, so that
+    // every wave stores two chunks per block, which the wait below counts.)
+    const bool wave_idle = CAUSAL && !DS && (kw0 > qi0 + BR - 1 + off);
     if (!wave_idle) {
       const T* const tQ = sQ0 + P * QTILE;
       const T* const tdO = sdO0 + P * QTILE;
@@ -514,16 +558,22 @@ __device__ __forceinline__ void dkdv_body(
       };
 #pragma unroll
       for (int i = 0; i < 8; i += 2) pds_ds(i, pds_p(i));
+      T* const ds_blk = DS ? ds_wave + (size_t)(qi0 / BR) * ds_row : nullptr;
+      if constexpr (DS) __builtin_nontemporal_store(dsf[0], (T8*)(ds_blk + ds_lane[0]));
       // The dV/dK MFMAs run at a raised issue priority, so that the two waves
       // of a SIMD (from the two workgroups of a CU) tend to alternate between
       // this phase and the other's S / dP loads and MFMAs (about 2% faster
       // than equal priorities on the long-sequence backward).
       __builtin_amdgcn_s_setprio(1);
       dvdk(0, true);   // probabilities of rows 16..31 overlap the MFMAs of rows 0..15
+      if constexpr (DS) __builtin_nontemporal_store(dsf[1], (T8*)(ds_blk + ds_lane[1]));
       dvdk(1, false);
       __builtin_amdgcn_s_setprio(0);
     }
-    vm_wait_all();  // this wave's part of the next query block has landed
+    // this wave's part of the next query block has landed (DS: the two dS
+    // stores, issued after those loads, may still be in flight)
+    if constexpr (DS) asm volatile("s_waitcnt vmcnt(2)" ::: "memory");
+    else vm_wait_all();
     __syncthreads();
   };
   for (int it = 0; it < nloop; it += 2) {
@@ -553,16 +603,16 @@ __device__ __forceinline__ void dkdv_body(
   }
 }
 
-template <typename T, int D, bool CAUSAL, bool BIAS, bool DROP>
+template <typename T, int D, bool CAUSAL, bool BIAS, bool DROP, bool DS>
 __global__ __launch_bounds__(KvShape<BIAS>::kThreads, KvShape<BIAS>::kPerCU)
 __attribute__((amdgpu_waves_per_eu(2, 2)))
 void bwd_dkdv_kernel(const T* __restrict__ Q, const T* __restrict__ K, const T* __restrict__ V,
                      const T* __restrict__ dO, const float* __restrict__ LD, T* __restrict__ dK,
                      T* __restrict__ dV, int Nq, int Nk, int nkt, int BH, int hpx, float c,
-                     float scale, int off, BiasDev bias, DropDev drop) {
+                     float scale, int off, BiasDev bias, DropDev drop, T* __restrict__ dSg) {
   __shared__ DkdvLds<T, D, BIAS> lds;
-  dkdv_body<T, D, CAUSAL, BIAS, DROP>(Q, K, V, dO, LD, dK, dV, Nq, Nk, nkt, BH, hpx, c, scale,
-                                      off, bias, drop, lds, blockIdx.x);
+  dkdv_body<T, D, CAUSAL, BIAS, DROP, DS>(Q, K, V, dO, LD, dK, dV, Nq, Nk, nkt, BH, hpx, c,
+                                          scale, off, bias, drop, lds, blockIdx.x, dSg);
 }
 
 // ---------------------------------------------------------------------------
@@ -941,6 +991,189 @@ void bwd_dq_kernel(const T* __restrict__ Q, const T* __restrict__ K, const T* __
                                     lds, blockIdx.x, gridDim.x);
 }
 
+// dQ from the stored dS: dQ = scale * dS K, one workgroup per (query tile of
+// 128, batch*head) as in bwd_dq_kernel (causal tiles paired), K tiles and
+// each wave's dS chunks streamed through LDS.  No softmax work remains: per
+// 64-key tile a wave issues 16 (D = 128) or 8 MFMAs, reading K^T and dS^T
+// fragments with transposed LDS reads.
+template <typename T, int D>
+struct DqDsLds {
+  static constexpr int kWaveDs = 2 * kDsChunk;  // elements of a wave's dS per tile
+  __attribute__((aligned(1024))) T smem[2 * kDqBC * D + 2 * (kDqThreads / 64) * kWaveDs];
+};
+
+template <typename T, int D, bool CAUSAL>
+__device__ __forceinline__ void dq_ds_body(const T* __restrict__ K, const T* __restrict__ dSg,
+                                           T* __restrict__ dQ, int Nq, int Nk, int nqt,
+                                           float scale, int off, DqDsLds<T, D>& lds) {
+  typedef typename Vec<T>::x8 T8;
+  typedef typename Vec<T>::x4 T4;
+  constexpr int BR = kDqBR, BC = kDqBC;
+  constexpr int NNT = D / 32;
+  constexpr int TILE = BC * D;
+  constexpr int NW = kDqThreads / 64;
+  constexpr int WDS = DqDsLds<T, D>::kWaveDs;
+  static_assert(BC == 64 && BR == NW * 32, "two dS chunks per wave and key tile");
+  T* const sK0 = lds.smem;             // K tiles, buffers 0/1
+  T* const sD0 = lds.smem + 2 * TILE;  // dS, [buffer][wave][chunk 0/1]
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int half = lane >> 5, l32 = lane & 31;
+  const int g = lane >> 4, s16 = lane & 15;
+
+  const int nwg = CAUSAL ? (nqt + 1) / 2 : nqt;  // workgroups per head
+  const int logical = xcd_remap(blockIdx.x, gridDim.x);
+  const int bh = logical / nwg;
+  const int t = logical - bh * nwg;
+  const T* Kh = K + (size_t)bh * Nk * D;
+  const int nqb = (Nq + 31) / 32;
+  const int cpr = ds_chunks_per_row(Nk);
+
+  using KV = BufTile<D, BC, kDqThreads>;
+  const KV kv(wave, lane);
+
+  // K^T fragments (A operand): step st of half mt reads the 16 keys of chunk
+  // st / NNT of half mt, head-dim tile st % NNT (as in bwd_dq_kernel).
+  unsigned ta[2 * NNT];
+  {
+    const int tr_row = (g >> 1) * 4 + (s16 >> 2);
+    const int tr_col = (g & 1) * 16 + (s16 & 3) * 4;
+    const SwzTr<D> trsw(tr_row, tr_col);
+#pragma unroll
+    for (int hi = 0; hi < 2; ++hi)
+#pragma unroll
+      for (int nt = 0; nt < NNT; ++nt) ta[hi * NNT + nt] = trsw.off(0, hi, nt * 32);
+  }
+  auto kt_frag = [&](int buf, int mt, int st) {
+    const unsigned rb = (mt * 32 + (st / NNT) * 16) * 2 * D;
+    const T* base = sK0 + buf * TILE;
+    return concat(lds_read_tr<T>(to_lds(at_byte<T>(base, ta[st % NNT] + rb))),
+                  lds_read_tr<T>(to_lds(at_byte<T>(base, ta[NNT + st % NNT] + rb))));
+  };
+  // dS^T fragments (B operand): lane l takes row l%32 of the wave's block and
+  // the keys 16h + (e/4)*8 + (l/32)*4 + e%4 of chunk mt.  Each transposed read
+  // has lane 4r + cc of a 16-lane group point at key 4*(g/2) + r (+8 for the
+  // second read) and rows 16*(g%2) + 4cc .. +3 of the chunk, which the slot
+  // layout puts at ds_chunk_off(g%2, cc%2, key) + (cc/2)*8; keys +8 and +16
+  // flip slot bit 3 (byte 128) and add 256 bytes.
+  const int r4 = s16 >> 2, cc = s16 & 3;
+  const unsigned dsa = ds_chunk_off(g & 1, cc & 1, (g >> 1) * 4 + r4) + (unsigned)(cc >> 1) * 8;
+  const unsigned dsb = dsa ^ 128u;
+  auto ds_frag = [&](int buf, int mt, int h) {
+    const T* base = sD0 + (buf * NW + wave) * WDS;
+    const unsigned o = (unsigned)(mt * 2048 + h * 256);
+    return concat(lds_read_tr<T>(to_lds(at_byte<T>(base, dsa + o))),
+                  lds_read_tr<T>(to_lds(at_byte<T>(base, dsb + o))));
+  };
+  constexpr int TRING = 3;
+
+  for (int pass = 0; pass < (CAUSAL ? 2 : 1); ++pass) {
+    const int qt = !CAUSAL ? t : (pass == 0 ? nqt - 1 - t : t);
+    if (CAUSAL && pass == 1 && t == nqt - 1 - t) break;  // odd count: the middle tile once
+    if (pass == 1) __syncthreads();  // the first tile's last LDS reads precede the new loads
+    const int q0 = qt * BR;
+    const int qb = qt * NW + wave;  // this wave's 32-row query block
+    const int wrow_lo = q0 + wave * 32;
+    const int qrow = wrow_lo + l32;
+    // chunks 2j, 2j+1 (4 KB) of the wave's row of dS chunks into buffer buf
+    // (a row past Nq reads as zeros).  The loads are issued from inline
+    // assembly, which the compiler's wait tracking does not see (its own
+    // direct-to-LDS loads made it wait for them before this tile's reads);
+    // the wait at the end of the tile covers them.
+    const i32x4 rdw = rsrc_words(dSg + ((size_t)bh * nqb + min(qb, nqb - 1)) * cpr * kDsChunk,
+                                 qb < nqb ? (unsigned)cpr * kDsChunk * 2 : 0u);
+    auto ds_load = [&](int j, int buf) {
+#pragma unroll
+      for (int u = 0; u < 4; ++u)
+        lds_dma16_asm<true>(rdw, (unsigned)(j * 4096 + u * 1024 + lane * 16),
+                             (const FA_LDS void*)(sD0 + (buf * NW + wave) * WDS + u * 512));
+    };
+
+    const int kend = CAUSAL ? min(Nk, q0 + BR + off) : Nk;
+    const int ntiles = kend > 0 ? (kend + BC - 1) / BC : 0;
+    // Causal: key tiles past the diagonal of this wave's last row hold no
+    // dS for it; after its last useful tile (and at once, for a wave whose
+    // rows all lie past Nq) the wave only takes its part in the K loads and
+    // barriers of the rest.  The dK/dV kernel stores every chunk with a key
+    // visible to a row of its block; of this wave's tiles before jact only
+    // the second chunk of the last may have none (and is then never read).
+    const int jact = qb >= nqb ? 0
+                     : CAUSAL ? min(ntiles, max(wrow_lo + 31 + off, -1) / BC + 1) : ntiles;
+    const bool last_half_live = !CAUSAL || (2 * jact - 1) * 32 <= wrow_lo + 31 + off;
+
+    f32x16 dqacc[NNT];
+#pragma unroll
+    for (int nt = 0; nt < NNT; ++nt) dqacc[nt] = (f32x16){};
+
+    if (ntiles > 0) kv.tile(Kh, 0, Nk, sK0);
+    if (jact > 0) ds_load(0, 0);
+    vm_wait_all();
+    __syncthreads();
+
+    auto tile_step = [&](const int P, int j) __attribute__((always_inline)) {
+      // K tile j+1 and this wave's dS chunks of tile j+1 (past the last
+      // tile: data nobody reads)
+#pragma unroll
+      for (int u = 0; u < KV::PER; ++u) kv.part(Kh, (j + 1) * BC, Nk, sK0 + (1 - P) * TILE, u);
+      ds_load(j + 1, 1 - P);
+#pragma unroll
+      for (int mt = 0; mt < 2; ++mt) {
+        T8 d0 = ds_frag(P, mt, 0), d1 = ds_frag(P, mt, 1);
+        if (mt == 1 && j == jact - 1 && !last_half_live) {
+          d0 = zero8<T8>();
+          d1 = zero8<T8>();
+        }
+        T8 ring[TRING];
+#pragma unroll
+        for (int st = 0; st < TRING; ++st) ring[st] = kt_frag(P, mt, st);
+#pragma unroll
+        for (int st = 0; st < 2 * NNT; ++st) {
+          const T8 a = ring[st % TRING];
+          if (st + TRING < 2 * NNT) ring[st % TRING] = kt_frag(P, mt, st + TRING);
+          dqacc[st % NNT] = mfma32(a, st < NNT ? d0 : d1, dqacc[st % NNT]);
+        }
+      }
+      vm_wait_all();  // this wave's part of tile j+1 has landed
+      __syncthreads();
+    };
+    for (int j = 0; j < jact; j += 2) {
+      tile_step(0, j);
+      if (j + 1 < jact) tile_step(1, j + 1);
+    }
+    for (int j = max(jact, 0); j < ntiles; ++j) {
+      const int P = j & 1;
+#pragma unroll
+      for (int u = 0; u < KV::PER; ++u) kv.part(Kh, (j + 1) * BC, Nk, sK0 + (1 - P) * TILE, u);
+      vm_wait_all();
+      __syncthreads();
+    }
+
+    // Epilogue: dQ = scale * dQ_acc; lane holds row qrow.
+    if (qrow < Nq) {
+      T* out = dQ + ((size_t)bh * Nq + qrow) * D;
+#pragma unroll
+      for (int nt = 0; nt < NNT; ++nt)
+#pragma unroll
+        for (int gg = 0; gg < 4; ++gg) {
+          T4 v;
+#pragma unroll
+          for (int e = 0; e < 4; ++e) v[e] = (T)(dqacc[nt][gg * 4 + e] * scale);
+          *(T4*)(out + nt * 32 + gg * 8 + half * 4) = v;
+        }
+    }
+  }
+}
+
+template <typename T, int D, bool CAUSAL>
+__global__ __launch_bounds__(kDqThreads, 2) __attribute__((amdgpu_waves_per_eu(2, 2)))
+void bwd_dq_ds_kernel(const T* __restrict__ K, const T* __restrict__ dSg, T* __restrict__ dQ,
+                      int Nq, int Nk, int nqt, float scale, int off) {
+  __shared__ DqDsLds<T, D> lds;
+  dq_ds_body<T, D, CAUSAL>(K, dSg, dQ, Nq, Nk, nqt, scale, off, lds);
+}
+
 // dK/dV and dQ in one launch (no bias: both then run 256-thread workgroups,
 // two per CU), sharing one LDS allocation.  Workgroups start in block order,
 // and both grids already list their workgroups longest first, so the launch
@@ -1163,6 +1396,43 @@ hipError_t launch_bwd_mfma(const BwdArgs& a, int stages, hipStream_t s) {
     if (e != hipSuccess) return e;
   }
   if constexpr (!BIAS) {
+    if (a.dS != nullptr) {
+      // stored dS (set only with Nq, Nk > 0): dK/dV writes dS, dQ = scale *
+      // dS K reads it (stage 4 needs stage 2 to have run on the same workspace)
+      T* const dS = (T*)a.dS;
+      if ((stages & 2) && a.Nk > 0 && a.Nq > 0) {
+        constexpr int kKvBC = KvShape<false>::kBC;
+        const int nkt = (a.Nk + kKvBC - 1) / kKvBC;
+        const int hpx = (BH % kNumXcd == 0) ? BH / kNumXcd : 0;
+#define FA_DKDV_DS_LAUNCH(DD, CC)                                                              \
+  hipLaunchKernelGGL((bwd_dkdv_kernel<T, DD, CC, false, DROP, true>), dim3(nkt * BH),           \
+                     dim3(KvShape<false>::kThreads), 0, s, Q, K, V, dO, a.LD, (T*)a.dK,        \
+                     (T*)a.dV, a.Nq, a.Nk, nkt, BH, hpx, c, a.scale, off, bias, drop, dS)
+        if (a.d == 128) {
+          if (a.causal) FA_DKDV_DS_LAUNCH(128, true); else FA_DKDV_DS_LAUNCH(128, false);
+        } else {
+          if (a.causal) FA_DKDV_DS_LAUNCH(64, true); else FA_DKDV_DS_LAUNCH(64, false);
+        }
+#undef FA_DKDV_DS_LAUNCH
+        const hipError_t e = hipGetLastError();
+        if (e != hipSuccess) return e;
+      }
+      if ((stages & 4) && a.Nq > 0) {
+        const int nqt = (a.Nq + kDqBR - 1) / kDqBR;
+        const int nblocks = (a.causal ? (nqt + 1) / 2 : nqt) * BH;
+#define FA_DQ_DS_LAUNCH(DD, CC)                                                                \
+  hipLaunchKernelGGL((bwd_dq_ds_kernel<T, DD, CC>), dim3(nblocks), dim3(kDqThreads), 0, s, K, \
+                     (const T*)dS, (T*)a.dQ, a.Nq, a.Nk, nqt, a.scale, off)
+        if (a.d == 128) {
+          if (a.causal) FA_DQ_DS_LAUNCH(128, true); else FA_DQ_DS_LAUNCH(128, false);
+        } else {
+          if (a.causal) FA_DQ_DS_LAUNCH(64, true); else FA_DQ_DS_LAUNCH(64, false);
+        }
+#undef FA_DQ_DS_LAUNCH
+        return hipGetLastError();
+      }
+      return hipSuccess;
+    }
     if ((stages & 6) == 6 && a.Nk > 0 && a.Nq > 0) {
       constexpr int kKvBC = KvShape<false>::kBC;
       const int nkt = (a.Nk + kKvBC - 1) / kKvBC;
@@ -1191,10 +1461,10 @@ hipError_t launch_bwd_mfma(const BwdArgs& a, int stages, hipStream_t s) {
     const int nblocks = nkt * BH;
     const int hpx = (BH % kNumXcd == 0) ? BH / kNumXcd : 0;
 #define FA_DKDV_LAUNCH(DD, CC)                                                                 \
-  hipLaunchKernelGGL((bwd_dkdv_kernel<T, DD, CC, BIAS, DROP>), dim3(nblocks),                    \
+  hipLaunchKernelGGL((bwd_dkdv_kernel<T, DD, CC, BIAS, DROP, false>), dim3(nblocks),             \
                      dim3(KvShape<BIAS>::kThreads),                                             \
                      0, s, Q, K, V, dO, a.LD, (T*)a.dK, (T*)a.dV, a.Nq, a.Nk, nkt, BH, hpx, c,  \
-                     a.scale, off, bias, drop)
+                     a.scale, off, bias, drop, nullptr)
     if (a.d == 128) {
       if (a.causal) FA_DKDV_LAUNCH(128, true); else FA_DKDV_LAUNCH(128, false);
     } else {
@@ -1231,6 +1501,10 @@ hipError_t launch_bwd_typed(const BwdArgs& a, int stages, hipStream_t s) {
 }
 
 }  // namespace
+
+size_t bwd_ds_bytes(int BH, int Nq, int Nk) {
+  return (size_t)BH * ((Nq + 31) / 32) * ds_chunks_per_row(Nk) * kDsChunk * 2;
+}
 
 hipError_t launch_bwd_bf16(const BwdArgs& a, int stages, hipStream_t s) {
   return launch_bwd_typed<bf16>(a, stages, s);

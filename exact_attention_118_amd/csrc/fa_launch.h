@@ -59,7 +59,14 @@ struct BwdArgs {
   float* LD;  // fp32 workspace: per head and block of 32 query rows, L * log2(e) and -D, D = rowsum(dO * O)
   BiasArgs bias;
   DropArgs drop;
+  // 16-bit dtypes without a bias: the dS buffer (bwd_ds_bytes) when the
+  // backward stores dS in the dK/dV kernel and forms dQ from it; nullptr:
+  // the dQ kernel recomputes S and dP instead.
+  void* dS = nullptr;
 };
+
+// Bytes of the dS buffer of the stored-dS backward for B*H heads.
+size_t bwd_ds_bytes(int BH, int Nq, int Nk);
 
 // Tiled forward (Q-tile per workgroup, K/V streamed through LDS).
 hipError_t launch_fwd_bf16(const FwdArgs& a, hipStream_t s);

@@ -100,10 +100,19 @@ fa_status fa_fwd(const void* Q, const void* K, const void* V, void* O, float* L,
  *  aligned, written by the first stage: per head and block of 32 query rows
  *  64 fp32, the rows' L*log2(e) and -D, D = rowsum(dO * O) (rows past Nq
  *  zero), laid out for the kernels that read them (by row pair with dropout,
- *  as two runs of 32 without).  dK and dV are computed per key block and dQ
- *  per query block by workgroups that recompute P and dP for their rows, so
- *  there are no atomic operations and every output is deterministic.  Both
- *  kinds of workgroup run in one launch after the preprocess launch.
+ *  as two runs of 32 without).  dK and dV are computed per key block by
+ *  workgroups that recompute P and dP for their rows.  dQ comes one of two
+ *  ways, with no atomic operations either way, so every output is
+ *  deterministic:
+ *   - stored dS (bf16 and fp16, d = 128, Nq and Nk >= 2048, no bias, a dS
+ *     buffer of at most 8 GiB): the dK/dV workgroups also store dS, in a
+ *     buffer after the per-row block (2 bytes per query-key pair, padded to
+ *     32 x 32 blocks: B*H*ceil(Nq/32)*ceil(Nk/128)*8 KiB), and a second
+ *     launch forms dQ = scale * dS K from it: the five GEMMs per tile pair
+ *     of the 51CTO notes ("FlashAttention V2相比V1有哪些改进");
+ *   - otherwise, workgroups per query block recompute P and dP for their
+ *     rows and accumulate dQ in registers, in one launch with the dK/dV
+ *     workgroups (seven GEMMs; faster at d = 64 and on short sequences).
  */
 fa_status fa_bwd(const void* Q, const void* K, const void* V, const void* O, const float* L,
                  const void* dO, void* dQ, void* dK, void* dV,
@@ -117,9 +126,10 @@ fa_status fa_bwd(const void* Q, const void* K, const void* V, const void* O, con
  *   FA_BWD_DKDV       (2): dK and dV written (reads the workspace);
  *   FA_BWD_DQ         (4): dQ written (reads the workspace).
  * fa_bwd(...) is fa_bwd_stages(..., FA_BWD_ALL).  Stages 2 and 4 need stage 1
- * to have run on the same workspace; a mask of 0 or above 7 returns
+ * to have run on the same workspace, and on the stored-dS path stage 4 reads
+ * the dS that stage 2 stored there; a mask of 0 or above 7 returns
  * FA_ERR_UNSUPPORTED.  Stages 2 and 4 in one mask run as one launch (as two
- * with a bias); the results are the same bit for bit either way.
+ * with a bias or stored dS); the results are the same bit for bit either way.
  */
 enum { FA_BWD_PREPROCESS = 1, FA_BWD_DKDV = 2, FA_BWD_DQ = 4, FA_BWD_ALL = 7 };
 fa_status fa_bwd_stages(const void* Q, const void* K, const void* V, const void* O,
@@ -140,6 +150,8 @@ fa_status fa_bwd_stages(const void* Q, const void* K, const void* V, const void*
  * allocates or frees memory.  Calls on one GPU share the array, so calls
  * that overlap on one GPU (different streams, or threads) race: serialise
  * them.  Every row the kernels read is written earlier in the same call.
+ * dQ is always recomputed (no dS buffer): where fa_bwd takes the stored-dS
+ * path, dQ may differ from its result in the last bits (dK and dV do not).
  */
 fa_status fa_bwd_noalloc(const void* Q, const void* K, const void* V, const void* O,
                          const float* L, const void* dO, void* dQ, void* dK, void* dV,
@@ -254,8 +266,14 @@ fa_status fa_bias_tile_map(const void* bias, long long bias_sb, long long bias_s
 /* Workspace bytes fa_fwd needs for these arguments (0 when none). */
 size_t fa_fwd_workspace_size(int B, int H, int Nq, int Nk, int d, fa_dtype dtype, int num_splits);
 
-/* Workspace bytes fa_bwd needs for these arguments. */
+/* Workspace bytes fa_bwd needs for these arguments, with the dS buffer where
+ * the stored-dS path runs (see fa_bwd); enough for fa_bwd_stages, fa_bwd_ex
+ * and fa_bwd_bias with the same sizes. */
 size_t fa_bwd_workspace_size(int B, int H, int Nq, int Nk, int d, fa_dtype dtype);
+
+/* Workspace bytes fa_bwd_bias, and fa_bwd_ex with a bias, need: the per-row
+ * block only (with a bias dQ is always recomputed).  0 for invalid sizes. */
+size_t fa_bwd_bias_workspace_size(int B, int H, int Nq, int Nk, int d, fa_dtype dtype);
 
 /* Number of key splits fa_fwd uses for these arguments (1 on the tiled path). */
 int fa_fwd_num_splits(int B, int H, int Nq, int Nk, int d, fa_dtype dtype, int num_splits);

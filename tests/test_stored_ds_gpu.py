@@ -1,0 +1,87 @@
+"""The stored-dS backward (bf16/fp16, d = 128, Nq and Nk >= 2048, no bias).
+
+There the dK/dV kernel stores dS in the workspace and dQ = scale * dS K is
+formed from it; elsewhere a dQ kernel recomputes S and dP.  These tests run
+shapes above the threshold with ragged tails and bottom-right causal offsets
+against the float64 oracle, and compare the path with the recomputing one
+(fa_bwd_noalloc always recomputes): dK and dV come from the same arithmetic
+and must agree bit for bit; dQ may differ where a dS element rounds the other
+way to 16 bits, so the two are held to one rounding of dQ to bf16 (relative
+L2 2^-8) apart.
+"""
+
+import math
+
+import pytest
+import torch
+
+import oracle
+
+from test_parity_gpu import f64, make, rel_l2, say, tolerances
+
+pytestmark = pytest.mark.gpu
+
+CASES = [
+    # B, H, Nq, Nk, causal, dtype
+    (1, 2, 2080, 2200, True, torch.bfloat16),    # bottom-right causal, ragged, Nq < Nk
+    (1, 2, 2200, 2080, False, torch.bfloat16),   # Nq > Nk, ragged
+    (2, 1, 2048, 2048, True, torch.bfloat16),    # exact tiles
+    (1, 2, 2111, 2111, True, torch.float16),
+    (1, 1, 2048, 2300, False, torch.float16),
+]
+
+
+def _id(c):
+    B, H, Nq, Nk, causal, dt = c
+    return f"b{B}h{H}q{Nq}k{Nk}{'c' if causal else ''}-{str(dt).split('.')[-1]}"
+
+
+def _linear_ws(B, H, Nq):
+    return ((B * H * ((Nq + 31) // 32) * 32 * 2 * 4) + 255) // 256 * 256
+
+
+@pytest.mark.parametrize("case", CASES, ids=_id)
+def test_stored_ds_backward_against_the_oracle(gpu_lib, case):
+    fa = gpu_lib
+    B, H, Nq, Nk, causal, dt = case
+    d = 128
+    say(f"stored-dS backward {_id(case)}")
+    code = fa.FA_BF16 if dt == torch.bfloat16 else fa.FA_FP16
+    # the workspace query includes the dS buffer: the path runs
+    assert fa.bwd_workspace_size(B, H, Nq, Nk, d, code) > _linear_ws(B, H, Nq)
+    x = make(B, H, Nq, Nk, d, dt, seed=21)
+    scale = 1.0 / math.sqrt(d)
+    O, L = fa.forward(x["Q"], x["K"], x["V"], scale, causal)
+    dQ, dK, dV = fa.backward(x["Q"], x["K"], x["V"], O, L, x["dO"], scale, causal)
+    torch.cuda.synchronize()
+    ref = oracle.attention_backward_batched(f64(x["Q"]), f64(x["K"]), f64(x["V"]), f64(x["dO"]),
+                                            scale, causal)
+    _, _, tg = tolerances(dt)
+    for name, got, want in zip(("dQ", "dK", "dV"), (dQ, dK, dV), ref):
+        assert rel_l2(f64(got), want) <= tg, name
+
+
+@pytest.mark.parametrize("causal", [True, False])
+def test_stored_ds_matches_the_recomputing_path(gpu_lib, causal):
+    fa = gpu_lib
+    B, H, N, d = 1, 4, 2304, 128
+    say(f"stored dS against recomputation b{B}h{H}n{N} causal={causal}")
+    x = make(B, H, N, N, d, torch.bfloat16, seed=22)
+    scale = 1.0 / math.sqrt(d)
+    O, L = fa.forward(x["Q"], x["K"], x["V"], scale, causal)
+    ds = fa.backward(x["Q"], x["K"], x["V"], O, L, x["dO"], scale, causal)
+    rc = [torch.full_like(t, float("nan")) for t in ds]
+    fa.fa_bwd_noalloc(x["Q"], x["K"], x["V"], O, L, x["dO"], *rc, scale, causal)
+    torch.cuda.synchronize()
+    assert torch.equal(ds[1], rc[1]) and torch.equal(ds[2], rc[2])
+    assert rel_l2(f64(ds[0]), f64(rc[0])) <= 2.0 ** -8
+    # the stages of the stored-dS path give the same bits run one by one
+    st = [torch.full_like(t, float("nan")) for t in ds]
+    ws = torch.empty(fa.bwd_workspace_size(B, H, N, N, d, fa.FA_BF16), dtype=torch.uint8,
+                     device="cuda")
+    for stage in (fa.FA_BWD_PREPROCESS, fa.FA_BWD_DKDV, fa.FA_BWD_DQ):
+        fa.fa_bwd(x["Q"], x["K"], x["V"], O, L, x["dO"], *st, scale, causal,
+                  workspace=ws, stages=stage)
+    torch.cuda.synchronize()
+    for a, b in zip(st, ds):
+        assert torch.equal(a, b)

@@ -1,7 +1,8 @@
 """fa_bwd_noalloc (the backward pass without a caller workspace) against fa_bwd.
 
-Both run the same kernels; the allocation-free entry point keeps the per-row
-L*log2(e) and -D in the library's scratch array.  Two calls in a row, the
+At these sizes (below those where fa_bwd stores dS, which the allocation-free
+entry point never does) both run the same kernels; the allocation-free entry
+point keeps the per-row L*log2(e) and -D in the library's scratch array.  Two calls in a row, the
 second on a smaller problem, must each equal fa_bwd bit for bit (the array
 keeps the first call's rows; nothing of them may leak into the second).
 """
