@@ -33,11 +33,13 @@ def _capture(fn):
     return g, out
 
 
-@pytest.mark.parametrize("variant", ["plain", "dropout", "bias_map", "decode"])
+@pytest.mark.parametrize("variant", ["plain", "dropout", "bias_map", "decode", "stored_ds"])
 def test_graph_replays_match_eager(gpu_lib, variant):
     fa = gpu_lib
     say(f"graph capture {variant}")
-    B, H, Nq, Nk, d = (16, 8, 1, 4096, 128) if variant == "decode" else (2, 4, 500, 500, 128)
+    B, H, Nq, Nk, d = {"decode": (16, 8, 1, 4096, 128),
+                       # long enough for the backward to store dS (three launches)
+                       "stored_ds": (1, 2, 2048, 2048, 128)}.get(variant, (2, 4, 500, 500, 128))
     causal = variant != "decode"
     scale = 1.0 / math.sqrt(d)
     x = make(B, H, Nq, Nk, d, torch.bfloat16, seed=31)

@@ -1,7 +1,8 @@
 """Calls enqueued on a side stream (the `stream` argument of the binding).
 
 The workspaces the binding allocates for such a call (split-path partials,
-the backward pass's per-row pairs) must stay reserved for that stream until
+the backward pass's per-row pairs and, from 2048 rows and keys at d = 128, its
+stored dS) must stay reserved for that stream until
 its kernels have used them; the results are checked against the float64
 oracle after synchronising.  Other allocations on the current stream run in
 between, so a workspace handed to them too early would be overwritten.
@@ -31,12 +32,17 @@ def test_side_stream_split_forward_and_backward(gpu_lib):
                             seed=21, device="cpu")
     x = synth.make_inputs(synth.Workload("bwd", 2, 4, 700, 700, 128, True, torch.bfloat16),
                           seed=22, device="cpu")
+    # long enough for the backward to store dS in its workspace
+    y = synth.make_inputs(synth.Workload("bwd_ds", 1, 2, 2048, 2048, 128, True, torch.bfloat16),
+                          seed=23, device="cpu")
     dec = {k: v.cuda() for k, v in dec.items()}
     x = {k: v.cuda() for k, v in x.items()}
+    y = {k: v.cuda() for k, v in y.items()}
     side = torch.cuda.Stream()
     side.wait_stream(torch.cuda.current_stream())
     with torch.cuda.stream(side):
         O0, L0 = fa.forward(x["Q"], x["K"], x["V"], scale, True)
+        O1, L1 = fa.forward(y["Q"], y["K"], y["V"], scale, True)
     side.synchronize()
     outs = []
     for _ in range(3):
@@ -47,16 +53,21 @@ def test_side_stream_split_forward_and_backward(gpu_lib):
             torch.cuda._sleep(20_000_000)
         Od, Ld = fa.forward(dec["Q"], dec["K"], dec["V"], scale, False, num_splits=3, stream=side)
         g = fa.backward(x["Q"], x["K"], x["V"], O0, L0, x["dO"], scale, True, stream=side)
+        g1 = fa.backward(y["Q"], y["K"], y["V"], O1, L1, y["dO"], scale, True, stream=side)
         junk = [torch.full((1 << 20,), 7.0, device="cuda") for _ in range(32)]
-        outs.append((Od, Ld, g))
+        outs.append((Od, Ld, g, g1))
         del busy, junk
     side.synchronize()
     torch.cuda.synchronize()
     Or, Lr = oracle.attention_forward_batched(f64(dec["Q"]), f64(dec["K"]), f64(dec["V"]), scale, False)
     ref = oracle.attention_backward_batched(f64(x["Q"]), f64(x["K"]), f64(x["V"]), f64(x["dO"]),
                                             scale, True)
-    for Od, Ld, g in outs:
+    ref1 = oracle.attention_backward_batched(f64(y["Q"]), f64(y["K"]), f64(y["V"]), f64(y["dO"]),
+                                             scale, True)
+    for Od, Ld, g, g1 in outs:
         assert float(np.max(np.abs(f64(Od) - Or))) <= 2e-2
         assert float(np.max(np.abs(f64(Ld) - Lr))) <= 1e-3
         for got, want in zip(g, ref):
+            assert np.linalg.norm(f64(got) - want) / np.linalg.norm(want) <= 1e-2
+        for got, want in zip(g1, ref1):
             assert np.linalg.norm(f64(got) - want) / np.linalg.norm(want) <= 1e-2
