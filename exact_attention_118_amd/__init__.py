@@ -29,8 +29,7 @@ FA_BWD_PREPROCESS, FA_BWD_DKDV, FA_BWD_DQ, FA_BWD_ALL = 1, 2, 4, 7
 
 EXPORTED_SYMBOLS = ("fa_fwd", "fa_bwd", "fa_bwd_stages", "fa_fwd_bias", "fa_bwd_bias",
                     "fa_fwd_ex", "fa_bwd_ex", "fa_bias_tile_map", "fa_bias_tile_map_size",
-                    "fa_fwd_workspace_size", "fa_bwd_workspace_size",
-                    "fa_bwd_bias_workspace_size", "fa_fwd_num_splits",
+                    "fa_fwd_workspace_size", "fa_bwd_workspace_size", "fa_fwd_num_splits",
                     "fa_status_string", "fa_version", "fa_bwd_noalloc", "fa_bwd_noalloc_max_rows")
 
 _LIB = None
@@ -87,8 +86,6 @@ def load_library():
     lib.fa_fwd_workspace_size.restype = sz
     lib.fa_bwd_workspace_size.argtypes = [i, i, i, i, i, i]
     lib.fa_bwd_workspace_size.restype = sz
-    lib.fa_bwd_bias_workspace_size.argtypes = [i, i, i, i, i, i]
-    lib.fa_bwd_bias_workspace_size.restype = sz
     lib.fa_fwd_num_splits.argtypes = [i, i, i, i, i, i, i]
     lib.fa_fwd_num_splits.restype = i
     lib.fa_status_string.argtypes = [i]
@@ -329,7 +326,7 @@ def fa_bwd_bias(Q, K, V, bias, O, L, dO, dQ, dK, dV, scale, causal, workspace=No
     _check_tensor("L", L, (B, H, Nq), _torch().float32, dev)
     sb, sh, sq = _bias_strides(bias, B, H, Nq, Nk, Q.dtype, dev)
     code = _dtype_code(Q)
-    need = lib.fa_bwd_bias_workspace_size(B, H, Nq, Nk, d, code)
+    need = lib.fa_bwd_workspace_size(B, H, Nq, Nk, d, code)
     if workspace is None:
         workspace = _alloc_workspace(need, dev, stream)
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
@@ -412,8 +409,7 @@ def fa_bwd_ex(Q, K, V, O, L, dO, dQ, dK, dV, scale, causal, bias=None, dropout_p
     sb, sh, sq = (0, 0, 0) if bias is None else _bias_strides(bias, B, H, Nq, Nk, Q.dtype, dev)
     map_ptr, map_bytes = _tile_map_arg(lib, tile_map, bias, sb, sh, B, H, Nq, Nk, dev)
     code = _dtype_code(Q)
-    need = (lib.fa_bwd_workspace_size if bias is None else lib.fa_bwd_bias_workspace_size)(
-        B, H, Nq, Nk, d, code)
+    need = lib.fa_bwd_workspace_size(B, H, Nq, Nk, d, code)
     if workspace is None:
         workspace = _alloc_workspace(need, dev, stream)
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()

@@ -121,10 +121,12 @@ size_t bwd_ws_bytes(int BH, int Nq) {
 // the dK/dV kernel stores dS and dQ = dS K reads it, instead of a dQ kernel
 // that recomputes S and dP (two of its three GEMMs).  The buffer holds 2
 // bytes per (query, key) pair, padded to 32 x 32 blocks, so it grows with
-// Nq * Nk.  The path runs for bf16 and fp16 at d = 128, without a bias, with
-// Nq and Nk of at least kDsMinLen and a buffer of at most kDsMaxBytes.
-// Measured against recomputation (same process, steady state): 4-9% faster
-// at d = 128 for N = 2048-8192; slower at d = 64, where the recomputed GEMMs
+// Nq * Nk.  The path runs for bf16 and fp16 at d = 128, with or without a
+// bias, with Nq and Nk of at least kDsMinLen and a buffer of at most
+// kDsMaxBytes.  Measured against recomputation (same process): 4-9% faster
+// at d = 128 for N = 2048-8192 (steady state), 6-12% with a dense bias
+// (single calls: its dQ kernel no longer reads the bias); slower at d = 64,
+// where the recomputed GEMMs
 // cost half as much and the dS traffic the same, and on short sequences,
 // where the fused recomputing launch runs dQ beside the key blocks' chains.
 constexpr size_t kDsMaxBytes = size_t(8) << 30;
@@ -199,11 +201,6 @@ size_t fa_fwd_workspace_size(int B, int H, int Nq, int Nk, int d, fa_dtype dtype
 size_t fa_bwd_workspace_size(int B, int H, int Nq, int Nk, int d, fa_dtype dtype) {
   if (check_dims(B, H, Nq, Nk, d, 1.f, 0, dtype) != FA_OK) return 0;
   return bwd_ws_bytes(B * H, Nq) + bwd_ds_ws_bytes(B * H, Nq, Nk, d, dtype);
-}
-
-size_t fa_bwd_bias_workspace_size(int B, int H, int Nq, int Nk, int d, fa_dtype dtype) {
-  if (check_dims(B, H, Nq, Nk, d, 1.f, 0, dtype) != FA_OK) return 0;
-  return bwd_ws_bytes(B * H, Nq);
 }
 
 }  // extern "C"
@@ -337,9 +334,9 @@ fa_status bwd_impl(const void* Q, const void* K, const void* V, const fa::BiasAr
   if (!aligned(K) || !aligned(V) || !aligned(dK) || !aligned(dV)) return FA_ERR_ALIGN;
   if (Nq > 0 && (!aligned(Q) || !aligned(O) || !aligned(L) || !aligned(dO) || !aligned(dQ)))
     return FA_ERR_ALIGN;
-  // stored dS without a bias, when its buffer is within the limit
+  // stored dS, where it runs (not for fa_bwd_noalloc)
   const size_t ws_ld = bwd_ws_bytes(B * H, Nq);
-  const size_t ws_ds = (allow_ds && !bias.ptr) ? bwd_ds_ws_bytes(B * H, Nq, Nk, d, dtype) : 0;
+  const size_t ws_ds = allow_ds ? bwd_ds_ws_bytes(B * H, Nq, Nk, d, dtype) : 0;
   if (Nq > 0 && (!workspace || workspace_bytes < ws_ld + ws_ds)) return FA_ERR_WORKSPACE;
   if (Nq > 0 && !aligned(workspace)) return FA_ERR_ALIGN;
   fa::BwdArgs a{Q, K, V, O, L, dO, dQ, dK, dV, B, H, Nq, Nk, d, scale, causal != 0,

@@ -100,8 +100,9 @@ constexpr int ld_nd_off() { return DROP ? 1 : kLdRows; }
 
 // dS buffer of the stored-dS backward (dK/dV kernel writes, dQ kernel reads):
 // per head and 32-row query block, one 2 KB chunk per group of 32 keys (the
-// keys of one dK/dV wave), 4 groups per 128-key block; the chunks of a query
-// block are consecutive.  A chunk holds the 16-bit dS of its 32 x 32 block as
+// keys of one dK/dV wave), 8 groups per 256 keys (keys padded to 256, which
+// covers both the 128-key and, with a bias, the 256-key dK/dV workgroups);
+// the chunks of a query block are consecutive.  A chunk holds the 16-bit dS of its 32 x 32 block as
 // 64 16-byte slots: slot (kc, h, k) has the dS of key k of the group for the
 // rows kc*16 + (e/4)*8 + h*4 + e%4 of the block (e = 0..7, one element each),
 // i.e. what lane h*32 + k of the dK/dV wave holds as the MFMA operand of row
@@ -109,7 +110,7 @@ constexpr int ld_nd_off() { return DROP ? 1 : kLdRows; }
 // each dK/dV store fills 1 KB in one piece, and the XOR spreads the dQ
 // kernel's transposed reads of a chunk over all LDS banks.
 constexpr int kDsChunk = 1024;  // elements per chunk
-__host__ __device__ __forceinline__ int ds_chunks_per_row(int Nk) { return ((Nk + 127) / 128) * 4; }
+__host__ __device__ __forceinline__ int ds_chunks_per_row(int Nk) { return ((Nk + 255) / 256) * 8; }
 __host__ __device__ __forceinline__ unsigned ds_chunk_off(int kc, int h, int k) {
   return (unsigned)(kc * 1024 + h * 512 + ((k ^ (4 * (2 * kc + h))) * 16));
 }
@@ -232,7 +233,7 @@ __device__ __forceinline__ void dkdv_body(
   [[maybe_unused]] size_t ds_row = 0;
   [[maybe_unused]] unsigned ds_lane[2] = {0u, 0u};
   if constexpr (DS) {
-    static_assert(BIAS == false && BR == 32, "dS chunks: 32 x 32 blocks of the 4-wave shape");
+    static_assert(BR == 32, "dS chunks: 32 x 32 blocks");
     ds_row = (size_t)ds_chunks_per_row(Nk) * kDsChunk;
     ds_wave = dSg + (size_t)bh * nqb_ld * ds_row + (size_t)(kw0 / 32) * kDsChunk;
     ds_lane[0] = ds_chunk_off(0, half, l32) / 2;
@@ -1005,7 +1006,8 @@ struct DqDsLds {
 template <typename T, int D, bool CAUSAL>
 __device__ __forceinline__ void dq_ds_body(const T* __restrict__ K, const T* __restrict__ dSg,
                                            T* __restrict__ dQ, int Nq, int Nk, int nqt,
-                                           float scale, int off, DqDsLds<T, D>& lds) {
+                                           float scale, int off, BiasDev bias,
+                                           DqDsLds<T, D>& lds) {
   typedef typename Vec<T>::x8 T8;
   typedef typename Vec<T>::x4 T4;
   constexpr int BR = kDqBR, BC = kDqBC;
@@ -1092,7 +1094,24 @@ __device__ __forceinline__ void dq_ds_body(const T* __restrict__ K, const T* __r
     };
 
     const int kend = CAUSAL ? min(Nk, q0 + BR + off) : Nk;
-    const int ntiles = kend > 0 ? (kend + BC - 1) / BC : 0;
+    int ntiles = kend > 0 ? (kend + BC - 1) / BC : 0;
+    // Bias tile map: only the key tiles from the first to the last active one
+    // of this query tile (jbeg even, so tile j keeps K buffer j & 1); an
+    // inactive tile inside holds no stored dS and contributes zeros.
+    int jbeg = 0;
+    const unsigned char* mrow = nullptr;
+    if (bias.tmap) {
+      const int b = bh / bias.H, h = bh - b * bias.H;
+      mrow = bias.tmap + b * bias.tm_sb + h * bias.tm_sh + (size_t)qt * bias.nkt4;
+      int lo, hi;
+      map_range(mrow, (Nk + BC - 1) / BC, lane, lo, hi);
+      if (lo > hi) {
+        ntiles = 0;
+      } else {
+        jbeg = lo & ~1;
+        ntiles = min(ntiles, hi + 1);
+      }
+    }
     // Causal: key tiles past the diagonal of this wave's last row hold no
     // dS for it; after its last useful tile (and at once, for a wave whose
     // rows all lie past Nq) the wave only takes its part in the K loads and
@@ -1107,8 +1126,8 @@ __device__ __forceinline__ void dq_ds_body(const T* __restrict__ K, const T* __r
 #pragma unroll
     for (int nt = 0; nt < NNT; ++nt) dqacc[nt] = (f32x16){};
 
-    if (ntiles > 0) kv.tile(Kh, 0, Nk, sK0);
-    if (jact > 0) ds_load(0, 0);
+    if (ntiles > jbeg) kv.tile(Kh, jbeg * BC, Nk, sK0);
+    if (jact > jbeg) ds_load(jbeg, 0);
     vm_wait_all();
     __syncthreads();
 
@@ -1118,10 +1137,11 @@ __device__ __forceinline__ void dq_ds_body(const T* __restrict__ K, const T* __r
 #pragma unroll
       for (int u = 0; u < KV::PER; ++u) kv.part(Kh, (j + 1) * BC, Nk, sK0 + (1 - P) * TILE, u);
       ds_load(j + 1, 1 - P);
+      const bool tile_on = !mrow || mrow[j] != 0;
 #pragma unroll
       for (int mt = 0; mt < 2; ++mt) {
         T8 d0 = ds_frag(P, mt, 0), d1 = ds_frag(P, mt, 1);
-        if (mt == 1 && j == jact - 1 && !last_half_live) {
+        if (!tile_on || (mt == 1 && j == jact - 1 && !last_half_live)) {
           d0 = zero8<T8>();
           d1 = zero8<T8>();
         }
@@ -1138,11 +1158,11 @@ __device__ __forceinline__ void dq_ds_body(const T* __restrict__ K, const T* __r
       vm_wait_all();  // this wave's part of tile j+1 has landed
       __syncthreads();
     };
-    for (int j = 0; j < jact; j += 2) {
+    for (int j = jbeg; j < jact; j += 2) {
       tile_step(0, j);
       if (j + 1 < jact) tile_step(1, j + 1);
     }
-    for (int j = max(jact, 0); j < ntiles; ++j) {
+    for (int j = max(jact, jbeg); j < ntiles; ++j) {
       const int P = j & 1;
 #pragma unroll
       for (int u = 0; u < KV::PER; ++u) kv.part(Kh, (j + 1) * BC, Nk, sK0 + (1 - P) * TILE, u);
@@ -1169,9 +1189,9 @@ __device__ __forceinline__ void dq_ds_body(const T* __restrict__ K, const T* __r
 template <typename T, int D, bool CAUSAL>
 __global__ __launch_bounds__(kDqThreads, 2) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void bwd_dq_ds_kernel(const T* __restrict__ K, const T* __restrict__ dSg, T* __restrict__ dQ,
-                      int Nq, int Nk, int nqt, float scale, int off) {
+                      int Nq, int Nk, int nqt, float scale, int off, BiasDev bias) {
   __shared__ DqDsLds<T, D> lds;
-  dq_ds_body<T, D, CAUSAL>(K, dSg, dQ, Nq, Nk, nqt, scale, off, lds);
+  dq_ds_body<T, D, CAUSAL>(K, dSg, dQ, Nq, Nk, nqt, scale, off, bias, lds);
 }
 
 // dK/dV and dQ in one launch (no bias: both then run 256-thread workgroups,
@@ -1395,44 +1415,44 @@ hipError_t launch_bwd_mfma(const BwdArgs& a, int stages, hipStream_t s) {
     const hipError_t e = (a.d == 128) ? launch_pre<128, T>(a, s) : launch_pre<64, T>(a, s);
     if (e != hipSuccess) return e;
   }
-  if constexpr (!BIAS) {
-    if (a.dS != nullptr) {
-      // stored dS (set only with Nq, Nk > 0): dK/dV writes dS, dQ = scale *
-      // dS K reads it (stage 4 needs stage 2 to have run on the same workspace)
-      T* const dS = (T*)a.dS;
-      if ((stages & 2) && a.Nk > 0 && a.Nq > 0) {
-        constexpr int kKvBC = KvShape<false>::kBC;
-        const int nkt = (a.Nk + kKvBC - 1) / kKvBC;
-        const int hpx = (BH % kNumXcd == 0) ? BH / kNumXcd : 0;
+  if (a.dS != nullptr) {
+    // stored dS (set only with Nq, Nk > 0): dK/dV writes dS, dQ = scale *
+    // dS K reads it (stage 4 needs stage 2 to have run on the same workspace)
+    T* const dS = (T*)a.dS;
+    if ((stages & 2) && a.Nk > 0 && a.Nq > 0) {
+      constexpr int kKvBC = KvShape<BIAS>::kBC;
+      const int nkt = (a.Nk + kKvBC - 1) / kKvBC;
+      const int hpx = (BH % kNumXcd == 0) ? BH / kNumXcd : 0;
 #define FA_DKDV_DS_LAUNCH(DD, CC)                                                              \
-  hipLaunchKernelGGL((bwd_dkdv_kernel<T, DD, CC, false, DROP, true>), dim3(nkt * BH),           \
-                     dim3(KvShape<false>::kThreads), 0, s, Q, K, V, dO, a.LD, (T*)a.dK,        \
+  hipLaunchKernelGGL((bwd_dkdv_kernel<T, DD, CC, BIAS, DROP, true>), dim3(nkt * BH),           \
+                     dim3(KvShape<BIAS>::kThreads), 0, s, Q, K, V, dO, a.LD, (T*)a.dK,        \
                      (T*)a.dV, a.Nq, a.Nk, nkt, BH, hpx, c, a.scale, off, bias, drop, dS)
-        if (a.d == 128) {
-          if (a.causal) FA_DKDV_DS_LAUNCH(128, true); else FA_DKDV_DS_LAUNCH(128, false);
-        } else {
-          if (a.causal) FA_DKDV_DS_LAUNCH(64, true); else FA_DKDV_DS_LAUNCH(64, false);
-        }
-#undef FA_DKDV_DS_LAUNCH
-        const hipError_t e = hipGetLastError();
-        if (e != hipSuccess) return e;
+      if (a.d == 128) {
+        if (a.causal) FA_DKDV_DS_LAUNCH(128, true); else FA_DKDV_DS_LAUNCH(128, false);
+      } else {
+        if (a.causal) FA_DKDV_DS_LAUNCH(64, true); else FA_DKDV_DS_LAUNCH(64, false);
       }
-      if ((stages & 4) && a.Nq > 0) {
-        const int nqt = (a.Nq + kDqBR - 1) / kDqBR;
-        const int nblocks = (a.causal ? (nqt + 1) / 2 : nqt) * BH;
+#undef FA_DKDV_DS_LAUNCH
+      const hipError_t e = hipGetLastError();
+      if (e != hipSuccess) return e;
+    }
+    if ((stages & 4) && a.Nq > 0) {
+      const int nqt = (a.Nq + kDqBR - 1) / kDqBR;
+      const int nblocks = (a.causal ? (nqt + 1) / 2 : nqt) * BH;
 #define FA_DQ_DS_LAUNCH(DD, CC)                                                                \
   hipLaunchKernelGGL((bwd_dq_ds_kernel<T, DD, CC>), dim3(nblocks), dim3(kDqThreads), 0, s, K, \
-                     (const T*)dS, (T*)a.dQ, a.Nq, a.Nk, nqt, a.scale, off)
-        if (a.d == 128) {
-          if (a.causal) FA_DQ_DS_LAUNCH(128, true); else FA_DQ_DS_LAUNCH(128, false);
-        } else {
-          if (a.causal) FA_DQ_DS_LAUNCH(64, true); else FA_DQ_DS_LAUNCH(64, false);
-        }
-#undef FA_DQ_DS_LAUNCH
-        return hipGetLastError();
+                     (const T*)dS, (T*)a.dQ, a.Nq, a.Nk, nqt, a.scale, off, bias)
+      if (a.d == 128) {
+        if (a.causal) FA_DQ_DS_LAUNCH(128, true); else FA_DQ_DS_LAUNCH(128, false);
+      } else {
+        if (a.causal) FA_DQ_DS_LAUNCH(64, true); else FA_DQ_DS_LAUNCH(64, false);
       }
-      return hipSuccess;
+#undef FA_DQ_DS_LAUNCH
+      return hipGetLastError();
     }
+    return hipSuccess;
+  }
+  if constexpr (!BIAS) {
     if ((stages & 6) == 6 && a.Nk > 0 && a.Nq > 0) {
       constexpr int kKvBC = KvShape<false>::kBC;
       const int nkt = (a.Nk + kKvBC - 1) / kKvBC;

@@ -59,7 +59,7 @@ struct BwdArgs {
   float* LD;  // fp32 workspace: per head and block of 32 query rows, L * log2(e) and -D, D = rowsum(dO * O)
   BiasArgs bias;
   DropArgs drop;
-  // 16-bit dtypes without a bias: the dS buffer (bwd_ds_bytes) when the
+  // 16-bit dtypes at d = 128: the dS buffer (bwd_ds_bytes) when the
   // backward stores dS in the dK/dV kernel and forms dQ from it; nullptr:
   // the dQ kernel recomputes S and dP instead.
   void* dS = nullptr;

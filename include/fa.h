@@ -104,12 +104,13 @@ fa_status fa_fwd(const void* Q, const void* K, const void* V, void* O, float* L,
  *  workgroups that recompute P and dP for their rows.  dQ comes one of two
  *  ways, with no atomic operations either way, so every output is
  *  deterministic:
- *   - stored dS (bf16 and fp16, d = 128, Nq and Nk >= 2048, no bias, a dS
- *     buffer of at most 8 GiB): the dK/dV workgroups also store dS, in a
- *     buffer after the per-row block (2 bytes per query-key pair, padded to
- *     32 x 32 blocks: B*H*ceil(Nq/32)*ceil(Nk/128)*8 KiB), and a second
- *     launch forms dQ = scale * dS K from it: the five GEMMs per tile pair
- *     of the 51CTO notes ("FlashAttention V2相比V1有哪些改进");
+ *   - stored dS (bf16 and fp16, d = 128, Nq and Nk >= 2048, a dS buffer of
+ *     at most 8 GiB; with or without a bias): the dK/dV workgroups also
+ *     store dS, in a buffer after the per-row block (2 bytes per query-key
+ *     pair, padded to 32 x 32 blocks and keys to 256:
+ *     B*H*ceil(Nq/32)*ceil(Nk/256)*16 KiB), and a second launch forms
+ *     dQ = scale * dS K from it: the five GEMMs per tile pair of the 51CTO
+ *     notes ("FlashAttention V2相比V1有哪些改进");
  *   - otherwise, workgroups per query block recompute P and dP for their
  *     rows and accumulate dQ in registers, in one launch with the dK/dV
  *     workgroups (seven GEMMs; faster at d = 64 and on short sequences).
@@ -266,14 +267,10 @@ fa_status fa_bias_tile_map(const void* bias, long long bias_sb, long long bias_s
 /* Workspace bytes fa_fwd needs for these arguments (0 when none). */
 size_t fa_fwd_workspace_size(int B, int H, int Nq, int Nk, int d, fa_dtype dtype, int num_splits);
 
-/* Workspace bytes fa_bwd needs for these arguments, with the dS buffer where
- * the stored-dS path runs (see fa_bwd); enough for fa_bwd_stages, fa_bwd_ex
- * and fa_bwd_bias with the same sizes. */
+/* Workspace bytes fa_bwd, fa_bwd_stages, fa_bwd_bias and fa_bwd_ex need for
+ * these arguments: the per-row block, and the dS buffer where the stored-dS
+ * path runs (see fa_bwd). */
 size_t fa_bwd_workspace_size(int B, int H, int Nq, int Nk, int d, fa_dtype dtype);
-
-/* Workspace bytes fa_bwd_bias, and fa_bwd_ex with a bias, need: the per-row
- * block only (with a bias dQ is always recomputed).  0 for invalid sizes. */
-size_t fa_bwd_bias_workspace_size(int B, int H, int Nq, int Nk, int d, fa_dtype dtype);
 
 /* Number of key splits fa_fwd uses for these arguments (1 on the tiled path). */
 int fa_fwd_num_splits(int B, int H, int Nq, int Nk, int d, fa_dtype dtype, int num_splits);

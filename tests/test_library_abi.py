@@ -282,21 +282,20 @@ def test_workspace_queries(lib):
 def test_stored_ds_workspace_rule(lib):
     """The backward stores dS (the buffer follows the per-row block) for bf16
     and fp16 at d = 128 with Nq, Nk >= 2048 and a buffer of at most 8 GiB;
-    with a bias, at d = 64, for fp32, short sides or larger buffers it
-    recomputes and needs the per-row block only."""
+    at d = 64, for fp32, short sides or larger buffers it recomputes and
+    needs the per-row block only."""
     def up(x):
         return (x + 255) // 256 * 256
 
     def rows(B, H, Nq):
         return up(B * H * ((Nq + 31) // 32) * 32 * 2 * 4)
 
-    def ds(B, H, Nq, Nk):  # 2 KB per 32 x 32 block, keys padded to 128
-        return up(B * H * ((Nq + 31) // 32) * 4 * ((Nk + 127) // 128) * 2048)
+    def ds(B, H, Nq, Nk):  # 2 KB per 32 x 32 block, keys padded to 256
+        return up(B * H * ((Nq + 31) // 32) * 8 * ((Nk + 255) // 256) * 2048)
 
     B, H, Nq, Nk = 1, 2, 2080, 2200
     for code in (fa.FA_BF16, fa.FA_FP16):
         assert lib.fa_bwd_workspace_size(B, H, Nq, Nk, 128, code) == rows(B, H, Nq) + ds(B, H, Nq, Nk)
-        assert lib.fa_bwd_bias_workspace_size(B, H, Nq, Nk, 128, code) == rows(B, H, Nq)
     assert lib.fa_bwd_workspace_size(B, H, Nq, Nk, 64, fa.FA_BF16) == rows(B, H, Nq)
     assert lib.fa_bwd_workspace_size(B, H, Nq, Nk, 128, fa.FA_FP32) == rows(B, H, Nq)
     assert lib.fa_bwd_workspace_size(B, H, 2047, Nk, 128, fa.FA_BF16) == rows(B, H, 2047)
@@ -305,15 +304,14 @@ def test_stored_ds_workspace_rule(lib):
     # the long-sequence workload: 4 GiB of dS blocks (the causal half is used)
     assert lib.fa_bwd_workspace_size(1, 32, 8192, 8192, 128, fa.FA_BF16) == \
         rows(1, 32, 8192) + 32 * 256 * 256 * 2048
-    assert lib.fa_bwd_bias_workspace_size(1, 1, 16, 16, 96, fa.FA_BF16) == 0
 
 
 def test_stored_ds_path_rejects_a_per_row_workspace(lib):
     """Without its dS buffer the stored-dS backward returns FA_ERR_WORKSPACE
-    before any launch; the per-row block alone is enough with a bias."""
+    before any launch."""
     B, H, N = 1, 1, 2048
     need = lib.fa_bwd_workspace_size(B, H, N, N, 128, fa.FA_BF16)
-    small = lib.fa_bwd_bias_workspace_size(B, H, N, N, 128, fa.FA_BF16)
+    small = ((B * H * (N // 32) * 64 * 4) + 255) // 256 * 256  # the per-row block alone
     assert small < need
     assert bwd(lib, B=B, H=H, Nq=N, Nk=N, d=128, ws=A, ws_bytes=small) == fa.FA_ERR_WORKSPACE
     assert bwd(lib, B=B, H=H, Nq=N, Nk=N, d=128, ws=A, ws_bytes=need - 256) == fa.FA_ERR_WORKSPACE

@@ -1,4 +1,4 @@
-"""The stored-dS backward (bf16/fp16, d = 128, Nq and Nk >= 2048, no bias).
+"""The stored-dS backward (bf16/fp16, d = 128, Nq and Nk >= 2048).
 
 There the dK/dV kernel stores dS in the workspace and dQ = scale * dS K is
 formed from it; elsewhere a dQ kernel recomputes S and dP.  These tests run
