@@ -3,7 +3,9 @@
 There the dK/dV kernel stores dS in the workspace and dQ = scale * dS K is
 formed from it; elsewhere a dQ kernel recomputes S and dP.  These tests run
 shapes above the threshold with ragged tails and bottom-right causal offsets
-against the float64 oracle, and compare the path with the recomputing one
+against the float64 oracle, with and without a bias (whose dK/dV workgroups
+cover 256 keys) and with a bias tile map, and compare the path with the
+recomputing one
 (fa_bwd_noalloc always recomputes): dK and dV come from the same arithmetic
 and must agree bit for bit; dQ may differ where a dS element rounds the other
 way to 16 bits, so the two are held to one rounding of dQ to bf16 (relative
@@ -17,7 +19,10 @@ import torch
 
 import oracle
 
+from exact_attention_118_amd import synth
+
 from test_parity_gpu import f64, make, rel_l2, say, tolerances
+from test_tilemap_gpu import _band, _padded
 
 pytestmark = pytest.mark.gpu
 
@@ -85,3 +90,54 @@ def test_stored_ds_matches_the_recomputing_path(gpu_lib, causal):
     torch.cuda.synchronize()
     for a, b in zip(st, ds):
         assert torch.equal(a, b)
+
+
+@pytest.mark.parametrize("causal", [True, False])
+def test_stored_ds_with_a_bias_against_the_oracle(gpu_lib, causal):
+    """A dense bias with dropped keys on a ragged shape above the threshold:
+    the 256-key dK/dV workgroups of the bias path store dS (keys padded to
+    256 in the dS buffer) and dQ is formed from it."""
+    fa = gpu_lib
+    B, H, Nq, Nk, d = 1, 2, 2080, 2300, 128
+    say(f"stored-dS backward with a bias q{Nq}k{Nk} causal={causal}")
+    assert fa.bwd_workspace_size(B, H, Nq, Nk, d, fa.FA_BF16) > _linear_ws(B, H, Nq)
+    x = make(B, H, Nq, Nk, d, torch.bfloat16, seed=24)
+    sq = (Nk + 7) // 8 * 8
+    bias = _padded(synth.make_bias(B, H, Nq, Nk, torch.bfloat16, seed=25, per_batch=False,
+                                   row_stride=sq, drop=0.1).cuda(), sq)
+    scale = 1.0 / math.sqrt(d)
+    O, L = fa.forward(x["Q"], x["K"], x["V"], scale, causal, bias=bias)
+    dQ, dK, dV = fa.backward(x["Q"], x["K"], x["V"], O, L, x["dO"], scale, causal, bias=bias)
+    torch.cuda.synchronize()
+    ref = oracle.attention_backward_batched(f64(x["Q"]), f64(x["K"]), f64(x["V"]), f64(x["dO"]),
+                                            scale, causal, bias=f64(bias))
+    _, _, tg = tolerances(torch.bfloat16)
+    for name, got, want in zip(("dQ", "dK", "dV"), (dQ, dK, dV), ref):
+        assert rel_l2(f64(got), want) <= tg, name
+
+
+def test_stored_ds_with_a_tile_map_changes_no_bit(gpu_lib):
+    """A banded bias (keys within 300 of the row) on a ragged shape above the
+    threshold, with and without its tile map: the dK/dV kernel then stores
+    only the query blocks of its key block's active tiles and the dQ kernel
+    feeds zeros for inactive tiles; the gradients must match bit for bit,
+    and the oracle."""
+    fa = gpu_lib
+    B, H, Nq, Nk, d = 1, 2, 2100, 2300, 128
+    say(f"stored-dS backward with a tile map q{Nq}k{Nk}")
+    x = make(B, H, Nq, Nk, d, torch.bfloat16, seed=26)
+    b2 = _band(Nq, Nk, 300, torch.bfloat16)
+    bias = _padded(b2.expand(1, H, Nq, Nk).contiguous(), (Nk + 7) // 8 * 8)
+    tmap = fa.fa_bias_tile_map(bias, B, H, Nq, Nk)
+    scale = 1.0 / math.sqrt(d)
+    O, L = fa.forward(x["Q"], x["K"], x["V"], scale, True, bias=bias)
+    g0 = fa.backward(x["Q"], x["K"], x["V"], O, L, x["dO"], scale, True, bias=bias)
+    g1 = fa.backward(x["Q"], x["K"], x["V"], O, L, x["dO"], scale, True, bias=bias, tile_map=tmap)
+    torch.cuda.synchronize()
+    for a, b in zip(g0, g1):
+        assert torch.equal(a, b)
+    ref = oracle.attention_backward_batched(f64(x["Q"]), f64(x["K"]), f64(x["V"]), f64(x["dO"]),
+                                            scale, True, bias=f64(bias))
+    _, _, tg = tolerances(torch.bfloat16)
+    for name, got, want in zip(("dQ", "dK", "dV"), g1, ref):
+        assert rel_l2(f64(got), want) <= tg, name
