@@ -60,11 +60,8 @@ KERNEL_RE = r"(fwd_kernel|bwd_fused_kernel|bwd_dkdv_kernel|bwd_dq_kernel|bwd_dq_
 
 
 def stores_ds(fa, w, code):
-    """True where fa_bwd takes the stored-dS path: its workspace then holds
-    the dS buffer after the per-row block (fa.h: 64 fp32 per head and block
-    of 32 query rows, rounded up to 256 bytes)."""
-    rows = (w.B * w.H * ((w.Nq + 31) // 32) * 64 * 4 + 255) // 256 * 256
-    return fa.load_library().fa_bwd_workspace_size(w.B, w.H, w.Nq, w.Nk, w.d, code) > rows
+    """True where fa_bwd takes the stored-dS path (dK/dV, then dQ from dS)."""
+    return fa.bwd_stores_ds(w.B, w.H, w.Nq, w.Nk, w.d, w.causal, code)
 
 
 def source_sha(path):

@@ -16,7 +16,8 @@ __all__ = [
     "FAError", "load_library", "lib_path", "fa_fwd", "fa_bwd", "fa_fwd_bias", "fa_bwd_bias",
     "fa_fwd_ex", "fa_bwd_ex", "fa_bias_tile_map", "fa_bwd_noalloc", "bwd_noalloc_max_rows",
     "forward", "backward",
-    "fwd_workspace_size", "bwd_workspace_size", "fwd_num_splits", "status_string", "version",
+    "fwd_workspace_size", "bwd_workspace_size", "bwd_stores_ds", "fwd_num_splits",
+    "status_string", "version",
     "FA_OK", "FA_ERR_NULL", "FA_ERR_SHAPE", "FA_ERR_UNSUPPORTED", "FA_ERR_ALIGN",
     "FA_ERR_WORKSPACE", "FA_ERR_HIP", "FA_BF16", "FA_FP32", "FA_FP16", "EXPORTED_SYMBOLS",
     "FA_BWD_PREPROCESS", "FA_BWD_DKDV", "FA_BWD_DQ", "FA_BWD_ALL",
@@ -29,7 +30,8 @@ FA_BWD_PREPROCESS, FA_BWD_DKDV, FA_BWD_DQ, FA_BWD_ALL = 1, 2, 4, 7
 
 EXPORTED_SYMBOLS = ("fa_fwd", "fa_bwd", "fa_bwd_stages", "fa_fwd_bias", "fa_bwd_bias",
                     "fa_fwd_ex", "fa_bwd_ex", "fa_bias_tile_map", "fa_bias_tile_map_size",
-                    "fa_fwd_workspace_size", "fa_bwd_workspace_size", "fa_fwd_num_splits",
+                    "fa_fwd_workspace_size", "fa_bwd_workspace_size", "fa_bwd_stores_ds",
+                    "fa_fwd_num_splits",
                     "fa_status_string", "fa_version", "fa_bwd_noalloc", "fa_bwd_noalloc_max_rows")
 
 _LIB = None
@@ -86,6 +88,8 @@ def load_library():
     lib.fa_fwd_workspace_size.restype = sz
     lib.fa_bwd_workspace_size.argtypes = [i, i, i, i, i, i]
     lib.fa_bwd_workspace_size.restype = sz
+    lib.fa_bwd_stores_ds.argtypes = [i, i, i, i, i, i, i]
+    lib.fa_bwd_stores_ds.restype = i
     lib.fa_fwd_num_splits.argtypes = [i, i, i, i, i, i, i]
     lib.fa_fwd_num_splits.restype = i
     lib.fa_status_string.argtypes = [i]
@@ -154,6 +158,11 @@ def fwd_workspace_size(B, H, Nq, Nk, d, dtype_code, num_splits=0) -> int:
 
 def bwd_workspace_size(B, H, Nq, Nk, d, dtype_code) -> int:
     return load_library().fa_bwd_workspace_size(B, H, Nq, Nk, d, dtype_code)
+
+
+def bwd_stores_ds(B, H, Nq, Nk, d, causal, dtype_code) -> bool:
+    """Whether fa_bwd with these arguments stores dS and forms dQ from it."""
+    return bool(load_library().fa_bwd_stores_ds(B, H, Nq, Nk, d, int(bool(causal)), dtype_code))
 
 
 def fwd_num_splits(B, H, Nq, Nk, d, dtype_code, num_splits=0) -> int:

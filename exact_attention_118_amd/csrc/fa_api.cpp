@@ -3,6 +3,7 @@
 
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
 #include <climits>
 #include <cmath>
 #include <cstdint>
@@ -122,19 +123,31 @@ size_t bwd_ws_bytes(int BH, int Nq) {
 // that recomputes S and dP (two of its three GEMMs).  The buffer holds 2
 // bytes per (query, key) pair, padded to 32 x 32 blocks, so it grows with
 // Nq * Nk.  The path runs for bf16 and fp16 at d = 128, with or without a
-// bias, with Nq and Nk of at least kDsMinLen and a buffer of at most
-// kDsMaxBytes.  Measured against recomputation (same process): 4-9% faster
-// at d = 128 for N = 2048-8192 (steady state), 6-12% with a dense bias
-// (single calls: its dQ kernel no longer reads the bias); slower at d = 64,
-// where the recomputed GEMMs
-// cost half as much and the dS traffic the same, and on short sequences,
-// where the fused recomputing launch runs dQ beside the key blocks' chains.
+// bias, with Nq and Nk of at least kDsMinLen, a buffer of at most
+// kDsMaxBytes, and a grid of at least kDsMinBlocks 128-key blocks over all
+// heads (B*H*ceil(min(Nq, Nk)/128); twice that with a causal mask).
+// Measured against recomputation (same process, steady state): 4-15% faster
+// at d = 128 from 1024 such blocks (N = 1024-8192), and non-causal from 512;
+// 6-12% with a dense bias (single calls: its dQ kernel no longer reads the
+// bias).  Slower at d = 64, where the recomputed GEMMs cost half as much and
+// the dS traffic the same, and on small grids (6-58% with 128-512 blocks
+// causal, 40% with 128 non-causal), where the fused recomputing launch runs
+// the dQ workgroups on the CUs that the key blocks' chains leave idle.
 constexpr size_t kDsMaxBytes = size_t(8) << 30;
-constexpr int kDsMinLen = 2048;
-size_t bwd_ds_ws_bytes(int BH, int Nq, int Nk, int d, fa_dtype dtype) {
-  if (dtype == FA_FP32 || d != 128 || BH <= 0 || Nq < kDsMinLen || Nk < kDsMinLen) return 0;
-  const size_t b = fa::bwd_ds_bytes(BH, Nq, Nk);
-  return b <= kDsMaxBytes ? round_up(b, kWsAlign) : 0;
+constexpr int kDsMinLen = 1024;
+constexpr long long kDsMinBlocks = 512;
+bool bwd_stores_ds(int BH, int Nq, int Nk, int d, bool causal, fa_dtype dtype) {
+  if (dtype == FA_FP32 || d != 128 || BH <= 0 || Nq < kDsMinLen || Nk < kDsMinLen) return false;
+  const long long blocks = (long long)BH * ((std::min(Nq, Nk) + 127) / 128);
+  if (blocks < (causal ? 2 : 1) * kDsMinBlocks) return false;
+  return fa::bwd_ds_bytes(BH, Nq, Nk) <= kDsMaxBytes;
+}
+// dS buffer bytes of a call with these sizes (0: it recomputes dQ).  The
+// workspace query, which has no causal argument, asks for the non-causal
+// rule, whose grid bound is the lower one.
+size_t bwd_ds_ws_bytes(int BH, int Nq, int Nk, int d, bool causal, fa_dtype dtype) {
+  return bwd_stores_ds(BH, Nq, Nk, d, causal, dtype) ? round_up(fa::bwd_ds_bytes(BH, Nq, Nk), kWsAlign)
+                                                     : 0;
 }
 
 // Scratch of fa_bwd_noalloc: the per-row L*log2(e) and -D that fa_bwd keeps
@@ -200,7 +213,12 @@ size_t fa_fwd_workspace_size(int B, int H, int Nq, int Nk, int d, fa_dtype dtype
 
 size_t fa_bwd_workspace_size(int B, int H, int Nq, int Nk, int d, fa_dtype dtype) {
   if (check_dims(B, H, Nq, Nk, d, 1.f, 0, dtype) != FA_OK) return 0;
-  return bwd_ws_bytes(B * H, Nq) + bwd_ds_ws_bytes(B * H, Nq, Nk, d, dtype);
+  return bwd_ws_bytes(B * H, Nq) + bwd_ds_ws_bytes(B * H, Nq, Nk, d, false, dtype);
+}
+
+int fa_bwd_stores_ds(int B, int H, int Nq, int Nk, int d, int causal, fa_dtype dtype) {
+  if (check_dims(B, H, Nq, Nk, d, 1.f, causal, dtype) != FA_OK) return 0;
+  return bwd_stores_ds(B * H, Nq, Nk, d, causal != 0, dtype) ? 1 : 0;
 }
 
 }  // extern "C"
@@ -336,7 +354,7 @@ fa_status bwd_impl(const void* Q, const void* K, const void* V, const fa::BiasAr
     return FA_ERR_ALIGN;
   // stored dS, where it runs (not for fa_bwd_noalloc)
   const size_t ws_ld = bwd_ws_bytes(B * H, Nq);
-  const size_t ws_ds = allow_ds ? bwd_ds_ws_bytes(B * H, Nq, Nk, d, dtype) : 0;
+  const size_t ws_ds = allow_ds ? bwd_ds_ws_bytes(B * H, Nq, Nk, d, causal != 0, dtype) : 0;
   if (Nq > 0 && (!workspace || workspace_bytes < ws_ld + ws_ds)) return FA_ERR_WORKSPACE;
   if (Nq > 0 && !aligned(workspace)) return FA_ERR_ALIGN;
   fa::BwdArgs a{Q, K, V, O, L, dO, dQ, dK, dV, B, H, Nq, Nk, d, scale, causal != 0,

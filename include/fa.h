@@ -104,8 +104,10 @@ fa_status fa_fwd(const void* Q, const void* K, const void* V, void* O, float* L,
  *  workgroups that recompute P and dP for their rows.  dQ comes one of two
  *  ways, with no atomic operations either way, so every output is
  *  deterministic:
- *   - stored dS (bf16 and fp16, d = 128, Nq and Nk >= 2048, a dS buffer of
- *     at most 8 GiB; with or without a bias): the dK/dV workgroups also
+ *   - stored dS (bf16 and fp16, d = 128, Nq and Nk >= 1024, at least 512
+ *     128-key blocks over all heads, B*H*ceil(min(Nq, Nk)/128), or 1024 with
+ *     a causal mask, a dS buffer of at most 8 GiB; with or without a bias;
+ *     fa_bwd_stores_ds tells): the dK/dV workgroups also
  *     store dS, in a buffer after the per-row block (2 bytes per query-key
  *     pair, padded to 32 x 32 blocks and keys to 256:
  *     B*H*ceil(Nq/32)*ceil(Nk/256)*16 KiB), and a second launch forms
@@ -113,7 +115,8 @@ fa_status fa_fwd(const void* Q, const void* K, const void* V, void* O, float* L,
  *     notes ("FlashAttention V2相比V1有哪些改进");
  *   - otherwise, workgroups per query block recompute P and dP for their
  *     rows and accumulate dQ in registers, in one launch with the dK/dV
- *     workgroups (seven GEMMs; faster at d = 64 and on short sequences).
+ *     workgroups (seven GEMMs; faster at d = 64 and on small grids, where
+ *     the dQ workgroups run on CUs that the key blocks' chains leave idle).
  */
 fa_status fa_bwd(const void* Q, const void* K, const void* V, const void* O, const float* L,
                  const void* dO, void* dQ, void* dK, void* dV,
@@ -268,9 +271,15 @@ fa_status fa_bias_tile_map(const void* bias, long long bias_sb, long long bias_s
 size_t fa_fwd_workspace_size(int B, int H, int Nq, int Nk, int d, fa_dtype dtype, int num_splits);
 
 /* Workspace bytes fa_bwd, fa_bwd_stages, fa_bwd_bias and fa_bwd_ex need for
- * these arguments: the per-row block, and the dS buffer where the stored-dS
- * path runs (see fa_bwd). */
+ * these arguments, causal or not: the per-row block, and the dS buffer where
+ * the stored-dS path runs for a non-causal call (see fa_bwd; a causal call
+ * with the same sizes uses it or needs less). */
 size_t fa_bwd_workspace_size(int B, int H, int Nq, int Nk, int d, fa_dtype dtype);
+
+/* 1 when fa_bwd (and fa_bwd_stages, fa_bwd_bias, fa_bwd_ex) with these
+ * arguments stores dS and forms dQ from it, 0 when it recomputes dQ (and for
+ * invalid arguments).  fa_bwd_noalloc always recomputes. */
+int fa_bwd_stores_ds(int B, int H, int Nq, int Nk, int d, int causal, fa_dtype dtype);
 
 /* Number of key splits fa_fwd uses for these arguments (1 on the tiled path). */
 int fa_fwd_num_splits(int B, int H, int Nq, int Nk, int d, fa_dtype dtype, int num_splits);

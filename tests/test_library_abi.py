@@ -281,9 +281,10 @@ def test_workspace_queries(lib):
 
 def test_stored_ds_workspace_rule(lib):
     """The backward stores dS (the buffer follows the per-row block) for bf16
-    and fp16 at d = 128 with Nq, Nk >= 2048 and a buffer of at most 8 GiB;
-    at d = 64, for fp32, short sides or larger buffers it recomputes and
-    needs the per-row block only."""
+    and fp16 at d = 128 with Nq, Nk >= 1024, at least 512 128-key blocks over
+    all heads (1024 with a causal mask) and a buffer of at most 8 GiB; else
+    it recomputes dQ and needs the per-row block only.  The workspace query
+    has no causal argument and sizes for the non-causal rule."""
     def up(x):
         return (x + 255) // 256 * 256
 
@@ -293,29 +294,43 @@ def test_stored_ds_workspace_rule(lib):
     def ds(B, H, Nq, Nk):  # 2 KB per 32 x 32 block, keys padded to 256
         return up(B * H * ((Nq + 31) // 32) * 8 * ((Nk + 255) // 256) * 2048)
 
-    B, H, Nq, Nk = 1, 2, 2080, 2200
+    def stores(B, H, Nq, Nk, d=128, causal=1, code=fa.FA_BF16):
+        return lib.fa_bwd_stores_ds(B, H, Nq, Nk, d, causal, code)
+
+    # 128 heads x 9 blocks: both rules
     for code in (fa.FA_BF16, fa.FA_FP16):
-        assert lib.fa_bwd_workspace_size(B, H, Nq, Nk, 128, code) == rows(B, H, Nq) + ds(B, H, Nq, Nk)
-    assert lib.fa_bwd_workspace_size(B, H, Nq, Nk, 64, fa.FA_BF16) == rows(B, H, Nq)
-    assert lib.fa_bwd_workspace_size(B, H, Nq, Nk, 128, fa.FA_FP32) == rows(B, H, Nq)
-    assert lib.fa_bwd_workspace_size(B, H, 2047, Nk, 128, fa.FA_BF16) == rows(B, H, 2047)
-    assert lib.fa_bwd_workspace_size(B, H, Nq, 2047, 128, fa.FA_BF16) == rows(B, H, Nq)
-    assert lib.fa_bwd_workspace_size(4, 32, 16384, 16384, 128, fa.FA_BF16) == rows(4, 32, 16384)
+        assert lib.fa_bwd_workspace_size(1, 128, 1056, 1100, 128, code) == \
+            rows(1, 128, 1056) + ds(1, 128, 1056, 1100)
+        assert stores(1, 128, 1056, 1100, code=code) == 1
+        assert stores(1, 128, 1056, 1100, causal=0, code=code) == 1
+    # 64 heads x 9 blocks: non-causal only; the query sizes for it
+    assert stores(1, 64, 1100, 1040, causal=0) == 1 and stores(1, 64, 1100, 1040) == 0
+    assert lib.fa_bwd_workspace_size(1, 64, 1100, 1040, 128, fa.FA_BF16) == \
+        rows(1, 64, 1100) + ds(1, 64, 1100, 1040)
+    # small grids, d = 64, fp32, short sides, buffers above 8 GiB: recomputed
+    for args in ((1, 8, 2048, 2048, 128, fa.FA_BF16), (2, 64, 2048, 2048, 64, fa.FA_BF16),
+                 (2, 64, 2048, 2048, 128, fa.FA_FP32), (4, 128, 1000, 2048, 128, fa.FA_BF16),
+                 (4, 32, 16384, 16384, 128, fa.FA_BF16)):
+        B, H, Nq, Nk, d, code = args
+        assert stores(B, H, Nq, Nk, d, 0, code) == 0, args
+        assert lib.fa_bwd_workspace_size(B, H, Nq, Nk, d, code) == rows(B, H, Nq), args
     # the long-sequence workload: 4 GiB of dS blocks (the causal half is used)
+    assert stores(1, 32, 8192, 8192) == 1
     assert lib.fa_bwd_workspace_size(1, 32, 8192, 8192, 128, fa.FA_BF16) == \
         rows(1, 32, 8192) + 32 * 256 * 256 * 2048
+    assert stores(1, 1, 16, 16, d=96) == 0
 
 
 def test_stored_ds_path_rejects_a_per_row_workspace(lib):
     """Without its dS buffer the stored-dS backward returns FA_ERR_WORKSPACE
     before any launch."""
-    B, H, N = 1, 1, 2048
+    B, H, N = 1, 128, 1024
+    assert lib.fa_bwd_stores_ds(B, H, N, N, 128, 0, fa.FA_BF16) == 1
     need = lib.fa_bwd_workspace_size(B, H, N, N, 128, fa.FA_BF16)
     small = ((B * H * (N // 32) * 64 * 4) + 255) // 256 * 256  # the per-row block alone
     assert small < need
     assert bwd(lib, B=B, H=H, Nq=N, Nk=N, d=128, ws=A, ws_bytes=small) == fa.FA_ERR_WORKSPACE
     assert bwd(lib, B=B, H=H, Nq=N, Nk=N, d=128, ws=A, ws_bytes=need - 256) == fa.FA_ERR_WORKSPACE
-
 
 def test_binding_fails_loudly_without_the_library(monkeypatch, tmp_path):
     monkeypatch.setattr(fa, "_LIB", None)

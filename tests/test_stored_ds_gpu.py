@@ -1,15 +1,16 @@
-"""The stored-dS backward (bf16/fp16, d = 128, Nq and Nk >= 2048).
+"""The stored-dS backward (bf16/fp16, d = 128, Nq and Nk >= 1024, at least
+512 128-key blocks over all heads, 1024 with a causal mask).
 
 There the dK/dV kernel stores dS in the workspace and dQ = scale * dS K is
 formed from it; elsewhere a dQ kernel recomputes S and dP.  These tests run
-shapes above the threshold with ragged tails and bottom-right causal offsets
-against the float64 oracle, with and without a bias (whose dK/dV workgroups
-cover 256 keys) and with a bias tile map, and compare the path with the
-recomputing one
-(fa_bwd_noalloc always recomputes): dK and dV come from the same arithmetic
-and must agree bit for bit; dQ may differ where a dS element rounds the other
-way to 16 bits, so the two are held to one rounding of dQ to bf16 (relative
-L2 2^-8) apart.
+shapes that take the path, with ragged tails and bottom-right causal offsets,
+with and without a bias (whose dK/dV workgroups cover 256 keys) and with a
+bias tile map, against the float64 oracle on a few heads (the first, a middle
+and the last: the grids need many heads), and compare the path with the
+recomputing one (fa_bwd_noalloc always recomputes): dK and dV come from the
+same arithmetic and must agree bit for bit; dQ may differ where a dS element
+rounds the other way to 16 bits, so the two are held to one rounding of dQ
+to bf16 (relative L2 2^-8) apart.
 """
 
 import math
@@ -18,7 +19,6 @@ import pytest
 import torch
 
 import oracle
-
 from exact_attention_118_amd import synth
 
 from test_parity_gpu import f64, make, rel_l2, say, tolerances
@@ -28,11 +28,11 @@ pytestmark = pytest.mark.gpu
 
 CASES = [
     # B, H, Nq, Nk, causal, dtype
-    (1, 2, 2080, 2200, True, torch.bfloat16),    # bottom-right causal, ragged, Nq < Nk
-    (1, 2, 2200, 2080, False, torch.bfloat16),   # Nq > Nk, ragged
-    (2, 1, 2048, 2048, True, torch.bfloat16),    # exact tiles
-    (1, 2, 2111, 2111, True, torch.float16),
-    (1, 1, 2048, 2300, False, torch.float16),
+    (1, 128, 1056, 1100, True, torch.bfloat16),   # bottom-right causal, ragged, Nq < Nk
+    (1, 64, 1100, 1040, False, torch.bfloat16),   # Nq > Nk, ragged
+    (2, 64, 1024, 1024, True, torch.bfloat16),    # exact tiles
+    (1, 128, 1111, 1111, True, torch.float16),
+    (1, 64, 1024, 1300, False, torch.float16),
 ]
 
 
@@ -41,8 +41,23 @@ def _id(c):
     return f"b{B}h{H}q{Nq}k{Nk}{'c' if causal else ''}-{str(dt).split('.')[-1]}"
 
 
-def _linear_ws(B, H, Nq):
-    return ((B * H * ((Nq + 31) // 32) * 32 * 2 * 4) + 255) // 256 * 256
+def _code(fa, dt):
+    return fa.FA_BF16 if dt == torch.bfloat16 else fa.FA_FP16
+
+
+def _check_heads(x, grads, scale, causal, dt, bias=None):
+    """dQ, dK, dV of heads 0, BH/2 and BH-1 against the oracle."""
+    B, H = x["Q"].shape[:2]
+    BH = B * H
+    flat = {k: v.reshape(BH, v.shape[2], v.shape[3]) for k, v in x.items()}
+    g = [t.reshape(BH, t.shape[2], t.shape[3]) for t in grads]
+    _, _, tg = tolerances(dt)
+    for h in (0, BH // 2, BH - 1):
+        hb = None if bias is None else f64(bias[0, h % H])
+        Q, K, V, dO = (f64(flat[k][h]) for k in ("Q", "K", "V", "dO"))
+        ref = oracle.attention_backward(Q, K, V, dO, scale, causal, bias=hb)
+        for name, got, want in zip(("dQ", "dK", "dV"), g, ref):
+            assert rel_l2(f64(got[h]), want) <= tg, (h, name)
 
 
 @pytest.mark.parametrize("case", CASES, ids=_id)
@@ -51,26 +66,21 @@ def test_stored_ds_backward_against_the_oracle(gpu_lib, case):
     B, H, Nq, Nk, causal, dt = case
     d = 128
     say(f"stored-dS backward {_id(case)}")
-    code = fa.FA_BF16 if dt == torch.bfloat16 else fa.FA_FP16
-    # the workspace query includes the dS buffer: the path runs
-    assert fa.bwd_workspace_size(B, H, Nq, Nk, d, code) > _linear_ws(B, H, Nq)
+    assert fa.bwd_stores_ds(B, H, Nq, Nk, d, causal, _code(fa, dt))
     x = make(B, H, Nq, Nk, d, dt, seed=21)
     scale = 1.0 / math.sqrt(d)
     O, L = fa.forward(x["Q"], x["K"], x["V"], scale, causal)
-    dQ, dK, dV = fa.backward(x["Q"], x["K"], x["V"], O, L, x["dO"], scale, causal)
+    grads = fa.backward(x["Q"], x["K"], x["V"], O, L, x["dO"], scale, causal)
     torch.cuda.synchronize()
-    ref = oracle.attention_backward_batched(f64(x["Q"]), f64(x["K"]), f64(x["V"]), f64(x["dO"]),
-                                            scale, causal)
-    _, _, tg = tolerances(dt)
-    for name, got, want in zip(("dQ", "dK", "dV"), (dQ, dK, dV), ref):
-        assert rel_l2(f64(got), want) <= tg, name
+    _check_heads(x, grads, scale, causal, dt)
 
 
 @pytest.mark.parametrize("causal", [True, False])
 def test_stored_ds_matches_the_recomputing_path(gpu_lib, causal):
     fa = gpu_lib
-    B, H, N, d = 1, 4, 2304, 128
+    B, H, N, d = 1, 128, 1024, 128
     say(f"stored dS against recomputation b{B}h{H}n{N} causal={causal}")
+    assert fa.bwd_stores_ds(B, H, N, N, d, causal, fa.FA_BF16)
     x = make(B, H, N, N, d, torch.bfloat16, seed=22)
     scale = 1.0 / math.sqrt(d)
     O, L = fa.forward(x["Q"], x["K"], x["V"], scale, causal)
@@ -94,37 +104,33 @@ def test_stored_ds_matches_the_recomputing_path(gpu_lib, causal):
 
 @pytest.mark.parametrize("causal", [True, False])
 def test_stored_ds_with_a_bias_against_the_oracle(gpu_lib, causal):
-    """A dense bias with dropped keys on a ragged shape above the threshold:
-    the 256-key dK/dV workgroups of the bias path store dS (keys padded to
-    256 in the dS buffer) and dQ is formed from it."""
+    """A dense bias with dropped keys on a ragged shape: the 256-key dK/dV
+    workgroups of the bias path store dS (keys padded to 256 in the dS
+    buffer) and dQ is formed from it."""
     fa = gpu_lib
-    B, H, Nq, Nk, d = 1, 2, 2080, 2300, 128
+    B, H, Nq, Nk, d = 1, 128, 1056, 1100, 128
     say(f"stored-dS backward with a bias q{Nq}k{Nk} causal={causal}")
-    assert fa.bwd_workspace_size(B, H, Nq, Nk, d, fa.FA_BF16) > _linear_ws(B, H, Nq)
+    assert fa.bwd_stores_ds(B, H, Nq, Nk, d, causal, fa.FA_BF16)
     x = make(B, H, Nq, Nk, d, torch.bfloat16, seed=24)
     sq = (Nk + 7) // 8 * 8
     bias = _padded(synth.make_bias(B, H, Nq, Nk, torch.bfloat16, seed=25, per_batch=False,
                                    row_stride=sq, drop=0.1).cuda(), sq)
     scale = 1.0 / math.sqrt(d)
     O, L = fa.forward(x["Q"], x["K"], x["V"], scale, causal, bias=bias)
-    dQ, dK, dV = fa.backward(x["Q"], x["K"], x["V"], O, L, x["dO"], scale, causal, bias=bias)
+    grads = fa.backward(x["Q"], x["K"], x["V"], O, L, x["dO"], scale, causal, bias=bias)
     torch.cuda.synchronize()
-    ref = oracle.attention_backward_batched(f64(x["Q"]), f64(x["K"]), f64(x["V"]), f64(x["dO"]),
-                                            scale, causal, bias=f64(bias))
-    _, _, tg = tolerances(torch.bfloat16)
-    for name, got, want in zip(("dQ", "dK", "dV"), (dQ, dK, dV), ref):
-        assert rel_l2(f64(got), want) <= tg, name
+    _check_heads(x, grads, scale, causal, torch.bfloat16, bias=bias)
 
 
 def test_stored_ds_with_a_tile_map_changes_no_bit(gpu_lib):
-    """A banded bias (keys within 300 of the row) on a ragged shape above the
-    threshold, with and without its tile map: the dK/dV kernel then stores
-    only the query blocks of its key block's active tiles and the dQ kernel
-    feeds zeros for inactive tiles; the gradients must match bit for bit,
-    and the oracle."""
+    """A banded bias (keys within 300 of the row) on a ragged shape, with and
+    without its tile map: the dK/dV kernel then stores only the query blocks
+    of its key block's active tiles and the dQ kernel feeds zeros for
+    inactive tiles; the gradients must match bit for bit, and the oracle."""
     fa = gpu_lib
-    B, H, Nq, Nk, d = 1, 2, 2100, 2300, 128
+    B, H, Nq, Nk, d = 1, 128, 1100, 1300, 128
     say(f"stored-dS backward with a tile map q{Nq}k{Nk}")
+    assert fa.bwd_stores_ds(B, H, Nq, Nk, d, True, fa.FA_BF16)
     x = make(B, H, Nq, Nk, d, torch.bfloat16, seed=26)
     b2 = _band(Nq, Nk, 300, torch.bfloat16)
     bias = _padded(b2.expand(1, H, Nq, Nk).contiguous(), (Nk + 7) // 8 * 8)
@@ -136,8 +142,22 @@ def test_stored_ds_with_a_tile_map_changes_no_bit(gpu_lib):
     torch.cuda.synchronize()
     for a, b in zip(g0, g1):
         assert torch.equal(a, b)
-    ref = oracle.attention_backward_batched(f64(x["Q"]), f64(x["K"]), f64(x["V"]), f64(x["dO"]),
-                                            scale, True, bias=f64(bias))
-    _, _, tg = tolerances(torch.bfloat16)
-    for name, got, want in zip(("dQ", "dK", "dV"), g1, ref):
-        assert rel_l2(f64(got), want) <= tg, name
+    _check_heads(x, g1, scale, True, torch.bfloat16, bias=bias)
+
+
+def test_small_grids_recompute(gpu_lib):
+    """Where the grid is small the backward keeps the recomputing launch; its
+    results are those of fa_bwd_noalloc bit for bit."""
+    fa = gpu_lib
+    B, H, N, d = 1, 8, 2048, 128
+    say(f"small grid b{B}h{H}n{N} recomputes")
+    assert not fa.bwd_stores_ds(B, H, N, N, d, True, fa.FA_BF16)
+    x = make(B, H, N, N, d, torch.bfloat16, seed=27)
+    scale = 1.0 / math.sqrt(d)
+    O, L = fa.forward(x["Q"], x["K"], x["V"], scale, True)
+    g = fa.backward(x["Q"], x["K"], x["V"], O, L, x["dO"], scale, True)
+    rc = [torch.full_like(t, float("nan")) for t in g]
+    fa.fa_bwd_noalloc(x["Q"], x["K"], x["V"], O, L, x["dO"], *rc, scale, True)
+    torch.cuda.synchronize()
+    for a, b in zip(g, rc):
+        assert torch.equal(a, b)

@@ -1,11 +1,12 @@
 """Calls enqueued on a side stream (the `stream` argument of the binding).
 
 The workspaces the binding allocates for such a call (split-path partials,
-the backward pass's per-row pairs and, from 2048 rows and keys at d = 128, its
-stored dS) must stay reserved for that stream until
-its kernels have used them; the results are checked against the float64
-oracle after synchronising.  Other allocations on the current stream run in
-between, so a workspace handed to them too early would be overwritten.
+the backward pass's per-row pairs and, on a grid of 128 heads of 1024 rows and
+keys at d = 128, its stored dS) must stay reserved for that stream until its
+kernels have used them; the results are checked against the float64 oracle
+after synchronising (on three of those 128 heads).  Other allocations on the
+current stream run in between, so a workspace handed to them too early would
+be overwritten.
 """
 
 import math
@@ -32,9 +33,10 @@ def test_side_stream_split_forward_and_backward(gpu_lib):
                             seed=21, device="cpu")
     x = synth.make_inputs(synth.Workload("bwd", 2, 4, 700, 700, 128, True, torch.bfloat16),
                           seed=22, device="cpu")
-    # long enough for the backward to store dS in its workspace
-    y = synth.make_inputs(synth.Workload("bwd_ds", 1, 2, 2048, 2048, 128, True, torch.bfloat16),
+    # enough heads and keys for the backward to store dS in its workspace
+    y = synth.make_inputs(synth.Workload("bwd_ds", 1, 128, 1024, 1024, 128, True, torch.bfloat16),
                           seed=23, device="cpu")
+    assert fa.bwd_stores_ds(1, 128, 1024, 1024, 128, True, fa.FA_BF16)
     dec = {k: v.cuda() for k, v in dec.items()}
     x = {k: v.cuda() for k, v in x.items()}
     y = {k: v.cuda() for k, v in y.items()}
@@ -62,7 +64,8 @@ def test_side_stream_split_forward_and_backward(gpu_lib):
     Or, Lr = oracle.attention_forward_batched(f64(dec["Q"]), f64(dec["K"]), f64(dec["V"]), scale, False)
     ref = oracle.attention_backward_batched(f64(x["Q"]), f64(x["K"]), f64(x["V"]), f64(x["dO"]),
                                             scale, True)
-    ref1 = oracle.attention_backward_batched(f64(y["Q"]), f64(y["K"]), f64(y["V"]), f64(y["dO"]),
+    heads = [0, 63, 127]
+    ref1 = oracle.attention_backward_batched(*(f64(y[k][:, heads]) for k in ("Q", "K", "V", "dO")),
                                              scale, True)
     for Od, Ld, g, g1 in outs:
         assert float(np.max(np.abs(f64(Od) - Or))) <= 2e-2
@@ -70,4 +73,5 @@ def test_side_stream_split_forward_and_backward(gpu_lib):
         for got, want in zip(g, ref):
             assert np.linalg.norm(f64(got) - want) / np.linalg.norm(want) <= 1e-2
         for got, want in zip(g1, ref1):
-            assert np.linalg.norm(f64(got) - want) / np.linalg.norm(want) <= 1e-2
+            got = f64(got[:, heads])
+            assert np.linalg.norm(got - want) / np.linalg.norm(want) <= 1e-2
