@@ -115,7 +115,7 @@ SplitWs split_ws(int BH, int d, int splits) {
 // Backward workspace: per head and block of 32 query rows, the rows' fp32
 // L*log2(e) and then their -D (rows past Nq zero).
 size_t bwd_ws_bytes(int BH, int Nq) {
-  return round_up((size_t)BH * ((Nq + 31) / 32) * 64 * sizeof(float), kWsAlign);
+  return round_up((size_t)BH * ((Nq + 31LL) / 32) * 64 * sizeof(float), kWsAlign);
 }
 
 // After it, the dS buffer of the stored-dS backward, where that path runs:
@@ -138,8 +138,13 @@ constexpr int kDsMinLen = 1024;
 constexpr long long kDsMinBlocks = 512;
 bool bwd_stores_ds(int BH, int Nq, int Nk, int d, bool causal, fa_dtype dtype) {
   if (dtype == FA_FP32 || d != 128 || BH <= 0 || Nq < kDsMinLen || Nk < kDsMinLen) return false;
-  const long long blocks = (long long)BH * ((std::min(Nq, Nk) + 127) / 128);
+  const long long blocks = (long long)BH * ((std::min(Nq, Nk) + 127LL) / 128);
   if (blocks < (causal ? 2 : 1) * kDsMinBlocks) return false;
+  // The padded buffer holds at least 2 bytes per pair: past the bound by that
+  // count (in 128-bit arithmetic), the call recomputes.  Below it Nq and Nk
+  // are at most 2^22, far from overflowing fa::bwd_ds_bytes, which sizes the
+  // padded buffer exactly (check_dims admits Nk near 2^31).
+  if ((unsigned __int128)BH * (unsigned)Nq * (unsigned)Nk * 2 > kDsMaxBytes) return false;
   return fa::bwd_ds_bytes(BH, Nq, Nk) <= kDsMaxBytes;
 }
 // dS buffer bytes of a call with these sizes (0: it recomputes dQ).  The
@@ -236,8 +241,8 @@ MapGeom map_geom(long long sb, long long sh, int B, int H, int Nq, int Nk) {
   MapGeom g;
   g.Bb = sb ? B : 1;
   g.Hb = sh ? H : 1;
-  g.nqt = (Nq + 127) / 128;
-  g.nkt4 = ((Nk + 63) / 64 + 3) / 4 * 4;
+  g.nqt = (Nq + 127LL) / 128;
+  g.nkt4 = ((Nk + 63LL) / 64 + 3) / 4 * 4;
   return g;
 }
 

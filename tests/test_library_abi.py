@@ -319,6 +319,14 @@ def test_stored_ds_workspace_rule(lib):
     assert lib.fa_bwd_workspace_size(1, 32, 8192, 8192, 128, fa.FA_BF16) == \
         rows(1, 32, 8192) + 32 * 256 * 256 * 2048
     assert stores(1, 1, 16, 16, d=96) == 0
+    # the largest sides the argument checks admit (B*H*ceil(N/64) < 2^31):
+    # far past 8 GiB, sized without overflow
+    big = 2 ** 31 // 64 * 64 - 64
+    for args in ((1, 64, 1024, big), (1, 1, 65536, big), (1, 1, big, big),
+                 (1, 1, 2 ** 31 - 1, 2 ** 31 - 1)):
+        B, H, Nq, Nk = args
+        assert lib.fa_bwd_stores_ds(B, H, Nq, Nk, 128, 0, fa.FA_BF16) == 0, args
+        assert lib.fa_bwd_workspace_size(B, H, Nq, Nk, 128, fa.FA_BF16) == rows(B, H, Nq), args
 
 
 def test_stored_ds_path_rejects_a_per_row_workspace(lib):
